@@ -1,0 +1,163 @@
+"""Direct receive: packed NVFP4 rows -> the expert GEMM's grouped operands (CPU oracle; test only).
+
+P1, PR description and first commit message: the receiver builds the grouped
+NVFP4 tensor for the expert GEMM straight from the received rows in one pass;
+the rowwise operand reuses the sender's codes, and the columnwise operand is
+an RHT operand quantized with a per-expert scale derived from a bound, so that
+neither a BF16 round trip nor an amax pass is needed.  P3, description and bot
+summary: row-scaled (per-token) NVFP4 tensors are GEMM operands, which is the
+form the reused rowwise codes take here.
+
+This module defines the direct receive as the unfused pipeline
+
+    route_plan -> gather the packed rows -> decode to exact values ->
+    16-point RHT down each column -> quantize with the bound-derived scale.
+
+Decoded NVFP4 values carry at most 6 significant bits, so a BF16 round trip
+would be lossless: the one-pass kernel must equal this pipeline exactly.
+"""
+
+import numpy as np
+
+from . import formats as F
+from . import nvfp4
+from .rht import rht16
+from .routing import route_plan
+
+
+# ------------------------------------------------------------------ shared columnwise quantizer
+def quantize_blocks(y, D, mode):
+    """Quantize post-RHT blocks y [..., 16] (float32) with global decode scale D.
+
+    a = max |y_i| over the block; s = E4M3(fl32(fl32(a / 6) / D)).
+    mode "pow2" (R16; D a power of two): index = E2M1 rounding (R2) of
+        v = fl32(|y| / (s * D)), the exact quotient rounded once to float32.
+    mode "fp32" (R19/R20; D any float32): c = fl32(s * D), v = fl32(|y| / c).
+    D = 0, or s = 0, gives magnitude index 0.  The code's sign is y's sign bit.
+    Returns (codes uint8 [..., 16], scale codes uint8 [...]).
+    """
+    y = np.asarray(y, dtype=np.float32)
+    D32 = np.float32(D)
+    a = np.abs(y).max(axis=-1)
+    if D32 > 0:
+        pre = (a / np.float32(6.0)) / D32                 # two float32 roundings, as written
+        s_code = F.e4m3_encode(pre.astype(np.float64))
+    else:
+        s_code = np.zeros(a.shape, dtype=np.uint8)
+    s_val = F.e4m3_decode(s_code)
+    ay = np.abs(y)
+    ok = (s_val > 0)[..., None] & np.ones(y.shape, dtype=bool)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        if mode == "pow2":
+            q = ay.astype(np.float64) / (s_val[..., None] * float(D32))
+            v = q.astype(np.float32)
+        elif mode == "fp32":
+            c = (s_val.astype(np.float32) * D32)[..., None]
+            v = ay / c
+        else:
+            raise ValueError(mode)
+    v = np.where(ok, v, np.float32(0.0))
+    idx = F.e2m1_index(v.astype(np.float64))
+    sign = (y.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
+    return (sign << np.uint8(3)) | idx, s_code
+
+
+def columnwise_operand(values, count, D, mode):
+    """One expert's columnwise operand from its grouped rows.
+
+    values [count, H]: exact values of the expert's rows (float64), in grouped
+    order; rows count..P-1 (P = roundup(count, 16)) are zero padding.
+    Returns (codes uint8 [H, P/2], scale codes uint8 [H, P/16]).
+    """
+    values = np.asarray(values, dtype=np.float64)
+    h = values.shape[1]
+    p = (count + 15) // 16 * 16
+    full = np.zeros((p, h), dtype=np.float64)
+    full[:count] = values[:count]
+    blocks = full.T.reshape(h, p // 16, 16)             # [H, P/16, 16] : column h, block m, row i
+    y = rht16(blocks)
+    codes, s_code = quantize_blocks(y, D, mode)
+    return F.pack_nibbles(codes.reshape(h, p)), s_code
+
+
+def expert_decode_scale(t_rows):
+    """R14: D_e = 4 * max t over the expert's rows (a power of two); 0 if the expert is empty."""
+    t_rows = np.asarray(t_rows, dtype=np.float64)
+    return 4.0 * float(t_rows.max()) if t_rows.size else 0.0
+
+
+# ------------------------------------------------------------------ the direct receive
+def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None, columnwise=True):
+    """R12-R16.  Returns the routing plan plus the grouped operands.
+
+    Rowwise (R13): grouped row g with source token s >= 0 holds the sender's
+    code bytes, scale bytes and t unchanged; padding rows are zero bytes
+    (t = 0).  Rows from off_E to r_cap are left zero here (unspecified).
+    Columnwise (R14-R16): per expert, D_e = 4 * max t; the operand is
+    ``columnwise_operand`` of the decoded grouped rows in mode "pow2".
+    Expert e's codes are an [H, P_e/2] byte matrix at byte H * off_e / 2 of
+    ``col_codes``; its scales an [H, P_e/16] matrix at byte H * off_e / 16.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    t_tok, k = np.asarray(topk_idx).shape
+    plan = route_plan(topk_idx, num_experts, alignment, r_cap)
+    r_cap = plan["src_row"].shape[0]
+    src = plan["src_row"].astype(np.int64)
+    off = plan["offsets"].astype(np.int64)
+    counts = plan["counts"].astype(np.int64)
+    h = hidden
+    codes, s_code, t = nvfp4.split_rows(packed, h)
+    ok = src >= 0
+    row_codes = np.zeros((r_cap, h // 2), dtype=np.uint8)
+    row_scales = np.zeros((r_cap, h // 16), dtype=np.uint8)
+    row_t = np.zeros(r_cap, dtype=np.float32)
+    row_codes[ok] = packed[src[ok], : h // 2]
+    row_scales[ok] = packed[src[ok], h // 2 : h // 2 + h // 16]
+    row_t[ok] = t[src[ok]].astype(np.float32)
+    out = dict(plan, row_codes=row_codes, row_scales=row_scales, row_t=row_t)
+    if not columnwise:
+        return out
+    D = np.zeros(num_experts, dtype=np.float32)
+    col_codes = np.zeros(r_cap * h // 2, dtype=np.uint8)
+    col_scales = np.zeros(r_cap * h // 16, dtype=np.uint8)
+    exact = nvfp4.decode_exact(packed, h)
+    for e in range(num_experts):
+        c = int(counts[e])
+        rows = src[off[e] : off[e] + c]
+        D[e] = expert_decode_scale(t[rows])
+        if c == 0:
+            continue
+        cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2")
+        p = int(off[e + 1] - off[e])
+        pc = (c + 15) // 16 * 16
+        # P_e may exceed roundup(count, 16) when alignment > 16: the extra
+        # 16-row blocks are all padding (codes 0, scales 0).
+        full_c = np.zeros((h, p // 2), dtype=np.uint8)
+        full_s = np.zeros((h, p // 16), dtype=np.uint8)
+        full_c[:, : pc // 2] = cc
+        full_s[:, : pc // 16] = cs
+        col_codes[h * off[e] // 2 : h * off[e + 1] // 2] = full_c.reshape(-1)
+        col_scales[h * off[e] // 16 : h * off[e + 1] // 16] = full_s.reshape(-1)
+    out.update(col_codes=col_codes, col_scales=col_scales, col_scale=D)
+    return out
+
+
+def columnwise_sample(packed, hidden, plan, expert, col_lo, col_hi, blk_lo, blk_hi, D):
+    """Columnwise codes/scales of one expert restricted to columns [col_lo, col_hi)
+    and 16-row blocks [blk_lo, blk_hi) -- for sampled checks at full size.
+
+    Returns (codes uint8 [cols, 16*(blk_hi-blk_lo)] unpacked 4-bit codes,
+    scale codes uint8 [cols, blk_hi-blk_lo])."""
+    src = plan["src_row"].astype(np.int64)
+    off = int(plan["offsets"][expert])
+    rows = src[off + 16 * blk_lo : off + 16 * blk_hi]
+    vals = np.zeros((rows.shape[0], col_hi - col_lo), dtype=np.float64)
+    ok = rows >= 0
+    if ok.any():
+        sub = np.asarray(packed)[rows[ok]]
+        ex = nvfp4.decode_exact(sub, hidden)
+        vals[ok] = ex[:, col_lo:col_hi]
+    blocks = vals.T.reshape(col_hi - col_lo, blk_hi - blk_lo, 16)
+    y = rht16(blocks)
+    codes, s_code = quantize_blocks(y, D, "pow2")
+    return codes.reshape(col_hi - col_lo, -1), s_code
