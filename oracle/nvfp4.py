@@ -39,22 +39,27 @@ def token_scale_exponent(amax):
 
 
 def _row_scales(ax32):
-    """Token exponents e [N], block scale codes [N, H/16] for |x| as float32 [N, H]."""
+    """Token exponents e [N] and block scale codes [N, H/16] for |x| as float32 [N, H].
+
+    R5: s_b = E4M3 round-to-nearest-even of the exact value a_b / (6 * t), with
+    a_b = max |x| over the 16-element block.  The float64 quotient is exact when
+    3 divides a_b's significand; otherwise the exact quotient is a periodic binary
+    fraction (period 2) that is never an E4M3 tie, so the float64 value rounds to
+    E4M3 exactly as the exact one does.
+    """
     n, h = ax32.shape
     amax = ax32.max(axis=1).astype(np.float64)
     e = token_scale_exponent(amax)
-    a_b = ax32.reshape(n, h // 16, 16).max(axis=2)                      # float32, exact
-    pre = a_b / np.float32(6.0)                                          # R5: fl32(a_b / 6)
-    pre = np.ldexp(pre, (-e)[:, None].astype(np.int32)).astype(np.float32)  # exact power-of-two scaling
-    s_code = F.e4m3_encode(pre.astype(np.float64))
-    return e, s_code
+    a_b = ax32.reshape(n, h // 16, 16).max(axis=2).astype(np.float64)
+    y = a_b / (6.0 * np.ldexp(1.0, e)[:, None])
+    return e, F.e4m3_encode(y)
 
 
 def pack_rows(x_bits, sr_seed=None, sr_counter_base=0, sr_mode="element"):
     """R4-R9: BF16 rows [N, H] (uint16 bit patterns) -> packed rows uint8 [N, 9H/16 + 4].
 
-    Block scale (R5): s_b = E4M3(fl32(a_b / 6) * 2^-e), a_b = max |x| over the
-    16-element block.
+    Block scale (R5): s_b = E4M3(a_b / (6 * t)), a_b = max |x| over the
+    16-element block, rounded once from the exact value.
 
     Codes, round-to-nearest (R6): s_b = 0 gives magnitude index 0.  Otherwise
     the index is the E2M1 rounding (R2) of the exact quotient |x| / (s_b * t).

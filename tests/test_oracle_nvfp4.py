@@ -42,11 +42,10 @@ def _check_block_bound(x_bits, packed, h):
     step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
     bound = np.where(v <= 6, st * step / 2, (v - 6) * st)
     assert np.all(err[pos] <= bound[pos] * (1 + 1e-12))
-    # blocks whose scale flushes to zero are exactly those with fl32(a_b/6)*2^-e <= 2^-10
-    a_b = np.abs(F.bf16_to_f32(x_bits)).reshape(x.shape[0], h // 16, 16).max(axis=2)
-    e = np.log2(t).astype(np.int64)
-    pre = np.ldexp(a_b / np.float32(6), (-e)[:, None].astype(np.int32)).astype(np.float64)
-    np.testing.assert_array_equal(s_code == 0, pre <= 2.0 ** -10)
+    # blocks whose scale flushes to zero are exactly those with a_b / (6 t) <= 2^-10
+    # (the tie at 2^-10 rounds to the even code 0); compared without division
+    a_b = np.abs(F.bf16_to_f32(x_bits)).reshape(x.shape[0], h // 16, 16).max(axis=2).astype(np.float64)
+    np.testing.assert_array_equal(s_code == 0, a_b <= 6.0 * t[:, None] * 2.0 ** -10)
     # flushed blocks decode to (signed) zero
     assert np.all(xh[~pos] == 0)
     # the largest block scale of each non-zero row lies in (224, 448]
@@ -211,3 +210,18 @@ def test_sr_word_positions():
     a = nvfp4.pack_rows(w.x_bits, sr_seed=5, sr_counter_base=base)
     b = nvfp4.pack_rows(w.x_bits[1:], sr_seed=5, sr_counter_base=base + 64)
     np.testing.assert_array_equal(a[1:], b)
+
+
+def test_block_scale_exact_rounding_exhaustive():
+    """R5: the E4M3 block scale of a_b / (6 * 2^e) for every positive finite BF16 a_b
+    and e in [-24, 24] equals torch's E4M3 cast of the float32-rounded quotient (the
+    quotient by 6 never lands on an E4M3 tie unless exact, so one rounding or two
+    agree) -- an independent library route to the same codes."""
+    import torch
+    a = _all_bf16_pos()
+    for e in range(-24, 25):
+        y = a / (6.0 * 2.0 ** e)
+        keep = y <= 448.0
+        ours = F.e4m3_encode(y[keep])
+        ref = torch.from_numpy(y[keep].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(ours, ref)
