@@ -62,16 +62,18 @@ def quantize_blocks(y, D, mode):
     return (sign << np.uint8(3)) | idx, s_code
 
 
-def columnwise_operand(values, count, D, mode):
+def columnwise_operand(values, count, D, mode, padded_rows=None):
     """One expert's columnwise operand from its grouped rows.
 
     values [count, H]: exact values of the expert's rows (float64), in grouped
-    order; rows count..P-1 (P = roundup(count, 16)) are zero padding.
+    order; rows count..P-1 are zero padding, P = padded_rows (default
+    roundup(count, 16)).  Padding rows are transformed and quantized like any
+    other rows (their codes carry the sign bits of the signed-zero results).
     Returns (codes uint8 [H, P/2], scale codes uint8 [H, P/16]).
     """
     values = np.asarray(values, dtype=np.float64)
     h = values.shape[1]
-    p = (count + 15) // 16 * 16
+    p = (count + 15) // 16 * 16 if padded_rows is None else int(padded_rows)
     full = np.zeros((p, h), dtype=np.float64)
     full[:count] = values[:count]
     blocks = full.T.reshape(h, p // 16, 16)             # [H, P/16, 16] : column h, block m, row i
@@ -127,17 +129,10 @@ def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None,
         D[e] = expert_decode_scale(t[rows])
         if c == 0:
             continue
-        cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2")
-        p = int(off[e + 1] - off[e])
-        pc = (c + 15) // 16 * 16
-        # P_e may exceed roundup(count, 16) when alignment > 16: the extra
-        # 16-row blocks are all padding (codes 0, scales 0).
-        full_c = np.zeros((h, p // 2), dtype=np.uint8)
-        full_s = np.zeros((h, p // 16), dtype=np.uint8)
-        full_c[:, : pc // 2] = cc
-        full_s[:, : pc // 16] = cs
-        col_codes[h * off[e] // 2 : h * off[e + 1] // 2] = full_c.reshape(-1)
-        col_scales[h * off[e] // 16 : h * off[e + 1] // 16] = full_s.reshape(-1)
+        p = int(off[e + 1] - off[e])                    # P_e: all padded rows of the slot
+        cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2", padded_rows=p)
+        col_codes[h * off[e] // 2 : h * off[e + 1] // 2] = cc.reshape(-1)
+        col_scales[h * off[e] // 16 : h * off[e + 1] // 16] = cs.reshape(-1)
     out.update(col_codes=col_codes, col_scales=col_scales, col_scale=D)
     return out
 
