@@ -1,0 +1,279 @@
+"""Python binding of the C ABI in ``include/moe_token_block.h``.
+
+Argument marshalling only: every step of the path runs in the gfx950 kernels
+of ``libmoe_token_block.so``.  PyTorch provides device memory and the stream;
+each call runs on the input tensor's device and that device's current stream
+(P1, commit messages: launch stream, allocations and the stochastic-rounding
+state follow the input tensor's device).  There is no CPU fallback: if the
+library is missing, every entry point raises.
+"""
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_token_block.so")
+
+EP_ROUND_NEAREST, EP_ROUND_SR_ELEMENT, EP_ROUND_SR_STREAM = 0, 1, 2
+EP_IDX_INT32, EP_IDX_INT64 = 0, 1
+EP_DEVERR_EXPERT_ID = 1
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "ep_abi_version": (_I32, []),
+    "ep_status_string": (ctypes.c_char_p, [_I32]),
+    "ep_nvfp4_packed_row_bytes": (_I64, [_I64]),
+    "ep_route_capacity": (_I64, [_I64, _I64, _I64, _I64]),
+    "ep_route_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "ep_rht_sign_mask": (ctypes.c_uint32, []),
+    "dswiglu_workspace_bytes": (_SZ, [_I64]),
+    "ep_nvfp4_pack": (_I32, [_P, _I64, _I64, _P, _I32, _P, _P]),
+    "ep_mxfp8_pack": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "ep_nvfp4_unpack": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "ep_route_plan": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "ep_nvfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded library (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m moe_token_block_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+class EpError(RuntimeError):
+    pass
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().ep_status_string(status).decode()
+        raise EpError(f"{what}: status {status} ({msg})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must live on a GPU (no CPU path)")
+    return t.device
+
+
+def _need(t, dtype, name, dev=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+# ------------------------------------------------------------------ helpers
+def ep_abi_version():
+    return lib().ep_abi_version()
+
+
+def ep_status_string(status):
+    return lib().ep_status_string(status).decode()
+
+
+def ep_nvfp4_packed_row_bytes(hidden):
+    return lib().ep_nvfp4_packed_row_bytes(hidden)
+
+
+def ep_route_capacity(tokens, top_k, num_experts, alignment):
+    r = lib().ep_route_capacity(tokens, top_k, num_experts, alignment)
+    _check(r if r < 0 else 0, "ep_route_capacity")
+    return r
+
+
+def ep_rht_sign_mask():
+    return lib().ep_rht_sign_mask()
+
+
+# ------------------------------------------------------------------ pack / unpack
+def ep_nvfp4_pack(x, round_mode=EP_ROUND_NEAREST, sr_state=None, out=None):
+    """BF16 rows [T, H] -> packed NVFP4 rows uint8 [T, 9H/16 + 4].
+
+    ``sr_state``: int64 device tensor [2] = {seed, counter_base} for the
+    stochastic modes (a pre-quantized or non-BF16 input is refused)."""
+    dev = _dev(x)
+    _need(x, torch.bfloat16, "x")
+    t, h = x.shape
+    rb = lib().ep_nvfp4_packed_row_bytes(h)
+    _check(rb if rb < 0 else 0, "ep_nvfp4_pack")
+    if out is None:
+        out = torch.empty((t, rb), dtype=torch.uint8, device=dev)
+    _need(out, torch.uint8, "out", dev)
+    if round_mode != EP_ROUND_NEAREST:
+        if sr_state is None:
+            raise ValueError("stochastic rounding needs sr_state")
+        _need(sr_state, torch.int64, "sr_state", dev)
+        if sr_state.numel() < 2:
+            raise ValueError("sr_state holds {seed, counter_base}: two int64 values")
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_pack(_ptr(x), t, h, _ptr(out), round_mode, _ptr(sr_state), _stream(dev)),
+               "ep_nvfp4_pack")
+    return out
+
+
+def ep_nvfp4_unpack(packed, hidden, src_row=None, out=None):
+    """Packed rows -> BF16 [rows_out, H]; with ``src_row`` (int32 [rows_out]) output
+    row g decodes packed row src_row[g] (-1: zeros)."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    rows_in = packed.shape[0]
+    rows_out = rows_in if src_row is None else src_row.shape[0]
+    if src_row is not None:
+        _need(src_row, torch.int32, "src_row", dev)
+    if out is None:
+        out = torch.empty((rows_out, hidden), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_unpack(_ptr(packed), rows_in, hidden, _ptr(src_row), rows_out, _ptr(out), _stream(dev)),
+               "ep_nvfp4_unpack")
+    return out
+
+
+def ep_mxfp8_pack(x, out=None):
+    """BF16 rows [T, H] -> (data uint8 [T, H], scales uint8 [T, H/32]) carved from one
+    data-then-scales buffer (returned as the third element)."""
+    dev = _dev(x)
+    _need(x, torch.bfloat16, "x")
+    t, h = x.shape
+    if out is None:
+        out = torch.empty(t * h + t * (h // 32), dtype=torch.uint8, device=dev)
+    data = out[: t * h].view(t, h)
+    scales = out[t * h : t * h + t * (h // 32)].view(t, h // 32)
+    with torch.cuda.device(dev):
+        _check(lib().ep_mxfp8_pack(_ptr(x), t, h, _ptr(data), _ptr(scales), _stream(dev)), "ep_mxfp8_pack")
+    return data, scales, out
+
+
+# ------------------------------------------------------------------ routing / receive
+def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None, workspace=None):
+    """Routing plan of topk_idx [T, k] (int32 or int64): dict of counts, offsets,
+    dst_row, src_row (device int32), d_error (device int32 [1]) and r_cap."""
+    dev = _dev(topk_idx)
+    if topk_idx.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_idx must be int32 or int64")
+    if not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous")
+    t, k = topk_idx.shape
+    cap = ep_route_capacity(t, k, num_experts, alignment)
+    r_cap = cap if r_cap is None else r_cap
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = torch.empty(num_experts, **i32)
+    offsets = torch.empty(num_experts + 1, **i32)
+    dst_row = torch.empty((t, k), **i32)
+    src_row = torch.empty(r_cap, **i32)
+    if d_error is None:
+        d_error = torch.zeros(1, **i32)
+    wsb = lib().ep_route_workspace_bytes(t, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_route_plan(_ptr(topk_idx), EP_IDX_INT64 if topk_idx.dtype == torch.int64 else EP_IDX_INT32,
+                                   t, k, num_experts, alignment, r_cap, _ptr(counts), _ptr(offsets), _ptr(dst_row),
+                                   _ptr(src_row), _ptr(workspace), workspace.numel(), _ptr(d_error), _stream(dev)),
+               "ep_route_plan")
+    return dict(counts=counts, offsets=offsets, dst_row=dst_row, src_row=src_row, d_error=d_error, r_cap=r_cap,
+                num_experts=num_experts)
+
+
+def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
+    """Grouped rowwise (+ RHT columnwise) NVFP4 operands from packed rows and a
+    routing plan (from ``ep_route_plan``)."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    t = packed.shape[0]
+    e = plan["num_experts"]
+    r_cap = plan["r_cap"]
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = dict(row_codes=torch.empty((r_cap, hidden // 2), **u8),
+                   row_scales=torch.empty((r_cap, hidden // 16), **u8),
+                   row_t=torch.empty(r_cap, dtype=torch.float32, device=dev))
+        if columnwise:
+            out.update(col_codes=torch.empty(r_cap * hidden // 2, **u8),
+                       col_scales=torch.empty(r_cap * hidden // 16, **u8),
+                       col_scale=torch.empty(e, dtype=torch.float32, device=dev))
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_direct_receive(
+            _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]), _ptr(plan["src_row"]),
+            _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
+            _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _ptr(out.get("col_scale")),
+            _stream(dev)), "ep_nvfp4_direct_receive")
+    return out
+
+
+def ep_mxfp8_direct_receive(data, scales, plan, out=None):
+    dev = _dev(data)
+    _need(data, torch.uint8, "data", dev)
+    t, h = data.shape
+    r_cap = plan["r_cap"]
+    if out is None:
+        out = (torch.empty((r_cap, h), dtype=torch.uint8, device=dev),
+               torch.empty((r_cap, h // 32), dtype=torch.uint8, device=dev))
+    with torch.cuda.device(dev):
+        _check(lib().ep_mxfp8_direct_receive(_ptr(data), _ptr(scales), t, h, r_cap, _ptr(plan["src_row"]),
+                                             _ptr(out[0]), _ptr(out[1]), _stream(dev)), "ep_mxfp8_direct_receive")
+    return out
+
+
+# ------------------------------------------------------------------ dSwiGLU
+def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None):
+    """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
+    ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors."""
+    dev = _dev(preact)
+    _need(preact, torch.bfloat16, "preact", dev)
+    _need(dy, torch.bfloat16, "dy", dev)
+    _need(counts, torch.int32, "counts", dev)
+    t, f = dy.shape
+    e = counts.shape[0]
+    cap = t + 15 * e
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(dx=torch.empty((t, 2 * f), dtype=torch.bfloat16, device=dev), amax=torch.empty(e, **f32),
+                   row_codes=torch.empty((t, f), **u8), row_scales=torch.empty((t, 2 * f // 16), **u8),
+                   row_scale=torch.empty(e, **f32), col_codes=torch.empty(2 * f * cap // 2, **u8),
+                   col_scales=torch.empty(2 * f * cap // 16, **u8), col_scale=torch.empty(e, **f32))
+    wsb = lib().dswiglu_workspace_bytes(e)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dswiglu_nvfp4_quant(
+            _ptr(preact), _ptr(dy), t, f, _ptr(counts), e, _ptr(out["dx"]), _ptr(out["amax"]),
+            _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]),
+            _ptr(workspace), workspace.numel(), _stream(dev)), "dswiglu_nvfp4_quant")
+    return out

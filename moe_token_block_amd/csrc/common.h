@@ -1,0 +1,194 @@
+// Device helpers shared by the gfx950 kernels of the token codec.
+//
+// Everything here is written for CDNA4 (gfx950, wave64).  The hardware
+// conversion instructions used below were characterised on gfx950:
+//   * v_cvt_scalef32_pk_fp4_f32 rounds to nearest-even onto the E2M1 grid,
+//     saturates at 6, keeps the sign of zero, and divides by 2^k where k is
+//     only the EXPONENT of its f32 scale operand (the significand is ignored);
+//   * v_cvt_scalef32_pk_f32_fp4 multiplies by that same 2^k;
+//   * v_cvt_pk_fp8_f32 is OCP E4M3FN round-to-nearest-even below 464;
+//   * v_cvt_scalef32_pk_fp8_bf16 is E4M3 RNE of x / 2^k (exponent only).
+// So any division by a block scale with a non-power-of-two significand is
+// done in software (see quot_split below) and only the power of two is handed
+// to the conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtb {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: do not keep it in the caches).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+constexpr int kWave = 64;
+constexpr float kTokenBound = 2688.0f;  // 6 * 448
+
+// ----------------------------------------------------------------- bit casts
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Power of two 2^k as a float, k in [-126, 127] (normal range only).
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// Exponent of a float that is a power of two (normal or subnormal).
+__device__ __forceinline__ int pow2_exponent(float p) {
+  uint32_t b = __float_as_uint(p);
+  uint32_t ef = (b >> 23) & 0xFFu;
+  if (ef) return (int)ef - 127;
+  return -149 + (31 - __builtin_clz(b & 0x7FFFFFu));  // subnormal: position of the single set bit
+}
+
+// ----------------------------------------------------------------- E4M3
+// E4M3FN code of y in [0, 448] (RNE; the caller guarantees the range).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
+}
+// Value of an E4M3FN code held in the low byte of w.
+__device__ __forceinline__ float e4m3_decode(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, 0); }
+
+// ----------------------------------------------------------------- exact quotients
+// A divisor s with a short significand (E4M3 scales: 4 bits) split as
+// s = m * 2^k with m in [1, 2).  r_hi + r_lo approximates 1/m to about 2^-46:
+// r_hi is rcp(m) moved down by one ulp if needed so that r_hi <= 1/m, and the
+// residual 1 - m*r_hi (exact for a 4-bit m, and >= 0) gives r_lo >= 0.  Then
+// fma(x, r_hi, x*r_lo) is the correctly rounded fl32(x / m) for any x whose
+// exact quotient is at least 2^-28 (relative) away from a float32 rounding
+// midpoint -- true for every x of at most 24 bits divided by a 4-bit m -- and
+// it keeps the sign of x also for x = -0 (both terms carry x's sign).
+struct QuotSplit {
+  float r_hi, r_lo;
+  int k;  // exponent of the divisor
+};
+
+// r ~ 1/m (positive) lowered to r <= 1/m; returns the non-negative residual in e.
+__device__ __forceinline__ float rcp_below(float m, float& e) {
+  float r = __builtin_amdgcn_rcpf(m);
+  e = __builtin_fmaf(-m, r, 1.0f);
+  if (e < 0.0f) {
+    r = __uint_as_float(__float_as_uint(r) - 1u);
+    e = __builtin_fmaf(-m, r, 1.0f);
+  }
+  return r;
+}
+
+__device__ __forceinline__ QuotSplit quot_split(float s) {
+  QuotSplit q;
+  q.k = __builtin_amdgcn_frexp_expf(s) - 1;   // s = m * 2^k, m in [1, 2)
+  float m = __builtin_amdgcn_frexp_mantf(s) * 2.0f;
+  float e;
+  q.r_hi = rcp_below(m, e);
+  q.r_lo = e * q.r_hi;
+  return q;
+}
+
+__device__ __forceinline__ float quot_apply(float x, float r_hi, float r_lo) {
+  return __builtin_fmaf(x, r_hi, x * r_lo);
+}
+
+// fl32(a / 6) for a >= 0 in float32's normal range: a / 1.5 with the split
+// reciprocal of 1.5 (2/3 = R_HI + R_LO to ~2^-48), then an exact * 0.25.
+__device__ __forceinline__ float div6(float a) {
+  const float R_HI = 0.666666686534881591796875f;        // RN(2/3)
+  const float R_LO = -1.98682149251302083333e-08f;       // RN(2/3 - R_HI)
+  return __builtin_fmaf(a, R_HI, a * R_LO) * 0.25f;
+}
+
+// ----------------------------------------------------------------- E2M1
+// Four E2M1 codes of u0..u3 / 2^k packed as the two bytes of a 16-bit result
+// written into byte pair `sel`; `scale` is 2^k as a float (exponent only).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+// E2M1 value (times 2^k) of the two nibbles of byte SEL of w.
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4_unpack2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+// ----------------------------------------------------------------- RHT
+// The 16-bit sign mask of the 16-point RHT: d_i = -1 iff bit i is set.  It is
+// the low half of word 0 of Philox4x32-10 at key (0,0), counter (0,0,0,0).
+constexpr uint32_t kRhtSignMask = 0xE8D5u;
+
+__host__ __device__ constexpr float rht_in_scale(int i) {
+  return ((kRhtSignMask >> i) & 1u) ? -0.25f : 0.25f;
+}
+
+// In-place butterfly on z[0..15]: strides 1, 2, 4, 8; pair (i, i+h) with
+// (i & h) == 0 becomes (z_i + z_{i+h}, z_i - z_{i+h}).  The inputs already
+// carry the d_i / 4 factor.  No contraction can apply: adds only.
+__device__ __forceinline__ void rht16_butterfly(float* z) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      float a = z[i], b = z[i + h];
+      z[i] = a + b;
+      z[i + h] = a - b;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror, Shaw (SC'11): ten rounds of two 32x32->64 products,
+// Weyl key schedule between rounds.
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// ----------------------------------------------------------------- reductions
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t other = (uint32_t)__shfl_xor((int)v, o, kWave);
+    v = v > other ? v : other;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// max of |bf16| over the two halves of 4 packed words, as a 16-bit magnitude pattern.
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 v) {
+  u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+  u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
+  u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
+  u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+  u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  uint32_t lo = m[0], hi = m[1];
+  return lo > hi ? lo : hi;
+}
+
+}  // namespace mtb

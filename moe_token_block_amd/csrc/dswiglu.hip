@@ -1,0 +1,337 @@
+// Grouped dSwiGLU epilogue with per-expert amax, then FC1-gradient NVFP4
+// quantization that uses that amax instead of an amax pass (P4, description:
+// the rowwise amax is the epilogue's exact amax rounded to BF16, the
+// post-RHT columnwise amax is bounded by 4x the rowwise amax, the separate
+// grouped amax pass is skipped).
+//
+// Launch 1 (setup): expert row offsets (plain and 16-padded) from the device
+//   counts into the workspace; amax zeroed (a fill, not a memset).
+// Launch 2 (epilogue): one wave per token row; per pair (a_j, b_j, dy_j):
+//   s = sigmoid(a), da = dy*b*s*(1 + a*(1-s)), db = dy*a*s in FP32 -> BF16;
+//   the row's max |dX| (over the BF16 values) goes to amax[e] with an
+//   integer atomic max on the bit pattern (order-independent, deterministic).
+// Launch 3 (quant): one workgroup per 256 padded rows x 128 columns, as the
+//   direct receive: thread (cg, m) owns 8 columns x one 16-row block; the
+//   rowwise operand (per-expert scale D_row = amax/2688) and the RHT
+//   columnwise operand (D_col = 4*D_row) come out of the same load of dX.
+#include "common.h"
+#include "launch.h"
+
+namespace mtb {
+
+constexpr int kQTileRows = 256;
+constexpr int kQTileCols = 128;
+constexpr int kQBlocks = kQTileRows / 16;
+
+__global__ __launch_bounds__(1024) void k_dswiglu_setup(const int32_t* __restrict__ counts, int E, int T,
+                                                        int32_t* __restrict__ offs, int32_t* __restrict__ poffs,
+                                                        float* __restrict__ amax) {
+  // Counts are device data: they are clamped so that the experts never cover
+  // more than the T rows that exist (a running total above T is cut at T).
+  __shared__ int32_t a[1024], b[1024];
+  const int tid = threadIdx.x;
+  int c = tid < E ? max(counts[tid], 0) : 0;
+  a[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int va = tid >= o ? a[tid - o] : 0;
+    __syncthreads();
+    a[tid] += va;
+    __syncthreads();
+  }
+  const int incl = min(a[tid], T), excl = min(a[tid] - c, T);
+  b[tid] = (incl - excl + 15) / 16 * 16;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int vb = tid >= o ? b[tid - o] : 0;
+    __syncthreads();
+    b[tid] += vb;
+    __syncthreads();
+  }
+  if (tid < E) {
+    offs[tid + 1] = incl;
+    poffs[tid + 1] = b[tid];
+    amax[tid] = 0.0f;
+  }
+  if (tid == 0) {
+    offs[0] = 0;
+    poffs[0] = 0;
+  }
+}
+
+__device__ __forceinline__ int expert_of(const int32_t* offs, int E, int r) {
+  int lo = 0, hi = E - 1;  // last e with offs[e] <= r
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void dswiglu_pair(float a, float b, float dy, float& da, float& db) {
+  float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+  float silu = a * sg;
+  da = dy * b * sg * (1.0f + a * (1.0f - sg));
+  db = dy * silu;
+}
+
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __restrict__ preact,
+                                                          const uint16_t* __restrict__ dy, int T, int F, int E,
+                                                          const int32_t* __restrict__ offs,
+                                                          uint16_t* __restrict__ dx, float* __restrict__ amax) {
+  const int lane = threadIdx.x & 63;
+  const int r = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (r >= T) return;
+  const uint4* pa = reinterpret_cast<const uint4*>(preact + (size_t)r * 2 * F);
+  const uint4* pb = reinterpret_cast<const uint4*>(preact + (size_t)r * 2 * F + F);
+  const uint4* pd = reinterpret_cast<const uint4*>(dy + (size_t)r * F);
+  uint4* oa = reinterpret_cast<uint4*>(dx + (size_t)r * 2 * F);
+  uint4* ob = reinterpret_cast<uint4*>(dx + (size_t)r * 2 * F + F);
+  uint32_t m = 0;
+  for (int j = lane; j < (F >> 3); j += 64) {
+    uint4 va = ld_stream16(pa + j), vb = ld_stream16(pb + j), vd = ld_stream16(pd + j);
+    uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w}, wd[4] = {vd.x, vd.y, vd.z, vd.w};
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float da0, db0, da1, db1;
+      dswiglu_pair(bf16lo(wa[i]), bf16lo(wb[i]), bf16lo(wd[i]), da0, db0);
+      dswiglu_pair(bf16hi(wa[i]), bf16hi(wb[i]), bf16hi(wd[i]), da1, db1);
+      ra[i] = bf16pair(da0, da1);
+      rb[i] = bf16pair(db0, db1);
+    }
+    uint4 oA = make_uint4(ra[0], ra[1], ra[2], ra[3]), oB = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+    oa[j] = oA;
+    ob[j] = oB;
+    uint32_t x = absmax_bf16x8(oA), y = absmax_bf16x8(oB);
+    x = x > y ? x : y;
+    m = m > x ? m : x;
+  }
+  m = wave_max_u32(m);
+  // non-negative floats order like their bit patterns: an integer max is exact
+  if (lane == 0 && m && r < offs[E])
+    atomicMax(reinterpret_cast<unsigned int*>(amax) + expert_of(offs, E, r), m << 16);
+}
+
+// ------------------------------------------------------------------ grouped quant
+// fl32(x / c) for a general float c: split reciprocal (r_hi <= 1/c, the
+// non-negative residual by fma); the result can differ from the correctly
+// rounded quotient only when x/c lies within ~2^-45 (relative) of a float32
+// midpoint.  r_lo >= 0 keeps the sign of x = -0.
+struct GenQuot {
+  float r_hi, r_lo;
+};
+__device__ __forceinline__ GenQuot gen_split(float c) {
+  float e;
+  float r = rcp_below(c, e);
+  return GenQuot{r, e * r};
+}
+
+// Scale code for a block max a with decode scale D (D > 0): E4M3(fl32(fl32(a/6)/D)).
+__device__ __forceinline__ uint32_t gen_scale_code(float a, float D) {
+  float pre = a / 6.0f;          // correctly rounded (IEEE division)
+  float y = pre / D;             // correctly rounded
+  return e4m3_encode(fminf(y, 448.0f));
+}
+
+// Codes of n values x[] with block scale code sc and decode scale D:
+// c = fl32(s*D), v = fl32(|x|/c), E2M1 RNE (the converter at scale 1).
+struct GenBlock {
+  float r_hi, r_lo;
+  bool zero, exact_div;
+  float c;
+};
+__device__ __forceinline__ GenBlock gen_block(uint32_t sc, float D) {
+  GenBlock g;
+  float s = e4m3_decode(sc);
+  g.c = s * D;
+  g.zero = !(g.c > 0.0f);
+  // far from the float32 range ends the split reciprocal is accurate; near
+  // them fall back to the IEEE division
+  g.exact_div = g.c < 0x1p-100f || g.c > 0x1p100f;
+  GenQuot q = gen_split(g.zero ? 1.0f : g.c);
+  g.r_hi = g.zero ? 0.0f : q.r_hi;
+  g.r_lo = g.zero ? 0.0f : q.r_lo;
+  return g;
+}
+__device__ __forceinline__ float gen_apply(float x, const GenBlock& g) {
+  if (g.exact_div && !g.zero) return x / g.c;
+  return quot_apply(x, g.r_hi, g.r_lo);
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t enc_pair(uint32_t old, float a, float b, const GenBlock& g) {
+  return fp4_pack2<SEL>(old, gen_apply(a, g), gen_apply(b, g), 1.0f);
+}
+
+__global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, int T, int W /* 2F */, int E,
+                                                   const int32_t* __restrict__ offs, const int32_t* __restrict__ poffs,
+                                                   const float* __restrict__ amax,
+                                                   uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+                                                   float* __restrict__ row_scale, uint8_t* __restrict__ col_codes,
+                                                   uint8_t* __restrict__ col_scales, float* __restrict__ col_scale) {
+  __shared__ uint2 stage_codes[kQTileCols * kQBlocks];
+  __shared__ uint8_t stage_sc[kQTileCols * kQBlocks];
+  __shared__ int s_e[kQBlocks], s_poff[kQBlocks], s_plen[kQBlocks], s_row0[kQBlocks], s_cnt[kQBlocks];
+  __shared__ float s_drow[kQBlocks], s_dcol[kQBlocks];
+
+  const int tid = threadIdx.x;
+  const int ct = blockIdx.x;
+  const int gp_base = blockIdx.y * kQTileRows;  // first padded row of the tile
+  const int col0 = ct * kQTileCols;
+  const int ncols = min(kQTileCols, W - col0);
+  const int ptotal = poffs[E];
+
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int e = tid; e < E; e += 256) {
+      float D = amax[e] / kTokenBound;
+      row_scale[e] = D;
+      col_scale[e] = 4.0f * D;
+    }
+  }
+  if (tid < kQBlocks) {
+    int gp = gp_base + 16 * tid;
+    int e = -1;
+    if (gp < ptotal) {
+      e = expert_of(poffs, E, gp);
+      s_poff[tid] = poffs[e];
+      s_plen[tid] = poffs[e + 1] - poffs[e];
+      s_row0[tid] = offs[e] + (gp - poffs[e]);           // real row of the block's first row
+      s_cnt[tid] = offs[e + 1] - (offs[e] + (gp - poffs[e]));  // real rows left in the expert from there
+      float D = amax[e] / kTokenBound;
+      s_drow[tid] = D;
+      s_dcol[tid] = 4.0f * D;
+    }
+    s_e[tid] = e;
+  }
+  __syncthreads();
+
+  const int cg = tid & 15, m = tid >> 4;
+  if (s_e[m] >= 0 && cg * 8 < ncols) {
+    const int row0 = s_row0[m];
+    const int nreal = min(16, max(0, s_cnt[m]));
+    const float Drow = s_drow[m], Dcol = s_dcol[m];
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = i < nreal ? ld_stream16(dx + (size_t)(row0 + i) * W + col0 + 8 * cg) : make_uint4(0, 0, 0, 0);
+    // ---- rowwise: the 16-column block is split over lanes cg, cg^1
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t am = absmax_bf16x8(v[i]);
+      uint32_t o = (uint32_t)__shfl_xor((int)am, 1, kWave);
+      am = am > o ? am : o;
+      if (i >= nreal) continue;
+      uint32_t sc = Drow > 0.0f ? gen_scale_code(__uint_as_float(am << 16), Drow) : 0u;
+      GenBlock gb = gen_block(sc, Drow);
+      uint32_t w = 0;
+      w = enc_pair<0>(w, bf16lo(v[i].x), bf16hi(v[i].x), gb);
+      w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
+      w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
+      w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
+      const size_t r = (size_t)(row0 + i);
+      *reinterpret_cast<uint32_t*>(row_codes + r * (W >> 1) + ((col0 + 8 * cg) >> 1)) = w;
+      if ((cg & 1) == 0) row_scales[r * (W >> 4) + ((col0 + 8 * cg) >> 4)] = (uint8_t)sc;
+    }
+    // ---- columnwise: RHT down each of the 8 columns, D_col = 4 * D_row
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float z0[16], z1[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t wv = p == 0 ? v[i].x : (p == 1 ? v[i].y : (p == 2 ? v[i].z : v[i].w));
+        z0[i] = bf16lo(wv) * rht_in_scale(i);
+        z1[i] = bf16hi(wv) * rht_in_scale(i);
+      }
+      rht16_butterfly(z0);
+      rht16_butterfly(z1);
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a0 = fmaxf(a0, fabsf(z0[i]));
+        a1 = fmaxf(a1, fabsf(z1[i]));
+      }
+      uint32_t sc0 = Dcol > 0.0f ? gen_scale_code(a0, Dcol) : 0u;
+      uint32_t sc1 = Dcol > 0.0f ? gen_scale_code(a1, Dcol) : 0u;
+      GenBlock g0 = gen_block(sc0, Dcol), g1 = gen_block(sc1, Dcol);
+      uint32_t c00 = 0, c01 = 0, c10 = 0, c11 = 0;
+      c00 = enc_pair<0>(c00, z0[0], z0[1], g0);
+      c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
+      c00 = enc_pair<2>(c00, z0[4], z0[5], g0);
+      c00 = enc_pair<3>(c00, z0[6], z0[7], g0);
+      c01 = enc_pair<0>(c01, z0[8], z0[9], g0);
+      c01 = enc_pair<1>(c01, z0[10], z0[11], g0);
+      c01 = enc_pair<2>(c01, z0[12], z0[13], g0);
+      c01 = enc_pair<3>(c01, z0[14], z0[15], g0);
+      c10 = enc_pair<0>(c10, z1[0], z1[1], g1);
+      c10 = enc_pair<1>(c10, z1[2], z1[3], g1);
+      c10 = enc_pair<2>(c10, z1[4], z1[5], g1);
+      c10 = enc_pair<3>(c10, z1[6], z1[7], g1);
+      c11 = enc_pair<0>(c11, z1[8], z1[9], g1);
+      c11 = enc_pair<1>(c11, z1[10], z1[11], g1);
+      c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
+      c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
+      const int c0 = cg * 8 + 2 * p;
+      stage_codes[c0 * kQBlocks + m] = make_uint2(c00, c01);
+      stage_codes[(c0 + 1) * kQBlocks + m] = make_uint2(c10, c11);
+      stage_sc[c0 * kQBlocks + m] = (uint8_t)sc0;
+      stage_sc[(c0 + 1) * kQBlocks + m] = (uint8_t)sc1;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < (kQTileCols * kQBlocks) / 256; ++rr) {
+    int it = rr * 256 + tid;
+    int c = it >> 4, b = it & 15;
+    if (s_e[b] < 0 || c >= ncols) continue;
+    int poff = s_poff[b], plen = s_plen[b];
+    int gp = gp_base + 16 * b;
+    size_t h = (size_t)(col0 + c);
+    uint2* dst = reinterpret_cast<uint2*>(col_codes + (size_t)W * (poff >> 1) + h * (size_t)(plen >> 1) + ((gp - poff) >> 1));
+    *dst = stage_codes[c * kQBlocks + b];
+    col_scales[(size_t)W * (poff >> 4) + h * (size_t)(plen >> 4) + ((gp - poff) >> 4)] = stage_sc[c * kQBlocks + b];
+  }
+}
+
+}  // namespace mtb
+
+using namespace mtb;
+
+MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t num_experts) {
+  if (num_experts < 1) return 0;
+  return (size_t)(2 * (num_experts + 1) * sizeof(int32_t));
+}
+
+MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                                       const int32_t* counts, int64_t num_experts, uint16_t* dx, float* amax,
+                                       uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                       uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (tokens < 0 || ffn <= 0 || ffn % 64 != 0 || num_experts < 1 || num_experts > 1024) return EP_ERR_SHAPE;
+  if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
+  if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
+  if (tokens > 0 && (!preact || !dy || !dx || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
+  if (!workspace || workspace_bytes < dswiglu_workspace_bytes(num_experts)) return EP_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = (int)tokens, F = (int)ffn, E = (int)num_experts;
+  int32_t* offs = (int32_t*)workspace;
+  int32_t* poffs = offs + (E + 1);
+  hipLaunchKernelGGL(k_dswiglu_setup, dim3(1), dim3(1024), 0, s, counts, E, T, offs, poffs, amax);
+  if (T > 0) {
+    hipLaunchKernelGGL(k_dswiglu_epilogue, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, E, offs, dx,
+                       amax);
+  }
+  // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
+  const int64_t prow_bound = tokens + 15 * num_experts;
+  dim3 grid((unsigned)((2 * F + kQTileCols - 1) / kQTileCols), (unsigned)((prow_bound + kQTileRows - 1) / kQTileRows));
+  hipLaunchKernelGGL(k_fc1_quant, grid, dim3(256), 0, s, dx, T, 2 * F, E, offs, poffs, amax, row_codes, row_scales,
+                     row_scale, col_codes, col_scales, col_scale);
+  return launch_status();
+}

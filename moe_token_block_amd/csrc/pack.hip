@@ -1,0 +1,339 @@
+// NVFP4 row pack (round-to-nearest and stochastic) and MXFP8 pack for gfx950.
+//
+// NVFP4 (P1, PR description): one BF16 token row -> E2M1 codes, one E4M3
+// scale per 16 elements and a power-of-two FP32 token scale t.  MXFP8 (P2,
+// description): E4M3 data with one E8M0 scale per 32 elements.
+//
+// Mapping: one wave64 per row; lane l owns 16-element blocks l, l+64, ...,
+// loaded as two 16-byte vectors, so a block's max needs no cross-lane work and
+// one wave-wide reduction gives the row max.  The whole row stays in VGPRs
+// between the max and the encode (hidden <= 16384: at most 16 blocks/lane).
+#include "common.h"
+#include "launch.h"
+
+namespace mtb {
+
+struct BlockQuant {
+  float r_hi, r_lo;  // split reciprocal of the scale significand, times 2^P
+  float scale;       // 2^(k + e + P): handed to the converter (exponent only)
+  int kexp;          // k + e + P
+};
+
+// Block scale code and the quotient parameters for one 16-element block of a
+// row with token exponent e.  ab = block max |x|.
+__device__ __forceinline__ BlockQuant nvfp4_block(float ab, int e, uint32_t& sc_out) {
+  // s_b = E4M3(ab / (6 * 2^e)): fl32(ab/6) never sits on an E4M3 tie unless it
+  // is exact, so one float32 rounding before the E4M3 rounding changes nothing.
+  bool tiny = ab < 0x1p-100f;
+  float abs_ = tiny ? ab * 0x1p64f : ab;
+  float y = __builtin_ldexpf(div6(abs_), -e - (tiny ? 64 : 0));
+  uint32_t sc = e4m3_encode(fminf(y, 448.0f));
+  float s = e4m3_decode(sc);
+  sc_out = sc;
+  BlockQuant q;
+  if (s > 0.0f) {
+    QuotSplit qs = quot_split(s);
+    int K = qs.k + e;
+    int P = K < -104 ? -104 - K : 0;  // keep x * r_lo and the converter's scale in normal range
+    q.r_hi = __builtin_ldexpf(qs.r_hi, P);
+    q.r_lo = __builtin_ldexpf(qs.r_lo, P);
+    q.kexp = K + P;
+  } else {
+    q.r_hi = 0.0f;  // every element becomes a signed zero
+    q.r_lo = 0.0f;
+    q.kexp = 0;
+  }
+  q.scale = pow2f(q.kexp);
+  return q;
+}
+
+__device__ __forceinline__ int token_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int E, sub = 0;
+  if (amax < 0x1p-126f) { amax *= 0x1p64f; sub = 64; }  // BF16 subnormal: normalise first
+  E = __builtin_amdgcn_frexp_expf(amax) - 1 - sub;
+  float m = __builtin_amdgcn_frexp_mantf(amax) * 2.0f;
+  return E - 11 + (m > 1.3125f ? 1 : 0);  // least e with amax <= 2688 * 2^e
+}
+
+// Stochastic rounding of one element: u = x / (m 2^-P) (signed), magnitude
+// v = |u| * 2^-kexp = fl32(|x| / (s t)); r = 24 random bits.  Returns the
+// rounded grid value with x's sign (then encoded exactly by the converter).
+__device__ __forceinline__ float sr_round(float u, int kexp, uint32_t r) {
+  float v = __builtin_ldexpf(fabsf(u), -kexp);
+  float rf = (float)r * 0x1p-24f;
+  float res;
+  if (v >= 6.0f) {
+    res = 6.0f;
+  } else {
+    float sinv = v < 2.0f ? 2.0f : (v < 4.0f ? 1.0f : 0.5f);
+    float w = v * sinv;
+    float fl = __builtin_floorf(w);
+    float frac = w - fl;
+    res = (fl + (rf < frac ? 1.0f : 0.0f)) * (1.0f / sinv);
+  }
+  return __builtin_copysignf(res, u);
+}
+
+template <int NB>
+__device__ __forceinline__ void store_block(uint8_t* orow, int H, int j, uint32_t o0, uint32_t o1, uint32_t sc) {
+  uint32_t* cw = reinterpret_cast<uint32_t*>(orow + 8 * j);
+  cw[0] = o0;
+  cw[1] = o1;
+  orow[(H >> 1) + j] = (uint8_t)sc;
+}
+
+__device__ __forceinline__ void encode_rne(const uint4& v0, const uint4& v1, const BlockQuant& q,
+                                           uint32_t& o0, uint32_t& o1) {
+  uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float u[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u[2 * i] = quot_apply(bf16lo(w[i]), q.r_hi, q.r_lo);
+    u[2 * i + 1] = quot_apply(bf16hi(w[i]), q.r_hi, q.r_lo);
+  }
+  o0 = fp4_pack2<0>(0u, u[0], u[1], q.scale);
+  o0 = fp4_pack2<1>(o0, u[2], u[3], q.scale);
+  o0 = fp4_pack2<2>(o0, u[4], u[5], q.scale);
+  o0 = fp4_pack2<3>(o0, u[6], u[7], q.scale);
+  o1 = fp4_pack2<0>(0u, u[8], u[9], q.scale);
+  o1 = fp4_pack2<1>(o1, u[10], u[11], q.scale);
+  o1 = fp4_pack2<2>(o1, u[12], u[13], q.scale);
+  o1 = fp4_pack2<3>(o1, u[14], u[15], q.scale);
+}
+
+// Stochastic encode of one 16-element block at stream positions n0 .. n0+15.
+template <int MODE>
+__device__ __forceinline__ void encode_sr(const uint4& v0, const uint4& v1, const BlockQuant& q, uint64_t n0,
+                                          uint32_t seed_lo, uint32_t seed_hi, uint32_t& o0, uint32_t& o1) {
+  uint32_t rnd[16];
+  if (MODE == EP_ROUND_SR_ELEMENT) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint64_t n = n0 + i;
+      rnd[i] = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), 0u, 0u, seed_lo, seed_hi).x >> 8;
+    }
+  } else {
+    // word n of the stream is word (n & 3) of block n >> 2
+    uint64_t cur = n0 >> 2;
+    U4 blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, seed_lo, seed_hi);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint64_t n = n0 + i;
+      if ((n >> 2) != cur) {
+        cur = n >> 2;
+        blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, seed_lo, seed_hi);
+      }
+      uint32_t sel = (uint32_t)n & 3u;
+      uint32_t wd = sel == 0 ? blk.x : (sel == 1 ? blk.y : (sel == 2 ? blk.z : blk.w));
+      rnd[i] = wd >> 8;
+    }
+  }
+  uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float g[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    g[2 * i] = sr_round(quot_apply(bf16lo(w[i]), q.r_hi, q.r_lo), q.kexp, rnd[2 * i]);
+    g[2 * i + 1] = sr_round(quot_apply(bf16hi(w[i]), q.r_hi, q.r_lo), q.kexp, rnd[2 * i + 1]);
+  }
+  // g holds exact grid values with x's sign: encode with scale 1
+  o0 = fp4_pack2<0>(0u, g[0], g[1], 1.0f);
+  o0 = fp4_pack2<1>(o0, g[2], g[3], 1.0f);
+  o0 = fp4_pack2<2>(o0, g[4], g[5], 1.0f);
+  o0 = fp4_pack2<3>(o0, g[6], g[7], 1.0f);
+  o1 = fp4_pack2<0>(0u, g[8], g[9], 1.0f);
+  o1 = fp4_pack2<1>(o1, g[10], g[11], 1.0f);
+  o1 = fp4_pack2<2>(o1, g[12], g[13], 1.0f);
+  o1 = fp4_pack2<3>(o1, g[14], g[15], 1.0f);
+}
+
+// Round-to-nearest: the row stays in VGPRs between the max and the encode.
+template <int NB>
+__global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__ x, int rows, int H,
+                                                   uint8_t* __restrict__ out, int row_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int row = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (row >= rows) return;
+  const int nblk = H >> 4;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * H);
+
+  uint4 v[NB][2];
+  uint32_t bmax[NB];
+  uint32_t rmax = 0;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    int j = c * 64 + lane;
+    if (j < nblk) {
+      v[c][0] = ld_stream16(xr + 2 * j);
+      v[c][1] = ld_stream16(xr + 2 * j + 1);
+      uint32_t a = absmax_bf16x8(v[c][0]), b = absmax_bf16x8(v[c][1]);
+      bmax[c] = a > b ? a : b;
+    } else {
+      v[c][0] = v[c][1] = make_uint4(0, 0, 0, 0);
+      bmax[c] = 0;
+    }
+    rmax = rmax > bmax[c] ? rmax : bmax[c];
+  }
+  rmax = wave_max_u32(rmax);
+  const int e = token_exponent(__uint_as_float(rmax << 16));
+  uint8_t* orow = out + (size_t)row * row_bytes;
+  if (lane == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    int j = c * 64 + lane;
+    if (j >= nblk) continue;
+    uint32_t sc, o0, o1;
+    BlockQuant q = nvfp4_block(__uint_as_float(bmax[c] << 16), e, sc);
+    encode_rne(v[c][0], v[c][1], q, o0, o1);
+    store_block<NB>(orow, H, j, o0, o1, sc);
+  }
+}
+
+// Stochastic rounding: ALU-bound on the Philox blocks, so the second pass
+// re-reads each block (from cache) instead of holding the row in VGPRs.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restrict__ x, int rows, int H,
+                                                      uint8_t* __restrict__ out, int row_bytes,
+                                                      const uint64_t* __restrict__ sr_state) {
+  const int lane = threadIdx.x & 63;
+  const int row = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (row >= rows) return;
+  const int nblk = H >> 4;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * H);
+  uint32_t rmax = 0;
+  for (int j = lane; j < nblk; j += 64) {
+    uint32_t a = absmax_bf16x8(xr[2 * j]), b = absmax_bf16x8(xr[2 * j + 1]);
+    a = a > b ? a : b;
+    rmax = rmax > a ? rmax : a;
+  }
+  rmax = wave_max_u32(rmax);
+  const int e = token_exponent(__uint_as_float(rmax << 16));
+  uint8_t* orow = out + (size_t)row * row_bytes;
+  if (lane == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+  const uint64_t seed = sr_state[0];
+  const uint32_t seed_lo = (uint32_t)seed, seed_hi = (uint32_t)(seed >> 32);
+  const uint64_t n_row = sr_state[1] + (uint64_t)row * (uint64_t)H;
+#pragma unroll 1
+  for (int j = lane; j < nblk; j += 64) {
+    uint4 v0 = xr[2 * j], v1 = xr[2 * j + 1];
+    uint32_t a = absmax_bf16x8(v0), b = absmax_bf16x8(v1);
+    uint32_t sc, o0, o1;
+    BlockQuant q = nvfp4_block(__uint_as_float((a > b ? a : b) << 16), e, sc);
+    encode_sr<MODE>(v0, v1, q, n_row + (uint64_t)(16 * j), seed_lo, seed_hi, o0, o1);
+    store_block<1>(orow, H, j, o0, o1, sc);
+  }
+}
+
+// ----------------------------------------------------------------- MXFP8
+// Two lanes per 32-element block (16 elements each): one xor-1 exchange gives
+// the block max.  Data goes out as one 16-byte store per lane.
+__device__ __forceinline__ int mx_exponent(float a) {
+  if (!(a > 0.0f)) return 0;
+  int sub = 0;
+  if (a < 0x1p-126f) { a *= 0x1p64f; sub = 64; }
+  int E = __builtin_amdgcn_frexp_expf(a) - 1 - sub;
+  float m = __builtin_amdgcn_frexp_mantf(a) * 2.0f;
+  int e = E - 8 + (m > 1.75f ? 1 : 0);  // least e with a <= 448 * 2^e
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+__device__ __forceinline__ uint32_t fp8x4_from_bf16(uint32_t w0, uint32_t w1, float scale) {
+  i16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w0), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w1), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Tiny blocks (e < -126): scale the inputs by 2^64 first so that the
+// converter's power of two stays a normal float.
+__device__ __forceinline__ uint32_t fp8x4_from_bf16_tiny(uint32_t w0, uint32_t w1, float scale) {
+  i16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, bf16lo(w0) * 0x1p64f, bf16hi(w0) * 0x1p64f, scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, bf16lo(w1) * 0x1p64f, bf16hi(w1) * 0x1p64f, scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__global__ __launch_bounds__(256) void k_mxfp8_pack(const uint16_t* __restrict__ x, int64_t total_chunks,
+                                                    int H, uint8_t* __restrict__ data,
+                                                    uint8_t* __restrict__ scales) {
+  // one lane per 16-element chunk; chunk index runs over the whole tensor
+  int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool valid = ch < total_chunks;
+  int64_t chc = valid ? ch : 0;
+  const uint4* xp = reinterpret_cast<const uint4*>(x) + 2 * chc;
+  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+  if (valid) {
+    a = ld_stream16(xp);
+    b = ld_stream16(xp + 1);
+  }
+  uint32_t m0 = absmax_bf16x8(a), m1 = absmax_bf16x8(b);
+  uint32_t m = m0 > m1 ? m0 : m1;
+  uint32_t o = (uint32_t)__shfl_xor((int)m, 1, kWave);  // partner chunk of the same block
+  m = m > o ? m : o;
+  if (!valid) return;
+  int e = mx_exponent(__uint_as_float(m << 16));
+  uint4 d;
+  if (e >= -126) {
+    float sc = pow2f(e);
+    d.x = fp8x4_from_bf16(a.x, a.y, sc);
+    d.y = fp8x4_from_bf16(a.z, a.w, sc);
+    d.z = fp8x4_from_bf16(b.x, b.y, sc);
+    d.w = fp8x4_from_bf16(b.z, b.w, sc);
+  } else {
+    float sc = pow2f(e + 64);
+    d.x = fp8x4_from_bf16_tiny(a.x, a.y, sc);
+    d.y = fp8x4_from_bf16_tiny(a.z, a.w, sc);
+    d.z = fp8x4_from_bf16_tiny(b.x, b.y, sc);
+    d.w = fp8x4_from_bf16_tiny(b.z, b.w, sc);
+  }
+  reinterpret_cast<uint4*>(data)[ch] = d;
+  // scales [rows, H/32] row-major: block (row, col/32) is global block ch/2
+  if ((ch & 1) == 0) scales[ch >> 1] = (uint8_t)(e + 127);
+}
+
+}  // namespace mtb
+
+using namespace mtb;
+
+MTB_EXPORT int32_t ep_nvfp4_pack(const uint16_t* x, int64_t rows, int64_t hidden, uint8_t* packed,
+                                 int32_t round_mode, const uint64_t* sr_state, void* stream) {
+  if (rows < 0 || hidden <= 0 || hidden % 64 != 0 || hidden > 16384) return EP_ERR_SHAPE;
+  if (rows > (int64_t)INT32_MAX / 4 || rows * hidden >= ((int64_t)1 << 40)) return EP_ERR_RANGE;
+  if (round_mode < EP_ROUND_NEAREST || round_mode > EP_ROUND_SR_STREAM) return EP_ERR_DTYPE;
+  if (rows == 0) return EP_OK;
+  if (!x || !packed) return EP_ERR_NULL;
+  if (round_mode != EP_ROUND_NEAREST && !sr_state) return EP_ERR_NULL;
+  const int H = (int)hidden;
+  const int row_bytes = 9 * H / 16 + 4;
+  const int nb = (H / 16 + 63) / 64;
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  if (round_mode == EP_ROUND_SR_ELEMENT) {
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
+  } else if (round_mode == EP_ROUND_SR_STREAM) {
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
+  } else if (nb <= 1) {
+    hipLaunchKernelGGL(k_nvfp4_pack<1>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+  } else if (nb <= 2) {
+    hipLaunchKernelGGL(k_nvfp4_pack<2>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+  } else if (nb <= 4) {
+    hipLaunchKernelGGL(k_nvfp4_pack<4>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+  } else if (nb <= 8) {
+    hipLaunchKernelGGL(k_nvfp4_pack<8>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+  } else {
+    hipLaunchKernelGGL(k_nvfp4_pack<16>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+  }
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_mxfp8_pack(const uint16_t* x, int64_t rows, int64_t hidden, uint8_t* data,
+                                 uint8_t* scales, void* stream) {
+  if (rows < 0 || hidden <= 0 || hidden % 32 != 0) return EP_ERR_SHAPE;
+  if (rows * hidden >= ((int64_t)1 << 40)) return EP_ERR_RANGE;
+  if (rows == 0) return EP_OK;
+  if (!x || !data || !scales) return EP_ERR_NULL;
+  int64_t chunks = rows * hidden / 16;
+  dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
+  hipLaunchKernelGGL(k_mxfp8_pack, grid, block, 0, (hipStream_t)stream, x, chunks, (int)hidden, data, scales);
+  return launch_status();
+}

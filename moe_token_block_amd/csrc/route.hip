@@ -1,0 +1,211 @@
+// Local routing permutation: a stable counting sort of (token, slot) entries
+// by expert, with each expert's slot padded to the alignment (P2, review
+// comments: routing prepared once and cached for dispatch and combine;
+// padded expert slots.  P1, commit messages: top_k, alignment and the index
+// dtype are arguments of the NVFP4 paths).
+//
+// Three launches, no atomics on global memory except the error flag:
+//   1. count   -- each wave counts its 256 consecutive entries per expert
+//                 (LDS atomics: order does not matter for counts);
+//   2. scan    -- one workgroup turns the per-wave histograms into per-wave
+//                 starting ranks, the counts, the padded offsets, and writes
+//                 -1 into every padding / unused row of src_row;
+//   3. scatter -- each wave walks its entries in order, 64 at a time; lanes
+//                 with equal expert ids are found with one ballot per id bit,
+//                 so the rank inside a step is a popcount and the order is
+//                 stable (token order, then slot order).
+#include "common.h"
+#include "launch.h"
+
+namespace mtb {
+
+constexpr int kRouteChunk = 256;  // entries per wave
+constexpr int kMaxExperts = 1024;
+
+template <typename IDX>
+__device__ __forceinline__ int load_expert(const IDX* idx, int64_t i, int E, bool& bad) {
+  int64_t v = (int64_t)idx[i];
+  bad = (v < -1) || (v >= E);
+  return (v >= 0 && v < E) ? (int)v : -1;
+}
+
+template <typename IDX>
+__global__ __launch_bounds__(256) void k_route_count(const IDX* __restrict__ idx, int64_t R, int E, int W,
+                                                     int32_t* __restrict__ hist, int32_t* __restrict__ d_error) {
+  __shared__ int32_t cnt[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
+  const int w = blockIdx.x * 4 + wl;
+  for (int e = lane; e < E; e += 64) cnt[wl][e] = 0;
+  __syncthreads();
+  if (w < W) {
+    bool any_bad = false;
+    for (int s = 0; s < kRouteChunk / 64; ++s) {
+      int64_t i = (int64_t)w * kRouteChunk + s * 64 + lane;
+      if (i < R) {
+        bool bad;
+        int x = load_expert(idx, i, E, bad);
+        any_bad |= bad;
+        if (x >= 0) atomicAdd(&cnt[wl][x], 1);
+      }
+    }
+    if (any_bad) atomicOr(d_error, EP_DEVERR_EXPERT_ID);
+  }
+  __syncthreads();
+  if (w < W)
+    for (int e = lane; e < E; e += 64) hist[(int64_t)w * E + e] = cnt[wl][e];
+}
+
+// One workgroup of 1024 threads.  hist [W, E] -> per-wave starting rank
+// (exclusive prefix over waves), counts, padded offsets, -1 padding rows.
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist, int W, int E, int A, int r_cap,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ src_row) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x;
+  const int G = 1024 / E;           // wave groups per expert (E <= 1024)
+  const int e = tid % E, g = tid / E;
+  const bool active = g < G;
+  const int wpg = (W + G - 1) / G;
+  const int w0 = active ? g * wpg : 0, w1 = active ? min(W, w0 + wpg) : 0;
+  int32_t local = 0;
+  for (int w = w0; w < w1; ++w) local += hist[(int64_t)w * E + e];
+  if (active) part[g * E + e] = local;
+  __syncthreads();
+  if (tid < E) {
+    int32_t run = 0;
+    for (int gg = 0; gg < G; ++gg) {
+      int32_t c = part[gg * E + tid];
+      part[gg * E + tid] = run;
+      run += c;
+    }
+    counts[tid] = run;
+    scan[tid] = (run + A - 1) / A * A;
+  }
+  __syncthreads();
+  if (active) {
+    int32_t run = part[g * E + e];
+    for (int w = w0; w < w1; ++w) {
+      int32_t c = hist[(int64_t)w * E + e];
+      hist[(int64_t)w * E + e] = run;
+      run += c;
+    }
+  }
+  // inclusive scan of the padded sizes over experts (Hillis-Steele in LDS)
+  for (int o = 1; o < E; o <<= 1) {
+    int32_t v = 0;
+    if (tid < E && tid >= o) v = scan[tid - o];
+    __syncthreads();
+    if (tid < E) scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid + 1] = scan[tid];
+  if (tid == 0) offsets[0] = 0;
+  // padding rows of each expert, then everything from off_E to r_cap: -1
+  if (tid < E) {
+    int32_t end = scan[tid];
+    int32_t c = (tid ? scan[tid - 1] : 0) + counts[tid];
+    for (int32_t r = c; r < end; ++r) src_row[r] = -1;
+  }
+  const int32_t total = scan[E - 1];
+  for (int32_t r = total + tid; r < r_cap; r += 1024) src_row[r] = -1;
+}
+
+template <typename IDX>
+__global__ __launch_bounds__(256) void k_route_scatter(const IDX* __restrict__ idx, int64_t R, int k, int E, int W,
+                                                       int ebits, const int32_t* __restrict__ hist,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row) {
+  __shared__ int32_t base[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
+  const int w = blockIdx.x * 4 + wl;
+  if (w < W)
+    for (int e = lane; e < E; e += 64) base[wl][e] = hist[(int64_t)w * E + e] + offsets[e];
+  __syncthreads();
+  if (w >= W) return;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int s = 0; s < kRouteChunk / 64; ++s) {
+    int64_t i = (int64_t)w * kRouteChunk + s * 64 + lane;
+    int x = -1;
+    if (i < R) {
+      bool bad;
+      x = load_expert(idx, i, E, bad);
+    }
+    const bool valid = x >= 0;
+    uint64_t m = __ballot(valid);
+    // lanes whose expert id agrees with this lane's on every id bit
+#pragma unroll 1
+    for (int b = 0; b < ebits; ++b) {
+      uint64_t bb = __ballot(valid && ((x >> b) & 1));
+      m &= ((x >> b) & 1) ? bb : ~bb;
+    }
+    if (valid) {
+      int32_t b0 = base[wl][x];
+      int32_t rank = __popcll(m & lt);
+      int32_t d = b0 + rank;
+      dst_row[i] = d;
+      src_row[d] = (int32_t)(i / k);
+      if ((m >> lane) == 1ull) base[wl][x] = b0 + __popcll(m);  // the group's last lane advances the base
+    } else if (i < R) {
+      dst_row[i] = -1;
+    }
+  }
+}
+
+}  // namespace mtb
+
+using namespace mtb;
+
+static int64_t route_waves(int64_t tokens, int64_t top_k) { return (tokens * top_k + kRouteChunk - 1) / kRouteChunk; }
+
+MTB_EXPORT int64_t ep_route_capacity(int64_t tokens, int64_t top_k, int64_t num_experts, int64_t alignment) {
+  if (tokens < 0 || top_k < 1 || num_experts < 1) return EP_ERR_SHAPE;
+  if (alignment < 16 || alignment % 16 != 0) return EP_ERR_ALIGN;
+  return tokens * top_k + num_experts * (alignment - 1);
+}
+
+MTB_EXPORT size_t ep_route_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_experts) {
+  if (tokens < 0 || top_k < 1 || num_experts < 1) return 0;
+  int64_t w = route_waves(tokens, top_k);
+  return (size_t)((w > 0 ? w : 1) * num_experts * sizeof(int32_t));
+}
+
+MTB_EXPORT int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, int64_t top_k,
+                                 int64_t num_experts, int64_t alignment, int64_t r_cap, int32_t* counts,
+                                 int32_t* offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
+                                 size_t workspace_bytes, int32_t* d_error, void* stream) {
+  if (tokens < 0 || top_k < 1 || num_experts < 1 || r_cap < 0) return EP_ERR_SHAPE;
+  if (num_experts > kMaxExperts) return EP_ERR_SHAPE;
+  if (alignment < 16 || alignment % 16 != 0) return EP_ERR_ALIGN;
+  if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64) return EP_ERR_DTYPE;
+  if (tokens * top_k + num_experts * alignment >= (int64_t)INT32_MAX || r_cap >= (int64_t)INT32_MAX) return EP_ERR_RANGE;
+  if (r_cap < ep_route_capacity(tokens, top_k, num_experts, alignment)) return EP_ERR_CAPACITY;
+  if (!counts || !offsets || !src_row || !d_error || (tokens > 0 && (!topk_idx || !dst_row))) return EP_ERR_NULL;
+  if (!workspace || workspace_bytes < ep_route_workspace_bytes(tokens, top_k, num_experts)) return EP_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = tokens * top_k;
+  const int W = (int)route_waves(tokens, top_k);
+  const int E = (int)num_experts;
+  int32_t* hist = (int32_t*)workspace;
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  if (W > 0) {
+    dim3 grid((unsigned)((W + 3) / 4)), block(256);
+    if (idx_dtype == EP_IDX_INT32)
+      hipLaunchKernelGGL(k_route_count<int32_t>, grid, block, 0, s, (const int32_t*)topk_idx, R, E, W, hist, d_error);
+    else
+      hipLaunchKernelGGL(k_route_count<int64_t>, grid, block, 0, s, (const int64_t*)topk_idx, R, E, W, hist, d_error);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, hist, W, E, (int)alignment, (int)r_cap, counts,
+                     offsets, src_row);
+  if (W > 0) {
+    dim3 grid((unsigned)((W + 3) / 4)), block(256);
+    if (idx_dtype == EP_IDX_INT32)
+      hipLaunchKernelGGL(k_route_scatter<int32_t>, grid, block, 0, s, (const int32_t*)topk_idx, R, (int)top_k, E, W,
+                         ebits, hist, offsets, dst_row, src_row);
+    else
+      hipLaunchKernelGGL(k_route_scatter<int64_t>, grid, block, 0, s, (const int64_t*)topk_idx, R, (int)top_k, E, W,
+                         ebits, hist, offsets, dst_row, src_row);
+  }
+  return launch_status();
+}

@@ -1,0 +1,142 @@
+// NVFP4 rows -> BF16 (P1, PR description: rows not consumed directly are
+// decoded to BF16), with an optional gather by a source-row map; and the
+// MXFP8 grouped receive (a plain row gather).
+//
+// Unpack mapping: one wave64 per output row, lane l owns 16-element blocks
+// l, l+64, ...: an 8-byte code load, one scale byte, two 16-byte BF16 stores.
+// Decode: the converter gives e2m1 * 2^(k+e) exactly (k = the scale's
+// exponent, e = the row's), one multiply by the scale's significand makes the
+// exact product e2m1 * s * t, and v_cvt_pk_bf16_f32 rounds it to BF16.
+#include "common.h"
+#include "launch.h"
+
+namespace mtb {
+
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 E2M1 codes of word w (4 bytes) times the block multiplier -> 4 packed BF16 pairs.
+__device__ __forceinline__ void decode8(uint32_t w, float scale, float mant, uint32_t* o) {
+  f32x2 p0 = fp4_unpack2<0>(w, scale), p1 = fp4_unpack2<1>(w, scale);
+  f32x2 p2 = fp4_unpack2<2>(w, scale), p3 = fp4_unpack2<3>(w, scale);
+  o[0] = bf16pair(p0[0] * mant, p0[1] * mant);
+  o[1] = bf16pair(p1[0] * mant, p1[1] * mant);
+  o[2] = bf16pair(p2[0] * mant, p2[1] * mant);
+  o[3] = bf16pair(p3[0] * mant, p3[1] * mant);
+}
+
+// Rows whose k + e falls below -126 (t < 2^-117): exact e2m1 * s first, then
+// one rounding by the power of two.
+__device__ __forceinline__ void decode8_tiny(uint32_t w, float s, int e, uint32_t* o) {
+  f32x2 p[4] = {fp4_unpack2<0>(w, 1.0f), fp4_unpack2<1>(w, 1.0f), fp4_unpack2<2>(w, 1.0f), fp4_unpack2<3>(w, 1.0f)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = bf16pair(__builtin_ldexpf(p[i][0] * s, e), __builtin_ldexpf(p[i][1] * s, e));
+}
+
+__global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict__ packed, int rows_in, int H,
+                                                      int row_bytes, const int32_t* __restrict__ src_row,
+                                                      int rows_out, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int g = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (g >= rows_out) return;
+  int src = src_row ? src_row[g] : g;
+  if (src >= rows_in) src = -1;  // out-of-range map entries decode as zero rows
+  const int nblk = H >> 4;
+  uint4* orow = reinterpret_cast<uint4*>(out + (size_t)g * H);
+  if (src < 0) {
+    for (int j = lane; j < nblk; j += 64) {
+      orow[2 * j] = make_uint4(0, 0, 0, 0);
+      orow[2 * j + 1] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  const uint8_t* prow = packed + (size_t)src * row_bytes;
+  const float t = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
+  const int e = pow2_exponent(t);
+  for (int j = lane; j < nblk; j += 64) {
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(prow + 8 * j);
+    uint32_t w0 = cw[0], w1 = cw[1];
+    float s = e4m3_decode(prow[(H >> 1) + j]);
+    uint32_t o[8];
+    if (s == 0.0f) {
+      // zero scale: every element is a signed zero
+      decode8(w0, 1.0f, 0.0f, o);
+      decode8(w1, 1.0f, 0.0f, o + 4);
+    } else {
+      int k = __builtin_amdgcn_frexp_expf(s) - 1;
+      float mant = __builtin_amdgcn_frexp_mantf(s) * 2.0f;
+      int K = k + e;
+      if (K >= -126) {
+        float sc = pow2f(K);
+        decode8(w0, sc, mant, o);
+        decode8(w1, sc, mant, o + 4);
+      } else {
+        decode8_tiny(w0, s, e, o);
+        decode8_tiny(w1, s, e, o + 4);
+      }
+    }
+    orow[2 * j] = make_uint4(o[0], o[1], o[2], o[3]);
+    orow[2 * j + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// MXFP8 grouped receive: grouped row g copies token src_row[g] (data + scales);
+// -1 rows are zero.  One wave per grouped row, 16-byte copies.
+__global__ __launch_bounds__(256) void k_mxfp8_receive(const uint8_t* __restrict__ data,
+                                                       const uint8_t* __restrict__ scales, int tokens, int H,
+                                                       const int32_t* __restrict__ src_row, int r_cap,
+                                                       uint8_t* __restrict__ g_data, uint8_t* __restrict__ g_scales) {
+  const int lane = threadIdx.x & 63;
+  const int g = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (g >= r_cap) return;
+  const int src = src_row[g];
+  const int n16 = H >> 4, ns = H >> 5;
+  uint4* dst = reinterpret_cast<uint4*>(g_data + (size_t)g * H);
+  uint8_t* ds = g_scales + (size_t)g * ns;
+  if (src < 0 || src >= tokens) {  // padding (or an out-of-range entry): zero bytes
+    for (int i = lane; i < n16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
+    for (int i = lane; i < ns; i += 64) ds[i] = 0;
+    return;
+  }
+  const uint4* sp = reinterpret_cast<const uint4*>(data + (size_t)src * H);
+  for (int i = lane; i < n16; i += 64) dst[i] = sp[i];
+  const uint8_t* ss = scales + (size_t)src * ns;
+  for (int i = lane; i < ns; i += 64) ds[i] = ss[i];
+}
+
+}  // namespace mtb
+
+using namespace mtb;
+
+MTB_EXPORT int32_t ep_nvfp4_unpack(const uint8_t* packed, int64_t rows_in, int64_t hidden, const int32_t* src_row,
+                                   int64_t rows_out, uint16_t* out, void* stream) {
+  if (rows_in < 0 || rows_out < 0 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
+  if (!src_row && rows_out != rows_in) return EP_ERR_SHAPE;
+  if (rows_in > INT32_MAX / 4 || rows_out > INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
+  if (rows_out == 0) return EP_OK;
+  if (!out || (rows_in > 0 && !packed)) return EP_ERR_NULL;
+  if (!src_row && rows_in == 0) return EP_OK;
+  const int H = (int)hidden;
+  dim3 grid((unsigned)((rows_out + 3) / 4)), block(256);
+  hipLaunchKernelGGL(k_nvfp4_unpack, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
+                     9 * H / 16 + 4, src_row, (int)rows_out, out);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_mxfp8_direct_receive(const uint8_t* data, const uint8_t* scales, int64_t tokens,
+                                           int64_t hidden, int64_t r_cap, const int32_t* src_row,
+                                           uint8_t* g_data, uint8_t* g_scales, void* stream) {
+  if (tokens < 0 || r_cap < 0 || hidden <= 0 || hidden % 32 != 0) return EP_ERR_SHAPE;
+  if (tokens > INT32_MAX / 4 || r_cap > INT32_MAX / 4 || hidden > (1 << 24)) return EP_ERR_RANGE;
+  if (r_cap == 0) return EP_OK;
+  if (!src_row || !g_data || !g_scales || (tokens > 0 && (!data || !scales))) return EP_ERR_NULL;
+  dim3 grid((unsigned)((r_cap + 3) / 4)), block(256);
+  hipLaunchKernelGGL(k_mxfp8_receive, grid, block, 0, (hipStream_t)stream, data, scales, (int)tokens, (int)hidden, src_row,
+                     (int)r_cap, g_data, g_scales);
+  return launch_status();
+}

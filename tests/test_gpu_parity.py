@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact for codes, block scales, token scales, MXFP8 data/scales,
+routing (counts, offsets, dst_row, src_row), the rowwise grouped operand, the
+expert scales D_e, unpacked BF16 and stochastic rounding; for values derived
+from FP32 amaxes or post-RHT values, the tolerance in ``gpu_util.tolerant_codes``
+(north bar: a differing E2M1 code is off by one grid step, in at most 1e-4 of
+elements).  Inputs come from ``workloads`` (seeded, synthetic).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_token_block_amd as mtb
+import workloads
+from oracle import formats as F
+from oracle import mxfp8 as omx
+from oracle import nvfp4 as onv
+from oracle import dswiglu as odsw
+from oracle import receive as orecv
+from oracle.routing import route_plan as o_route
+
+from gpu_util import require_gpu, bf16_dev, host, i32_dev, assert_bytes_equal, tolerant_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _edge_rows(h, rng):
+    """Rows that exercise the corner cases of the token / block scale rules."""
+    rows = []
+    rows.append(np.zeros(h))                                   # all-zero row
+    r = rng.standard_normal(h); r[:16] = 0.0; rows.append(r)   # a zero block
+    rows.append(rng.standard_normal(h) * 1e-38)                # BF16 subnormal territory
+    rows.append(rng.standard_normal(h) * 1e-30)                # tiny t
+    rows.append(rng.standard_normal(h) * 1e36)                 # huge t
+    r = rng.standard_normal(h) * 1e-3; r[5] = 1e3; rows.append(r)  # one outlier
+    r = np.full(h, -0.0); rows.append(r)                      # all -0
+    r = rng.standard_normal(h); r[::7] = -0.0; rows.append(r)
+    # values on exact E2M1 ties relative to the block scale
+    r = np.tile([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, -0.25, 0.5, 3.0, 4.0, 1.5, 1.0, 2.0], h // 16)
+    rows.append(r * 3.0)
+    r = rng.standard_normal(h) * np.exp(rng.uniform(-20, 20, h)); rows.append(r)  # wide in-row range
+    return np.array(rows)
+
+
+def _bits(x):
+    return F.f32_to_bf16(np.asarray(x, dtype=np.float32))
+
+
+# ------------------------------------------------------------------ NVFP4 pack / unpack
+@pytest.mark.parametrize("h", [64, 128, 192, 1024, 2112, 7168, 16384])
+def test_pack_unpack_bit_exact(dev, h):
+    rng = np.random.default_rng(h)
+    n = 37
+    x = rng.standard_normal((n, h)) * 10.0 ** rng.uniform(-4, 4, size=(n, 1))
+    x = np.concatenate([x, _edge_rows(h, rng)])
+    bits = _bits(x)
+    print(f"pack/unpack h={h} rows={bits.shape[0]}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    want = onv.pack_rows(bits)
+    assert_bytes_equal(host(packed), want, f"pack h={h}")
+    un = mtb.ep_nvfp4_unpack(packed, h)
+    assert_bytes_equal(host(un), onv.unpack_rows(want, h), f"unpack h={h}")
+    src = rng.integers(-1, bits.shape[0], size=2 * bits.shape[0]).astype(np.int32)
+    un2 = mtb.ep_nvfp4_unpack(packed, h, src_row=i32_dev(src, dev))
+    assert_bytes_equal(host(un2), onv.unpack_rows(want, h, src), f"unpack gather h={h}")
+
+
+def test_pack_empty_and_config1(dev):
+    out = mtb.ep_nvfp4_pack(torch.empty((0, 128), dtype=torch.bfloat16, device=dev))
+    assert out.shape == (0, 76)
+    w = workloads.config1()
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    want = onv.pack_rows(w.x_bits)
+    assert_bytes_equal(host(packed), want, "pack config1")
+    assert_bytes_equal(host(mtb.ep_nvfp4_unpack(packed, 1024)), onv.unpack_rows(want, 1024), "unpack config1")
+
+
+@pytest.mark.parametrize("mode,seed,base", [(1, 1234, 0), (1, 2 ** 40 + 3, 12345), (2, 1234, 0), (2, 77, 6)])
+def test_stochastic_rounding_bit_exact(dev, mode, seed, base):
+    rng = np.random.default_rng(seed % 1000 + mode)
+    h = 256
+    x = rng.standard_t(3, size=(48, h)) * 1e-3
+    x = np.concatenate([x, _edge_rows(h, rng)])
+    bits = _bits(x)
+    st = torch.tensor([seed, base], dtype=torch.int64, device=dev)
+    print(f"sr mode={mode} seed={seed} base={base}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev), round_mode=mode, sr_state=st)
+    want = onv.pack_rows(bits, sr_seed=seed, sr_counter_base=base, sr_mode="element" if mode == 1 else "stream")
+    assert_bytes_equal(host(packed), want, f"SR mode {mode}")
+
+
+# ------------------------------------------------------------------ MXFP8
+@pytest.mark.parametrize("h", [32, 96, 1024, 4096])
+def test_mxfp8_pack_bit_exact(dev, h):
+    rng = np.random.default_rng(100 + h)
+    x = rng.standard_normal((41, h)) * 10.0 ** rng.uniform(-5, 5, size=(41, 1))
+    if h >= 64:
+        x = np.concatenate([x, _edge_rows(h, rng)])
+    x[0, :32] = 1e-39
+    bits = _bits(x)
+    data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(bits, dev))
+    wd, ws = omx.pack_rows(bits)
+    assert_bytes_equal(host(scales), ws, f"mxfp8 scales h={h}")
+    assert_bytes_equal(host(data), wd, f"mxfp8 data h={h}")
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("tokens,k,E,A,idx64,unused", [
+    (1, 1, 1, 16, False, 0.0), (97, 3, 6, 16, False, 0.1), (300, 2, 8, 128, True, 0.0),
+    (513, 4, 33, 256, False, 0.05), (2048, 8, 32, 16, True, 0.0), (1000, 1, 1024, 16, False, 0.0),
+    (0, 2, 4, 16, False, 0.0)])
+def test_route_plan_bit_exact(dev, tokens, k, E, A, idx64, unused):
+    rng = np.random.default_rng(tokens * 7 + E)
+    topk = np.array([rng.permutation(E)[:k] for _ in range(tokens)], dtype=np.int32).reshape(tokens, k)
+    if unused:
+        topk[rng.random(topk.shape) < unused] = -1
+    if E > 2 and tokens > 0:
+        topk[topk == E - 2] = -1                       # one empty expert
+    t_dev = torch.from_numpy(topk.astype(np.int64 if idx64 else np.int32)).to(dev)
+    plan = mtb.ep_route_plan(t_dev, E, A)
+    want = o_route(topk, E, A)
+    for key in ("counts", "offsets", "dst_row", "src_row"):
+        assert_bytes_equal(host(plan[key]), want[key], f"route {key}")
+    assert int(host(plan["d_error"])[0]) == 0
+
+
+def test_route_plan_flags_bad_ids(dev):
+    topk = np.array([[0, 1], [5, -1], [2, -3], [1, 0]], dtype=np.int32)
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), 4, 16)
+    want = o_route(topk, 4, 16)
+    assert int(host(plan["d_error"])[0]) == mtb.EP_DEVERR_EXPERT_ID
+    for key in ("counts", "offsets", "dst_row", "src_row"):
+        assert_bytes_equal(host(plan[key]), want[key], f"route {key}")
+
+
+# ------------------------------------------------------------------ direct receive
+def _check_receive(dev, w, packed_np, got, plan_np, hidden, exact=True):
+    off = plan_np["offsets"].astype(np.int64)
+    rc = host(got["row_codes"])[: off[-1]]
+    want = orecv.direct_receive(packed_np, hidden, w.topk_idx, w.num_experts, w.alignment)
+    assert_bytes_equal(rc, want["row_codes"][: off[-1]], "rowwise codes")
+    assert_bytes_equal(host(got["row_scales"])[: off[-1]], want["row_scales"][: off[-1]], "rowwise scales")
+    assert_bytes_equal(host(got["row_t"])[: off[-1]].view(np.uint32), want["row_t"][: off[-1]].view(np.uint32), "row t")
+    assert_bytes_equal(host(got["col_scale"]).view(np.uint32), want["col_scale"].view(np.uint32), "D_e")
+    n = hidden * off[-1]
+    gc = host(got["col_codes"])[: n // 2]
+    gs = host(got["col_scales"])[: n // 16]
+    if exact:
+        assert_bytes_equal(gs, want["col_scales"][: n // 16], "columnwise scales")
+        assert_bytes_equal(gc, want["col_codes"][: n // 2], "columnwise codes")
+    else:
+        tolerant_codes(F.unpack_nibbles(gc), F.unpack_nibbles(want["col_codes"][: n // 2]), gs,
+                       want["col_scales"][: n // 16], "columnwise")
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=1, tokens=150, hidden=256, E=5, k=2, A=16, unused=0.05, empty=[3]),
+    dict(seed=2, tokens=600, hidden=128, E=8, k=2, A=128, unused=0.0, empty=[]),
+    dict(seed=3, tokens=333, hidden=192, E=3, k=1, A=256, unused=0.2, empty=[]),
+    dict(seed=4, tokens=1024, hidden=512, E=16, k=4, A=16, unused=0.0, empty=[0, 15]),
+    dict(seed=5, tokens=7, hidden=64, E=4, k=2, A=16, unused=0.0, empty=[]),
+])
+def test_direct_receive_bit_exact(dev, case):
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
+    print(f"receive case {case}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    packed_np = onv.pack_rows(w.x_bits)
+    assert_bytes_equal(host(packed), packed_np, "pack")
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    got = mtb.ep_nvfp4_direct_receive(packed, w.x_bits.shape[1], plan)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    _check_receive(dev, w, packed_np, got, plan_np, w.x_bits.shape[1])
+
+
+def test_direct_receive_config1(dev):
+    w = workloads.config1()
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 4, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, 1024, plan)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    _check_receive(dev, w, onv.pack_rows(w.x_bits), got, plan_np, 1024)
+    # P1 test analogue: decoding the grouped rowwise rows equals decoding the sender rows in grouped order
+    off = int(plan_np["offsets"][-1])
+    dec = mtb.ep_nvfp4_unpack(packed, 1024, src_row=plan["src_row"][:off].contiguous())
+    assert_bytes_equal(host(dec), onv.unpack_rows(onv.pack_rows(w.x_bits), 1024, plan_np["src_row"][:off]),
+                       "grouped decode")
+
+
+def test_direct_receive_rowwise_only(dev):
+    w = workloads.small_dispatch(9, 200, 192, 4, 2)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 4, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, 192, plan, columnwise=False)
+    want = orecv.direct_receive(onv.pack_rows(w.x_bits), 192, w.topk_idx, 4, 16, columnwise=False)
+    off = int(host(plan["offsets"])[-1])
+    assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "rowwise-only codes")
+
+
+def test_mxfp8_receive_bit_exact(dev):
+    w = workloads.small_dispatch(11, 300, 256, 6, 2, alignment=128, unused_frac=0.1)
+    data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 6, 128)
+    gd, gs = mtb.ep_mxfp8_direct_receive(data, scales, plan)
+    wd, ws = omx.pack_rows(w.x_bits)
+    src = host(plan["src_row"])
+    ed, es = omx.grouped_receive(wd, ws, src)
+    assert_bytes_equal(host(gd), ed, "mxfp8 grouped data")
+    assert_bytes_equal(host(gs), es, "mxfp8 grouped scales")
+
+
+# ------------------------------------------------------------------ dSwiGLU
+@pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([5, 40, 0, 16, 1], 128),
+                                        ([300, 0, 129], 256), ([1], 64)])
+def test_dswiglu_two_stage(dev, counts, ffn):
+    w = workloads.small_dswiglu(sum(counts) + ffn, counts, ffn)
+    out = mtb.dswiglu_nvfp4_quant(bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    dx = host(out["dx"])
+    # stage 1: dX within one BF16 ulp of the float64 oracle; amax == max |dX_gpu| exactly
+    want_dx = odsw.dswiglu(w.preact_bits, w.dy_bits)
+    ulp = np.abs(dx.view(np.int16).astype(np.int64) - want_dx.view(np.int16).astype(np.int64))
+    assert ulp.max(initial=0) <= 1, f"dX differs by {ulp.max()} ulp"
+    am = host(out["amax"])
+    assert_bytes_equal(am.view(np.uint32), odsw.expert_amax(dx, w.counts).view(np.uint32), "amax")
+    # stage 2: the oracle quantizer on the GPU's own dX and amax
+    q = odsw.fc1_grad_quant(dx, w.counts, am)
+    assert_bytes_equal(host(out["row_scale"]).view(np.uint32), q["row_scale"].view(np.uint32), "D_row")
+    assert_bytes_equal(host(out["col_scale"]).view(np.uint32), q["col_scale"].view(np.uint32), "D_col")
+    t = sum(counts)
+    tolerant_codes(F.unpack_nibbles(host(out["row_codes"])), F.unpack_nibbles(q["row_codes"]),
+                   host(out["row_scales"]), q["row_scales"], "fc1 rowwise")
+    n = q["col_codes"].size
+    tolerant_codes(F.unpack_nibbles(host(out["col_codes"])[:n]), F.unpack_nibbles(q["col_codes"]),
+                   host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "fc1 columnwise")
+
+
+# ------------------------------------------------------------------ determinism and graph capture
+def test_deterministic_and_graph_capturable(dev):
+    w = workloads.small_dispatch(21, 700, 512, 8, 2, unused_frac=0.02)
+    x = bf16_dev(w.x_bits, dev)
+    topk = torch.from_numpy(w.topk_idx).to(dev)
+    plan = mtb.ep_route_plan(topk, 8, 16)
+    packed = mtb.ep_nvfp4_pack(x)
+    ref = mtb.ep_nvfp4_direct_receive(packed, 512, plan)
+    again = mtb.ep_nvfp4_direct_receive(packed, 512, mtb.ep_route_plan(topk, 8, 16))
+    off = int(plan["offsets"][-1])          # rows from off_E on are not written by the receive
+    for k in ("row_codes", "row_scales", "row_t"):
+        assert torch.equal(ref[k][:off], again[k][:off]), k
+    assert torch.equal(ref["col_codes"][: 256 * off], again["col_codes"][: 256 * off])
+    assert torch.equal(ref["col_scales"][: 32 * off], again["col_scales"][: 32 * off])
+    assert torch.equal(ref["col_scale"], again["col_scale"])
+    # capture pack -> route -> receive in one HIP graph; replay several times with
+    # eager work in between and check every replay against the eager result
+    out_p = torch.empty_like(packed)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    derr = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = {k: torch.empty_like(v) for k, v in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm-up on a side stream before capture
+        mtb.ep_nvfp4_pack(x, out=out_p)
+        wplan = mtb.ep_route_plan(topk, 8, 16, d_error=derr, workspace=ws)
+        mtb.ep_nvfp4_direct_receive(out_p, 512, wplan, out=outs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mtb.ep_nvfp4_pack(x, out=out_p)
+        gplan = mtb.ep_route_plan(topk, 8, 16, d_error=derr, workspace=ws)
+        mtb.ep_nvfp4_direct_receive(out_p, 512, gplan, out=outs)
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        out_p.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_p, packed), rep
+        assert torch.equal(gplan["src_row"], plan["src_row"]), rep
+        assert torch.equal(gplan["dst_row"], plan["dst_row"]), rep
+        off = int(plan["offsets"][-1])
+        for k in ("row_codes", "row_scales", "row_t"):
+            assert torch.equal(outs[k][:off], ref[k][:off]), (rep, k)
+        n = 512 * off
+        assert torch.equal(outs["col_codes"][: n // 2], ref["col_codes"][: n // 2]), rep
+        assert torch.equal(outs["col_scales"][: n // 16], ref["col_scales"][: n // 16]), rep
+        assert torch.equal(outs["col_scale"], ref["col_scale"]), rep
