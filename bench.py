@@ -1,0 +1,314 @@
+"""Benchmark of the block-scaled token codec hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of the dispatch workload
+(4096 tokens x hidden 4096 BF16 ~ N(0,1), top-2 of 8 experts with
+Zipf(1.2)-skewed routing and expert 7 empty, 16-row aligned slots):
+
+  route plan -> NVFP4 pack -> NVFP4 direct receive (rowwise + RHT columnwise)
+  -> MXFP8 pack -> MXFP8 receive -> unpack of the received rows to BF16
+  -> combine backward: stochastic-rounding NVFP4 pack of a same-shaped
+     gradient (Student-t(3) * 1e-3, Philox seed 1234) + its direct receive
+  -> grouped dSwiGLU epilogue + FC1-gradient NVFP4 quantization over the
+     routed rows (ffn 2048; preact ~ N(0,1), dy ~ N(0, 1e-2^2)).
+
+value = algorithmic bytes (distinct inputs read once + outputs, padding rows
+excluded) of all kernels of a step / step time, in GB/s.  Inputs are resident
+in HBM before the timed region.  Per-call durations come from HIP events on
+the stream the kernels run on.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DOMINANT = "nvfp4_direct_receive"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--json-out", default=None)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------- bytes
+def row_bytes(h):
+    return 9 * h // 16 + 4
+
+
+def algorithmic_bytes(T, H, k, E, r_cap, R, Tg, F):
+    """Distinct input bytes read once + output bytes, per call of the step.
+    R = routed rows (T*k), Tg = rows of the grouped MLP (= R), padding excluded."""
+    rb = row_bytes(H)
+    b = {}
+    b["route_plan"] = T * k * 4 + E * 4 + (E + 1) * 4 + T * k * 4 + r_cap * 4
+    b["nvfp4_pack"] = T * H * 2 + T * rb
+    b["nvfp4_expert_scale"] = R * 4 + r_cap * 4 + (E + 1) * 4 + E * 4
+    b["nvfp4_direct_receive"] = (T * rb + r_cap * 4 + (E + 1) * 4 + E * 4
+                                 + R * (H // 2 + H // 16 + 4) + R * (H // 2 + H // 16))
+    b["mxfp8_pack"] = T * H * 2 + T * H + T * (H // 32)
+    b["mxfp8_receive"] = T * (H + H // 32) + r_cap * 4 + R * (H + H // 32)
+    b["nvfp4_unpack"] = T * rb + R * 4 + R * H * 2
+    b["nvfp4_pack_sr"] = T * H * 2 + T * rb + 16
+    b["nvfp4_expert_scale_grad"] = b["nvfp4_expert_scale"]
+    b["nvfp4_direct_receive_grad"] = b["nvfp4_direct_receive"]
+    b["dswiglu_nvfp4_quant"] = (Tg * 2 * F * 2 + Tg * F * 2 + E * 4                 # epilogue in
+                                + Tg * 2 * F * 2 + E * 4                            # dX out, amax
+                                + Tg * 2 * F * 2                                    # quant reads dX
+                                + 2 * Tg * (F + 2 * F // 16) + 2 * E * 4)            # row + col operands
+    return b
+
+
+# ---------------------------------------------------------------------------- inputs
+def make_inputs(dev):
+    import torch
+    import workloads
+    w = workloads.config2()
+    T, H = w.x_bits.shape
+    k = w.topk_idx.shape[1]
+    rng = [np.random.default_rng(s) for s in np.random.SeedSequence(7).spawn(3)]
+    grad = workloads.to_bf16_bits(rng[0].standard_t(3, size=(T, H)) * 1e-3)
+    F = 2048
+    R = T * k
+    pre = workloads.to_bf16_bits(rng[1].standard_normal((R, 2 * F), dtype=np.float32))
+    dy = workloads.to_bf16_bits(rng[2].standard_normal((R, F), dtype=np.float32) * np.float32(1e-2))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    return dict(w=w, T=T, H=H, k=k, E=w.num_experts, A=w.alignment, F=F, R=R,
+                x=bf(w.x_bits), grad=bf(grad), preact=bf(pre), dy=bf(dy),
+                topk=torch.from_numpy(w.topk_idx).to(dev),
+                sr=torch.tensor([1234, 0], dtype=torch.int64, device=dev),
+                host=dict(x=w.x_bits, grad=grad, pre=pre, dy=dy, topk=w.topk_idx))
+
+
+# ---------------------------------------------------------------------------- the step
+class Step:
+    """Pre-allocated outputs; ``run`` launches one pass of the path."""
+
+    def __init__(self, inp):
+        import torch
+        import moe_token_block_amd as m
+        self.m = m
+        self.inp = inp
+        dev = inp["x"].device
+        T, H, k, E, A, F, R = (inp[s] for s in ("T", "H", "k", "E", "A", "F", "R"))
+        self.r_cap = m.ep_route_capacity(T, k, E, A)
+        self.ws = torch.empty(max(m.lib().ep_route_workspace_bytes(T, k, E), 4), dtype=torch.uint8, device=dev)
+        self.derr = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.plan = m.ep_route_plan(inp["topk"], E, A, d_error=self.derr, workspace=self.ws)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.packed = torch.empty((T, row_bytes(H)), **u8)
+        self.packed_g = torch.empty((T, row_bytes(H)), **u8)
+        mk = lambda: dict(row_codes=torch.empty((self.r_cap, H // 2), **u8),
+                          row_scales=torch.empty((self.r_cap, H // 16), **u8),
+                          row_t=torch.empty(self.r_cap, dtype=torch.float32, device=dev),
+                          col_codes=torch.empty(self.r_cap * H // 2, **u8),
+                          col_scales=torch.empty(self.r_cap * H // 16, **u8),
+                          col_scale=torch.empty(E, dtype=torch.float32, device=dev))
+        self.recv, self.recv_g = mk(), mk()
+        self.mx = torch.empty(T * H + T * H // 32, **u8)
+        self.mx_out = (torch.empty((self.r_cap, H), **u8), torch.empty((self.r_cap, H // 32), **u8))
+        self.unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        # the unpack decodes the routed rows in grouped order (padding rows skipped)
+        off = self.plan["offsets"].cpu().numpy()
+        src = self.plan["src_row"].cpu().numpy()
+        self.src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
+        self.counts = self.plan["counts"]
+        self.dsw_ws = torch.empty(m.lib().dswiglu_workspace_bytes(E), **u8)
+        cap = R + 15 * E
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dsw = dict(dx=torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev), amax=torch.empty(E, **f32),
+                        row_codes=torch.empty((R, F), **u8), row_scales=torch.empty((R, 2 * F // 16), **u8),
+                        row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
+                        col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
+        self.names = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
+                      "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
+                      "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
+        self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: 4x the MALL
+
+    def calls(self):
+        m, i = self.m, self.inp
+        H, E, A = i["H"], i["E"], i["A"]
+        return [
+            lambda: m.ep_route_plan(i["topk"], E, A, d_error=self.derr, workspace=self.ws, out=self.plan),
+            lambda: m.ep_nvfp4_pack(i["x"], out=self.packed),
+            lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan, col_scale=self.recv["col_scale"]),
+            lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
+            lambda: m.ep_mxfp8_pack(i["x"], out=self.mx),
+            lambda: m.ep_mxfp8_direct_receive(self.mx[: i["T"] * H].view(i["T"], H),
+                                              self.mx[i["T"] * H:].view(i["T"], H // 32), self.plan, out=self.mx_out),
+            lambda: m.ep_nvfp4_unpack(self.packed, H, src_row=self.src_valid, out=self.unpacked),
+            lambda: m.ep_nvfp4_pack(i["grad"], m.EP_ROUND_SR_ELEMENT, i["sr"], out=self.packed_g),
+            lambda: m.ep_nvfp4_expert_scale(self.packed_g, H, self.plan, col_scale=self.recv_g["col_scale"]),
+            lambda: m.ep_nvfp4_direct_receive_scaled(self.packed_g, H, self.plan, self.recv_g),
+            lambda: m.dswiglu_nvfp4_quant(i["preact"], i["dy"], self.counts, out=self.dsw, workspace=self.dsw_ws),
+        ]
+
+    def run(self, events=None):
+        calls = self.calls()
+        if events is not None:
+            # a 1 GiB fill first: it evicts the MALL and keeps the GPU busy while the
+            # host enqueues the whole step, so each event pair brackets GPU time only
+            self.flush.fill_(1.0)
+        for j, c in enumerate(calls):
+            if events is not None:
+                events[j][0].record()
+            c()
+            if events is not None:
+                events[j][1].record()
+
+
+# ---------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(inp, n_tok):
+    """The oracle, as it stands, on the first n_tok tokens of the same workload (their
+    routing, their gradient rows, and the grouped dSwiGLU rows they route to)."""
+    from oracle import nvfp4, receive, mxfp8, dswiglu
+    from oracle.routing import route_plan
+    h = inp["host"]
+    H, E, A, F, k = inp["H"], inp["E"], inp["A"], inp["F"], inp["k"]
+    x = h["x"][:n_tok]
+    topk = h["topk"][:n_tok]
+    grad = h["grad"][:n_tok]
+    R = n_tok * k
+    pre, dy = h["pre"][:R], h["dy"][:R]
+    t0 = time.perf_counter()
+    plan = route_plan(topk, E, A)
+    packed = nvfp4.pack_rows(x)
+    receive.direct_receive(packed, H, topk, E, A)
+    d, s = mxfp8.pack_rows(x)
+    mxfp8.grouped_receive(d, s, plan["src_row"])
+    nvfp4.unpack_rows(packed, H, plan["src_row"][plan["src_row"] >= 0])
+    pg = nvfp4.pack_rows(grad, sr_seed=1234)
+    receive.direct_receive(pg, H, topk, E, A)
+    counts = plan["counts"]
+    dx = dswiglu.dswiglu(pre, dy)
+    dswiglu.fc1_grad_quant(dx, counts, dswiglu.expert_amax(dx, counts))
+    dt = time.perf_counter() - t0
+    r_cap = plan["src_row"].shape[0]
+    total = sum(algorithmic_bytes(n_tok, H, k, E, r_cap, R, R, F).values())
+    return dict(value=round(total / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"first {n_tok} tokens of the workload (their routing, gradient rows and "
+                       f"{R} grouped dSwiGLU rows); {dt:.1f} s single-threaded numpy")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_token_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_label):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel_label)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
+                                   "(multi-GPU expert-parallel transport is not part of it)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    inp = make_inputs(dev)
+    step = Step(inp)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    # the timed region: K replays of one captured step (no host work per kernel)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    # per-call durations: HIP events on the launch stream around every call of
+    # eager steps (each preceded by the GPU-side fill described in Step.run)
+    n = len(step.names)
+    reps = max(5, min(args.steps, 50))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+          for _ in range(reps)]
+    for r in range(reps):
+        step.run(ev[r])
+    torch.cuda.synchronize()
+    per_ms = {name: float(np.mean([ev[r][j][0].elapsed_time(ev[r][j][1]) for r in range(reps)]))
+              for j, name in enumerate(step.names)}
+    T, H, k, E, R, F = (inp[s] for s in ("T", "H", "k", "E", "R", "F"))
+    by = algorithmic_bytes(T, H, k, E, step.r_cap, R, R, F)
+    total = sum(by.values())
+    value = total / (ms_step / 1e3) / 1e9
+    kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=by[nm], gbs=round(by[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
+                        frac=round(by[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
+    dom = kernels[DOMINANT]
+    traffic = traffic_from_profile("k_nvfp4_receive")
+    roofline = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dom["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="k_nvfp4_receive (one-pass NVFP4 direct receive, rowwise + RHT columnwise)",
+                    bytes_per_launch=by[DOMINANT], ms_per_launch=dom["ms"])
+    out = {
+        "metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->nvfp4/mxfp8", "data": "synthetic",
+        "config": {"workload": "dispatch-4096x4096-e8-top2-zipf1.2 (+ SR combine-bwd grads, grouped dSwiGLU ffn 2048)",
+                   "tokens": T, "hidden": H, "experts": E, "top_k": k, "alignment": inp["A"],
+                   "bytes_per_step": total, "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    else:
+        out["cpu_baseline"] = None
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -192,6 +192,24 @@ int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t h
                                 uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                 void* stream);
 
+/* The two halves of ep_nvfp4_direct_receive, for callers that schedule them
+ * separately (e.g. to reuse D_e, or to time the one-pass kernel alone):
+ *   ep_nvfp4_expert_scale: col_scale[e] = D_e = 4 * max t over expert e's rows
+ *     (0 if empty), reading only the 4-byte token scales (no amax pass);
+ *   ep_nvfp4_direct_receive_scaled: the one-pass rowwise + columnwise kernel
+ *     with D_e taken from col_scale (each a power of two, or 0 for an empty
+ *     expert).  Arguments and layouts as in ep_nvfp4_direct_receive; col_codes,
+ *     col_scales and col_scale are required here. */
+int32_t ep_nvfp4_expert_scale(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                              int64_t r_cap, const int32_t* offsets, const int32_t* src_row, float* col_scale,
+                              void* stream);
+int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                       int64_t num_experts, int64_t r_cap,
+                                       const int32_t* offsets, const int32_t* src_row,
+                                       uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                       uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
+                                       void* stream);
+
 /* MXFP8 receive (P2, description and review comments: received data and block
  * scales are returned per expert, grouped, with 128-aligned slots there --
  * here any multiple of 16): grouped row g copies token src_row[g]'s data row

@@ -41,6 +41,8 @@ _SIGS = {
     "ep_nvfp4_unpack": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "ep_route_plan": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "ep_nvfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_nvfp4_expert_scale": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "ep_nvfp4_direct_receive_scaled": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -179,9 +181,10 @@ def ep_mxfp8_pack(x, out=None):
 
 
 # ------------------------------------------------------------------ routing / receive
-def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None, workspace=None):
+def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None, workspace=None, out=None):
     """Routing plan of topk_idx [T, k] (int32 or int64): dict of counts, offsets,
-    dst_row, src_row (device int32), d_error (device int32 [1]) and r_cap."""
+    dst_row, src_row (device int32), d_error (device int32 [1]) and r_cap.
+    ``out``: a plan returned earlier for the same sizes, refilled in place."""
     dev = _dev(topk_idx)
     if topk_idx.dtype not in (torch.int32, torch.int64):
         raise TypeError("topk_idx must be int32 or int64")
@@ -191,10 +194,17 @@ def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None,
     cap = ep_route_capacity(t, k, num_experts, alignment)
     r_cap = cap if r_cap is None else r_cap
     i32 = dict(dtype=torch.int32, device=dev)
-    counts = torch.empty(num_experts, **i32)
-    offsets = torch.empty(num_experts + 1, **i32)
-    dst_row = torch.empty((t, k), **i32)
-    src_row = torch.empty(r_cap, **i32)
+    if out is not None:
+        counts, offsets, dst_row, src_row = out["counts"], out["offsets"], out["dst_row"], out["src_row"]
+        if d_error is None:
+            d_error = out["d_error"]
+        if src_row.numel() != r_cap or counts.numel() != num_experts:
+            raise ValueError("out plan was made for other sizes")
+    else:
+        counts = torch.empty(num_experts, **i32)
+        offsets = torch.empty(num_experts + 1, **i32)
+        dst_row = torch.empty((t, k), **i32)
+        src_row = torch.empty(r_cap, **i32)
     if d_error is None:
         d_error = torch.zeros(1, **i32)
     wsb = lib().ep_route_workspace_bytes(t, k, num_experts)
@@ -232,6 +242,33 @@ def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
             _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _ptr(out.get("col_scale")),
             _stream(dev)), "ep_nvfp4_direct_receive")
+    return out
+
+
+def ep_nvfp4_expert_scale(packed, hidden, plan, col_scale=None):
+    """D_e = 4 * max t over each expert's rows -> float32 [E] (the first half of the receive)."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    e = plan["num_experts"]
+    if col_scale is None:
+        col_scale = torch.empty(e, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_expert_scale(_ptr(packed), packed.shape[0], hidden, e, plan["r_cap"],
+                                           _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(col_scale),
+                                           _stream(dev)), "ep_nvfp4_expert_scale")
+    return col_scale
+
+
+def ep_nvfp4_direct_receive_scaled(packed, hidden, plan, out):
+    """The one-pass receive kernel alone, with out["col_scale"] already holding D_e."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_direct_receive_scaled(
+            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _stream(dev)),
+            "ep_nvfp4_direct_receive_scaled")
     return out
 
 

@@ -287,29 +287,65 @@ __global__ __launch_bounds__(256) void k_nvfp4_receive(const uint8_t* __restrict
 
 using namespace mtb;
 
+static int32_t receive_check(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                             int64_t r_cap, const int32_t* offsets, const int32_t* src_row) {
+  if (tokens < 0 || r_cap < 0 || num_experts < 1 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
+  if (tokens >= INT32_MAX / 4 || r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
+  if (!offsets || !src_row) return EP_ERR_NULL;
+  if (tokens > 0 && !packed) return EP_ERR_NULL;
+  return EP_OK;
+}
+
+MTB_EXPORT int32_t ep_nvfp4_expert_scale(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                                         int64_t r_cap, const int32_t* offsets, const int32_t* src_row,
+                                         float* col_scale, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!col_scale) return EP_ERR_NULL;
+  const int H = (int)hidden;
+  hipLaunchKernelGGL(k_expert_scale, dim3((unsigned)num_experts), dim3(1024), 0, (hipStream_t)stream, packed,
+                     (int)tokens, H, 9 * H / 16 + 4, offsets, src_row, col_scale);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                                  int64_t num_experts, int64_t r_cap, const int32_t* offsets,
+                                                  const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                                  float* row_t, uint8_t* col_codes, uint8_t* col_scales,
+                                                  const float* col_scale, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale) return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  dim3 grid((unsigned)((H + kTileCols - 1) / kTileCols), (unsigned)((r_cap + kTileRows - 1) / kTileRows));
+  hipLaunchKernelGGL(k_nvfp4_receive<true>, grid, dim3(256), 0, (hipStream_t)stream, packed, (int)tokens, H,
+                     9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes, row_scales, row_t,
+                     col_codes, col_scales, col_scale);
+  return launch_status();
+}
+
 MTB_EXPORT int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
                                            int64_t r_cap, const int32_t* offsets, const int32_t* src_row,
                                            uint8_t* row_codes, uint8_t* row_scales, float* row_t,
                                            uint8_t* col_codes, uint8_t* col_scales, float* col_scale, void* stream) {
-  if (tokens < 0 || r_cap < 0 || num_experts < 1 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
-  if (tokens >= INT32_MAX / 4 || r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
-  if (!offsets || !src_row || !row_codes || !row_scales || !row_t) return EP_ERR_NULL;
-  if (tokens > 0 && !packed) return EP_ERR_NULL;
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t) return EP_ERR_NULL;
   const bool col = col_codes != nullptr;
   if (col && (!col_scales || !col_scale)) return EP_ERR_NULL;
-  if (r_cap == 0) return EP_OK;
-  hipStream_t s = (hipStream_t)stream;
-  const int H = (int)hidden, T = (int)tokens, E = (int)num_experts;
-  const int row_bytes = 9 * H / 16 + 4;
-  if (col)
-    hipLaunchKernelGGL(k_expert_scale, dim3((unsigned)E), dim3(1024), 0, s, packed, T, H, row_bytes, offsets, src_row,
-                       col_scale);
+  if (r_cap == 0) return col ? ep_nvfp4_expert_scale(packed, tokens, hidden, num_experts, r_cap, offsets, src_row,
+                                                       col_scale, stream) : EP_OK;
+  if (col) {
+    st = ep_nvfp4_expert_scale(packed, tokens, hidden, num_experts, r_cap, offsets, src_row, col_scale, stream);
+    if (st != EP_OK) return st;
+    return ep_nvfp4_direct_receive_scaled(packed, tokens, hidden, num_experts, r_cap, offsets, src_row, row_codes,
+                                          row_scales, row_t, col_codes, col_scales, col_scale, stream);
+  }
+  const int H = (int)hidden;
   dim3 grid((unsigned)((H + kTileCols - 1) / kTileCols), (unsigned)((r_cap + kTileRows - 1) / kTileRows));
-  if (col)
-    hipLaunchKernelGGL(k_nvfp4_receive<true>, grid, dim3(256), 0, s, packed, T, H, row_bytes, offsets, E, src_row,
-                       (int)r_cap, row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
-  else
-    hipLaunchKernelGGL(k_nvfp4_receive<false>, grid, dim3(256), 0, s, packed, T, H, row_bytes, offsets, E, src_row,
-                       (int)r_cap, row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
+  hipLaunchKernelGGL(k_nvfp4_receive<false>, grid, dim3(256), 0, (hipStream_t)stream, packed, (int)tokens, H,
+                     9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes, row_scales, row_t,
+                     col_codes, col_scales, col_scale);
   return launch_status();
 }

@@ -1,0 +1,201 @@
+"""GPU parity at the full workload sizes, on sampled outputs the oracle computes
+one by one (plus properties that hold at any size).  The oracle only ever sees
+the seeded inputs (never a GPU output), except stage 2 of the dSwiGLU check,
+which by definition runs the oracle quantizer on the GPU's own dX and amax."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_token_block_amd as mtb
+import workloads
+from oracle import formats as F
+from oracle import nvfp4 as onv
+from oracle import mxfp8 as omx
+from oracle import receive as orecv
+from oracle import dswiglu as odsw
+from oracle.routing import route_plan as o_route
+
+from gpu_util import require_gpu, bf16_dev, host, i32_dev, assert_bytes_equal, tolerant_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _token_t(x_bits):
+    """Oracle token scales of all rows (needs only the row maxima)."""
+    amax = np.abs(F.bf16_to_f32(x_bits)).max(axis=1).astype(np.float64)
+    return np.ldexp(1.0, onv.token_scale_exponent(amax))
+
+
+def _check_dispatch(dev, w, name, sr=None, rng_seed=0, n_rows=96, n_col_samples=12):
+    T, H = w.x_bits.shape
+    E, A = w.num_experts, w.alignment
+    print(f"{name}: T={T} H={H} E={E} k={w.topk_idx.shape[1]}", flush=True)
+    rng = np.random.default_rng(rng_seed)
+    x = bf16_dev(w.x_bits, dev)
+    if sr is None:
+        packed = mtb.ep_nvfp4_pack(x)
+        opack = lambda rows: onv.pack_rows(w.x_bits[rows])
+    else:
+        st = torch.tensor([sr[0], sr[1]], dtype=torch.int64, device=dev)
+        packed = mtb.ep_nvfp4_pack(x, mtb.EP_ROUND_SR_ELEMENT, st)
+        # counter positions follow the source row: pack the sampled rows at their own offsets
+        opack = lambda rows: np.concatenate([onv.pack_rows(w.x_bits[r:r + 1], sr_seed=sr[0],
+                                                           sr_counter_base=sr[1] + int(r) * H) for r in rows])
+    # pack: sampled rows (with the extremes of the t range among them)
+    t_all = _token_t(w.x_bits)
+    rows = np.unique(np.concatenate([rng.integers(0, T, n_rows), [int(np.argmin(t_all)), int(np.argmax(t_all)), T - 1]]))
+    assert_bytes_equal(host(packed[torch.from_numpy(rows).to(dev)]), opack(rows), f"{name} pack (sampled rows)")
+    # routing: the whole plan
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), E, A)
+    want = o_route(w.topk_idx, E, A)
+    for key in ("counts", "offsets", "dst_row", "src_row"):
+        assert_bytes_equal(host(plan[key]), want[key], f"{name} route {key}")
+    got = mtb.ep_nvfp4_direct_receive(packed, H, plan)
+    off = want["offsets"].astype(np.int64)
+    src = want["src_row"].astype(np.int64)
+    # D_e from the oracle's token scales of all rows
+    D = np.array([orecv.expert_decode_scale(t_all[src[off[e]:off[e] + want["counts"][e]]]) for e in range(E)],
+                 dtype=np.float32)
+    assert_bytes_equal(host(got["col_scale"]).view(np.uint32), D.view(np.uint32), f"{name} D_e")
+    # rowwise: sampled grouped rows (padding rows among them)
+    g = np.unique(np.concatenate([rng.integers(0, off[-1], 256), off[1:] - 1]))
+    gs = torch.from_numpy(g).to(dev)
+    rc, rsc, rt = host(got["row_codes"][gs]), host(got["row_scales"][gs]), host(got["row_t"][gs])
+    ok = src[g] >= 0
+    exp_rows = np.zeros((g.size, onv.packed_row_bytes(H)), dtype=np.uint8)
+    exp_rows[ok] = opack(src[g][ok])
+    assert_bytes_equal(rc, exp_rows[:, : H // 2], f"{name} rowwise codes (sampled)")
+    assert_bytes_equal(rsc, exp_rows[:, H // 2: H // 2 + H // 16], f"{name} rowwise scales (sampled)")
+    assert_bytes_equal(rt.view(np.uint32), exp_rows[:, H // 2 + H // 16:].copy().view(np.uint32).reshape(-1),
+                       f"{name} row t (sampled)")
+    # columnwise: sampled (expert, 16-row blocks, columns) windows, incl. each expert's last block
+    cc_all = got["col_codes"]
+    cs_all = got["col_scales"]
+    nonempty = [e for e in range(E) if want["counts"][e] > 0]
+    picks = []
+    for e in nonempty:
+        nb = int(off[e + 1] - off[e]) // 16
+        picks.append((e, nb - 1))
+    for _ in range(n_col_samples):
+        e = int(rng.choice(nonempty))
+        picks.append((e, int(rng.integers(0, int(off[e + 1] - off[e]) // 16))))
+    for e, b in picks:
+        p = int(off[e + 1] - off[e])
+        c0 = int(rng.integers(0, H // 64)) * 64
+        b0, b1 = max(0, b - 1), b + 1
+        blk_rows = src[off[e] + 16 * b0: off[e] + 16 * b1]
+        okr = blk_rows >= 0
+        sub = np.zeros((blk_rows.size, onv.packed_row_bytes(H)), dtype=np.uint8)
+        sub[okr] = opack(blk_rows[okr])
+        local = dict(src_row=np.where(okr, np.arange(blk_rows.size), -1), offsets=np.array([0]))
+        codes, sc = orecv.columnwise_sample(sub, H, local, 0, c0, c0 + 64, 0, b1 - b0, D[e])
+        # the GPU's [H, P/2] matrix of expert e, columns c0..c0+64, bytes of blocks b0..b1
+        base = H * int(off[e]) // 2
+        idx = (base + (np.arange(c0, c0 + 64)[:, None] * (p // 2)) + np.arange(8 * b0, 8 * b1)[None, :]).reshape(-1)
+        gcodes = F.unpack_nibbles(host(cc_all[torch.from_numpy(idx).to(dev)]).reshape(64, -1))
+        sbase = H * int(off[e]) // 16
+        sidx = (sbase + np.arange(c0, c0 + 64)[:, None] * (p // 16) + np.arange(b0, b1)[None, :]).reshape(-1)
+        gsc = host(cs_all[torch.from_numpy(sidx).to(dev)]).reshape(64, -1)
+        assert_bytes_equal(gsc, sc, f"{name} columnwise scales e={e} blocks {b0}..{b1} cols {c0}")
+        assert_bytes_equal(gcodes, codes, f"{name} columnwise codes e={e} blocks {b0}..{b1} cols {c0}")
+    return packed, plan, want
+
+
+def test_config2_nvfp4_and_mxfp8(dev):
+    w = workloads.config2()
+    _, plan, want = _check_dispatch(dev, w, "config2", rng_seed=2)
+    assert want["counts"][7] == 0
+    data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
+    wd, ws = omx.pack_rows(w.x_bits)
+    assert_bytes_equal(host(data), wd, "config2 MXFP8 data")
+    assert_bytes_equal(host(scales), ws, "config2 MXFP8 scales")
+    gd, gs = mtb.ep_mxfp8_direct_receive(data, scales, plan)
+    ed, es = omx.grouped_receive(wd, ws, want["src_row"])
+    off = int(want["offsets"][-1])
+    assert_bytes_equal(host(gd)[:off], ed[:off], "config2 MXFP8 grouped data")
+    assert_bytes_equal(host(gs)[:off], es[:off], "config2 MXFP8 grouped scales")
+
+
+def test_config3_dsv3_share(dev):
+    w = workloads.config3()
+    packed, plan, want = _check_dispatch(dev, w, "config3", rng_seed=3)
+    # unpack of the received rows (grouped order) on sampled rows
+    off = int(want["offsets"][-1])
+    src = want["src_row"][:off]
+    rng = np.random.default_rng(33)
+    g = rng.integers(0, off, 128)
+    un = mtb.ep_nvfp4_unpack(packed, 7168, src_row=i32_dev(src[g], dev))
+    assert_bytes_equal(host(un), onv.unpack_rows(onv.pack_rows(w.x_bits[np.maximum(src[g], 0)]), 7168,
+                                                 np.where(src[g] >= 0, np.arange(g.size), -1)),
+                       "config3 unpack (sampled grouped rows)")
+
+
+def test_config4_sr_combine_backward(dev):
+    w = workloads.config4()
+    _check_dispatch(dev, w, "config4", sr=(w.sr_seed, w.sr_counter_base), rng_seed=4, n_rows=48)
+
+
+def test_config5_dswiglu(dev):
+    w = workloads.config5()
+    out = mtb.dswiglu_nvfp4_quant(bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    dx = host(out["dx"])
+    am = host(out["amax"])
+    off = odsw.expert_offsets(w.counts)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, dx.shape[0], 512), off[1:-1], off[2:] - 1]))
+    rows = rows[rows < dx.shape[0]]
+    want = odsw.dswiglu(w.preact_bits[rows], w.dy_bits[rows])
+    ulp = np.abs(dx[rows].view(np.int16).astype(np.int64) - want.view(np.int16).astype(np.int64))
+    assert ulp.max() <= 1, f"config5 dX differs by {ulp.max()} BF16 ulp"
+    assert (ulp > 0).mean() < 1e-3
+    # the epilogue amax is exactly max |dX| of the GPU's BF16 dX, 0 for the empty expert
+    assert_bytes_equal(am.view(np.uint32), odsw.expert_amax(dx, w.counts).view(np.uint32), "config5 amax")
+    assert am[0] == 0.0
+    # stage 2 on the GPU's own dX: rowwise on sampled rows, columnwise on sampled blocks
+    D = (am / np.float32(2688.0)).astype(np.float32)
+    assert_bytes_equal(host(out["row_scale"]).view(np.uint32), D.view(np.uint32), "config5 D_row")
+    assert_bytes_equal(host(out["col_scale"]).view(np.uint32), (np.float32(4) * D).view(np.uint32), "config5 D_col")
+    sub_counts = np.zeros(8, dtype=np.int32)
+    rc = F.unpack_nibbles(host(out["row_codes"])[rows])
+    rs = host(out["row_scales"])[rows]
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    wc = np.zeros_like(rc); wsc = np.zeros_like(rs)
+    for e in np.unique(e_of):
+        sel = e_of == e
+        c, s, _ = odsw.rowwise_quant(dx[rows[sel]], np.array([sel.sum()]), am[e:e + 1])
+        wc[sel] = F.unpack_nibbles(c)
+        wsc[sel] = s
+    tolerant_codes(rc, wc, rs, wsc, "config5 rowwise (sampled rows)")
+    poff = odsw.expert_offsets(w.counts, 16)
+    W = 4096
+    gc_all = host(out["col_codes"])
+    gs_all = host(out["col_scales"])
+    n_bad = 0
+    for e in range(8):
+        c = int(w.counts[e])
+        if c == 0:
+            continue
+        p = int(poff[e + 1] - poff[e])
+        nb = p // 16
+        for b in sorted({0, nb - 1, int(rng.integers(0, nb))}):
+            c0 = int(rng.integers(0, W // 64)) * 64
+            r0 = off[e] + 16 * b
+            nreal = max(0, min(16, c - 16 * b))
+            vals = np.zeros((16, 64))
+            vals[:nreal] = F.bf16_to_f32(dx[r0:r0 + nreal, c0:c0 + 64]).astype(np.float64)
+            from oracle.rht import rht16
+            y = rht16(vals.T.reshape(64, 1, 16))
+            codes, sc = orecv.quantize_blocks(y, np.float32(4) * D[e], "fp32")
+            base = W * int(poff[e]) // 2
+            idx = (base + np.arange(c0, c0 + 64)[:, None] * (p // 2) + np.arange(8 * b, 8 * b + 8)[None, :])
+            gcodes = F.unpack_nibbles(gc_all[idx.reshape(-1)].reshape(64, 8))
+            sidx = W * int(poff[e]) // 16 + np.arange(c0, c0 + 64) * (p // 16) + b
+            n_bad += tolerant_codes(gcodes, codes.reshape(64, 16), gs_all[sidx].reshape(64, 1), sc.reshape(64, 1),
+                                    f"config5 columnwise e={e} b={b}", frac=1e-2)[0]
+    assert n_bad <= 2
