@@ -43,6 +43,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
     p.add_argument("--json-out", default=None)
+    p.add_argument("--only", default=None,
+                   help="profiling aid: run only this call of the path (or 'copy': a 1 GiB device copy, the "
+                        "reference for memory counters) --steps times, eagerly, and print what ran")
+    p.add_argument("--workload", default="dispatch", choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5"],
+                   help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
+                        "configuration's own path, for per-kernel figures")
     return p.parse_args()
 
 
@@ -131,7 +137,7 @@ class Step:
         src = self.plan["src_row"].cpu().numpy()
         self.src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
         self.counts = self.plan["counts"]
-        self.dsw_ws = torch.empty(m.lib().dswiglu_workspace_bytes(E), **u8)
+        self.dsw_ws = torch.empty(m.lib().dswiglu_workspace_bytes(R, E), **u8)
         cap = R + 15 * E
         f32 = dict(dtype=torch.float32, device=dev)
         self.dsw = dict(dx=torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev), amax=torch.empty(E, **f32),
@@ -161,6 +167,37 @@ class Step:
             lambda: m.dswiglu_nvfp4_quant(i["preact"], i["dy"], self.counts, out=self.dsw, workspace=self.dsw_ws),
         ]
 
+    def run_concurrent(self):
+        """The same calls as ``run`` as four dependent chains on their own streams
+        (default priority), joined back into the calling stream: the NVFP4 dispatch
+        chain, the MXFP8 chain, the SR combine-backward chain and the dSwiGLU chain
+        wait only for what they read (the route plan)."""
+        import torch
+        c = self.calls()
+        main = torch.cuda.current_stream()
+        if not hasattr(self, "side"):
+            self.side = [torch.cuda.Stream() for _ in range(3)]
+        for st in self.side:
+            st.wait_stream(main)
+        with torch.cuda.stream(self.side[0]):
+            c[7]()                                   # SR pack of the gradient rows (independent of routing)
+        with torch.cuda.stream(self.side[1]):
+            c[4]()                                   # MXFP8 pack
+        c[0]()                                       # route plan
+        routed = torch.cuda.Event()
+        routed.record(main)
+        for st in self.side:
+            st.wait_event(routed)
+        with torch.cuda.stream(self.side[0]):
+            c[8](); c[9]()                           # expert scale + receive of the gradient rows
+        with torch.cuda.stream(self.side[1]):
+            c[5]()                                   # MXFP8 receive
+        with torch.cuda.stream(self.side[2]):
+            c[10]()                                  # dSwiGLU + FC1-grad quantization (needs the counts)
+        c[1](); c[2](); c[3](); c[6]()              # NVFP4 pack, expert scale, receive, unpack
+        for st in self.side:
+            main.wait_stream(st)
+
     def run(self, events=None):
         calls = self.calls()
         if events is not None:
@@ -168,6 +205,104 @@ class Step:
             # host enqueues the whole step, so each event pair brackets GPU time only
             self.flush.fill_(1.0)
         for j, c in enumerate(calls):
+            if events is not None:
+                events[j][0].record()
+            c()
+            if events is not None:
+                events[j][1].record()
+
+
+# ---------------------------------------------------------------------------- per-config paths
+class ConfigStep:
+    """The path of one configuration on its own inputs (for per-kernel figures):
+    cfg1/cfg3: route -> pack -> expert scale -> direct receive -> unpack of the grouped rows;
+    cfg2: route -> pack -> expert scale -> direct receive -> MXFP8 pack -> MXFP8 receive;
+    cfg4: route -> SR pack -> expert scale -> direct receive; cfg5: dSwiGLU + FC1-grad quant."""
+
+    def __init__(self, which, dev):
+        import torch
+        import moe_token_block_amd as m
+        import workloads
+        self.m = m
+        n = int(which[3:])
+        w = workloads.CONFIGS[n]()
+        self.w, self.n = w, n
+        u8 = dict(dtype=torch.uint8, device=dev)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.names, self.calls_, self.bytes = [], [], {}
+        if n == 5:
+            T, F, E = w.preact_bits.shape[0], w.dy_bits.shape[1], len(w.counts)
+            self.pre, self.dy = bf(w.preact_bits), bf(w.dy_bits)
+            self.counts = torch.from_numpy(w.counts).to(dev)
+            cap = T + 15 * E
+            f32 = dict(dtype=torch.float32, device=dev)
+            self.out = dict(dx=torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev), amax=torch.empty(E, **f32),
+                            row_codes=torch.empty((T, F), **u8), row_scales=torch.empty((T, 2 * F // 16), **u8),
+                            row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
+                            col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
+            self.ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
+            self._add("dswiglu_nvfp4_quant", lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out,
+                                                                           workspace=self.ws),
+                      T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16) + 2 * E * 4)
+            self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)
+            return
+        T, H = w.x_bits.shape
+        k, E, A = w.topk_idx.shape[1], w.num_experts, w.alignment
+        R = T * k
+        self.x = bf(w.x_bits)
+        self.topk = torch.from_numpy(w.topk_idx).to(dev)
+        r_cap = m.ep_route_capacity(T, k, E, A)
+        self.ws = torch.empty(max(m.lib().ep_route_workspace_bytes(T, k, E), 4), **u8)
+        self.derr = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.plan = m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws)
+        self.packed = torch.empty((T, row_bytes(H)), **u8)
+        self.recv = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
+                         row_t=torch.empty(r_cap, dtype=torch.float32, device=dev),
+                         col_codes=torch.empty(r_cap * H // 2, **u8), col_scales=torch.empty(r_cap * H // 16, **u8),
+                         col_scale=torch.empty(E, dtype=torch.float32, device=dev))
+        b = algorithmic_bytes(T, H, k, E, r_cap, R, R, 0)
+        self._add("route_plan", lambda: m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws,
+                                                        out=self.plan), b["route_plan"])
+        if n == 4:
+            self.sr = torch.tensor([w.sr_seed, w.sr_counter_base], dtype=torch.int64, device=dev)
+            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(self.x, m.EP_ROUND_SR_ELEMENT, self.sr, out=self.packed),
+                      b["nvfp4_pack_sr"])
+        else:
+            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(self.x, out=self.packed), b["nvfp4_pack"])
+        self._add("nvfp4_expert_scale", lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan,
+                                                                        col_scale=self.recv["col_scale"]),
+                  b["nvfp4_expert_scale"])
+        self._add("nvfp4_direct_receive", lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
+                  b["nvfp4_direct_receive"])
+        if n == 2:
+            self.mx = torch.empty(T * H + T * H // 32, **u8)
+            self.mx_out = (torch.empty((r_cap, H), **u8), torch.empty((r_cap, H // 32), **u8))
+            self._add("mxfp8_pack", lambda: m.ep_mxfp8_pack(self.x, out=self.mx), b["mxfp8_pack"])
+            self._add("mxfp8_receive", lambda: m.ep_mxfp8_direct_receive(
+                self.mx[: T * H].view(T, H), self.mx[T * H:].view(T, H // 32), self.plan, out=self.mx_out),
+                b["mxfp8_receive"])
+        if n in (1, 3):
+            off = self.plan["offsets"].cpu().numpy()
+            src = self.plan["src_row"].cpu().numpy()
+            self.src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
+            self.unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            self._add("nvfp4_unpack", lambda: m.ep_nvfp4_unpack(self.packed, H, src_row=self.src_valid,
+                                                                out=self.unpacked), b["nvfp4_unpack"])
+        self.desc = dict(workload=w.name, tokens=T, hidden=H, experts=E, top_k=k, alignment=A)
+
+    def _add(self, name, fn, nbytes):
+        self.names.append(name)
+        self.calls_.append(fn)
+        self.bytes[name] = nbytes
+
+    def calls(self):
+        return self.calls_
+
+    def run(self, events=None):
+        if events is not None:
+            self.flush.fill_(1.0)
+        for j, c in enumerate(self.calls_):
             if events is not None:
                 events[j][0].record()
             c()
@@ -229,19 +364,10 @@ def traffic_from_profile(kernel_label):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
-                                   "(multi-GPU expert-parallel transport is not part of it)"}))
-        sys.exit(2)
+def time_step(step, args):
+    """K graph replays of one captured step (the timed region), then per-call HIP
+    events in eager passes that each start with a 1 GiB fill (see Step.run)."""
     import torch
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    inp = make_inputs(dev)
-    step = Step(inp)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -251,11 +377,16 @@ def main():
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         step.run()
+        if hasattr(step, "run_concurrent"):
+            step.run_concurrent()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step.run()
+        if hasattr(step, "run_concurrent"):
+            step.run_concurrent()
+        else:
+            step.run()
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -276,6 +407,82 @@ def main():
     torch.cuda.synchronize()
     per_ms = {name: float(np.mean([ev[r][j][0].elapsed_time(ev[r][j][1]) for r in range(reps)]))
               for j, name in enumerate(step.names)}
+    return ms_step, per_ms
+
+
+def main_config(args, dev):
+    import torch
+    step = ConfigStep(args.workload, dev)
+    ms_step, per_ms = time_step(step, args)
+    total = sum(step.bytes.values())
+    kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=step.bytes[nm],
+                        gbs=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
+                        frac=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
+    dom = max(step.names, key=lambda nm: per_ms[nm])
+    out = {"metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
+           "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16->nvfp4/mxfp8", "data": "synthetic",
+           "config": dict(step.desc, bytes_per_step=total),
+           "roofline": dict(bound="hbm", achieved=kernels[dom]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                            frac=kernels[dom]["frac"], traffic=None, kernel=dom, bytes_per_launch=step.bytes[dom],
+                            ms_per_launch=kernels[dom]["ms"]),
+           "kernels": kernels, "cpu_baseline": None}
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def main_only(args, dev):
+    """Repeat one call of a path (or a 1 GiB copy) for counter collection."""
+    import torch
+    if args.only == "copy":
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                          "launches": args.steps}))
+        return
+    step = ConfigStep(args.workload, dev) if args.workload != "dispatch" else Step(make_inputs(dev))
+    for _ in range(2):
+        step.run()
+    torch.cuda.synchronize()
+    j = step.names.index(args.only)
+    call = step.calls()[j]
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    if hasattr(step, "bytes"):
+        nbytes = step.bytes[args.only]
+    else:
+        i = step.inp
+        nbytes = algorithmic_bytes(i["T"], i["H"], i["k"], i["E"], step.r_cap, i["R"], i["R"], i["F"])[args.only]
+    print(json.dumps({"only": args.only, "workload": args.workload, "launches": args.steps,
+                      "algorithmic_bytes_per_launch": nbytes}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
+                                   "(multi-GPU expert-parallel transport is not part of it)"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.only is not None:
+        return main_only(args, dev)
+    if args.workload != "dispatch":
+        return main_config(args, dev)
+    inp = make_inputs(dev)
+    step = Step(inp)
+    ms_step, per_ms = time_step(step, args)
     T, H, k, E, R, F = (inp[s] for s in ("T", "H", "k", "E", "R", "F"))
     by = algorithmic_bytes(T, H, k, E, step.r_cap, R, R, F)
     total = sum(by.values())

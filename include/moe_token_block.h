@@ -97,8 +97,8 @@ size_t ep_route_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_exper
  * caller can apply the same transform to the other wgrad operand. */
 uint32_t ep_rht_sign_mask(void);
 
-/* Workspace bytes dswiglu_nvfp4_quant needs. */
-size_t dswiglu_workspace_bytes(int64_t num_experts);
+/* Workspace bytes dswiglu_nvfp4_quant needs (offsets + one word per token row). */
+size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts);
 
 /* ---------------------------------------------------------------- pack */
 
@@ -184,7 +184,7 @@ int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, i
  *   scales an [hidden, P_e/16] matrix at byte hidden*off_e/16 of col_scales
  *   (P_e = off_{e+1} - off_e); col_codes/col_scales need hidden*r_cap/2 and
  *   hidden*r_cap/16 bytes.
- *   Requires hidden a positive multiple of 128 when col_codes != NULL, else of 64. */
+ *   Requires hidden a positive multiple of 64 and 1 <= num_experts <= 1024. */
 int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden,
                                 int64_t num_experts, int64_t r_cap,
                                 const int32_t* offsets, const int32_t* src_row,
@@ -241,7 +241,7 @@ int32_t ep_mxfp8_direct_receive(const uint8_t* data, const uint8_t* scales, int6
  *   2*ffn*poff_e/2 (poff = padded offsets) and its scales [2*ffn, P_e/16] at
  *   byte 2*ffn*poff_e/16; col_codes and col_scales need
  *   2*ffn*(tokens + 15*E)/2 and 2*ffn*(tokens + 15*E)/16 bytes.
- *   workspace: device memory of dswiglu_workspace_bytes(E) bytes.
+ *   workspace: device memory of dswiglu_workspace_bytes(tokens, E) bytes.
  *   Requires ffn a positive multiple of 64. */
 int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
                             const int32_t* counts, int64_t num_experts,

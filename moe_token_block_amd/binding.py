@@ -35,7 +35,7 @@ _SIGS = {
     "ep_route_capacity": (_I64, [_I64, _I64, _I64, _I64]),
     "ep_route_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "ep_rht_sign_mask": (ctypes.c_uint32, []),
-    "dswiglu_workspace_bytes": (_SZ, [_I64]),
+    "dswiglu_workspace_bytes": (_SZ, [_I64, _I64]),
     "ep_nvfp4_pack": (_I32, [_P, _I64, _I64, _P, _I32, _P, _P]),
     "ep_mxfp8_pack": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "ep_nvfp4_unpack": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
@@ -304,7 +304,7 @@ def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None):
                    row_codes=torch.empty((t, f), **u8), row_scales=torch.empty((t, 2 * f // 16), **u8),
                    row_scale=torch.empty(e, **f32), col_codes=torch.empty(2 * f * cap // 2, **u8),
                    col_scales=torch.empty(2 * f * cap // 16, **u8), col_scale=torch.empty(e, **f32))
-    wsb = lib().dswiglu_workspace_bytes(e)
+    wsb = lib().dswiglu_workspace_bytes(t, e)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):

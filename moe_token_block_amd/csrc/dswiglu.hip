@@ -4,12 +4,13 @@
 // post-RHT columnwise amax is bounded by 4x the rowwise amax, the separate
 // grouped amax pass is skipped).
 //
-// Launch 1 (setup): expert row offsets (plain and 16-padded) from the device
-//   counts into the workspace; amax zeroed (a fill, not a memset).
-// Launch 2 (epilogue): one wave per token row; per pair (a_j, b_j, dy_j):
+// Launch 1 (epilogue): one wave per token row; per pair (a_j, b_j, dy_j):
 //   s = sigmoid(a), da = dy*b*s*(1 + a*(1-s)), db = dy*a*s in FP32 -> BF16;
-//   the row's max |dX| (over the BF16 values) goes to amax[e] with an
-//   integer atomic max on the bit pattern (order-independent, deterministic).
+//   the row's max |dX| (over the BF16 values) goes to the workspace (one word
+//   per row: no atomics, no contention).
+// Launch 2 (reduce): one workgroup per expert: the expert row offsets (plain
+//   and 16-padded) from the device counts, amax_e = max over its rows, and
+//   D_row = amax/2688, D_col = 4 * D_row.
 // Launch 3 (quant): one workgroup per 256 padded rows x 128 columns, as the
 //   direct receive: thread (cg, m) owns 8 columns x one 16-row block; the
 //   rowwise operand (per-expert scale D_row = amax/2688) and the RHT
@@ -23,12 +24,11 @@ constexpr int kQTileRows = 256;
 constexpr int kQTileCols = 128;
 constexpr int kQBlocks = kQTileRows / 16;
 
-__global__ __launch_bounds__(1024) void k_dswiglu_setup(const int32_t* __restrict__ counts, int E, int T,
-                                                        int32_t* __restrict__ offs, int32_t* __restrict__ poffs,
-                                                        float* __restrict__ amax) {
-  // Counts are device data: they are clamped so that the experts never cover
-  // more than the T rows that exist (a running total above T is cut at T).
-  __shared__ int32_t a[1024], b[1024];
+// Inclusive prefix sums of the (clamped) counts and of their 16-padded sizes
+// into a[] and b[] (1024 entries, LDS); E <= 1024.  Counts are device data:
+// a running total above T is cut at T, so the experts never cover more rows
+// than exist.
+__device__ __forceinline__ void expert_prefix(const int32_t* counts, int E, int T, int32_t* a, int32_t* b) {
   const int tid = threadIdx.x;
   int c = tid < E ? max(counts[tid], 0) : 0;
   a[tid] = c;
@@ -40,6 +40,8 @@ __global__ __launch_bounds__(1024) void k_dswiglu_setup(const int32_t* __restric
     __syncthreads();
   }
   const int incl = min(a[tid], T), excl = min(a[tid] - c, T);
+  __syncthreads();
+  a[tid] = incl;
   b[tid] = (incl - excl + 15) / 16 * 16;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -48,14 +50,42 @@ __global__ __launch_bounds__(1024) void k_dswiglu_setup(const int32_t* __restric
     b[tid] += vb;
     __syncthreads();
   }
-  if (tid < E) {
-    offs[tid + 1] = incl;
-    poffs[tid + 1] = b[tid];
-    amax[tid] = 0.0f;
+}
+
+// One workgroup per expert.  Workgroup 0 also publishes the offsets.
+__global__ __launch_bounds__(1024) void k_dswiglu_reduce(const int32_t* __restrict__ counts, int E, int T,
+                                                         const uint32_t* __restrict__ rowmax,
+                                                         int32_t* __restrict__ offs, int32_t* __restrict__ poffs,
+                                                         float* __restrict__ amax, float* __restrict__ row_scale,
+                                                         float* __restrict__ col_scale) {
+  __shared__ int32_t a[1024], b[1024];
+  __shared__ uint32_t red[16];
+  const int tid = threadIdx.x, e = blockIdx.x;
+  expert_prefix(counts, E, T, a, b);
+  if (e == 0) {
+    if (tid < E) {
+      offs[tid + 1] = a[tid];
+      poffs[tid + 1] = b[tid];
+    }
+    if (tid == 0) {
+      offs[0] = 0;
+      poffs[0] = 0;
+    }
   }
+  const int r0 = e ? a[e - 1] : 0, r1 = a[e];
+  uint32_t m = 0;
+  for (int r = r0 + tid; r < r1; r += 1024) m = max(m, rowmax[r]);
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
   if (tid == 0) {
-    offs[0] = 0;
-    poffs[0] = 0;
+    uint32_t r = 0;
+    for (int i = 0; i < 16; ++i) r = max(r, red[i]);
+    float am = __uint_as_float(r);  // a BF16 value (max |dX|), 0 for an empty expert
+    float D = am / kTokenBound;     // fl32(amax / 2688)
+    amax[e] = am;
+    row_scale[e] = D;
+    col_scale[e] = 4.0f * D;        // = fl32(4 * amax / 2688) exactly
   }
 }
 
@@ -83,9 +113,8 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
 }
 
 __global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __restrict__ preact,
-                                                          const uint16_t* __restrict__ dy, int T, int F, int E,
-                                                          const int32_t* __restrict__ offs,
-                                                          uint16_t* __restrict__ dx, float* __restrict__ amax) {
+                                                          const uint16_t* __restrict__ dy, int T, int F,
+                                                          uint16_t* __restrict__ dx, uint32_t* __restrict__ rowmax) {
   const int lane = threadIdx.x & 63;
   const int r = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
   if (r >= T) return;
@@ -115,87 +144,102 @@ __global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __rest
     m = m > x ? m : x;
   }
   m = wave_max_u32(m);
-  // non-negative floats order like their bit patterns: an integer max is exact
-  if (lane == 0 && m && r < offs[E])
-    atomicMax(reinterpret_cast<unsigned int*>(amax) + expert_of(offs, E, r), m << 16);
+  // non-negative floats order like their bit patterns: the integer max is exact
+  if (lane == 0) rowmax[r] = m << 16;
 }
 
 // ------------------------------------------------------------------ grouped quant
-// fl32(x / c) for a general float c: split reciprocal (r_hi <= 1/c, the
-// non-negative residual by fma); the result can differ from the correctly
-// rounded quotient only when x/c lies within ~2^-45 (relative) of a float32
-// midpoint.  r_lo >= 0 keeps the sign of x = -0.
-struct GenQuot {
-  float r_hi, r_lo;
-};
-__device__ __forceinline__ GenQuot gen_split(float c) {
-  float e;
-  float r = rcp_below(c, e);
-  return GenQuot{r, e * r};
+// The FC1-gradient quantizer divides by a general FP32 decode scale D (and by
+// c = fl32(s*D) per block).  Each divisor is split as m * 2^k with m in
+// [1, 2); x/m is fma(x, r_hi, x*r_lo) with the split reciprocal of m, and 2^k
+// goes to the converter (or to an exact ldexp).  With a 24-bit m the split
+// reciprocal is within ~2^-45 of 1/m, so a quotient can differ from the
+// correctly rounded one only within that distance of a float32 midpoint.
+
+// x = m * 2^k, m in [1, 2), for any x > 0 (normal or subnormal).
+__device__ __forceinline__ float split_pow2(float x, int& k) {
+  int sub = 0;
+  if (x < 0x1p-126f) { x *= 0x1p64f; sub = 64; }
+  k = __builtin_amdgcn_frexp_expf(x) - 1 - sub;
+  return __builtin_amdgcn_frexp_mantf(x) * 2.0f;
 }
 
-// Scale code for a block max a with decode scale D (D > 0): E4M3(fl32(fl32(a/6)/D)).
-__device__ __forceinline__ uint32_t gen_scale_code(float a, float D) {
-  float pre = a / 6.0f;          // correctly rounded (IEEE division)
-  float y = pre / D;             // correctly rounded
+// Per-expert constants: D = m_D * 2^kD and the split reciprocal of m_D.
+struct DScale {
+  float D, r_hi, r_lo;
+  int kD;
+};
+__device__ __forceinline__ DScale dscale(float D) {
+  DScale d;
+  d.D = D;
+  d.kD = 0;
+  d.r_hi = d.r_lo = 0.0f;
+  if (D > 0.0f) {
+    float e;
+    float m = split_pow2(D, d.kD);
+    d.r_hi = rcp_below(m, e);
+    d.r_lo = e * d.r_hi;
+  }
+  return d;
+}
+
+// E4M3 code of fl32(fl32(a / 6) / D) for a block max a (D > 0).
+__device__ __forceinline__ uint32_t gen_scale_code(float a, const DScale& d) {
+  if (!(d.D > 0.0f)) return 0u;
+  bool tiny = a < 0x1p-100f;
+  float pre = div6(tiny ? a * 0x1p64f : a);                 // fl32(a/6) * 2^(64 if tiny)
+  float q = quot_apply(pre, d.r_hi, d.r_lo);                // ~ pre / m_D
+  float y = __builtin_ldexpf(q, -d.kD - (tiny ? 64 : 0));   // / 2^kD, exact unless it underflows
   return e4m3_encode(fminf(y, 448.0f));
 }
 
-// Codes of n values x[] with block scale code sc and decode scale D:
-// c = fl32(s*D), v = fl32(|x|/c), E2M1 RNE (the converter at scale 1).
+// Block parameters for codes of x / c, c = fl32(s * D): split reciprocal of
+// c's significand (times 2^P) and the converter scale 2^(kc + P).
 struct GenBlock {
-  float r_hi, r_lo;
-  bool zero, exact_div;
-  float c;
+  float r_hi, r_lo, scale;
 };
 __device__ __forceinline__ GenBlock gen_block(uint32_t sc, float D) {
   GenBlock g;
-  float s = e4m3_decode(sc);
-  g.c = s * D;
-  g.zero = !(g.c > 0.0f);
-  // far from the float32 range ends the split reciprocal is accurate; near
-  // them fall back to the IEEE division
-  g.exact_div = g.c < 0x1p-100f || g.c > 0x1p100f;
-  GenQuot q = gen_split(g.zero ? 1.0f : g.c);
-  g.r_hi = g.zero ? 0.0f : q.r_hi;
-  g.r_lo = g.zero ? 0.0f : q.r_lo;
+  float c = e4m3_decode(sc) * D;   // fl32(s * D), rounded as written
+  if (!(c > 0.0f)) {
+    g.r_hi = g.r_lo = 0.0f;        // every code becomes a signed zero
+    g.scale = 1.0f;
+    return g;
+  }
+  int kc;
+  float m = split_pow2(c, kc);
+  float e;
+  float r = rcp_below(m, e);
+  int P = kc < -104 ? -104 - kc : 0;  // keep x * r_lo and the converter scale in range
+  g.r_hi = __builtin_ldexpf(r, P);
+  g.r_lo = __builtin_ldexpf(e * r, P);
+  g.scale = pow2f(kc + P);
   return g;
-}
-__device__ __forceinline__ float gen_apply(float x, const GenBlock& g) {
-  if (g.exact_div && !g.zero) return x / g.c;
-  return quot_apply(x, g.r_hi, g.r_lo);
 }
 
 template <int SEL>
 __device__ __forceinline__ uint32_t enc_pair(uint32_t old, float a, float b, const GenBlock& g) {
-  return fp4_pack2<SEL>(old, gen_apply(a, g), gen_apply(b, g), 1.0f);
+  return fp4_pack2<SEL>(old, quot_apply(a, g.r_hi, g.r_lo), quot_apply(b, g.r_hi, g.r_lo), g.scale);
 }
 
 __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, int T, int W /* 2F */, int E,
                                                    const int32_t* __restrict__ offs, const int32_t* __restrict__ poffs,
-                                                   const float* __restrict__ amax,
+                                                   const float* __restrict__ row_scale,
+                                                   const float* __restrict__ col_scale,
                                                    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-                                                   float* __restrict__ row_scale, uint8_t* __restrict__ col_codes,
-                                                   uint8_t* __restrict__ col_scales, float* __restrict__ col_scale) {
+                                                   uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales) {
   __shared__ uint2 stage_codes[kQTileCols * kQBlocks];
   __shared__ uint8_t stage_sc[kQTileCols * kQBlocks];
   __shared__ int s_e[kQBlocks], s_poff[kQBlocks], s_plen[kQBlocks], s_row0[kQBlocks], s_cnt[kQBlocks];
   __shared__ float s_drow[kQBlocks], s_dcol[kQBlocks];
 
   const int tid = threadIdx.x;
-  const int ct = blockIdx.x;
-  const int gp_base = blockIdx.y * kQTileRows;  // first padded row of the tile
+  const int ct = blockIdx.y;                     // column tile (y: at most 2F/128)
+  const int gp_base = blockIdx.x * kQTileRows;  // first padded row of the tile
   const int col0 = ct * kQTileCols;
   const int ncols = min(kQTileCols, W - col0);
   const int ptotal = poffs[E];
 
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int e = tid; e < E; e += 256) {
-      float D = amax[e] / kTokenBound;
-      row_scale[e] = D;
-      col_scale[e] = 4.0f * D;
-    }
-  }
   if (tid < kQBlocks) {
     int gp = gp_base + 16 * tid;
     int e = -1;
@@ -205,9 +249,8 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
       s_plen[tid] = poffs[e + 1] - poffs[e];
       s_row0[tid] = offs[e] + (gp - poffs[e]);           // real row of the block's first row
       s_cnt[tid] = offs[e + 1] - (offs[e] + (gp - poffs[e]));  // real rows left in the expert from there
-      float D = amax[e] / kTokenBound;
-      s_drow[tid] = D;
-      s_dcol[tid] = 4.0f * D;
+      s_drow[tid] = row_scale[e];
+      s_dcol[tid] = col_scale[e];
     }
     s_e[tid] = e;
   }
@@ -218,6 +261,7 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
     const int row0 = s_row0[m];
     const int nreal = min(16, max(0, s_cnt[m]));
     const float Drow = s_drow[m], Dcol = s_dcol[m];
+    const DScale dsr = dscale(Drow), dsc = dscale(Dcol);
     uint4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -229,7 +273,7 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
       uint32_t o = (uint32_t)__shfl_xor((int)am, 1, kWave);
       am = am > o ? am : o;
       if (i >= nreal) continue;
-      uint32_t sc = Drow > 0.0f ? gen_scale_code(__uint_as_float(am << 16), Drow) : 0u;
+      uint32_t sc = gen_scale_code(__uint_as_float(am << 16), dsr);
       GenBlock gb = gen_block(sc, Drow);
       uint32_t w = 0;
       w = enc_pair<0>(w, bf16lo(v[i].x), bf16hi(v[i].x), gb);
@@ -258,8 +302,8 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
         a0 = fmaxf(a0, fabsf(z0[i]));
         a1 = fmaxf(a1, fabsf(z1[i]));
       }
-      uint32_t sc0 = Dcol > 0.0f ? gen_scale_code(a0, Dcol) : 0u;
-      uint32_t sc1 = Dcol > 0.0f ? gen_scale_code(a1, Dcol) : 0u;
+      uint32_t sc0 = gen_scale_code(a0, dsc);
+      uint32_t sc1 = gen_scale_code(a1, dsc);
       GenBlock g0 = gen_block(sc0, Dcol), g1 = gen_block(sc1, Dcol);
       uint32_t c00 = 0, c01 = 0, c10 = 0, c11 = 0;
       c00 = enc_pair<0>(c00, z0[0], z0[1], g0);
@@ -304,9 +348,9 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
 
 using namespace mtb;
 
-MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t num_experts) {
-  if (num_experts < 1) return 0;
-  return (size_t)(2 * (num_experts + 1) * sizeof(int32_t));
+MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts) {
+  if (num_experts < 1 || tokens < 0) return 0;
+  return (size_t)(2 * (num_experts + 1) * sizeof(int32_t) + tokens * sizeof(uint32_t));
 }
 
 MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
@@ -318,20 +362,20 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
   if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
   if (tokens > 0 && (!preact || !dy || !dx || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
-  if (!workspace || workspace_bytes < dswiglu_workspace_bytes(num_experts)) return EP_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < dswiglu_workspace_bytes(tokens, num_experts)) return EP_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int T = (int)tokens, F = (int)ffn, E = (int)num_experts;
   int32_t* offs = (int32_t*)workspace;
   int32_t* poffs = offs + (E + 1);
-  hipLaunchKernelGGL(k_dswiglu_setup, dim3(1), dim3(1024), 0, s, counts, E, T, offs, poffs, amax);
-  if (T > 0) {
-    hipLaunchKernelGGL(k_dswiglu_epilogue, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, E, offs, dx,
-                       amax);
-  }
+  uint32_t* rowmax = (uint32_t*)(poffs + (E + 1));
+  if (T > 0)
+    hipLaunchKernelGGL(k_dswiglu_epilogue, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, dx, rowmax);
+  hipLaunchKernelGGL(k_dswiglu_reduce, dim3((unsigned)E), dim3(1024), 0, s, counts, E, T, rowmax, offs, poffs, amax,
+                     row_scale, col_scale);
   // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
   const int64_t prow_bound = tokens + 15 * num_experts;
-  dim3 grid((unsigned)((2 * F + kQTileCols - 1) / kQTileCols), (unsigned)((prow_bound + kQTileRows - 1) / kQTileRows));
-  hipLaunchKernelGGL(k_fc1_quant, grid, dim3(256), 0, s, dx, T, 2 * F, E, offs, poffs, amax, row_codes, row_scales,
-                     row_scale, col_codes, col_scales, col_scale);
+  dim3 grid((unsigned)((prow_bound + kQTileRows - 1) / kQTileRows), (unsigned)((2 * F + kQTileCols - 1) / kQTileCols));
+  hipLaunchKernelGGL(k_fc1_quant, grid, dim3(256), 0, s, dx, T, 2 * F, E, offs, poffs, row_scale, col_scale, row_codes,
+                     row_scales, col_codes, col_scales);
   return launch_status();
 }

@@ -189,6 +189,52 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__
   }
 }
 
+// Rows of >= 256 blocks (H >= 4096): one workgroup of 256 threads per row,
+// thread j owns blocks j, j+256, ... (NBW of them), so a 4096-wide row is one
+// block per thread; the row max goes through LDS.
+template <int NBW>
+__global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restrict__ x, int rows, int H,
+                                                      uint8_t* __restrict__ out, int row_bytes) {
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int nblk = H >> 4;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * H);
+  uint4 v[NBW][2];
+  uint32_t bmax[NBW];
+  uint32_t rmax = 0;
+#pragma unroll
+  for (int c = 0; c < NBW; ++c) {
+    int j = c * 256 + tid;
+    if (j < nblk) {
+      v[c][0] = ld_stream16(xr + 2 * j);
+      v[c][1] = ld_stream16(xr + 2 * j + 1);
+      uint32_t a = absmax_bf16x8(v[c][0]), b = absmax_bf16x8(v[c][1]);
+      bmax[c] = a > b ? a : b;
+    } else {
+      v[c][0] = v[c][1] = make_uint4(0, 0, 0, 0);
+      bmax[c] = 0;
+    }
+    rmax = rmax > bmax[c] ? rmax : bmax[c];
+  }
+  rmax = wave_max_u32(rmax);
+  if ((tid & 63) == 0) red[tid >> 6] = rmax;
+  __syncthreads();
+  rmax = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int e = token_exponent(__uint_as_float(rmax << 16));
+  uint8_t* orow = out + (size_t)row * row_bytes;
+  if (tid == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+#pragma unroll
+  for (int c = 0; c < NBW; ++c) {
+    int j = c * 256 + tid;
+    if (j >= nblk) continue;
+    uint32_t sc, o0, o1;
+    BlockQuant q = nvfp4_block(__uint_as_float(bmax[c] << 16), e, sc);
+    encode_rne(v[c][0], v[c][1], q, o0, o1);
+    store_block<1>(orow, H, j, o0, o1, sc);
+  }
+}
+
 // Stochastic rounding: ALU-bound on the Philox blocks, so the second pass
 // re-reads each block (from cache) instead of holding the row in VGPRs.
 template <int MODE>
@@ -312,6 +358,15 @@ MTB_EXPORT int32_t ep_nvfp4_pack(const uint16_t* x, int64_t rows, int64_t hidden
     hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
   } else if (round_mode == EP_ROUND_SR_STREAM) {
     hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
+  } else if (H >= 4096) {
+    const int nbw = (H / 16 + 255) / 256;
+    dim3 g1((unsigned)rows);
+    if (nbw <= 1)
+      hipLaunchKernelGGL(k_nvfp4_pack_wg<1>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
+    else if (nbw <= 2)
+      hipLaunchKernelGGL(k_nvfp4_pack_wg<2>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
+    else
+      hipLaunchKernelGGL(k_nvfp4_pack_wg<4>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
   } else if (nb <= 1) {
     hipLaunchKernelGGL(k_nvfp4_pack<1>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
   } else if (nb <= 2) {

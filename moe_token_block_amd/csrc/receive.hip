@@ -8,19 +8,24 @@
 // Launch 1 (k_expert_scale): D_e = 4 * max t over expert e's rows.  It reads
 // only the 4-byte token scales, not the codes: no amax pass.
 // Launch 2 (k_nvfp4_receive): one workgroup per 256 grouped rows x 128
-// columns.  Thread (cg, m) owns columns [8cg, 8cg+8) of the tile and the
-// 16-row block m:
-//   * loads the 16 code dwords of its rows (gathered through src_row; a wave
-//     reads 4 rows x 64 contiguous bytes per instruction) and stores them
-//     unchanged to the rowwise operand;
-//   * decodes them exactly (E2M1 via the converter, times s*t/4*d_i);
-//   * runs the 16-point butterfly down each of its 8 columns in registers;
+// columns, tiles ordered so that one XCD runs all column tiles of a row tile
+// together (shared L2 lines).  Thread (cg, m) owns columns [8cg, 8cg+8) of
+// the tile and the 16-row block m:
+//   * gathers the 16 code dwords of its rows through src_row (a wave reads
+//     4 rows x 64 contiguous bytes per instruction) and stores them unchanged
+//     to the rowwise operand;
+//   * decodes them exactly (E2M1 via the converter, times s*t/4*d_i), fused
+//     with the first butterfly stage, then runs the other three stages down
+//     each of its 8 columns in registers;
 //   * quantizes each 16-value column block with the expert's power-of-two D_e
-//     and stages 8 code bytes + 1 scale byte per column in LDS;
+//     (reciprocals of the 127 possible block scales from an LDS table) and
+//     stages 8 code bytes + 1 scale per column in LDS;
 // then the workgroup writes the staged transposed tile with stores where 16
 // consecutive threads cover one column's 128 contiguous bytes.
 // Tiles are aligned to 256 global grouped rows; a tile may straddle experts
 // (slots are 16-aligned), so every 16-row block looks up its own expert.
+// Without the columnwise operand the receive is a plain row gather
+// (k_nvfp4_gather).
 #include "common.h"
 #include "launch.h"
 
@@ -29,6 +34,7 @@ namespace mtb {
 constexpr int kTileRows = 256;
 constexpr int kTileCols = 128;
 constexpr int kBlocks = kTileRows / 16;  // 16-row blocks per tile
+constexpr int kXcds = 8;                 // CDNA4: 8 XCDs, workgroups dealt round-robin
 
 __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
                                                        const int32_t* __restrict__ offsets,
@@ -56,13 +62,33 @@ __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict
   }
 }
 
+// Reciprocal split of every E4M3 block-scale code (see quot_split): entry c
+// holds r_hi, r_lo of the significand of s = E4M3(c) and s's exponent; code 0
+// (and the NaN code) hold zeros, which quantize every value to a signed zero.
+struct RcpEntry {
+  float r_hi, r_lo;
+  int k, pad;
+};
+
+__device__ __forceinline__ RcpEntry rcp_entry(int c) {
+  RcpEntry r{0.0f, 0.0f, 0, 0};
+  float s = e4m3_decode((uint32_t)c);
+  if (c != 0 && c < 0x7F) {
+    QuotSplit q = quot_split(s);
+    r.r_hi = q.r_hi;
+    r.r_lo = q.r_lo;
+    r.k = q.k;
+  }
+  return r;
+}
+
 // Quantizer parameters of one post-RHT column block with decode scale 2^dexp.
 struct ColQuant {
   float r_hi, r_lo, scale;
   uint32_t sc;
 };
 
-__device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp) {
+__device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp, const RcpEntry* tab) {
   // s = E4M3(fl32(amax / 6) / D): fl32(amax/6) is exact by div6 for normal
   // amax; tiny amax are scaled by 2^64 first (their E4M3 code is 0 unless D
   // is tiny too, and then the scaled path is the exact one).
@@ -71,19 +97,14 @@ __device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp) {
   float y = __builtin_ldexpf(div6(a), -dexp - (tiny ? 64 : 0));
   ColQuant q;
   q.sc = e4m3_encode(fminf(y, 448.0f));
-  float s = e4m3_decode(q.sc);
-  if (s > 0.0f) {
-    QuotSplit qs = quot_split(s);
-    int K = qs.k + dexp;
-    int P = K < -104 ? -104 - K : 0;
-    q.r_hi = __builtin_ldexpf(qs.r_hi, P);
-    q.r_lo = __builtin_ldexpf(qs.r_lo, P);
-    q.scale = pow2f(K + P);
-  } else {
-    q.r_hi = 0.0f;
-    q.r_lo = 0.0f;
-    q.scale = 1.0f;
-  }
+  RcpEntry r = tab[q.sc & 0x7F];
+  // quotient by s * D = m * 2^K; for K < -104 the quotient is first scaled
+  // up by 2^P (exact) so that the power handed to the converter stays normal
+  int K = r.k + dexp;
+  int P = max(-104 - K, 0);
+  q.r_hi = __builtin_ldexpf(r.r_hi, P);
+  q.r_lo = __builtin_ldexpf(r.r_lo, P);
+  q.scale = q.sc ? pow2f(K + P) : 1.0f;
   return q;
 }
 
@@ -109,178 +130,290 @@ __device__ __forceinline__ float absmax16(const float* y) {
   return m;
 }
 
-// Decode byte SEL (two columns) of the 16 code words into z0 (even column),
-// z1 (odd column).  Fast rows: z = e2m1 * c with c = s*t*d/4 exact.  Slow
-// rows (t tiny): z = ldexp(e2m1 * s*d/4, e), rounded once.
-template <int SEL>
-__device__ __forceinline__ void decode_pair(const uint32_t* cw, const float* cm, const int* ce, bool slow,
-                                            float* z0, float* z1) {
+// Butterfly stages 2, 4, 8 (stage 1 is fused into the decode).
+__device__ __forceinline__ void rht16_upper(float* z) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    f32x2 g = fp4_unpack2<SEL>(cw[i], 1.0f);
-    if (!slow) {
-      z0[i] = g[0] * cm[i];
-      z1[i] = g[1] * cm[i];
-    } else {
-      z0[i] = __builtin_ldexpf(g[0] * cm[i], ce[i]);
-      z1[i] = __builtin_ldexpf(g[1] * cm[i], ce[i]);
+  for (int h = 2; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      float a = z[i], b = z[i + h];
+      z[i] = a + b;
+      z[i + h] = a - b;
     }
   }
 }
 
-template <int SEL, bool COL>
+// Decode byte SEL (two columns) of the 16 code words and apply the first
+// butterfly stage.  Fast blocks: the decoded value is e2m1 * c with c =
+// s*t*d/4, each product exact, so stage 1's pair (i, i+1) becomes
+// fma(g_i, c_i, +-g_{i+1} c_{i+1}) -- the same two roundings as adding the
+// decoded values.  Slow blocks (a row with t < 2^-100): z = ldexp(e2m1 *
+// s*d/4, e) rounded once per row, then the plain stage.
+template <int SEL>
+__device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* cm, const int* ce, bool slow,
+                                              float* z0, float* z1) {
+  if (!slow) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      f32x2 g = fp4_unpack2<SEL>(cw[i], 1.0f), h = fp4_unpack2<SEL>(cw[i + 1], 1.0f);
+      float b0 = h[0] * cm[i + 1], b1 = h[1] * cm[i + 1];
+      z0[i] = __builtin_fmaf(g[0], cm[i], b0);
+      z0[i + 1] = __builtin_fmaf(g[0], cm[i], -b0);
+      z1[i] = __builtin_fmaf(g[1], cm[i], b1);
+      z1[i + 1] = __builtin_fmaf(g[1], cm[i], -b1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      f32x2 g = fp4_unpack2<SEL>(cw[i], 1.0f), h = fp4_unpack2<SEL>(cw[i + 1], 1.0f);
+      float a0 = __builtin_ldexpf(g[0] * cm[i], ce[i]), a1 = __builtin_ldexpf(g[1] * cm[i], ce[i]);
+      float b0 = __builtin_ldexpf(h[0] * cm[i + 1], ce[i + 1]), b1 = __builtin_ldexpf(h[1] * cm[i + 1], ce[i + 1]);
+      z0[i] = a0 + b0;
+      z0[i + 1] = a0 - b0;
+      z1[i] = a1 + b1;
+      z1[i + 1] = a1 - b1;
+    }
+  }
+}
+
+// LDS staging of the transposed tile: entry (column c, block b) sits at
+// c*16 + (b ^ ((c >> 3) & 15)).  The column phase writes, for a fixed byte
+// pair, 16 lanes with columns 8 apart and one block each -- the XOR spreads
+// them over 16 distinct bank pairs; the copy-out reads all 16 blocks of one
+// column, a permutation inside one 128-byte row.
+__device__ __forceinline__ int stage_at(int c, int b) { return c * kBlocks + (b ^ ((c >> 3) & 15)); }
+
+template <int SEL>
 __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm, const int* ce, bool slow, int dexp,
-                                            uint2* stage_codes, uint8_t* stage_sc, int col0, int m) {
+                                            const RcpEntry* tab, uint2* stage_codes, uint32_t* stage_sc, int col0,
+                                            int m) {
   float z0[16], z1[16];
-  decode_pair<SEL>(cw, cm, ce, slow, z0, z1);
-  rht16_butterfly(z0);
-  rht16_butterfly(z1);
-  ColQuant q0 = col_block_quant(absmax16(z0), dexp);
-  ColQuant q1 = col_block_quant(absmax16(z1), dexp);
+  decode_stage1<SEL>(cw, cm, ce, slow, z0, z1);
+  rht16_upper(z0);
+  rht16_upper(z1);
+  ColQuant q0 = col_block_quant(absmax16(z0), dexp, tab);
+  ColQuant q1 = col_block_quant(absmax16(z1), dexp, tab);
   uint32_t a0, a1, b0, b1;
   col_encode(z0, q0, a0, a1);
   col_encode(z1, q1, b0, b1);
   const int c0 = col0 + 2 * SEL, c1 = c0 + 1;
-  stage_codes[c0 * kBlocks + m] = make_uint2(a0, a1);
-  stage_codes[c1 * kBlocks + m] = make_uint2(b0, b1);
-  stage_sc[c0 * kBlocks + m] = (uint8_t)q0.sc;
-  stage_sc[c1 * kBlocks + m] = (uint8_t)q1.sc;
+  stage_codes[stage_at(c0, m)] = make_uint2(a0, a1);
+  stage_codes[stage_at(c1, m)] = make_uint2(b0, b1);
+  stage_sc[stage_at(c0, m)] = q0.sc;
+  stage_sc[stage_at(c1, m)] = q1.sc;
 }
 
-template <bool COL>
+// One workgroup per 256 grouped rows x 128 columns; 1-D grid of
+// row_tiles * col_tiles workgroups.  Workgroup i runs on XCD i % 8, so the
+// logical tile is taken from a contiguous range per XCD, column tile
+// fastest: all column tiles of a row tile run on one XCD at about the same
+// time, and the halves of each 128-byte code line, the scale lines and the
+// token scales they share are fetched into that XCD's L2 once (and partial
+// line writes of the rowwise scales merge there).
 __global__ __launch_bounds__(256) void k_nvfp4_receive(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
                                                        const int32_t* __restrict__ offsets, int E,
-                                                       const int32_t* __restrict__ src_row, int r_cap,
+                                                       const int32_t* __restrict__ src_row, int r_cap, int n_ct,
                                                        uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
                                                        float* __restrict__ row_t, uint8_t* __restrict__ col_codes,
                                                        uint8_t* __restrict__ col_scales,
                                                        const float* __restrict__ col_scale) {
-  __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block] 8 bytes
-  __shared__ uint8_t stage_sc[kTileCols * kBlocks];    // [column][block]
+  __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block ^ swizzle] 8 code bytes; offsets first
+  __shared__ uint32_t stage_sc[kTileCols * kBlocks];   // [column][block ^ swizzle] scale code
+  __shared__ RcpEntry s_tab[128];
   __shared__ int s_src[kTileRows];
   __shared__ float s_t[kTileRows];
+  __shared__ float s_tq[kTileRows];                    // t * d_i / 4 (i = row mod 16)
   __shared__ uint32_t s_sw[kTileRows][2];              // the tile's 8 scale bytes of each row
-  __shared__ int s_bexp[kBlocks];                      // expert of each 16-row block (-1: beyond off_E)
-  __shared__ int s_off[kBlocks], s_len[kBlocks], s_dexp[kBlocks];
+  __shared__ int s_dexp[kBlocks], s_slow[kBlocks], s_live[kBlocks];
+  __shared__ uint64_t s_cbase[kBlocks], s_sbase[kBlocks];
+  __shared__ uint32_t s_cstr[kBlocks], s_sstr[kBlocks];
+  int* s_offs = reinterpret_cast<int*>(stage_codes);  // offsets[0..E] until the column phase
 
   const int tid = threadIdx.x;
-  const int ct = blockIdx.x;                 // column tile
-  const int g_base = blockIdx.y * kTileRows;  // first grouped row of the tile
+  const unsigned nb = gridDim.x, bx = blockIdx.x;
+  const unsigned xq = nb / kXcds, xr = nb % kXcds, x = bx % kXcds;
+  const unsigned lt = x * xq + min(x, xr) + bx / kXcds;
+  const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
+  const int g_base = rt * kTileRows;  // first grouped row of the tile
   const int col0 = ct * kTileCols;
   const int ncols = min(kTileCols, H - col0);
-  const int off_end = offsets[E];
   const int toff = (H >> 1) + (H >> 4);
 
+  // round 1: source rows, expert offsets, the reciprocal table.
+  // src_row is -1 for padding and from off_E to r_cap.
+  {
+    int g = g_base + tid;
+    int src = g < r_cap ? src_row[g] : -1;
+    s_src[tid] = (src >= 0 && src < T) ? src : -1;
+    for (int i = tid; i <= E; i += 256) s_offs[i] = offsets[i];
+    if (tid < 128) s_tab[tid] = rcp_entry(tid);
+  }
+  __syncthreads();
+  const int off_end = min(s_offs[E], r_cap & ~15);  // whole 16-row blocks inside the outputs
+
+  // round 2a: each 16-row block's expert -> its decode exponent and output bases.
   if (tid < kBlocks) {
-    int g = g_base + 16 * tid;
-    int e = -1;
-    if (g < off_end && g < r_cap) {
-      int lo = 0, hi = E - 1;  // last expert with offsets[e] <= g
+    const int gb = g_base + 16 * tid;
+    int live = gb < off_end;
+    int e = 0;
+    if (live) {
+      int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
       while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (offsets[mid] <= g) lo = mid; else hi = mid - 1;
+        if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
       }
       e = lo;
-      s_off[tid] = offsets[e];
-      s_len[tid] = offsets[e + 1] - offsets[e];
-      s_dexp[tid] = COL ? pow2_exponent(col_scale[e]) : 0;
     }
-    s_bexp[tid] = e;
+    s_live[tid] = live;
+    if (live) {
+      const int off = s_offs[e], len = s_offs[e + 1] - off;
+      s_dexp[tid] = pow2_exponent(col_scale[e]);
+      s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+      s_cstr[tid] = (uint32_t)(len >> 1);
+      s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint32_t)((gb - off) >> 4);
+      s_sstr[tid] = (uint32_t)(len >> 4);
+    }
   }
+
+  // round 2b (one row per thread): t and the tile's scale words into LDS; the
+  // rowwise scales and t go out here.
   {
-    // prologue: one thread per tile row -- source row, t, the tile's scale
-    // bytes; rowwise scale bytes and t go out here.
-    int g = g_base + tid;
-    bool live = g < off_end && g < r_cap;
-    int src = live ? src_row[g] : -1;
-    if (src >= T) src = -1;
+    const int g = g_base + tid;
+    const int src = s_src[tid];
     float t = 0.0f;
     uint32_t sw0 = 0, sw1 = 0;
     if (src >= 0) {
-      const uint8_t* prow = packed + (size_t)src * row_bytes;
+      const uint8_t* prow = packed + (size_t)(uint32_t)src * (uint32_t)row_bytes;
       t = *reinterpret_cast<const float*>(prow + toff);
       const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
       sw0 = sp[0];
       if (ncols > 64) sw1 = sp[1];
     }
-    s_src[tid] = src;
-    s_t[tid] = t;
-    s_sw[tid][0] = sw0;
-    s_sw[tid][1] = sw1;
-    if (live) {
+    {
+      s_t[tid] = t;
+      s_tq[tid] = t * rht_in_scale(tid & 15);
+      s_sw[tid][0] = sw0;
+      s_sw[tid][1] = sw1;
+      // a block with a row of t < 2^-100 takes the two-step decode
+      uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);
+      if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
+    }
+    if (g < off_end) {
       uint32_t* rs = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
       rs[0] = sw0;
       if (ncols > 64) rs[1] = sw1;
       if (ct == 0) row_t[g] = t;
     }
   }
-  __syncthreads();
 
+  // round 2c: thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8)
+  // of the 16 rows of block m (a wave reads 4 rows x 64 contiguous bytes per
+  // instruction) and stores them unchanged to the rowwise operand.
   const int cg = tid & 15, m = tid >> 4;
-  const bool live = s_bexp[m] >= 0 && cg * 8 < ncols;
-  if (live) {
-    uint32_t cw[16];
-    float cm[16];
-    int ce[16];
-    bool slow = false;
-    const int r0 = 16 * m;
+  const int r0 = 16 * m;
+  const int gb = g_base + r0;
+  const bool live = gb < off_end && cg * 8 < ncols;
+  uint32_t cw[16];
+  {
+    int4 sv[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int src = s_src[r0 + i];
-      cw[i] = src >= 0 ? *reinterpret_cast<const uint32_t*>(packed + (size_t)src * row_bytes + (col0 >> 1) + 4 * cg) : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int g = g_base + r0 + i;
-      *reinterpret_cast<uint32_t*>(row_codes + (size_t)g * (H >> 1) + (col0 >> 1) + 4 * cg) = cw[i];
-    }
-    if (COL) {
+    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
+    const int* sr = reinterpret_cast<const int*>(sv);
+    const uint8_t* base = packed + (col0 >> 1) + 4 * cg;
+    if (live && T > 0) {
+      // branch-free: padding rows read row 0 and are zeroed
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        uint32_t sw = s_sw[r0 + i][cg >> 3];
-        float s = e4m3_decode(sw >> (8 * ((cg >> 1) & 3)));
-        float t = s_t[r0 + i];
-        float sd = s * rht_in_scale(i);  // exact: s has 4 significant bits
-        // t >= 2^-100 keeps s*t/4 and every product e2m1*s*t/4 exact or one rounding
-        bool tiny = t < 0x1p-100f && t > 0.0f;
-        slow |= tiny;
-        cm[i] = sd;
-        ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
-        if (!tiny) cm[i] = sd * t;
+        const int src = sr[i];
+        uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes);
+        cw[i] = src >= 0 ? v : 0u;
       }
-      if (slow) {
-        // one row of the block is tiny: use the per-element two-step decode for all 16
+    } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          uint32_t sw = s_sw[r0 + i][cg >> 3];
-          cm[i] = e4m3_decode(sw >> (8 * ((cg >> 1) & 3))) * rht_in_scale(i);
-          if (s_t[r0 + i] == 0.0f) cm[i] = 0.0f;
-        }
-      }
-      const int dexp = s_dexp[m];
-      column_pair<0, COL>(cw, cm, ce, slow, dexp, stage_codes, stage_sc, cg * 8, m);
-      column_pair<1, COL>(cw, cm, ce, slow, dexp, stage_codes, stage_sc, cg * 8, m);
-      column_pair<2, COL>(cw, cm, ce, slow, dexp, stage_codes, stage_sc, cg * 8, m);
-      column_pair<3, COL>(cw, cm, ce, slow, dexp, stage_codes, stage_sc, cg * 8, m);
+      for (int i = 0; i < 16; ++i) cw[i] = 0u;
+    }
+    if (live) {
+      uint8_t* rc = row_codes + (size_t)gb * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(rc + (size_t)i * (uint32_t)(H >> 1)) = cw[i];
     }
   }
-  if (!COL) return;
   __syncthreads();
-  // transposed copy-out: item = (column, block); 16 consecutive threads cover
-  // one column's blocks, i.e. up to 128 contiguous code bytes.
+
+  // column phase: decode, 16-point RHT down each column, quantize with D_e.
+  if (live) {
+    float cm[16];
+    int ce[16];
+    const bool slow = s_slow[m] != 0;
+    const int sh = 8 * ((cg >> 1) & 3);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
+      cm[i] = s * s_tq[r0 + i];  // exact: s has 4 significant bits, t/4 is a power of two
+      ce[i] = 0;
+    }
+    if (slow) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float t = s_t[r0 + i];
+        ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
+        cm[i] = t == 0.0f ? 0.0f : e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * rht_in_scale(i);
+      }
+    }
+    const int dexp = s_dexp[m];
+    column_pair<0>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+    column_pair<1>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+    column_pair<2>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+    column_pair<3>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+  }
+  __syncthreads();
+  // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...;
+  // 16 consecutive threads cover one column's 128 contiguous code bytes.
+  const int b = tid & 15;
+  if (!s_live[b]) return;
+  const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
+  const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
 #pragma unroll
   for (int r = 0; r < (kTileCols * kBlocks) / 256; ++r) {
-    int it = r * 256 + tid;
-    int c = it >> 4, b = it & 15;
-    int e = s_bexp[b];
-    if (e < 0 || c >= ncols) continue;
-    int off = s_off[b], len = s_len[b];
-    int g = g_base + 16 * b;
-    size_t h = (size_t)(col0 + c);
-    uint2* dst = reinterpret_cast<uint2*>(col_codes + (size_t)H * (off >> 1) + h * (size_t)(len >> 1) + ((g - off) >> 1));
-    *dst = stage_codes[c * kBlocks + b];
-    col_scales[(size_t)H * (off >> 4) + h * (size_t)(len >> 4) + ((g - off) >> 4)] = stage_sc[c * kBlocks + b];
+    const int c = r * 16 + (tid >> 4);
+    if (c >= ncols) break;
+    const uint32_t h = (uint32_t)(col0 + c);
+    *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[stage_at(c, b)];
+    col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[stage_at(c, b)];
   }
+}
+
+// Rowwise-only receive: a plain gather of whole packed rows (codes, scales
+// and t), one wave per grouped row; rows below off_E with no source are zero.
+__global__ __launch_bounds__(256) void k_nvfp4_gather(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      const int32_t* __restrict__ src_row, int r_cap,
+                                                      uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+                                                      float* __restrict__ row_t) {
+  const int lane = threadIdx.x & 63;
+  const int g = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (g >= r_cap || g >= offsets[E]) return;
+  int src = src_row[g];
+  if (src >= T) src = -1;
+  const int cb = H >> 1, sb = H >> 4;  // code and scale bytes of a row (multiples of 32 and 4)
+  uint8_t* rc = row_codes + (size_t)g * cb;
+  uint8_t* rs = row_scales + (size_t)g * sb;
+  if (src < 0) {
+    for (int i = lane; i < cb / 16; i += 64) reinterpret_cast<uint4*>(rc)[i] = make_uint4(0, 0, 0, 0);
+    for (int i = lane; i < sb / 4; i += 64) reinterpret_cast<uint32_t*>(rs)[i] = 0u;
+    if (lane == 0) row_t[g] = 0.0f;
+    return;
+  }
+  const uint8_t* prow = packed + (size_t)src * row_bytes;
+  // codes start 4-byte aligned only (row_bytes = 9H/16 + 4): dword loads, 16-byte stores
+  for (int i = lane; i < cb / 16; i += 64) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(prow + 16 * i);
+    reinterpret_cast<uint4*>(rc)[i] = make_uint4(p[0], p[1], p[2], p[3]);
+  }
+  for (int i = lane; i < sb / 4; i += 64)
+    reinterpret_cast<uint32_t*>(rs)[i] = reinterpret_cast<const uint32_t*>(prow + cb)[i];
+  if (lane == 0) row_t[g] = *reinterpret_cast<const float*>(prow + cb + sb);
 }
 
 }  // namespace mtb
@@ -289,7 +422,8 @@ using namespace mtb;
 
 static int32_t receive_check(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
                              int64_t r_cap, const int32_t* offsets, const int32_t* src_row) {
-  if (tokens < 0 || r_cap < 0 || num_experts < 1 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
+  if (tokens < 0 || r_cap < 0 || num_experts < 1 || num_experts > 1024 || hidden <= 0 || hidden % 64 != 0)
+    return EP_ERR_SHAPE;
   if (tokens >= INT32_MAX / 4 || r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
   if (!offsets || !src_row) return EP_ERR_NULL;
   if (tokens > 0 && !packed) return EP_ERR_NULL;
@@ -318,10 +452,11 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale) return EP_ERR_NULL;
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
-  dim3 grid((unsigned)((H + kTileCols - 1) / kTileCols), (unsigned)((r_cap + kTileRows - 1) / kTileRows));
-  hipLaunchKernelGGL(k_nvfp4_receive<true>, grid, dim3(256), 0, (hipStream_t)stream, packed, (int)tokens, H,
-                     9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes, row_scales, row_t,
-                     col_codes, col_scales, col_scale);
+  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
+  if (n_rt * n_ct * 256 >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  hipLaunchKernelGGL(k_nvfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, (hipStream_t)stream, packed,
+                     (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
+                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
   return launch_status();
 }
 
@@ -343,9 +478,8 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens
                                           row_scales, row_t, col_codes, col_scales, col_scale, stream);
   }
   const int H = (int)hidden;
-  dim3 grid((unsigned)((H + kTileCols - 1) / kTileCols), (unsigned)((r_cap + kTileRows - 1) / kTileRows));
-  hipLaunchKernelGGL(k_nvfp4_receive<false>, grid, dim3(256), 0, (hipStream_t)stream, packed, (int)tokens, H,
-                     9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes, row_scales, row_t,
-                     col_codes, col_scales, col_scale);
+  hipLaunchKernelGGL(k_nvfp4_gather, dim3((unsigned)((r_cap + 3) / 4)), dim3(256), 0, (hipStream_t)stream, packed,
+                     (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes,
+                     row_scales, row_t);
   return launch_status();
 }

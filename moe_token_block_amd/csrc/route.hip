@@ -4,7 +4,11 @@
 // padded expert slots.  P1, commit messages: top_k, alignment and the index
 // dtype are arguments of the NVFP4 paths).
 //
-// Three launches, no atomics on global memory except the error flag:
+// Up to kSingleMax entries everything runs in ONE workgroup
+// of 16 waves (k_route_single): per-wave histograms in LDS, the cross-wave
+// scan and the padded offsets in LDS, then the stable scatter -- one launch.
+// Larger inputs use three launches, no atomics on global memory except the
+// error flag:
 //   1. count   -- each wave counts its 256 consecutive entries per expert
 //                 (LDS atomics: order does not matter for counts);
 //   2. scan    -- one workgroup turns the per-wave histograms into per-wave
@@ -152,6 +156,94 @@ __global__ __launch_bounds__(256) void k_route_scatter(const IDX* __restrict__ i
   }
 }
 
+// ------------------------------------------------------------------ single workgroup
+constexpr int kSingleWaves = 16;
+constexpr int64_t kSingleMax = 16384;  // beyond this one CU's scattered stores dominate
+
+template <typename IDX>
+__global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ idx, int R, int k, int E, int A,
+                                                       int r_cap, int ebits, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ dst_row,
+                                                       int32_t* __restrict__ src_row, int32_t* __restrict__ d_error) {
+  __shared__ int32_t hist[kSingleWaves][kMaxExperts];  // per-wave counts, then per-wave starting rows
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int chunk = ((R + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
+  const int c0 = w * chunk, c1 = min(R, c0 + chunk);
+  for (int e = lane; e < E; e += 64) hist[w][e] = 0;
+  __syncthreads();
+  bool any_bad = false;
+  for (int i = c0 + lane; i < c1; i += 64) {
+    bool bad;
+    int x = load_expert(idx, i, E, bad);
+    any_bad |= bad;
+    if (x >= 0) atomicAdd(&hist[w][x], 1);
+  }
+  if (any_bad) atomicOr(d_error, EP_DEVERR_EXPERT_ID);
+  __syncthreads();
+  int32_t cnt = 0;
+  if (tid < E) {
+    for (int ww = 0; ww < kSingleWaves; ++ww) {
+      int32_t c = hist[ww][tid];
+      hist[ww][tid] = cnt;
+      cnt += c;
+    }
+    counts[tid] = cnt;
+  }
+  scan[tid] = tid < E ? (cnt + A - 1) / A * A : 0;
+  __syncthreads();
+  for (int o = 1; o < E; o <<= 1) {
+    int32_t v = (tid < E && tid >= o) ? scan[tid - o] : 0;
+    __syncthreads();
+    if (tid < E) scan[tid] += v;
+    __syncthreads();
+  }
+  // exclusive offset of each expert -> add it to every wave's starting rank
+  if (tid < E) {
+    const int32_t start = tid ? scan[tid - 1] : 0;
+    offsets[tid + 1] = scan[tid];
+    for (int ww = 0; ww < kSingleWaves; ++ww) hist[ww][tid] += start;
+    for (int32_t r = start + cnt; r < scan[tid]; ++r) src_row[r] = -1;  // padding rows
+  }
+  if (tid == 0) offsets[0] = 0;
+  const int32_t total = scan[E - 1];
+  for (int32_t r = total + tid; r < r_cap; r += 1024) src_row[r] = -1;
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // entries are fetched 8 steps (512 entries) at a time, so the loads do not
+  // wait behind the LDS updates of the previous step
+  for (int grp = c0; grp < c1; grp += 8 * 64) {
+    int xs[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      int i = grp + st * 64 + lane;
+      bool bad;
+      xs[st] = i < c1 ? load_expert(idx, i, E, bad) : -1;
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      int i = grp + st * 64 + lane;
+      int x = xs[st];
+      const bool valid = x >= 0;
+      uint64_t m = __ballot(valid);
+#pragma unroll 1
+      for (int b = 0; b < ebits; ++b) {
+        uint64_t bb = __ballot(valid && ((x >> b) & 1));
+        m &= ((x >> b) & 1) ? bb : ~bb;
+      }
+      if (valid) {
+        int32_t b0 = hist[w][x];
+        int32_t d = b0 + __popcll(m & lt);
+        dst_row[i] = d;
+        src_row[d] = i / k;
+        if ((m >> lane) == 1ull) hist[w][x] = b0 + __popcll(m);
+      } else if (i < c1) {
+        dst_row[i] = -1;
+      }
+    }
+  }
+}
+
 }  // namespace mtb
 
 using namespace mtb;
@@ -189,6 +281,15 @@ MTB_EXPORT int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_
   int32_t* hist = (int32_t*)workspace;
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
+  if (R <= kSingleMax) {
+    if (idx_dtype == EP_IDX_INT32)
+      hipLaunchKernelGGL(k_route_single<int32_t>, dim3(1), dim3(1024), 0, s, (const int32_t*)topk_idx, (int)R,
+                         (int)top_k, E, (int)alignment, (int)r_cap, ebits, counts, offsets, dst_row, src_row, d_error);
+    else
+      hipLaunchKernelGGL(k_route_single<int64_t>, dim3(1), dim3(1024), 0, s, (const int64_t*)topk_idx, (int)R,
+                         (int)top_k, E, (int)alignment, (int)r_cap, ebits, counts, offsets, dst_row, src_row, d_error);
+    return launch_status();
+  }
   if (W > 0) {
     dim3 grid((unsigned)((W + 3) / 4)), block(256);
     if (idx_dtype == EP_IDX_INT32)

@@ -2,8 +2,8 @@
 // decoded to BF16), with an optional gather by a source-row map; and the
 // MXFP8 grouped receive (a plain row gather).
 //
-// Unpack mapping: one wave64 per output row, lane l owns 16-element blocks
-// l, l+64, ...: an 8-byte code load, one scale byte, two 16-byte BF16 stores.
+// Unpack mapping: one wave64 per output row, lane l owns 8-element chunks
+// l, l+64, ...: a 4-byte code load, the block's scale byte, one 16-byte store.
 // Decode: the converter gives e2m1 * 2^(k+e) exactly (k = the scale's
 // exponent, e = the row's), one multiply by the scale's significand makes the
 // exact product e2m1 * s * t, and v_cvt_pk_bf16_f32 rounds it to BF16.
@@ -38,6 +38,9 @@ __device__ __forceinline__ void decode8_tiny(uint32_t w, float s, int e, uint32_
     o[i] = bf16pair(__builtin_ldexpf(p[i][0] * s, e), __builtin_ldexpf(p[i][1] * s, e));
 }
 
+// One wave per output row; lane l decodes 8-element chunks l, l+64, ... (a
+// dword of codes -> 16 bytes of BF16), so every load instruction reads 256
+// contiguous code bytes and every store writes 1 KiB contiguously.
 __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict__ packed, int rows_in, int H,
                                                       int row_bytes, const int32_t* __restrict__ src_row,
                                                       int rows_out, uint16_t* __restrict__ out) {
@@ -46,42 +49,31 @@ __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict_
   if (g >= rows_out) return;
   int src = src_row ? src_row[g] : g;
   if (src >= rows_in) src = -1;  // out-of-range map entries decode as zero rows
-  const int nblk = H >> 4;
+  const int nch = H >> 3;
   uint4* orow = reinterpret_cast<uint4*>(out + (size_t)g * H);
   if (src < 0) {
-    for (int j = lane; j < nblk; j += 64) {
-      orow[2 * j] = make_uint4(0, 0, 0, 0);
-      orow[2 * j + 1] = make_uint4(0, 0, 0, 0);
-    }
+    for (int c = lane; c < nch; c += 64) orow[c] = make_uint4(0, 0, 0, 0);
     return;
   }
   const uint8_t* prow = packed + (size_t)src * row_bytes;
   const float t = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
   const int e = pow2_exponent(t);
-  for (int j = lane; j < nblk; j += 64) {
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(prow + 8 * j);
-    uint32_t w0 = cw[0], w1 = cw[1];
-    float s = e4m3_decode(prow[(H >> 1) + j]);
-    uint32_t o[8];
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(prow);
+#pragma unroll 2
+  for (int c = lane; c < nch; c += 64) {
+    uint32_t w = cw[c];
+    float s = e4m3_decode(prow[(H >> 1) + (c >> 1)]);
+    uint32_t o[4];
     if (s == 0.0f) {
-      // zero scale: every element is a signed zero
-      decode8(w0, 1.0f, 0.0f, o);
-      decode8(w1, 1.0f, 0.0f, o + 4);
+      decode8(w, 1.0f, 0.0f, o);  // zero scale: signed zeros
     } else {
       int k = __builtin_amdgcn_frexp_expf(s) - 1;
       float mant = __builtin_amdgcn_frexp_mantf(s) * 2.0f;
       int K = k + e;
-      if (K >= -126) {
-        float sc = pow2f(K);
-        decode8(w0, sc, mant, o);
-        decode8(w1, sc, mant, o + 4);
-      } else {
-        decode8_tiny(w0, s, e, o);
-        decode8_tiny(w1, s, e, o + 4);
-      }
+      if (K >= -126) decode8(w, pow2f(K), mant, o);
+      else decode8_tiny(w, s, e, o);
     }
-    orow[2 * j] = make_uint4(o[0], o[1], o[2], o[3]);
-    orow[2 * j + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 

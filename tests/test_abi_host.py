@@ -57,7 +57,7 @@ def test_helpers(lib):
     assert lib.ep_route_capacity(1, 1, 1, 24) == -3
     assert m.ep_rht_sign_mask() == 0xE8D5
     assert m.ep_status_string(-4).startswith("r_cap")
-    assert lib.dswiglu_workspace_bytes(8) == 72
+    assert lib.dswiglu_workspace_bytes(10, 8) == 72 + 40
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="passes fake pointers: only where no GPU exists")
@@ -79,6 +79,7 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_route_plan(P, 0, 10, 2, 4, 16, 80, P, P, P, P, P, 4, P, N) == -7
     assert lib.ep_route_plan(P, 0, 10, 2, 2000, 16, 80000, P, P, P, P, P, 1 << 30, P, N) == -2
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, N, P, P, P, P, N, N, N, N) == -1
+    assert lib.ep_nvfp4_direct_receive(P, 4, 128, 1025, 64, P, P, P, P, P, N, N, N, N) == -2
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, P, P, P, P, P, P, N, P, N) == -1
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 100, P, 2, P, P, P, P, P, P, P, P, P, 16, N) == -2
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, P, 4, N) == -7
