@@ -32,7 +32,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DOMINANT = "nvfp4_direct_receive"
+# Philox multiplies: 256 CUs x 64 lanes x 2.4 GHz, one 32x32->64-bit multiply
+# (v_mad_u64_u32) per lane per clock (its measured issue rate on gfx950)
+ALU_PEAK_TMULS = 256 * 64 * 2.4e9 / 1e12
+PHILOX_MULS_PER_ELEMENT = 20          # ten rounds of two multiplies, one Philox call per element
+
+# source files each call's kernels are built from (a counter summary is used
+# only while these are unchanged)
+_COMMON = ("common.h", "launch.h")
+CALL_SOURCES = {
+    "route_plan": ("route.hip",),
+    "nvfp4_pack": ("pack.hip",), "nvfp4_pack_sr": ("pack.hip",), "mxfp8_pack": ("pack.hip",),
+    "nvfp4_expert_scale": ("receive.hip",), "nvfp4_expert_scale_grad": ("receive.hip",),
+    "nvfp4_direct_receive": ("receive.hip",), "nvfp4_direct_receive_grad": ("receive.hip",),
+    "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
+    "dswiglu_nvfp4_quant": ("dswiglu.hip",),
+}
+STEP_NAMES = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
+              "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
+              "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
 
 
 def parse():
@@ -144,9 +162,7 @@ class Step:
                         row_codes=torch.empty((R, F), **u8), row_scales=torch.empty((R, 2 * F // 16), **u8),
                         row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
                         col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
-        self.names = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
-                      "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
-                      "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
+        self.names = list(STEP_NAMES)
         self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: 4x the MALL
 
     def calls(self):
@@ -231,6 +247,7 @@ class ConfigStep:
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         self.flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         self.names, self.calls_, self.bytes = [], [], {}
+        self.elements = None
         if n == 5:
             T, F, E = w.preact_bits.shape[0], w.dy_bits.shape[1], len(w.counts)
             self.pre, self.dy = bf(w.preact_bits), bf(w.dy_bits)
@@ -250,6 +267,7 @@ class ConfigStep:
         T, H = w.x_bits.shape
         k, E, A = w.topk_idx.shape[1], w.num_experts, w.alignment
         R = T * k
+        self.elements = T * H
         self.x = bf(w.x_bits)
         self.topk = torch.from_numpy(w.topk_idx).to(dev)
         r_cap = m.ep_route_capacity(T, k, E, A)
@@ -343,25 +361,44 @@ def cpu_baseline(inp, n_tok):
                        f"{R} grouped dSwiGLU rows); {dt:.1f} s single-threaded numpy")
 
 
-def kernel_source_hash():
+def kernel_source_hash(call):
+    """Hash of the sources the call's kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_token_block_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(CALL_SOURCES[call] + _COMMON):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_label):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernels changed since the counters were taken."""
+def traffic_from_profile(call, workload="dispatch"):
+    """HBM bytes per launch of one call from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy reference), or None when the
+    call's kernels changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic_counters.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("workload") != workload:
         return None
-    k = d.get("kernels", {}).get(kernel_label)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    k = d.get("calls", {}).get(call)
+    if k is None or k.get("source_hash") != kernel_source_hash(call):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def roofline_of(call, nbytes, ms, elements=None, workload="dispatch"):
+    """Roofline record of one call: HBM-bound calls against 8 TB/s; the
+    stochastic-rounding pack, bound by its Philox arithmetic, against the
+    multiply issue rate."""
+    if call == "nvfp4_pack_sr" and elements is not None:
+        tmul = elements * PHILOX_MULS_PER_ELEMENT / (ms / 1e3) / 1e12
+        return dict(bound="alu", achieved=round(tmul, 3), peak=round(ALU_PEAK_TMULS, 2), unit="Tmul/s",
+                    frac=round(tmul / ALU_PEAK_TMULS, 4), traffic=traffic_from_profile(call, workload),
+                    kernel=call, bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                traffic=traffic_from_profile(call, workload), kernel=call, bytes_per_launch=nbytes,
+                ms_per_launch=round(ms, 5))
 
 
 def time_step(step, args):
@@ -418,15 +455,16 @@ def main_config(args, dev):
     kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=step.bytes[nm],
                         gbs=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
                         frac=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
+    for nm in step.names:
+        kernels[nm]["traffic"] = traffic_from_profile(nm, args.workload)
     dom = max(step.names, key=lambda nm: per_ms[nm])
     out = {"metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
            "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16->nvfp4/mxfp8", "data": "synthetic",
            "config": dict(step.desc, bytes_per_step=total),
-           "roofline": dict(bound="hbm", achieved=kernels[dom]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                            frac=kernels[dom]["frac"], traffic=None, kernel=dom, bytes_per_launch=step.bytes[dom],
-                            ms_per_launch=kernels[dom]["ms"]),
+           "roofline": roofline_of(dom, step.bytes[dom], per_ms[dom], elements=step.elements,
+                                   workload=args.workload),
            "kernels": kernels, "cpu_baseline": None}
     line = json.dumps(out)
     print(line, flush=True)
@@ -436,11 +474,19 @@ def main_config(args, dev):
 
 
 def main_only(args, dev):
-    """Repeat one call of a path (or a 1 GiB copy) for counter collection."""
+    """Counter-collection aid: run the calls before ONLY once each, launch a
+    marker kernel (a torch random fill, used nowhere else), then run ONLY
+    --steps times; a profile's dispatches after the marker are ONLY's.
+    ONLY = 'copy' runs a 1 GiB device-to-device copy instead (the reference
+    that scales the memory counters)."""
     import torch
+    marker = torch.empty(64, dtype=torch.float32, device=dev)
     if args.only == "copy":
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        marker.random_()
+        torch.cuda.synchronize()
         for _ in range(args.steps):
             b.copy_(a)
         torch.cuda.synchronize()
@@ -448,13 +494,15 @@ def main_only(args, dev):
                           "launches": args.steps}))
         return
     step = ConfigStep(args.workload, dev) if args.workload != "dispatch" else Step(make_inputs(dev))
-    for _ in range(2):
-        step.run()
-    torch.cuda.synchronize()
     j = step.names.index(args.only)
-    call = step.calls()[j]
+    calls = step.calls()
+    for c in calls[:j]:
+        c()
+    torch.cuda.synchronize()
+    marker.random_()
+    torch.cuda.synchronize()
     for _ in range(args.steps):
-        call()
+        calls[j]()
     torch.cuda.synchronize()
     if hasattr(step, "bytes"):
         nbytes = step.bytes[args.only]
@@ -489,12 +537,12 @@ def main():
     value = total / (ms_step / 1e3) / 1e9
     kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=by[nm], gbs=round(by[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
                         frac=round(by[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
-    dom = kernels[DOMINANT]
-    traffic = traffic_from_profile("k_nvfp4_receive")
-    roofline = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(dom["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="k_nvfp4_receive (one-pass NVFP4 direct receive, rowwise + RHT columnwise)",
-                    bytes_per_launch=by[DOMINANT], ms_per_launch=dom["ms"])
+    for nm in step.names:
+        kernels[nm]["traffic"] = traffic_from_profile(nm)
+    # the dominant kernel: the call with the largest share of the step's time
+    dom = max(step.names, key=lambda nm: per_ms[nm])
+    roofline = roofline_of(dom, by[dom], per_ms[dom], elements=T * H)
+    roofline["dominant_by"] = "largest per-call time in the step"
     out = {
         "metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

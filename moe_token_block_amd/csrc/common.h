@@ -144,7 +144,12 @@ __device__ __forceinline__ void rht16_butterfly(float* z) {
 
 // ----------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw (SC'11): ten rounds of two 32x32->64 products,
-// Weyl key schedule between rounds.
+// Weyl key schedule between rounds.  The three-way XORs of a round are one
+// v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 struct U4 { uint32_t x, y, z, w; };
 
 __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
@@ -154,8 +159,8 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -165,6 +170,12 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
 }
 
 // ----------------------------------------------------------------- reductions
+// The value of the neighbouring lane (lane ^ 1), by a DPP quad permutation
+// [1, 0, 3, 2] inside the VALU instead of an LDS permute.
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {

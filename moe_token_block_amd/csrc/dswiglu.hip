@@ -23,6 +23,7 @@ namespace mtb {
 constexpr int kQTileRows = 256;
 constexpr int kQTileCols = 128;
 constexpr int kQBlocks = kQTileRows / 16;
+constexpr unsigned kXcdsQ = 8;  // CDNA4: 8 XCDs, workgroups dealt round-robin
 
 // Inclusive prefix sums of the (clamped) counts and of their 16-padded sizes
 // into a[] and b[] (1024 entries, LDS); E <= 1024.  Counts are device data:
@@ -222,77 +223,193 @@ __device__ __forceinline__ uint32_t enc_pair(uint32_t old, float a, float b, con
   return fp4_pack2<SEL>(old, quot_apply(a, g.r_hi, g.r_lo), quot_apply(b, g.r_hi, g.r_lo), g.scale);
 }
 
+// Per 16-row block of a tile: the split reciprocals of c = fl32(s * D) for
+// the 8 significands of s.  s * D = (m_s * m_D) * 2^(k_s + k_D), and while c
+// is a normal float fl32(s * D) = fl32(m_s * m_D) * 2^(k_s + k_D); the table
+// holds m_c = fl32(m_s * m_D) normalised to [1, 2) (kadj = 1 if it was >= 2).
+struct MantEntry {
+  float r_hi, r_lo;
+  int kadj, pad;
+};
+
+__device__ __forceinline__ MantEntry mant_entry(int j, float mD) {
+  float mc = (1.0f + 0.125f * (float)j) * mD;  // exact product rounded once
+  MantEntry t;
+  t.kadj = mc >= 2.0f ? 1 : 0;
+  float m = t.kadj ? mc * 0.5f : mc;
+  float e;
+  t.r_hi = rcp_below(m, e);
+  t.r_lo = e * t.r_hi;
+  t.pad = 0;
+  return t;
+}
+
+// Block parameters for E4M3 code sc with decode scale D = mD * 2^kD, from the
+// block's significand table; falls back to gen_block when c is tiny (P > 0)
+// or subnormal.
+__device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, const MantEntry* tab) {
+  float s = e4m3_decode(sc);
+  GenBlock g;
+  if (!(s > 0.0f) || !(D > 0.0f)) {
+    g.r_hi = g.r_lo = 0.0f;
+    g.scale = 1.0f;
+    return g;
+  }
+  int ks = __builtin_amdgcn_frexp_expf(s) - 1;
+  const MantEntry t = tab[(__float_as_uint(s) >> 20) & 7u];
+  int kc = ks + kD + t.kadj;
+  if (kc < -104) return gen_block(sc, D);
+  g.r_hi = t.r_hi;
+  g.r_lo = t.r_lo;
+  g.scale = pow2f(kc);
+  return g;
+}
+
+// E4M3 code of fl32(fl32(a / 6) / D) * 2^-x2 for a block max a that is 2^x2
+// times the true one (x2 = 2: the unscaled RHT below).
+__device__ __forceinline__ uint32_t gen_scale_code_x(float a, const DScale& d, int x2) {
+  if (!(d.D > 0.0f)) return 0u;
+  bool tiny = a < 0x1p-100f;
+  float pre = div6(tiny ? a * 0x1p64f : a);
+  float q = quot_apply(pre, d.r_hi, d.r_lo);
+  float y = __builtin_ldexpf(q, -d.kD - x2 - (tiny ? 64 : 0));
+  return e4m3_encode(fminf(y, 448.0f));
+}
+
+// LDS staging of the transposed tile, as in the direct receive: entry
+// (column c, block b) at c*16 + (b ^ ((c >> 3) & 15)).
+__device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (b ^ ((c >> 3) & 15)); }
+
+// One workgroup per 256 padded rows x 128 columns of dX, 1-D grid with the
+// tiles dealt to the 8 XCDs in contiguous ranges, column tile fastest (as in
+// the direct receive).  Thread (cg, m) loads 8 columns x the 16 rows of block
+// m once; the rowwise operand (16-element blocks split over lanes cg, cg^1)
+// and the RHT columnwise operand come out of that one load.  The columnwise
+// butterfly runs on the unscaled values with the signs d_i folded into its
+// adds: the result is 4x the RHT exactly, and the 4 goes into the powers of
+// two of the quantizer.
 __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, int T, int W /* 2F */, int E,
-                                                   const int32_t* __restrict__ offs, const int32_t* __restrict__ poffs,
+                                                   int n_ct, const int32_t* __restrict__ offs,
+                                                   const int32_t* __restrict__ poffs,
                                                    const float* __restrict__ row_scale,
                                                    const float* __restrict__ col_scale,
                                                    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
                                                    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales) {
-  __shared__ uint2 stage_codes[kQTileCols * kQBlocks];
-  __shared__ uint8_t stage_sc[kQTileCols * kQBlocks];
-  __shared__ int s_e[kQBlocks], s_poff[kQBlocks], s_plen[kQBlocks], s_row0[kQBlocks], s_cnt[kQBlocks];
+  __shared__ uint2 stage_codes[kQTileCols * kQBlocks];   // offsets, padded offsets first
+  __shared__ uint32_t stage_sc[kQTileCols * kQBlocks];
+  __shared__ MantEntry s_tab[kQBlocks][2][8];            // [block][row / col][significand of s]
+  __shared__ int s_live[kQBlocks], s_row0[kQBlocks], s_nreal[kQBlocks];
   __shared__ float s_drow[kQBlocks], s_dcol[kQBlocks];
+  __shared__ uint64_t s_cbase[kQBlocks], s_sbase[kQBlocks];
+  __shared__ uint32_t s_cstr[kQBlocks], s_sstr[kQBlocks];
+  int* s_offs = reinterpret_cast<int*>(stage_codes);
+  int* s_poffs = s_offs + 1025;
 
   const int tid = threadIdx.x;
-  const int ct = blockIdx.y;                     // column tile (y: at most 2F/128)
-  const int gp_base = blockIdx.x * kQTileRows;  // first padded row of the tile
+  const unsigned nb = gridDim.x, bx = blockIdx.x;
+  const unsigned xq = nb / kXcdsQ, xr = nb % kXcdsQ, x = bx % kXcdsQ;
+  const unsigned lt = x * xq + min(x, xr) + bx / kXcdsQ;
+  const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
+  const int gp_base = rt * kQTileRows;  // first padded row of the tile
   const int col0 = ct * kQTileCols;
   const int ncols = min(kQTileCols, W - col0);
-  const int ptotal = poffs[E];
 
-  if (tid < kQBlocks) {
-    int gp = gp_base + 16 * tid;
-    int e = -1;
-    if (gp < ptotal) {
-      e = expert_of(poffs, E, gp);
-      s_poff[tid] = poffs[e];
-      s_plen[tid] = poffs[e + 1] - poffs[e];
-      s_row0[tid] = offs[e] + (gp - poffs[e]);           // real row of the block's first row
-      s_cnt[tid] = offs[e + 1] - (offs[e] + (gp - poffs[e]));  // real rows left in the expert from there
-      s_drow[tid] = row_scale[e];
-      s_dcol[tid] = col_scale[e];
-    }
-    s_e[tid] = e;
+  for (int i = tid; i <= E; i += 256) {
+    s_offs[i] = offs[i];
+    s_poffs[i] = poffs[i];
   }
   __syncthreads();
+  const int ptotal = s_poffs[E];
+  if (gp_base >= ptotal) return;  // whole tile beyond the padded rows (uniform)
+
+  if (tid < kQBlocks) {
+    const int gp = gp_base + 16 * tid;
+    const int live = gp < ptotal;
+    s_live[tid] = live;
+    if (live) {
+      int lo = 0, hi = E - 1;  // last e with poffs[e] <= gp
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (s_poffs[mid] <= gp) lo = mid; else hi = mid - 1;
+      }
+      const int e = lo;
+      const int poff = s_poffs[e], plen = s_poffs[e + 1] - poff;
+      const int row0 = s_offs[e] + (gp - poff);                   // real row of the block's first row
+      s_row0[tid] = row0;
+      s_nreal[tid] = min(16, max(0, s_offs[e + 1] - row0));       // real rows of the block
+      s_drow[tid] = row_scale[e];
+      s_dcol[tid] = col_scale[e];
+      s_cbase[tid] = (uint64_t)W * (uint32_t)(poff >> 1) + (uint32_t)((gp - poff) >> 1);
+      s_cstr[tid] = (uint32_t)(plen >> 1);
+      s_sbase[tid] = (uint64_t)W * (uint32_t)(poff >> 4) + (uint32_t)((gp - poff) >> 4);
+      s_sstr[tid] = (uint32_t)(plen >> 4);
+    }
+  }
+  __syncthreads();
+  {
+    // significand tables: thread = (block, row/col, j)
+    const int b = tid >> 4, rc = (tid >> 3) & 1, j = tid & 7;
+    if (s_live[b]) {
+      const float D = rc ? s_dcol[b] : s_drow[b];
+      int kD = 0;
+      const float mD = D > 0.0f ? split_pow2(D, kD) : 1.0f;
+      s_tab[b][rc][j] = mant_entry(j, mD);
+    }
+  }
 
   const int cg = tid & 15, m = tid >> 4;
-  if (s_e[m] >= 0 && cg * 8 < ncols) {
-    const int row0 = s_row0[m];
-    const int nreal = min(16, max(0, s_cnt[m]));
+  const bool live = s_live[m] && cg * 8 < ncols;
+  uint4 v[16];
+  if (live) {
+    const int row0 = s_row0[m], nreal = s_nreal[m];
+    if (nreal > 0) {
+      // branch-free: rows past the expert's end re-read its last row and are zeroed
+      const uint16_t* base = dx + col0 + 8 * cg;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint4 t = ld_stream16(base + (size_t)(uint32_t)(row0 + min(i, nreal - 1)) * (uint32_t)W);
+        v[i] = i < nreal ? t : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // tables ready
+
+  if (live) {
+    const int row0 = s_row0[m], nreal = s_nreal[m];
     const float Drow = s_drow[m], Dcol = s_dcol[m];
     const DScale dsr = dscale(Drow), dsc = dscale(Dcol);
-    uint4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = i < nreal ? ld_stream16(dx + (size_t)(row0 + i) * W + col0 + 8 * cg) : make_uint4(0, 0, 0, 0);
     // ---- rowwise: the 16-column block is split over lanes cg, cg^1
+    uint8_t* rcp = row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + ((col0 + 8 * cg) >> 1);
+    uint8_t* rsp = row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + ((col0 + 8 * cg) >> 4);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       uint32_t am = absmax_bf16x8(v[i]);
-      uint32_t o = (uint32_t)__shfl_xor((int)am, 1, kWave);
+      uint32_t o = lane_xor1(am);
       am = am > o ? am : o;
       if (i >= nreal) continue;
-      uint32_t sc = gen_scale_code(__uint_as_float(am << 16), dsr);
-      GenBlock gb = gen_block(sc, Drow);
+      uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
+      GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, s_tab[m][0]);
       uint32_t w = 0;
       w = enc_pair<0>(w, bf16lo(v[i].x), bf16hi(v[i].x), gb);
       w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
       w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
       w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
-      const size_t r = (size_t)(row0 + i);
-      *reinterpret_cast<uint32_t*>(row_codes + r * (W >> 1) + ((col0 + 8 * cg) >> 1)) = w;
-      if ((cg & 1) == 0) row_scales[r * (W >> 4) + ((col0 + 8 * cg) >> 4)] = (uint8_t)sc;
+      *reinterpret_cast<uint32_t*>(rcp + (size_t)i * (uint32_t)(W >> 1)) = w;
+      if ((cg & 1) == 0) rsp[(size_t)i * (uint32_t)(W >> 4)] = (uint8_t)sc;
     }
-    // ---- columnwise: RHT down each of the 8 columns, D_col = 4 * D_row
+    // ---- columnwise: 4x the RHT down each of the 8 columns, D_col = 4 * D_row
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float z0[16], z1[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint32_t wv = p == 0 ? v[i].x : (p == 1 ? v[i].y : (p == 2 ? v[i].z : v[i].w));
-        z0[i] = bf16lo(wv) * rht_in_scale(i);
-        z1[i] = bf16hi(wv) * rht_in_scale(i);
+        const bool neg = (kRhtSignMask >> i) & 1u;
+        z0[i] = neg ? -bf16lo(wv) : bf16lo(wv);
+        z1[i] = neg ? -bf16hi(wv) : bf16hi(wv);
       }
       rht16_butterfly(z0);
       rht16_butterfly(z1);
@@ -302,9 +419,13 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
         a0 = fmaxf(a0, fabsf(z0[i]));
         a1 = fmaxf(a1, fabsf(z1[i]));
       }
-      uint32_t sc0 = gen_scale_code(a0, dsc);
-      uint32_t sc1 = gen_scale_code(a1, dsc);
-      GenBlock g0 = gen_block(sc0, Dcol), g1 = gen_block(sc1, Dcol);
+      uint32_t sc0 = gen_scale_code_x(a0, dsc, 2);
+      uint32_t sc1 = gen_scale_code_x(a1, dsc, 2);
+      GenBlock g0 = gen_block_tab(sc0, Dcol, dsc.kD, s_tab[m][1]);
+      GenBlock g1 = gen_block_tab(sc1, Dcol, dsc.kD, s_tab[m][1]);
+      // the values are 4x the transform: divide by 4 more
+      g0.scale *= 4.0f;
+      g1.scale *= 4.0f;
       uint32_t c00 = 0, c01 = 0, c10 = 0, c11 = 0;
       c00 = enc_pair<0>(c00, z0[0], z0[1], g0);
       c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
@@ -323,24 +444,25 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
       c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
       c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
       const int c0 = cg * 8 + 2 * p;
-      stage_codes[c0 * kQBlocks + m] = make_uint2(c00, c01);
-      stage_codes[(c0 + 1) * kQBlocks + m] = make_uint2(c10, c11);
-      stage_sc[c0 * kQBlocks + m] = (uint8_t)sc0;
-      stage_sc[(c0 + 1) * kQBlocks + m] = (uint8_t)sc1;
+      stage_codes[qstage_at(c0, m)] = make_uint2(c00, c01);
+      stage_codes[qstage_at(c0 + 1, m)] = make_uint2(c10, c11);
+      stage_sc[qstage_at(c0, m)] = sc0;
+      stage_sc[qstage_at(c0 + 1, m)] = sc1;
     }
   }
   __syncthreads();
+  // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...
+  const int b = tid & 15;
+  if (!s_live[b]) return;
+  const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
+  const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
 #pragma unroll
-  for (int rr = 0; rr < (kQTileCols * kQBlocks) / 256; ++rr) {
-    int it = rr * 256 + tid;
-    int c = it >> 4, b = it & 15;
-    if (s_e[b] < 0 || c >= ncols) continue;
-    int poff = s_poff[b], plen = s_plen[b];
-    int gp = gp_base + 16 * b;
-    size_t h = (size_t)(col0 + c);
-    uint2* dst = reinterpret_cast<uint2*>(col_codes + (size_t)W * (poff >> 1) + h * (size_t)(plen >> 1) + ((gp - poff) >> 1));
-    *dst = stage_codes[c * kQBlocks + b];
-    col_scales[(size_t)W * (poff >> 4) + h * (size_t)(plen >> 4) + ((gp - poff) >> 4)] = stage_sc[c * kQBlocks + b];
+  for (int r = 0; r < (kQTileCols * kQBlocks) / 256; ++r) {
+    const int c = r * 16 + (tid >> 4);
+    if (c >= ncols) break;
+    const uint32_t h = (uint32_t)(col0 + c);
+    *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[qstage_at(c, b)];
+    col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[qstage_at(c, b)];
   }
 }
 
@@ -374,8 +496,9 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
                      row_scale, col_scale);
   // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
   const int64_t prow_bound = tokens + 15 * num_experts;
-  dim3 grid((unsigned)((prow_bound + kQTileRows - 1) / kQTileRows), (unsigned)((2 * F + kQTileCols - 1) / kQTileCols));
-  hipLaunchKernelGGL(k_fc1_quant, grid, dim3(256), 0, s, dx, T, 2 * F, E, offs, poffs, row_scale, col_scale, row_codes,
-                     row_scales, col_codes, col_scales);
+  const int64_t n_rt = (prow_bound + kQTileRows - 1) / kQTileRows, n_ct = (2 * F + kQTileCols - 1) / kQTileCols;
+  if (n_rt * n_ct * 256 >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  hipLaunchKernelGGL(k_fc1_quant, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, T, 2 * F, E, (int)n_ct, offs,
+                     poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
   return launch_status();
 }

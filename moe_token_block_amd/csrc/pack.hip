@@ -66,11 +66,12 @@ __device__ __forceinline__ float sr_round(float u, int kexp, uint32_t r) {
   if (v >= 6.0f) {
     res = 6.0f;
   } else {
-    float sinv = v < 2.0f ? 2.0f : (v < 4.0f ? 1.0f : 0.5f);
-    float w = v * sinv;
+    // grid spacing 2^q: 0.5 on [0, 2), 1 on [2, 4), 2 on [4, 6)
+    int q = v < 2.0f ? -1 : (v < 4.0f ? 0 : 1);
+    float w = __builtin_ldexpf(v, -q);
     float fl = __builtin_floorf(w);
     float frac = w - fl;
-    res = (fl + (rf < frac ? 1.0f : 0.0f)) * (1.0f / sinv);
+    res = __builtin_ldexpf(fl + (rf < frac ? 1.0f : 0.0f), q);
   }
   return __builtin_copysignf(res, u);
 }
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_pack(const uint16_t* __restrict__
   }
   uint32_t m0 = absmax_bf16x8(a), m1 = absmax_bf16x8(b);
   uint32_t m = m0 > m1 ? m0 : m1;
-  uint32_t o = (uint32_t)__shfl_xor((int)m, 1, kWave);  // partner chunk of the same block
+  uint32_t o = lane_xor1(m);  // partner chunk of the same block
   m = m > o ? m : o;
   if (!valid) return;
   int e = mx_exponent(__uint_as_float(m << 16));

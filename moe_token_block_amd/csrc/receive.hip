@@ -32,6 +32,7 @@
 namespace mtb {
 
 constexpr int kTileRows = 256;
+constexpr int kThreads = kTileRows;       // one grouped row per thread in the row rounds
 constexpr int kTileCols = 128;
 constexpr int kBlocks = kTileRows / 16;  // 16-row blocks per tile
 constexpr int kXcds = 8;                 // CDNA4: 8 XCDs, workgroups dealt round-robin
@@ -150,10 +151,10 @@ __device__ __forceinline__ void rht16_upper(float* z) {
 // fma(g_i, c_i, +-g_{i+1} c_{i+1}) -- the same two roundings as adding the
 // decoded values.  Slow blocks (a row with t < 2^-100): z = ldexp(e2m1 *
 // s*d/4, e) rounded once per row, then the plain stage.
-template <int SEL>
-__device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* cm, const int* ce, bool slow,
-                                              float* z0, float* z1) {
-  if (!slow) {
+template <int SEL, bool SLOW>
+__device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* cm, const int* ce, float* z0,
+                                              float* z1) {
+  if (!SLOW) {
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       f32x2 g = fp4_unpack2<SEL>(cw[i], 1.0f), h = fp4_unpack2<SEL>(cw[i + 1], 1.0f);
@@ -182,14 +183,14 @@ __device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* c
 // pair, 16 lanes with columns 8 apart and one block each -- the XOR spreads
 // them over 16 distinct bank pairs; the copy-out reads all 16 blocks of one
 // column, a permutation inside one 128-byte row.
-__device__ __forceinline__ int stage_at(int c, int b) { return c * kBlocks + (b ^ ((c >> 3) & 15)); }
+__device__ __forceinline__ int stage_at(int c, int b) { return c * kBlocks + (b ^ ((c >> 3) & (kBlocks - 1))); }
 
-template <int SEL>
-__device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm, const int* ce, bool slow, int dexp,
+template <int SEL, bool SLOW>
+__device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm, const int* ce, int dexp,
                                             const RcpEntry* tab, uint2* stage_codes, uint32_t* stage_sc, int col0,
                                             int m) {
   float z0[16], z1[16];
-  decode_stage1<SEL>(cw, cm, ce, slow, z0, z1);
+  decode_stage1<SEL, SLOW>(cw, cm, ce, z0, z1);
   rht16_upper(z0);
   rht16_upper(z1);
   ColQuant q0 = col_block_quant(absmax16(z0), dexp, tab);
@@ -211,7 +212,7 @@ __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm,
 // time, and the halves of each 128-byte code line, the scale lines and the
 // token scales they share are fetched into that XCD's L2 once (and partial
 // line writes of the rowwise scales merge there).
-__global__ __launch_bounds__(256) void k_nvfp4_receive(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
+__global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
                                                        const int32_t* __restrict__ offsets, int E,
                                                        const int32_t* __restrict__ src_row, int r_cap, int n_ct,
                                                        uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(256) void k_nvfp4_receive(const uint8_t* __restrict
     int g = g_base + tid;
     int src = g < r_cap ? src_row[g] : -1;
     s_src[tid] = (src >= 0 && src < T) ? src : -1;
-    for (int i = tid; i <= E; i += 256) s_offs[i] = offsets[i];
-    if (tid < 128) s_tab[tid] = rcp_entry(tid);
+    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+    for (int i = tid; i < 128; i += kThreads) s_tab[i] = rcp_entry(i);
   }
   __syncthreads();
   const int off_end = min(s_offs[E], r_cap & ~15);  // whole 16-row blocks inside the outputs
@@ -344,39 +345,42 @@ __global__ __launch_bounds__(256) void k_nvfp4_receive(const uint8_t* __restrict
   // column phase: decode, 16-point RHT down each column, quantize with D_e.
   if (live) {
     float cm[16];
-    int ce[16];
-    const bool slow = s_slow[m] != 0;
     const int sh = 8 * ((cg >> 1) & 3);
+    const int dexp = s_dexp[m];
+    if (s_slow[m] == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
-      cm[i] = s * s_tq[r0 + i];  // exact: s has 4 significant bits, t/4 is a power of two
-      ce[i] = 0;
-    }
-    if (slow) {
+      for (int i = 0; i < 16; ++i) {
+        float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
+        cm[i] = s * s_tq[r0 + i];  // exact: s has 4 significant bits, t/4 is a power of two
+      }
+      column_pair<0, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<1, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<2, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<3, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+    } else {
+      int ce[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float t = s_t[r0 + i];
         ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
         cm[i] = t == 0.0f ? 0.0f : e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * rht_in_scale(i);
       }
+      column_pair<0, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<1, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<2, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<3, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
     }
-    const int dexp = s_dexp[m];
-    column_pair<0>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-    column_pair<1>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-    column_pair<2>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-    column_pair<3>(cw, cm, ce, slow, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
   }
   __syncthreads();
   // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...;
   // 16 consecutive threads cover one column's 128 contiguous code bytes.
-  const int b = tid & 15;
+  const int b = tid % kBlocks;
   if (!s_live[b]) return;
   const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
   const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
 #pragma unroll
-  for (int r = 0; r < (kTileCols * kBlocks) / 256; ++r) {
-    const int c = r * 16 + (tid >> 4);
+  for (int r = 0; r < (kTileCols * kBlocks) / kThreads; ++r) {
+    const int c = r * (kThreads / kBlocks) + tid / kBlocks;
     if (c >= ncols) break;
     const uint32_t h = (uint32_t)(col0 + c);
     *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[stage_at(c, b)];
@@ -453,8 +457,8 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
   const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_rt * n_ct * 256 >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
-  hipLaunchKernelGGL(k_nvfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, (hipStream_t)stream, packed,
+  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  hipLaunchKernelGGL(k_nvfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, packed,
                      (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
   return launch_status();

@@ -4,9 +4,11 @@ Bars: bit-exact for codes, block scales, token scales, MXFP8 data/scales,
 routing (counts, offsets, dst_row, src_row), the rowwise grouped operand, the
 expert scales D_e, unpacked BF16 and stochastic rounding; for values derived
 from FP32 amaxes or post-RHT values, the tolerance in ``gpu_util.tolerant_codes``
-(north bar: a differing E2M1 code is off by one grid step, in at most 1e-4 of
+(the bar: a differing E2M1 code is off by one grid step, in at most 1e-4 of
 elements).  Inputs come from ``workloads`` (seeded, synthetic).
 """
+
+import types
 
 import numpy as np
 import pytest
@@ -180,6 +182,27 @@ def test_direct_receive_bit_exact(dev, case):
     _check_receive(dev, w, packed_np, got, plan_np, w.x_bits.shape[1])
 
 
+def test_direct_receive_edge_rows(dev):
+    """Zero, -0, subnormal, tiny-t (t < 2^-100: the two-step decode), huge-t and
+    outlier rows routed among ordinary rows, so 16-row blocks mix them."""
+    rng = np.random.default_rng(21)
+    h = 256
+    edge = _edge_rows(h, rng)
+    x = np.concatenate([rng.standard_normal((70, h)) * 10.0 ** rng.uniform(-1, 1, (70, 1)), edge, edge, edge])
+    x = x[rng.permutation(len(x))]
+    bits = _bits(x)
+    topk = np.argsort(-rng.standard_normal((len(x), 4)), axis=1)[:, :2].astype(np.int32)
+    print("receive edge rows", bits.shape, flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    packed_np = onv.pack_rows(bits)
+    assert_bytes_equal(host(packed), packed_np, "pack")
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), 4, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    w = types.SimpleNamespace(topk_idx=topk, num_experts=4, alignment=16)
+    _check_receive(dev, w, packed_np, got, plan_np, h, exact=False)
+
+
 def test_direct_receive_config1(dev):
     w = workloads.config1()
     packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
@@ -217,10 +240,14 @@ def test_mxfp8_receive_bit_exact(dev):
 
 
 # ------------------------------------------------------------------ dSwiGLU
-@pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([5, 40, 0, 16, 1], 128),
-                                        ([300, 0, 129], 256), ([1], 64)])
-def test_dswiglu_two_stage(dev, counts, ffn):
-    w = workloads.small_dswiglu(sum(counts) + ffn, counts, ffn)
+@pytest.mark.parametrize("counts,ffn,dy_scales", [([0, 17, 64, 1, 0, 33], 64, None), ([5, 40, 0, 16, 1], 128, None),
+                                                  ([300, 0, 129], 256, None), ([1], 64, None),
+                                                  # tiny D (c = s*D below 2^-104: the general block path),
+                                                  # huge values, and an all-zero expert
+                                                  ([40, 24, 19, 8], 64, [1e-33, 1e32, 0.0, 1.0])])
+def test_dswiglu_two_stage(dev, counts, ffn, dy_scales):
+    w = workloads.small_dswiglu(sum(counts) + ffn, counts, ffn, dy_scales)
+    print(f"dswiglu counts={counts} ffn={ffn} dy_scales={dy_scales}", flush=True)
     out = mtb.dswiglu_nvfp4_quant(bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
     dx = host(out["dx"])
     # stage 1: dX within one BF16 ulp of the float64 oracle; amax == max |dX_gpu| exactly

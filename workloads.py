@@ -133,11 +133,14 @@ def small_dispatch(seed, tokens, hidden, num_experts, top_k, alignment=16, scale
                     topk_idx=topk.astype(np.int32), num_experts=num_experts, alignment=alignment)
 
 
-def small_dswiglu(seed, counts, ffn):
+def small_dswiglu(seed, counts, ffn, dy_scales=None):
+    """A small grouped dSwiGLU case; dy_scales (one per expert) rescale each expert's dy rows."""
     counts = np.asarray(counts, dtype=np.int32)
     t = int(counts.sum())
     r = _streams(seed, 2)
     pre = r[0].standard_normal((t, 2 * ffn))
     dy = r[1].standard_normal((t, ffn)) * 1e-2
+    if dy_scales is not None:
+        dy = dy * np.repeat(np.asarray(dy_scales, dtype=np.float64), counts)[:, None]
     return Workload(f"small-dswiglu-{t}x{ffn}", preact_bits=to_bf16_bits(pre), dy_bits=to_bf16_bits(dy),
                     counts=counts, num_experts=len(counts))
