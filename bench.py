@@ -48,6 +48,16 @@ CALL_SOURCES = {
     "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
 }
+# the kernels each call launches (as named in a rocprofv3 kernel trace)
+CALL_KERNELS = {
+    "route_plan": ["k_route_single (<= 16K entries) or k_route_count + k_route_scan + k_route_scatter"],
+    "nvfp4_pack": ["k_nvfp4_pack_wg (H >= 4096) or k_nvfp4_pack"], "nvfp4_pack_sr": ["k_nvfp4_pack_sr"],
+    "mxfp8_pack": ["k_mxfp8_pack"], "nvfp4_expert_scale": ["k_expert_scale"],
+    "nvfp4_expert_scale_grad": ["k_expert_scale"], "nvfp4_direct_receive": ["k_nvfp4_receive"],
+    "nvfp4_direct_receive_grad": ["k_nvfp4_receive"], "mxfp8_receive": ["k_mxfp8_receive"],
+    "nvfp4_unpack": ["k_nvfp4_unpack"],
+    "dswiglu_nvfp4_quant": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"],
+}
 STEP_NAMES = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
               "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
               "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
@@ -394,11 +404,11 @@ def roofline_of(call, nbytes, ms, elements=None, workload="dispatch"):
         tmul = elements * PHILOX_MULS_PER_ELEMENT / (ms / 1e3) / 1e12
         return dict(bound="alu", achieved=round(tmul, 3), peak=round(ALU_PEAK_TMULS, 2), unit="Tmul/s",
                     frac=round(tmul / ALU_PEAK_TMULS, 4), traffic=traffic_from_profile(call, workload),
-                    kernel=call, bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
+                    kernel=call, kernels=CALL_KERNELS[call], bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
     gbs = nbytes / (ms / 1e3) / 1e9
     return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                traffic=traffic_from_profile(call, workload), kernel=call, bytes_per_launch=nbytes,
-                ms_per_launch=round(ms, 5))
+                traffic=traffic_from_profile(call, workload), kernel=call, kernels=CALL_KERNELS[call],
+                bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
 
 
 def time_step(step, args):

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
   const int ncols = min(kTileCols, H - col0);
   const int toff = (H >> 1) + (H >> 4);
 
-  // round 1: source rows, expert offsets, the reciprocal table.
+  // phase 1: source rows, expert offsets, the reciprocal table.
   // src_row is -1 for padding and from off_E to r_cap.
   {
     int g = g_base + tid;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
   __syncthreads();
   const int off_end = min(s_offs[E], r_cap & ~15);  // whole 16-row blocks inside the outputs
 
-  // round 2a: each 16-row block's expert -> its decode exponent and output bases.
+  // phase 2a: each 16-row block's expert -> its decode exponent and output bases.
   if (tid < kBlocks) {
     const int gb = g_base + 16 * tid;
     int live = gb < off_end;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
     }
   }
 
-  // round 2b (one row per thread): t and the tile's scale words into LDS; the
+  // phase 2b (one row per thread): t and the tile's scale words into LDS; the
   // rowwise scales and t go out here.
   {
     const int g = g_base + tid;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
     }
   }
 
-  // round 2c: thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8)
+  // phase 2c: thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8)
   // of the 16 rows of block m (a wave reads 4 rows x 64 contiguous bytes per
   // instruction) and stores them unchanged to the rowwise operand.
   const int cg = tid & 15, m = tid >> 4;
