@@ -19,7 +19,8 @@ Source pages (cited by title and section):
 
 The pages name the formats and the passes but fix no rounding rule, constant,
 byte order or random-number mapping.  Every such rule is a reading written out
-in the docstring of the function that implements it (rules R1..R21).
+in the docstring of the function that implements it (rules R1..R21, and R8b:
+a second stochastic-rounding decision rule, the carry form).
 
 Precision: where a rule says ``fl32(.)`` the oracle computes in numpy float32
 (IEEE binary32, round-to-nearest-even, gradual underflow); everything else is

@@ -55,7 +55,7 @@ def _row_scales(ax32):
     return e, F.e4m3_encode(y)
 
 
-def pack_rows(x_bits, sr_seed=None, sr_counter_base=0, sr_mode="element"):
+def pack_rows(x_bits, sr_seed=None, sr_counter_base=0, sr_mode="element", sr_rule="threshold"):
     """R4-R9: BF16 rows [N, H] (uint16 bit patterns) -> packed rows uint8 [N, 9H/16 + 4].
 
     Block scale (R5): s_b = E4M3(a_b / (6 * t)), a_b = max |x| over the
@@ -72,9 +72,11 @@ def pack_rows(x_bits, sr_seed=None, sr_counter_base=0, sr_mode="element"):
     quotient: the quotient's binary expansion is finite or periodic with
     period <= 12 and never lands on a float32 midpoint).  v >= 6 gives index 7.
     Otherwise g_lo <= v < g_hi are neighbouring grid points,
-    frac = (v - g_lo) / (g_hi - g_lo) (exact), r = top 24 bits of the Philox
-    word for stream position n = counter_base + row*H + col, and the code
-    rounds up iff r * 2^-24 < frac.
+    frac = (v - g_lo) / (g_hi - g_lo) (exact), w = the Philox word for stream
+    position n = counter_base + row*H + col, and the code rounds up
+    * ``sr_rule="threshold"`` (R8): iff r * 2^-24 < frac, r = the top 24 bits of w;
+    * ``sr_rule="carry"`` (R8b): iff floor(frac * 2^32) + w >= 2^32, i.e. the
+      32 random bits are added below the kept precision and the sum truncated.
 
     The code's sign bit is the sign bit of x, always (also for -0 and for
     values that round to zero).
@@ -99,8 +101,13 @@ def pack_rows(x_bits, sr_seed=None, sr_counter_base=0, sr_mode="element"):
         rows = np.arange(n, dtype=np.uint64)[:, None]
         cols = np.arange(h, dtype=np.uint64)[None, :]
         pos = np.uint64(sr_counter_base) + rows * np.uint64(h) + cols
-        r = (sr_word(pos, sr_seed, sr_mode) >> np.uint32(8)).astype(np.float64)
-        idx = stochastic_e2m1_index(v, r)
+        w = sr_word(pos, sr_seed, sr_mode)
+        if sr_rule == "threshold":
+            idx = stochastic_e2m1_index(v, (w >> np.uint32(8)).astype(np.float64))
+        elif sr_rule == "carry":
+            idx = stochastic_e2m1_index_carry(v, w)
+        else:
+            raise ValueError(sr_rule)
     codes = (sign << np.uint8(3)) | idx
     out = np.empty((n, packed_row_bytes(h)), dtype=np.uint8)
     out[:, : h // 2] = F.pack_nibbles(codes)
@@ -119,6 +126,27 @@ def stochastic_e2m1_index(v, r):
     with np.errstate(divide="ignore", invalid="ignore"):
         frac = np.where(hi > lo, (v - g_lo) / np.where(hi > lo, g_hi - g_lo, 1.0), 0.0)
     up = (hi > lo) & (r * 2.0 ** -24 < frac)
+    return np.where(up, hi, lo).astype(np.uint8)
+
+
+def stochastic_e2m1_index_carry(v, w):
+    """R8b rounding step: magnitude v >= 0 (float32 values), w 32-bit random words.
+
+    v >= 6 gives index 7.  Otherwise frac is v's position between its two
+    neighbouring grid points (exact in float64: v has 24 significant bits and
+    the grid steps are powers of two), D = floor(frac * 2^32), and the index
+    rounds up iff D + w >= 2^32.  So P(up) = D / 2^32 over uniform w, and grid
+    points (frac = 0) never move.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    w = np.asarray(w, dtype=np.uint64)
+    lo = np.clip(np.searchsorted(F.E2M1_GRID, v, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    g_lo, g_hi = F.E2M1_GRID[lo], F.E2M1_GRID[hi]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        frac = np.where(hi > lo, (v - g_lo) / np.where(hi > lo, g_hi - g_lo, 1.0), 0.0)
+    d = np.floor(np.ldexp(frac, 32)).astype(np.uint64)
+    up = (hi > lo) & (d + w >= np.uint64(1 << 32))
     return np.where(up, hi, lo).astype(np.uint8)
 
 

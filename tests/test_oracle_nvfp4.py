@@ -212,6 +212,78 @@ def test_sr_word_positions():
     np.testing.assert_array_equal(a[1:], b)
 
 
+# ------------------------------------------------------------------ stochastic rounding, carry rule (R8b)
+def test_sr_carry_on_grid_values_never_move():
+    rng = np.random.default_rng(18)
+    g = F.E2M1_GRID[rng.integers(0, 8, size=(16, 64))]
+    g.reshape(16, -1, 16)[:, :, 3] = 6.0         # every block holds a 6: its values sit on the grid
+    bits = F.f32_to_bf16((g * 448.0 * 2.0 ** -5).astype(np.float32))
+    np.testing.assert_array_equal(nvfp4.pack_rows(bits), nvfp4.pack_rows(bits, sr_seed=7, sr_rule="carry"))
+
+
+def test_sr_carry_matches_exact_rationals():
+    """R8b against exact rational arithmetic: up iff frac + w / 2^32 >= 1, frac the exact
+    position of v between its grid neighbours (Python fractions, no floating point)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(19)
+    v = rng.uniform(0, 6.5, 4000).astype(np.float32)
+    v[:50] = np.float32(2.0) ** -rng.integers(10, 140, 50).astype(np.float32)   # tiny values
+    w = rng.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32)
+    idx = nvfp4.stochastic_e2m1_index_carry(v.astype(np.float64), w)
+    grid = [Fraction(g) for g in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    for vi, wi, got in zip(v, w, idx):
+        fv = Fraction(float(vi))
+        if fv >= 6:
+            assert got == 7
+            continue
+        lo = max(i for i in range(7) if grid[i] <= fv)
+        frac = (fv - grid[lo]) / (grid[lo + 1] - grid[lo])
+        want = lo + 1 if frac + Fraction(int(wi), 2 ** 32) >= 1 else lo
+        assert got == want, (float(vi), int(wi))
+
+
+def test_sr_carry_boundary_words():
+    """For each v the words that round up are exactly [2^32 - D, 2^32), D = floor(frac 2^32):
+    P(up) = D / 2^32, so the bias is below 2^-32 of a grid step."""
+    from fractions import Fraction
+    rng = np.random.default_rng(20)
+    v = rng.uniform(0, 6, 500).astype(np.float32)
+    grid = [Fraction(g) for g in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    for vi in v:
+        fv = Fraction(float(vi))
+        lo = max(i for i in range(7) if grid[i] <= fv)
+        d = int((fv - grid[lo]) / (grid[lo + 1] - grid[lo]) * 2 ** 32)
+        if d == 0:
+            continue
+        ws = np.array([2 ** 32 - d - 1, 2 ** 32 - d, 2 ** 32 - 1, 0], dtype=np.uint32)
+        got = nvfp4.stochastic_e2m1_index_carry(np.full(4, float(vi)), ws)
+        np.testing.assert_array_equal(got, [lo, lo + 1, lo + 1, lo if d < 2 ** 32 else lo + 1])
+
+
+def test_sr_carry_unbiased_1e6_draws():
+    vals = []
+    for lo, hi in zip(F.E2M1_GRID[:-1], F.E2M1_GRID[1:]):
+        vals += [lo + (hi - lo) * f for f in (0.0625, 0.5, 0.9375)]
+    n = 1_000_000
+    for j, v in enumerate(np.array(vals, dtype=np.float32)):
+        w = sr_word(np.arange(n, dtype=np.uint64) + np.uint64(j * n), 1234, "element")
+        q = F.E2M1_GRID[nvfp4.stochastic_e2m1_index_carry(np.full(n, v, dtype=np.float64), w)]
+        lo = F.E2M1_GRID[np.searchsorted(F.E2M1_GRID, v, side="right") - 1]
+        hi = F.E2M1_GRID[np.searchsorted(F.E2M1_GRID, v, side="right")]
+        p = (v - lo) / (hi - lo)
+        assert abs(q.mean() - v) < 5 * (hi - lo) * np.sqrt(p * (1 - p) / n), (v, q.mean())
+        assert set(np.unique(q)) <= {lo, hi}
+
+
+def test_sr_carry_scales_and_positions():
+    """Scales and t are the deterministic ones; the counter of (row, col) is base + row*H + col."""
+    w = workloads.small_dispatch(13, 8, 128, 2, 1)
+    a = nvfp4.pack_rows(w.x_bits, sr_seed=5, sr_counter_base=300, sr_rule="carry")
+    b = nvfp4.pack_rows(w.x_bits[2:], sr_seed=5, sr_counter_base=300 + 2 * 128, sr_rule="carry")
+    np.testing.assert_array_equal(a[2:], b)
+    np.testing.assert_array_equal(a[:, 64:], nvfp4.pack_rows(w.x_bits)[:, 64:])
+
+
 def test_block_scale_exact_rounding_exhaustive():
     """R5: the E4M3 block scale of a_b / (6 * 2^e) for every positive finite BF16 a_b
     and e in [-24, 24] equals torch's E4M3 cast of the float32-rounded quotient (the
