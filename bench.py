@@ -58,6 +58,9 @@ CALL_KERNELS = {
     "nvfp4_unpack": ["k_nvfp4_unpack"],
     "dswiglu_nvfp4_quant": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"],
 }
+# the combine-backward SR pack: one Philox4x32-10 word per element at counter
+# row*hidden + col (element mode), carry-form decision (the hardware converter)
+SR_MODE = 3  # EP_ROUND_SR_ELEMENT_CARRY
 STEP_NAMES = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
               "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
               "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
@@ -187,7 +190,7 @@ class Step:
             lambda: m.ep_mxfp8_direct_receive(self.mx[: i["T"] * H].view(i["T"], H),
                                               self.mx[i["T"] * H:].view(i["T"], H // 32), self.plan, out=self.mx_out),
             lambda: m.ep_nvfp4_unpack(self.packed, H, src_row=self.src_valid, out=self.unpacked),
-            lambda: m.ep_nvfp4_pack(i["grad"], m.EP_ROUND_SR_ELEMENT, i["sr"], out=self.packed_g),
+            lambda: m.ep_nvfp4_pack(i["grad"], SR_MODE, i["sr"], out=self.packed_g),
             lambda: m.ep_nvfp4_expert_scale(self.packed_g, H, self.plan, col_scale=self.recv_g["col_scale"]),
             lambda: m.ep_nvfp4_direct_receive_scaled(self.packed_g, H, self.plan, self.recv_g),
             lambda: m.dswiglu_nvfp4_quant(i["preact"], i["dy"], self.counts, out=self.dsw, workspace=self.dsw_ws),
@@ -294,7 +297,7 @@ class ConfigStep:
                                                         out=self.plan), b["route_plan"])
         if n == 4:
             self.sr = torch.tensor([w.sr_seed, w.sr_counter_base], dtype=torch.int64, device=dev)
-            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(self.x, m.EP_ROUND_SR_ELEMENT, self.sr, out=self.packed),
+            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(self.x, SR_MODE, self.sr, out=self.packed),
                       b["nvfp4_pack_sr"])
         else:
             self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(self.x, out=self.packed), b["nvfp4_pack"])
@@ -358,7 +361,7 @@ def cpu_baseline(inp, n_tok):
     d, s = mxfp8.pack_rows(x)
     mxfp8.grouped_receive(d, s, plan["src_row"])
     nvfp4.unpack_rows(packed, H, plan["src_row"][plan["src_row"] >= 0])
-    pg = nvfp4.pack_rows(grad, sr_seed=1234)
+    pg = nvfp4.pack_rows(grad, sr_seed=1234, sr_rule="carry")
     receive.direct_receive(pg, H, topk, E, A)
     counts = plan["counts"]
     dx = dswiglu.dswiglu(pre, dy)

@@ -69,6 +69,8 @@ enum ep_status {
 #define EP_ROUND_NEAREST 0   /* round-to-nearest-even                          */
 #define EP_ROUND_SR_ELEMENT 1 /* Philox4x32-10 word 0 at counter n             */
 #define EP_ROUND_SR_STREAM 2  /* 32-bit word n of the Philox4x32-10 stream     */
+#define EP_ROUND_SR_ELEMENT_CARRY 3 /* as SR_ELEMENT, carry-form decision      */
+#define EP_ROUND_SR_STREAM_CARRY 4  /* as SR_STREAM, carry-form decision       */
 
 /* top-k index dtypes for ep_route_plan */
 #define EP_IDX_INT32 0
@@ -112,9 +114,14 @@ size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts);
  *   code = sign(x) | E2M1 index of |x| / (s_b t) (0 if s_b = 0).
  *   round_mode EP_ROUND_NEAREST: round-to-nearest-even, sr_state ignored.
  *   round_mode EP_ROUND_SR_*: stochastic rounding of v = fl32(|x|/(s_b t))
- *     with r = top 24 bits of a Philox4x32-10 word (key = seed), rounding up
- *     iff r*2^-24 < (v - g_lo)/(g_hi - g_lo); stream position
- *     n = counter_base + row*hidden + col.  sr_state is a DEVICE pointer to
+ *     between its grid neighbours g_lo <= v < g_hi with the Philox4x32-10
+ *     word w (key = seed) of stream position n = counter_base + row*hidden
+ *     + col (SR_ELEMENT*: counter n, word 0; SR_STREAM*: counter n>>2, word
+ *     n&3); frac = (v - g_lo)/(g_hi - g_lo).  SR_ELEMENT, SR_STREAM: up iff
+ *     (w >> 8) * 2^-24 < frac.  SR_*_CARRY: up iff floor(frac*2^32) + w >=
+ *     2^32 (the 32 random bits added below the kept precision, then
+ *     truncated -- the decision gfx950's stochastic FP4 conversion makes,
+ *     which these modes use).  sr_state is a DEVICE pointer to
  *     two uint64 {seed, counter_base} (read by the kernel, so a captured
  *     graph can be re-seeded between replays); required for SR modes.
  *   Requires hidden a positive multiple of 64, hidden <= 16384, rows >= 0. */

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_token_block.so")
 
 EP_ROUND_NEAREST, EP_ROUND_SR_ELEMENT, EP_ROUND_SR_STREAM = 0, 1, 2
+EP_ROUND_SR_ELEMENT_CARRY, EP_ROUND_SR_STREAM_CARRY = 3, 4
 EP_IDX_INT32, EP_IDX_INT64 = 0, 1
 EP_DEVERR_EXPERT_ID = 1
 

@@ -70,6 +70,8 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_nvfp4_pack(N, 4, 128, P, 0, N, N) == -1
     assert lib.ep_nvfp4_pack(P, 4, 128, P, 1, N, N) == -1           # SR without state
     assert lib.ep_nvfp4_pack(P, 4, 128, P, 7, N, N) == -5
+    assert lib.ep_nvfp4_pack(P, 4, 128, P, 5, N, N) == -5           # past the last SR mode
+    assert lib.ep_nvfp4_pack(P, 4, 128, P, 3, N, N) == -1           # carry-form SR without state
     assert lib.ep_nvfp4_pack(P, 0, 128, N, 0, N, N) == 0            # empty: nothing to do
     assert lib.ep_mxfp8_pack(P, 4, 48, P, P, N) == -2
     assert lib.ep_nvfp4_unpack(P, 4, 128, N, 5, P, N) == -2         # rows_out != rows_in without a map

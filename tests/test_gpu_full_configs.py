@@ -43,10 +43,13 @@ def _check_dispatch(dev, w, name, sr=None, rng_seed=0, n_rows=96, n_col_samples=
         opack = lambda rows: onv.pack_rows(w.x_bits[rows])
     else:
         st = torch.tensor([sr[0], sr[1]], dtype=torch.int64, device=dev)
-        packed = mtb.ep_nvfp4_pack(x, mtb.EP_ROUND_SR_ELEMENT, st)
+        mode = sr[2] if len(sr) > 2 else mtb.EP_ROUND_SR_ELEMENT
+        rule = "carry" if mode == mtb.EP_ROUND_SR_ELEMENT_CARRY else "threshold"
+        packed = mtb.ep_nvfp4_pack(x, mode, st)
         # counter positions follow the source row: pack the sampled rows at their own offsets
         opack = lambda rows: np.concatenate([onv.pack_rows(w.x_bits[r:r + 1], sr_seed=sr[0],
-                                                           sr_counter_base=sr[1] + int(r) * H) for r in rows])
+                                                           sr_counter_base=sr[1] + int(r) * H, sr_rule=rule)
+                                             for r in rows])
     # pack: sampled rows (with the extremes of the t range among them)
     t_all = _token_t(w.x_bits)
     rows = np.unique(np.concatenate([rng.integers(0, T, n_rows), [int(np.argmin(t_all)), int(np.argmax(t_all)), T - 1]]))
@@ -139,6 +142,13 @@ def test_config3_dsv3_share(dev):
 def test_config4_sr_combine_backward(dev):
     w = workloads.config4()
     _check_dispatch(dev, w, "config4", sr=(w.sr_seed, w.sr_counter_base), rng_seed=4, n_rows=48)
+
+
+def test_config4_sr_carry_combine_backward(dev):
+    """The carry-form SR mode (the one bench.py times for the combine backward)."""
+    w = workloads.config4()
+    _check_dispatch(dev, w, "config4 carry", sr=(w.sr_seed, w.sr_counter_base, mtb.EP_ROUND_SR_ELEMENT_CARRY),
+                    rng_seed=5, n_rows=48)
 
 
 def test_config5_dswiglu(dev):

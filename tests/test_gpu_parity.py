@@ -84,7 +84,8 @@ def test_pack_empty_and_config1(dev):
     assert_bytes_equal(host(mtb.ep_nvfp4_unpack(packed, 1024)), onv.unpack_rows(want, 1024), "unpack config1")
 
 
-@pytest.mark.parametrize("mode,seed,base", [(1, 1234, 0), (1, 2 ** 40 + 3, 12345), (2, 1234, 0), (2, 77, 6)])
+@pytest.mark.parametrize("mode,seed,base", [(1, 1234, 0), (1, 2 ** 40 + 3, 12345), (2, 1234, 0), (2, 77, 6),
+                                           (3, 1234, 0), (3, 2 ** 40 + 3, 12345), (4, 1234, 0), (4, 77, 6)])
 def test_stochastic_rounding_bit_exact(dev, mode, seed, base):
     rng = np.random.default_rng(seed % 1000 + mode)
     h = 256
@@ -94,7 +95,8 @@ def test_stochastic_rounding_bit_exact(dev, mode, seed, base):
     st = torch.tensor([seed, base], dtype=torch.int64, device=dev)
     print(f"sr mode={mode} seed={seed} base={base}", flush=True)
     packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev), round_mode=mode, sr_state=st)
-    want = onv.pack_rows(bits, sr_seed=seed, sr_counter_base=base, sr_mode="element" if mode == 1 else "stream")
+    want = onv.pack_rows(bits, sr_seed=seed, sr_counter_base=base, sr_mode="element" if mode in (1, 3) else "stream",
+                         sr_rule="carry" if mode >= 3 else "threshold")
     assert_bytes_equal(host(packed), want, f"SR mode {mode}")
 
 
