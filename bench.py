@@ -199,8 +199,9 @@ class Step:
     def run_concurrent(self):
         """The same calls as ``run`` as four dependent chains on their own streams
         (default priority), joined back into the calling stream: the NVFP4 dispatch
-        chain, the MXFP8 chain, the SR combine-backward chain and the dSwiGLU chain
-        wait only for what they read (the route plan)."""
+        chain, the MXFP8 chain, the SR combine-backward chain and the dSwiGLU chain.
+        Each call waits only for what it reads: the three packs start at once,
+        beside the route plan."""
         import torch
         c = self.calls()
         main = torch.cuda.current_stream()
@@ -212,6 +213,10 @@ class Step:
             c[7]()                                   # SR pack of the gradient rows (independent of routing)
         with torch.cuda.stream(self.side[1]):
             c[4]()                                   # MXFP8 pack
+        with torch.cuda.stream(self.side[2]):
+            c[1]()                                   # NVFP4 pack
+            packed = torch.cuda.Event()
+            packed.record(self.side[2])
         c[0]()                                       # route plan
         routed = torch.cuda.Event()
         routed.record(main)
@@ -223,7 +228,8 @@ class Step:
             c[5]()                                   # MXFP8 receive
         with torch.cuda.stream(self.side[2]):
             c[10]()                                  # dSwiGLU + FC1-grad quantization (needs the counts)
-        c[1](); c[2](); c[3](); c[6]()              # NVFP4 pack, expert scale, receive, unpack
+        main.wait_event(packed)
+        c[2](); c[3](); c[6]()                       # NVFP4 expert scale, receive, unpack
         for st in self.side:
             main.wait_stream(st)
 
