@@ -47,6 +47,7 @@ CALL_SOURCES = {
     "nvfp4_direct_receive": ("receive.hip",), "nvfp4_direct_receive_grad": ("receive.hip",),
     "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
+    "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
 }
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
@@ -57,6 +58,8 @@ CALL_KERNELS = {
     "nvfp4_direct_receive_grad": ["k_nvfp4_receive"], "mxfp8_receive": ["k_mxfp8_receive"],
     "nvfp4_unpack": ["k_nvfp4_unpack"],
     "dswiglu_nvfp4_quant": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"],
+    "nvfp4_pack_scatter": ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"],
+    "nvfp4_columnwise_grouped": ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"],
 }
 # the combine-backward SR pack: one Philox4x32-10 word per element at counter
 # row*hidden + col (element mode), carry-form decision (the hardware converter)
@@ -77,7 +80,8 @@ def parse():
     p.add_argument("--only", default=None,
                    help="profiling aid: run only this call of the path (or 'copy': a 1 GiB device copy, the "
                         "reference for memory counters) --steps times, eagerly, and print what ran")
-    p.add_argument("--workload", default="dispatch", choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5"],
+    p.add_argument("--workload", default="dispatch",
+                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f"],
                    help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
                         "configuration's own path, for per-kernel figures")
     return p.parse_args()
@@ -259,7 +263,8 @@ class ConfigStep:
         import moe_token_block_amd as m
         import workloads
         self.m = m
-        n = int(which[3:])
+        fused = which.endswith("f")
+        n = int(which[3:-1] if fused else which[3:])
         w = workloads.CONFIGS[n]()
         self.w, self.n = w, n
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -301,6 +306,17 @@ class ConfigStep:
         b = algorithmic_bytes(T, H, k, E, r_cap, R, R, 0)
         self._add("route_plan", lambda: m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws,
                                                         out=self.plan), b["route_plan"])
+        if fused:
+            # sender-side fused dispatch: pack straight into the grouped rows, then
+            # the columnwise operand from those contiguous rows
+            rb = row_bytes(H)
+            self._add("nvfp4_pack_scatter", lambda: m.ep_nvfp4_pack_scatter(self.x, self.plan, out=self.recv),
+                      T * H * 2 + R * rb)
+            self._add("nvfp4_columnwise_grouped", lambda: m.ep_nvfp4_columnwise_grouped(self.recv, H, self.plan,
+                                                                                        out=self.recv),
+                      R * rb + R * (H // 2 + H // 16) + E * 4)
+            self.desc = dict(workload=w.name + " (fused dispatch)", tokens=T, hidden=H, experts=E, top_k=k, alignment=A)
+            return
         if n == 4:
             self.sr = torch.tensor([w.sr_seed, w.sr_counter_base], dtype=torch.int64, device=dev)
             self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(self.x, SR_MODE, self.sr, out=self.packed),

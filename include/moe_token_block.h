@@ -227,6 +227,35 @@ int32_t ep_mxfp8_direct_receive(const uint8_t* data, const uint8_t* scales, int6
                                 int64_t hidden, int64_t r_cap, const int32_t* src_row,
                                 uint8_t* g_data, uint8_t* g_scales, void* stream);
 
+/* ---------------------------------------------------------------- fused dispatch */
+
+/* Sender-side pack + scatter (P1, PR description: token rows are quantized
+ * once into the format the expert GEMM reads, with no BF16 round trip; here
+ * the pack writes each packed row directly into its grouped slots, so the
+ * intermediate [tokens, 9H/16+4] buffer and its k-fold re-read disappear).
+ *   x [tokens, hidden] BF16; dst_row [tokens, top_k] int32 from
+ *   ep_route_plan (entries outside [0, r_cap) are skipped); counts [E] and
+ *   offsets [E+1] from the same plan.  Writes row_codes [r_cap, hidden/2],
+ *   row_scales [r_cap, hidden/16], row_t [r_cap]: byte-identical to
+ *   ep_nvfp4_pack (round to nearest) followed by the rowwise operand of
+ *   ep_nvfp4_direct_receive (padding rows below offsets[E] zero, rows from
+ *   offsets[E] to r_cap untouched).  top_k <= 32 (EP_ERR_RANGE), hidden as
+ *   for ep_nvfp4_pack, 1 <= num_experts <= 1024. */
+int32_t ep_nvfp4_pack_scatter(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t top_k,
+                              const int32_t* dst_row, int64_t num_experts, int64_t r_cap,
+                              const int32_t* counts, const int32_t* offsets, uint8_t* row_codes,
+                              uint8_t* row_scales, float* row_t, void* stream);
+
+/* The columnwise half of the direct receive from a grouped rowwise operand
+ * (as written by ep_nvfp4_pack_scatter or ep_nvfp4_direct_receive): the rows
+ * are contiguous, so there is no gather.  D_e = 4 * max row_t over expert e's
+ * rows -> col_scale [E]; col_codes / col_scales as in ep_nvfp4_direct_receive,
+ * byte-identical.  hidden % 64 == 0, 1 <= num_experts <= 1024. */
+int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const uint8_t* row_scales, const float* row_t,
+                                    int64_t hidden, int64_t num_experts, int64_t r_cap,
+                                    const int32_t* offsets, uint8_t* col_codes, uint8_t* col_scales,
+                                    float* col_scale, void* stream);
+
 /* ---------------------------------------------------------------- dSwiGLU */
 
 /* Fused grouped dSwiGLU epilogue with per-expert amax, then FC1-gradient NVFP4

@@ -45,6 +45,8 @@ _SIGS = {
     "ep_nvfp4_expert_scale": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_scaled": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
@@ -243,6 +245,44 @@ def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
             _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _ptr(out.get("col_scale")),
             _stream(dev)), "ep_nvfp4_direct_receive")
+    return out
+
+
+def ep_nvfp4_pack_scatter(x, plan, out=None):
+    """BF16 token rows [T, H] packed straight into the grouped rowwise operand of a
+    routing plan (each token once, written to its top-k grouped rows; padding rows
+    zeroed): the same bytes as ep_nvfp4_pack followed by the rowwise receive."""
+    dev = _dev(x)
+    _need(x, torch.bfloat16, "x")
+    t, h = x.shape
+    r_cap, e = plan["r_cap"], plan["num_experts"]
+    k = plan["dst_row"].shape[1] if plan["dst_row"].dim() == 2 else 1
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = dict(row_codes=torch.empty((r_cap, h // 2), **u8), row_scales=torch.empty((r_cap, h // 16), **u8),
+                   row_t=torch.empty(r_cap, dtype=torch.float32, device=dev))
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_pack_scatter(_ptr(x), t, h, k, _ptr(plan["dst_row"]), e, r_cap, _ptr(plan["counts"]),
+                                           _ptr(plan["offsets"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
+                                           _ptr(out["row_t"]), _stream(dev)), "ep_nvfp4_pack_scatter")
+    return out
+
+
+def ep_nvfp4_columnwise_grouped(rowwise, hidden, plan, out=None):
+    """D_e and the RHT columnwise operand from a grouped rowwise operand
+    (``rowwise``: dict with row_codes, row_scales, row_t): the same bytes as the
+    direct receive's columnwise outputs."""
+    dev = _dev(rowwise["row_codes"])
+    r_cap, e = plan["r_cap"], plan["num_experts"]
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = dict(col_codes=torch.empty(r_cap * hidden // 2, **u8), col_scales=torch.empty(r_cap * hidden // 16, **u8),
+                   col_scale=torch.empty(e, dtype=torch.float32, device=dev))
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_columnwise_grouped(
+            _ptr(rowwise["row_codes"]), _ptr(rowwise["row_scales"]), _ptr(rowwise["row_t"]), hidden, e, r_cap,
+            _ptr(plan["offsets"]), _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]),
+            _stream(dev)), "ep_nvfp4_columnwise_grouped")
     return out
 
 

@@ -76,12 +76,43 @@ __device__ __forceinline__ float sr_round(float u, int kexp, uint32_t r) {
   return __builtin_copysignf(res, u);
 }
 
-template <int NB>
-__device__ __forceinline__ void store_block(uint8_t* orow, int H, int j, uint32_t o0, uint32_t o1, uint32_t sc) {
-  uint32_t* cw = reinterpret_cast<uint32_t*>(orow + 8 * j);
+// Where a packed row goes: the packed-row buffer (codes, scales and t of row r
+// at r * row_bytes) or the grouped rowwise operand (codes, scales and t in
+// three arrays, grouped row g at g * H/2, g * H/16 and g).
+constexpr int kMaxScatter = 32;  // top-k limit of the fused pack + scatter
+
+struct RowOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  uint8_t* t;
+  uint32_t cstride, sstride, tstride;  // bytes between consecutive rows
+};
+
+__device__ __forceinline__ void store_block(const RowOut& o, uint32_t g, int j, uint32_t o0, uint32_t o1, uint32_t sc) {
+  uint32_t* cw = reinterpret_cast<uint32_t*>(o.codes + (size_t)g * o.cstride + 8 * j);
   cw[0] = o0;
   cw[1] = o1;
-  orow[(H >> 1) + j] = (uint8_t)sc;
+  o.scales[(size_t)g * o.sstride + j] = (uint8_t)sc;
+}
+
+__device__ __forceinline__ void store_t(const RowOut& o, uint32_t g, float t) {
+  *reinterpret_cast<float*>(o.t + (size_t)g * o.tstride) = t;
+}
+
+// The destinations of token row `row`: itself (packed rows), or its top-k
+// grouped rows dst_row[row*k + j] (SCATTER; entries outside [0, r_cap) skipped).
+template <bool SCATTER>
+__device__ __forceinline__ int row_dests(int row, const int32_t* dst_row, int k, int r_cap, uint32_t* g) {
+  if (!SCATTER) {
+    g[0] = (uint32_t)row;
+    return 1;
+  }
+  int n = 0;
+  for (int j = 0; j < k; ++j) {
+    int d = dst_row[(size_t)row * k + j];
+    if (d >= 0 && d < r_cap) g[n++] = (uint32_t)d;
+  }
+  return n;
 }
 
 __device__ __forceinline__ void encode_rne(const uint4& v0, const uint4& v1, const BlockQuant& q,
@@ -177,9 +208,9 @@ __device__ __forceinline__ void encode_sr(const uint4& v0, const uint4& v1, cons
 }
 
 // Round-to-nearest: the row stays in VGPRs between the max and the encode.
-template <int NB>
-__global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__ x, int rows, int H,
-                                                   uint8_t* __restrict__ out, int row_bytes) {
+template <int NB, bool SCATTER>
+__global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__ x, int rows, int H, const RowOut o,
+                                                   const int32_t* __restrict__ dst_row, int k, int r_cap) {
   const int lane = threadIdx.x & 63;
   const int row = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
   if (row >= rows) return;
@@ -205,8 +236,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__
   }
   rmax = wave_max_u32(rmax);
   const int e = token_exponent(__uint_as_float(rmax << 16));
-  uint8_t* orow = out + (size_t)row * row_bytes;
-  if (lane == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+  uint32_t g[SCATTER ? kMaxScatter : 1];
+  const int nd = row_dests<SCATTER>(row, dst_row, k, r_cap, g);
+  if (lane == 0)
+    for (int d = 0; d < nd; ++d) store_t(o, g[d], __builtin_ldexpf(1.0f, e));
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     int j = c * 64 + lane;
@@ -214,16 +247,16 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__
     uint32_t sc, o0, o1;
     BlockQuant q = nvfp4_block(__uint_as_float(bmax[c] << 16), e, sc);
     encode_rne(v[c][0], v[c][1], q, o0, o1);
-    store_block<NB>(orow, H, j, o0, o1, sc);
+    for (int d = 0; d < nd; ++d) store_block(o, g[d], j, o0, o1, sc);
   }
 }
 
 // Rows of >= 256 blocks (H >= 4096): one workgroup of 256 threads per row,
 // thread j owns blocks j, j+256, ... (NBW of them), so a 4096-wide row is one
 // block per thread; the row max goes through LDS.
-template <int NBW>
-__global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restrict__ x, int rows, int H,
-                                                      uint8_t* __restrict__ out, int row_bytes) {
+template <int NBW, bool SCATTER>
+__global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restrict__ x, int rows, int H, const RowOut o,
+                                                      const int32_t* __restrict__ dst_row, int k, int r_cap) {
   __shared__ uint32_t red[4];
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -251,8 +284,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restric
   __syncthreads();
   rmax = max(max(red[0], red[1]), max(red[2], red[3]));
   const int e = token_exponent(__uint_as_float(rmax << 16));
-  uint8_t* orow = out + (size_t)row * row_bytes;
-  if (tid == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+  uint32_t g[SCATTER ? kMaxScatter : 1];
+  const int nd = row_dests<SCATTER>(row, dst_row, k, r_cap, g);
+  if (tid == 0)
+    for (int d = 0; d < nd; ++d) store_t(o, g[d], __builtin_ldexpf(1.0f, e));
 #pragma unroll
   for (int c = 0; c < NBW; ++c) {
     int j = c * 256 + tid;
@@ -260,15 +295,14 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restric
     uint32_t sc, o0, o1;
     BlockQuant q = nvfp4_block(__uint_as_float(bmax[c] << 16), e, sc);
     encode_rne(v[c][0], v[c][1], q, o0, o1);
-    store_block<1>(orow, H, j, o0, o1, sc);
+    for (int d = 0; d < nd; ++d) store_block(o, g[d], j, o0, o1, sc);
   }
 }
 
 // Stochastic rounding: ALU-bound on the Philox blocks, so the second pass
 // re-reads each block (from cache) instead of holding the row in VGPRs.
 template <int MODE>
-__global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restrict__ x, int rows, int H,
-                                                      uint8_t* __restrict__ out, int row_bytes,
+__global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restrict__ x, int rows, int H, const RowOut o,
                                                       const uint64_t* __restrict__ sr_state) {
   const int lane = threadIdx.x & 63;
   const int row = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
@@ -283,8 +317,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restric
   }
   rmax = wave_max_u32(rmax);
   const int e = token_exponent(__uint_as_float(rmax << 16));
-  uint8_t* orow = out + (size_t)row * row_bytes;
-  if (lane == 0) *reinterpret_cast<float*>(orow + (H >> 1) + (H >> 4)) = __builtin_ldexpf(1.0f, e);
+  if (lane == 0) store_t(o, (uint32_t)row, __builtin_ldexpf(1.0f, e));
   const uint64_t seed = sr_state[0];
   const uint32_t seed_lo = (uint32_t)seed, seed_hi = (uint32_t)(seed >> 32);
   const uint64_t n_row = sr_state[1] + (uint64_t)row * (uint64_t)H;
@@ -295,7 +328,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restric
     uint32_t sc, o0, o1;
     BlockQuant q = nvfp4_block(__uint_as_float((a > b ? a : b) << 16), e, sc);
     encode_sr<MODE>(v0, v1, q, n_row + (uint64_t)(16 * j), seed_lo, seed_hi, o0, o1);
-    store_block<1>(orow, H, j, o0, o1, sc);
+    store_block(o, (uint32_t)row, j, o0, o1, sc);
   }
 }
 
@@ -370,6 +403,34 @@ __global__ __launch_bounds__(256) void k_mxfp8_pack(const uint16_t* __restrict__
 
 using namespace mtb;
 
+// Round-to-nearest pack launch: workgroup per row for H >= 4096, else wave per row.
+template <bool SCATTER>
+static void launch_rne_pack(const uint16_t* x, int rows, int H, const RowOut& o, const int32_t* dst_row, int k,
+                            int r_cap, hipStream_t s) {
+  const int nb = (H / 16 + 63) / 64;
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (H >= 4096) {
+    const int nbw = (H / 16 + 255) / 256;
+    dim3 g1((unsigned)rows);
+    if (nbw <= 1)
+      hipLaunchKernelGGL((k_nvfp4_pack_wg<1, SCATTER>), g1, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+    else if (nbw <= 2)
+      hipLaunchKernelGGL((k_nvfp4_pack_wg<2, SCATTER>), g1, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+    else
+      hipLaunchKernelGGL((k_nvfp4_pack_wg<4, SCATTER>), g1, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  } else if (nb <= 1) {
+    hipLaunchKernelGGL((k_nvfp4_pack<1, SCATTER>), grid, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  } else if (nb <= 2) {
+    hipLaunchKernelGGL((k_nvfp4_pack<2, SCATTER>), grid, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  } else if (nb <= 4) {
+    hipLaunchKernelGGL((k_nvfp4_pack<4, SCATTER>), grid, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  } else if (nb <= 8) {
+    hipLaunchKernelGGL((k_nvfp4_pack<8, SCATTER>), grid, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  } else {
+    hipLaunchKernelGGL((k_nvfp4_pack<16, SCATTER>), grid, block, 0, s, x, rows, H, o, dst_row, k, r_cap);
+  }
+}
+
 MTB_EXPORT int32_t ep_nvfp4_pack(const uint16_t* x, int64_t rows, int64_t hidden, uint8_t* packed,
                                  int32_t round_mode, const uint64_t* sr_state, void* stream) {
   if (rows < 0 || hidden <= 0 || hidden % 64 != 0 || hidden > 16384) return EP_ERR_SHAPE;
@@ -379,40 +440,64 @@ MTB_EXPORT int32_t ep_nvfp4_pack(const uint16_t* x, int64_t rows, int64_t hidden
   if (!x || !packed) return EP_ERR_NULL;
   if (round_mode != EP_ROUND_NEAREST && !sr_state) return EP_ERR_NULL;
   const int H = (int)hidden;
-  const int row_bytes = 9 * H / 16 + 4;
-  const int nb = (H / 16 + 63) / 64;
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowOut o{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
   if (round_mode == EP_ROUND_SR_ELEMENT) {
-    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT>, grid, block, 0, s, x, (int)rows, H, o, sr_state);
   } else if (round_mode == EP_ROUND_SR_STREAM) {
-    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes, sr_state);
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM>, grid, block, 0, s, x, (int)rows, H, o, sr_state);
   } else if (round_mode == EP_ROUND_SR_ELEMENT_CARRY) {
-    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT_CARRY>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes,
-                       sr_state);
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT_CARRY>, grid, block, 0, s, x, (int)rows, H, o, sr_state);
   } else if (round_mode == EP_ROUND_SR_STREAM_CARRY) {
-    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM_CARRY>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes,
-                       sr_state);
-  } else if (H >= 4096) {
-    const int nbw = (H / 16 + 255) / 256;
-    dim3 g1((unsigned)rows);
-    if (nbw <= 1)
-      hipLaunchKernelGGL(k_nvfp4_pack_wg<1>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
-    else if (nbw <= 2)
-      hipLaunchKernelGGL(k_nvfp4_pack_wg<2>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
-    else
-      hipLaunchKernelGGL(k_nvfp4_pack_wg<4>, g1, block, 0, s, x, (int)rows, H, packed, row_bytes);
-  } else if (nb <= 1) {
-    hipLaunchKernelGGL(k_nvfp4_pack<1>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
-  } else if (nb <= 2) {
-    hipLaunchKernelGGL(k_nvfp4_pack<2>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
-  } else if (nb <= 4) {
-    hipLaunchKernelGGL(k_nvfp4_pack<4>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
-  } else if (nb <= 8) {
-    hipLaunchKernelGGL(k_nvfp4_pack<8>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+    hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_STREAM_CARRY>, grid, block, 0, s, x, (int)rows, H, o, sr_state);
   } else {
-    hipLaunchKernelGGL(k_nvfp4_pack<16>, grid, block, 0, s, x, (int)rows, H, packed, row_bytes);
+    launch_rne_pack<false>(x, (int)rows, H, o, nullptr, 1, 0, s);
   }
+  return launch_status();
+}
+
+// Padding rows of the grouped rowwise operand (from off_e + count_e to
+// off_{e+1}) are zero bytes, as the direct receive leaves them: one
+// workgroup per expert.
+__global__ __launch_bounds__(256) void k_zero_padding(const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets, int r_cap, int H,
+                                                      uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+                                                      float* __restrict__ row_t) {
+  const int e = blockIdx.x;
+  const int o0 = min(max(offsets[e], 0), r_cap), o1 = min(max(offsets[e + 1], o0), r_cap);
+  const int g0 = min(o0 + max(counts[e], 0), o1);
+  const int cw = H >> 3, sw = H >> 6;  // dwords of codes and of scales per row
+  for (int g = g0; g < o1; ++g) {
+    uint32_t* c = reinterpret_cast<uint32_t*>(row_codes + (size_t)g * (H >> 1));
+    uint32_t* sc = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4));
+    for (int i = threadIdx.x; i < cw; i += 256) c[i] = 0u;
+    for (int i = threadIdx.x; i < sw; i += 256) sc[i] = 0u;
+    if (threadIdx.x == 0) row_t[g] = 0.0f;
+  }
+}
+
+MTB_EXPORT int32_t ep_nvfp4_pack_scatter(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t top_k,
+                                         const int32_t* dst_row, int64_t num_experts, int64_t r_cap,
+                                         const int32_t* counts, const int32_t* offsets, uint8_t* row_codes,
+                                         uint8_t* row_scales, float* row_t, void* stream) {
+  if (tokens < 0 || hidden <= 0 || hidden % 64 != 0 || hidden > 16384 || top_k < 1 || num_experts < 1 ||
+      num_experts > 1024 || r_cap < 0)
+    return EP_ERR_SHAPE;
+  if (top_k > kMaxScatter) return EP_ERR_RANGE;
+  if (tokens > (int64_t)INT32_MAX / 4 || tokens * hidden >= ((int64_t)1 << 40) || r_cap >= INT32_MAX / 4)
+    return EP_ERR_RANGE;
+  if (!counts || !offsets) return EP_ERR_NULL;
+  if (r_cap > 0 && (!row_codes || !row_scales || !row_t)) return EP_ERR_NULL;
+  if (tokens > 0 && (!x || !dst_row)) return EP_ERR_NULL;
+  const int H = (int)hidden;
+  hipStream_t s = (hipStream_t)stream;
+  const RowOut o{row_codes, row_scales, reinterpret_cast<uint8_t*>(row_t), (uint32_t)(H / 2), (uint32_t)(H / 16), 4u};
+  if (tokens > 0 && r_cap > 0) launch_rne_pack<true>(x, (int)tokens, H, o, dst_row, (int)top_k, (int)r_cap, s);
+  if (r_cap > 0)
+    hipLaunchKernelGGL(k_zero_padding, dim3((unsigned)num_experts), dim3(256), 0, s, counts, offsets, (int)r_cap, H,
+                       row_codes, row_scales, row_t);
   return launch_status();
 }
 

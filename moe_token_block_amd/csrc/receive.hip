@@ -63,6 +63,29 @@ __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict
   }
 }
 
+// D_e from the grouped rowwise operand: the expert's rows are contiguous, so
+// this is a max over row_t[off_e .. off_{e+1}) (padding rows hold t = 0).
+__global__ __launch_bounds__(1024) void k_expert_scale_grouped(const float* __restrict__ row_t, int r_cap,
+                                                               const int32_t* __restrict__ offsets,
+                                                               float* __restrict__ col_scale) {
+  __shared__ uint32_t red[16];
+  const int e = blockIdx.x;
+  const int g0 = max(0, offsets[e]), g1 = min(r_cap, offsets[e + 1]);
+  uint32_t m = 0;  // t >= 0: compare bit patterns
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += 1024) {
+    uint32_t tb = __float_as_uint(row_t[g]);
+    m = m > tb ? m : tb;
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < 16; ++i) r = r > red[i] ? r : red[i];
+    col_scale[e] = 4.0f * __uint_as_float(r);
+  }
+}
+
 // Reciprocal split of every E4M3 block-scale code (see quot_split): entry c
 // holds r_hi, r_lo of the significand of s = E4M3(c) and s's exponent; code 0
 // (and the NaN code) hold zeros, which quantize every value to a signed zero.
@@ -212,7 +235,18 @@ __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm,
 // time, and the halves of each 128-byte code line, the scale lines and the
 // token scales they share are fetched into that XCD's L2 once (and partial
 // line writes of the rowwise scales merge there).
-__global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
+// Where the kernel reads a row's codes, scales and t: the packed rows
+// gathered through src_row (the direct receive), or the grouped rowwise
+// operand itself (GROUPED: grouped row g is its own source).
+struct RowSrc {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint8_t* t;
+  uint32_t cstride, sstride, tstride;  // bytes between consecutive rows
+};
+
+template <bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
                                                        const int32_t* __restrict__ offsets, int E,
                                                        const int32_t* __restrict__ src_row, int r_cap, int n_ct,
                                                        uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
@@ -239,13 +273,12 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
   const int g_base = rt * kTileRows;  // first grouped row of the tile
   const int col0 = ct * kTileCols;
   const int ncols = min(kTileCols, H - col0);
-  const int toff = (H >> 1) + (H >> 4);
 
   // phase 1: source rows, expert offsets, the reciprocal table.
   // src_row is -1 for padding and from off_E to r_cap.
   {
     int g = g_base + tid;
-    int src = g < r_cap ? src_row[g] : -1;
+    int src = g < r_cap ? (GROUPED ? g : src_row[g]) : -1;
     s_src[tid] = (src >= 0 && src < T) ? src : -1;
     for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
     for (int i = tid; i < 128; i += kThreads) s_tab[i] = rcp_entry(i);
@@ -285,9 +318,9 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
     float t = 0.0f;
     uint32_t sw0 = 0, sw1 = 0;
     if (src >= 0) {
-      const uint8_t* prow = packed + (size_t)(uint32_t)src * (uint32_t)row_bytes;
-      t = *reinterpret_cast<const float*>(prow + toff);
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
+      t = *reinterpret_cast<const float*>(rs.t + (size_t)(uint32_t)src * rs.tstride);
+      const uint32_t* sp =
+          reinterpret_cast<const uint32_t*>(rs.scales + (size_t)(uint32_t)src * rs.sstride + (col0 >> 4));
       sw0 = sp[0];
       if (ncols > 64) sw1 = sp[1];
     }
@@ -300,10 +333,10 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
       uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);
       if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
     }
-    if (g < off_end) {
-      uint32_t* rs = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
-      rs[0] = sw0;
-      if (ncols > 64) rs[1] = sw1;
+    if (!GROUPED && g < off_end) {
+      uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
+      rsc[0] = sw0;
+      if (ncols > 64) rsc[1] = sw1;
       if (ct == 0) row_t[g] = t;
     }
   }
@@ -321,20 +354,20 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const uint8_t* __res
 #pragma unroll
     for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
     const int* sr = reinterpret_cast<const int*>(sv);
-    const uint8_t* base = packed + (col0 >> 1) + 4 * cg;
+    const uint8_t* base = rs.codes + (col0 >> 1) + 4 * cg;
     if (live && T > 0) {
       // branch-free: padding rows read row 0 and are zeroed
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int src = sr[i];
-        uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes);
+        uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * rs.cstride);
         cw[i] = src >= 0 ? v : 0u;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) cw[i] = 0u;
     }
-    if (live) {
+    if (!GROUPED && live) {
       uint8_t* rc = row_codes + (size_t)gb * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg;
 #pragma unroll
       for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(rc + (size_t)i * (uint32_t)(H >> 1)) = cw[i];
@@ -458,9 +491,11 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   const int H = (int)hidden;
   const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
   if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
-  hipLaunchKernelGGL(k_nvfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, packed,
-                     (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
-                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL(k_nvfp4_receive<false>, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+                     (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
+                     row_t, col_codes, col_scales, col_scale);
   return launch_status();
 }
 
@@ -485,5 +520,27 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens
   hipLaunchKernelGGL(k_nvfp4_gather, dim3((unsigned)((r_cap + 3) / 4)), dim3(256), 0, (hipStream_t)stream, packed,
                      (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, row_codes,
                      row_scales, row_t);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const uint8_t* row_scales, const float* row_t,
+                                               int64_t hidden, int64_t num_experts, int64_t r_cap,
+                                               const int32_t* offsets, uint8_t* col_codes, uint8_t* col_scales,
+                                               float* col_scale, void* stream) {
+  if (r_cap < 0 || num_experts < 1 || num_experts > 1024 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
+  if (r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
+  if (!offsets || !col_scale) return EP_ERR_NULL;
+  if (r_cap > 0 && (!row_codes || !row_scales || !row_t || !col_codes || !col_scales)) return EP_ERR_NULL;
+  const int H = (int)hidden;
+  hipLaunchKernelGGL(k_expert_scale_grouped, dim3((unsigned)num_experts), dim3(1024), 0, (hipStream_t)stream, row_t,
+                     (int)r_cap, offsets, col_scale);
+  if (r_cap == 0) return launch_status();
+  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
+  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const RowSrc src{row_codes, row_scales, reinterpret_cast<const uint8_t*>(row_t), (uint32_t)(H / 2),
+                   (uint32_t)(H / 16), 4u};
+  hipLaunchKernelGGL(k_nvfp4_receive<true>, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+                     (int)r_cap, H, offsets, (int)num_experts, nullptr, (int)r_cap, (int)n_ct, nullptr, nullptr, nullptr,
+                     col_codes, col_scales, col_scale);
   return launch_status();
 }

@@ -72,6 +72,13 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_nvfp4_pack(P, 4, 128, P, 7, N, N) == -5
     assert lib.ep_nvfp4_pack(P, 4, 128, P, 5, N, N) == -5           # past the last SR mode
     assert lib.ep_nvfp4_pack(P, 4, 128, P, 3, N, N) == -1           # carry-form SR without state
+    assert lib.ep_nvfp4_pack_scatter(P, 4, 128, 33, P, 4, 64, P, P, P, P, P, N) == -8   # top_k > 32
+    assert lib.ep_nvfp4_pack_scatter(P, 4, 100, 2, P, 4, 64, P, P, P, P, P, N) == -2    # hidden % 64
+    assert lib.ep_nvfp4_pack_scatter(P, 4, 128, 2, P, 0, 64, P, P, P, P, P, N) == -2    # no experts
+    assert lib.ep_nvfp4_pack_scatter(P, 4, 128, 2, N, 4, 64, P, P, P, P, P, N) == -1    # no dst_row
+    assert lib.ep_nvfp4_columnwise_grouped(P, P, P, 100, 4, 64, P, P, P, P, N) == -2
+    assert lib.ep_nvfp4_columnwise_grouped(P, P, P, 128, 1025, 64, P, P, P, P, N) == -2
+    assert lib.ep_nvfp4_columnwise_grouped(P, P, P, 128, 4, 64, N, P, P, P, N) == -1
     assert lib.ep_nvfp4_pack(P, 0, 128, N, 0, N, N) == 0            # empty: nothing to do
     assert lib.ep_mxfp8_pack(P, 4, 48, P, P, N) == -2
     assert lib.ep_nvfp4_unpack(P, 4, 128, N, 5, P, N) == -2         # rows_out != rows_in without a map

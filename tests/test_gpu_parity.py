@@ -229,6 +229,34 @@ def test_direct_receive_rowwise_only(dev):
     assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "rowwise-only codes")
 
 
+@pytest.mark.parametrize("case", [
+    dict(seed=31, tokens=150, hidden=256, E=5, k=2, A=16, unused=0.05, empty=[3]),
+    dict(seed=32, tokens=600, hidden=4096, E=8, k=2, A=128, unused=0.0, empty=[]),
+    dict(seed=33, tokens=333, hidden=192, E=3, k=1, A=256, unused=0.2, empty=[]),
+    dict(seed=34, tokens=257, hidden=512, E=16, k=8, A=16, unused=0.0, empty=[0, 15]),
+])
+def test_pack_scatter_and_grouped_columnwise(dev, case):
+    """Fused dispatch: the pack writing grouped rows directly, then the columnwise operand
+    from those rows, equal the oracle's direct receive byte for byte (and the unfused GPU path)."""
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
+    h = case["hidden"]
+    print(f"pack-scatter case {case}", flush=True)
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    rows = mtb.ep_nvfp4_pack_scatter(bf16_dev(w.x_bits, dev), plan)
+    got = dict(rows)
+    got.update(mtb.ep_nvfp4_columnwise_grouped(rows, h, plan))
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    _check_receive(dev, w, onv.pack_rows(w.x_bits), got, plan_np, h)
+    # and the unfused GPU receive of the same rows
+    ref = mtb.ep_nvfp4_direct_receive(mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev)), h, plan)
+    off = int(plan_np["offsets"][-1])
+    for key in ("row_codes", "row_scales", "row_t"):
+        assert_bytes_equal(host(got[key])[:off], host(ref[key])[:off], f"fused vs unfused {key}")
+    n = h * off
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], host(ref["col_codes"])[: n // 2], "fused vs unfused col codes")
+
+
 def test_mxfp8_receive_bit_exact(dev):
     w = workloads.small_dispatch(11, 300, 256, 6, 2, alignment=128, unused_frac=0.1)
     data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
