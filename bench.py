@@ -48,6 +48,7 @@ CALL_SOURCES = {
     "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
     "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
+    "nvfp4_direct_receive_kblock": ("receive.hip",),
 }
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
@@ -60,6 +61,7 @@ CALL_KERNELS = {
     "dswiglu_nvfp4_quant": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"],
     "nvfp4_pack_scatter": ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"],
     "nvfp4_columnwise_grouped": ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"],
+    "nvfp4_direct_receive_kblock": ["k_nvfp4_receive (K-blocked columnwise layout)"],
 }
 # the combine-backward SR pack: one Philox4x32-10 word per element at counter
 # row*hidden + col (element mode), carry-form decision (the hardware converter)
@@ -81,7 +83,7 @@ def parse():
                    help="profiling aid: run only this call of the path (or 'copy': a 1 GiB device copy, the "
                         "reference for memory counters) --steps times, eagerly, and print what ran")
     p.add_argument("--workload", default="dispatch",
-                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f"],
+                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k"],
                    help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
                         "configuration's own path, for per-kernel figures")
     return p.parse_args()
@@ -263,8 +265,8 @@ class ConfigStep:
         import moe_token_block_amd as m
         import workloads
         self.m = m
-        fused = which.endswith("f")
-        n = int(which[3:-1] if fused else which[3:])
+        fused, kblock = which.endswith("f"), which.endswith("k")
+        n = int(which[3:-1] if fused or kblock else which[3:])
         w = workloads.CONFIGS[n]()
         self.w, self.n = w, n
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -326,8 +328,14 @@ class ConfigStep:
         self._add("nvfp4_expert_scale", lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan,
                                                                         col_scale=self.recv["col_scale"]),
                   b["nvfp4_expert_scale"])
-        self._add("nvfp4_direct_receive", lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
-                  b["nvfp4_direct_receive"])
+        if kblock:
+            self._add("nvfp4_direct_receive_kblock",
+                      lambda: m.ep_nvfp4_direct_receive_kblock(self.packed, H, self.plan, self.recv),
+                      b["nvfp4_direct_receive"])
+        else:
+            self._add("nvfp4_direct_receive",
+                      lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
+                      b["nvfp4_direct_receive"])
         if n == 2:
             self.mx = torch.empty(T * H + T * H // 32, **u8)
             self.mx_out = (torch.empty((r_cap, H), **u8), torch.empty((r_cap, H // 32), **u8))

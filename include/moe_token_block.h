@@ -217,6 +217,23 @@ int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t tokens, in
                                        uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
                                        void* stream);
 
+/* The direct receive with the columnwise operand in K-blocks, a layout a
+ * grouped GEMM can stream (P1, PR description: the receiver builds the expert
+ * GEMM's grouped operand): per expert, the grouped rows are cut into blocks
+ * of 256 (the last one shorter, a multiple of 16); block kb of expert e
+ * holds an [H, len/2] code matrix at byte H*off_e/2 + 128*H*kb of col_codes
+ * and an [H, len/16] scale matrix at byte H*off_e/16 + 16*H*kb of
+ * col_scales.  Same values as ep_nvfp4_direct_receive_scaled's compact
+ * layout (the same bytes, re-placed); the rowwise operand is identical.
+ * col_scale holds D_e (from ep_nvfp4_expert_scale).  Each 256 x 128 tile's
+ * columnwise output is one contiguous 16 KB region. */
+int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                       int64_t num_experts, int64_t r_cap,
+                                       const int32_t* offsets, const int32_t* src_row,
+                                       uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                       uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
+                                       void* stream);
+
 /* MXFP8 receive (P2, description and review comments: received data and block
  * scales are returned per expert, grouped, with 128-aligned slots there --
  * here any multiple of 16): grouped row g copies token src_row[g]'s data row

@@ -45,6 +45,7 @@ _SIGS = {
     "ep_nvfp4_expert_scale": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_scaled": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "ep_nvfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -245,6 +246,20 @@ def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
             _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _ptr(out.get("col_scale")),
             _stream(dev)), "ep_nvfp4_direct_receive")
+    return out
+
+
+def ep_nvfp4_direct_receive_kblock(packed, hidden, plan, out):
+    """The one-pass receive with the columnwise operand in 256-row K-blocks
+    (out["col_scale"] already holding D_e, as for ep_nvfp4_direct_receive_scaled)."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_direct_receive_kblock(
+            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _stream(dev)),
+            "ep_nvfp4_direct_receive_kblock")
     return out
 
 

@@ -228,13 +228,6 @@ __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm,
   stage_sc[stage_at(c1, m)] = q1.sc;
 }
 
-// One workgroup per 256 grouped rows x 128 columns; 1-D grid of
-// row_tiles * col_tiles workgroups.  Workgroup i runs on XCD i % 8, so the
-// logical tile is taken from a contiguous range per XCD, column tile
-// fastest: all column tiles of a row tile run on one XCD at about the same
-// time, and the halves of each 128-byte code line, the scale lines and the
-// token scales they share are fetched into that XCD's L2 once (and partial
-// line writes of the rowwise scales merge there).
 // Where the kernel reads a row's codes, scales and t: the packed rows
 // gathered through src_row (the direct receive), or the grouped rowwise
 // operand itself (GROUPED: grouped row g is its own source).
@@ -245,7 +238,19 @@ struct RowSrc {
   uint32_t cstride, sstride, tstride;  // bytes between consecutive rows
 };
 
-template <bool GROUPED>
+// One workgroup per 256 grouped rows x 128 columns; 1-D grid of
+// row_tiles * col_tiles workgroups.  Workgroup i runs on XCD i % 8, so the
+// logical tile is taken from a contiguous range per XCD, column tile
+// fastest: all column tiles of a row tile run on one XCD at about the same
+// time, and the halves of each 128-byte code line, the scale lines and the
+// token scales they share are fetched into that XCD's L2 once (and partial
+// line writes of the rowwise scales merge there).
+// KBLOCK: the columnwise operand in K-blocks -- each expert's grouped rows in
+// blocks of 256 (the last one shorter, a multiple of 16), block kb of expert e
+// an [H, len/2] code matrix at byte H*off_e/2 + 128*H*kb (scales [H, len/16]
+// at H*off_e/16 + 16*H*kb).  Tiles then follow the K-blocks (never straddling
+// experts), so a tile's columnwise output is one contiguous region.
+template <bool GROUPED, bool KBLOCK>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
                                                        const int32_t* __restrict__ offsets, int E,
                                                        const int32_t* __restrict__ src_row, int r_cap, int n_ct,
@@ -270,9 +275,53 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
   const unsigned xq = nb / kXcds, xr = nb % kXcds, x = bx % kXcds;
   const unsigned lt = x * xq + min(x, xr) + bx / kXcds;
   const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
-  const int g_base = rt * kTileRows;  // first grouped row of the tile
   const int col0 = ct * kTileCols;
   const int ncols = min(kTileCols, H - col0);
+  int g_base = rt * kTileRows;  // first grouped row of the tile
+  int kb = 0, tile_rows = kTileRows;
+  if (KBLOCK) {
+    // the tile is K-block rt of the concatenated per-expert K-block lists
+    __shared__ int s_kbstart[1025];
+    __shared__ int s_wsum[kThreads / 64];
+    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+    __syncthreads();
+    int loc[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      loc[i] = sum;
+      sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kTileRows - 1) / kTileRows : 0;
+    }
+    int incl = sum;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_wsum[tid >> 6] = incl;
+    __syncthreads();
+    int wofs = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      wofs += w < (tid >> 6) ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * tid + i < E) s_kbstart[4 * tid + i] = wofs + incl - sum + loc[i];
+    if (tid == 0) s_kbstart[E] = total;
+    __syncthreads();
+    if (rt >= total) return;  // beyond the last K-block (uniform)
+    int lo = 0, hi = E - 1;   // last expert whose first K-block is <= rt (empty experts share starts)
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_kbstart[mid] <= rt) lo = mid; else hi = mid - 1;
+    }
+    kb = rt - s_kbstart[lo];
+    g_base = s_offs[lo] + kb * kTileRows;
+    tile_rows = min(kTileRows, s_offs[lo + 1] - g_base);
+  }
 
   // phase 1: source rows, expert offsets, the reciprocal table.
   // src_row is -1 for padding and from off_E to r_cap.
@@ -285,11 +334,12 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
   }
   __syncthreads();
   const int off_end = min(s_offs[E], r_cap & ~15);  // whole 16-row blocks inside the outputs
+  const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
 
   // phase 2a: each 16-row block's expert -> its decode exponent and output bases.
   if (tid < kBlocks) {
     const int gb = g_base + 16 * tid;
-    int live = gb < off_end;
+    int live = gb < tile_end;
     int e = 0;
     if (live) {
       int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
@@ -303,10 +353,17 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     if (live) {
       const int off = s_offs[e], len = s_offs[e + 1] - off;
       s_dexp[tid] = pow2_exponent(col_scale[e]);
-      s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
-      s_cstr[tid] = (uint32_t)(len >> 1);
-      s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint32_t)((gb - off) >> 4);
-      s_sstr[tid] = (uint32_t)(len >> 4);
+      if (KBLOCK) {
+        s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * tid;
+        s_cstr[tid] = (uint32_t)(tile_rows >> 1);
+        s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint64_t)H * 16u * (uint32_t)kb + (uint32_t)tid;
+        s_sstr[tid] = (uint32_t)(tile_rows >> 4);
+      } else {
+        s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+        s_cstr[tid] = (uint32_t)(len >> 1);
+        s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint32_t)((gb - off) >> 4);
+        s_sstr[tid] = (uint32_t)(len >> 4);
+      }
     }
   }
 
@@ -333,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
       uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);
       if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
     }
-    if (!GROUPED && g < off_end) {
+    if (!GROUPED && g < tile_end) {
       uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
       rsc[0] = sw0;
       if (ncols > 64) rsc[1] = sw1;
@@ -347,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
   const int cg = tid & 15, m = tid >> 4;
   const int r0 = 16 * m;
   const int gb = g_base + r0;
-  const bool live = gb < off_end && cg * 8 < ncols;
+  const bool live = gb < tile_end && cg * 8 < ncols;
   uint32_t cw[16];
   {
     int4 sv[4];
@@ -493,7 +550,7 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL(k_nvfp4_receive<false>, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
                      (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
                      row_t, col_codes, col_scales, col_scale);
   return launch_status();
@@ -539,8 +596,29 @@ MTB_EXPORT int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const u
   if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const RowSrc src{row_codes, row_scales, reinterpret_cast<const uint8_t*>(row_t), (uint32_t)(H / 2),
                    (uint32_t)(H / 16), 4u};
-  hipLaunchKernelGGL(k_nvfp4_receive<true>, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+  hipLaunchKernelGGL((k_nvfp4_receive<true, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
                      (int)r_cap, H, offsets, (int)num_experts, nullptr, (int)r_cap, (int)n_ct, nullptr, nullptr, nullptr,
                      col_codes, col_scales, col_scale);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                                  int64_t num_experts, int64_t r_cap, const int32_t* offsets,
+                                                  const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                                  float* row_t, uint8_t* col_codes, uint8_t* col_scales,
+                                                  const float* col_scale, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale) return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  // K-blocks over all experts: at most r_cap/256 + E of them
+  const int64_t n_kb = (r_cap + kTileRows - 1) / kTileRows + num_experts, n_ct = (H + kTileCols - 1) / kTileCols;
+  if (n_kb * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL((k_nvfp4_receive<false, true>), dim3((unsigned)(n_kb * n_ct)), dim3(kThreads), 0,
+                     (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
+                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
   return launch_status();
 }

@@ -137,6 +137,38 @@ def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None,
     return out
 
 
+def kblock_layout(col_codes, col_scales, offsets, hidden, block_rows=256):
+    """The columnwise operand re-laid in K-blocks (a GEMM-ready variant of R16).
+
+    Per expert e (P_e = offsets[e+1] - offsets[e] grouped rows), the grouped
+    rows are cut into K-blocks of ``block_rows`` (the last one shorter); block
+    kb holds rows [kb*block_rows, kb*block_rows + len) as an [H, len/2] code
+    matrix (row h = column h, grouped-row order, low nibble first) at byte
+    H*off_e/2 + H*kb*block_rows/2, and an [H, len/16] scale matrix at byte
+    H*off_e/16 + H*kb*block_rows/16.  The values are those of the compact
+    layout; only their places change.
+    """
+    col_codes = np.asarray(col_codes, dtype=np.uint8)
+    col_scales = np.asarray(col_scales, dtype=np.uint8)
+    off = np.asarray(offsets, dtype=np.int64)
+    h = hidden
+    out_c = np.zeros_like(col_codes)
+    out_s = np.zeros_like(col_scales)
+    for e in range(off.shape[0] - 1):
+        o, p = int(off[e]), int(off[e + 1] - off[e])
+        if p == 0:
+            continue
+        cm = col_codes[h * o // 2 : h * (o + p) // 2].reshape(h, p // 2)
+        sm = col_scales[h * o // 16 : h * (o + p) // 16].reshape(h, p // 16)
+        for r0 in range(0, p, block_rows):
+            ln = min(block_rows, p - r0)
+            c0 = h * (o + r0) // 2
+            s0 = h * (o + r0) // 16
+            out_c[c0 : c0 + h * ln // 2] = cm[:, r0 // 2 : (r0 + ln) // 2].reshape(-1)
+            out_s[s0 : s0 + h * ln // 16] = sm[:, r0 // 16 : (r0 + ln) // 16].reshape(-1)
+    return out_c, out_s
+
+
 def columnwise_sample(packed, hidden, plan, expert, col_lo, col_hi, blk_lo, blk_hi, D):
     """Columnwise codes/scales of one expert restricted to columns [col_lo, col_hi)
     and 16-row blocks [blk_lo, blk_hi) -- for sampled checks at full size.

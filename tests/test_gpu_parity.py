@@ -257,6 +257,34 @@ def test_pack_scatter_and_grouped_columnwise(dev, case):
     assert_bytes_equal(host(got["col_codes"])[: n // 2], host(ref["col_codes"])[: n // 2], "fused vs unfused col codes")
 
 
+@pytest.mark.parametrize("case", [
+    dict(seed=41, tokens=300, hidden=256, E=5, k=2, A=16, unused=0.05, empty=[3]),
+    dict(seed=42, tokens=700, hidden=4096, E=3, k=1, A=16, unused=0.0, empty=[]),    # experts of > 256 rows
+    dict(seed=43, tokens=257, hidden=512, E=16, k=8, A=128, unused=0.0, empty=[0, 15]),
+])
+def test_direct_receive_kblock_layout(dev, case):
+    """The K-blocked columnwise layout: the oracle's operand re-laid by oracle.kblock_layout,
+    byte for byte; the rowwise operand and D_e as in the compact receive."""
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
+    h = case["hidden"]
+    print(f"kblock receive case {case}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    got = mtb.ep_nvfp4_direct_receive(packed, h, plan)           # compact, with D_e
+    kb = {k: torch.empty_like(v) for k, v in got.items()}
+    kb["col_scale"] = got["col_scale"].clone()
+    mtb.ep_nvfp4_direct_receive_kblock(packed, h, plan, kb)
+    want = orecv.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment)
+    off = host(plan["offsets"]).astype(np.int64)
+    n = h * int(off[-1])
+    wc, ws = orecv.kblock_layout(want["col_codes"][: n // 2], want["col_scales"][: n // 16], off, h)
+    assert_bytes_equal(host(kb["col_codes"])[: n // 2], wc, "K-block columnwise codes")
+    assert_bytes_equal(host(kb["col_scales"])[: n // 16], ws, "K-block columnwise scales")
+    for key in ("row_codes", "row_scales", "row_t"):
+        assert_bytes_equal(host(kb[key])[: off[-1]], host(got[key])[: off[-1]], f"K-block receive {key}")
+
+
 def test_mxfp8_receive_bit_exact(dev):
     w = workloads.small_dispatch(11, 300, 256, 6, 2, alignment=128, unused_frac=0.1)
     data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))

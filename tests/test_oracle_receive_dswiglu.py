@@ -215,3 +215,36 @@ def test_fc1_wgrad_error_within_5_percent_of_default():
             errs[name] += ((wg @ wx.T - ref) ** 2).sum()
     assert np.sqrt(errs["fused"]) <= 1.05 * np.sqrt(errs["default"]), errs
     assert np.sqrt(errs["default"]) / np.sqrt(ref_norm) < 0.2
+
+
+def test_kblock_layout_is_a_permutation_read_back_by_a_blocked_consumer():
+    """The K-blocked columnwise layout holds the compact operand's bytes: a consumer that
+    walks experts, then K-blocks, then columns recovers every (column, grouped row) code
+    and scale of the compact layout -- including experts of 272 rows (blocks 256 + 16),
+    exactly 256, 16 and empty."""
+    from oracle.receive import kblock_layout
+    rng = np.random.default_rng(41)
+    h = 64
+    sizes = [272, 0, 256, 16, 528, 32]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    comp_c = rng.integers(0, 256, h * n // 2, dtype=np.uint8)
+    comp_s = rng.integers(0, 127, h * n // 16, dtype=np.uint8)
+    kc, ks = kblock_layout(comp_c, comp_s, off, h)
+    assert sorted(kc.tolist()) == sorted(comp_c.tolist())          # a permutation of the bytes
+    for e, p in enumerate(sizes):
+        o = int(off[e])
+        cpos = h * o // 2
+        spos = h * o // 16
+        for r0 in range(0, p, 256):
+            ln = min(256, p - r0)
+            for col in range(h):
+                for j in range(0, ln, 2):              # grouped rows r0 + j, r0 + j + 1 share a byte
+                    want = comp_c[h * o // 2 + col * (p // 2) + (r0 + j) // 2]
+                    assert kc[cpos] == want, (e, r0, col, j)
+                    cpos += 1
+            for col in range(h):
+                for b in range(ln // 16):
+                    assert ks[spos] == comp_s[h * o // 16 + col * (p // 16) + r0 // 16 + b]
+                    spos += 1
+        assert cpos == h * (o + p) // 2 and spos == h * (o + p) // 16
