@@ -48,7 +48,7 @@ CALL_SOURCES = {
     "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
     "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
-    "nvfp4_direct_receive_kblock": ("receive.hip",),
+    "nvfp4_direct_receive_kblock": ("receive.hip",), "dswiglu_nvfp4_quant_nodx": ("dswiglu.hip",),
 }
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
@@ -62,6 +62,7 @@ CALL_KERNELS = {
     "nvfp4_pack_scatter": ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"],
     "nvfp4_columnwise_grouped": ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"],
     "nvfp4_direct_receive_kblock": ["k_nvfp4_receive (K-blocked columnwise layout)"],
+    "dswiglu_nvfp4_quant_nodx": ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce", "k_fc1_quant (recompute)"],
 }
 # the combine-backward SR pack: one Philox4x32-10 word per element at counter
 # row*hidden + col (element mode), carry-form decision (the hardware converter)
@@ -83,7 +84,8 @@ def parse():
                    help="profiling aid: run only this call of the path (or 'copy': a 1 GiB device copy, the "
                         "reference for memory counters) --steps times, eagerly, and print what ran")
     p.add_argument("--workload", default="dispatch",
-                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k"],
+                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k",
+                            "cfg5r"],
                    help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
                         "configuration's own path, for per-kernel figures")
     return p.parse_args()
@@ -265,8 +267,8 @@ class ConfigStep:
         import moe_token_block_amd as m
         import workloads
         self.m = m
-        fused, kblock = which.endswith("f"), which.endswith("k")
-        n = int(which[3:-1] if fused or kblock else which[3:])
+        fused, kblock, recompute = which.endswith("f"), which.endswith("k"), which.endswith("r")
+        n = int(which[3:-1] if fused or kblock or recompute else which[3:])
         w = workloads.CONFIGS[n]()
         self.w, self.n = w, n
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -280,15 +282,24 @@ class ConfigStep:
             self.counts = torch.from_numpy(w.counts).to(dev)
             cap = T + 15 * E
             f32 = dict(dtype=torch.float32, device=dev)
-            self.out = dict(dx=torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev), amax=torch.empty(E, **f32),
+            self.out = dict(dx=None if recompute else torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev),
+                            amax=torch.empty(E, **f32),
                             row_codes=torch.empty((T, F), **u8), row_scales=torch.empty((T, 2 * F // 16), **u8),
                             row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
                             col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
             self.ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
-            self._add("dswiglu_nvfp4_quant", lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out,
-                                                                           workspace=self.ws),
-                      T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16) + 2 * E * 4)
-            self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)
+            if recompute:
+                # no dX written: inputs read once + the quantized operands and the maxima
+                self._add("dswiglu_nvfp4_quant_nodx",
+                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws),
+                          T * 2 * F * 2 + T * F * 2 + E * 4 + 2 * T * (F + 2 * F // 16) + 2 * E * 4)
+            else:
+                self._add("dswiglu_nvfp4_quant",
+                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws),
+                          T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16)
+                          + 2 * E * 4)
+            self.desc = dict(workload=w.name + (" (dX not materialized)" if recompute else ""), tokens=T, ffn=F,
+                             experts=E)
             return
         T, H = w.x_bits.shape
         k, E, A = w.topk_idx.shape[1], w.num_experts, w.alignment

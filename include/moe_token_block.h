@@ -295,7 +295,11 @@ int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const uint8_t* row
  *   byte 2*ffn*poff_e/16; col_codes and col_scales need
  *   2*ffn*(tokens + 15*E)/2 and 2*ffn*(tokens + 15*E)/16 bytes.
  *   workspace: device memory of dswiglu_workspace_bytes(tokens, E) bytes.
- *   Requires ffn a positive multiple of 64. */
+ *   Requires ffn a positive multiple of 64.
+ *   dx may be NULL: then no BF16 dX is written; the epilogue keeps only each
+ *   row's max |dX| and the quantizer recomputes dX from preact and dy with
+ *   the same arithmetic (so every output equals the dx != NULL call's).
+ */
 int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
                             const int32_t* counts, int64_t num_experts,
                             uint16_t* dx, float* amax,

@@ -343,9 +343,11 @@ def ep_mxfp8_direct_receive(data, scales, plan, out=None):
 
 
 # ------------------------------------------------------------------ dSwiGLU
-def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None):
+def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True):
     """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
-    ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors."""
+    ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors.
+    ``materialize_dx=False``: no BF16 dX is written (out["dx"] is None); the
+    quantizer recomputes dX from preact and dy."""
     dev = _dev(preact)
     _need(preact, torch.bfloat16, "preact", dev)
     _need(dy, torch.bfloat16, "dy", dev)
@@ -356,7 +358,8 @@ def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None):
     if out is None:
         u8 = dict(dtype=torch.uint8, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
-        out = dict(dx=torch.empty((t, 2 * f), dtype=torch.bfloat16, device=dev), amax=torch.empty(e, **f32),
+        out = dict(dx=torch.empty((t, 2 * f), dtype=torch.bfloat16, device=dev) if materialize_dx else None,
+                   amax=torch.empty(e, **f32),
                    row_codes=torch.empty((t, f), **u8), row_scales=torch.empty((t, 2 * f // 16), **u8),
                    row_scale=torch.empty(e, **f32), col_codes=torch.empty(2 * f * cap // 2, **u8),
                    col_scales=torch.empty(2 * f * cap // 16, **u8), col_scale=torch.empty(e, **f32))

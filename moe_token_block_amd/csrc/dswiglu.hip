@@ -113,6 +113,7 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+template <bool STORE>
 __global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __restrict__ preact,
                                                           const uint16_t* __restrict__ dy, int T, int F,
                                                           uint16_t* __restrict__ dx, uint32_t* __restrict__ rowmax) {
@@ -138,8 +139,10 @@ __global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __rest
       rb[i] = bf16pair(db0, db1);
     }
     uint4 oA = make_uint4(ra[0], ra[1], ra[2], ra[3]), oB = make_uint4(rb[0], rb[1], rb[2], rb[3]);
-    oa[j] = oA;
-    ob[j] = oB;
+    if (STORE) {
+      oa[j] = oA;
+      ob[j] = oB;
+    }
     uint32_t x = absmax_bf16x8(oA), y = absmax_bf16x8(oB);
     x = x > y ? x : y;
     m = m > x ? m : x;
@@ -276,6 +279,15 @@ __device__ __forceinline__ uint32_t gen_scale_code_x(float a, const DScale& d, i
   return e4m3_encode(fminf(y, 448.0f));
 }
 
+// dX column of the tile's column c (0..127): the tile's 128 contiguous
+// columns, or with RECOMPUTE 64 da columns then the matching 64 db columns.
+template <bool RECOMPUTE>
+__device__ __forceinline__ int qtile_col(int col0, int c, int W) {
+  if (!RECOMPUTE) return col0 + c;
+  const int j0 = col0 >> 1;
+  return c < 64 ? j0 + c : (W >> 1) + j0 + (c - 64);
+}
+
 // LDS staging of the transposed tile, as in the direct receive: entry
 // (column c, block b) at c*16 + (b ^ ((c >> 3) & 15)).
 __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (b ^ ((c >> 3) & 15)); }
@@ -288,7 +300,14 @@ __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (
 // butterfly runs on the unscaled values with the signs d_i folded into its
 // adds: the result is 4x the RHT exactly, and the 4 goes into the powers of
 // two of the quantizer.
-__global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, int T, int W /* 2F */, int E,
+// RECOMPUTE: dX is not materialized; tile ct covers the da columns
+// [64ct, 64ct + 64) and the db columns F + [64ct, 64ct + 64), and each thread
+// recomputes its 8 columns of dX from preact and dy with the epilogue's own
+// arithmetic (so the values, and the amax already taken from them, agree bit
+// for bit).
+template <bool RECOMPUTE>
+__global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
+                                                   const uint16_t* __restrict__ dy, int T, int W /* 2F */, int E,
                                                    int n_ct, const int32_t* __restrict__ offs,
                                                    const int32_t* __restrict__ poffs,
                                                    const float* __restrict__ row_scale,
@@ -364,11 +383,32 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
     const int row0 = s_row0[m], nreal = s_nreal[m];
     if (nreal > 0) {
       // branch-free: rows past the expert's end re-read its last row and are zeroed
-      const uint16_t* base = dx + col0 + 8 * cg;
+      if (!RECOMPUTE) {
+        const uint16_t* base = dx + col0 + 8 * cg;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint4 t = ld_stream16(base + (size_t)(uint32_t)(row0 + min(i, nreal - 1)) * (uint32_t)W);
-        v[i] = i < nreal ? t : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+          uint4 t = ld_stream16(base + (size_t)(uint32_t)(row0 + min(i, nreal - 1)) * (uint32_t)W);
+          v[i] = i < nreal ? t : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        const int F = W >> 1, j = (col0 >> 1) + 8 * (cg & 7);  // col0 = 128 ct: j0 = 64 ct
+        const bool want_b = cg >= 8;                             // this thread keeps db (else da)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const size_t r = (size_t)(uint32_t)(row0 + min(i, nreal - 1));
+          uint4 va = ld_stream16(preact + r * (uint32_t)W + j), vb = ld_stream16(preact + r * (uint32_t)W + F + j);
+          uint4 vd = ld_stream16(dy + r * (uint32_t)F + j);
+          uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w}, wd[4] = {vd.x, vd.y, vd.z, vd.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float da0, db0, da1, db1;
+            dswiglu_pair(bf16lo(wa[q]), bf16lo(wb[q]), bf16lo(wd[q]), da0, db0);
+            dswiglu_pair(bf16hi(wa[q]), bf16hi(wb[q]), bf16hi(wd[q]), da1, db1);
+            o[q] = want_b ? bf16pair(db0, db1) : bf16pair(da0, da1);
+          }
+          v[i] = i < nreal ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -382,8 +422,9 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
     const float Drow = s_drow[m], Dcol = s_dcol[m];
     const DScale dsr = dscale(Drow), dsc = dscale(Dcol);
     // ---- rowwise: the 16-column block is split over lanes cg, cg^1
-    uint8_t* rcp = row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + ((col0 + 8 * cg) >> 1);
-    uint8_t* rsp = row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + ((col0 + 8 * cg) >> 4);
+    const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
+    uint8_t* rcp = row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + (xcol >> 1);
+    uint8_t* rsp = row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + (xcol >> 4);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       uint32_t am = absmax_bf16x8(v[i]);
@@ -460,7 +501,7 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
   for (int r = 0; r < (kQTileCols * kQBlocks) / 256; ++r) {
     const int c = r * 16 + (tid >> 4);
     if (c >= ncols) break;
-    const uint32_t h = (uint32_t)(col0 + c);
+    const uint32_t h = (uint32_t)qtile_col<RECOMPUTE>(col0, c, W);
     *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[qstage_at(c, b)];
     col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[qstage_at(c, b)];
   }
@@ -483,22 +524,30 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
   if (tokens < 0 || ffn <= 0 || ffn % 64 != 0 || num_experts < 1 || num_experts > 1024) return EP_ERR_SHAPE;
   if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
-  if (tokens > 0 && (!preact || !dy || !dx || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
+  if (tokens > 0 && (!preact || !dy || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
   if (!workspace || workspace_bytes < dswiglu_workspace_bytes(tokens, num_experts)) return EP_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int T = (int)tokens, F = (int)ffn, E = (int)num_experts;
   int32_t* offs = (int32_t*)workspace;
   int32_t* poffs = offs + (E + 1);
   uint32_t* rowmax = (uint32_t*)(poffs + (E + 1));
-  if (T > 0)
-    hipLaunchKernelGGL(k_dswiglu_epilogue, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, dx, rowmax);
+  if (T > 0 && dx)
+    hipLaunchKernelGGL(k_dswiglu_epilogue<true>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, dx,
+                       rowmax);
+  else if (T > 0)  // dX not wanted: the epilogue keeps only each row's max |dX|
+    hipLaunchKernelGGL(k_dswiglu_epilogue<false>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F,
+                       dx, rowmax);
   hipLaunchKernelGGL(k_dswiglu_reduce, dim3((unsigned)E), dim3(1024), 0, s, counts, E, T, rowmax, offs, poffs, amax,
                      row_scale, col_scale);
   // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
   const int64_t prow_bound = tokens + 15 * num_experts;
   const int64_t n_rt = (prow_bound + kQTileRows - 1) / kQTileRows, n_ct = (2 * F + kQTileCols - 1) / kQTileCols;
   if (n_rt * n_ct * 256 >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
-  hipLaunchKernelGGL(k_fc1_quant, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, T, 2 * F, E, (int)n_ct, offs,
-                     poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
+  if (dx)
+    hipLaunchKernelGGL(k_fc1_quant<false>, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, preact, dy, T, 2 * F, E,
+                       (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
+  else
+    hipLaunchKernelGGL(k_fc1_quant<true>, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, preact, dy, T, 2 * F, E,
+                       (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
   return launch_status();
 }

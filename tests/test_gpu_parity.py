@@ -326,6 +326,29 @@ def test_dswiglu_two_stage(dev, counts, ffn, dy_scales):
                    host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "fc1 columnwise")
 
 
+@pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([300, 0, 129], 256), ([40, 24, 19, 8], 128)])
+def test_dswiglu_without_dx(dev, counts, ffn):
+    """dX not materialized: the quantizer recomputes it; every output equals the
+    materializing call's byte for byte (and that call is checked against the oracle above)."""
+    w = workloads.small_dswiglu(sum(counts) + 7 * ffn, counts, ffn)
+    print(f"dswiglu recompute counts={counts} ffn={ffn}", flush=True)
+    args = (bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    ref = mtb.dswiglu_nvfp4_quant(*args)
+    got = mtb.dswiglu_nvfp4_quant(*args, materialize_dx=False)
+    assert got["dx"] is None
+    t = sum(counts)
+    for key in ("amax", "row_scale", "col_scale", "row_codes", "row_scales", "col_codes", "col_scales"):
+        g, r = host(got[key]), host(ref[key])
+        if key in ("col_codes", "col_scales"):
+            n = 2 * ffn * sum((c + 15) // 16 * 16 for c in counts) // (2 if key == "col_codes" else 16)
+            g, r = g[:n], r[:n]
+        assert_bytes_equal(g, r, f"recompute {key}")
+    # and against the oracle quantizer on the materialized dX
+    q = odsw.fc1_grad_quant(host(ref["dx"]), w.counts, host(ref["amax"]))
+    tolerant_codes(F.unpack_nibbles(host(got["row_codes"])), F.unpack_nibbles(q["row_codes"]),
+                   host(got["row_scales"]), q["row_scales"], "recompute rowwise")
+
+
 # ------------------------------------------------------------------ determinism and graph capture
 def test_deterministic_and_graph_capturable(dev):
     w = workloads.small_dispatch(21, 700, 512, 8, 2, unused_frac=0.02)
