@@ -294,7 +294,8 @@ int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const uint8_t* row
  *   2*ffn*poff_e/2 (poff = padded offsets) and its scales [2*ffn, P_e/16] at
  *   byte 2*ffn*poff_e/16; col_codes and col_scales need
  *   2*ffn*(tokens + 15*E)/2 and 2*ffn*(tokens + 15*E)/16 bytes.
- *   workspace: device memory of dswiglu_workspace_bytes(tokens, E) bytes.
+ *   workspace: device memory of dswiglu_workspace_bytes(tokens, E) bytes,
+ *   16-byte aligned (EP_ERR_WORKSPACE otherwise).
  *   Requires ffn a positive multiple of 64.
  *   dx may be NULL: then no BF16 dX is written; the epilogue keeps only each
  *   row's max |dX| and the quantizer recomputes dX from preact and dy with

@@ -25,57 +25,76 @@ constexpr int kQTileCols = 128;
 constexpr int kQBlocks = kQTileRows / 16;
 constexpr unsigned kXcdsQ = 8;  // CDNA4: 8 XCDs, workgroups dealt round-robin
 
-// Inclusive prefix sums of the (clamped) counts and of their 16-padded sizes
-// into a[] and b[] (1024 entries, LDS); E <= 1024.  Counts are device data:
-// a running total above T is cut at T, so the experts never cover more rows
-// than exist.
-__device__ __forceinline__ void expert_prefix(const int32_t* counts, int E, int T, int32_t* a, int32_t* b) {
-  const int tid = threadIdx.x;
-  int c = tid < E ? max(counts[tid], 0) : 0;
-  a[tid] = c;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int va = tid >= o ? a[tid - o] : 0;
-    __syncthreads();
-    a[tid] += va;
-    __syncthreads();
+// Inclusive scan of one int per lane with the running total cut at cap
+// (a saturating add of non-negative values is associative).
+__device__ __forceinline__ int wave_scan_sat(int x, int cap) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x = min(x + y, cap);
   }
-  const int incl = min(a[tid], T), excl = min(a[tid] - c, T);
-  __syncthreads();
-  a[tid] = incl;
-  b[tid] = (incl - excl + 15) / 16 * 16;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int vb = tid >= o ? b[tid - o] : 0;
-    __syncthreads();
-    b[tid] += vb;
-    __syncthreads();
-  }
+  return x;
 }
 
-// One workgroup per expert.  Workgroup 0 also publishes the offsets.
+// Block scan (1024 threads, one value each, non-negative): inclusive, cut at cap.
+__device__ __forceinline__ int block_scan_sat(int x, int cap, int32_t* wsum /* 32 */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  x = wave_scan_sat(x, cap);
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int t = wave_scan_sat(lane < 16 ? wsum[lane] : 0, cap);
+    if (lane < 16) wsum[16 + lane] = t;
+  }
+  __syncthreads();
+  return w ? min(wsum[16 + w - 1] + x, cap) : x;
+}
+
+// Expert row offsets from the device counts: a[e] = first row of expert e,
+// b[e] = its first 16-padded row, a[E], b[E] the totals (E <= 1024 entries,
+// 1024 threads).  Counts are device data: negative counts count as 0 and the
+// running total is cut at T, so the experts never cover more rows than exist.
+__device__ __forceinline__ void expert_prefix(const int32_t* counts, int E, int T, int32_t* a, int32_t* b,
+                                              int32_t* wsum) {
+  const int tid = threadIdx.x;
+  const int c = tid < E ? min(max(counts[tid], 0), T) : 0;
+  const int incl = block_scan_sat(c, T, wsum);
+  a[tid + 1] = incl;
+  if (tid == 0) a[0] = b[0] = 0;
+  __syncthreads();
+  const int pc = (incl - a[tid] + 15) & ~15;  // padded size (0 past E); totals stay below 2^31
+  b[tid + 1] = block_scan_sat(pc, INT32_MAX, wsum);
+  __syncthreads();
+}
+
+// One workgroup per expert.  Workgroup 0 also publishes the offsets.  The
+// row maxima are read 4 rows per load (the workspace pads them to a multiple
+// of 4 rows; rows outside the expert are masked).
 __global__ __launch_bounds__(1024) void k_dswiglu_reduce(const int32_t* __restrict__ counts, int E, int T,
                                                          const uint32_t* __restrict__ rowmax,
                                                          int32_t* __restrict__ offs, int32_t* __restrict__ poffs,
                                                          float* __restrict__ amax, float* __restrict__ row_scale,
                                                          float* __restrict__ col_scale) {
-  __shared__ int32_t a[1024], b[1024];
+  __shared__ int32_t a[1025], b[1025], wsum[32];
   __shared__ uint32_t red[16];
   const int tid = threadIdx.x, e = blockIdx.x;
-  expert_prefix(counts, E, T, a, b);
-  if (e == 0) {
-    if (tid < E) {
-      offs[tid + 1] = a[tid];
-      poffs[tid + 1] = b[tid];
-    }
-    if (tid == 0) {
-      offs[0] = 0;
-      poffs[0] = 0;
-    }
+  expert_prefix(counts, E, T, a, b, wsum);
+  if (e == 0 && tid <= E) {
+    offs[tid] = a[tid];
+    poffs[tid] = b[tid];
   }
-  const int r0 = e ? a[e - 1] : 0, r1 = a[e];
+  const int r0 = a[e], r1 = a[e + 1];
+  const uint4* rm4 = reinterpret_cast<const uint4*>(rowmax);
   uint32_t m = 0;
-  for (int r = r0 + tid; r < r1; r += 1024) m = max(m, rowmax[r]);
+  for (int g = (r0 >> 2) + tid; 4 * g < r1; g += 1024) {
+    const uint4 q = rm4[g];
+    const int r = 4 * g;
+    if (r >= r0) m = max(m, q.x);
+    if (r + 1 >= r0 && r + 1 < r1) m = max(m, q.y);
+    if (r + 2 >= r0 && r + 2 < r1) m = max(m, q.z);
+    if (r + 3 < r1) m = max(m, q.w);
+  }
   m = wave_max_u32(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
@@ -226,6 +245,14 @@ __device__ __forceinline__ uint32_t enc_pair(uint32_t old, float a, float b, con
   return fp4_pack2<SEL>(old, quot_apply(a, g.r_hi, g.r_lo), quot_apply(b, g.r_hi, g.r_lo), g.scale);
 }
 
+// The first byte pair of a word whose four byte pairs all get written: the
+// converter's merge operand is the first quotient's own register (its other
+// bytes are overwritten later), so no zeroed word is needed.
+__device__ __forceinline__ uint32_t enc_first(float a, float b, const GenBlock& g) {
+  const float qa = quot_apply(a, g.r_hi, g.r_lo);
+  return fp4_pack2<0>(__float_as_uint(qa), qa, quot_apply(b, g.r_hi, g.r_lo), g.scale);
+}
+
 // Per 16-row block of a tile: the split reciprocals of c = fl32(s * D) for
 // the 8 significands of s.  s * D = (m_s * m_D) * 2^(k_s + k_D), and while c
 // is a normal float fl32(s * D) = fl32(m_s * m_D) * 2^(k_s + k_D); the table
@@ -253,7 +280,7 @@ __device__ __forceinline__ MantEntry mant_entry(int j, float mD) {
 __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, const MantEntry* tab) {
   float s = e4m3_decode(sc);
   GenBlock g;
-  if (!(s > 0.0f) || !(D > 0.0f)) {
+  if (!(s > 0.0f)) {  // (D = 0 only gives the code 0)
     g.r_hi = g.r_lo = 0.0f;
     g.scale = 1.0f;
     return g;
@@ -271,7 +298,7 @@ __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, 
 // E4M3 code of fl32(fl32(a / 6) / D) * 2^-x2 for a block max a that is 2^x2
 // times the true one (x2 = 2: the unscaled RHT below).
 __device__ __forceinline__ uint32_t gen_scale_code_x(float a, const DScale& d, int x2) {
-  if (!(d.D > 0.0f)) return 0u;
+  // D = 0 (an all-zero expert: a = 0) needs no test: its split reciprocal is 0, so the code is 0
   bool tiny = a < 0x1p-100f;
   float pre = div6(tiny ? a * 0x1p64f : a);
   float q = quot_apply(pre, d.r_hi, d.r_lo);
@@ -291,6 +318,87 @@ __device__ __forceinline__ int qtile_col(int col0, int c, int W) {
 // LDS staging of the transposed tile, as in the direct receive: entry
 // (column c, block b) at c*16 + (b ^ ((c >> 3) & 15)).
 __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (b ^ ((c >> 3) & 15)); }
+
+// Rowwise operand of one thread's 16 rows x 8 columns (half of each 16-column
+// block; lane cg ^ 1 holds the other half): the pair's block max by a lane
+// swap, the E4M3 scale from D_row, the codes of the 8 values.  Rows at or
+// past nreal are not stored (every lane still takes part in the swap).
+__device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, float Drow, const MantEntry* tab,
+                                            uint8_t* rcp, uint8_t* rsp, uint32_t W, bool even) {
+  const DScale dsr = dscale(Drow);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t am = absmax_bf16x8(v[i]);
+    uint32_t o = lane_xor1(am);
+    am = am > o ? am : o;
+    if (i >= nreal) continue;
+    uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
+    GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, tab);
+    uint32_t w = enc_first(bf16lo(v[i].x), bf16hi(v[i].x), gb);
+    w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
+    w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
+    w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
+    *reinterpret_cast<uint32_t*>(rcp + (size_t)i * (W >> 1)) = w;
+    if (even) rsp[(size_t)i * (W >> 4)] = (uint8_t)sc;
+  }
+}
+
+// Columnwise operand of column pairs [P0, P1) of one thread's 8 columns x 16
+// rows (one block per column): 4x the RHT down each column (signs folded into the butterfly's
+// adds), the E4M3 scale from D_col, the 16 codes; codes and scales go to the
+// LDS stage at (column cg*8 + k, block m).
+template <int P0, int P1, typename ScT>
+__device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol, const MantEntry* tab, int cg, int m,
+                                               uint2* stage_codes, ScT* stage_sc) {
+  const DScale dsc = dscale(Dcol);
+#pragma unroll
+  for (int p = P0; p < P1; ++p) {
+    float z0[16], z1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t wv = p == 0 ? v[i].x : (p == 1 ? v[i].y : (p == 2 ? v[i].z : v[i].w));
+      const bool neg = (kRhtSignMask >> i) & 1u;
+      z0[i] = neg ? -bf16lo(wv) : bf16lo(wv);
+      z1[i] = neg ? -bf16hi(wv) : bf16hi(wv);
+    }
+    rht16_butterfly(z0);
+    rht16_butterfly(z1);
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a0 = fmaxf(a0, fabsf(z0[i]));
+      a1 = fmaxf(a1, fabsf(z1[i]));
+    }
+    uint32_t sc0 = gen_scale_code_x(a0, dsc, 2);
+    uint32_t sc1 = gen_scale_code_x(a1, dsc, 2);
+    GenBlock g0 = gen_block_tab(sc0, Dcol, dsc.kD, tab);
+    GenBlock g1 = gen_block_tab(sc1, Dcol, dsc.kD, tab);
+    // the values are 4x the transform: divide by 4 more
+    g0.scale *= 4.0f;
+    g1.scale *= 4.0f;
+    uint32_t c00 = enc_first(z0[0], z0[1], g0);
+    c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
+    c00 = enc_pair<2>(c00, z0[4], z0[5], g0);
+    c00 = enc_pair<3>(c00, z0[6], z0[7], g0);
+    uint32_t c01 = enc_first(z0[8], z0[9], g0);
+    c01 = enc_pair<1>(c01, z0[10], z0[11], g0);
+    c01 = enc_pair<2>(c01, z0[12], z0[13], g0);
+    c01 = enc_pair<3>(c01, z0[14], z0[15], g0);
+    uint32_t c10 = enc_first(z1[0], z1[1], g1);
+    c10 = enc_pair<1>(c10, z1[2], z1[3], g1);
+    c10 = enc_pair<2>(c10, z1[4], z1[5], g1);
+    c10 = enc_pair<3>(c10, z1[6], z1[7], g1);
+    uint32_t c11 = enc_first(z1[8], z1[9], g1);
+    c11 = enc_pair<1>(c11, z1[10], z1[11], g1);
+    c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
+    c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
+    const int c0 = cg * 8 + 2 * p;
+    stage_codes[qstage_at(c0, m)] = make_uint2(c00, c01);
+    stage_codes[qstage_at(c0 + 1, m)] = make_uint2(c10, c11);
+    stage_sc[qstage_at(c0, m)] = (ScT)sc0;
+    stage_sc[qstage_at(c0 + 1, m)] = (ScT)sc1;
+  }
+}
 
 // One workgroup per 256 padded rows x 128 columns of dX, 1-D grid with the
 // tiles dealt to the 8 XCDs in contiguous ranges, column tile fastest (as in
@@ -417,103 +525,44 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
   }
   __syncthreads();  // tables ready
 
-  if (live) {
-    const int row0 = s_row0[m], nreal = s_nreal[m];
-    const float Drow = s_drow[m], Dcol = s_dcol[m];
-    const DScale dsr = dscale(Drow), dsc = dscale(Dcol);
-    // ---- rowwise: the 16-column block is split over lanes cg, cg^1
-    const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
-    uint8_t* rcp = row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + (xcol >> 1);
-    uint8_t* rsp = row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + (xcol >> 4);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t am = absmax_bf16x8(v[i]);
-      uint32_t o = lane_xor1(am);
-      am = am > o ? am : o;
-      if (i >= nreal) continue;
-      uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
-      GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, s_tab[m][0]);
-      uint32_t w = 0;
-      w = enc_pair<0>(w, bf16lo(v[i].x), bf16hi(v[i].x), gb);
-      w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
-      w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
-      w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
-      *reinterpret_cast<uint32_t*>(rcp + (size_t)i * (uint32_t)(W >> 1)) = w;
-      if ((cg & 1) == 0) rsp[(size_t)i * (uint32_t)(W >> 4)] = (uint8_t)sc;
-    }
-    // ---- columnwise: 4x the RHT down each of the 8 columns, D_col = 4 * D_row
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float z0[16], z1[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t wv = p == 0 ? v[i].x : (p == 1 ? v[i].y : (p == 2 ? v[i].z : v[i].w));
-        const bool neg = (kRhtSignMask >> i) & 1u;
-        z0[i] = neg ? -bf16lo(wv) : bf16lo(wv);
-        z1[i] = neg ? -bf16hi(wv) : bf16hi(wv);
-      }
-      rht16_butterfly(z0);
-      rht16_butterfly(z1);
-      float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        a0 = fmaxf(a0, fabsf(z0[i]));
-        a1 = fmaxf(a1, fabsf(z1[i]));
-      }
-      uint32_t sc0 = gen_scale_code_x(a0, dsc, 2);
-      uint32_t sc1 = gen_scale_code_x(a1, dsc, 2);
-      GenBlock g0 = gen_block_tab(sc0, Dcol, dsc.kD, s_tab[m][1]);
-      GenBlock g1 = gen_block_tab(sc1, Dcol, dsc.kD, s_tab[m][1]);
-      // the values are 4x the transform: divide by 4 more
-      g0.scale *= 4.0f;
-      g1.scale *= 4.0f;
-      uint32_t c00 = 0, c01 = 0, c10 = 0, c11 = 0;
-      c00 = enc_pair<0>(c00, z0[0], z0[1], g0);
-      c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
-      c00 = enc_pair<2>(c00, z0[4], z0[5], g0);
-      c00 = enc_pair<3>(c00, z0[6], z0[7], g0);
-      c01 = enc_pair<0>(c01, z0[8], z0[9], g0);
-      c01 = enc_pair<1>(c01, z0[10], z0[11], g0);
-      c01 = enc_pair<2>(c01, z0[12], z0[13], g0);
-      c01 = enc_pair<3>(c01, z0[14], z0[15], g0);
-      c10 = enc_pair<0>(c10, z1[0], z1[1], g1);
-      c10 = enc_pair<1>(c10, z1[2], z1[3], g1);
-      c10 = enc_pair<2>(c10, z1[4], z1[5], g1);
-      c10 = enc_pair<3>(c10, z1[6], z1[7], g1);
-      c11 = enc_pair<0>(c11, z1[8], z1[9], g1);
-      c11 = enc_pair<1>(c11, z1[10], z1[11], g1);
-      c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
-      c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
-      const int c0 = cg * 8 + 2 * p;
-      stage_codes[qstage_at(c0, m)] = make_uint2(c00, c01);
-      stage_codes[qstage_at(c0 + 1, m)] = make_uint2(c10, c11);
-      stage_sc[qstage_at(c0, m)] = sc0;
-      stage_sc[qstage_at(c0 + 1, m)] = sc1;
-    }
-  }
+  // columnwise first: its transposed copy-out stores then drain while the
+  // rowwise operand is computed (rowwise first leaves them as a final burst)
+  if (live) fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
   __syncthreads();
   // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...
   const int b = tid & 15;
-  if (!s_live[b]) return;
-  const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
-  const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
+  if (s_live[b]) {
+    const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
+    const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
 #pragma unroll
-  for (int r = 0; r < (kQTileCols * kQBlocks) / 256; ++r) {
-    const int c = r * 16 + (tid >> 4);
-    if (c >= ncols) break;
-    const uint32_t h = (uint32_t)qtile_col<RECOMPUTE>(col0, c, W);
-    *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[qstage_at(c, b)];
-    col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[qstage_at(c, b)];
+    for (int r = 0; r < (kQTileCols * kQBlocks) / 256; ++r) {
+      const int c = r * 16 + (tid >> 4);
+      if (c >= ncols) break;
+      const uint32_t h = (uint32_t)qtile_col<RECOMPUTE>(col0, c, W);
+      *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[qstage_at(c, b)];
+      col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[qstage_at(c, b)];
+    }
+  }
+  if (live) {
+    const int row0 = s_row0[m], nreal = s_nreal[m];
+    const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
+    fc1_rowwise(v, nreal, s_drow[m], s_tab[m][0], row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + (xcol >> 1),
+                row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + (xcol >> 4), (uint32_t)W, (cg & 1) == 0);
   }
 }
+
 
 }  // namespace mtb
 
 using namespace mtb;
 
+// Workspace: the row maxima (one word per row, padded to a multiple of 4
+// rows, 16-byte aligned at the start), then the offsets and padded offsets.
+static size_t rowmax_bytes(int64_t tokens) { return (size_t)((tokens + 3) / 4) * 16; }
+
 MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts) {
   if (num_experts < 1 || tokens < 0) return 0;
-  return (size_t)(2 * (num_experts + 1) * sizeof(int32_t) + tokens * sizeof(uint32_t));
+  return rowmax_bytes(tokens) + (size_t)(2 * (num_experts + 1) * sizeof(int32_t));
 }
 
 MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
@@ -525,12 +574,13 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
   if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
   if (tokens > 0 && (!preact || !dy || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
-  if (!workspace || workspace_bytes < dswiglu_workspace_bytes(tokens, num_experts)) return EP_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < dswiglu_workspace_bytes(tokens, num_experts) || ((uintptr_t)workspace & 15))
+    return EP_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const int T = (int)tokens, F = (int)ffn, E = (int)num_experts;
-  int32_t* offs = (int32_t*)workspace;
+  uint32_t* rowmax = (uint32_t*)workspace;
+  int32_t* offs = (int32_t*)((char*)workspace + rowmax_bytes(tokens));
   int32_t* poffs = offs + (E + 1);
-  uint32_t* rowmax = (uint32_t*)(poffs + (E + 1));
   if (T > 0 && dx)
     hipLaunchKernelGGL(k_dswiglu_epilogue<true>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, dx,
                        rowmax);

@@ -57,7 +57,7 @@ def test_helpers(lib):
     assert lib.ep_route_capacity(1, 1, 1, 24) == -3
     assert m.ep_rht_sign_mask() == 0xE8D5
     assert m.ep_status_string(-4).startswith("r_cap")
-    assert lib.dswiglu_workspace_bytes(10, 8) == 72 + 40
+    assert lib.dswiglu_workspace_bytes(10, 8) == 72 + 48  # offsets + row maxima padded to 4 rows
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="passes fake pointers: only where no GPU exists")
@@ -92,6 +92,7 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, P, P, P, P, P, P, N, P, N) == -1
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 100, P, 2, P, P, P, P, P, P, P, P, P, 16, N) == -2
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, P, 4, N) == -7
+    assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, ctypes.c_void_p(0x1008), 4096, N) == -7  # misaligned
 
 
 def test_binding_refuses_cpu_and_wrong_dtypes(lib):
