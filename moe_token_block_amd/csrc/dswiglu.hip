@@ -23,6 +23,7 @@ namespace mtb {
 constexpr int kQTileRows = 256;
 constexpr int kQTileCols = 128;
 constexpr int kQBlocks = kQTileRows / 16;
+constexpr int kQThreads = 16 * kQBlocks;  // 16 threads (8 columns each) per 16-row block
 constexpr unsigned kXcdsQ = 8;  // CDNA4: 8 XCDs, workgroups dealt round-robin
 
 // Inclusive scan of one int per lane with the running total cut at cap
@@ -316,15 +317,16 @@ __device__ __forceinline__ int qtile_col(int col0, int c, int W) {
 }
 
 // LDS staging of the transposed tile, as in the direct receive: entry
-// (column c, block b) at c*16 + (b ^ ((c >> 3) & 15)).
-__device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (b ^ ((c >> 3) & 15)); }
+// (column c, block b) at c*kQBlocks + (b ^ ((c >> 3) % kQBlocks)).
+__device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (b ^ ((c >> 3) & (kQBlocks - 1))); }
 
 // Rowwise operand of one thread's 16 rows x 8 columns (half of each 16-column
 // block; lane cg ^ 1 holds the other half): the pair's block max by a lane
 // swap, the E4M3 scale from D_row, the codes of the 8 values.  Rows at or
 // past nreal are not stored (every lane still takes part in the swap).
 __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, float Drow, const MantEntry* tab,
-                                            uint8_t* rcp, uint8_t* rsp, uint32_t W, bool even) {
+                                            uint8_t* cbase, uint32_t coff, uint8_t* sbase, uint32_t soff, uint32_t W,
+                                            bool even) {
   const DScale dsr = dscale(Drow);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -338,8 +340,8 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
     w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
     w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
     w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
-    *reinterpret_cast<uint32_t*>(rcp + (size_t)i * (W >> 1)) = w;
-    if (even) rsp[(size_t)i * (W >> 4)] = (uint8_t)sc;
+    *reinterpret_cast<uint32_t*>(cbase + (coff + (uint32_t)i * (W >> 1))) = w;
+    if (even) sbase[soff + (uint32_t)i * (W >> 4)] = (uint8_t)sc;
   }
 }
 
@@ -414,7 +416,7 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
 // arithmetic (so the values, and the amax already taken from them, agree bit
 // for bit).
 template <bool RECOMPUTE>
-__global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
+__global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
                                                    const uint16_t* __restrict__ dy, int T, int W /* 2F */, int E,
                                                    int n_ct, const int32_t* __restrict__ offs,
                                                    const int32_t* __restrict__ poffs,
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
                                                    const float* __restrict__ col_scale,
                                                    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
                                                    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales) {
-  __shared__ uint2 stage_codes[kQTileCols * kQBlocks];   // offsets, padded offsets first
+  __shared__ uint2 stage_codes[kQTileCols * kQBlocks > 1025 ? kQTileCols * kQBlocks : 1025];  // offsets, padded offsets first
   __shared__ uint32_t stage_sc[kQTileCols * kQBlocks];
   __shared__ MantEntry s_tab[kQBlocks][2][8];            // [block][row / col][significand of s]
   __shared__ int s_live[kQBlocks], s_row0[kQBlocks], s_nreal[kQBlocks];
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
   const int col0 = ct * kQTileCols;
   const int ncols = min(kQTileCols, W - col0);
 
-  for (int i = tid; i <= E; i += 256) {
+  for (int i = tid; i <= E; i += kQThreads) {
     s_offs[i] = offs[i];
     s_poffs[i] = poffs[i];
   }
@@ -486,26 +488,39 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
 
   const int cg = tid & 15, m = tid >> 4;
   const bool live = s_live[m] && cg * 8 < ncols;
+  // Addresses: a workgroup-uniform base at the tile's first real row (block 0
+  // of a live tile is live) plus 32-bit per-lane offsets, so each access costs
+  // one 24-bit multiply-add instead of 64-bit address arithmetic.  The tile's
+  // rows lie within 256 + 15 rows of that base: offsets stay below 2^32.
+  const uint32_t rbase = (uint32_t)__builtin_amdgcn_readfirstlane(s_row0[0]);
   uint4 v[16];
   if (live) {
     const int row0 = s_row0[m], nreal = s_nreal[m];
+    const uint32_t rrel = (uint32_t)row0 - rbase;
     if (nreal > 0) {
       // branch-free: rows past the expert's end re-read its last row and are zeroed
       if (!RECOMPUTE) {
-        const uint16_t* base = dx + col0 + 8 * cg;
+        const char* base = reinterpret_cast<const char*>(dx + (size_t)rbase * (uint32_t)W + col0);
+        const uint32_t w2 = 2u * (uint32_t)W, o0 = rrel * w2 + 16u * (uint32_t)cg;
+        // plain loads, not streaming ones: dX was just written by the epilogue
+        // and much of it still sits in the last-level cache
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          uint4 t = ld_stream16(base + (size_t)(uint32_t)(row0 + min(i, nreal - 1)) * (uint32_t)W);
+          uint4 t = *reinterpret_cast<const uint4*>(base + (o0 + __umul24((uint32_t)min(i, nreal - 1), w2)));
           v[i] = i < nreal ? t : make_uint4(0, 0, 0, 0);
         }
       } else {
         const int F = W >> 1, j = (col0 >> 1) + 8 * (cg & 7);  // col0 = 128 ct: j0 = 64 ct
         const bool want_b = cg >= 8;                             // this thread keeps db (else da)
+        const char* pbase = reinterpret_cast<const char*>(preact + (size_t)rbase * (uint32_t)W + (col0 >> 1));
+        const char* dbase = reinterpret_cast<const char*>(dy + (size_t)rbase * (uint32_t)F + (col0 >> 1));
+        const uint32_t w2 = 2u * (uint32_t)W, f2 = 2u * (uint32_t)F, jl = 16u * (uint32_t)(cg & 7);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const size_t r = (size_t)(uint32_t)(row0 + min(i, nreal - 1));
-          uint4 va = ld_stream16(preact + r * (uint32_t)W + j), vb = ld_stream16(preact + r * (uint32_t)W + F + j);
-          uint4 vd = ld_stream16(dy + r * (uint32_t)F + j);
+          const uint32_t r = rrel + (uint32_t)min(i, nreal - 1);
+          const uint32_t op = __umul24(r, w2) + jl, od = __umul24(r, f2) + jl;
+          uint4 va = ld_stream16(pbase + op), vb = ld_stream16(pbase + (op + f2));
+          uint4 vd = ld_stream16(dbase + od);
           uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w}, wd[4] = {vd.x, vd.y, vd.z, vd.w};
           uint32_t o[4];
 #pragma unroll
@@ -530,24 +545,37 @@ __global__ __launch_bounds__(256) void k_fc1_quant(const uint16_t* __restrict__ 
   if (live) fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
   __syncthreads();
   // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...
-  const int b = tid & 15;
+  const int b = tid % kQBlocks;
   if (s_live[b]) {
-    const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
-    const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
+    const uint64_t cstr = s_cstr[b], sstr = s_sstr[b];
+    // running pointers: column c advances by kQThreads / kQBlocks per step
+    // (the recompute mapping's db half starts at column 64: its own base)
+    const int c0 = tid / kQBlocks;
+    const uint64_t h0 = (uint64_t)qtile_col<RECOMPUTE>(col0, c0, W);
+    uint8_t* pc = col_codes + s_cbase[b] + h0 * cstr;
+    uint8_t* ps = col_scales + s_sbase[b] + h0 * sstr;
+    const uint64_t cstep = (uint64_t)(kQThreads / kQBlocks) * cstr, sstep = (uint64_t)(kQThreads / kQBlocks) * sstr;
 #pragma unroll
-    for (int r = 0; r < (kQTileCols * kQBlocks) / 256; ++r) {
-      const int c = r * 16 + (tid >> 4);
+    for (int r = 0; r < (kQTileCols * kQBlocks) / kQThreads; ++r) {
+      const int c = r * (kQThreads / kQBlocks) + c0;
       if (c >= ncols) break;
-      const uint32_t h = (uint32_t)qtile_col<RECOMPUTE>(col0, c, W);
-      *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[qstage_at(c, b)];
-      col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[qstage_at(c, b)];
+      if (RECOMPUTE && c == 64 + c0) {  // da columns end, db columns begin
+        const uint64_t h = (uint64_t)qtile_col<RECOMPUTE>(col0, c, W);
+        pc = col_codes + s_cbase[b] + h * cstr;
+        ps = col_scales + s_sbase[b] + h * sstr;
+      }
+      *reinterpret_cast<uint2*>(pc) = stage_codes[qstage_at(c, b)];
+      *ps = (uint8_t)stage_sc[qstage_at(c, b)];
+      pc += cstep;
+      ps += sstep;
     }
   }
   if (live) {
-    const int row0 = s_row0[m], nreal = s_nreal[m];
+    const uint32_t rrel = (uint32_t)s_row0[m] - rbase;
     const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
-    fc1_rowwise(v, nreal, s_drow[m], s_tab[m][0], row_codes + (size_t)(uint32_t)row0 * (uint32_t)(W >> 1) + (xcol >> 1),
-                row_scales + (size_t)(uint32_t)row0 * (uint32_t)(W >> 4) + (xcol >> 4), (uint32_t)W, (cg & 1) == 0);
+    fc1_rowwise(v, s_nreal[m], s_drow[m], s_tab[m][0], row_codes + (size_t)rbase * (uint32_t)(W >> 1),
+                rrel * (uint32_t)(W >> 1) + (uint32_t)(xcol >> 1), row_scales + (size_t)rbase * (uint32_t)(W >> 4),
+                rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4), (uint32_t)W, (cg & 1) == 0);
   }
 }
 
@@ -592,12 +620,12 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
   // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
   const int64_t prow_bound = tokens + 15 * num_experts;
   const int64_t n_rt = (prow_bound + kQTileRows - 1) / kQTileRows, n_ct = (2 * F + kQTileCols - 1) / kQTileCols;
-  if (n_rt * n_ct * 256 >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  if (n_rt * n_ct * kQThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   if (dx)
-    hipLaunchKernelGGL(k_fc1_quant<false>, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, preact, dy, T, 2 * F, E,
+    hipLaunchKernelGGL(k_fc1_quant<false>, dim3((unsigned)(n_rt * n_ct)), dim3(kQThreads), 0, s, dx, preact, dy, T, 2 * F, E,
                        (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
   else
-    hipLaunchKernelGGL(k_fc1_quant<true>, dim3((unsigned)(n_rt * n_ct)), dim3(256), 0, s, dx, preact, dy, T, 2 * F, E,
+    hipLaunchKernelGGL(k_fc1_quant<true>, dim3((unsigned)(n_rt * n_ct)), dim3(kQThreads), 0, s, dx, preact, dy, T, 2 * F, E,
                        (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
   return launch_status();
 }
