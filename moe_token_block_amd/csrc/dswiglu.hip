@@ -81,9 +81,10 @@ __global__ __launch_bounds__(1024) void k_dswiglu_reduce(const int32_t* __restri
   __shared__ uint32_t red[16];
   const int tid = threadIdx.x, e = blockIdx.x;
   expert_prefix(counts, E, T, a, b, wsum);
-  if (e == 0 && tid <= E) {
-    offs[tid] = a[tid];
-    poffs[tid] = b[tid];
+  if (e == 0 && tid < E) {  // entries 1..E (E may be 1024 = the block size), then entry 0
+    offs[tid + 1] = a[tid + 1];
+    poffs[tid + 1] = b[tid + 1];
+    if (tid == 0) offs[0] = poffs[0] = 0;
   }
   const int r0 = a[e], r1 = a[e + 1];
   const uint4* rm4 = reinterpret_cast<const uint4*>(rowmax);

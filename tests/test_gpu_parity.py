@@ -302,7 +302,11 @@ def test_mxfp8_receive_bit_exact(dev):
                                                   ([300, 0, 129], 256, None), ([1], 64, None),
                                                   # tiny D (c = s*D below 2^-104: the general block path),
                                                   # huge values, and an all-zero expert
-                                                  ([40, 24, 19, 8], 64, [1e-33, 1e32, 0.0, 1.0])])
+                                                  ([40, 24, 19, 8], 64, [1e-33, 1e32, 0.0, 1.0]),
+                                                  # many experts, mostly empty (the offsets scan spans waves)
+                                                  ([3] + [0] * 200 + [17] + [0] * 97 + [5], 64, None),
+                                                  # the maximum expert count, one row each
+                                                  ([1] * 1024, 64, None)])
 def test_dswiglu_two_stage(dev, counts, ffn, dy_scales):
     w = workloads.small_dswiglu(sum(counts) + ffn, counts, ffn, dy_scales)
     print(f"dswiglu counts={counts} ffn={ffn} dy_scales={dy_scales}", flush=True)
@@ -324,6 +328,34 @@ def test_dswiglu_two_stage(dev, counts, ffn, dy_scales):
     n = q["col_codes"].size
     tolerant_codes(F.unpack_nibbles(host(out["col_codes"])[:n]), F.unpack_nibbles(q["col_codes"]),
                    host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "fc1 columnwise")
+
+
+@pytest.mark.parametrize("dev_counts,rows", [([30, 40], 50), ([-5, 50, 7], 50), ([0, 0], 9)])
+def test_dswiglu_counts_cut_at_tokens(dev, dev_counts, rows):
+    """Counts are device data: a negative count is 0 and the running total is cut
+    at the token count, so the call reads and writes only the tokens' rows; the
+    result is the oracle's for the counts so cut."""
+    cut, run = [], 0
+    for c in dev_counts:
+        c = min(max(c, 0), rows - run)
+        cut.append(c)
+        run += c
+    w = workloads.small_dswiglu(rows + 11, [rows], 64)
+    print(f"dswiglu device counts={dev_counts} rows={rows} -> {cut}", flush=True)
+    out = mtb.dswiglu_nvfp4_quant(bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev),
+                                  i32_dev(np.array(dev_counts, dtype=np.int32), dev))
+    dx, am = host(out["dx"]), host(out["amax"])
+    cut = np.array(cut, dtype=np.int32)
+    assert_bytes_equal(am.view(np.uint32), odsw.expert_amax(dx[: cut.sum()], cut).view(np.uint32), "amax")
+    if cut.sum() == 0:
+        return
+    q = odsw.fc1_grad_quant(dx[: cut.sum()], cut, am)
+    n = int(cut.sum())
+    tolerant_codes(F.unpack_nibbles(host(out["row_codes"])[:n]), F.unpack_nibbles(q["row_codes"]),
+                   host(out["row_scales"])[:n], q["row_scales"], "cut rowwise")
+    m = q["col_codes"].size
+    tolerant_codes(F.unpack_nibbles(host(out["col_codes"])[:m]), F.unpack_nibbles(q["col_codes"]),
+                   host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "cut columnwise")
 
 
 @pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([300, 0, 129], 256), ([40, 24, 19, 8], 128)])
