@@ -46,11 +46,18 @@ __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict
   const int g0 = offsets[e], g1 = offsets[e + 1];
   const int toff = (H >> 1) + (H >> 4);
   uint32_t m = 0;  // t > 0 is a power of two: compare bit patterns
-  for (int g = g0 + (int)threadIdx.x; g < g1; g += 1024) {
-    int src = src_row[g];
-    if (src >= 0 && src < T) {
-      uint32_t tb = *reinterpret_cast<const uint32_t*>(packed + (size_t)src * row_bytes + toff);
-      m = m > tb ? m : tb;
+  // four rows per thread per round: the four source-row loads go out together,
+  // then the four t loads (two dependent round trips per 4096 rows, not per 1024)
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += 4 * 1024) {
+    int src[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) src[q] = g + q * 1024 < g1 ? src_row[g + q * 1024] : -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (src[q] >= 0 && src[q] < T) {
+        uint32_t tb = *reinterpret_cast<const uint32_t*>(packed + (size_t)src[q] * row_bytes + toff);
+        m = m > tb ? m : tb;
+      }
     }
   }
   m = wave_max_u32(m);
@@ -72,9 +79,12 @@ __global__ __launch_bounds__(1024) void k_expert_scale_grouped(const float* __re
   const int e = blockIdx.x;
   const int g0 = max(0, offsets[e]), g1 = min(r_cap, offsets[e + 1]);
   uint32_t m = 0;  // t >= 0: compare bit patterns
-  for (int g = g0 + (int)threadIdx.x; g < g1; g += 1024) {
-    uint32_t tb = __float_as_uint(row_t[g]);
-    m = m > tb ? m : tb;
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += 4 * 1024) {
+    uint32_t tb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tb[q] = g + q * 1024 < g1 ? __float_as_uint(row_t[g + q * 1024]) : 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = m > tb[q] ? m : tb[q];
   }
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
