@@ -41,6 +41,10 @@ __device__ __forceinline__ void decode8_tiny(uint32_t w, float s, int e, uint32_
 // One wave per output row; lane l decodes 8-element chunks l, l+64, ... (a
 // dword of codes -> 16 bytes of BF16), so every load instruction reads 256
 // contiguous code bytes and every store writes 1 KiB contiguously.
+// NT: streaming (nontemporal) stores, for outputs much larger than the last-level
+// cache -- measured 548 -> 405 us on a 1.9 GB output, but slower on outputs the
+// 256 MB MALL holds (23.4 -> 24.7 us on 67 MB), so the host picks by size.
+template <bool NT>
 __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict__ packed, int rows_in, int H,
                                                       int row_bytes, const int32_t* __restrict__ src_row,
                                                       int rows_out, uint16_t* __restrict__ out) {
@@ -73,7 +77,12 @@ __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict_
       if (K >= -126) decode8(w, pow2f(K), mant, o);
       else decode8_tiny(w, s, e, o);
     }
-    orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    if (NT) {
+      const u32x4 ov = {o[0], o[1], o[2], o[3]};
+      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(orow + c));
+    } else {
+      orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
@@ -115,8 +124,12 @@ MTB_EXPORT int32_t ep_nvfp4_unpack(const uint8_t* packed, int64_t rows_in, int64
   if (!src_row && rows_in == 0) return EP_OK;
   const int H = (int)hidden;
   dim3 grid((unsigned)((rows_out + 3) / 4)), block(256);
-  hipLaunchKernelGGL(k_nvfp4_unpack, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
-                     9 * H / 16 + 4, src_row, (int)rows_out, out);
+  if ((uint64_t)rows_out * (uint64_t)H * 2u > kStreamStoreBytes)
+    hipLaunchKernelGGL(k_nvfp4_unpack<true>, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
+                       9 * H / 16 + 4, src_row, (int)rows_out, out);
+  else
+    hipLaunchKernelGGL(k_nvfp4_unpack<false>, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
+                       9 * H / 16 + 4, src_row, (int)rows_out, out);
   return launch_status();
 }
 
