@@ -19,8 +19,9 @@ Source pages (cited by title and section):
 
 The pages name the formats and the passes but fix no rounding rule, constant,
 byte order or random-number mapping.  Every such rule is a reading written out
-in the docstring of the function that implements it (rules R1..R21, and R8b:
-a second stochastic-rounding decision rule, the carry form).
+in the docstring of the function that implements it (rules R1..R21, R8b: a
+second stochastic-rounding decision rule, the carry form, and R22..R23 in
+``mxfp4``: an MXFP4 variant of the receive that no page describes).
 
 Precision: where a rule says ``fl32(.)`` the oracle computes in numpy float32
 (IEEE binary32, round-to-nearest-even, gradual underflow); everything else is
@@ -31,4 +32,4 @@ something other than itself, except the choice of the RHT sign vector (an
 arbitrary fixed constant by design) -- parity unpinned for that choice only.
 """
 
-from . import formats, philox, nvfp4, mxfp8, routing, rht, receive, dswiglu  # noqa: F401
+from . import formats, philox, nvfp4, mxfp8, mxfp4, routing, rht, receive, dswiglu  # noqa: F401
