@@ -234,6 +234,30 @@ int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, in
                                        uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
                                        void* stream);
 
+/* MXFP4 variant of the direct receive.  No page describes it: gfx950's
+ * block-scaled matrix instructions take E2M1 elements with one E8M0 scale (a
+ * power of two) per 32 elements along K, not NVFP4's E4M3 scale per 16, so
+ * this receive re-quantizes the same routed rows to that format in one pass.
+ * Decode (exact) and the columnwise RHT are those of ep_nvfp4_direct_receive;
+ * the quantizer, per block of 32 values x: e = the least integer with
+ * max|x| <= 6 * 2^e, clamped to [-127, 127] (0 for an all-zero block); scale
+ * byte e + 127; code = sign(x) | E2M1 round-to-nearest-even of |x| / 2^e
+ * (exact, nothing clips).  No per-expert scale and no amax pass.
+ *   Rowwise: row_codes [r_cap, hidden/2] (element 2j in the low nibble of byte
+ *   j), row_scales [r_cap, hidden/32], for grouped rows g < off_E; padding rows
+ *   are zero values (codes 0, scale byte 127); rows >= off_E untouched.
+ *   Columnwise: blocks of 32 consecutive grouped rows of one column (two RHT
+ *   blocks).  Expert e's codes are an [hidden, P_e/2] byte matrix at byte
+ *   hidden*off_e/2 of col_codes, its scales an [hidden, P_e/32] matrix at byte
+ *   hidden*off_e/32 of col_scales (hidden*r_cap/2 and hidden*r_cap/32 bytes).
+ *   alignment: the one the route plan was made with; a multiple of 32
+ *   (EP_ERR_ALIGN otherwise), so no 32-row block straddles two experts.
+ *   Requires hidden a positive multiple of 64 and 1 <= num_experts <= 1024. */
+int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                                int64_t alignment, int64_t r_cap, const int32_t* offsets, const int32_t* src_row,
+                                uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                                void* stream);
+
 /* MXFP8 receive (P2, description and review comments: received data and block
  * scales are returned per expert, grouped, with 128-aligned slots there --
  * here any multiple of 16): grouped row g copies token src_row[g]'s data row

@@ -46,6 +46,7 @@ _SIGS = {
     "ep_nvfp4_direct_receive_scaled": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_mxfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -220,7 +221,7 @@ def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None,
                                    _ptr(src_row), _ptr(workspace), workspace.numel(), _ptr(d_error), _stream(dev)),
                "ep_route_plan")
     return dict(counts=counts, offsets=offsets, dst_row=dst_row, src_row=src_row, d_error=d_error, r_cap=r_cap,
-                num_experts=num_experts)
+                num_experts=num_experts, alignment=alignment)
 
 
 def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
@@ -260,6 +261,25 @@ def ep_nvfp4_direct_receive_kblock(packed, hidden, plan, out):
             _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _stream(dev)),
             "ep_nvfp4_direct_receive_kblock")
+    return out
+
+
+def ep_mxfp4_direct_receive(packed, hidden, plan, out=None):
+    """MXFP4 rowwise and RHT columnwise grouped operands (E2M1 codes, one E8M0 scale
+    per 32 elements) from NVFP4 packed rows and a routing plan whose alignment is a
+    multiple of 32."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    r_cap = plan["r_cap"]
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=dev)
+        out = dict(row_codes=torch.empty((r_cap, hidden // 2), **u8), row_scales=torch.empty((r_cap, hidden // 32), **u8),
+                   col_codes=torch.empty(r_cap * hidden // 2, **u8), col_scales=torch.empty(r_cap * hidden // 32, **u8))
+    with torch.cuda.device(dev):
+        _check(lib().ep_mxfp4_direct_receive(
+            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan.get("alignment", 16), r_cap,
+            _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _stream(dev)), "ep_mxfp4_direct_receive")
     return out
 
 

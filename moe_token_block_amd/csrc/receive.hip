@@ -488,6 +488,261 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
   }
 }
 
+// ------------------------------------------------------------------ MXFP4 receive
+// The same routed rows re-quantized to MXFP4 -- E2M1 codes with one E8M0 scale
+// (a power of two) per 32 elements, the operand format of gfx950's
+// block-scaled matrix instructions -- rowwise along H and columnwise after the
+// 16-point RHT, 32 grouped rows per columnwise block (two RHT blocks).  The
+// NVFP4 decode and the RHT are exactly the NVFP4 receive's; only the final
+// quantizer differs, and it needs no per-expert scale: no amax pass at all.
+
+// Exponent of an MXFP4 block with max a >= 0: the least e with a <= 6 * 2^e
+// (no element clipped), clamped to [-127, 127]; a = 0 gives 0.  For
+// a = m * 2^E, m in [1, 2): e = E - 2 + [m > 1.5].
+__device__ __forceinline__ int mx4_exponent(float a) {
+  if (!(a > 0.0f)) return 0;
+  int sub = 0;
+  if (a < 0x1p-126f) { a *= 0x1p64f; sub = 64; }
+  const int E = __builtin_amdgcn_frexp_expf(a) - 1 - sub;
+  const float m = __builtin_amdgcn_frexp_mantf(a) * 2.0f;
+  const int e = E - 2 + (m > 1.5f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Eight values / 2^e -> one word of E2M1 codes (value 2j in the low nibble of
+// byte j): the converter's rounding is an exact round-to-nearest-even of the
+// quotient by its power of two.  Below 2^-126 that power is not a normal
+// float, so the values are scaled by 2^64 first (exact).
+__device__ __forceinline__ uint32_t mx4_word(const float* v, int e) {
+  float k = 1.0f, sc;
+  if (e >= -126) {
+    sc = pow2f(e);
+  } else {
+    k = 0x1p64f;
+    sc = pow2f(e + 64);
+  }
+  uint32_t w = fp4_pack2<0>(__float_as_uint(v[0]), v[0] * k, v[1] * k, sc);
+  w = fp4_pack2<1>(w, v[2] * k, v[3] * k, sc);
+  w = fp4_pack2<2>(w, v[4] * k, v[5] * k, sc);
+  return fp4_pack2<3>(w, v[6] * k, v[7] * k, sc);
+}
+
+// The value of lane ^ 2 (DPP quad permutation [2, 3, 0, 1]).
+__device__ __forceinline__ float lane_xor2_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// One workgroup per 256 grouped rows x 128 columns, as the NVFP4 receive.
+// Thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8) of the 16
+// rows of block m.  Rowwise: a 32-column block spans lanes 4j..4j+3 (its max by
+// two lane swaps).  Columnwise: decode + RHT per column pair as the NVFP4
+// receive, a 32-row block spans blocks m and m^1 (lanes 16 apart in one wave).
+// Every expert's padded rows are a multiple of 32 (the host checks the
+// alignment), so a 32-row block never straddles two experts.
+__global__ __launch_bounds__(kThreads) void k_mxfp4_receive(const uint8_t* __restrict__ packed, int T, int H,
+                                                       int row_bytes, const int32_t* __restrict__ offsets, int E,
+                                                       const int32_t* __restrict__ src_row, int r_cap, int n_ct,
+                                                       uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+                                                       uint8_t* __restrict__ col_codes,
+                                                       uint8_t* __restrict__ col_scales) {
+  __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block ^ swizzle]; offsets first
+  __shared__ uint8_t stage_sc[kTileCols * (kBlocks / 2)];  // [column][32-row block]
+  __shared__ int s_src[kTileRows];
+  __shared__ float s_t[kTileRows];
+  __shared__ float s_tq[kTileRows];                    // t * d_i / 4 (i = row mod 16)
+  __shared__ uint32_t s_sw[kTileRows][2];              // the tile's 8 NVFP4 scale bytes of each row
+  __shared__ int s_slow[kBlocks], s_live[kBlocks];
+  __shared__ uint64_t s_cbase[kBlocks], s_sbase[kBlocks / 2];
+  __shared__ uint32_t s_cstr[kBlocks], s_sstr[kBlocks / 2];
+  int* s_offs = reinterpret_cast<int*>(stage_codes);  // offsets[0..E] until the column phase
+
+  const int tid = threadIdx.x;
+  const unsigned nb = gridDim.x, bx = blockIdx.x;
+  const unsigned xq = nb / kXcds, xr = nb % kXcds, x = bx % kXcds;
+  const unsigned lt = x * xq + min(x, xr) + bx / kXcds;
+  const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
+  const int col0 = ct * kTileCols;
+  const int ncols = min(kTileCols, H - col0);
+  const int g_base = rt * kTileRows;
+
+  {
+    const int g = g_base + tid;
+    const int src = g < r_cap ? src_row[g] : -1;
+    s_src[tid] = (src >= 0 && src < T) ? src : -1;
+    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+  }
+  __syncthreads();
+  const int tile_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
+
+  if (tid < kBlocks) {
+    const int gb = g_base + 16 * tid;
+    const int live = gb < tile_end;
+    s_live[tid] = live;
+    if (live) {
+      int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
+      }
+      const int off = s_offs[lo], len = s_offs[lo + 1] - off;
+      s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+      s_cstr[tid] = (uint32_t)(len >> 1);
+      if ((tid & 1) == 0) {
+        s_sbase[tid >> 1] = (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
+        s_sstr[tid >> 1] = (uint32_t)(len >> 5);
+      }
+    }
+  }
+  {
+    const int src = s_src[tid];
+    float t = 0.0f;
+    uint32_t sw0 = 0, sw1 = 0;
+    if (src >= 0) {
+      const uint8_t* prow = packed + (size_t)(uint32_t)src * (uint32_t)row_bytes;
+      t = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
+      sw0 = sp[0];
+      if (ncols > 64) sw1 = sp[1];
+    }
+    s_t[tid] = t;
+    s_tq[tid] = t * rht_in_scale(tid & 15);
+    s_sw[tid][0] = sw0;
+    s_sw[tid][1] = sw1;
+    const uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
+    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
+  }
+  const int cg = tid & 15, m = tid >> 4;
+  const int r0 = 16 * m;
+  const int gb = g_base + r0;
+  const bool live = gb < tile_end && cg * 8 < ncols;
+  uint32_t cw[16];
+  {
+    int4 sv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
+    const int* sr = reinterpret_cast<const int*>(sv);
+    const uint8_t* base = packed + (col0 >> 1) + 4 * cg;
+    if (live && T > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int src = sr[i];
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes);
+        cw[i] = src >= 0 ? v : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cw[i] = 0u;
+    }
+  }
+  __syncthreads();
+
+  // column phase (every lane takes part: the 32-row max crosses lanes 16 apart)
+  {
+    const int sh = 8 * ((cg >> 1) & 3);
+    const bool slow = s_slow[m] != 0;
+    float cm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
+      const float t = s_t[r0 + i];
+      // fast: s * t * d_i / 4 (exact: s has 4 significant bits, t/4 is a power
+      // of two); slow (a row with t < 2^-100): s * d_i / 4, t applied per row
+      cm[i] = !slow ? s * s_tq[r0 + i] : (t == 0.0f ? 0.0f : s * rht_in_scale(i));
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float z0[16], z1[16];
+      if (!slow) {
+        if (p == 0) decode_stage1<0, false>(cw, cm, nullptr, z0, z1);
+        if (p == 1) decode_stage1<1, false>(cw, cm, nullptr, z0, z1);
+        if (p == 2) decode_stage1<2, false>(cw, cm, nullptr, z0, z1);
+        if (p == 3) decode_stage1<3, false>(cw, cm, nullptr, z0, z1);
+      } else {
+        int ce[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float t = s_t[r0 + i];
+          ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
+        }
+        if (p == 0) decode_stage1<0, true>(cw, cm, ce, z0, z1);
+        if (p == 1) decode_stage1<1, true>(cw, cm, ce, z0, z1);
+        if (p == 2) decode_stage1<2, true>(cw, cm, ce, z0, z1);
+        if (p == 3) decode_stage1<3, true>(cw, cm, ce, z0, z1);
+      }
+      rht16_upper(z0);
+      rht16_upper(z1);
+      float a0 = absmax16(z0), a1 = absmax16(z1);
+      a0 = fmaxf(a0, __shfl_xor(a0, 16, kWave));  // block m ^ 1 of the same columns
+      a1 = fmaxf(a1, __shfl_xor(a1, 16, kWave));
+      const int e0 = mx4_exponent(a0), e1 = mx4_exponent(a1);
+      const int c0 = cg * 8 + 2 * p;
+      if (live) {
+        stage_codes[stage_at(c0, m)] = make_uint2(mx4_word(z0, e0), mx4_word(z0 + 8, e0));
+        stage_codes[stage_at(c0 + 1, m)] = make_uint2(mx4_word(z1, e1), mx4_word(z1 + 8, e1));
+        if ((m & 1) == 0) {
+          stage_sc[c0 * (kBlocks / 2) + (m >> 1)] = (uint8_t)(e0 + 127);
+          stage_sc[(c0 + 1) * (kBlocks / 2) + (m >> 1)] = (uint8_t)(e1 + 127);
+        }
+      }
+    }
+  }
+
+  // rowwise: the decoded values of each row, a 32-column block over lanes 4j..4j+3
+  {
+    const int sh = 8 * ((cg >> 1) & 3);
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const float st = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * s_t[r0 + i];
+      float v[8];
+      f32x2 g;
+      g = fp4_unpack2<0>(cw[i], 1.0f); v[0] = g[0] * st; v[1] = g[1] * st;
+      g = fp4_unpack2<1>(cw[i], 1.0f); v[2] = g[0] * st; v[3] = g[1] * st;
+      g = fp4_unpack2<2>(cw[i], 1.0f); v[4] = g[0] * st; v[5] = g[1] * st;
+      g = fp4_unpack2<3>(cw[i], 1.0f); v[6] = g[0] * st; v[7] = g[1] * st;
+      float a = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a = fmaxf(a, fabsf(v[q]));
+      a = fmaxf(a, __uint_as_float(lane_xor1(__float_as_uint(a))));
+      a = fmaxf(a, lane_xor2_f(a));
+      const int e = mx4_exponent(a);
+      const uint32_t w = mx4_word(v, e);
+      if (live) {
+        const size_t g_row = (size_t)(uint32_t)(gb + i);
+        *reinterpret_cast<uint32_t*>(row_codes + g_row * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg) = w;
+        if ((cg & 3) == 0) row_scales[g_row * (uint32_t)(H >> 5) + ((col0 + 8 * cg) >> 5)] = (uint8_t)(e + 127);
+      }
+    }
+  }
+  __syncthreads();
+  // transposed copy-out of the columnwise codes (as the NVFP4 receive), then
+  // the scales: thread (pair, j) writes 32-row block `pair` of columns j, j+32, ...
+  {
+    const int b = tid % kBlocks;
+    if (s_live[b]) {
+      const uint64_t cbase = s_cbase[b];
+      const uint32_t cstr = s_cstr[b];
+#pragma unroll
+      for (int r = 0; r < (kTileCols * kBlocks) / kThreads; ++r) {
+        const int c = r * (kThreads / kBlocks) + tid / kBlocks;
+        if (c >= ncols) break;
+        *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)(uint32_t)(col0 + c) * cstr) =
+            stage_codes[stage_at(c, b)];
+      }
+    }
+    const int pr = tid % (kBlocks / 2);
+    if (s_live[2 * pr]) {
+      const uint64_t sbase = s_sbase[pr];
+      const uint32_t sstr = s_sstr[pr];
+#pragma unroll
+      for (int r = 0; r < (kTileCols * (kBlocks / 2)) / kThreads; ++r) {
+        const int c = r * (kThreads / (kBlocks / 2)) + tid / (kBlocks / 2);
+        if (c >= ncols) break;
+        col_scales[sbase + (uint64_t)(uint32_t)(col0 + c) * sstr] = stage_sc[c * (kBlocks / 2) + pr];
+      }
+    }
+  }
+}
+
 // Rowwise-only receive: a plain gather of whole packed rows (codes, scales
 // and t), one wave per grouped row; rows below off_E with no source are zero.
 __global__ __launch_bounds__(256) void k_nvfp4_gather(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
@@ -630,5 +885,23 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t
   hipLaunchKernelGGL((k_nvfp4_receive<false, true>), dim3((unsigned)(n_kb * n_ct)), dim3(kThreads), 0,
                      (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                                           int64_t alignment, int64_t r_cap, const int32_t* offsets,
+                                           const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                           uint8_t* col_codes, uint8_t* col_scales, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (alignment < 32 || alignment % 32 != 0) return EP_ERR_ALIGN;
+  if (!row_codes || !row_scales || !col_codes || !col_scales) return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
+  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  hipLaunchKernelGGL(k_mxfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, packed,
+                     (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
+                     row_codes, row_scales, col_codes, col_scales);
   return launch_status();
 }

@@ -38,13 +38,14 @@ def assert_bytes_equal(got, want, what):
                              f"got {got[idx]} want {want[idx]}")
 
 
-def tolerant_codes(got_codes, want_codes, got_sc, want_sc, what, frac=1e-4):
+def tolerant_codes(got_codes, want_codes, got_sc, want_sc, what, frac=1e-4, block=16):
     """The bar for values derived from FP32 amaxes / post-RHT values: block scales
     differ by at most one E4M3 step in at most ``frac`` of blocks; where the scales
     agree, E2M1 codes differ by at most one grid step in at most ``frac`` of
     elements; where they differ, the decoded values are within one grid step at
     the larger scale.  Codes are unpacked 4-bit codes [..., 16 * nblocks] laid
-    out block-major along the last axis, scales [..., nblocks]."""
+    out block-major along the last axis, scales [..., nblocks]; ``block`` elements
+    per scale (16 for NVFP4, 32 for MXFP4, whose scale steps are powers of two)."""
     gc = np.asarray(got_codes, dtype=np.int64)
     wc = np.asarray(want_codes, dtype=np.int64)
     gs = np.asarray(got_sc, dtype=np.int64)
@@ -54,7 +55,7 @@ def tolerant_codes(got_codes, want_codes, got_sc, want_sc, what, frac=1e-4):
     sdiff = np.abs(gs - ws)
     assert sdiff.max(initial=0) <= 1, f"{what}: a block scale differs by {sdiff.max()} E4M3 steps"
     assert (sdiff > 0).sum() <= max(0, frac * nblk), f"{what}: {(sdiff > 0).sum()} of {nblk} block scales differ"
-    same = np.repeat((sdiff == 0).reshape(gs.shape), 16, axis=-1)
+    same = np.repeat((sdiff == 0).reshape(gs.shape), block, axis=-1)
     # one grid step: same sign and adjacent magnitude index (or +-0 vs the smallest step)
     gv = F.e2m1_value(gc.astype(np.uint8)) * 2
     wv = F.e2m1_value(wc.astype(np.uint8)) * 2

@@ -18,6 +18,7 @@ import moe_token_block_amd as mtb
 import workloads
 from oracle import formats as F
 from oracle import mxfp8 as omx
+from oracle import mxfp4 as omx4
 from oracle import nvfp4 as onv
 from oracle import dswiglu as odsw
 from oracle import receive as orecv
@@ -287,6 +288,59 @@ def test_direct_receive_kblock_layout(dev, case):
     assert_bytes_equal(host(kb["col_scales"])[: n // 16], ws, "K-block columnwise scales")
     for key in ("row_codes", "row_scales", "row_t"):
         assert_bytes_equal(host(kb[key])[: off[-1]], host(got[key])[: off[-1]], f"K-block receive {key}")
+
+
+def _check_mxfp4(got, want, off, h, exact=True):
+    assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "mxfp4 rowwise codes")
+    assert_bytes_equal(host(got["row_scales"])[:off], want["row_scales"][:off], "mxfp4 rowwise scales")
+    n = h * off
+    gc, gs = host(got["col_codes"])[: n // 2], host(got["col_scales"])[: n // 32]
+    if exact:
+        assert_bytes_equal(gs, want["col_scales"][: n // 32], "mxfp4 columnwise scales")
+        assert_bytes_equal(gc, want["col_codes"][: n // 2], "mxfp4 columnwise codes")
+    else:
+        tolerant_codes(F.unpack_nibbles(gc), F.unpack_nibbles(want["col_codes"][: n // 2]), gs,
+                       want["col_scales"][: n // 32], "mxfp4 columnwise", block=32)
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=51, tokens=150, hidden=256, E=5, k=2, A=32, unused=0.05, empty=[3]),
+    dict(seed=52, tokens=600, hidden=192, E=8, k=2, A=128, unused=0.0, empty=[]),     # a 64-column last tile
+    dict(seed=53, tokens=333, hidden=64, E=3, k=1, A=64, unused=0.2, empty=[]),
+    dict(seed=54, tokens=257, hidden=512, E=16, k=8, A=32, unused=0.0, empty=[0, 15]),
+    dict(seed=55, tokens=700, hidden=4096, E=3, k=1, A=32, unused=0.0, empty=[]),     # experts of > 256 rows
+    dict(seed=56, tokens=1000, hidden=128, E=1024, k=1, A=32, unused=0.0, empty=[]),  # the maximum expert count
+])
+def test_mxfp4_receive_bit_exact(dev, case):
+    """The MXFP4 receive (rowwise re-quantization and RHT columnwise operand) equals
+    the oracle byte for byte."""
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
+    h = case["hidden"]
+    print(f"mxfp4 receive case {case}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    got = mtb.ep_mxfp4_direct_receive(packed, h, plan)
+    want = omx4.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment)
+    _check_mxfp4(got, want, int(host(plan["offsets"])[-1]), h)
+
+
+def test_mxfp4_receive_edge_rows(dev):
+    """Zero, -0, subnormal, tiny-t (the two-step decode), huge-t, outlier and
+    exact-tie rows routed among ordinary rows: byte for byte as well."""
+    rng = np.random.default_rng(57)
+    h = 256
+    edge = _edge_rows(h, rng)
+    x = np.concatenate([rng.standard_normal((70, h)) * 10.0 ** rng.uniform(-1, 1, (70, 1)), edge, edge, edge])
+    x = x[rng.permutation(len(x))]
+    bits = _bits(x)
+    topk = np.argsort(-rng.standard_normal((len(x), 4)), axis=1)[:, :2].astype(np.int32)
+    print("mxfp4 receive edge rows", bits.shape, flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), 4, 32)
+    got = mtb.ep_mxfp4_direct_receive(packed, h, plan)
+    want = omx4.direct_receive(onv.pack_rows(bits), h, topk, 4, 32)
+    _check_mxfp4(got, want, int(host(plan["offsets"])[-1]), h)
 
 
 def test_mxfp8_receive_bit_exact(dev):
