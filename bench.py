@@ -49,6 +49,7 @@ CALL_SOURCES = {
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
     "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
     "nvfp4_direct_receive_kblock": ("receive.hip",), "dswiglu_nvfp4_quant_nodx": ("dswiglu.hip",),
+    "mxfp4_receive": ("receive.hip",),
 }
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
@@ -63,6 +64,7 @@ CALL_KERNELS = {
     "nvfp4_columnwise_grouped": ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"],
     "nvfp4_direct_receive_kblock": ["k_nvfp4_receive (K-blocked columnwise layout)"],
     "dswiglu_nvfp4_quant_nodx": ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce", "k_fc1_quant (recompute)"],
+    "mxfp4_receive": ["k_mxfp4_receive"],
 }
 # the combine-backward SR pack: one Philox4x32-10 word per element at counter
 # row*hidden + col (element mode), carry-form decision (the hardware converter)
@@ -85,7 +87,7 @@ def parse():
                         "reference for memory counters) --steps times, eagerly, and print what ran")
     p.add_argument("--workload", default="dispatch",
                    choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k",
-                            "cfg5r"],
+                            "cfg5r", "cfg2m", "cfg3m"],
                    help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
                         "configuration's own path, for per-kernel figures")
     return p.parse_args()
@@ -258,7 +260,8 @@ class ConfigStep:
         import workloads
         self.m = m
         fused, kblock, recompute = which.endswith("f"), which.endswith("k"), which.endswith("r")
-        n = int(which[3:-1] if fused or kblock or recompute else which[3:])
+        mxfp4 = which.endswith("m")
+        n = int(which[3:-1] if fused or kblock or recompute or mxfp4 else which[3:])
         w = workloads.CONFIGS[n]()
         self.w, self.n = w, n
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -309,6 +312,19 @@ class ConfigStep:
         b = algorithmic_bytes(T, H, k, E, r_cap, R, R, 0)
         self._add("route_plan", lambda: m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws,
                                                         out=self.plan), b["route_plan"])
+        if mxfp4:
+            # the MXFP4 receive of the same packed rows (alignment 32: 32-row columnwise blocks)
+            A32 = max(A, 32)
+            r_cap32 = m.ep_route_capacity(T, k, E, A32)
+            self.plan32 = m.ep_route_plan(self.topk, E, A32)
+            self.mx4 = dict(row_codes=torch.empty((r_cap32, H // 2), **u8), row_scales=torch.empty((r_cap32, H // 32), **u8),
+                            col_codes=torch.empty(r_cap32 * H // 2, **u8), col_scales=torch.empty(r_cap32 * H // 32, **u8))
+            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(self.x, out=self.packed), b["nvfp4_pack"])
+            self._add("mxfp4_receive", lambda: m.ep_mxfp4_direct_receive(self.packed, H, self.plan32, out=self.mx4),
+                      T * row_bytes(H) + r_cap32 * 4 + (E + 1) * 4 + 2 * R * (H // 2 + H // 32))
+            self.desc = dict(workload=w.name + " (MXFP4 receive, alignment 32)", tokens=T, hidden=H, experts=E,
+                             top_k=k, alignment=A32)
+            return
         if fused:
             # sender-side fused dispatch: pack straight into the grouped rows, then
             # the columnwise operand from those contiguous rows
