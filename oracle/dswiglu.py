@@ -14,6 +14,7 @@ import numpy as np
 
 from . import formats as F
 from .receive import columnwise_operand, quantize_blocks
+from .philox import sr_word
 from .rht import rht16
 from .nvfp4 import TOKEN_SCALE_BOUND
 
@@ -64,14 +65,16 @@ def expert_amax(dx_bits, counts):
     return out
 
 
-def rowwise_quant(dx_bits, counts, amax):
+def rowwise_quant(dx_bits, counts, amax, sr=None):
     """R19: per-expert rowwise NVFP4 operand of the FC1 gradient.
 
     D_row,e = fl32(amax_e / 2688).  Per 16-element block of a row of expert e:
     s_b = E4M3(fl32(fl32(a_b / 6) / D_row,e)); c = fl32(s_b * D_row,e);
     v = fl32(|x| / c); index = E2M1 rounding (R2).  D = 0 or s_b = 0 gives
-    index 0.  Returns (codes uint8 [T, F] packed, scale codes [T, 2F/16],
-    D_row float32 [E]).
+    index 0.  With ``sr`` = (seed, counter_base) the index is the carry-form
+    stochastic rounding of v (R24): element (row, col) at stream position
+    counter_base + row * 2F + col, its index in the [T, 2F] code array.
+    Returns (codes uint8 [T, F] packed, scale codes [T, 2F/16], D_row float32 [E]).
     """
     x = F.bf16_to_f32(dx_bits)
     t, h = x.shape
@@ -84,13 +87,18 @@ def rowwise_quant(dx_bits, counts, amax):
         if r1 == r0:
             continue
         blk = x[r0:r1].reshape(r1 - r0, h // 16, 16)
-        c, s = quantize_blocks(blk, D[e], "fp32")
+        words = None
+        if sr is not None:
+            pos = np.uint64(sr[1]) + (np.arange(r0, r1, dtype=np.uint64)[:, None] * np.uint64(h)
+                                      + np.arange(h, dtype=np.uint64)[None, :])
+            words = sr_word(pos.reshape(r1 - r0, h // 16, 16), sr[0])
+        c, s = quantize_blocks(blk, D[e], "fp32", words)
         codes[r0:r1] = c.reshape(r1 - r0, h)
         scales[r0:r1] = s
     return F.pack_nibbles(codes), scales, D
 
 
-def columnwise_quant(dx_bits, counts, amax, exact_amax=False):
+def columnwise_quant(dx_bits, counts, amax, exact_amax=False, sr=None):
     """R20 (and R21 with ``exact_amax``): per-expert RHT columnwise operand.
 
     D_col,e = fl32(4 * amax_e / 2688) -- the bound from P4 -- or, for the
@@ -98,7 +106,9 @@ def columnwise_quant(dx_bits, counts, amax, exact_amax=False):
     max |y| over the expert's post-RHT values.  Rows are zero-padded to
     P_e = roundup(count_e, 16).  Expert e's codes form an [2F, P_e/2] matrix
     at byte 2F * off_e / 2 and its scales an [2F, P_e/16] matrix at byte
-    2F * off_e / 16, with off_e the padded offsets.
+    2F * off_e / 16, with off_e the padded offsets.  With ``sr`` = (seed,
+    counter_base), stochastic codes (R24): expert e's element (h, r) at stream
+    position counter_base + 2F * off_e + h * P_e + r, its index in the codes.
     """
     x = F.bf16_to_f32(dx_bits).astype(np.float64)
     t, h = x.shape
@@ -118,14 +128,19 @@ def columnwise_quant(dx_bits, counts, amax, exact_amax=False):
             D[e] = np.float32(amax_post) / np.float32(TOKEN_SCALE_BOUND)
         else:
             D[e] = (np.float32(4.0) * np.float32(amax[e])) / np.float32(TOKEN_SCALE_BOUND)
-        cc, cs = columnwise_operand(x[off[e] : off[e + 1]], c, D[e], "fp32")
+        cc, cs = columnwise_operand(x[off[e] : off[e + 1]], c, D[e], "fp32",
+                                    sr=None if sr is None else (sr[0], sr[1] + h * int(poff[e])))
         codes[h * poff[e] // 2 : h * poff[e + 1] // 2] = cc.reshape(-1)
         scales[h * poff[e] // 16 : h * poff[e + 1] // 16] = cs.reshape(-1)
     return codes, scales, D
 
 
-def fc1_grad_quant(dx_bits, counts, amax):
-    """The fused path after the epilogue: rowwise (R19) and columnwise (R20) operands."""
-    rc, rs, drow = rowwise_quant(dx_bits, counts, amax)
-    cc, cs, dcol = columnwise_quant(dx_bits, counts, amax)
+def fc1_grad_quant(dx_bits, counts, amax, sr=None):
+    """The fused path after the epilogue: rowwise (R19) and columnwise (R20) operands;
+    ``sr`` = (seed, counter_base) makes both stochastic (R24), the columnwise
+    operand's positions following the rowwise operand's T * 2F."""
+    t, h = np.asarray(dx_bits).shape
+    rc, rs, drow = rowwise_quant(dx_bits, counts, amax, sr)
+    cc, cs, dcol = columnwise_quant(dx_bits, counts, amax,
+                                    sr=None if sr is None else (sr[0], sr[1] + t * h))
     return dict(row_codes=rc, row_scales=rs, row_scale=drow, col_codes=cc, col_scales=cs, col_scale=dcol)

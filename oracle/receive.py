@@ -21,12 +21,13 @@ import numpy as np
 
 from . import formats as F
 from . import nvfp4
+from .philox import sr_word
 from .rht import rht16
 from .routing import route_plan
 
 
 # ------------------------------------------------------------------ shared columnwise quantizer
-def quantize_blocks(y, D, mode):
+def quantize_blocks(y, D, mode, words=None):
     """Quantize post-RHT blocks y [..., 16] (float32) with global decode scale D.
 
     a = max |y_i| over the block; s = E4M3(fl32(fl32(a / 6) / D)).
@@ -34,6 +35,9 @@ def quantize_blocks(y, D, mode):
         v = fl32(|y| / (s * D)), the exact quotient rounded once to float32.
     mode "fp32" (R19/R20; D any float32): c = fl32(s * D), v = fl32(|y| / c).
     D = 0, or s = 0, gives magnitude index 0.  The code's sign is y's sign bit.
+    ``words`` (R24): 32-bit random words, one per element (y's shape); the
+    index is then the carry-form stochastic rounding of v (R8b) instead of R2.
+    The scales are the same either way.
     Returns (codes uint8 [..., 16], scale codes uint8 [...]).
     """
     y = np.asarray(y, dtype=np.float32)
@@ -57,18 +61,24 @@ def quantize_blocks(y, D, mode):
         else:
             raise ValueError(mode)
     v = np.where(ok, v, np.float32(0.0))
-    idx = F.e2m1_index(v.astype(np.float64))
+    if words is None:
+        idx = F.e2m1_index(v.astype(np.float64))
+    else:
+        idx = nvfp4.stochastic_e2m1_index_carry(v.astype(np.float64), np.asarray(words).reshape(v.shape))
     sign = (y.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
     return (sign << np.uint8(3)) | idx, s_code
 
 
-def columnwise_operand(values, count, D, mode, padded_rows=None):
+def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None):
     """One expert's columnwise operand from its grouped rows.
 
     values [count, H]: exact values of the expert's rows (float64), in grouped
     order; rows count..P-1 are zero padding, P = padded_rows (default
     roundup(count, 16)).  Padding rows are transformed and quantized like any
     other rows (their codes carry the sign bits of the signed-zero results).
+    ``sr`` = (seed, n0): stochastic codes (R24); the element of column h and
+    grouped row r (0-based in the expert) has stream position n0 + h * P + r,
+    its index in the expert's [H, P] code matrix plus n0.
     Returns (codes uint8 [H, P/2], scale codes uint8 [H, P/16]).
     """
     values = np.asarray(values, dtype=np.float64)
@@ -78,7 +88,11 @@ def columnwise_operand(values, count, D, mode, padded_rows=None):
     full[:count] = values[:count]
     blocks = full.T.reshape(h, p // 16, 16)             # [H, P/16, 16] : column h, block m, row i
     y = rht16(blocks)
-    codes, s_code = quantize_blocks(y, D, mode)
+    words = None
+    if sr is not None:
+        seed, n0 = sr
+        words = sr_word(np.uint64(n0) + np.arange(h * p, dtype=np.uint64).reshape(h, p // 16, 16), seed)
+    codes, s_code = quantize_blocks(y, D, mode, words)
     return F.pack_nibbles(codes.reshape(h, p)), s_code
 
 
@@ -89,8 +103,11 @@ def expert_decode_scale(t_rows):
 
 
 # ------------------------------------------------------------------ the direct receive
-def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None, columnwise=True):
-    """R12-R16.  Returns the routing plan plus the grouped operands.
+def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None, columnwise=True, sr=None):
+    """R12-R16 (and R24 with ``sr`` = (seed, counter_base): stochastic columnwise
+    codes, expert e's element (h, r) at stream position counter_base +
+    H * off_e + h * P_e + r -- the code's index in ``col_codes``, two per byte).
+    Returns the routing plan plus the grouped operands.
 
     Rowwise (R13): grouped row g with source token s >= 0 holds the sender's
     code bytes, scale bytes and t unchanged; padding rows are zero bytes
@@ -130,7 +147,8 @@ def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None,
         if c == 0:
             continue
         p = int(off[e + 1] - off[e])                    # P_e: all padded rows of the slot
-        cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2", padded_rows=p)
+        cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2", padded_rows=p,
+                                    sr=None if sr is None else (sr[0], sr[1] + h * int(off[e])))
         col_codes[h * off[e] // 2 : h * off[e + 1] // 2] = cc.reshape(-1)
         col_scales[h * off[e] // 16 : h * off[e + 1] // 16] = cs.reshape(-1)
     out.update(col_codes=col_codes, col_scales=col_scales, col_scale=D)
