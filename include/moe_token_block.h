@@ -217,6 +217,23 @@ int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t tokens, in
                                        uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
                                        void* stream);
 
+/* ep_nvfp4_direct_receive_scaled with stochastic columnwise codes (for a
+ * gradient operand; TE's NVFP4 recipe, which P1's PR description follows,
+ * rounds gradients stochastically).  Same scales; each columnwise code is the
+ * carry-form stochastic rounding (see ep_nvfp4_pack, SR_ELEMENT_CARRY) of the
+ * same quotient, with word 0 of Philox4x32-10 (key = seed) at counter n =
+ * counter_base + the code's index in col_codes (two codes per byte, low nibble
+ * first), i.e. counter_base + hidden*off_e + h*P_e + (g - off_e) for column h
+ * and grouped row g of expert e.  The rowwise operand is the sender's bytes,
+ * as in the deterministic receive.  sr_state: DEVICE pointer to {seed,
+ * counter_base} (two uint64). */
+int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                   int64_t num_experts, int64_t r_cap,
+                                   const int32_t* offsets, const int32_t* src_row,
+                                   uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                   uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
+                                   const uint64_t* sr_state, void* stream);
+
 /* The direct receive with the columnwise operand in K-blocks, a layout a
  * grouped GEMM can stream (P1, PR description: the receiver builds the expert
  * GEMM's grouped operand): per expert, the grouped rows are cut into blocks
@@ -331,6 +348,21 @@ int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t 
                             uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
                             uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* dswiglu_nvfp4_quant with stochastic FC1-gradient codes: the same scales, each
+ * rowwise and columnwise code the carry-form stochastic rounding of the same
+ * quotient with word 0 of Philox4x32-10 (key = seed) at counter n: rowwise
+ * element (row, col) n = counter_base + row*2*ffn + col; columnwise code n =
+ * counter_base + tokens*2*ffn + its index in col_codes (two per byte, low
+ * nibble first), i.e. + 2*ffn*poff_e + h*P_e + (g - poff_e).  sr_state:
+ * DEVICE pointer to {seed, counter_base} (two uint64); other arguments as in
+ * dswiglu_nvfp4_quant (dx may be NULL). */
+int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                               const int32_t* counts, int64_t num_experts,
+                               uint16_t* dx, float* amax,
+                               uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                               uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                               void* workspace, size_t workspace_bytes, const uint64_t* sr_state, void* stream);
 
 #ifdef __cplusplus
 }

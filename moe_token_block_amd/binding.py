@@ -47,9 +47,11 @@ _SIGS = {
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_nvfp4_direct_receive_sr": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dswiglu_nvfp4_quant_sr": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -348,6 +350,21 @@ def ep_nvfp4_direct_receive_scaled(packed, hidden, plan, out):
     return out
 
 
+def ep_nvfp4_direct_receive_sr(packed, hidden, plan, out, sr_state):
+    """The one-pass receive with stochastic columnwise codes; out["col_scale"] must
+    hold D_e (ep_nvfp4_expert_scale); sr_state: device int64 [seed, counter_base]."""
+    dev = _dev(packed)
+    _need(packed, torch.uint8, "packed", dev)
+    _need(sr_state, torch.int64, "sr_state", dev)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_direct_receive_sr(
+            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _ptr(sr_state), _stream(dev)),
+            "ep_nvfp4_direct_receive_sr")
+    return out
+
+
 def ep_mxfp8_direct_receive(data, scales, plan, out=None):
     dev = _dev(data)
     _need(data, torch.uint8, "data", dev)
@@ -363,11 +380,12 @@ def ep_mxfp8_direct_receive(data, scales, plan, out=None):
 
 
 # ------------------------------------------------------------------ dSwiGLU
-def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True):
+def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None):
     """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
     ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors.
     ``materialize_dx=False``: no BF16 dX is written (out["dx"] is None); the
-    quantizer recomputes dX from preact and dy."""
+    quantizer recomputes dX from preact and dy.  ``sr_state`` (device int64
+    [seed, counter_base]): stochastic FC1-gradient codes."""
     dev = _dev(preact)
     _need(preact, torch.bfloat16, "preact", dev)
     _need(dy, torch.bfloat16, "dy", dev)
@@ -387,9 +405,13 @@ def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materializ
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        _check(lib().dswiglu_nvfp4_quant(
-            _ptr(preact), _ptr(dy), t, f, _ptr(counts), e, _ptr(out["dx"]), _ptr(out["amax"]),
-            _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
-            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]),
-            _ptr(workspace), workspace.numel(), _stream(dev)), "dswiglu_nvfp4_quant")
+        args = (_ptr(preact), _ptr(dy), t, f, _ptr(counts), e, _ptr(out["dx"]), _ptr(out["amax"]),
+                _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
+                _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]),
+                _ptr(workspace), workspace.numel())
+        if sr_state is not None:
+            _need(sr_state, torch.int64, "sr_state", dev)
+            _check(lib().dswiglu_nvfp4_quant_sr(*args, _ptr(sr_state), _stream(dev)), "dswiglu_nvfp4_quant_sr")
+            return out
+        _check(lib().dswiglu_nvfp4_quant(*args, _stream(dev)), "dswiglu_nvfp4_quant")
     return out

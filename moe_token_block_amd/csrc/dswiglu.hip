@@ -325,9 +325,13 @@ __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (
 // block; lane cg ^ 1 holds the other half): the pair's block max by a lane
 // swap, the E4M3 scale from D_row, the codes of the 8 values.  Rows at or
 // past nreal are not stored (every lane still takes part in the swap).
+// SR: stochastic codes, element (row0 + i, xcol + k) at stream position
+// n0 + i * W + k (n0 = the counter base + row0 * W + xcol: its index in the
+// [T, W] code array).
+template <bool SR = false>
 __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, float Drow, const MantEntry* tab,
                                             uint8_t* cbase, uint32_t coff, uint8_t* sbase, uint32_t soff, uint32_t W,
-                                            bool even) {
+                                            bool even, uint64_t n0 = 0, uint32_t klo = 0, uint32_t khi = 0) {
   const DScale dsr = dscale(Drow);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -337,10 +341,22 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
     if (i >= nreal) continue;
     uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
     GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, tab);
-    uint32_t w = enc_first(bf16lo(v[i].x), bf16hi(v[i].x), gb);
-    w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
-    w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
-    w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
+    uint32_t w;
+    if (!SR) {
+      w = enc_first(bf16lo(v[i].x), bf16hi(v[i].x), gb);
+      w = enc_pair<1>(w, bf16lo(v[i].y), bf16hi(v[i].y), gb);
+      w = enc_pair<2>(w, bf16lo(v[i].z), bf16hi(v[i].z), gb);
+      w = enc_pair<3>(w, bf16lo(v[i].w), bf16hi(v[i].w), gb);
+    } else {
+      const uint32_t wv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      float u[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[2 * k] = quot_apply(bf16lo(wv[k]), gb.r_hi, gb.r_lo);
+        u[2 * k + 1] = quot_apply(bf16hi(wv[k]), gb.r_hi, gb.r_lo);
+      }
+      w = sr_codes8(u, n0 + (uint64_t)i * W, klo, khi, gb.scale);
+    }
     *reinterpret_cast<uint32_t*>(cbase + (coff + (uint32_t)i * (W >> 1))) = w;
     if (even) sbase[soff + (uint32_t)i * (W >> 4)] = (uint8_t)sc;
   }
@@ -350,9 +366,13 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
 // rows (one block per column): 4x the RHT down each column (signs folded into the butterfly's
 // adds), the E4M3 scale from D_col, the 16 codes; codes and scales go to the
 // LDS stage at (column cg*8 + k, block m).
-template <int P0, int P1, typename ScT>
+// SR: stochastic codes, the block's row 0 in the thread's column k at stream
+// position n0 + k * n_step (its index in the columnwise code array plus the
+// counter base).
+template <int P0, int P1, bool SR = false, typename ScT>
 __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol, const MantEntry* tab, int cg, int m,
-                                               uint2* stage_codes, ScT* stage_sc) {
+                                               uint2* stage_codes, ScT* stage_sc, uint64_t n0 = 0,
+                                               uint64_t n_step = 0, uint32_t klo = 0, uint32_t khi = 0) {
   const DScale dsc = dscale(Dcol);
 #pragma unroll
   for (int p = P0; p < P1; ++p) {
@@ -379,22 +399,37 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
     // the values are 4x the transform: divide by 4 more
     g0.scale *= 4.0f;
     g1.scale *= 4.0f;
-    uint32_t c00 = enc_first(z0[0], z0[1], g0);
-    c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
-    c00 = enc_pair<2>(c00, z0[4], z0[5], g0);
-    c00 = enc_pair<3>(c00, z0[6], z0[7], g0);
-    uint32_t c01 = enc_first(z0[8], z0[9], g0);
-    c01 = enc_pair<1>(c01, z0[10], z0[11], g0);
-    c01 = enc_pair<2>(c01, z0[12], z0[13], g0);
-    c01 = enc_pair<3>(c01, z0[14], z0[15], g0);
-    uint32_t c10 = enc_first(z1[0], z1[1], g1);
-    c10 = enc_pair<1>(c10, z1[2], z1[3], g1);
-    c10 = enc_pair<2>(c10, z1[4], z1[5], g1);
-    c10 = enc_pair<3>(c10, z1[6], z1[7], g1);
-    uint32_t c11 = enc_first(z1[8], z1[9], g1);
-    c11 = enc_pair<1>(c11, z1[10], z1[11], g1);
-    c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
-    c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
+    uint32_t c00, c01, c10, c11;
+    if (!SR) {
+      c00 = enc_first(z0[0], z0[1], g0);
+      c00 = enc_pair<1>(c00, z0[2], z0[3], g0);
+      c00 = enc_pair<2>(c00, z0[4], z0[5], g0);
+      c00 = enc_pair<3>(c00, z0[6], z0[7], g0);
+      c01 = enc_first(z0[8], z0[9], g0);
+      c01 = enc_pair<1>(c01, z0[10], z0[11], g0);
+      c01 = enc_pair<2>(c01, z0[12], z0[13], g0);
+      c01 = enc_pair<3>(c01, z0[14], z0[15], g0);
+      c10 = enc_first(z1[0], z1[1], g1);
+      c10 = enc_pair<1>(c10, z1[2], z1[3], g1);
+      c10 = enc_pair<2>(c10, z1[4], z1[5], g1);
+      c10 = enc_pair<3>(c10, z1[6], z1[7], g1);
+      c11 = enc_first(z1[8], z1[9], g1);
+      c11 = enc_pair<1>(c11, z1[10], z1[11], g1);
+      c11 = enc_pair<2>(c11, z1[12], z1[13], g1);
+      c11 = enc_pair<3>(c11, z1[14], z1[15], g1);
+    } else {
+      float u0[16], u1[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        u0[i] = quot_apply(z0[i], g0.r_hi, g0.r_lo);
+        u1[i] = quot_apply(z1[i], g1.r_hi, g1.r_lo);
+      }
+      const uint64_t na = n0 + (uint64_t)(2 * p) * n_step, nb = na + n_step;
+      c00 = sr_codes8(u0, na, klo, khi, g0.scale);
+      c01 = sr_codes8(u0 + 8, na + 8, klo, khi, g0.scale);
+      c10 = sr_codes8(u1, nb, klo, khi, g1.scale);
+      c11 = sr_codes8(u1 + 8, nb + 8, klo, khi, g1.scale);
+    }
     const int c0 = cg * 8 + 2 * p;
     stage_codes[qstage_at(c0, m)] = make_uint2(c00, c01);
     stage_codes[qstage_at(c0 + 1, m)] = make_uint2(c10, c11);
@@ -416,7 +451,9 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
 // recomputes its 8 columns of dX from preact and dy with the epilogue's own
 // arithmetic (so the values, and the amax already taken from them, agree bit
 // for bit).
-template <bool RECOMPUTE>
+// SR: stochastic codes (rowwise at counter base + row * W + col, columnwise at
+// counter base + T * W + the code's index in the columnwise code array).
+template <bool RECOMPUTE, bool SR = false>
 __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
                                                    const uint16_t* __restrict__ dy, int T, int W /* 2F */, int E,
                                                    int n_ct, const int32_t* __restrict__ offs,
@@ -424,7 +461,8 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
                                                    const float* __restrict__ row_scale,
                                                    const float* __restrict__ col_scale,
                                                    uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-                                                   uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales) {
+                                                   uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
+                                                   const uint64_t* __restrict__ sr_state) {
   __shared__ uint2 stage_codes[kQTileCols * kQBlocks > 1025 ? kQTileCols * kQBlocks : 1025];  // offsets, padded offsets first
   __shared__ uint32_t stage_sc[kQTileCols * kQBlocks];
   __shared__ MantEntry s_tab[kQBlocks][2][8];            // [block][row / col][significand of s]
@@ -543,7 +581,25 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
 
   // columnwise first: its transposed copy-out stores then drain while the
   // rowwise operand is computed (rowwise first leaves them as a final burst)
-  if (live) fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
+  uint32_t klo = 0, khi = 0;
+  uint64_t n_base = 0;
+  if (SR) {
+    const uint64_t seed = sr_state[0];
+    klo = (uint32_t)seed;
+    khi = (uint32_t)(seed >> 32);
+    n_base = sr_state[1];
+  }
+  if (live) {
+    if (!SR) {
+      fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
+    } else {
+      // the thread's 8 columns are contiguous in dX (also in the recompute mapping)
+      const uint64_t h0 = (uint64_t)qtile_col<RECOMPUTE>(col0, 8 * cg, W);
+      const uint64_t n0 = n_base + (uint64_t)(uint32_t)T * (uint32_t)W + 2 * (s_cbase[m] + h0 * s_cstr[m]);
+      fc1_columnwise<0, 4, true>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc, n0,
+                                 2 * (uint64_t)s_cstr[m], klo, khi);
+    }
+  }
   __syncthreads();
   // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...
   const int b = tid % kQBlocks;
@@ -574,9 +630,10 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
   if (live) {
     const uint32_t rrel = (uint32_t)s_row0[m] - rbase;
     const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
-    fc1_rowwise(v, s_nreal[m], s_drow[m], s_tab[m][0], row_codes + (size_t)rbase * (uint32_t)(W >> 1),
-                rrel * (uint32_t)(W >> 1) + (uint32_t)(xcol >> 1), row_scales + (size_t)rbase * (uint32_t)(W >> 4),
-                rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4), (uint32_t)W, (cg & 1) == 0);
+    fc1_rowwise<SR>(v, s_nreal[m], s_drow[m], s_tab[m][0], row_codes + (size_t)rbase * (uint32_t)(W >> 1),
+                    rrel * (uint32_t)(W >> 1) + (uint32_t)(xcol >> 1), row_scales + (size_t)rbase * (uint32_t)(W >> 4),
+                    rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4), (uint32_t)W, (cg & 1) == 0,
+                    n_base + (uint64_t)(uint32_t)s_row0[m] * (uint32_t)W + (uint32_t)xcol, klo, khi);
   }
 }
 
@@ -594,11 +651,12 @@ MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts) {
   return rowmax_bytes(tokens) + (size_t)(2 * (num_experts + 1) * sizeof(int32_t));
 }
 
-MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+static int32_t dswiglu_quant_impl(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
                                        const int32_t* counts, int64_t num_experts, uint16_t* dx, float* amax,
                                        uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
                                        uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* workspace, size_t workspace_bytes,
+                                       const uint64_t* sr_state, void* stream) {
   if (tokens < 0 || ffn <= 0 || ffn % 64 != 0 || num_experts < 1 || num_experts > 1024) return EP_ERR_SHAPE;
   if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
@@ -622,11 +680,38 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
   const int64_t prow_bound = tokens + 15 * num_experts;
   const int64_t n_rt = (prow_bound + kQTileRows - 1) / kQTileRows, n_ct = (2 * F + kQTileCols - 1) / kQTileCols;
   if (n_rt * n_ct * kQThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
-  if (dx)
-    hipLaunchKernelGGL(k_fc1_quant<false>, dim3((unsigned)(n_rt * n_ct)), dim3(kQThreads), 0, s, dx, preact, dy, T, 2 * F, E,
-                       (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
+  const dim3 grid((unsigned)(n_rt * n_ct)), block(kQThreads);
+  if (dx && !sr_state)
+    hipLaunchKernelGGL((k_fc1_quant<false, false>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
+                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
+  else if (!sr_state)
+    hipLaunchKernelGGL((k_fc1_quant<true, false>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
+                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
+  else if (dx)
+    hipLaunchKernelGGL((k_fc1_quant<false, true>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
+                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
   else
-    hipLaunchKernelGGL(k_fc1_quant<true>, dim3((unsigned)(n_rt * n_ct)), dim3(kQThreads), 0, s, dx, preact, dy, T, 2 * F, E,
-                       (int)n_ct, offs, poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales);
+    hipLaunchKernelGGL((k_fc1_quant<true, true>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
+                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
   return launch_status();
+}
+
+MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                                       const int32_t* counts, int64_t num_experts, uint16_t* dx, float* amax,
+                                       uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                       uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
+                            col_codes, col_scales, col_scale, workspace, workspace_bytes, nullptr, stream);
+}
+
+MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                                          const int32_t* counts, int64_t num_experts, uint16_t* dx, float* amax,
+                                          uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                          uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                          void* workspace, size_t workspace_bytes, const uint64_t* sr_state,
+                                          void* stream) {
+  if (!sr_state) return EP_ERR_NULL;
+  return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
+                            col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, stream);
 }

@@ -218,10 +218,23 @@ __device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* c
 // column, a permutation inside one 128-byte row.
 __device__ __forceinline__ int stage_at(int c, int b) { return c * kBlocks + (b ^ ((c >> 3) & (kBlocks - 1))); }
 
-template <int SEL, bool SLOW>
+// Stochastic variant of col_encode: the same quotients, each code drawn by the
+// carry-form converter with the Philox word of its stream position n0 + i.
+__device__ __forceinline__ void col_encode_sr(const float* y, const ColQuant& q, uint64_t n0, uint32_t klo,
+                                              uint32_t khi, uint32_t& w0, uint32_t& w1) {
+  float u[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = quot_apply(y[i], q.r_hi, q.r_lo);
+  w0 = sr_codes8(u, n0, klo, khi, q.scale);
+  w1 = sr_codes8(u + 8, n0 + 8, klo, khi, q.scale);
+}
+
+// SR: the stream position of the block's row 0 in column c is n_col + c * n_step
+// (the code's index in the columnwise code array plus the counter base).
+template <int SEL, bool SLOW, bool SR>
 __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm, const int* ce, int dexp,
                                             const RcpEntry* tab, uint2* stage_codes, uint32_t* stage_sc, int col0,
-                                            int m) {
+                                            int m, uint64_t n_col, uint64_t n_step, uint32_t klo, uint32_t khi) {
   float z0[16], z1[16];
   decode_stage1<SEL, SLOW>(cw, cm, ce, z0, z1);
   rht16_upper(z0);
@@ -229,8 +242,14 @@ __device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm,
   ColQuant q0 = col_block_quant(absmax16(z0), dexp, tab);
   ColQuant q1 = col_block_quant(absmax16(z1), dexp, tab);
   uint32_t a0, a1, b0, b1;
-  col_encode(z0, q0, a0, a1);
-  col_encode(z1, q1, b0, b1);
+  if (!SR) {
+    col_encode(z0, q0, a0, a1);
+    col_encode(z1, q1, b0, b1);
+  } else {
+    const uint64_t n0 = n_col + (uint64_t)(col0 + 2 * SEL) * n_step;
+    col_encode_sr(z0, q0, n0, klo, khi, a0, a1);
+    col_encode_sr(z1, q1, n0 + n_step, klo, khi, b0, b1);
+  }
   const int c0 = col0 + 2 * SEL, c1 = c0 + 1;
   stage_codes[stage_at(c0, m)] = make_uint2(a0, a1);
   stage_codes[stage_at(c1, m)] = make_uint2(b0, b1);
@@ -260,14 +279,18 @@ struct RowSrc {
 // an [H, len/2] code matrix at byte H*off_e/2 + 128*H*kb (scales [H, len/16]
 // at H*off_e/16 + 16*H*kb).  Tiles then follow the K-blocks (never straddling
 // experts), so a tile's columnwise output is one contiguous region.
-template <bool GROUPED, bool KBLOCK>
+// SR (the compact layout only): stochastic columnwise codes, the code of
+// column h and grouped row g of expert e at stream position counter_base +
+// H*off_e + h*P_e + (g - off_e) -- its index in col_codes, two per byte.
+template <bool GROUPED, bool KBLOCK, bool SR = false>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
                                                        const int32_t* __restrict__ offsets, int E,
                                                        const int32_t* __restrict__ src_row, int r_cap, int n_ct,
                                                        uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
                                                        float* __restrict__ row_t, uint8_t* __restrict__ col_codes,
                                                        uint8_t* __restrict__ col_scales,
-                                                       const float* __restrict__ col_scale) {
+                                                       const float* __restrict__ col_scale,
+                                                       const uint64_t* __restrict__ sr_state) {
   __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block ^ swizzle] 8 code bytes; offsets first
   __shared__ uint32_t stage_sc[kTileCols * kBlocks];   // [column][block ^ swizzle] scale code
   __shared__ RcpEntry s_tab[128];
@@ -447,16 +470,29 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     float cm[16];
     const int sh = 8 * ((cg >> 1) & 3);
     const int dexp = s_dexp[m];
+    uint64_t n_col = 0, n_step = 0;
+    uint32_t klo = 0, khi = 0;
+    if (SR) {
+      const uint64_t seed = sr_state[0];
+      klo = (uint32_t)seed;
+      khi = (uint32_t)(seed >> 32);
+      n_col = sr_state[1] + 2 * (s_cbase[m] + (uint64_t)(uint32_t)col0 * s_cstr[m]);
+      n_step = 2 * (uint64_t)s_cstr[m];
+    }
     if (s_slow[m] == 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
         cm[i] = s * s_tq[r0 + i];  // exact: s has 4 significant bits, t/4 is a power of two
       }
-      column_pair<0, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<1, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<2, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<3, false>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<0, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<1, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<2, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<3, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
     } else {
       int ce[16];
 #pragma unroll
@@ -465,10 +501,14 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
         ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
         cm[i] = t == 0.0f ? 0.0f : e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * rht_in_scale(i);
       }
-      column_pair<0, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<1, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<2, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
-      column_pair<3, true>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m);
+      column_pair<0, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<1, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<2, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
+      column_pair<3, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
+                                   klo, khi);
     }
   }
   __syncthreads();
@@ -817,7 +857,28 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
   hipLaunchKernelGGL((k_nvfp4_receive<false, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
                      (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
-                     row_t, col_codes, col_scales, col_scale);
+                     row_t, col_codes, col_scales, col_scale, nullptr);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                              int64_t num_experts, int64_t r_cap, const int32_t* offsets,
+                                              const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                              float* row_t, uint8_t* col_codes, uint8_t* col_scales,
+                                              const float* col_scale, const uint64_t* sr_state, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale || !sr_state)
+    return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
+  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false, true>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0,
+                     (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
+                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale, sr_state);
   return launch_status();
 }
 
@@ -863,7 +924,7 @@ MTB_EXPORT int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const u
                    (uint32_t)(H / 16), 4u};
   hipLaunchKernelGGL((k_nvfp4_receive<true, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
                      (int)r_cap, H, offsets, (int)num_experts, nullptr, (int)r_cap, (int)n_ct, nullptr, nullptr, nullptr,
-                     col_codes, col_scales, col_scale);
+                     col_codes, col_scales, col_scale, nullptr);
   return launch_status();
 }
 
@@ -884,7 +945,7 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
   hipLaunchKernelGGL((k_nvfp4_receive<false, true>), dim3((unsigned)(n_kb * n_ct)), dim3(kThreads), 0,
                      (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
-                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale);
+                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale, nullptr);
   return launch_status();
 }
 

@@ -92,6 +92,8 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, P, P, P, P, P, P, N, P, N) == -1
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 100, P, 2, P, P, P, P, P, P, P, P, P, 16, N) == -2
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 16, 64, P, P, P, P, P, P, N) == -3   # alignment not a multiple of 32
+    assert lib.ep_nvfp4_direct_receive_sr(P, 4, 128, 2, 64, P, P, P, P, P, P, P, P, N, N) == -1   # sr_state NULL
+    assert lib.dswiglu_nvfp4_quant_sr(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, P, 4096, N, N) == -1
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 48, 64, P, P, P, P, P, P, N) == -3
     assert lib.ep_mxfp4_direct_receive(P, 4, 100, 2, 32, 64, P, P, P, P, P, P, N) == -2   # hidden not a multiple of 64
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 32, 64, P, P, P, P, N, P, N) == -1   # col_codes NULL

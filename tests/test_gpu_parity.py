@@ -343,6 +343,35 @@ def test_mxfp4_receive_edge_rows(dev):
     _check_mxfp4(got, want, int(host(plan["offsets"])[-1]), h)
 
 
+@pytest.mark.parametrize("case", [
+    dict(seed=61, tokens=150, hidden=256, E=5, k=2, A=16, unused=0.05, empty=[3]),
+    dict(seed=62, tokens=600, hidden=192, E=8, k=2, A=128, unused=0.0, empty=[]),
+    dict(seed=63, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),
+])
+def test_direct_receive_sr_bit_exact(dev, case):
+    """Stochastic columnwise codes (R24) equal the oracle's byte for byte; the scales
+    and the rowwise operand equal the deterministic receive's."""
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
+    h = case["hidden"]
+    seed, base = 1234 + case["seed"], (1 << 33) + 5
+    print(f"receive SR case {case}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    ref = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    got = {k: torch.empty_like(v) for k, v in ref.items()}
+    got["col_scale"] = ref["col_scale"].clone()
+    sr = torch.tensor([seed, base], dtype=torch.int64, device=dev)
+    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, sr)
+    want = orecv.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment, sr=(seed, base))
+    off = int(host(plan["offsets"])[-1])
+    n = h * off
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], want["col_codes"][: n // 2], "SR columnwise codes")
+    assert_bytes_equal(host(got["col_scales"])[: n // 16], host(ref["col_scales"])[: n // 16], "SR columnwise scales")
+    for key in ("row_codes", "row_scales"):
+        assert_bytes_equal(host(got[key])[:off], host(ref[key])[:off], f"SR receive {key}")
+
+
 def test_mxfp8_receive_bit_exact(dev):
     w = workloads.small_dispatch(11, 300, 256, 6, 2, alignment=128, unused_frac=0.1)
     data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
@@ -414,6 +443,31 @@ def test_dswiglu_counts_cut_at_tokens(dev, dev_counts, rows):
     m = q["col_codes"].size
     tolerant_codes(F.unpack_nibbles(host(out["col_codes"])[:m]), F.unpack_nibbles(q["col_codes"]),
                    host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "cut columnwise")
+
+
+@pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([300, 0, 129], 256), ([40, 24, 19, 8], 128)])
+def test_dswiglu_sr_bit_exact(dev, counts, ffn):
+    """Stochastic FC1-gradient codes (R24) equal the oracle's on the GPU's own dX and
+    amax byte for byte, with and without a materialized dX; scales as the RNE call's."""
+    w = workloads.small_dswiglu(sum(counts) + 3 * ffn, counts, ffn)
+    print(f"dswiglu SR counts={counts} ffn={ffn}", flush=True)
+    args = (bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    seed, base = 777, (1 << 32) + 3
+    sr = torch.tensor([seed, base], dtype=torch.int64, device=dev)
+    got = mtb.dswiglu_nvfp4_quant(*args, sr_state=sr)
+    got_nodx = mtb.dswiglu_nvfp4_quant(*args, materialize_dx=False, sr_state=sr)
+    ref = mtb.dswiglu_nvfp4_quant(*args)
+    q = odsw.fc1_grad_quant(host(got["dx"]), w.counts, host(got["amax"]), sr=(seed, base))
+    t = sum(counts)
+    n = 2 * ffn * sum((c + 15) // 16 * 16 for c in counts)
+    assert_bytes_equal(host(got["row_codes"]), q["row_codes"], "SR rowwise codes")
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], q["col_codes"], "SR columnwise codes")
+    for key in ("row_scales", "col_scales"):
+        m = n // 16 if key == "col_scales" else None
+        assert_bytes_equal(host(got[key])[:m], host(ref[key])[:m], f"SR {key}")
+    for key in ("row_codes", "row_scales", "col_codes", "col_scales"):
+        m = (n // 2 if key == "col_codes" else n // 16) if key.startswith("col") else None
+        assert_bytes_equal(host(got_nodx[key])[:m], host(got[key])[:m], f"SR recompute {key}")
 
 
 @pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([300, 0, 129], 256), ([40, 24, 19, 8], 128)])
