@@ -49,7 +49,8 @@ CALL_SOURCES = {
     "dswiglu_nvfp4_quant": ("dswiglu.hip",),
     "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
     "nvfp4_direct_receive_kblock": ("receive.hip",), "dswiglu_nvfp4_quant_nodx": ("dswiglu.hip",),
-    "mxfp4_receive": ("receive.hip",),
+    "mxfp4_receive": ("receive.hip",), "nvfp4_direct_receive_sr": ("receive.hip",),
+    "dswiglu_nvfp4_quant_sr": ("dswiglu.hip",),
 }
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
@@ -65,6 +66,8 @@ CALL_KERNELS = {
     "nvfp4_direct_receive_kblock": ["k_nvfp4_receive (K-blocked columnwise layout)"],
     "dswiglu_nvfp4_quant_nodx": ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce", "k_fc1_quant (recompute)"],
     "mxfp4_receive": ["k_mxfp4_receive"],
+    "nvfp4_direct_receive_sr": ["k_nvfp4_receive (stochastic columnwise codes)"],
+    "dswiglu_nvfp4_quant_sr": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant (stochastic codes)"],
 }
 # the combine-backward SR pack: one Philox4x32-10 word per element at counter
 # row*hidden + col (element mode), carry-form decision (the hardware converter)
@@ -87,7 +90,7 @@ def parse():
                         "reference for memory counters) --steps times, eagerly, and print what ran")
     p.add_argument("--workload", default="dispatch",
                    choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k",
-                            "cfg5r", "cfg2m", "cfg3m"],
+                            "cfg5r", "cfg2m", "cfg3m", "cfg4s", "cfg5s"],
                    help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
                         "configuration's own path, for per-kernel figures")
     return p.parse_args()
@@ -260,8 +263,8 @@ class ConfigStep:
         import workloads
         self.m = m
         fused, kblock, recompute = which.endswith("f"), which.endswith("k"), which.endswith("r")
-        mxfp4 = which.endswith("m")
-        n = int(which[3:-1] if fused or kblock or recompute or mxfp4 else which[3:])
+        mxfp4, sr_grad = which.endswith("m"), which.endswith("s")
+        n = int(which[3:-1] if fused or kblock or recompute or mxfp4 or sr_grad else which[3:])
         w = workloads.CONFIGS[n]()
         self.w, self.n = w, n
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -281,6 +284,15 @@ class ConfigStep:
                             row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
                             col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
             self.ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
+            if sr_grad:
+                self.sr5 = torch.tensor([1234, 0], dtype=torch.int64, device=dev)
+                self._add("dswiglu_nvfp4_quant_sr",
+                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws,
+                                                        sr_state=self.sr5),
+                          T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16)
+                          + 2 * E * 4)
+                self.desc = dict(workload=w.name + " (stochastic FC1-grad codes)", tokens=T, ffn=F, experts=E)
+                return
             if recompute:
                 # no dX written: inputs read once + the quantized operands and the maxima
                 self._add("dswiglu_nvfp4_quant_nodx",
@@ -345,7 +357,12 @@ class ConfigStep:
         self._add("nvfp4_expert_scale", lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan,
                                                                         col_scale=self.recv["col_scale"]),
                   b["nvfp4_expert_scale"])
-        if kblock:
+        if sr_grad:
+            self.sr_recv = torch.tensor([w.sr_seed or 1234, 1 << 40], dtype=torch.int64, device=dev)
+            self._add("nvfp4_direct_receive_sr",
+                      lambda: m.ep_nvfp4_direct_receive_sr(self.packed, H, self.plan, self.recv, self.sr_recv),
+                      b["nvfp4_direct_receive"])
+        elif kblock:
             self._add("nvfp4_direct_receive_kblock",
                       lambda: m.ep_nvfp4_direct_receive_kblock(self.packed, H, self.plan, self.recv),
                       b["nvfp4_direct_receive"])
