@@ -113,27 +113,27 @@ def trace(args):
           "Command (from the repository root, via `python rocprof_summaries.py trace --workload "
           f"{args.workload}`):", "", "```", shown, "```", "",
           "All dispatches of the run: warm-up, the graph replays of the timed region and the eager per-call "
-          "passes (each preceded by a 1 GiB fill that evicts the MALL; the FillFunctor<float> row).", "",
+          "passes (each pass preceded by a 1 GiB read that evicts the MALL; the reduce_kernel row).", "",
           "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].split("(")[0].replace("void ", "")
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    # the eager per-call passes: every dispatch from the first 1 GiB fill on runs alone
+    # the eager per-call passes: every dispatch from the first 1 GiB read on runs alone
     # (one stream, nothing concurrent), so these durations compare with the bench's
     # per-call figures; the graph replays before them overlap calls on four streams
     trace_rows = list(csv.DictReader(open(os.path.join(out, "run_kernel_trace.csv"))))
     trace_rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = [(r["Kernel_Name"].split("(")[0].replace("void ", ""),
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace_rows]
-    first_fill = next((i for i, (n, us) in enumerate(dur) if "FillFunctor<float>" in n and us > 50.0), None)
-    if first_fill is not None:
+    first_sweep = next((i for i, (n, us) in enumerate(dur) if "reduce_kernel" in n and us > 50.0), None)
+    if first_sweep is not None:
         eager = {}
-        for n, us in dur[first_fill:]:
-            if "FillFunctor" in n:
+        for n, us in dur[first_sweep:]:
+            if "reduce_kernel" in n or "fillBuffer" in n:     # the read and its reduction's semaphore clear
                 continue
             eager.setdefault(n, []).append(us)
-        md += ["", "Eager per-call passes only (each call alone after the fill; compare with the bench's "
+        md += ["", "Eager per-call passes only (each call alone, each pass after the MALL-evicting read; compare with the bench's "
                "per-call times below):", "", "| kernel | dispatches | avg us | min us |", "|---|---|---|---|"]
         for n, v in eager.items():
             md.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
