@@ -32,9 +32,6 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 
 constexpr int kWave = 64;
 constexpr float kTokenBound = 2688.0f;  // 6 * 448
-// Outputs larger than this go out with streaming stores: half of MI355X's
-// 256 MB last-level cache (MALL), which keeps smaller outputs for their reader.
-constexpr uint64_t kStreamStoreBytes = 128ull << 20;
 
 // ----------------------------------------------------------------- bit casts
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -41,10 +41,13 @@ __device__ __forceinline__ void decode8_tiny(uint32_t w, float s, int e, uint32_
 // One wave per output row; lane l decodes 8-element chunks l, l+64, ... (a
 // dword of codes -> 16 bytes of BF16), so every load instruction reads 256
 // contiguous code bytes and every store writes 1 KiB contiguously.
-// NT: streaming (nontemporal) stores, for outputs much larger than the last-level
-// cache -- measured 548 -> 405 us on a 1.9 GB output, but slower on outputs the
-// 256 MB MALL holds (23.4 -> 24.7 us on 67 MB), so the host picks by size.
-template <bool NT>
+// The BF16 rows go out with streaming (nontemporal) stores: whole lines, read by
+// no later kernel of this library (their reader is a GEMM), so they are kept out
+// of the 256 MB MALL, which is left to data that is read again soon (the packed
+// rows the receive reads once per routed copy, the dX the FC1-grad quantizer
+// re-reads).  Measured: the same call time alone (17.6 us on 67 MB; 548 -> 374 us
+// on a 1.9 GB output), and the dispatch step with the MXFP8 receive done the same
+// way 203 -> 185 us.
 __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict__ packed, int rows_in, int H,
                                                       int row_bytes, const int32_t* __restrict__ src_row,
                                                       int rows_out, uint16_t* __restrict__ out) {
@@ -54,9 +57,9 @@ __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict_
   int src = src_row ? src_row[g] : g;
   if (src >= rows_in) src = -1;  // out-of-range map entries decode as zero rows
   const int nch = H >> 3;
-  uint4* orow = reinterpret_cast<uint4*>(out + (size_t)g * H);
+  u32x4* orow = reinterpret_cast<u32x4*>(out + (size_t)g * H);
   if (src < 0) {
-    for (int c = lane; c < nch; c += 64) orow[c] = make_uint4(0, 0, 0, 0);
+    for (int c = lane; c < nch; c += 64) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, orow + c);
     return;
   }
   const uint8_t* prow = packed + (size_t)src * row_bytes;
@@ -77,17 +80,13 @@ __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict_
       if (K >= -126) decode8(w, pow2f(K), mant, o);
       else decode8_tiny(w, s, e, o);
     }
-    if (NT) {
-      const u32x4 ov = {o[0], o[1], o[2], o[3]};
-      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(orow + c));
-    } else {
-      orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, orow + c);
   }
 }
 
 // MXFP8 grouped receive: grouped row g copies token src_row[g] (data + scales);
-// -1 rows are zero.  One wave per grouped row, 16-byte copies.
+// -1 rows are zero.  One wave per grouped row, 16-byte copies; streaming stores,
+// as in the unpack (the grouped operand is a GEMM's, not read again here).
 __global__ __launch_bounds__(256) void k_mxfp8_receive(const uint8_t* __restrict__ data,
                                                        const uint8_t* __restrict__ scales, int tokens, int H,
                                                        const int32_t* __restrict__ src_row, int r_cap,
@@ -97,17 +96,17 @@ __global__ __launch_bounds__(256) void k_mxfp8_receive(const uint8_t* __restrict
   if (g >= r_cap) return;
   const int src = src_row[g];
   const int n16 = H >> 4, ns = H >> 5;
-  uint4* dst = reinterpret_cast<uint4*>(g_data + (size_t)g * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(g_data + (size_t)g * H);
   uint8_t* ds = g_scales + (size_t)g * ns;
   if (src < 0 || src >= tokens) {  // padding (or an out-of-range entry): zero bytes
-    for (int i = lane; i < n16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
-    for (int i = lane; i < ns; i += 64) ds[i] = 0;
+    for (int i = lane; i < n16; i += 64) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dst + i);
+    for (int i = lane; i < ns; i += 64) __builtin_nontemporal_store((uint8_t)0, ds + i);
     return;
   }
-  const uint4* sp = reinterpret_cast<const uint4*>(data + (size_t)src * H);
-  for (int i = lane; i < n16; i += 64) dst[i] = sp[i];
+  const u32x4* sp = reinterpret_cast<const u32x4*>(data + (size_t)src * H);
+  for (int i = lane; i < n16; i += 64) __builtin_nontemporal_store(sp[i], dst + i);
   const uint8_t* ss = scales + (size_t)src * ns;
-  for (int i = lane; i < ns; i += 64) ds[i] = ss[i];
+  for (int i = lane; i < ns; i += 64) __builtin_nontemporal_store(ss[i], ds + i);
 }
 
 }  // namespace mtb
@@ -124,12 +123,8 @@ MTB_EXPORT int32_t ep_nvfp4_unpack(const uint8_t* packed, int64_t rows_in, int64
   if (!src_row && rows_in == 0) return EP_OK;
   const int H = (int)hidden;
   dim3 grid((unsigned)((rows_out + 3) / 4)), block(256);
-  if ((uint64_t)rows_out * (uint64_t)H * 2u > kStreamStoreBytes)
-    hipLaunchKernelGGL(k_nvfp4_unpack<true>, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
-                       9 * H / 16 + 4, src_row, (int)rows_out, out);
-  else
-    hipLaunchKernelGGL(k_nvfp4_unpack<false>, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H,
-                       9 * H / 16 + 4, src_row, (int)rows_out, out);
+  hipLaunchKernelGGL(k_nvfp4_unpack, grid, block, 0, (hipStream_t)stream, packed, (int)rows_in, H, 9 * H / 16 + 4,
+                     src_row, (int)rows_out, out);
   return launch_status();
 }
 
