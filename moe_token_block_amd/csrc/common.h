@@ -41,11 +41,13 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 __device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
 
 // Exponent of a float that is a power of two (normal or subnormal).
+// Branch-free (a select), so that a load of p need not be waited for before
+// the loads that follow it in program order are issued.  p = 0 gives -149.
 __device__ __forceinline__ int pow2_exponent(float p) {
   uint32_t b = __float_as_uint(p);
   uint32_t ef = (b >> 23) & 0xFFu;
-  if (ef) return (int)ef - 127;
-  return -149 + (31 - __builtin_clz(b & 0x7FFFFFu));  // subnormal: position of the single set bit
+  const int sub = -149 + (31 - __builtin_clz((b & 0x7FFFFFu) | 1u));  // subnormal: position of the single set bit
+  return ef ? (int)ef - 127 : sub;
 }
 
 // ----------------------------------------------------------------- E4M3

@@ -47,18 +47,20 @@ __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict
   const int toff = (H >> 1) + (H >> 4);
   uint32_t m = 0;  // t > 0 is a power of two: compare bit patterns
   // four rows per thread per round: the four source-row loads go out together,
-  // then the four t loads (two dependent round trips per 4096 rows, not per 1024)
-  for (int g = g0 + (int)threadIdx.x; g < g1; g += 4 * 1024) {
+  // then the four t loads (two dependent round trips per 4096 rows, not per
+  // 1024).  The loads are unconditional, at indices clamped into range, so that
+  // none waits behind a branch; out-of-range rows are dropped after.
+  for (int g = g0 + (int)threadIdx.x; g < g1 && T > 0; g += 4 * 1024) {
     int src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) src[q] = g + q * 1024 < g1 ? src_row[g + q * 1024] : -1;
+    for (int q = 0; q < 4; ++q) src[q] = src_row[min(g + q * 1024, g1 - 1)];
+    uint32_t tb[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (src[q] >= 0 && src[q] < T) {
-        uint32_t tb = *reinterpret_cast<const uint32_t*>(packed + (size_t)src[q] * row_bytes + toff);
-        m = m > tb ? m : tb;
-      }
-    }
+    for (int q = 0; q < 4; ++q)
+      tb[q] = *reinterpret_cast<const uint32_t*>(packed + (size_t)min(max(src[q], 0), T - 1) * row_bytes + toff);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (g + q * 1024 < g1 && src[q] >= 0 && src[q] < T) m = m > tb[q] ? m : tb[q];
   }
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;

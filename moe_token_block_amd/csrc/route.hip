@@ -27,13 +27,6 @@ constexpr int kRouteChunk = 256;  // entries per wave
 constexpr int kMaxExperts = 1024;
 
 template <typename IDX>
-__device__ __forceinline__ int load_expert(const IDX* idx, int64_t i, int E, bool& bad) {
-  int64_t v = (int64_t)idx[i];
-  bad = (v < -1) || (v >= E);
-  return (v >= 0 && v < E) ? (int)v : -1;
-}
-
-template <typename IDX>
 __global__ __launch_bounds__(256) void k_route_count(const IDX* __restrict__ idx, int64_t R, int E, int W,
                                                      int32_t* __restrict__ hist, int32_t* __restrict__ d_error) {
   __shared__ int32_t cnt[4][kMaxExperts];
@@ -42,15 +35,17 @@ __global__ __launch_bounds__(256) void k_route_count(const IDX* __restrict__ idx
   for (int e = lane; e < E; e += 64) cnt[wl][e] = 0;
   __syncthreads();
   if (w < W) {
+    // the chunk's loads first (indices clamped into [0, R)), then the counts
+    IDX v[kRouteChunk / 64];
+#pragma unroll
+    for (int s = 0; s < kRouteChunk / 64; ++s) v[s] = idx[min((int64_t)w * kRouteChunk + s * 64 + lane, R - 1)];
     bool any_bad = false;
+#pragma unroll
     for (int s = 0; s < kRouteChunk / 64; ++s) {
-      int64_t i = (int64_t)w * kRouteChunk + s * 64 + lane;
-      if (i < R) {
-        bool bad;
-        int x = load_expert(idx, i, E, bad);
-        any_bad |= bad;
-        if (x >= 0) atomicAdd(&cnt[wl][x], 1);
-      }
+      const bool in = (int64_t)w * kRouteChunk + s * 64 + lane < R;
+      const int64_t q = in ? (int64_t)v[s] : -1;
+      any_bad |= (q < -1) || (q >= E);
+      if (q >= 0 && q < E) atomicAdd(&cnt[wl][(int)q], 1);
     }
     if (any_bad) atomicOr(d_error, EP_DEVERR_EXPERT_ID);
   }
@@ -128,13 +123,14 @@ __global__ __launch_bounds__(256) void k_route_scatter(const IDX* __restrict__ i
   __syncthreads();
   if (w >= W) return;
   const uint64_t lt = (1ull << lane) - 1ull;
+  IDX v[kRouteChunk / 64];
+#pragma unroll
+  for (int s = 0; s < kRouteChunk / 64; ++s) v[s] = idx[min((int64_t)w * kRouteChunk + s * 64 + lane, R - 1)];
+#pragma unroll
   for (int s = 0; s < kRouteChunk / 64; ++s) {
     int64_t i = (int64_t)w * kRouteChunk + s * 64 + lane;
-    int x = -1;
-    if (i < R) {
-      bool bad;
-      x = load_expert(idx, i, E, bad);
-    }
+    const int64_t q = i < R ? (int64_t)v[s] : -1;
+    const int x = (q >= 0 && q < E) ? (int)q : -1;
     const bool valid = x >= 0;
     uint64_t m = __ballot(valid);
     // lanes whose expert id agrees with this lane's on every id bit
@@ -159,26 +155,45 @@ __global__ __launch_bounds__(256) void k_route_scatter(const IDX* __restrict__ i
 // ------------------------------------------------------------------ single workgroup
 constexpr int kSingleWaves = 16;
 constexpr int64_t kSingleMax = 16384;  // beyond this one CU's scattered stores dominate
+constexpr int kSingleSteps = (int)(kSingleMax / kSingleWaves / 64);  // 64-entry steps per wave, at most
 
+// Each wave owns `chunk` consecutive entries and loads all of them into
+// registers up front (one memory round trip instead of one per 64 entries:
+// the kernel is latency-bound), counts them, and after the scan places them.
+// (Building src_row in LDS and writing it out coalesced at the end was measured
+// no faster than the scattered 4-byte stores.)
 template <typename IDX>
 __global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ idx, int R, int k, int E, int A,
                                                        int r_cap, int ebits, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ dst_row,
                                                        int32_t* __restrict__ src_row, int32_t* __restrict__ d_error) {
   __shared__ int32_t hist[kSingleWaves][kMaxExperts];  // per-wave counts, then per-wave starting rows
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t scan[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int chunk = ((R + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;
+  const int chunk = ((R + kSingleWaves - 1) / kSingleWaves + 63) / 64 * 64;  // <= kSingleSteps * 64
   const int c0 = w * chunk, c1 = min(R, c0 + chunk);
+  // all loads first, unconditional (indices clamped into [0, R)), so that they
+  // are in flight together; entries outside the wave's range are dropped after
+  IDX v[kSingleSteps];
+  if (R > 0) {
+#pragma unroll
+    for (int st = 0; st < kSingleSteps; ++st) v[st] = idx[min(c0 + st * 64 + lane, R - 1)];
+  }
+  int xs[kSingleSteps];
+  bool any_bad = false;
+#pragma unroll
+  for (int st = 0; st < kSingleSteps; ++st) {
+    const int i = c0 + st * 64 + lane;
+    const bool in = R > 0 && st * 64 < chunk && i < c1;
+    const int64_t q = in ? (int64_t)v[st] : -1;
+    any_bad |= (q < -1) || (q >= E);
+    xs[st] = (q >= 0 && q < E) ? (int)q : -1;
+  }
   for (int e = lane; e < E; e += 64) hist[w][e] = 0;
   __syncthreads();
-  bool any_bad = false;
-  for (int i = c0 + lane; i < c1; i += 64) {
-    bool bad;
-    int x = load_expert(idx, i, E, bad);
-    any_bad |= bad;
-    if (x >= 0) atomicAdd(&hist[w][x], 1);
-  }
+#pragma unroll
+  for (int st = 0; st < kSingleSteps; ++st)
+    if (xs[st] >= 0) atomicAdd(&hist[w][xs[st]], 1);
   if (any_bad) atomicOr(d_error, EP_DEVERR_EXPERT_ID);
   __syncthreads();
   int32_t cnt = 0;
@@ -189,8 +204,8 @@ __global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ i
       cnt += c;
     }
     counts[tid] = cnt;
+    scan[tid] = (cnt + A - 1) / A * A;
   }
-  scan[tid] = tid < E ? (cnt + A - 1) / A * A : 0;
   __syncthreads();
   for (int o = 1; o < E; o <<= 1) {
     int32_t v = (tid < E && tid >= o) ? scan[tid - o] : 0;
@@ -210,36 +225,27 @@ __global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ i
   for (int32_t r = total + tid; r < r_cap; r += 1024) src_row[r] = -1;
   __syncthreads();
   const uint64_t lt = (1ull << lane) - 1ull;
-  // entries are fetched 8 steps (512 entries) at a time, so the loads do not
-  // wait behind the LDS updates of the previous step
-  for (int grp = c0; grp < c1; grp += 8 * 64) {
-    int xs[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      int i = grp + st * 64 + lane;
-      bool bad;
-      xs[st] = i < c1 ? load_expert(idx, i, E, bad) : -1;
-    }
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      int i = grp + st * 64 + lane;
-      int x = xs[st];
-      const bool valid = x >= 0;
-      uint64_t m = __ballot(valid);
+  for (int st = 0; st < kSingleSteps; ++st) {
+    if (st * 64 >= chunk) break;  // wave-uniform
+    const int i = c0 + st * 64 + lane;
+    const int x = xs[st];
+    const bool valid = x >= 0;
+    uint64_t m = __ballot(valid);
+    // lanes whose expert id agrees with this lane's on every id bit
 #pragma unroll 1
-      for (int b = 0; b < ebits; ++b) {
-        uint64_t bb = __ballot(valid && ((x >> b) & 1));
-        m &= ((x >> b) & 1) ? bb : ~bb;
-      }
-      if (valid) {
-        int32_t b0 = hist[w][x];
-        int32_t d = b0 + __popcll(m & lt);
-        dst_row[i] = d;
-        src_row[d] = i / k;
-        if ((m >> lane) == 1ull) hist[w][x] = b0 + __popcll(m);
-      } else if (i < c1) {
-        dst_row[i] = -1;
-      }
+    for (int b = 0; b < ebits; ++b) {
+      uint64_t bb = __ballot(valid && ((x >> b) & 1));
+      m &= ((x >> b) & 1) ? bb : ~bb;
+    }
+    if (valid) {
+      int32_t b0 = hist[w][x];
+      int32_t d = b0 + __popcll(m & lt);
+      dst_row[i] = d;
+      src_row[d] = i / k;
+      if ((m >> lane) == 1ull) hist[w][x] = b0 + __popcll(m);
+    } else if (i < c1) {
+      dst_row[i] = -1;
     }
   }
 }

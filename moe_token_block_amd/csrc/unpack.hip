@@ -63,24 +63,43 @@ __global__ __launch_bounds__(256) void k_nvfp4_unpack(const uint8_t* __restrict_
     return;
   }
   const uint8_t* prow = packed + (size_t)src * row_bytes;
-  const float t = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
-  const int e = pow2_exponent(t);
   const uint32_t* cw = reinterpret_cast<const uint32_t*>(prow);
-#pragma unroll 2
-  for (int c = lane; c < nch; c += 64) {
-    uint32_t w = cw[c];
-    float s = e4m3_decode(prow[(H >> 1) + (c >> 1)]);
-    uint32_t o[4];
-    if (s == 0.0f) {
-      decode8(w, 1.0f, 0.0f, o);  // zero scale: signed zeros
-    } else {
-      int k = __builtin_amdgcn_frexp_expf(s) - 1;
-      float mant = __builtin_amdgcn_frexp_mantf(s) * 2.0f;
-      int K = k + e;
-      if (K >= -126) decode8(w, pow2f(K), mant, o);
-      else decode8_tiny(w, s, e, o);
+  // eight chunks per lane at a time: their code and scale loads go out together
+  // (indices clamped into the row), then the decodes and stores.  The row's t is
+  // loaded with the first group, so that it costs no round trip of its own.
+  uint32_t wv[8], sv[8];
+  auto load_group = [&](int cb) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(cb + u * 64 + lane, nch - 1);
+      wv[u] = cw[c];
+      sv[u] = prow[(H >> 1) + (c >> 1)];
     }
-    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, orow + c);
+  };
+  auto decode_group = [&](int cb, int e) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = cb + u * 64 + lane;  // lanes past the row decode a clamped chunk and skip the store
+      const float s = e4m3_decode(sv[u]);
+      uint32_t o[4];
+      if (s == 0.0f) {
+        decode8(wv[u], 1.0f, 0.0f, o);  // zero scale: signed zeros
+      } else {
+        int k = __builtin_amdgcn_frexp_expf(s) - 1;
+        float mant = __builtin_amdgcn_frexp_mantf(s) * 2.0f;
+        int K = k + e;
+        if (K >= -126) decode8(wv[u], pow2f(K), mant, o);
+        else decode8_tiny(wv[u], s, e, o);
+      }
+      if (c < nch) __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, orow + c);
+    }
+  };
+  load_group(0);
+  const int e = pow2_exponent(*reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4)));
+  decode_group(0, e);
+  for (int cb = 8 * 64; cb < nch; cb += 8 * 64) {
+    load_group(cb);
+    decode_group(cb, e);
   }
 }
 
@@ -103,10 +122,25 @@ __global__ __launch_bounds__(256) void k_mxfp8_receive(const uint8_t* __restrict
     for (int i = lane; i < ns; i += 64) __builtin_nontemporal_store((uint8_t)0, ds + i);
     return;
   }
+  // loads first, four per lane at a time at indices clamped into the row, so
+  // that a row needs one memory round trip per 4 KiB, not one per 1 KiB
   const u32x4* sp = reinterpret_cast<const u32x4*>(data + (size_t)src * H);
-  for (int i = lane; i < n16; i += 64) __builtin_nontemporal_store(sp[i], dst + i);
   const uint8_t* ss = scales + (size_t)src * ns;
-  for (int i = lane; i < ns; i += 64) __builtin_nontemporal_store(ss[i], ds + i);
+  for (int i0 = 0; i0 < n16 || i0 < ns; i0 += 4 * 64) {
+    u32x4 v[4];
+    uint32_t b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = sp[min(i0 + u * 64 + lane, n16 - 1)];
+      b[u] = ss[min(i0 + u * 64 + lane, ns - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 64 + lane;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+      if (i < ns) __builtin_nontemporal_store((uint8_t)b[u], ds + i);
+    }
+  }
 }
 
 }  // namespace mtb

@@ -120,7 +120,10 @@ def test_mxfp8_pack_bit_exact(dev, h):
 @pytest.mark.parametrize("tokens,k,E,A,idx64,unused", [
     (1, 1, 1, 16, False, 0.0), (97, 3, 6, 16, False, 0.1), (300, 2, 8, 128, True, 0.0),
     (513, 4, 33, 256, False, 0.05), (2048, 8, 32, 16, True, 0.0), (1000, 1, 1024, 16, False, 0.0),
-    (0, 2, 4, 16, False, 0.0)])
+    (0, 2, 4, 16, False, 0.0),
+    (600, 2, 40, 1024, False, 0.0),      # one workgroup, capacity beyond the LDS-staged src_row
+    (4100, 8, 16, 16, False, 0.02),      # > 16384 entries: the three-kernel path, a ragged last wave
+    (2049, 8, 64, 16, True, 0.0)])       # 16392 entries: just past the one-workgroup limit
 def test_route_plan_bit_exact(dev, tokens, k, E, A, idx64, unused):
     rng = np.random.default_rng(tokens * 7 + E)
     topk = np.array([rng.permutation(E)[:k] for _ in range(tokens)], dtype=np.int32).reshape(tokens, k)
