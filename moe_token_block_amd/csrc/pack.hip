@@ -8,6 +8,8 @@
 // loaded as two 16-byte vectors, so a block's max needs no cross-lane work and
 // one wave-wide reduction gives the row max.  The whole row stays in VGPRs
 // between the max and the encode (hidden <= 16384: at most 16 blocks/lane).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -318,6 +320,97 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack_sr(const uint16_t* __restric
   }
 }
 
+// The same for H <= 4096 (at most four 16-element blocks per lane), rows held
+// in registers and software-pipelined: a wave quantizes rows wave, wave + nw,
+// ... and issues the loads of its next row before the Philox work of the
+// current one, so the loads of one row overlap the arithmetic of the previous
+// (a grid of one row per wave runs every load before any arithmetic).
+template <int MODE>
+__device__ __forceinline__ void sr_block(const uint4& v0, const uint4& v1, int j, int e, uint64_t n_row,
+                                         uint32_t seed_lo, uint32_t seed_hi, const RowOut& o, int row) {
+  uint32_t a = absmax_bf16x8(v0), b = absmax_bf16x8(v1);
+  uint32_t sc, o0, o1;
+  BlockQuant q = nvfp4_block(__uint_as_float((a > b ? a : b) << 16), e, sc);
+  encode_sr<MODE>(v0, v1, q, n_row + (uint64_t)(16 * j), seed_lo, seed_hi, o0, o1);
+  store_block(o, (uint32_t)row, j, o0, o1, sc);
+}
+
+// One row's NB blocks per lane held in registers (blocks j = lane + 64k; a
+// lane past the row's end takes the last block: it computes and stores that
+// block's bytes again, the same values).  Everything is unconditional, so the
+// number of stores between two rows' loads is fixed and the wait for a row's
+// data does not wait for the previous row's stores.
+template <int NB>
+struct SrRow {
+  uint4 a[NB], b[NB];
+};
+
+template <int MODE, int NB>
+__global__ __launch_bounds__(256) void k_nvfp4_pack_sr_rows(const uint16_t* __restrict__ x, int rows, int H,
+                                                           const RowOut o, const uint64_t* __restrict__ sr_state) {
+  const int lane = threadIdx.x & 63;
+  const int nw = (int)gridDim.x * 4;
+  int row = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (row >= rows) return;
+  const int nblk = H >> 4;  // 64 * (NB / 2) < nblk <= 64 * NB
+  const uint64_t seed = sr_state[0];
+  const uint32_t seed_lo = (uint32_t)seed, seed_hi = (uint32_t)(seed >> 32);
+  const uint64_t n_base = sr_state[1];
+  int jb[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) jb[k] = min(lane + 64 * k, nblk - 1);
+  auto load = [&](int r, SrRow<NB>& d) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(r, rows - 1) * H);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      d.a[k] = xr[2 * jb[k]];
+      d.b[k] = xr[2 * jb[k] + 1];
+    }
+  };
+  auto quantize = [&](int r, const SrRow<NB>& d) {
+    uint32_t rmax = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const uint32_t m0 = absmax_bf16x8(d.a[k]), m1 = absmax_bf16x8(d.b[k]);
+      const uint32_t m = m0 > m1 ? m0 : m1;  // a clamped block repeats a block of the row: no effect
+      rmax = rmax > m ? rmax : m;
+    }
+    rmax = wave_max_u32(rmax);
+    const int e = token_exponent(__uint_as_float(rmax << 16));
+    store_t(o, (uint32_t)r, __builtin_ldexpf(1.0f, e));  // every lane, the same 4 bytes
+    const uint64_t n_row = n_base + (uint64_t)r * (uint64_t)H;
+    // written out, not a loop: the compiler does not unroll a loop of four
+    // Philox-heavy bodies, and the row's registers would then go to scratch
+    sr_block<MODE>(d.a[0], d.b[0], jb[0], e, n_row, seed_lo, seed_hi, o, r);
+    if constexpr (NB > 1) sr_block<MODE>(d.a[1], d.b[1], jb[1], e, n_row, seed_lo, seed_hi, o, r);
+    if constexpr (NB > 2) sr_block<MODE>(d.a[2], d.b[2], jb[2], e, n_row, seed_lo, seed_hi, o, r);
+    if constexpr (NB > 3) sr_block<MODE>(d.a[3], d.b[3], jb[3], e, n_row, seed_lo, seed_hi, o, r);
+  };
+  // Two register sets used in turn: while one row is quantized the next row's
+  // loads (row index clamped: always issued) are in flight.  The first row is
+  // peeled so that every quantize, also the first in the loop, has the same
+  // instructions between its loads and itself (its set's loads, one row's
+  // stores, the other set's loads): the wait for its data then never includes
+  // the stores before it.  The scheduling barriers keep the arithmetic of a
+  // row from being hoisted above the next row's loads.
+  SrRow<NB> s0, s1;
+  load(row, s0);
+  load(row + nw, s1);
+  __builtin_amdgcn_sched_barrier(0);
+  quantize(row, s0);
+  for (;;) {
+    if (row + nw >= rows) break;  // wave-uniform
+    load(row + 2 * nw, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    quantize(row + nw, s1);
+    if (row + 2 * nw >= rows) break;
+    load(row + 3 * nw, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    quantize(row + 2 * nw, s0);
+    row += 2 * nw;
+  }
+}
+
 // ----------------------------------------------------------------- MXFP8
 // Two lanes per 32-element block (16 elements each): one xor-1 exchange gives
 // the block max.  Data goes out as one 16-byte store per lane.
@@ -430,6 +523,25 @@ MTB_EXPORT int32_t ep_nvfp4_pack(const uint16_t* x, int64_t rows, int64_t hidden
   const RowOut o{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
+  if (round_mode != EP_ROUND_NEAREST && H <= 4096) {
+    // two or more rows per wave, at most 12 waves per CU (the 4-block kernel's
+    // registers allow 3 per SIMD: more would need a second round)
+    const int64_t waves = std::min<int64_t>((rows + 1) / 2, 256 * 12);
+    const dim3 g((unsigned)((waves + 3) / 4));
+    const int nb = (H / 16 + 63) / 64;
+#define MTB_SR_ROWS(M)                                                                                   \
+  do {                                                                                                   \
+    if (nb <= 1) hipLaunchKernelGGL((k_nvfp4_pack_sr_rows<M, 1>), g, block, 0, s, x, (int)rows, H, o, sr_state); \
+    else if (nb <= 2) hipLaunchKernelGGL((k_nvfp4_pack_sr_rows<M, 2>), g, block, 0, s, x, (int)rows, H, o, sr_state); \
+    else hipLaunchKernelGGL((k_nvfp4_pack_sr_rows<M, 4>), g, block, 0, s, x, (int)rows, H, o, sr_state); \
+  } while (0)
+    if (round_mode == EP_ROUND_SR_ELEMENT) MTB_SR_ROWS(EP_ROUND_SR_ELEMENT);
+    else if (round_mode == EP_ROUND_SR_STREAM) MTB_SR_ROWS(EP_ROUND_SR_STREAM);
+    else if (round_mode == EP_ROUND_SR_ELEMENT_CARRY) MTB_SR_ROWS(EP_ROUND_SR_ELEMENT_CARRY);
+    else MTB_SR_ROWS(EP_ROUND_SR_STREAM_CARRY);
+#undef MTB_SR_ROWS
+    return launch_status();
+  }
   if (round_mode == EP_ROUND_SR_ELEMENT) {
     hipLaunchKernelGGL(k_nvfp4_pack_sr<EP_ROUND_SR_ELEMENT>, grid, block, 0, s, x, (int)rows, H, o, sr_state);
   } else if (round_mode == EP_ROUND_SR_STREAM) {

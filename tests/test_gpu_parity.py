@@ -101,6 +101,24 @@ def test_stochastic_rounding_bit_exact(dev, mode, seed, base):
     assert_bytes_equal(host(packed), want, f"SR mode {mode}")
 
 
+@pytest.mark.parametrize("h,rows,mode", [(64, 13001, 3), (1088, 70, 3), (2048, 33, 1), (4096, 41, 3), (4096, 9, 2),
+                                         (8192, 9, 3)])
+def test_stochastic_rounding_shapes(dev, h, rows, mode):
+    """Row counts and widths that exercise the row-pipelined SR kernel (one, two and
+    four blocks per lane, lanes past the row's end, many rows per wave, a ragged
+    last pair of rows) and the two-pass kernel beyond 4096 columns."""
+    rng = np.random.default_rng(h + rows)
+    x = rng.standard_t(3, size=(rows, h)) * 10.0 ** rng.uniform(-4, 1, size=(rows, 1))
+    bits = _bits(x)
+    seed, base = 1234 + h, 99 * rows
+    st = torch.tensor([seed, base], dtype=torch.int64, device=dev)
+    print(f"sr shapes h={h} rows={rows} mode={mode}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev), round_mode=mode, sr_state=st)
+    want = onv.pack_rows(bits, sr_seed=seed, sr_counter_base=base, sr_mode="element" if mode in (1, 3) else "stream",
+                         sr_rule="carry" if mode >= 3 else "threshold")
+    assert_bytes_equal(host(packed), want, f"SR h={h} rows={rows} mode={mode}")
+
+
 # ------------------------------------------------------------------ MXFP8
 @pytest.mark.parametrize("h", [32, 96, 1024, 4096])
 def test_mxfp8_pack_bit_exact(dev, h):
@@ -375,16 +393,17 @@ def test_direct_receive_sr_bit_exact(dev, case):
         assert_bytes_equal(host(got[key])[:off], host(ref[key])[:off], f"SR receive {key}")
 
 
-def test_mxfp8_receive_bit_exact(dev):
-    w = workloads.small_dispatch(11, 300, 256, 6, 2, alignment=128, unused_frac=0.1)
+@pytest.mark.parametrize("h", [32, 96, 256, 4096, 7168])  # one to several 4 KiB load groups per row
+def test_mxfp8_receive_bit_exact(dev, h):
+    w = workloads.small_dispatch(11, 300, h, 6, 2, alignment=128, unused_frac=0.1)
     data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
     plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 6, 128)
     gd, gs = mtb.ep_mxfp8_direct_receive(data, scales, plan)
     wd, ws = omx.pack_rows(w.x_bits)
     src = host(plan["src_row"])
     ed, es = omx.grouped_receive(wd, ws, src)
-    assert_bytes_equal(host(gd), ed, "mxfp8 grouped data")
-    assert_bytes_equal(host(gs), es, "mxfp8 grouped scales")
+    assert_bytes_equal(host(gd), ed, f"mxfp8 grouped data h={h}")
+    assert_bytes_equal(host(gs), es, f"mxfp8 grouped scales h={h}")
 
 
 # ------------------------------------------------------------------ dSwiGLU
