@@ -55,7 +55,7 @@ CALL_SOURCES = {
 # the kernels each call launches (as named in a rocprofv3 kernel trace)
 CALL_KERNELS = {
     "route_plan": ["k_route_single (<= 16K entries) or k_route_count + k_route_scan + k_route_scatter"],
-    "nvfp4_pack": ["k_nvfp4_pack_wg (H >= 4096) or k_nvfp4_pack"], "nvfp4_pack_sr": ["k_nvfp4_pack_sr"],
+    "nvfp4_pack": ["k_nvfp4_pack_wg (H >= 4096) or k_nvfp4_pack"], "nvfp4_pack_sr": ["k_nvfp4_pack_sr_rows (H <= 4096) or k_nvfp4_pack_sr"],
     "mxfp8_pack": ["k_mxfp8_pack"], "nvfp4_expert_scale": ["k_expert_scale"],
     "nvfp4_expert_scale_grad": ["k_expert_scale"], "nvfp4_direct_receive": ["k_nvfp4_receive"],
     "nvfp4_direct_receive_grad": ["k_nvfp4_receive"], "mxfp8_receive": ["k_mxfp8_receive"],
