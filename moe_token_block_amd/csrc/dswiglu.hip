@@ -134,39 +134,57 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <bool STORE>
+// One wave per row; lane l owns 8-column chunks j = l + 64k of a, b and dy,
+// NB of them per group.  A group's 3 * NB loads are issued before any of its
+// arithmetic (chunks past the row's end load its last chunk and are not
+// stored), so a 2048-column row costs one memory round trip, not one per chunk
+// with the previous chunk's stores waited for too.
+template <bool STORE, int NB>
 __global__ __launch_bounds__(256) void k_dswiglu_epilogue(const uint16_t* __restrict__ preact,
                                                           const uint16_t* __restrict__ dy, int T, int F,
                                                           uint16_t* __restrict__ dx, uint32_t* __restrict__ rowmax) {
   const int lane = threadIdx.x & 63;
   const int r = (int)(blockIdx.x * 4u + (threadIdx.x >> 6));
   if (r >= T) return;
+  const int nch = F >> 3;
   const uint4* pa = reinterpret_cast<const uint4*>(preact + (size_t)r * 2 * F);
   const uint4* pb = reinterpret_cast<const uint4*>(preact + (size_t)r * 2 * F + F);
   const uint4* pd = reinterpret_cast<const uint4*>(dy + (size_t)r * F);
   uint4* oa = reinterpret_cast<uint4*>(dx + (size_t)r * 2 * F);
   uint4* ob = reinterpret_cast<uint4*>(dx + (size_t)r * 2 * F + F);
   uint32_t m = 0;
-  for (int j = lane; j < (F >> 3); j += 64) {
-    uint4 va = ld_stream16(pa + j), vb = ld_stream16(pb + j), vd = ld_stream16(pd + j);
-    uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w}, wd[4] = {vd.x, vd.y, vd.z, vd.w};
-    uint32_t ra[4], rb[4];
+  for (int c0 = 0; c0 < nch; c0 += 64 * NB) {
+    uint4 va[NB], vb[NB], vd[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float da0, db0, da1, db1;
-      dswiglu_pair(bf16lo(wa[i]), bf16lo(wb[i]), bf16lo(wd[i]), da0, db0);
-      dswiglu_pair(bf16hi(wa[i]), bf16hi(wb[i]), bf16hi(wd[i]), da1, db1);
-      ra[i] = bf16pair(da0, da1);
-      rb[i] = bf16pair(db0, db1);
+    for (int k = 0; k < NB; ++k) {
+      const int j = min(c0 + lane + 64 * k, nch - 1);
+      va[k] = ld_stream16(pa + j);
+      vb[k] = ld_stream16(pb + j);
+      vd[k] = ld_stream16(pd + j);
     }
-    uint4 oA = make_uint4(ra[0], ra[1], ra[2], ra[3]), oB = make_uint4(rb[0], rb[1], rb[2], rb[3]);
-    if (STORE) {
-      oa[j] = oA;
-      ob[j] = oB;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int j = c0 + lane + 64 * k;
+      const uint32_t wa[4] = {va[k].x, va[k].y, va[k].z, va[k].w}, wb[4] = {vb[k].x, vb[k].y, vb[k].z, vb[k].w};
+      const uint32_t wd[4] = {vd[k].x, vd[k].y, vd[k].z, vd[k].w};
+      uint32_t ra[4], rb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float da0, db0, da1, db1;
+        dswiglu_pair(bf16lo(wa[i]), bf16lo(wb[i]), bf16lo(wd[i]), da0, db0);
+        dswiglu_pair(bf16hi(wa[i]), bf16hi(wb[i]), bf16hi(wd[i]), da1, db1);
+        ra[i] = bf16pair(da0, da1);
+        rb[i] = bf16pair(db0, db1);
+      }
+      const uint4 oA = make_uint4(ra[0], ra[1], ra[2], ra[3]), oB = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+      if (STORE && j < nch) {
+        oa[j] = oA;
+        ob[j] = oB;
+      }
+      uint32_t x = absmax_bf16x8(oA), y = absmax_bf16x8(oB);
+      x = x > y ? x : y;
+      m = m > x ? m : x;  // a clamped chunk repeats one of the row: no effect on the max
     }
-    uint32_t x = absmax_bf16x8(oA), y = absmax_bf16x8(oB);
-    x = x > y ? x : y;
-    m = m > x ? m : x;
   }
   m = wave_max_u32(m);
   // non-negative floats order like their bit patterns: the integer max is exact
@@ -668,12 +686,22 @@ static int32_t dswiglu_quant_impl(const uint16_t* preact, const uint16_t* dy, in
   uint32_t* rowmax = (uint32_t*)workspace;
   int32_t* offs = (int32_t*)((char*)workspace + rowmax_bytes(tokens));
   int32_t* poffs = offs + (E + 1);
-  if (T > 0 && dx)
-    hipLaunchKernelGGL(k_dswiglu_epilogue<true>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F, dx,
-                       rowmax);
-  else if (T > 0)  // dX not wanted: the epilogue keeps only each row's max |dX|
-    hipLaunchKernelGGL(k_dswiglu_epilogue<false>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, preact, dy, T, F,
-                       dx, rowmax);
+  if (T > 0) {
+    // dX not wanted: the epilogue keeps only each row's max |dX|
+    const int nb = (F / 8 + 63) / 64;
+    const dim3 eg((unsigned)((T + 3) / 4)), eb(256);
+#define MTB_EPI(ST, NBV) hipLaunchKernelGGL((k_dswiglu_epilogue<ST, NBV>), eg, eb, 0, s, preact, dy, T, F, dx, rowmax)
+#define MTB_EPI_NB(ST)                  \
+  do {                                  \
+    if (nb <= 1) MTB_EPI(ST, 1);        \
+    else if (nb <= 2) MTB_EPI(ST, 2);   \
+    else MTB_EPI(ST, 4);                \
+  } while (0)
+    if (dx) MTB_EPI_NB(true);
+    else MTB_EPI_NB(false);
+#undef MTB_EPI_NB
+#undef MTB_EPI
+  }
   hipLaunchKernelGGL(k_dswiglu_reduce, dim3((unsigned)E), dim3(1024), 0, s, counts, E, T, rowmax, offs, poffs, amax,
                      row_scale, col_scale);
   // padded rows never exceed T + 15 E; tiles beyond poffs[E] exit at once
