@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mtb {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -28,6 +30,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, each
+// body its own straight-line copy.  For loops whose bodies are too large for
+// the compiler to unroll by itself: a loop left rolled indexes its register
+// arrays with a variable, and such arrays are moved to scratch memory.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 constexpr int kWave = 64;

@@ -351,12 +351,12 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
                                             uint8_t* cbase, uint32_t coff, uint8_t* sbase, uint32_t soff, uint32_t W,
                                             bool even, uint64_t n0 = 0, uint32_t klo = 0, uint32_t khi = 0) {
   const DScale dsr = dscale(Drow);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  static_for<0, 16>([&](auto I) {
+    constexpr int i = I;
     uint32_t am = absmax_bf16x8(v[i]);
     uint32_t o = lane_xor1(am);
     am = am > o ? am : o;
-    if (i >= nreal) continue;
+    if (i >= nreal) return;
     uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
     GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, tab);
     uint32_t w;
@@ -377,7 +377,7 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
     }
     *reinterpret_cast<uint32_t*>(cbase + (coff + (uint32_t)i * (W >> 1))) = w;
     if (even) sbase[soff + (uint32_t)i * (W >> 4)] = (uint8_t)sc;
-  }
+  });
 }
 
 // Columnwise operand of column pairs [P0, P1) of one thread's 8 columns x 16
@@ -392,8 +392,8 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
                                                uint2* stage_codes, ScT* stage_sc, uint64_t n0 = 0,
                                                uint64_t n_step = 0, uint32_t klo = 0, uint32_t khi = 0) {
   const DScale dsc = dscale(Dcol);
-#pragma unroll
-  for (int p = P0; p < P1; ++p) {
+  static_for<P0, P1>([&](auto PI) {
+    constexpr int p = PI;
     float z0[16], z1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -453,7 +453,7 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
     stage_codes[qstage_at(c0 + 1, m)] = make_uint2(c10, c11);
     stage_sc[qstage_at(c0, m)] = (ScT)sc0;
     stage_sc[qstage_at(c0 + 1, m)] = (ScT)sc1;
-  }
+  });
 }
 
 // One workgroup per 256 padded rows x 128 columns of dX, 1-D grid with the
