@@ -358,13 +358,25 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     tile_rows = min(kTileRows, s_offs[lo + 1] - g_base);
   }
 
-  // phase 1: source rows, expert offsets, the reciprocal table.
+  // phase 1: source rows, expert offsets and decode exponents, the reciprocal
+  // table.  The three loads go out together (clamped indices, results
+  // selected afterwards), so the phase waits for one memory round trip.
   // src_row is -1 for padding and from off_E to r_cap.
+  int* s_edexp = s_offs + 1040;  // decode exponent of each expert (E <= 1024)
   {
-    int g = g_base + tid;
-    int src = g < r_cap ? (GROUPED ? g : src_row[g]) : -1;
+    const int g = g_base + tid;
+    const int sl = GROUPED ? g : src_row[min(g, r_cap - 1)];
+    const int io = min(tid, E), ie = min(tid, E - 1);
+    const int o = offsets[io];
+    const float cs = col_scale[ie];
+    const int src = g < r_cap ? sl : -1;
     s_src[tid] = (src >= 0 && src < T) ? src : -1;
-    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+    s_offs[io] = o;  // threads past E rewrite the last entry with its own value
+    s_edexp[ie] = pow2_exponent(cs);
+    for (int i = tid + kThreads; i <= E; i += kThreads) {
+      s_offs[i] = offsets[i];
+      if (i < E) s_edexp[i] = pow2_exponent(col_scale[i]);
+    }
     for (int i = tid; i < 128; i += kThreads) s_tab[i] = rcp_entry(i);
   }
   __syncthreads();
@@ -387,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     s_live[tid] = live;
     if (live) {
       const int off = s_offs[e], len = s_offs[e + 1] - off;
-      s_dexp[tid] = pow2_exponent(col_scale[e]);
+      s_dexp[tid] = s_edexp[e];
       if (KBLOCK) {
         s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * tid;
         s_cstr[tid] = (uint32_t)(tile_rows >> 1);
@@ -402,29 +414,56 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     }
   }
 
-  // phase 2b (one row per thread): t and the tile's scale words into LDS; the
-  // rowwise scales and t go out here.
+  // phase 2b (one row per thread: t and the tile's scale words) and phase 2c
+  // (thread (cg, m): the code dwords of columns [8cg, 8cg+8) of the 16 rows
+  // of block m; a wave reads 4 rows x 64 contiguous bytes per instruction).
+  // Every load of both goes out before the first wait, at clamped indices:
+  // rows without a source read row 0 and are zeroed, a 64-column tile reads
+  // its first eight code dwords twice.  Then t and the scale words go to LDS
+  // and to the rowwise operand, and the code dwords, unchanged, to the
+  // rowwise operand.
+  const int cg = tid & 15, m = tid >> 4;
+  const int r0 = 16 * m;
+  const int gb = g_base + r0;
+  const bool live = gb < tile_end && cg * 8 < ncols;
+  uint32_t cw[16];
+  float t = 0.0f;
+  uint32_t sw0 = 0, sw1 = 0;
+  if (T > 0) {
+    const int src = s_src[tid];
+    const uint32_t srow = (uint32_t)max(src, 0);
+    const float tr = *reinterpret_cast<const float*>(rs.t + (size_t)srow * rs.tstride);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(rs.scales + (size_t)srow * rs.sstride + (col0 >> 4));
+    const uint32_t s0 = sp[0], s1 = sp[ncols > 64 ? 1 : 0];
+    int4 sv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
+    const int* sr = reinterpret_cast<const int*>(sv);
+    const uint8_t* base = rs.codes + (col0 >> 1) + 4 * (cg & ((ncols >> 3) - 1));
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(sr[i], 0) * rs.cstride);
+    if (src >= 0) {
+      t = tr;
+      sw0 = s0;
+      sw1 = ncols > 64 ? s1 : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i] = sr[i] >= 0 ? v[i] : 0u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i] = 0u;
+  }
   {
     const int g = g_base + tid;
-    const int src = s_src[tid];
-    float t = 0.0f;
-    uint32_t sw0 = 0, sw1 = 0;
-    if (src >= 0) {
-      t = *reinterpret_cast<const float*>(rs.t + (size_t)(uint32_t)src * rs.tstride);
-      const uint32_t* sp =
-          reinterpret_cast<const uint32_t*>(rs.scales + (size_t)(uint32_t)src * rs.sstride + (col0 >> 4));
-      sw0 = sp[0];
-      if (ncols > 64) sw1 = sp[1];
-    }
-    {
-      s_t[tid] = t;
-      s_tq[tid] = t * rht_in_scale(tid & 15);
-      s_sw[tid][0] = sw0;
-      s_sw[tid][1] = sw1;
-      // a block with a row of t < 2^-100 takes the two-step decode
-      uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);
-      if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
-    }
+    s_t[tid] = t;
+    s_tq[tid] = t * rht_in_scale(tid & 15);
+    s_sw[tid][0] = sw0;
+    s_sw[tid][1] = sw1;
+    // a block with a row of t < 2^-100 takes the two-step decode
+    uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);
+    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
     if (!GROUPED && g < tile_end) {
       uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
       rsc[0] = sw0;
@@ -432,38 +471,10 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
       if (ct == 0) row_t[g] = t;
     }
   }
-
-  // phase 2c: thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8)
-  // of the 16 rows of block m (a wave reads 4 rows x 64 contiguous bytes per
-  // instruction) and stores them unchanged to the rowwise operand.
-  const int cg = tid & 15, m = tid >> 4;
-  const int r0 = 16 * m;
-  const int gb = g_base + r0;
-  const bool live = gb < tile_end && cg * 8 < ncols;
-  uint32_t cw[16];
-  {
-    int4 sv[4];
+  if (!GROUPED && live) {
+    uint8_t* rc = row_codes + (size_t)gb * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
-    const int* sr = reinterpret_cast<const int*>(sv);
-    const uint8_t* base = rs.codes + (col0 >> 1) + 4 * cg;
-    if (live && T > 0) {
-      // branch-free: padding rows read row 0 and are zeroed
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int src = sr[i];
-        uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * rs.cstride);
-        cw[i] = src >= 0 ? v : 0u;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cw[i] = 0u;
-    }
-    if (!GROUPED && live) {
-      uint8_t* rc = row_codes + (size_t)gb * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(rc + (size_t)i * (uint32_t)(H >> 1)) = cw[i];
-    }
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(rc + (size_t)i * (uint32_t)(H >> 1)) = cw[i];
   }
   __syncthreads();
 
