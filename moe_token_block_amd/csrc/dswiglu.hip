@@ -500,9 +500,26 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
   const int col0 = ct * kQTileCols;
   const int ncols = min(kQTileCols, W - col0);
 
-  for (int i = tid; i <= E; i += kQThreads) {
-    s_offs[i] = offs[i];
-    s_poffs[i] = poffs[i];
+  // Offsets and the experts' decode scales (in the column staging area until
+  // the column phase): the four loads go out together at clamped indices.
+  float* s_erow = reinterpret_cast<float*>(stage_sc);  // D_row of each expert (E <= 1024)
+  float* s_ecol = s_erow + 1024;                       // D_col of each expert
+  {
+    const int io = min(tid, E), ie = min(tid, E - 1);
+    const int o = offs[io], po = poffs[io];
+    const float dr = row_scale[ie], dc = col_scale[ie];
+    s_offs[io] = o;  // threads past E rewrite the last entries with their own values
+    s_poffs[io] = po;
+    s_erow[ie] = dr;
+    s_ecol[ie] = dc;
+    for (int i = tid + kQThreads; i <= E; i += kQThreads) {
+      s_offs[i] = offs[i];
+      s_poffs[i] = poffs[i];
+      if (i < E) {
+        s_erow[i] = row_scale[i];
+        s_ecol[i] = col_scale[i];
+      }
+    }
   }
   __syncthreads();
   const int ptotal = s_poffs[E];
@@ -523,8 +540,8 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
       const int row0 = s_offs[e] + (gp - poff);                   // real row of the block's first row
       s_row0[tid] = row0;
       s_nreal[tid] = min(16, max(0, s_offs[e + 1] - row0));       // real rows of the block
-      s_drow[tid] = row_scale[e];
-      s_dcol[tid] = col_scale[e];
+      s_drow[tid] = s_erow[e];
+      s_dcol[tid] = s_ecol[e];
       s_cbase[tid] = (uint64_t)W * (uint32_t)(poff >> 1) + (uint32_t)((gp - poff) >> 1);
       s_cstr[tid] = (uint32_t)(plen >> 1);
       s_sbase[tid] = (uint64_t)W * (uint32_t)(poff >> 4) + (uint32_t)((gp - poff) >> 4);

@@ -619,10 +619,15 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_receive(const uint8_t* __res
   const int g_base = rt * kTileRows;
 
   {
+    // both loads go out together (clamped indices, results selected afterwards)
     const int g = g_base + tid;
-    const int src = g < r_cap ? src_row[g] : -1;
+    const int sl = src_row[min(g, r_cap - 1)];
+    const int io = min(tid, E);
+    const int o = offsets[io];
+    const int src = g < r_cap ? sl : -1;
     s_src[tid] = (src >= 0 && src < T) ? src : -1;
-    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+    s_offs[io] = o;  // threads past E rewrite the last entry with its own value
+    for (int i = tid + kThreads; i <= E; i += kThreads) s_offs[i] = offsets[i];
   }
   __syncthreads();
   const int tile_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
@@ -646,46 +651,51 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_receive(const uint8_t* __res
       }
     }
   }
-  {
-    const int src = s_src[tid];
-    float t = 0.0f;
-    uint32_t sw0 = 0, sw1 = 0;
-    if (src >= 0) {
-      const uint8_t* prow = packed + (size_t)(uint32_t)src * (uint32_t)row_bytes;
-      t = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
-      sw0 = sp[0];
-      if (ncols > 64) sw1 = sp[1];
-    }
-    s_t[tid] = t;
-    s_tq[tid] = t * rht_in_scale(tid & 15);
-    s_sw[tid][0] = sw0;
-    s_sw[tid][1] = sw1;
-    const uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
-    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
-  }
+  // One row per thread: t and the tile's scale words; thread (cg, m): the code
+  // dwords of columns [8cg, 8cg+8) of the 16 rows of block m.  Every load goes
+  // out before the first wait, at clamped indices (rows without a source read
+  // row 0, a 64-column tile reads its first eight code dwords twice); the
+  // results are selected afterwards.
   const int cg = tid & 15, m = tid >> 4;
   const int r0 = 16 * m;
   const int gb = g_base + r0;
   const bool live = gb < tile_end && cg * 8 < ncols;
   uint32_t cw[16];
-  {
+  float t = 0.0f;
+  uint32_t sw0 = 0, sw1 = 0;
+  if (T > 0) {
+    const int src = s_src[tid];
+    const uint8_t* prow = packed + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes;
+    const float tr = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
+    const uint32_t s0 = sp[0], s1 = sp[ncols > 64 ? 1 : 0];
     int4 sv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
     const int* sr = reinterpret_cast<const int*>(sv);
-    const uint8_t* base = packed + (col0 >> 1) + 4 * cg;
-    if (live && T > 0) {
+    const uint8_t* base = packed + (col0 >> 1) + 4 * (cg & ((ncols >> 3) - 1));
+    uint32_t v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int src = sr[i];
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes);
-        cw[i] = src >= 0 ? v : 0u;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cw[i] = 0u;
+    for (int i = 0; i < 16; ++i)
+      v[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(sr[i], 0) * (uint32_t)row_bytes);
+    if (src >= 0) {
+      t = tr;
+      sw0 = s0;
+      sw1 = ncols > 64 ? s1 : 0u;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i] = (live && sr[i] >= 0) ? v[i] : 0u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i] = 0u;
+  }
+  s_t[tid] = t;
+  s_tq[tid] = t * rht_in_scale(tid & 15);
+  s_sw[tid][0] = sw0;
+  s_sw[tid][1] = sw1;
+  {
+    const uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
+    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
   }
   __syncthreads();
 
