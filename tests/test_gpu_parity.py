@@ -253,6 +253,32 @@ def test_direct_receive_rowwise_only(dev):
     assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "rowwise-only codes")
 
 
+@pytest.mark.parametrize("tokens", [0, 50])
+def test_receives_without_routed_rows(dev, tokens):
+    """No routed row at all -- no tokens, or every slot unused (-1): the plans
+    hold only zero counts, and every receive returns cleanly with D_e = 0 and
+    the oracle's (empty) operands."""
+    h, E, A = 192, 4, 32
+    rng = np.random.default_rng(61 + tokens)
+    bits = _bits(rng.standard_normal((tokens, h)))
+    topk = np.full((tokens, 2), -1, np.int32)
+    print(f"receives without routed rows tokens={tokens}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    packed_np = onv.pack_rows(bits)
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), E, A)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    assert not plan_np["offsets"].any() and not plan_np["counts"].any()
+    assert (plan_np["src_row"] == -1).all()
+    w = types.SimpleNamespace(topk_idx=topk, num_experts=E, alignment=A)
+    _check_receive(dev, w, packed_np, mtb.ep_nvfp4_direct_receive(packed, h, plan), plan_np, h)
+    got4 = mtb.ep_mxfp4_direct_receive(packed, h, plan)
+    _check_mxfp4(got4, omx4.direct_receive(packed_np, h, topk, E, A), 0, h)
+    data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(bits, dev))
+    gd, gs = mtb.ep_mxfp8_direct_receive(data, scales, plan)
+    assert not host(gd).any() and not host(gs).any()  # every grouped row is padding
+    torch.cuda.synchronize(dev)
+
+
 @pytest.mark.parametrize("case", [
     dict(seed=31, tokens=150, hidden=256, E=5, k=2, A=16, unused=0.05, empty=[3]),
     dict(seed=32, tokens=600, hidden=4096, E=8, k=2, A=128, unused=0.0, empty=[]),
