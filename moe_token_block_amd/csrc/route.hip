@@ -191,9 +191,33 @@ __global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ i
   }
   for (int e = lane; e < E; e += 64) hist[w][e] = 0;
   __syncthreads();
+  // Counting and ranking in one pass: per 64-entry step, the lanes holding
+  // the same expert id (one ballot per id bit) elect their lowest lane, which
+  // adds the group's size to the wave's count of that expert and receives the
+  // count before it; every lane of the group takes that value plus its rank
+  // among the group's lanes.  One LDS atomic per distinct id and step, not
+  // one per entry, and the scatter below needs no further ranking.  A wave's
+  // LDS operations complete in order, so ranks follow the entries' order.
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int loc[kSingleSteps];
 #pragma unroll
-  for (int st = 0; st < kSingleSteps; ++st)
-    if (xs[st] >= 0) atomicAdd(&hist[w][xs[st]], 1);
+  for (int st = 0; st < kSingleSteps; ++st) {
+    loc[st] = 0;
+    if (st * 64 >= chunk) continue;  // wave-uniform
+    const int x = xs[st];
+    const bool valid = x >= 0;
+    uint64_t m = __ballot(valid);
+#pragma unroll 1
+    for (int b = 0; b < ebits; ++b) {
+      const uint64_t bb = __ballot(valid && ((x >> b) & 1));
+      m &= ((x >> b) & 1) ? bb : ~bb;
+    }
+    const int leader = valid ? __ffsll((unsigned long long)m) - 1 : lane;
+    int base = 0;
+    if (valid && leader == lane) base = atomicAdd(&hist[w][x], __popcll(m));
+    base = __shfl(base, leader, kWave);
+    loc[st] = base + __popcll(m & lt);
+  }
   if (any_bad) atomicOr(d_error, EP_DEVERR_EXPERT_ID);
   __syncthreads();
   int32_t cnt = 0;
@@ -224,26 +248,16 @@ __global__ __launch_bounds__(1024) void k_route_single(const IDX* __restrict__ i
   const int32_t total = scan[E - 1];
   for (int32_t r = total + tid; r < r_cap; r += 1024) src_row[r] = -1;
   __syncthreads();
-  const uint64_t lt = (1ull << lane) - 1ull;
+  // hist[w][e] is now the wave's first row of expert e: place the entries
 #pragma unroll
   for (int st = 0; st < kSingleSteps; ++st) {
     if (st * 64 >= chunk) break;  // wave-uniform
     const int i = c0 + st * 64 + lane;
     const int x = xs[st];
-    const bool valid = x >= 0;
-    uint64_t m = __ballot(valid);
-    // lanes whose expert id agrees with this lane's on every id bit
-#pragma unroll 1
-    for (int b = 0; b < ebits; ++b) {
-      uint64_t bb = __ballot(valid && ((x >> b) & 1));
-      m &= ((x >> b) & 1) ? bb : ~bb;
-    }
-    if (valid) {
-      int32_t b0 = hist[w][x];
-      int32_t d = b0 + __popcll(m & lt);
+    if (x >= 0) {
+      const int32_t d = hist[w][x] + loc[st];
       dst_row[i] = d;
       src_row[d] = i / k;
-      if ((m >> lane) == 1ull) hist[w][x] = b0 + __popcll(m);
     } else if (i < c1) {
       dst_row[i] = -1;
     }
