@@ -229,6 +229,29 @@ def test_direct_receive_edge_rows(dev):
     _check_receive(dev, w, packed_np, got, plan_np, h, exact=False)
 
 
+def test_direct_receive_tiny_expert(dev):
+    """An expert whose rows all have tiny token scales (t near 2^-110, so its
+    D_e < 2^-95 and every block of it, padding included, takes the general
+    decode and quantizer) beside an expert of ordinary rows: byte for byte."""
+    rng = np.random.default_rng(71)
+    h = 256
+    tiny = rng.standard_normal((37, h)) * 2.0 ** -100   # amax near 2^-98: t near 2^-110
+    mid = rng.standard_normal((5, h)) * 2.0 ** -80      # t near 2^-91: slow by t, ordinary D_e
+    big = rng.standard_normal((45, h))
+    bits = _bits(np.concatenate([tiny, mid, big]))
+    topk = np.concatenate([np.zeros(37), np.ones(5), np.ones(45)]).astype(np.int32)[:, None]
+    print("receive tiny expert", bits.shape, flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    packed_np = onv.pack_rows(bits)
+    assert_bytes_equal(host(packed), packed_np, "pack")
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), 2, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    assert host(got["col_scale"])[0] < 2.0 ** -95
+    w = types.SimpleNamespace(topk_idx=topk, num_experts=2, alignment=16)
+    _check_receive(dev, w, packed_np, got, plan_np, h)
+
+
 def test_direct_receive_config1(dev):
     w = workloads.config1()
     packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
