@@ -296,7 +296,9 @@ __device__ __forceinline__ MantEntry mant_entry(int j, float mD) {
 
 // Block parameters for E4M3 code sc with decode scale D = mD * 2^kD, from the
 // block's significand table; falls back to gen_block when c is tiny (P > 0)
-// or subnormal.
+// or subnormal.  FAST (D >= 2^-85): the power of c is at least
+// 2^(-9 - 85) > 2^-104, so the fallback is never taken and is left out.
+template <bool FAST = false>
 __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, const MantEntry* tab) {
   float s = e4m3_decode(sc);
   GenBlock g;
@@ -308,7 +310,7 @@ __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, 
   int ks = __builtin_amdgcn_frexp_expf(s) - 1;
   const MantEntry t = tab[(__float_as_uint(s) >> 20) & 7u];
   int kc = ks + kD + t.kadj;
-  if (kc < -104) return gen_block(sc, D);
+  if (!FAST && kc < -104) return gen_block(sc, D);
   g.r_hi = t.r_hi;
   g.r_lo = t.r_lo;
   g.scale = pow2f(kc);
@@ -317,9 +319,12 @@ __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, 
 
 // E4M3 code of fl32(fl32(a / 6) / D) * 2^-x2 for a block max a that is 2^x2
 // times the true one (x2 = 2: the unscaled RHT below).
+// FAST (D >= 2^-85): a block max below 2^-100 gives a quotient below 2^-17,
+// code 0 with or without the prescale that keeps div6 exact, so none is taken.
+template <bool FAST = false>
 __device__ __forceinline__ uint32_t gen_scale_code_x(float a, const DScale& d, int x2) {
   // D = 0 (an all-zero expert: a = 0) needs no test: its split reciprocal is 0, so the code is 0
-  bool tiny = a < 0x1p-100f;
+  const bool tiny = !FAST && a < 0x1p-100f;
   float pre = div6(tiny ? a * 0x1p64f : a);
   float q = quot_apply(pre, d.r_hi, d.r_lo);
   float y = __builtin_ldexpf(q, -d.kD - x2 - (tiny ? 64 : 0));
@@ -346,7 +351,7 @@ __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (
 // SR: stochastic codes, element (row0 + i, xcol + k) at stream position
 // n0 + i * W + k (n0 = the counter base + row0 * W + xcol: its index in the
 // [T, W] code array).
-template <bool SR = false>
+template <bool SR = false, bool FAST = false>
 __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, float Drow, const MantEntry* tab,
                                             uint8_t* cbase, uint32_t coff, uint8_t* sbase, uint32_t soff, uint32_t W,
                                             bool even, uint64_t n0 = 0, uint32_t klo = 0, uint32_t khi = 0) {
@@ -357,8 +362,8 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
     uint32_t o = lane_xor1(am);
     am = am > o ? am : o;
     if (i >= nreal) return;
-    uint32_t sc = gen_scale_code_x(__uint_as_float(am << 16), dsr, 0);
-    GenBlock gb = gen_block_tab(sc, Drow, dsr.kD, tab);
+    uint32_t sc = gen_scale_code_x<FAST>(__uint_as_float(am << 16), dsr, 0);
+    GenBlock gb = gen_block_tab<FAST>(sc, Drow, dsr.kD, tab);
     uint32_t w;
     if (!SR) {
       w = enc_first(bf16lo(v[i].x), bf16hi(v[i].x), gb);
@@ -387,7 +392,7 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
 // SR: stochastic codes, the block's row 0 in the thread's column k at stream
 // position n0 + k * n_step (its index in the columnwise code array plus the
 // counter base).
-template <int P0, int P1, bool SR = false, typename ScT>
+template <int P0, int P1, bool SR = false, bool FAST = false, typename ScT>
 __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol, const MantEntry* tab, int cg, int m,
                                                uint2* stage_codes, ScT* stage_sc, uint64_t n0 = 0,
                                                uint64_t n_step = 0, uint32_t klo = 0, uint32_t khi = 0) {
@@ -410,10 +415,10 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
       a0 = fmaxf(a0, fabsf(z0[i]));
       a1 = fmaxf(a1, fabsf(z1[i]));
     }
-    uint32_t sc0 = gen_scale_code_x(a0, dsc, 2);
-    uint32_t sc1 = gen_scale_code_x(a1, dsc, 2);
-    GenBlock g0 = gen_block_tab(sc0, Dcol, dsc.kD, tab);
-    GenBlock g1 = gen_block_tab(sc1, Dcol, dsc.kD, tab);
+    uint32_t sc0 = gen_scale_code_x<FAST>(a0, dsc, 2);
+    uint32_t sc1 = gen_scale_code_x<FAST>(a1, dsc, 2);
+    GenBlock g0 = gen_block_tab<FAST>(sc0, Dcol, dsc.kD, tab);
+    GenBlock g1 = gen_block_tab<FAST>(sc1, Dcol, dsc.kD, tab);
     // the values are 4x the transform: divide by 4 more
     g0.scale *= 4.0f;
     g1.scale *= 4.0f;
@@ -626,7 +631,10 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
   }
   if (live) {
     if (!SR) {
-      fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
+      // the block's expert has D_row >= 2^-85 (D_col = 4 D_row): the fast
+      // block quantizers give the same codes without two dormant checks
+      if (s_drow[m] >= 0x1p-85f) fc1_columnwise<0, 4, false, true>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
+      else fc1_columnwise<0, 4>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc);
     } else {
       // the thread's 8 columns are contiguous in dX (also in the recompute mapping)
       const uint64_t h0 = (uint64_t)qtile_col<RECOMPUTE>(col0, 8 * cg, W);
@@ -665,10 +673,16 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
   if (live) {
     const uint32_t rrel = (uint32_t)s_row0[m] - rbase;
     const int xcol = qtile_col<RECOMPUTE>(col0, 8 * cg, W);  // this thread's first dX column
-    fc1_rowwise<SR>(v, s_nreal[m], s_drow[m], s_tab[m][0], row_codes + (size_t)rbase * (uint32_t)(W >> 1),
-                    rrel * (uint32_t)(W >> 1) + (uint32_t)(xcol >> 1), row_scales + (size_t)rbase * (uint32_t)(W >> 4),
-                    rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4), (uint32_t)W, (cg & 1) == 0,
-                    n_base + (uint64_t)(uint32_t)s_row0[m] * (uint32_t)W + (uint32_t)xcol, klo, khi);
+    uint8_t* const rcb = row_codes + (size_t)rbase * (uint32_t)(W >> 1);
+    uint8_t* const rsb = row_scales + (size_t)rbase * (uint32_t)(W >> 4);
+    const uint32_t rco = rrel * (uint32_t)(W >> 1) + (uint32_t)(xcol >> 1);
+    const uint32_t rso = rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4);
+    const uint64_t rn0 = n_base + (uint64_t)(uint32_t)s_row0[m] * (uint32_t)W + (uint32_t)xcol;
+    if (!SR && s_drow[m] >= 0x1p-85f)
+      fc1_rowwise<false, true>(v, s_nreal[m], s_drow[m], s_tab[m][0], rcb, rco, rsb, rso, (uint32_t)W, (cg & 1) == 0);
+    else
+      fc1_rowwise<SR>(v, s_nreal[m], s_drow[m], s_tab[m][0], rcb, rco, rsb, rso, (uint32_t)W, (cg & 1) == 0, rn0, klo,
+                      khi);
   }
 }
 
