@@ -250,6 +250,19 @@ def test_direct_receive_tiny_expert(dev):
     assert host(got["col_scale"])[0] < 2.0 ** -95
     w = types.SimpleNamespace(topk_idx=topk, num_experts=2, alignment=16)
     _check_receive(dev, w, packed_np, got, plan_np, h)
+    # the K-blocked layout and the operand built from the grouped rows share the column code
+    want = orecv.direct_receive(packed_np, h, topk, 2, 16)
+    off = plan_np["offsets"].astype(np.int64)
+    n = h * int(off[-1])
+    kb = {k: torch.empty_like(v) for k, v in got.items()}
+    kb["col_scale"] = got["col_scale"].clone()
+    mtb.ep_nvfp4_direct_receive_kblock(packed, h, plan, kb)
+    wc, ws = orecv.kblock_layout(want["col_codes"][: n // 2], want["col_scales"][: n // 16], off, h)
+    assert_bytes_equal(host(kb["col_codes"])[: n // 2], wc, "K-block columnwise codes")
+    assert_bytes_equal(host(kb["col_scales"])[: n // 16], ws, "K-block columnwise scales")
+    grp = mtb.ep_nvfp4_columnwise_grouped(got, h, plan)
+    assert_bytes_equal(host(grp["col_codes"])[: n // 2], want["col_codes"][: n // 2], "grouped columnwise codes")
+    assert_bytes_equal(host(grp["col_scales"])[: n // 16], want["col_scales"][: n // 16], "grouped columnwise scales")
 
 
 def test_direct_receive_config1(dev):
