@@ -263,6 +263,14 @@ def test_direct_receive_tiny_expert(dev):
     grp = mtb.ep_nvfp4_columnwise_grouped(got, h, plan)
     assert_bytes_equal(host(grp["col_codes"])[: n // 2], want["col_codes"][: n // 2], "grouped columnwise codes")
     assert_bytes_equal(host(grp["col_scales"])[: n // 16], want["col_scales"][: n // 16], "grouped columnwise scales")
+    # and with stochastic columnwise codes
+    sr = torch.tensor([77, 3], dtype=torch.int64, device=dev)
+    srg = {k: torch.empty_like(v) for k, v in got.items()}
+    srg["col_scale"] = got["col_scale"].clone()
+    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, srg, sr)
+    want_sr = orecv.direct_receive(packed_np, h, topk, 2, 16, sr=(77, 3))
+    assert_bytes_equal(host(srg["col_codes"])[: n // 2], want_sr["col_codes"][: n // 2], "SR columnwise codes")
+    assert_bytes_equal(host(srg["col_scales"])[: n // 16], want["col_scales"][: n // 16], "SR columnwise scales")
 
 
 def test_direct_receive_config1(dev):
