@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
           v[i] = i < nreal ? t : make_uint4(0, 0, 0, 0);
         }
       } else {
-        const int F = W >> 1, j = (col0 >> 1) + 8 * (cg & 7);  // col0 = 128 ct: j0 = 64 ct
+        const int F = W >> 1;
         const bool want_b = cg >= 8;                             // this thread keeps db (else da)
         const char* pbase = reinterpret_cast<const char*>(preact + (size_t)rbase * (uint32_t)W + (col0 >> 1));
         const char* dbase = reinterpret_cast<const char*>(dy + (size_t)rbase * (uint32_t)F + (col0 >> 1));

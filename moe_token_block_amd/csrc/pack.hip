@@ -243,7 +243,8 @@ __global__ __launch_bounds__(256) void k_nvfp4_pack(const uint16_t* __restrict__
 // thread j owns blocks j, j+256, ... (NBW of them), so a 4096-wide row is one
 // block per thread; the row max goes through LDS.
 template <int NBW, bool SCATTER>
-__global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restrict__ x, int rows, int H, const RowOut o,
+__global__ __launch_bounds__(256) void k_nvfp4_pack_wg(const uint16_t* __restrict__ x, int /* rows: the grid */, int H,
+                                                      const RowOut o,
                                                       const int32_t* __restrict__ dst_row, int k, int r_cap) {
   __shared__ uint32_t red[4];
   const int tid = threadIdx.x;
@@ -441,7 +442,8 @@ __device__ __forceinline__ uint32_t fp8x4_from_bf16_tiny(uint32_t w0, uint32_t w
 }
 
 __global__ __launch_bounds__(256) void k_mxfp8_pack(const uint16_t* __restrict__ x, int64_t total_chunks,
-                                                    int H, uint8_t* __restrict__ data,
+                                                    int /* H: chunks run over the whole tensor */,
+                                                    uint8_t* __restrict__ data,
                                                     uint8_t* __restrict__ scales) {
   // one lane per 16-element chunk; chunk index runs over the whole tensor
   int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
