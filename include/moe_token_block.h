@@ -172,20 +172,24 @@ int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, i
 
 /* ---------------------------------------------------------------- receive */
 
-/* NVFP4 direct receive (P1, PR description: the receiver builds the expert
- * GEMM's grouped NVFP4 operands straight from the rows in one pass; the
- * rowwise operand reuses the sender's codes and the columnwise RHT operand is
- * quantized with a bound-derived per-expert scale; P4, description: the
- * post-RHT amax is bounded by 4x the rowwise amax).
+/* NVFP4 direct receive, from a routing plan (P1, PR description: the
+ * received rows are turned into the expert GEMM's grouped operands in a single
+ * pass -- the rowwise operand is the sender's bytes regrouped, and the
+ * columnwise operand gets an RHT and a per-expert scale derived from the token
+ * scales, so neither a BF16 copy nor a max pass over the codes is made; P4,
+ * description: the RHT output is bounded by four times the rowwise amax).
  *   packed [tokens, 9*hidden/16+4]; offsets [E+1], src_row [r_cap] from
- *   ep_route_plan (src_row values in [-1, tokens)).
+ *   ep_route_plan (src_row values in [-1, tokens)).  The plan is an input so
+ *   that one routing (the pages' cached routing, P2 review comments) serves
+ *   every receive of a step; ep_nvfp4_direct_receive_topk routes and receives
+ *   in one call.
  *   Rowwise (always): row_codes [r_cap, hidden/2], row_scales [r_cap, hidden/16],
  *   row_t [r_cap] FP32: grouped row g (< off_E) holds the code bytes, scale bytes
  *   and t of token src_row[g], zeros for padding.  Rows >= off_E untouched.
  *   Columnwise (when col_codes != NULL; col_scales and col_scale then required):
  *   D_e = 4 * max t over expert e's rows (0 if empty) -> col_scale [E];
  *   for each column h and 16-row block of expert e: y = (1/4) H16 diag(d) z
- *   (a fixed butterfly order, FP32), s = E4M3(fl32(max|y| / 6) / D_e),
+ *   (a fixed butterfly order, FP32), s = E4M3 of the exact max|y| / (6 D_e),
  *   code = E2M1 of fl32(|y| / (s D_e)).  Expert e's codes are an
  *   [hidden, P_e/2] byte matrix at byte hidden*off_e/2 of col_codes and its
  *   scales an [hidden, P_e/16] matrix at byte hidden*off_e/16 of col_scales
@@ -198,6 +202,24 @@ int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t h
                                 uint8_t* row_codes, uint8_t* row_scales, float* row_t,
                                 uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                 void* stream);
+
+/* Workspace bytes ep_nvfp4_direct_receive_topk needs (its routing plan's). */
+size_t ep_receive_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_experts);
+
+/* The direct receive in one call from the top-k indices (P1, PR description:
+ * dispatch then the one-pass receive; P1 commit messages: top_k, alignment and
+ * the index dtype are arguments): ep_route_plan into counts / offsets /
+ * dst_row / src_row (caller-owned, as for ep_route_plan), then
+ * ep_nvfp4_direct_receive on that plan.  Arguments, layouts and error words
+ * as for those two calls; workspace holds ep_receive_workspace_bytes(...)
+ * bytes.  Every argument is checked before the first launch. */
+int32_t ep_nvfp4_direct_receive_topk(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                     const void* topk_idx, int32_t idx_dtype, int64_t top_k,
+                                     int64_t num_experts, int64_t alignment, int64_t r_cap,
+                                     int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_row,
+                                     uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                     uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                     void* workspace, size_t workspace_bytes, int32_t* d_error, void* stream);
 
 /* The two halves of ep_nvfp4_direct_receive, for callers that schedule them
  * separately (e.g. to reuse D_e, or to time the one-pass kernel alone):
@@ -317,9 +339,10 @@ int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const uint8_t* row
 /* ---------------------------------------------------------------- dSwiGLU */
 
 /* Fused grouped dSwiGLU epilogue with per-expert amax, then FC1-gradient NVFP4
- * quantization without a separate amax pass (P4, description: the rowwise
- * amax is the epilogue's exact amax rounded to BF16, the columnwise post-RHT
- * amax is bounded by 4x the rowwise amax).
+ * quantization with global scales taken from that amax (P4, description: the
+ * epilogue's max of dX, rounded to BF16, serves as the rowwise amax and four
+ * times it bounds the columnwise amax after the RHT, so the quantizer makes
+ * no max pass of its own).
  *   preact [tokens, 2*ffn] BF16 = [a | b] (a = gate, first ffn columns);
  *   dy [tokens, ffn] BF16; rows are expert-major: expert e owns counts[e]
  *   consecutive rows (counts: DEVICE int32 [E], sum == tokens).

@@ -12,6 +12,6 @@ from .binding import (  # noqa: F401
     ep_nvfp4_pack, ep_nvfp4_unpack, ep_mxfp8_pack, ep_route_plan, ep_nvfp4_direct_receive,
     ep_mxfp8_direct_receive, ep_nvfp4_expert_scale, ep_nvfp4_direct_receive_scaled, dswiglu_nvfp4_quant,
     ep_nvfp4_pack_scatter, ep_nvfp4_columnwise_grouped, ep_nvfp4_direct_receive_kblock, ep_mxfp4_direct_receive,
-    ep_nvfp4_direct_receive_sr,
+    ep_nvfp4_direct_receive_sr, ep_receive_workspace_bytes, ep_nvfp4_direct_receive_topk,
     lib, LIB_PATH, EXPORTS,
 )

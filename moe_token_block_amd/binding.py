@@ -42,6 +42,9 @@ _SIGS = {
     "ep_nvfp4_unpack": (_I32, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "ep_route_plan": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "ep_nvfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_receive_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "ep_nvfp4_direct_receive_topk": (_I32, [_P, _I64, _I64, _P, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                                            _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "ep_nvfp4_expert_scale": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_scaled": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
@@ -96,13 +99,66 @@ def _dev(t):
     return t.device
 
 
-def _need(t, dtype, name, dev=None):
+def _need(t, dtype, name, dev=None, shape=None, numel=None):
+    """Checks a tensor handed to the library: dtype, contiguity, device, and its
+    size -- an exact ``shape``, or at least ``numel`` elements.  The C ABI gets
+    raw pointers, so this is the only place a buffer too small for the sizes
+    passed with it can be caught before a kernel writes past its end."""
+    if not torch.is_tensor(t):
+        raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dev is not None and t.device != dev:
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+
+
+def _row_bytes(hidden, what):
+    rb = lib().ep_nvfp4_packed_row_bytes(hidden)
+    _check(rb if rb < 0 else 0, what)
+    return rb
+
+
+def _packed(packed, hidden, dev, what):
+    """A packed-row tensor [rows, 9*hidden/16 + 4] (uint8)."""
+    _need(packed, torch.uint8, "packed", dev)
+    rb = _row_bytes(hidden, what)
+    if packed.dim() != 2 or packed.shape[1] != rb:
+        raise ValueError(f"{what}: packed has shape {tuple(packed.shape)}, rows of {rb} bytes expected "
+                         f"for hidden {hidden}")
+    return packed.shape[0]
+
+
+def _plan(plan, dev, tokens=None):
+    """Sizes of a routing plan as its tensors hold them."""
+    e, r_cap = int(plan["num_experts"]), int(plan["r_cap"])
+    _need(plan["offsets"], torch.int32, "plan offsets", dev, shape=(e + 1,))
+    _need(plan["counts"], torch.int32, "plan counts", dev, shape=(e,))
+    _need(plan["src_row"], torch.int32, "plan src_row", dev, shape=(r_cap,))
+    _need(plan["dst_row"], torch.int32, "plan dst_row", dev)
+    if tokens is not None and plan["dst_row"].shape[0] != tokens:
+        raise ValueError(f"the plan routes {plan['dst_row'].shape[0]} tokens, the input has {tokens}")
+    return e, r_cap
+
+
+def _receive_out(out, r_cap, hidden, e, dev, columnwise=True, scale_div=16, col_scale=True):
+    """Checks the grouped-operand buffers of a receive: rowwise codes / scales /
+    t for r_cap rows, columnwise codes and scales for r_cap * hidden elements,
+    the per-expert decode scales."""
+    _need(out["row_codes"], torch.uint8, "row_codes", dev, numel=r_cap * (hidden // 2))
+    _need(out["row_scales"], torch.uint8, "row_scales", dev, numel=r_cap * (hidden // scale_div))
+    if "row_t" in out:
+        _need(out["row_t"], torch.float32, "row_t", dev, numel=r_cap)
+    if columnwise:
+        _need(out["col_codes"], torch.uint8, "col_codes", dev, numel=r_cap * hidden // 2)
+        _need(out["col_scales"], torch.uint8, "col_scales", dev, numel=r_cap * hidden // scale_div)
+        if col_scale:
+            _need(out["col_scale"], torch.float32, "col_scale", dev, numel=e)
 
 
 # ------------------------------------------------------------------ helpers
@@ -136,18 +192,17 @@ def ep_nvfp4_pack(x, round_mode=EP_ROUND_NEAREST, sr_state=None, out=None):
     stochastic modes (a pre-quantized or non-BF16 input is refused)."""
     dev = _dev(x)
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
     t, h = x.shape
-    rb = lib().ep_nvfp4_packed_row_bytes(h)
-    _check(rb if rb < 0 else 0, "ep_nvfp4_pack")
+    rb = _row_bytes(h, "ep_nvfp4_pack")
     if out is None:
         out = torch.empty((t, rb), dtype=torch.uint8, device=dev)
-    _need(out, torch.uint8, "out", dev)
+    _need(out, torch.uint8, "out", dev, shape=(t, rb))
     if round_mode != EP_ROUND_NEAREST:
         if sr_state is None:
             raise ValueError("stochastic rounding needs sr_state")
-        _need(sr_state, torch.int64, "sr_state", dev)
-        if sr_state.numel() < 2:
-            raise ValueError("sr_state holds {seed, counter_base}: two int64 values")
+        _need(sr_state, torch.int64, "sr_state", dev, numel=2)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_pack(_ptr(x), t, h, _ptr(out), round_mode, _ptr(sr_state), _stream(dev)),
                "ep_nvfp4_pack")
@@ -158,14 +213,13 @@ def ep_nvfp4_unpack(packed, hidden, src_row=None, out=None):
     """Packed rows -> BF16 [rows_out, H]; with ``src_row`` (int32 [rows_out]) output
     row g decodes packed row src_row[g] (-1: zeros)."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
-    rows_in = packed.shape[0]
-    rows_out = rows_in if src_row is None else src_row.shape[0]
+    rows_in = _packed(packed, hidden, dev, "ep_nvfp4_unpack")
+    rows_out = rows_in if src_row is None else src_row.numel()
     if src_row is not None:
         _need(src_row, torch.int32, "src_row", dev)
     if out is None:
         out = torch.empty((rows_out, hidden), dtype=torch.bfloat16, device=dev)
-    _need(out, torch.bfloat16, "out", dev)
+    _need(out, torch.bfloat16, "out", dev, numel=rows_out * hidden)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_unpack(_ptr(packed), rows_in, hidden, _ptr(src_row), rows_out, _ptr(out), _stream(dev)),
                "ep_nvfp4_unpack")
@@ -177,9 +231,14 @@ def ep_mxfp8_pack(x, out=None):
     data-then-scales buffer (returned as the third element)."""
     dev = _dev(x)
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
     t, h = x.shape
+    if h % 32:
+        raise ValueError("hidden must be a multiple of 32")
     if out is None:
         out = torch.empty(t * h + t * (h // 32), dtype=torch.uint8, device=dev)
+    _need(out, torch.uint8, "out", dev, numel=t * h + t * (h // 32))
     data = out[: t * h].view(t, h)
     scales = out[t * h : t * h + t * (h // 32)].view(t, h // 32)
     with torch.cuda.device(dev):
@@ -188,25 +247,20 @@ def ep_mxfp8_pack(x, out=None):
 
 
 # ------------------------------------------------------------------ routing / receive
-def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None, workspace=None, out=None):
-    """Routing plan of topk_idx [T, k] (int32 or int64): dict of counts, offsets,
-    dst_row, src_row (device int32), d_error (device int32 [1]) and r_cap.
-    ``out``: a plan returned earlier for the same sizes, refilled in place."""
-    dev = _dev(topk_idx)
+def _topk(topk_idx):
     if topk_idx.dtype not in (torch.int32, torch.int64):
         raise TypeError("topk_idx must be int32 or int64")
-    if not topk_idx.is_contiguous():
-        raise ValueError("topk_idx must be contiguous")
-    t, k = topk_idx.shape
-    cap = ep_route_capacity(t, k, num_experts, alignment)
-    r_cap = cap if r_cap is None else r_cap
+    if not topk_idx.is_contiguous() or topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be a contiguous [tokens, top_k] tensor")
+    return EP_IDX_INT64 if topk_idx.dtype == torch.int64 else EP_IDX_INT32
+
+
+def _plan_buffers(t, k, num_experts, r_cap, dev, out, d_error):
     i32 = dict(dtype=torch.int32, device=dev)
     if out is not None:
         counts, offsets, dst_row, src_row = out["counts"], out["offsets"], out["dst_row"], out["src_row"]
         if d_error is None:
             d_error = out["d_error"]
-        if src_row.numel() != r_cap or counts.numel() != num_experts:
-            raise ValueError("out plan was made for other sizes")
     else:
         counts = torch.empty(num_experts, **i32)
         offsets = torch.empty(num_experts + 1, **i32)
@@ -214,35 +268,60 @@ def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None,
         src_row = torch.empty(r_cap, **i32)
     if d_error is None:
         d_error = torch.zeros(1, **i32)
+    _need(counts, torch.int32, "counts", dev, shape=(num_experts,))
+    _need(offsets, torch.int32, "offsets", dev, shape=(num_experts + 1,))
+    _need(dst_row, torch.int32, "dst_row", dev, numel=t * k)
+    _need(src_row, torch.int32, "src_row", dev, shape=(r_cap,))
+    _need(d_error, torch.int32, "d_error", dev, numel=1)
+    return dict(counts=counts, offsets=offsets, dst_row=dst_row, src_row=src_row, d_error=d_error, r_cap=r_cap,
+                num_experts=num_experts)
+
+
+def ep_route_plan(topk_idx, num_experts, alignment=16, r_cap=None, d_error=None, workspace=None, out=None):
+    """Routing plan of topk_idx [T, k] (int32 or int64): dict of counts, offsets,
+    dst_row, src_row (device int32), d_error (device int32 [1]) and r_cap.
+    ``out``: a plan returned earlier for the same sizes, refilled in place."""
+    dev = _dev(topk_idx)
+    idt = _topk(topk_idx)
+    t, k = topk_idx.shape
+    cap = ep_route_capacity(t, k, num_experts, alignment)
+    r_cap = cap if r_cap is None else r_cap
+    plan = _plan_buffers(t, k, num_experts, r_cap, dev, out, d_error)
     wsb = lib().ep_route_workspace_bytes(t, k, num_experts)
     if workspace is None:
         workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", dev, numel=wsb)
     with torch.cuda.device(dev):
-        _check(lib().ep_route_plan(_ptr(topk_idx), EP_IDX_INT64 if topk_idx.dtype == torch.int64 else EP_IDX_INT32,
-                                   t, k, num_experts, alignment, r_cap, _ptr(counts), _ptr(offsets), _ptr(dst_row),
-                                   _ptr(src_row), _ptr(workspace), workspace.numel(), _ptr(d_error), _stream(dev)),
+        _check(lib().ep_route_plan(_ptr(topk_idx), idt, t, k, num_experts, alignment, r_cap, _ptr(plan["counts"]),
+                                   _ptr(plan["offsets"]), _ptr(plan["dst_row"]), _ptr(plan["src_row"]),
+                                   _ptr(workspace), workspace.numel(), _ptr(plan["d_error"]), _stream(dev)),
                "ep_route_plan")
-    return dict(counts=counts, offsets=offsets, dst_row=dst_row, src_row=src_row, d_error=d_error, r_cap=r_cap,
-                num_experts=num_experts, alignment=alignment)
+    plan["alignment"] = alignment
+    return plan
+
+
+def _receive_buffers(r_cap, hidden, e, dev, columnwise=True):
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = dict(row_codes=torch.empty((r_cap, hidden // 2), **u8),
+               row_scales=torch.empty((r_cap, hidden // 16), **u8),
+               row_t=torch.empty(r_cap, dtype=torch.float32, device=dev))
+    if columnwise:
+        out.update(col_codes=torch.empty(r_cap * hidden // 2, **u8),
+                   col_scales=torch.empty(r_cap * hidden // 16, **u8),
+                   col_scale=torch.empty(e, dtype=torch.float32, device=dev))
+    return out
 
 
 def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
     """Grouped rowwise (+ RHT columnwise) NVFP4 operands from packed rows and a
     routing plan (from ``ep_route_plan``)."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
-    t = packed.shape[0]
-    e = plan["num_experts"]
-    r_cap = plan["r_cap"]
+    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive")
+    e, r_cap = _plan(plan, dev)
     if out is None:
-        u8 = dict(dtype=torch.uint8, device=dev)
-        out = dict(row_codes=torch.empty((r_cap, hidden // 2), **u8),
-                   row_scales=torch.empty((r_cap, hidden // 16), **u8),
-                   row_t=torch.empty(r_cap, dtype=torch.float32, device=dev))
-        if columnwise:
-            out.update(col_codes=torch.empty(r_cap * hidden // 2, **u8),
-                       col_scales=torch.empty(r_cap * hidden // 16, **u8),
-                       col_scale=torch.empty(e, dtype=torch.float32, device=dev))
+        out = _receive_buffers(r_cap, hidden, e, dev, columnwise)
+    columnwise = out.get("col_codes") is not None
+    _receive_out(out, r_cap, hidden, e, dev, columnwise)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_direct_receive(
             _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]), _ptr(plan["src_row"]),
@@ -252,14 +331,52 @@ def ep_nvfp4_direct_receive(packed, hidden, plan, columnwise=True, out=None):
     return out
 
 
+def ep_receive_workspace_bytes(tokens, top_k, num_experts):
+    return lib().ep_receive_workspace_bytes(tokens, top_k, num_experts)
+
+
+def ep_nvfp4_direct_receive_topk(packed, hidden, topk_idx, num_experts, alignment=16, columnwise=True, r_cap=None,
+                                 out=None, plan=None, workspace=None, d_error=None):
+    """The receive in one call from top-k indices [T, k] (int32 or int64): returns
+    (plan, operands), the plan refilled in ``plan`` if given."""
+    dev = _dev(packed)
+    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive_topk")
+    idt = _topk(topk_idx)
+    if topk_idx.device != dev or topk_idx.shape[0] != t:
+        raise ValueError("topk_idx must be [tokens, top_k] on the packed rows' device")
+    k = topk_idx.shape[1]
+    cap = ep_route_capacity(t, k, num_experts, alignment)
+    r_cap = cap if r_cap is None else r_cap
+    plan = _plan_buffers(t, k, num_experts, r_cap, dev, plan, d_error)
+    plan["alignment"] = alignment
+    if out is None:
+        out = _receive_buffers(r_cap, hidden, num_experts, dev, columnwise)
+    columnwise = out.get("col_codes") is not None
+    _receive_out(out, r_cap, hidden, num_experts, dev, columnwise)
+    wsb = lib().ep_receive_workspace_bytes(t, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", dev, numel=wsb)
+    with torch.cuda.device(dev):
+        _check(lib().ep_nvfp4_direct_receive_topk(
+            _ptr(packed), t, hidden, _ptr(topk_idx), idt, k, num_experts, alignment, r_cap, _ptr(plan["counts"]),
+            _ptr(plan["offsets"]), _ptr(plan["dst_row"]), _ptr(plan["src_row"]), _ptr(out["row_codes"]),
+            _ptr(out["row_scales"]), _ptr(out["row_t"]), _ptr(out.get("col_codes")), _ptr(out.get("col_scales")),
+            _ptr(out.get("col_scale")), _ptr(workspace), workspace.numel(), _ptr(plan["d_error"]), _stream(dev)),
+            "ep_nvfp4_direct_receive_topk")
+    return plan, out
+
+
 def ep_nvfp4_direct_receive_kblock(packed, hidden, plan, out):
     """The one-pass receive with the columnwise operand in 256-row K-blocks
     (out["col_scale"] already holding D_e, as for ep_nvfp4_direct_receive_scaled)."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
+    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive_kblock")
+    e, r_cap = _plan(plan, dev)
+    _receive_out(out, r_cap, hidden, e, dev)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_direct_receive_kblock(
-            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]),
             _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _stream(dev)),
             "ep_nvfp4_direct_receive_kblock")
@@ -271,15 +388,16 @@ def ep_mxfp4_direct_receive(packed, hidden, plan, out=None):
     per 32 elements) from NVFP4 packed rows and a routing plan whose alignment is a
     multiple of 32."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
-    r_cap = plan["r_cap"]
+    t = _packed(packed, hidden, dev, "ep_mxfp4_direct_receive")
+    e, r_cap = _plan(plan, dev)
     if out is None:
         u8 = dict(dtype=torch.uint8, device=dev)
         out = dict(row_codes=torch.empty((r_cap, hidden // 2), **u8), row_scales=torch.empty((r_cap, hidden // 32), **u8),
                    col_codes=torch.empty(r_cap * hidden // 2, **u8), col_scales=torch.empty(r_cap * hidden // 32, **u8))
+    _receive_out(out, r_cap, hidden, e, dev, scale_div=32, col_scale=False)
     with torch.cuda.device(dev):
         _check(lib().ep_mxfp4_direct_receive(
-            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan.get("alignment", 16), r_cap,
+            _ptr(packed), t, hidden, e, plan.get("alignment", 16), r_cap,
             _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _stream(dev)), "ep_mxfp4_direct_receive")
     return out
@@ -291,13 +409,19 @@ def ep_nvfp4_pack_scatter(x, plan, out=None):
     zeroed): the same bytes as ep_nvfp4_pack followed by the rowwise receive."""
     dev = _dev(x)
     _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
     t, h = x.shape
-    r_cap, e = plan["r_cap"], plan["num_experts"]
+    _row_bytes(h, "ep_nvfp4_pack_scatter")
+    e, r_cap = _plan(plan, dev, tokens=t)
     k = plan["dst_row"].shape[1] if plan["dst_row"].dim() == 2 else 1
+    if plan["dst_row"].numel() != t * k:
+        raise ValueError("plan dst_row must hold tokens * top_k entries")
     if out is None:
         u8 = dict(dtype=torch.uint8, device=dev)
         out = dict(row_codes=torch.empty((r_cap, h // 2), **u8), row_scales=torch.empty((r_cap, h // 16), **u8),
                    row_t=torch.empty(r_cap, dtype=torch.float32, device=dev))
+    _receive_out(out, r_cap, h, e, dev, columnwise=False)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_pack_scatter(_ptr(x), t, h, k, _ptr(plan["dst_row"]), e, r_cap, _ptr(plan["counts"]),
                                            _ptr(plan["offsets"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
@@ -310,11 +434,16 @@ def ep_nvfp4_columnwise_grouped(rowwise, hidden, plan, out=None):
     (``rowwise``: dict with row_codes, row_scales, row_t): the same bytes as the
     direct receive's columnwise outputs."""
     dev = _dev(rowwise["row_codes"])
-    r_cap, e = plan["r_cap"], plan["num_experts"]
+    _row_bytes(hidden, "ep_nvfp4_columnwise_grouped")
+    e, r_cap = _plan(plan, dev)
+    _receive_out(rowwise, r_cap, hidden, e, dev, columnwise=False)
     if out is None:
         u8 = dict(dtype=torch.uint8, device=dev)
         out = dict(col_codes=torch.empty(r_cap * hidden // 2, **u8), col_scales=torch.empty(r_cap * hidden // 16, **u8),
                    col_scale=torch.empty(e, dtype=torch.float32, device=dev))
+    _need(out["col_codes"], torch.uint8, "col_codes", dev, numel=r_cap * hidden // 2)
+    _need(out["col_scales"], torch.uint8, "col_scales", dev, numel=r_cap * hidden // 16)
+    _need(out["col_scale"], torch.float32, "col_scale", dev, numel=e)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_columnwise_grouped(
             _ptr(rowwise["row_codes"]), _ptr(rowwise["row_scales"]), _ptr(rowwise["row_t"]), hidden, e, r_cap,
@@ -326,12 +455,13 @@ def ep_nvfp4_columnwise_grouped(rowwise, hidden, plan, out=None):
 def ep_nvfp4_expert_scale(packed, hidden, plan, col_scale=None):
     """D_e = 4 * max t over each expert's rows -> float32 [E] (the first half of the receive)."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
-    e = plan["num_experts"]
+    t = _packed(packed, hidden, dev, "ep_nvfp4_expert_scale")
+    e, r_cap = _plan(plan, dev)
     if col_scale is None:
         col_scale = torch.empty(e, dtype=torch.float32, device=dev)
+    _need(col_scale, torch.float32, "col_scale", dev, numel=e)
     with torch.cuda.device(dev):
-        _check(lib().ep_nvfp4_expert_scale(_ptr(packed), packed.shape[0], hidden, e, plan["r_cap"],
+        _check(lib().ep_nvfp4_expert_scale(_ptr(packed), t, hidden, e, r_cap,
                                            _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(col_scale),
                                            _stream(dev)), "ep_nvfp4_expert_scale")
     return col_scale
@@ -340,10 +470,12 @@ def ep_nvfp4_expert_scale(packed, hidden, plan, col_scale=None):
 def ep_nvfp4_direct_receive_scaled(packed, hidden, plan, out):
     """The one-pass receive kernel alone, with out["col_scale"] already holding D_e."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
+    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive_scaled")
+    e, r_cap = _plan(plan, dev)
+    _receive_out(out, r_cap, hidden, e, dev)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_direct_receive_scaled(
-            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]),
             _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _stream(dev)),
             "ep_nvfp4_direct_receive_scaled")
@@ -354,11 +486,13 @@ def ep_nvfp4_direct_receive_sr(packed, hidden, plan, out, sr_state):
     """The one-pass receive with stochastic columnwise codes; out["col_scale"] must
     hold D_e (ep_nvfp4_expert_scale); sr_state: device int64 [seed, counter_base]."""
     dev = _dev(packed)
-    _need(packed, torch.uint8, "packed", dev)
-    _need(sr_state, torch.int64, "sr_state", dev)
+    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive_sr")
+    e, r_cap = _plan(plan, dev)
+    _receive_out(out, r_cap, hidden, e, dev)
+    _need(sr_state, torch.int64, "sr_state", dev, numel=2)
     with torch.cuda.device(dev):
         _check(lib().ep_nvfp4_direct_receive_sr(
-            _ptr(packed), packed.shape[0], hidden, plan["num_experts"], plan["r_cap"], _ptr(plan["offsets"]),
+            _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]),
             _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _ptr(sr_state), _stream(dev)),
             "ep_nvfp4_direct_receive_sr")
@@ -366,13 +500,20 @@ def ep_nvfp4_direct_receive_sr(packed, hidden, plan, out, sr_state):
 
 
 def ep_mxfp8_direct_receive(data, scales, plan, out=None):
+    """Grouped MXFP8 rows: grouped row g holds the data and scale bytes of token
+    src_row[g] (zero bytes for padding)."""
     dev = _dev(data)
     _need(data, torch.uint8, "data", dev)
+    if data.dim() != 2 or data.shape[1] % 32:
+        raise ValueError("data must be [tokens, hidden] with hidden a multiple of 32")
     t, h = data.shape
-    r_cap = plan["r_cap"]
+    _need(scales, torch.uint8, "scales", dev, shape=(t, h // 32))
+    _, r_cap = _plan(plan, dev)
     if out is None:
         out = (torch.empty((r_cap, h), dtype=torch.uint8, device=dev),
                torch.empty((r_cap, h // 32), dtype=torch.uint8, device=dev))
+    _need(out[0], torch.uint8, "grouped data", dev, numel=r_cap * h)
+    _need(out[1], torch.uint8, "grouped scales", dev, numel=r_cap * (h // 32))
     with torch.cuda.device(dev):
         _check(lib().ep_mxfp8_direct_receive(_ptr(data), _ptr(scales), t, h, r_cap, _ptr(plan["src_row"]),
                                              _ptr(out[0]), _ptr(out[1]), _stream(dev)), "ep_mxfp8_direct_receive")
@@ -380,17 +521,28 @@ def ep_mxfp8_direct_receive(data, scales, plan, out=None):
 
 
 # ------------------------------------------------------------------ dSwiGLU
-def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None):
-    """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
-    ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors.
-    ``materialize_dx=False``: no BF16 dX is written (out["dx"] is None); the
-    quantizer recomputes dX from preact and dy.  ``sr_state`` (device int64
-    [seed, counter_base]): stochastic FC1-gradient codes."""
+def _dswiglu_out(out, t, f, e, dev):
+    cap = t + 15 * e
+    if out["dx"] is not None:
+        _need(out["dx"], torch.bfloat16, "dx", dev, numel=t * 2 * f)
+    for name, n in (("amax", e), ("row_scale", e), ("col_scale", e)):
+        _need(out[name], torch.float32, name, dev, numel=n)
+    _need(out["row_codes"], torch.uint8, "row_codes", dev, numel=t * f)
+    _need(out["row_scales"], torch.uint8, "row_scales", dev, numel=t * (2 * f // 16))
+    _need(out["col_codes"], torch.uint8, "col_codes", dev, numel=2 * f * cap // 2)
+    _need(out["col_scales"], torch.uint8, "col_scales", dev, numel=2 * f * cap // 16)
+
+
+def _dswiglu_args(preact, dy, counts, out, materialize_dx):
     dev = _dev(preact)
-    _need(preact, torch.bfloat16, "preact", dev)
     _need(dy, torch.bfloat16, "dy", dev)
-    _need(counts, torch.int32, "counts", dev)
+    if dy.dim() != 2:
+        raise ValueError("dy must be [tokens, ffn]")
     t, f = dy.shape
+    _need(preact, torch.bfloat16, "preact", dev, shape=(t, 2 * f))
+    _need(counts, torch.int32, "counts", dev)
+    if counts.dim() != 1:
+        raise ValueError("counts must be [num_experts]")
     e = counts.shape[0]
     cap = t + 15 * e
     if out is None:
@@ -401,16 +553,28 @@ def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materializ
                    row_codes=torch.empty((t, f), **u8), row_scales=torch.empty((t, 2 * f // 16), **u8),
                    row_scale=torch.empty(e, **f32), col_codes=torch.empty(2 * f * cap // 2, **u8),
                    col_scales=torch.empty(2 * f * cap // 16, **u8), col_scale=torch.empty(e, **f32))
+    _dswiglu_out(out, t, f, e, dev)
+    args = (_ptr(preact), _ptr(dy), t, f, _ptr(counts), e, _ptr(out["dx"]), _ptr(out["amax"]),
+            _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]))
+    return dev, t, e, out, args
+
+
+def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None):
+    """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
+    ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors.
+    ``materialize_dx=False``: no BF16 dX is written (out["dx"] is None); the
+    quantizer recomputes dX from preact and dy.  ``sr_state`` (device int64
+    [seed, counter_base]): stochastic FC1-gradient codes."""
+    dev, t, e, out, args = _dswiglu_args(preact, dy, counts, out, materialize_dx)
     wsb = lib().dswiglu_workspace_bytes(t, e)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", dev, numel=wsb)
     with torch.cuda.device(dev):
-        args = (_ptr(preact), _ptr(dy), t, f, _ptr(counts), e, _ptr(out["dx"]), _ptr(out["amax"]),
-                _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
-                _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]),
-                _ptr(workspace), workspace.numel())
+        args = args + (_ptr(workspace), workspace.numel())
         if sr_state is not None:
-            _need(sr_state, torch.int64, "sr_state", dev)
+            _need(sr_state, torch.int64, "sr_state", dev, numel=2)
             _check(lib().dswiglu_nvfp4_quant_sr(*args, _ptr(sr_state), _stream(dev)), "dswiglu_nvfp4_quant_sr")
             return out
         _check(lib().dswiglu_nvfp4_quant(*args, _stream(dev)), "dswiglu_nvfp4_quant")

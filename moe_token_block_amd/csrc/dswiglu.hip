@@ -1,8 +1,8 @@
 // Grouped dSwiGLU epilogue with per-expert amax, then FC1-gradient NVFP4
-// quantization that uses that amax instead of an amax pass (P4, description:
-// the rowwise amax is the epilogue's exact amax rounded to BF16, the
-// post-RHT columnwise amax is bounded by 4x the rowwise amax, the separate
-// grouped amax pass is skipped).
+// quantization that takes its global scales from that amax (P4, description:
+// the epilogue already sees every dX value, so its max -- rounded to BF16 --
+// is the rowwise amax, and four times it bounds the columnwise amax after the
+// RHT; the quantizer then needs no max pass of its own).
 //
 // Launch 1 (epilogue): one wave per token row; per pair (a_j, b_j, dy_j):
 //   s = sigmoid(a), da = dy*b*s*(1 + a*(1-s)), db = dy*a*s in FP32 -> BF16;
@@ -10,11 +10,11 @@
 //   per row: no atomics, no contention).
 // Launch 2 (reduce): one workgroup per expert: the expert row offsets (plain
 //   and 16-padded) from the device counts, amax_e = max over its rows, and
-//   D_row = amax/2688, D_col = 4 * D_row.
+//   D_row = fl32(amax/2688), D_col = fl32(4*amax/2688) (= 4*D_row unless D_row is subnormal).
 // Launch 3 (quant): one workgroup per 256 padded rows x 128 columns, as the
 //   direct receive: thread (cg, m) owns 8 columns x one 16-row block; the
 //   rowwise operand (per-expert scale D_row = amax/2688) and the RHT
-//   columnwise operand (D_col = 4*D_row) come out of the same load of dX.
+//   columnwise operand (D_col) come out of the same load of dX.
 #include "common.h"
 #include "launch.h"
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(1024) void k_dswiglu_reduce(const int32_t* __restri
     float D = am / kTokenBound;     // fl32(amax / 2688)
     amax[e] = am;
     row_scale[e] = D;
-    col_scale[e] = 4.0f * D;        // = fl32(4 * amax / 2688) exactly
+    col_scale[e] = (4.0f * am) / kTokenBound;  // fl32(4 * amax / 2688): 4 * D only while D is a normal float
   }
 }
 
@@ -226,16 +226,6 @@ __device__ __forceinline__ DScale dscale(float D) {
   return d;
 }
 
-// E4M3 code of fl32(fl32(a / 6) / D) for a block max a (D > 0).
-__device__ __forceinline__ uint32_t gen_scale_code(float a, const DScale& d) {
-  if (!(d.D > 0.0f)) return 0u;
-  bool tiny = a < 0x1p-100f;
-  float pre = div6(tiny ? a * 0x1p64f : a);                 // fl32(a/6) * 2^(64 if tiny)
-  float q = quot_apply(pre, d.r_hi, d.r_lo);                // ~ pre / m_D
-  float y = __builtin_ldexpf(q, -d.kD - (tiny ? 64 : 0));   // / 2^kD, exact unless it underflows
-  return e4m3_encode(fminf(y, 448.0f));
-}
-
 // Block parameters for codes of x / c, c = fl32(s * D): split reciprocal of
 // c's significand (times 2^P) and the converter scale 2^(kc + P).
 struct GenBlock {
@@ -317,17 +307,28 @@ __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, 
   return g;
 }
 
-// E4M3 code of fl32(fl32(a / 6) / D) * 2^-x2 for a block max a that is 2^x2
-// times the true one (x2 = 2: the unscaled RHT below).
+// E4M3 code of fl32(fl32(a' / 6) / D) for a block max a = 2^x2 * a' (x2 = 2:
+// the unscaled RHT below), each fl32 an IEEE binary32 rounding.  For a block
+// max below 2^-100, a' / 6 may fall below FP32's normal range, where the first
+// rounding is on the subnormal grid: it is taken by the correctly rounded
+// division, and its result (at most 24 bits) scaled by 2^64 before the
+// quotient by D, which is then exact to the last bit as in the normal range.
+// Elsewhere div6 gives the same fl32(a / 6), and 2^x2 * fl32(a' / 6) =
+// fl32(a / 6) exactly.
 // FAST (D >= 2^-85): a block max below 2^-100 gives a quotient below 2^-17,
-// code 0 with or without the prescale that keeps div6 exact, so none is taken.
+// code 0 whichever way a / 6 is rounded, so the tiny path is left out.
 template <bool FAST = false>
 __device__ __forceinline__ uint32_t gen_scale_code_x(float a, const DScale& d, int x2) {
   // D = 0 (an all-zero expert: a = 0) needs no test: its split reciprocal is 0, so the code is 0
   const bool tiny = !FAST && a < 0x1p-100f;
-  float pre = div6(tiny ? a * 0x1p64f : a);
+  float pre;
+  if (tiny) {
+    pre = (__builtin_ldexpf(a, -x2) / 6.0f) * 0x1p64f;   // fl32(a' / 6), subnormal or not, times 2^64
+  } else {
+    pre = div6(a);
+  }
   float q = quot_apply(pre, d.r_hi, d.r_lo);
-  float y = __builtin_ldexpf(q, -d.kD - x2 - (tiny ? 64 : 0));
+  float y = __builtin_ldexpf(q, -d.kD - (tiny ? 64 : x2));
   return e4m3_encode(fminf(y, 448.0f));
 }
 
@@ -774,3 +775,4 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t
   return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
                             col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, stream);
 }
+

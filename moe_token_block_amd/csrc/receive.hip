@@ -1,9 +1,10 @@
-// NVFP4 direct receive for gfx950 (P1, PR description: the receiver builds the
-// expert GEMM's grouped NVFP4 operands straight from the packed rows in one
-// pass -- the rowwise operand reuses the sender's codes, the columnwise RHT
-// operand is quantized with a bound-derived per-expert scale, so there is no
-// BF16 round trip and no amax pass; P4, description: the post-RHT amax is
-// bounded by 4x the rowwise amax).
+// NVFP4 direct receive for gfx950 (P1, PR description: the receiving side
+// produces both grouped operands of the expert GEMM from the packed rows it is
+// handed -- the rowwise one by copying the sender's bytes into expert order,
+// the columnwise one by decoding, applying the RHT and re-quantizing against a
+// per-expert scale computed from the token scales alone, so neither a BF16
+// copy of the rows nor a max pass over them is needed; P4, description: four
+// times the rowwise amax bounds the RHT output).
 //
 // Launch 1 (k_expert_scale): D_e = 4 * max t over expert e's rows.  It reads
 // only the 4-byte token scales, not the codes: no amax pass.
@@ -1006,4 +1007,30 @@ MTB_EXPORT int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens
                      (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, col_codes, col_scales);
   return launch_status();
+}
+
+MTB_EXPORT size_t ep_receive_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_experts) {
+  return ep_route_workspace_bytes(tokens, top_k, num_experts);
+}
+
+// The receive from the top-k indices in one call: the routing plan, then D_e
+// and the grouped operands.  Every argument of both halves is checked before
+// the first launch.
+MTB_EXPORT int32_t ep_nvfp4_direct_receive_topk(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                                const void* topk_idx, int32_t idx_dtype, int64_t top_k,
+                                                int64_t num_experts, int64_t alignment, int64_t r_cap, int32_t* counts,
+                                                int32_t* offsets, int32_t* dst_row, int32_t* src_row,
+                                                uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                                uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                                void* workspace, size_t workspace_bytes, int32_t* d_error,
+                                                void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t) return EP_ERR_NULL;
+  if (col_codes && (!col_scales || !col_scale)) return EP_ERR_NULL;
+  st = ep_route_plan(topk_idx, idx_dtype, tokens, top_k, num_experts, alignment, r_cap, counts, offsets, dst_row,
+                     src_row, workspace, workspace_bytes, d_error, stream);
+  if (st != EP_OK) return st;
+  return ep_nvfp4_direct_receive(packed, tokens, hidden, num_experts, r_cap, offsets, src_row, row_codes, row_scales,
+                                 row_t, col_codes, col_scales, col_scale, stream);
 }

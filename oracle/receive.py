@@ -27,31 +27,49 @@ from .routing import route_plan
 
 
 # ------------------------------------------------------------------ shared columnwise quantizer
-def quantize_blocks(y, D, mode, words=None):
-    """Quantize post-RHT blocks y [..., 16] (float32) with global decode scale D.
+def block_scale_codes(a, D, mode):
+    """E4M3 scale codes of blocks with post-RHT maxima ``a`` (float32, >= 0).
 
-    a = max |y_i| over the block; s = E4M3(fl32(fl32(a / 6) / D)).
-    mode "pow2" (R16; D a power of two): index = E2M1 rounding (R2) of
-        v = fl32(|y| / (s * D)), the exact quotient rounded once to float32.
-    mode "fp32" (R19/R20; D any float32): c = fl32(s * D), v = fl32(|y| / c).
-    D = 0, or s = 0, gives magnitude index 0.  The code's sign is y's sign bit.
+    mode "pow2" (R16; D a power of two, the bound-derived per-expert decode
+        scale): s = E4M3 round-to-nearest-even of the exact a / (6 * D).  In
+        float64, a / 6 is within 2^-53 (relative) of the exact quotient, which
+        is never closer than about 2^-26 to an E4M3 tie (a has 24 bits, a tie
+        5), and the division by the power of two D is exact: so the float64
+        value rounds to E4M3 exactly as the exact one does.
+    mode "fp32" (R19/R20; D any float32): s = E4M3(fl32(fl32(a / 6) / D)),
+        fl32 being IEEE binary32 with gradual underflow, as written.
+    D = 0 gives code 0.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    D32 = np.float32(D)
+    if not D32 > 0:
+        return np.zeros(a.shape, dtype=np.uint8)
+    if mode == "pow2":
+        return F.e4m3_encode(a.astype(np.float64) / 6.0 / float(D32))
+    if mode == "fp32":
+        with np.errstate(under="ignore", over="ignore"):
+            pre = (a / np.float32(6.0)) / D32             # two float32 roundings, as written
+        return F.e4m3_encode(pre.astype(np.float64))
+    raise ValueError(mode)
+
+
+def block_codes(y, s_code, D, mode, words=None):
+    """E2M1 codes of post-RHT values y [..., 16] (float32) given each block's
+    scale code ``s_code`` [...] and the global decode scale D.
+
+    mode "pow2" (R16): index = E2M1 rounding (R2) of v = fl32(|y| / (s * D)),
+        the exact quotient rounded once to float32 (s * D is exact in float64).
+    mode "fp32" (R19/R20): c = fl32(s * D), v = fl32(|y| / c).
+    s = 0 (or D = 0) gives magnitude index 0.  The code's sign is y's sign bit.
     ``words`` (R24): 32-bit random words, one per element (y's shape); the
     index is then the carry-form stochastic rounding of v (R8b) instead of R2.
-    The scales are the same either way.
-    Returns (codes uint8 [..., 16], scale codes uint8 [...]).
     """
     y = np.asarray(y, dtype=np.float32)
     D32 = np.float32(D)
-    a = np.abs(y).max(axis=-1)
-    if D32 > 0:
-        pre = (a / np.float32(6.0)) / D32                 # two float32 roundings, as written
-        s_code = F.e4m3_encode(pre.astype(np.float64))
-    else:
-        s_code = np.zeros(a.shape, dtype=np.uint8)
     s_val = F.e4m3_decode(s_code)
     ay = np.abs(y)
     ok = (s_val > 0)[..., None] & np.ones(y.shape, dtype=bool)
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore", under="ignore"):
         if mode == "pow2":
             q = ay.astype(np.float64) / (s_val[..., None] * float(D32))
             v = q.astype(np.float32)
@@ -66,7 +84,17 @@ def quantize_blocks(y, D, mode, words=None):
     else:
         idx = nvfp4.stochastic_e2m1_index_carry(v.astype(np.float64), np.asarray(words).reshape(v.shape))
     sign = (y.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
-    return (sign << np.uint8(3)) | idx, s_code
+    return (sign << np.uint8(3)) | idx
+
+
+def quantize_blocks(y, D, mode, words=None):
+    """Quantize post-RHT blocks y [..., 16] (float32) with global decode scale D:
+    a = max |y_i| over the block, the scale by ``block_scale_codes``, the codes
+    by ``block_codes``.  Returns (codes uint8 [..., 16], scale codes uint8 [...]).
+    """
+    y = np.asarray(y, dtype=np.float32)
+    s_code = block_scale_codes(np.abs(y).max(axis=-1), D, mode)
+    return block_codes(y, s_code, D, mode, words), s_code
 
 
 def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None):

@@ -57,7 +57,3 @@ def route_plan(topk_idx, num_experts, alignment, r_cap=None):
                 dst_row=dst.reshape(t, k).astype(np.int32), src_row=src.astype(np.int32),
                 error=error)
 
-
-def expert_of_row(offsets, g):
-    """Expert that owns grouped row g (offsets [E+1])."""
-    return int(np.searchsorted(offsets, g, side="right") - 1)

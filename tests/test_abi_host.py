@@ -99,6 +99,15 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 32, 64, P, P, P, P, N, P, N) == -1   # col_codes NULL
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 32, 64, N, P, P, P, P, P, N) == -1   # offsets NULL
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, P, 4, N) == -7
+    # the one-call receive checks both halves before its first launch
+    R = (P, P, P, P, P, P, P, P, P, P)   # counts .. col_scale
+    assert lib.ep_nvfp4_direct_receive_topk(P, 10, 128, P, 0, 2, 4, 16, 59, *R, P, 1 << 20, P, N) == -4  # r_cap
+    assert lib.ep_nvfp4_direct_receive_topk(P, 10, 128, P, 0, 2, 4, 24, 100, *R, P, 1 << 20, P, N) == -3
+    assert lib.ep_nvfp4_direct_receive_topk(P, 10, 100, P, 0, 2, 4, 16, 80, *R, P, 1 << 20, P, N) == -2
+    assert lib.ep_nvfp4_direct_receive_topk(P, 10, 128, P, 0, 2, 4, 16, 80, P, P, P, P, N, P, P, P, P, P,
+                                            P, 1 << 20, P, N) == -1                                   # row_codes
+    assert lib.ep_nvfp4_direct_receive_topk(P, 10, 128, P, 0, 2, 4, 16, 80, *R, P, 4, P, N) == -7     # workspace
+    assert lib.ep_receive_workspace_bytes(10, 2, 4) == lib.ep_route_workspace_bytes(10, 2, 4)
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, ctypes.c_void_p(0x1008), 4096, N) == -7  # misaligned
 
 

@@ -112,8 +112,23 @@ def _check_dispatch(dev, w, name, sr=None, rng_seed=0, n_rows=96, n_col_samples=
 
 def test_config2_nvfp4_and_mxfp8(dev):
     w = workloads.config2()
-    _, plan, want = _check_dispatch(dev, w, "config2", rng_seed=2)
+    packed, plan, want = _check_dispatch(dev, w, "config2", rng_seed=2)
     assert want["counts"][7] == 0
+    # the whole tensors: the packed rows and every byte of the grouped operands
+    packed_np = onv.pack_rows(w.x_bits)
+    assert_bytes_equal(host(packed), packed_np, "config2 pack (whole tensor)")
+    full = orecv.direct_receive(packed_np, 4096, w.topk_idx, 8, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, 4096, plan)
+    off = int(full["offsets"][-1])
+    for key in ("row_codes", "row_scales"):
+        assert_bytes_equal(host(got[key])[:off], full[key][:off], f"config2 {key} (whole tensor)")
+    assert_bytes_equal(host(got["row_t"])[:off].view(np.uint32), full["row_t"][:off].view(np.uint32),
+                       "config2 row_t (whole tensor)")
+    n = 4096 * off
+    assert_bytes_equal(host(got["col_scales"])[: n // 16], full["col_scales"][: n // 16],
+                       "config2 columnwise scales (whole tensor)")
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], full["col_codes"][: n // 2],
+                       "config2 columnwise codes (whole tensor)")
     data, scales, _ = mtb.ep_mxfp8_pack(bf16_dev(w.x_bits, dev))
     wd, ws = omx.pack_rows(w.x_bits)
     assert_bytes_equal(host(data), wd, "config2 MXFP8 data")
@@ -128,6 +143,34 @@ def test_config2_nvfp4_and_mxfp8(dev):
 def test_config3_dsv3_share(dev):
     w = workloads.config3()
     packed, plan, want = _check_dispatch(dev, w, "config3", rng_seed=3)
+    H = 7168
+    got = mtb.ep_nvfp4_direct_receive(packed, H, plan)
+    # the whole rowwise operand is the gather of the packed rows (whose sampled rows
+    # equal the oracle's above): a property that holds at any size
+    src_all = want["src_row"].astype(np.int64)
+    off_all = want["offsets"].astype(np.int64)
+    pk = host(packed)
+    ok = src_all[: off_all[-1]] >= 0
+    rows = np.zeros((int(off_all[-1]), pk.shape[1]), dtype=np.uint8)
+    rows[ok] = pk[src_all[: off_all[-1]][ok]]
+    assert_bytes_equal(host(got["row_codes"])[: off_all[-1]], rows[:, : H // 2], "config3 rowwise codes (whole)")
+    assert_bytes_equal(host(got["row_scales"])[: off_all[-1]], rows[:, H // 2: H // 2 + H // 16],
+                       "config3 rowwise scales (whole)")
+    assert_bytes_equal(host(got["row_t"])[: off_all[-1]].view(np.uint32),
+                       rows[:, H // 2 + H // 16:].copy().view(np.uint32).reshape(-1), "config3 row t (whole)")
+    # every column block of one whole expert against the oracle, from the seeded inputs
+    e = 11
+    c = int(want["counts"][e])
+    erows = src_all[off_all[e]: off_all[e] + c]
+    ep = onv.pack_rows(w.x_bits[erows])
+    D = np.float32(orecv.expert_decode_scale(onv.split_rows(ep, H)[2]))
+    cc, cs = orecv.columnwise_operand(onv.decode_exact(ep, H), c, D, "pow2",
+                                      padded_rows=int(off_all[e + 1] - off_all[e]))
+    p = int(off_all[e + 1] - off_all[e])
+    gcc = host(got["col_codes"][H * int(off_all[e]) // 2: H * int(off_all[e + 1]) // 2]).reshape(H, p // 2)
+    gcs = host(got["col_scales"][H * int(off_all[e]) // 16: H * int(off_all[e + 1]) // 16]).reshape(H, p // 16)
+    assert_bytes_equal(gcs, cs, f"config3 columnwise scales of expert {e} (whole)")
+    assert_bytes_equal(gcc, cc, f"config3 columnwise codes of expert {e} (whole)")
     # unpack of the received rows (grouped order) on sampled rows
     off = int(want["offsets"][-1])
     src = want["src_row"][:off]
@@ -181,12 +224,12 @@ def test_config5_dswiglu(dev):
         c, s, _ = odsw.rowwise_quant(dx[rows[sel]], np.array([sel.sum()]), am[e:e + 1])
         wc[sel] = F.unpack_nibbles(c)
         wsc[sel] = s
-    tolerant_codes(rc, wc, rs, wsc, "config5 rowwise (sampled rows)")
+    assert_bytes_equal(rs, wsc, "config5 rowwise scales (sampled rows)")
+    assert_bytes_equal(rc, wc, "config5 rowwise codes (sampled rows)")
     poff = odsw.expert_offsets(w.counts, 16)
     W = 4096
     gc_all = host(out["col_codes"])
     gs_all = host(out["col_scales"])
-    n_bad = 0
     for e in range(8):
         c = int(w.counts[e])
         if c == 0:
@@ -206,6 +249,5 @@ def test_config5_dswiglu(dev):
             idx = (base + np.arange(c0, c0 + 64)[:, None] * (p // 2) + np.arange(8 * b, 8 * b + 8)[None, :])
             gcodes = F.unpack_nibbles(gc_all[idx.reshape(-1)].reshape(64, 8))
             sidx = W * int(poff[e]) // 16 + np.arange(c0, c0 + 64) * (p // 16) + b
-            n_bad += tolerant_codes(gcodes, codes.reshape(64, 16), gs_all[sidx].reshape(64, 1), sc.reshape(64, 1),
-                                    f"config5 columnwise e={e} b={b}", frac=1e-2)[0]
-    assert n_bad <= 2
+            assert_bytes_equal(gs_all[sidx].reshape(64, 1), sc.reshape(64, 1), f"config5 columnwise scales e={e} b={b}")
+            assert_bytes_equal(gcodes, codes.reshape(64, 16), f"config5 columnwise codes e={e} b={b}")

@@ -226,7 +226,58 @@ def test_direct_receive_edge_rows(dev):
     got = mtb.ep_nvfp4_direct_receive(packed, h, plan)
     plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
     w = types.SimpleNamespace(topk_idx=topk, num_experts=4, alignment=16)
-    _check_receive(dev, w, packed_np, got, plan_np, h, exact=False)
+    _check_receive(dev, w, packed_np, got, plan_np, h)
+
+
+def _tiny_max_rows(seed, h=256):
+    """Experts whose rows all have amax below 2^-110 (so D_e is 2^-122 .. 2^-135),
+    with 16-row blocks whose post-RHT max a has a / 6 below FP32's normal range:
+    the corner where the block-scale rule's rounding of a / 6 is on FP32's
+    subnormal grid.  Each expert's first row sets its D_e."""
+    rng = np.random.default_rng(seed)
+    rows, ex = [], []
+    for e, (lead, n, lo, hi) in enumerate([(-116, 64, -134, -121), (-113, 48, -134, -121), (-120, 80, -134, -121),
+                                           (-127.5, 512, -133, -127.5), (-126.7, 512, -133, -127)]):
+        r = rng.standard_normal((n, h)) * 2.0 ** rng.uniform(lo, hi, (n, 1))
+        r[0] = rng.standard_normal(h)
+        r[0] *= 2.0 ** lead / np.abs(r[0]).max()
+        rows.append(r)
+        ex += [e] * n
+    return _bits(np.concatenate(rows)), np.array(ex, np.int32)[:, None]
+
+
+def test_direct_receive_tiny_max_corner(dev):
+    """Columnwise blocks with a / 6 below FP32's normal range (R16: the scale is
+    E4M3 of the exact a / (6 D_e)), compared byte for byte; the oracle confirms
+    that thousands of such blocks have a nonzero scale."""
+    from oracle.rht import rht16
+    bits, topk = _tiny_max_rows(5)
+    h, E = bits.shape[1], 5
+    packed_np = onv.pack_rows(bits)
+    want = orecv.direct_receive(packed_np, h, topk, E, 16)
+    ex = onv.decode_exact(packed_np, h)
+    off, src = want["offsets"], want["src_row"]
+    n_corner = 0
+    for e in range(E):
+        y = rht16(ex[src[off[e]:off[e + 1]]].T.reshape(h, -1, 16))
+        a = np.abs(y).max(axis=-1)
+        s = orecv.block_scale_codes(a, want["col_scale"][e], "pow2")
+        n_corner += int(((a.astype(np.float64) / 6 < 2.0 ** -126) & (s > 0)).sum())
+    assert n_corner > 10000
+    assert want["col_scale"].max() < 2.0 ** -120
+    print("receive tiny-max corner", bits.shape, n_corner, flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    assert_bytes_equal(host(packed), packed_np, "pack")
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), E, 16)
+    got = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    w = types.SimpleNamespace(topk_idx=topk, num_experts=E, alignment=16)
+    _check_receive(dev, w, packed_np, got, plan_np, h)
+    # the operand built from the grouped rows takes the same rule
+    n = h * int(off[-1])
+    grp = mtb.ep_nvfp4_columnwise_grouped(got, h, plan)
+    assert_bytes_equal(host(grp["col_scales"])[: n // 16], want["col_scales"][: n // 16], "grouped columnwise scales")
+    assert_bytes_equal(host(grp["col_codes"])[: n // 2], want["col_codes"][: n // 2], "grouped columnwise codes")
 
 
 def test_direct_receive_tiny_expert(dev):
@@ -271,6 +322,76 @@ def test_direct_receive_tiny_expert(dev):
     want_sr = orecv.direct_receive(packed_np, h, topk, 2, 16, sr=(77, 3))
     assert_bytes_equal(host(srg["col_codes"])[: n // 2], want_sr["col_codes"][: n // 2], "SR columnwise codes")
     assert_bytes_equal(host(srg["col_scales"])[: n // 16], want["col_scales"][: n // 16], "SR columnwise scales")
+
+
+@pytest.mark.parametrize("idx64", [False, True])
+def test_direct_receive_topk_one_call(dev, idx64):
+    """The receive from top-k indices in one C call (route plan + D_e + operands)
+    equals the oracle byte for byte, plan included; a bad expert id sets the
+    device error word and the entry is dropped, as for the route plan alone."""
+    w = workloads.small_dispatch(81, 333, 192, 6, 2, alignment=32, unused_frac=0.05, empty=[4])
+    topk = w.topk_idx.copy()
+    topk[7, 1] = 9                                  # out of range: flagged and dropped
+    print(f"one-call receive idx64={idx64}", flush=True)
+    packed_np = onv.pack_rows(w.x_bits)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    t_dev = torch.from_numpy(topk.astype(np.int64 if idx64 else np.int32)).to(dev)
+    plan, got = mtb.ep_nvfp4_direct_receive_topk(packed, 192, t_dev, 6, 32)
+    want_plan = o_route(topk, 6, 32)
+    for key in ("counts", "offsets", "dst_row", "src_row"):
+        assert_bytes_equal(host(plan[key]), want_plan[key], f"one-call {key}")
+    assert int(host(plan["d_error"])[0]) == mtb.EP_DEVERR_EXPERT_ID
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    wv = types.SimpleNamespace(topk_idx=topk, num_experts=6, alignment=32)
+    _check_receive(dev, wv, packed_np, got, plan_np, 192)
+    # rowwise only
+    plan2, rows = mtb.ep_nvfp4_direct_receive_topk(packed, 192, t_dev, 6, 32, columnwise=False)
+    off = int(want_plan["offsets"][-1])
+    assert "col_codes" not in rows
+    assert_bytes_equal(host(rows["row_codes"])[:off], host(got["row_codes"])[:off], "one-call rowwise only")
+
+
+def test_binding_refuses_missized_buffers(dev):
+    """Buffers too small for the sizes passed with them, a packed width that does
+    not match hidden, and preact/dy shapes that disagree are refused before
+    anything is launched (the outputs keep their sentinel bytes)."""
+    w = workloads.small_dispatch(82, 64, 128, 4, 2)
+    x = bf16_dev(w.x_bits, dev)
+    packed = mtb.ep_nvfp4_pack(x)
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 4, 16)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        mtb.ep_nvfp4_pack(x, out=torch.full((64, 70), 0xAB, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        mtb.ep_nvfp4_unpack(packed, 192)                                   # 76-byte rows are hidden 128
+    small = torch.full((10, 128), 7, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        mtb.ep_nvfp4_unpack(packed, 128, out=small)
+    ref = mtb.ep_nvfp4_direct_receive(packed, 128, plan)
+    for key in ("row_codes", "row_scales", "row_t", "col_codes", "col_scales", "col_scale"):
+        bad = {k: v.clone() for k, v in ref.items()}
+        bad[key] = torch.full((bad[key].numel() - 1,), 3, dtype=bad[key].dtype, device=dev)
+        with pytest.raises(ValueError):
+            mtb.ep_nvfp4_direct_receive(packed, 128, plan, out=bad)
+        torch.cuda.synchronize()
+        assert (bad[key] == 3).all(), key
+    short_plan = dict(plan, src_row=plan["src_row"][:-1].clone())
+    with pytest.raises(ValueError):
+        mtb.ep_nvfp4_direct_receive(packed, 128, short_plan)
+    sw = workloads.small_dswiglu(83, [5, 9], 64)
+    pre, dy = bf16_dev(sw.preact_bits, dev), bf16_dev(sw.dy_bits, dev)
+    cnt = i32_dev(sw.counts, dev)
+    with pytest.raises(ValueError):
+        mtb.dswiglu_nvfp4_quant(pre[:, :96].contiguous(), dy, cnt)         # preact must be [T, 2F]
+    good = mtb.dswiglu_nvfp4_quant(pre, dy, cnt)
+    for key in ("amax", "row_codes", "col_scales"):
+        bad = dict(good)
+        bad[key] = torch.zeros(good[key].numel() - 1, dtype=good[key].dtype, device=dev)
+        with pytest.raises(ValueError):
+            mtb.dswiglu_nvfp4_quant(pre, dy, cnt, out=bad)
+    with pytest.raises(ValueError):
+        mtb.dswiglu_nvfp4_quant(pre, dy, cnt, workspace=torch.zeros(8, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
 
 
 def test_direct_receive_config1(dev):
@@ -501,12 +622,42 @@ def test_dswiglu_two_stage(dev, counts, ffn, dy_scales):
     q = odsw.fc1_grad_quant(dx, w.counts, am)
     assert_bytes_equal(host(out["row_scale"]).view(np.uint32), q["row_scale"].view(np.uint32), "D_row")
     assert_bytes_equal(host(out["col_scale"]).view(np.uint32), q["col_scale"].view(np.uint32), "D_col")
-    t = sum(counts)
-    tolerant_codes(F.unpack_nibbles(host(out["row_codes"])), F.unpack_nibbles(q["row_codes"]),
-                   host(out["row_scales"]), q["row_scales"], "fc1 rowwise")
+    # the quantizer follows R19/R20 to the last bit: byte for byte on the GPU's own dX
     n = q["col_codes"].size
-    tolerant_codes(F.unpack_nibbles(host(out["col_codes"])[:n]), F.unpack_nibbles(q["col_codes"]),
-                   host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "fc1 columnwise")
+    assert_bytes_equal(host(out["row_scales"]), q["row_scales"], "fc1 rowwise scales")
+    assert_bytes_equal(host(out["row_codes"]), q["row_codes"], "fc1 rowwise codes")
+    assert_bytes_equal(host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "fc1 columnwise scales")
+    assert_bytes_equal(host(out["col_codes"])[:n], q["col_codes"], "fc1 columnwise codes")
+
+
+def test_dswiglu_tiny_corner(dev):
+    """Experts whose dX is FP32-subnormal-sized (dy scaled to ~1e-38 .. 1e-41): block
+    maxima a with a / 6 below FP32's normal range and a subnormal D_row -- the
+    corner where R19/R20 round fl32(a / 6) on the subnormal grid.  Stage 2 byte
+    for byte; the oracle confirms the corner is reached."""
+    counts = [40, 24, 19, 64, 8]
+    w = workloads.small_dswiglu(91, counts, 64, [1e-36, 3e-37, 5e-38, 1e-34, 1.0])
+    print(f"dswiglu tiny corner counts={counts}", flush=True)
+    out = mtb.dswiglu_nvfp4_quant(bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    dx, am = host(out["dx"]), host(out["amax"])
+    want_dx = odsw.dswiglu(w.preact_bits, w.dy_bits)
+    ulp = np.abs(dx.view(np.int16).astype(np.int64) - want_dx.view(np.int16).astype(np.int64))
+    assert ulp.max(initial=0) <= 1
+    assert_bytes_equal(am.view(np.uint32), odsw.expert_amax(dx, w.counts).view(np.uint32), "amax")
+    q = odsw.fc1_grad_quant(dx, w.counts, am)
+    D = (am / np.float32(2688.0)).astype(np.float32)
+    assert (D[:3] < 2.0 ** -126).all() and (D[:3] > 0).all()          # subnormal D_row
+    a_b = np.abs(F.bf16_to_f32(dx[:83])).reshape(83, -1, 16).max(axis=-1)
+    assert ((a_b / np.float32(6) < 2.0 ** -126) & (a_b > 0)).sum() > 100
+    n = q["col_codes"].size
+    assert_bytes_equal(host(out["row_scale"]).view(np.uint32), q["row_scale"].view(np.uint32), "D_row")
+    # R20: D_col = fl32(4 amax / 2688), which is not 4 D_row once D_row is subnormal
+    assert_bytes_equal(host(out["col_scale"]).view(np.uint32), q["col_scale"].view(np.uint32), "D_col")
+    assert (q["col_scale"][:3] != np.float32(4) * q["row_scale"][:3]).any()
+    assert_bytes_equal(host(out["row_scales"]), q["row_scales"], "tiny rowwise scales")
+    assert_bytes_equal(host(out["row_codes"]), q["row_codes"], "tiny rowwise codes")
+    assert_bytes_equal(host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "tiny columnwise scales")
+    assert_bytes_equal(host(out["col_codes"])[:n], q["col_codes"], "tiny columnwise codes")
 
 
 @pytest.mark.parametrize("dev_counts,rows", [([30, 40], 50), ([-5, 50, 7], 50), ([0, 0], 9)])

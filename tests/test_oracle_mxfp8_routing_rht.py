@@ -95,6 +95,37 @@ def test_route_plan_brute_force(A, seed):
     assert np.all(np.asarray(off) % A == 0) and off[-1] <= r_cap
 
 
+@pytest.mark.parametrize("A", [32, 128])
+def test_mxfp8_grouped_receive_brute_force(A):
+    """P2, description and "Changes": the per-expert grouped receive holds each
+    expert's rows back to back in data-then-scale regions, slots padded to the
+    alignment.  Walked row by row from a brute-force plan: grouped row g holds
+    the data and scale bytes of its token, padding rows and every row from off_E
+    to r_cap are zero bytes, and the expert's rows appear in token order."""
+    rng = np.random.default_rng(A)
+    T, k, E, H = 61, 2, 5, 96
+    x = rng.standard_normal((T, H)) * 10.0 ** rng.uniform(-3, 3, (T, 1))
+    data, scales = mxfp8.pack_rows(F.f32_to_bf16(x.astype(np.float32)))
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    topk[topk == 3] = -1                                   # expert 3 empty
+    r_cap = capacity(T, k, E, A)
+    counts, off, dst, src, _ = _brute_plan(topk, E, A, r_cap)
+    gd, gs = mxfp8.grouped_receive(data, scales, src)
+    assert gd.shape == (r_cap, H) and gs.shape == (r_cap, H // 32)
+    for g in range(r_cap):
+        e = next((e for e in range(E) if off[e] <= g < off[e + 1]), None)
+        if e is not None and g - off[e] < counts[e]:
+            toks = sorted({t for t in range(T) for j in range(k) if topk[t, j] == e})
+            t = toks[g - off[e]]
+            assert bytes(gd[g]) == bytes(data[t]) and bytes(gs[g]) == bytes(scales[t]), g
+        else:
+            assert not gd[g].any() and not gs[g].any(), g
+    for t in range(T):
+        for j in range(k):
+            if topk[t, j] >= 0:
+                assert bytes(gd[dst[t, j]]) == bytes(data[t])
+
+
 def test_route_plan_config2_shape():
     w = workloads.config2()
     plan = route_plan(w.topk_idx, 8, 16)
