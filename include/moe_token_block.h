@@ -59,8 +59,15 @@ enum ep_status {
   EP_ERR_DTYPE = -5,     /* unknown index dtype or rounding mode             */
   EP_ERR_HIP = -6,       /* a kernel launch failed                            */
   EP_ERR_WORKSPACE = -7, /* workspace NULL or smaller than required          */
-  EP_ERR_RANGE = -8      /* a size exceeds what the kernels index (2^31)     */
+  EP_ERR_RANGE = -8,     /* a size exceeds what the kernels index (2^31)     */
+  EP_ERR_SCRATCH = -9    /* sizes need more than the static scratch of an
+                            allocation-free entry point                       */
 };
+
+/* Bytes of device scratch each GPU holds for the allocation-free entry point
+ * dswiglu_nvfp4_quant_noalloc (4 MiB: the workspace of up to 1,046,524 token
+ * rows with 1024 experts). */
+#define EP_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 
 /* device-side error bits written to *d_error (OR-ed) */
 #define EP_DEVERR_EXPERT_ID 1 /* a top-k entry outside [-1, num_experts)     */
@@ -386,6 +393,21 @@ int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t* dy, int64
                                uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
                                uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                void* workspace, size_t workspace_bytes, const uint64_t* sr_state, void* stream);
+
+/* dswiglu_nvfp4_quant without the workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, serving loops that forbid
+ * hipMalloc).  The workspace lives in a static device array of
+ * EP_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the library
+ * allocates nothing on this path.  Sizes whose workspace
+ * (dswiglu_workspace_bytes) exceeds it are refused with EP_ERR_SCRATCH before
+ * anything is launched.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * must be serialized by the caller.  Other arguments, layouts and results as
+ * for dswiglu_nvfp4_quant. */
+int32_t dswiglu_nvfp4_quant_noalloc(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                                    const int32_t* counts, int64_t num_experts, uint16_t* dx, float* amax,
+                                    uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                    uint8_t* col_codes, uint8_t* col_scales, float* col_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,5 +13,6 @@ from .binding import (  # noqa: F401
     ep_mxfp8_direct_receive, ep_nvfp4_expert_scale, ep_nvfp4_direct_receive_scaled, dswiglu_nvfp4_quant,
     ep_nvfp4_pack_scatter, ep_nvfp4_columnwise_grouped, ep_nvfp4_direct_receive_kblock, ep_mxfp4_direct_receive,
     ep_nvfp4_direct_receive_sr, ep_receive_workspace_bytes, ep_nvfp4_direct_receive_topk,
+    dswiglu_nvfp4_quant_noalloc, EP_NOALLOC_SCRATCH_BYTES, EP_ERR_SCRATCH,
     lib, LIB_PATH, EXPORTS,
 )

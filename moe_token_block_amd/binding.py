@@ -21,6 +21,8 @@ EP_ROUND_NEAREST, EP_ROUND_SR_ELEMENT, EP_ROUND_SR_STREAM = 0, 1, 2
 EP_ROUND_SR_ELEMENT_CARRY, EP_ROUND_SR_STREAM_CARRY = 3, 4
 EP_IDX_INT32, EP_IDX_INT64 = 0, 1
 EP_DEVERR_EXPERT_ID = 1
+EP_ERR_SCRATCH = -9
+EP_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -55,6 +57,7 @@ _SIGS = {
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dswiglu_nvfp4_quant_sr": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "dswiglu_nvfp4_quant_noalloc": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -558,6 +561,16 @@ def _dswiglu_args(preact, dy, counts, out, materialize_dx):
             _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_scale"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]))
     return dev, t, e, out, args
+
+
+def dswiglu_nvfp4_quant_noalloc(preact, dy, counts, out, materialize_dx=True):
+    """dswiglu_nvfp4_quant without a workspace: the library's static per-GPU
+    scratch serves instead (the caller passes every output; calls that overlap
+    on one GPU race)."""
+    dev, t, e, out, args = _dswiglu_args(preact, dy, counts, out, materialize_dx)
+    with torch.cuda.device(dev):
+        _check(lib().dswiglu_nvfp4_quant_noalloc(*args, _stream(dev)), "dswiglu_nvfp4_quant_noalloc")
+    return out
 
 
 def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None):

@@ -15,6 +15,7 @@ MTB_EXPORT const char* ep_status_string(int32_t status) {
     case EP_ERR_HIP: return "a kernel launch failed";
     case EP_ERR_WORKSPACE: return "workspace missing or too small";
     case EP_ERR_RANGE: return "a size exceeds the 32-bit indexing the kernels use";
+    case EP_ERR_SCRATCH: return "sizes need more than the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -15,6 +15,9 @@
 //   direct receive: thread (cg, m) owns 8 columns x one 16-row block; the
 //   rowwise operand (per-expert scale D_row = amax/2688) and the RHT
 //   columnwise operand (D_col) come out of the same load of dX.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -776,3 +779,54 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t
                             col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, stream);
 }
 
+// ------------------------------------------------------------------ allocation-free variant
+// dswiglu_nvfp4_quant for callers that cannot allocate (code under HIP graph
+// capture, serving loops that forbid hipMalloc): its workspace -- one max
+// |dX| word per row and the expert offsets, each fully written by the call
+// before it is read, so nothing needs clearing -- lives in a file-scope
+// device array instead of a caller buffer.  Each GPU holds its own copy for
+// the life of the process; every call on one GPU shares it, so calls that
+// overlap in time on one GPU race.
+namespace {
+constexpr size_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (the host-side name is only a stand-in for the symbol).
+int32_t scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EP_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return EP_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return EP_OK;
+}
+}  // namespace
+
+MTB_EXPORT int32_t dswiglu_nvfp4_quant_noalloc(const uint16_t* preact, const uint16_t* dy, int64_t tokens,
+                                               int64_t ffn, const int32_t* counts, int64_t num_experts, uint16_t* dx,
+                                               float* amax, uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                               uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                               void* stream) {
+  if (tokens < 0 || num_experts < 1) return EP_ERR_SHAPE;
+  if (dswiglu_workspace_bytes(tokens, num_experts) > kScratchBytes) return EP_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int32_t st = scratch_ptr(&ws);
+  if (st != EP_OK) return st;
+  return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
+                            col_codes, col_scales, col_scale, ws, kScratchBytes, nullptr, stream);
+}

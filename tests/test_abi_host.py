@@ -108,6 +108,9 @@ def test_argument_validation_before_launch(lib):
                                             P, 1 << 20, P, N) == -1                                   # row_codes
     assert lib.ep_nvfp4_direct_receive_topk(P, 10, 128, P, 0, 2, 4, 16, 80, *R, P, 4, P, N) == -7     # workspace
     assert lib.ep_receive_workspace_bytes(10, 2, 4) == lib.ep_route_workspace_bytes(10, 2, 4)
+    # the allocation-free dSwiGLU refuses sizes beyond its static scratch before anything else
+    assert lib.dswiglu_nvfp4_quant_noalloc(P, P, 1_100_000, 64, P, 8, P, P, P, P, P, P, P, P, N) == -9
+    assert lib.dswiglu_nvfp4_quant_noalloc(P, P, -1, 64, P, 8, P, P, P, P, P, P, P, P, N) == -2
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, ctypes.c_void_p(0x1008), 4096, N) == -7  # misaligned
 
 
