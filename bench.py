@@ -1,22 +1,30 @@
 """Benchmark of the block-scaled token codec hot path on one MI355X.
 
-One step is one pass of the whole path over one batch of the dispatch workload
-(4096 tokens x hidden 4096 BF16 ~ N(0,1), top-2 of 8 experts with
-Zipf(1.2)-skewed routing and expert 7 empty, 16-row aligned slots):
+Headline step: one pass of the path over the DeepSeek-V3-shaped one-GPU share
+(16384 tokens x hidden 7168 BF16 ~ N(0, 0.5^2) * 10^U(-2,2) per token, top-8
+of 32 experts from N(0,1) logits, 16-row aligned slots):
 
-  route plan -> NVFP4 pack -> NVFP4 direct receive (rowwise + RHT columnwise)
-  -> MXFP8 pack -> MXFP8 receive -> unpack of the received rows to BF16
-  -> combine backward: stochastic-rounding NVFP4 pack of a same-shaped
-     gradient (Student-t(3) * 1e-3, Philox seed 1234) + its direct receive
-  -> grouped dSwiGLU epilogue + FC1-gradient NVFP4 quantization over the
-     routed rows (ffn 2048; preact ~ N(0,1), dy ~ N(0, 1e-2^2)).
+  route plan -> NVFP4 pack -> per-expert decode scale D_e -> direct receive
+  (rowwise operand + 16-point-RHT columnwise operand) -> unpack of the
+  received rows to BF16.
 
 value = algorithmic bytes (distinct inputs read once + outputs, padding rows
-excluded) of all kernels of a step / step time, in GB/s.  Inputs are resident
-in HBM before the timed region.  Per-call durations come from HIP events on
-the stream the kernels run on.
+excluded) of the step / step time, in GB/s.  Inputs are resident in HBM
+before the timed region; the timed region is K eager steps on one stream,
+and HIP events on that stream bracket every call of every timed step.
+
+``kernels`` lists every call of the path at each of the five configurations
+(their own seeded inputs): its HIP-event time per launch (eager passes, each
+after a read of a 1 GiB buffer that evicts the 256 MB MALL), algorithmic GB/s
+and the fraction of the 8 TB/s HBM peak, and -- from the committed rocprofv3
+counter summary, when the call's kernels are unchanged since -- its measured
+traffic.  The stochastic-rounding packs are reported against VALU issue.
+
+``cpu_baseline``: the oracle (plain numpy, test infrastructure) timed on the
+host on config-3 tokens, one process and one process per core.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       [--configs 1,2,3,4,5] [--workload cfgN] [--only CALL --workload cfgN]
 """
 
 import argparse
@@ -31,545 +39,431 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
-# Philox multiplies: 256 CUs x 64 lanes x 2.4 GHz, one 32x32->64-bit multiply
-# (v_mad_u64_u32) per lane per clock (its measured issue rate on gfx950)
-ALU_PEAK_TMULS = 256 * 64 * 2.4e9 / 1e12
-PHILOX_MULS_PER_ELEMENT = 20          # ten rounds of two multiplies, one Philox call per element
+# VALU issue: 256 CUs, each issuing one wave64 vector instruction per clock
+# (four 16-lane SIMDs, four clocks per wave64 instruction each), at 2.4 GHz
+VALU_PEAK_GIPS = 256 * 2.4
+CPU_SAMPLE_TOKENS = 4096        # one process: about 10 s of oracle work on the GPU machine host
+CPU_CHUNK_TOKENS = 1024         # one process per core: each on its own chunk
 
+# ---------------------------------------------------------------------------- calls
 # source files each call's kernels are built from (a counter summary is used
-# only while these are unchanged)
+# only while these are unchanged) and the kernels it launches
 _COMMON = ("common.h", "launch.h")
-CALL_SOURCES = {
-    "route_plan": ("route.hip",),
-    "nvfp4_pack": ("pack.hip",), "nvfp4_pack_sr": ("pack.hip",), "mxfp8_pack": ("pack.hip",),
-    "nvfp4_expert_scale": ("receive.hip",), "nvfp4_expert_scale_grad": ("receive.hip",),
-    "nvfp4_direct_receive": ("receive.hip",), "nvfp4_direct_receive_grad": ("receive.hip",),
-    "mxfp8_receive": ("unpack.hip",), "nvfp4_unpack": ("unpack.hip",),
-    "dswiglu_nvfp4_quant": ("dswiglu.hip",),
-    "nvfp4_pack_scatter": ("pack.hip",), "nvfp4_columnwise_grouped": ("receive.hip",),
-    "nvfp4_direct_receive_kblock": ("receive.hip",), "dswiglu_nvfp4_quant_nodx": ("dswiglu.hip",),
-    "mxfp4_receive": ("receive.hip",), "nvfp4_direct_receive_sr": ("receive.hip",),
-    "dswiglu_nvfp4_quant_sr": ("dswiglu.hip",),
+CALLS = {
+    "route_plan": (("route.hip",), ["k_route_single (<= 16K entries)", "k_route_count + k_route_scan + k_route_scatter"]),
+    "nvfp4_pack": (("pack.hip",), ["k_nvfp4_pack_wg (H >= 4096)", "k_nvfp4_pack"]),
+    "nvfp4_pack_sr": (("pack.hip",), ["k_nvfp4_pack_sr_rows (H <= 4096)", "k_nvfp4_pack_sr"]),
+    "nvfp4_pack_sr_stream": (("pack.hip",), ["k_nvfp4_pack_sr_rows (H <= 4096)", "k_nvfp4_pack_sr"]),
+    "mxfp8_pack": (("pack.hip",), ["k_mxfp8_pack"]),
+    "nvfp4_expert_scale": (("receive.hip",), ["k_expert_scale"]),
+    "nvfp4_direct_receive": (("receive.hip",), ["k_nvfp4_receive"]),
+    "nvfp4_direct_receive_kblock": (("receive.hip",), ["k_nvfp4_receive (K-blocked columnwise layout)"]),
+    "nvfp4_direct_receive_sr": (("receive.hip",), ["k_nvfp4_receive (stochastic columnwise codes)"]),
+    "mxfp4_receive": (("receive.hip",), ["k_mxfp4_receive"]),
+    "nvfp4_pack_scatter": (("pack.hip",), ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"]),
+    "nvfp4_columnwise_grouped": (("receive.hip",), ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"]),
+    "mxfp8_receive": (("unpack.hip",), ["k_mxfp8_receive"]),
+    "nvfp4_unpack": (("unpack.hip",), ["k_nvfp4_unpack"]),
+    "dswiglu_nvfp4_quant": (("dswiglu.hip",), ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"]),
+    "dswiglu_nvfp4_quant_nodx": (("dswiglu.hip",), ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce",
+                                                    "k_fc1_quant (recompute)"]),
+    "dswiglu_nvfp4_quant_sr": (("dswiglu.hip",), ["k_dswiglu_epilogue", "k_dswiglu_reduce",
+                                                  "k_fc1_quant (stochastic codes)"]),
 }
-# the kernels each call launches (as named in a rocprofv3 kernel trace)
-CALL_KERNELS = {
-    "route_plan": ["k_route_single (<= 16K entries) or k_route_count + k_route_scan + k_route_scatter"],
-    "nvfp4_pack": ["k_nvfp4_pack_wg (H >= 4096) or k_nvfp4_pack"], "nvfp4_pack_sr": ["k_nvfp4_pack_sr_rows (H <= 4096) or k_nvfp4_pack_sr"],
-    "mxfp8_pack": ["k_mxfp8_pack"], "nvfp4_expert_scale": ["k_expert_scale"],
-    "nvfp4_expert_scale_grad": ["k_expert_scale"], "nvfp4_direct_receive": ["k_nvfp4_receive"],
-    "nvfp4_direct_receive_grad": ["k_nvfp4_receive"], "mxfp8_receive": ["k_mxfp8_receive"],
-    "nvfp4_unpack": ["k_nvfp4_unpack"],
-    "dswiglu_nvfp4_quant": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"],
-    "nvfp4_pack_scatter": ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"],
-    "nvfp4_columnwise_grouped": ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"],
-    "nvfp4_direct_receive_kblock": ["k_nvfp4_receive (K-blocked columnwise layout)"],
-    "dswiglu_nvfp4_quant_nodx": ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce", "k_fc1_quant (recompute)"],
-    "mxfp4_receive": ["k_mxfp4_receive"],
-    "nvfp4_direct_receive_sr": ["k_nvfp4_receive (stochastic columnwise codes)"],
-    "dswiglu_nvfp4_quant_sr": ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant (stochastic codes)"],
-}
-# the combine-backward SR pack: one Philox4x32-10 word per element at counter
-# row*hidden + col (element mode), carry-form decision (the hardware converter)
-SR_MODE = 3  # EP_ROUND_SR_ELEMENT_CARRY
-STEP_NAMES = ["route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive", "mxfp8_pack",
-              "mxfp8_receive", "nvfp4_unpack", "nvfp4_pack_sr", "nvfp4_expert_scale_grad",
-              "nvfp4_direct_receive_grad", "dswiglu_nvfp4_quant"]
+VALU_BOUND = ("nvfp4_pack_sr", "nvfp4_pack_sr_stream")
+SR_ELEMENT_CARRY, SR_STREAM_CARRY = 3, 4      # EP_ROUND_SR_ELEMENT_CARRY, EP_ROUND_SR_STREAM_CARRY
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--reps", type=int, default=20, help="eager passes per configuration for the per-call times")
+    p.add_argument("--configs", default="1,2,3,4,5", help="configurations listed under 'kernels'")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--cpu-sample-tokens", type=int, default=CPU_SAMPLE_TOKENS)
     p.add_argument("--json-out", default=None)
-    p.add_argument("--only", default=None,
-                   help="profiling aid: run only this call of the path (or 'copy': a 1 GiB device copy, the "
-                        "reference for memory counters) --steps times, eagerly, and print what ran")
-    p.add_argument("--workload", default="dispatch",
-                   choices=["dispatch", "cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg2f", "cfg3f", "cfg2k", "cfg3k",
-                            "cfg5r", "cfg2m", "cfg3m", "cfg4s", "cfg5s"],
-                   help="dispatch (default): the full step on the 4096x4096 dispatch workload; cfgN: that "
-                        "configuration's own path, for per-kernel figures")
+    p.add_argument("--workload", default=None, choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"],
+                   help="profiling aid: time only this configuration's calls (same JSON shape)")
+    p.add_argument("--counters-pass", action="store_true",
+                   help="profiling aid (with --workload): each call --steps times between marker kernels")
+    p.add_argument("--only", default=None, choices=["copy"],
+                   help="with --counters-pass: a 1 GiB device copy instead (the counter reference)")
     return p.parse_args()
 
 
-# ---------------------------------------------------------------------------- bytes
 def row_bytes(h):
     return 9 * h // 16 + 4
 
 
-def algorithmic_bytes(T, H, k, E, r_cap, R, Tg, F):
-    """Distinct input bytes read once + output bytes, per call of the step.
-    R = routed rows (T*k), Tg = rows of the grouped MLP (= R), padding excluded."""
+# ---------------------------------------------------------------------------- algorithmic bytes
+def dispatch_bytes(T, H, k, E, r_cap, R):
+    """Distinct input bytes read once + output bytes of each dispatch-side call
+    (R routed rows, padding rows excluded)."""
     rb = row_bytes(H)
     b = {}
     b["route_plan"] = T * k * 4 + E * 4 + (E + 1) * 4 + T * k * 4 + r_cap * 4
     b["nvfp4_pack"] = T * H * 2 + T * rb
+    b["nvfp4_pack_sr"] = b["nvfp4_pack_sr_stream"] = T * H * 2 + T * rb + 16
     b["nvfp4_expert_scale"] = R * 4 + r_cap * 4 + (E + 1) * 4 + E * 4
     b["nvfp4_direct_receive"] = (T * rb + r_cap * 4 + (E + 1) * 4 + E * 4
                                  + R * (H // 2 + H // 16 + 4) + R * (H // 2 + H // 16))
+    b["nvfp4_direct_receive_kblock"] = b["nvfp4_direct_receive_sr"] = b["nvfp4_direct_receive"]
+    b["mxfp4_receive"] = T * rb + r_cap * 4 + (E + 1) * 4 + 2 * R * (H // 2 + H // 32)
+    b["nvfp4_pack_scatter"] = T * H * 2 + T * k * 4 + R * rb
+    b["nvfp4_columnwise_grouped"] = R * rb + (E + 1) * 4 + R * (H // 2 + H // 16) + E * 4
     b["mxfp8_pack"] = T * H * 2 + T * H + T * (H // 32)
     b["mxfp8_receive"] = T * (H + H // 32) + r_cap * 4 + R * (H + H // 32)
     b["nvfp4_unpack"] = T * rb + R * 4 + R * H * 2
-    b["nvfp4_pack_sr"] = T * H * 2 + T * rb + 16
-    b["nvfp4_expert_scale_grad"] = b["nvfp4_expert_scale"]
-    b["nvfp4_direct_receive_grad"] = b["nvfp4_direct_receive"]
-    b["dswiglu_nvfp4_quant"] = (Tg * 2 * F * 2 + Tg * F * 2 + E * 4                 # epilogue in
-                                + Tg * 2 * F * 2 + E * 4                            # dX out, amax
-                                + Tg * 2 * F * 2                                    # quant reads dX
-                                + 2 * Tg * (F + 2 * F // 16) + 2 * E * 4)            # row + col operands
     return b
 
 
-# ---------------------------------------------------------------------------- inputs
-def make_inputs(dev):
-    import torch
-    import workloads
-    w = workloads.config2()
-    T, H = w.x_bits.shape
-    k = w.topk_idx.shape[1]
-    rng = [np.random.default_rng(s) for s in np.random.SeedSequence(7).spawn(3)]
-    grad = workloads.to_bf16_bits(rng[0].standard_t(3, size=(T, H)) * 1e-3)
-    F = 2048
-    R = T * k
-    pre = workloads.to_bf16_bits(rng[1].standard_normal((R, 2 * F), dtype=np.float32))
-    dy = workloads.to_bf16_bits(rng[2].standard_normal((R, F), dtype=np.float32) * np.float32(1e-2))
-
-    def bf(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    return dict(w=w, T=T, H=H, k=k, E=w.num_experts, A=w.alignment, F=F, R=R,
-                x=bf(w.x_bits), grad=bf(grad), preact=bf(pre), dy=bf(dy),
-                topk=torch.from_numpy(w.topk_idx).to(dev),
-                sr=torch.tensor([1234, 0], dtype=torch.int64, device=dev),
-                host=dict(x=w.x_bits, grad=grad, pre=pre, dy=dy, topk=w.topk_idx))
+def dswiglu_bytes(T, F, E, dx=True, sr=False):
+    """Inputs (preact [T,2F], dy [T,F], counts) read once + outputs (dX if written,
+    the per-expert amax and scales, rowwise and columnwise codes and scales)."""
+    b = T * 2 * F * 2 + T * F * 2 + E * 4 + 3 * E * 4 + 2 * T * (F + 2 * F // 16)
+    if dx:
+        b += T * 2 * F * 2
+    if sr:
+        b += 16
+    return b
 
 
-def evict_mall(buf):
-    """Read a 1 GiB buffer (4x the 256 MB MALL) before an eager pass of per-call
-    timings.  The read evicts what the MALL holds and writes back its dirty lines, so
-    the pass starts with its inputs in HBM and no write-backs of earlier work ahead of
-    its own traffic (a 1 GiB fill instead leaves 256 MB of dirty lines that the first
-    calls pay for: a plain 128 MiB read after a fill runs at 2.6 TB/s, after this read
-    at 6.0); it also keeps the GPU busy while the host enqueues the pass, so each event
-    pair brackets GPU time only.  One read per pass, not one per call: a read right
-    before every call made each call about 2 us slower, small ones included (7.8 ->
-    10.4 us for the expert-scale pass), a cold start that the calls of a step do not
-    see."""
-    buf.amax()
+# ---------------------------------------------------------------------------- paths
+class Call:
+    def __init__(self, name, fn, nbytes, in_step=True, elements=None):
+        self.name, self.fn, self.bytes, self.in_step, self.elements = name, fn, nbytes, in_step, elements
 
 
-# ---------------------------------------------------------------------------- the step
-class Step:
-    """Pre-allocated outputs; ``run`` launches one pass of the path."""
+class Path:
+    """One configuration's calls over its own seeded inputs, outputs pre-allocated.
+    ``step`` holds the calls of the configuration's path in order; the other
+    calls are variants of a step call (other layouts, formats, rounding modes)
+    timed on the same inputs."""
 
-    def __init__(self, inp):
-        import torch
-        import moe_token_block_amd as m
-        self.m = m
-        self.inp = inp
-        dev = inp["x"].device
-        T, H, k, E, A, F, R = (inp[s] for s in ("T", "H", "k", "E", "A", "F", "R"))
-        self.r_cap = m.ep_route_capacity(T, k, E, A)
-        self.ws = torch.empty(max(m.lib().ep_route_workspace_bytes(T, k, E), 4), dtype=torch.uint8, device=dev)
-        self.derr = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.plan = m.ep_route_plan(inp["topk"], E, A, d_error=self.derr, workspace=self.ws)
-        u8 = dict(dtype=torch.uint8, device=dev)
-        self.packed = torch.empty((T, row_bytes(H)), **u8)
-        self.packed_g = torch.empty((T, row_bytes(H)), **u8)
-        mk = lambda: dict(row_codes=torch.empty((self.r_cap, H // 2), **u8),
-                          row_scales=torch.empty((self.r_cap, H // 16), **u8),
-                          row_t=torch.empty(self.r_cap, dtype=torch.float32, device=dev),
-                          col_codes=torch.empty(self.r_cap * H // 2, **u8),
-                          col_scales=torch.empty(self.r_cap * H // 16, **u8),
-                          col_scale=torch.empty(E, dtype=torch.float32, device=dev))
-        self.recv, self.recv_g = mk(), mk()
-        self.mx = torch.empty(T * H + T * H // 32, **u8)
-        self.mx_out = (torch.empty((self.r_cap, H), **u8), torch.empty((self.r_cap, H // 32), **u8))
-        self.unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
-        # the unpack decodes the routed rows in grouped order (padding rows skipped)
-        off = self.plan["offsets"].cpu().numpy()
-        src = self.plan["src_row"].cpu().numpy()
-        self.src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
-        self.counts = self.plan["counts"]
-        self.dsw_ws = torch.empty(m.lib().dswiglu_workspace_bytes(R, E), **u8)
-        cap = R + 15 * E
-        f32 = dict(dtype=torch.float32, device=dev)
-        self.dsw = dict(dx=torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev), amax=torch.empty(E, **f32),
-                        row_codes=torch.empty((R, F), **u8), row_scales=torch.empty((R, 2 * F // 16), **u8),
-                        row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
-                        col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
-        self.names = list(STEP_NAMES)
-        self.flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: 4x the MALL
-
-    def calls(self):
-        m, i = self.m, self.inp
-        H, E, A = i["H"], i["E"], i["A"]
-        return [
-            lambda: m.ep_route_plan(i["topk"], E, A, d_error=self.derr, workspace=self.ws, out=self.plan),
-            lambda: m.ep_nvfp4_pack(i["x"], out=self.packed),
-            lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan, col_scale=self.recv["col_scale"]),
-            lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
-            lambda: m.ep_mxfp8_pack(i["x"], out=self.mx),
-            lambda: m.ep_mxfp8_direct_receive(self.mx[: i["T"] * H].view(i["T"], H),
-                                              self.mx[i["T"] * H:].view(i["T"], H // 32), self.plan, out=self.mx_out),
-            lambda: m.ep_nvfp4_unpack(self.packed, H, src_row=self.src_valid, out=self.unpacked),
-            lambda: m.ep_nvfp4_pack(i["grad"], SR_MODE, i["sr"], out=self.packed_g),
-            lambda: m.ep_nvfp4_expert_scale(self.packed_g, H, self.plan, col_scale=self.recv_g["col_scale"]),
-            lambda: m.ep_nvfp4_direct_receive_scaled(self.packed_g, H, self.plan, self.recv_g),
-            lambda: m.dswiglu_nvfp4_quant(i["preact"], i["dy"], self.counts, out=self.dsw, workspace=self.dsw_ws),
-        ]
-
-    def run_concurrent(self):
-        """The same calls as ``run``: the route plan first (every later call needs it
-        or its counts), then four independent chains on their own streams (default
-        priority) joined back into the calling stream -- the dSwiGLU chain, the
-        combine-backward chain and the MXFP8 chain on three side streams, in that
-        launch order, then the NVFP4 dispatch chain on the calling stream.  One fork
-        and one join, no other cross-stream waits: measured 1.5% faster than starting
-        the packs beside the route plan with a wait on it in every chain (each
-        cross-stream wait costs a dependency resolution in the graph).  The longest
-        chain (dSwiGLU) first: 182 -> 177 us against the order combine backward,
-        MXFP8, dSwiGLU; every order with it first is within 1.5 us of the best."""
-        import torch
-        c = self.calls()
-        main = torch.cuda.current_stream()
-        if not hasattr(self, "side"):
-            self.side = [torch.cuda.Stream() for _ in range(3)]
-        c[0]()                                       # route plan
-        for st in self.side:
-            st.wait_stream(main)
-        with torch.cuda.stream(self.side[2]):
-            c[10]()                                  # dSwiGLU + FC1-grad quantization (needs the counts)
-        with torch.cuda.stream(self.side[0]):
-            c[7](); c[8](); c[9]()                   # SR pack, expert scale, receive of the gradient rows
-        with torch.cuda.stream(self.side[1]):
-            c[4](); c[5]()                           # MXFP8 pack and receive
-        c[1](); c[2](); c[3](); c[6]()               # NVFP4 pack, expert scale, receive, unpack
-        for st in self.side:
-            main.wait_stream(st)
-
-    def run(self, events=None):
-        calls = self.calls()
-        if events is not None:
-            evict_mall(self.flush)
-        for j, c in enumerate(calls):
-            if events is not None:
-                events[j][0].record()
-            c()
-            if events is not None:
-                events[j][1].record()
-
-
-# ---------------------------------------------------------------------------- per-config paths
-class ConfigStep:
-    """The path of one configuration on its own inputs (for per-kernel figures):
-    cfg1/cfg3: route -> pack -> expert scale -> direct receive -> unpack of the grouped rows;
-    cfg2: route -> pack -> expert scale -> direct receive -> MXFP8 pack -> MXFP8 receive;
-    cfg4: route -> SR pack -> expert scale -> direct receive; cfg5: dSwiGLU + FC1-grad quant."""
-
-    def __init__(self, which, dev):
+    def __init__(self, n, dev, w=None):
         import torch
         import moe_token_block_amd as m
         import workloads
-        self.m = m
-        fused, kblock, recompute = which.endswith("f"), which.endswith("k"), which.endswith("r")
-        mxfp4, sr_grad = which.endswith("m"), which.endswith("s")
-        n = int(which[3:-1] if fused or kblock or recompute or mxfp4 or sr_grad else which[3:])
-        w = workloads.CONFIGS[n]()
-        self.w, self.n = w, n
+        self.n = n
+        self.dev = dev
+        w = w if w is not None else workloads.CONFIGS[n]()
+        self.w = w
         u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        self.flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
-        self.names, self.calls_, self.bytes = [], [], {}
-        self.elements = None
+        self.calls = []
         if n == 5:
             T, F, E = w.preact_bits.shape[0], w.dy_bits.shape[1], len(w.counts)
-            self.pre, self.dy = bf(w.preact_bits), bf(w.dy_bits)
-            self.counts = torch.from_numpy(w.counts).to(dev)
+            pre, dy = bf(w.preact_bits), bf(w.dy_bits)
+            counts = torch.from_numpy(w.counts).to(dev)
             cap = T + 15 * E
-            f32 = dict(dtype=torch.float32, device=dev)
-            self.out = dict(dx=None if recompute else torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev),
-                            amax=torch.empty(E, **f32),
-                            row_codes=torch.empty((T, F), **u8), row_scales=torch.empty((T, 2 * F // 16), **u8),
-                            row_scale=torch.empty(E, **f32), col_codes=torch.empty(2 * F * cap // 2, **u8),
-                            col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
-            self.ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
-            if sr_grad:
-                self.sr5 = torch.tensor([1234, 0], dtype=torch.int64, device=dev)
-                self._add("dswiglu_nvfp4_quant_sr",
-                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws,
-                                                        sr_state=self.sr5),
-                          T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16)
-                          + 2 * E * 4)
-                self.desc = dict(workload=w.name + " (stochastic FC1-grad codes)", tokens=T, ffn=F, experts=E)
-                return
-            if recompute:
-                # no dX written: inputs read once + the quantized operands and the maxima
-                self._add("dswiglu_nvfp4_quant_nodx",
-                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws),
-                          T * 2 * F * 2 + T * F * 2 + E * 4 + 2 * T * (F + 2 * F // 16) + 2 * E * 4)
-            else:
-                self._add("dswiglu_nvfp4_quant",
-                          lambda: m.dswiglu_nvfp4_quant(self.pre, self.dy, self.counts, out=self.out, workspace=self.ws),
-                          T * 2 * F * 2 + T * F * 2 + T * 2 * F * 2 + E * 4 + T * 2 * F * 2 + 2 * T * (F + 2 * F // 16)
-                          + 2 * E * 4)
-            self.desc = dict(workload=w.name + (" (dX not materialized)" if recompute else ""), tokens=T, ffn=F,
-                             experts=E)
+            mk = lambda dx: dict(dx=torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev) if dx else None,
+                                 amax=torch.empty(E, **f32), row_codes=torch.empty((T, F), **u8),
+                                 row_scales=torch.empty((T, 2 * F // 16), **u8), row_scale=torch.empty(E, **f32),
+                                 col_codes=torch.empty(2 * F * cap // 2, **u8),
+                                 col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
+            out, out_nodx = mk(True), mk(False)
+            ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
+            sr = torch.tensor([1234, 0], dtype=torch.int64, device=dev)
+            self._add("dswiglu_nvfp4_quant", lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws),
+                      dswiglu_bytes(T, F, E))
+            self._add("dswiglu_nvfp4_quant_nodx",
+                      lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out_nodx, workspace=ws),
+                      dswiglu_bytes(T, F, E, dx=False), in_step=False)
+            self._add("dswiglu_nvfp4_quant_sr",
+                      lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws, sr_state=sr),
+                      dswiglu_bytes(T, F, E, sr=True), in_step=False)
+            self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)
             return
         T, H = w.x_bits.shape
         k, E, A = w.topk_idx.shape[1], w.num_experts, w.alignment
         R = T * k
-        self.elements = T * H
-        self.x = bf(w.x_bits)
-        self.topk = torch.from_numpy(w.topk_idx).to(dev)
+        x = bf(w.x_bits)
+        topk = torch.from_numpy(w.topk_idx).to(dev)
         r_cap = m.ep_route_capacity(T, k, E, A)
-        self.ws = torch.empty(max(m.lib().ep_route_workspace_bytes(T, k, E), 4), **u8)
-        self.derr = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.plan = m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws)
-        self.packed = torch.empty((T, row_bytes(H)), **u8)
-        self.recv = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
-                         row_t=torch.empty(r_cap, dtype=torch.float32, device=dev),
-                         col_codes=torch.empty(r_cap * H // 2, **u8), col_scales=torch.empty(r_cap * H // 16, **u8),
-                         col_scale=torch.empty(E, dtype=torch.float32, device=dev))
-        b = algorithmic_bytes(T, H, k, E, r_cap, R, R, 0)
-        self._add("route_plan", lambda: m.ep_route_plan(self.topk, E, A, d_error=self.derr, workspace=self.ws,
-                                                        out=self.plan), b["route_plan"])
-        if mxfp4:
-            # the MXFP4 receive of the same packed rows (alignment 32: 32-row columnwise blocks)
-            A32 = max(A, 32)
-            r_cap32 = m.ep_route_capacity(T, k, E, A32)
-            self.plan32 = m.ep_route_plan(self.topk, E, A32)
-            self.mx4 = dict(row_codes=torch.empty((r_cap32, H // 2), **u8), row_scales=torch.empty((r_cap32, H // 32), **u8),
-                            col_codes=torch.empty(r_cap32 * H // 2, **u8), col_scales=torch.empty(r_cap32 * H // 32, **u8))
-            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(self.x, out=self.packed), b["nvfp4_pack"])
-            self._add("mxfp4_receive", lambda: m.ep_mxfp4_direct_receive(self.packed, H, self.plan32, out=self.mx4),
-                      T * row_bytes(H) + r_cap32 * 4 + (E + 1) * 4 + 2 * R * (H // 2 + H // 32))
-            self.desc = dict(workload=w.name + " (MXFP4 receive, alignment 32)", tokens=T, hidden=H, experts=E,
-                             top_k=k, alignment=A32)
-            return
-        if fused:
-            # sender-side fused dispatch: pack straight into the grouped rows, then
-            # the columnwise operand from those contiguous rows
-            rb = row_bytes(H)
-            self._add("nvfp4_pack_scatter", lambda: m.ep_nvfp4_pack_scatter(self.x, self.plan, out=self.recv),
-                      T * H * 2 + R * rb)
-            self._add("nvfp4_columnwise_grouped", lambda: m.ep_nvfp4_columnwise_grouped(self.recv, H, self.plan,
-                                                                                        out=self.recv),
-                      R * rb + R * (H // 2 + H // 16) + E * 4)
-            self.desc = dict(workload=w.name + " (fused dispatch)", tokens=T, hidden=H, experts=E, top_k=k, alignment=A)
-            return
+        ws = torch.empty(max(m.lib().ep_route_workspace_bytes(T, k, E), 4), **u8)
+        derr = torch.zeros(1, dtype=torch.int32, device=dev)
+        plan = m.ep_route_plan(topk, E, A, d_error=derr, workspace=ws)
+        packed = torch.empty((T, row_bytes(H)), **u8)
+        recv = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
+                    row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
+                    col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))
+        b = dispatch_bytes(T, H, k, E, r_cap, R)
+        self._add("route_plan", lambda: m.ep_route_plan(topk, E, A, d_error=derr, workspace=ws, out=plan),
+                  b["route_plan"])
         if n == 4:
-            self.sr = torch.tensor([w.sr_seed, w.sr_counter_base], dtype=torch.int64, device=dev)
-            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(self.x, SR_MODE, self.sr, out=self.packed),
-                      b["nvfp4_pack_sr"])
+            st = torch.tensor([w.sr_seed, w.sr_counter_base], dtype=torch.int64, device=dev)
+            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(x, SR_ELEMENT_CARRY, st, out=packed),
+                      b["nvfp4_pack_sr"], elements=T * H)
+            self._add("nvfp4_pack_sr_stream", lambda: m.ep_nvfp4_pack(x, SR_STREAM_CARRY, st, out=packed),
+                      b["nvfp4_pack_sr_stream"], in_step=False, elements=T * H)
+            # the step's receive reads the element-mode rows: pack them again after the variant
+            self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(x, SR_ELEMENT_CARRY, st, out=packed),
+                      b["nvfp4_pack_sr"], in_step=False, elements=T * H, record=False)
         else:
-            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(self.x, out=self.packed), b["nvfp4_pack"])
-        self._add("nvfp4_expert_scale", lambda: m.ep_nvfp4_expert_scale(self.packed, H, self.plan,
-                                                                        col_scale=self.recv["col_scale"]),
-                  b["nvfp4_expert_scale"])
-        if sr_grad:
-            self.sr_recv = torch.tensor([w.sr_seed or 1234, 1 << 40], dtype=torch.int64, device=dev)
-            self._add("nvfp4_direct_receive_sr",
-                      lambda: m.ep_nvfp4_direct_receive_sr(self.packed, H, self.plan, self.recv, self.sr_recv),
-                      b["nvfp4_direct_receive"])
-        elif kblock:
-            self._add("nvfp4_direct_receive_kblock",
-                      lambda: m.ep_nvfp4_direct_receive_kblock(self.packed, H, self.plan, self.recv),
-                      b["nvfp4_direct_receive"])
-        else:
-            self._add("nvfp4_direct_receive",
-                      lambda: m.ep_nvfp4_direct_receive_scaled(self.packed, H, self.plan, self.recv),
-                      b["nvfp4_direct_receive"])
+            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(x, out=packed), b["nvfp4_pack"])
+        self._add("nvfp4_expert_scale",
+                  lambda: m.ep_nvfp4_expert_scale(packed, H, plan, col_scale=recv["col_scale"]), b["nvfp4_expert_scale"])
+        self._add("nvfp4_direct_receive", lambda: m.ep_nvfp4_direct_receive_scaled(packed, H, plan, recv),
+                  b["nvfp4_direct_receive"])
         if n == 2:
-            self.mx = torch.empty(T * H + T * H // 32, **u8)
-            self.mx_out = (torch.empty((r_cap, H), **u8), torch.empty((r_cap, H // 32), **u8))
-            self._add("mxfp8_pack", lambda: m.ep_mxfp8_pack(self.x, out=self.mx), b["mxfp8_pack"])
+            mx = torch.empty(T * H + T * H // 32, **u8)
+            mx_out = (torch.empty((r_cap, H), **u8), torch.empty((r_cap, H // 32), **u8))
+            self._add("mxfp8_pack", lambda: m.ep_mxfp8_pack(x, out=mx), b["mxfp8_pack"])
             self._add("mxfp8_receive", lambda: m.ep_mxfp8_direct_receive(
-                self.mx[: T * H].view(T, H), self.mx[T * H:].view(T, H // 32), self.plan, out=self.mx_out),
-                b["mxfp8_receive"])
+                mx[: T * H].view(T, H), mx[T * H:].view(T, H // 32), plan, out=mx_out), b["mxfp8_receive"])
         if n in (1, 3):
-            off = self.plan["offsets"].cpu().numpy()
-            src = self.plan["src_row"].cpu().numpy()
-            self.src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
-            self.unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
-            self._add("nvfp4_unpack", lambda: m.ep_nvfp4_unpack(self.packed, H, src_row=self.src_valid,
-                                                                out=self.unpacked), b["nvfp4_unpack"])
+            off = plan["offsets"].cpu().numpy()
+            src = plan["src_row"].cpu().numpy()
+            src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
+            unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            self._add("nvfp4_unpack", lambda: m.ep_nvfp4_unpack(packed, H, src_row=src_valid, out=unpacked),
+                      b["nvfp4_unpack"])
+        if n == 4:
+            srr = torch.tensor([1234, 1 << 40], dtype=torch.int64, device=dev)
+            self._add("nvfp4_direct_receive_sr", lambda: m.ep_nvfp4_direct_receive_sr(packed, H, plan, recv, srr),
+                      b["nvfp4_direct_receive_sr"], in_step=False)
+        if n in (2, 3):
+            self._add("nvfp4_direct_receive_kblock", lambda: m.ep_nvfp4_direct_receive_kblock(packed, H, plan, recv),
+                      b["nvfp4_direct_receive_kblock"], in_step=False)
+            A32 = max(A, 32)
+            plan32 = m.ep_route_plan(topk, E, A32)
+            r32 = plan32["r_cap"]
+            mx4 = dict(row_codes=torch.empty((r32, H // 2), **u8), row_scales=torch.empty((r32, H // 32), **u8),
+                       col_codes=torch.empty(r32 * H // 2, **u8), col_scales=torch.empty(r32 * H // 32, **u8))
+            self._add("mxfp4_receive", lambda: m.ep_mxfp4_direct_receive(packed, H, plan32, out=mx4),
+                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive"], in_step=False)
+            fused = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
+                         row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
+                         col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))
+            self._add("nvfp4_pack_scatter", lambda: m.ep_nvfp4_pack_scatter(x, plan, out=fused),
+                      b["nvfp4_pack_scatter"], in_step=False)
+            self._add("nvfp4_columnwise_grouped", lambda: m.ep_nvfp4_columnwise_grouped(fused, H, plan, out=fused),
+                      b["nvfp4_columnwise_grouped"], in_step=False)
         self.desc = dict(workload=w.name, tokens=T, hidden=H, experts=E, top_k=k, alignment=A)
 
-    def _add(self, name, fn, nbytes):
-        self.names.append(name)
-        self.calls_.append(fn)
-        self.bytes[name] = nbytes
+    def _add(self, name, fn, nbytes, in_step=True, elements=None, record=True):
+        c = Call(name, fn, nbytes, in_step, elements)
+        c.record = record
+        c.dev = self.dev
+        self.calls.append(c)
 
-    def calls(self):
-        return self.calls_
-
-    def run(self, events=None):
-        if events is not None:
-            evict_mall(self.flush)
-        for j, c in enumerate(self.calls_):
-            if events is not None:
-                events[j][0].record()
-            c()
-            if events is not None:
-                events[j][1].record()
+    def step_calls(self):
+        return [c for c in self.calls if c.in_step]
 
 
-# ---------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(inp, n_tok):
-    """The oracle, as it stands, on the first n_tok tokens of the same workload (their
-    routing, their gradient rows, and the grouped dSwiGLU rows they route to)."""
-    from oracle import nvfp4, receive, mxfp8, dswiglu
-    from oracle.routing import route_plan
-    h = inp["host"]
-    H, E, A, F, k = inp["H"], inp["E"], inp["A"], inp["F"], inp["k"]
-    x = h["x"][:n_tok]
-    topk = h["topk"][:n_tok]
-    grad = h["grad"][:n_tok]
-    R = n_tok * k
-    pre, dy = h["pre"][:R], h["dy"][:R]
+def evict_mall(buf):
+    """Read a 1 GiB buffer (4x the 256 MB MALL) before an eager pass of per-call
+    timings: the pass then starts with its inputs in HBM and no write-backs of
+    earlier work ahead of its own traffic (a 1 GiB fill instead would leave 256
+    MB of dirty lines for the first calls to write back), and the GPU is busy
+    while the host enqueues the pass, so each event pair brackets GPU time."""
+    buf.amax()
+
+
+def time_calls(path, reps, flush):
+    """Per-call HIP-event times (ms per launch) over ``reps`` eager passes of all
+    the path's calls, each pass after the MALL-evicting read."""
+    import torch
+    calls = path.calls
+    for c in calls:                                   # warm-up pass
+        c.fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(reps)]
+    for r in range(reps):
+        evict_mall(flush)
+        for j, c in enumerate(calls):
+            ev[r][j][0].record()
+            c.fn()
+            ev[r][j][1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for j, c in enumerate(calls):
+        if getattr(c, "record", True) and c.name not in out:
+            out[c.name] = float(np.mean([ev[r][j][0].elapsed_time(ev[r][j][1]) for r in range(reps)]))
+    return out
+
+
+def time_step(path, steps, warmup):
+    """The timed region: ``steps`` eager passes of the step's calls on the current
+    stream, HIP events on that stream around every call; returns the wall time
+    per step and each call's mean event time over the timed steps."""
+    import torch
+    calls = path.step_calls()
+    for _ in range(warmup):
+        for c in calls:
+            c.fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(steps)]
+    # a marker kernel (a torch random fill, used nowhere else) before the timed
+    # region: in a kernel trace, the dispatches after it are the timed steps'
+    torch.empty(64, dtype=torch.float32, device=calls[0].dev).random_()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    plan = route_plan(topk, E, A)
-    packed = nvfp4.pack_rows(x)
-    receive.direct_receive(packed, H, topk, E, A)
-    d, s = mxfp8.pack_rows(x)
-    mxfp8.grouped_receive(d, s, plan["src_row"])
-    nvfp4.unpack_rows(packed, H, plan["src_row"][plan["src_row"] >= 0])
-    pg = nvfp4.pack_rows(grad, sr_seed=1234, sr_rule="carry")
-    receive.direct_receive(pg, H, topk, E, A)
-    counts = plan["counts"]
-    dx = dswiglu.dswiglu(pre, dy)
-    dswiglu.fc1_grad_quant(dx, counts, dswiglu.expert_amax(dx, counts))
-    dt = time.perf_counter() - t0
-    r_cap = plan["src_row"].shape[0]
-    total = sum(algorithmic_bytes(n_tok, H, k, E, r_cap, R, R, F).values())
-    return dict(value=round(total / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"first {n_tok} tokens of the workload (their routing, gradient rows and "
-                       f"{R} grouped dSwiGLU rows); {dt:.1f} s single-threaded numpy")
+    for s in range(steps):
+        for j, c in enumerate(calls):
+            ev[s][j][0].record()
+            c.fn()
+            ev[s][j][1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    per = {}
+    for j, c in enumerate(calls):
+        per.setdefault(c.name, []).extend(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps))
+    return ms_step, {k: float(np.mean(v)) for k, v in per.items()}
 
 
+# ---------------------------------------------------------------------------- counters
 def kernel_source_hash(call):
     """Hash of the sources the call's kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_token_block_amd", "csrc")
-    for f in sorted(CALL_SOURCES[call] + _COMMON):
+    for f in sorted(CALLS[call][0] + _COMMON):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(call, workload="dispatch"):
-    """HBM bytes per launch of one call from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the copy reference), or None when the
-    call's kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+def counters_of(cfg, call):
+    """The committed counter record of one call at one configuration (per launch:
+    HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by the copy reference, DRAM
+    request bytes, issued VALU instructions), or None when the call's kernels
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
-    d = json.load(open(path))
-    if d.get("workload") != workload:
+    rec = json.load(open(path)).get("calls", {}).get(f"cfg{cfg}/{call}")
+    if rec is None or rec.get("source_hash") != kernel_source_hash(call):
         return None
-    k = d.get("calls", {}).get(call)
-    if k is None or k.get("source_hash") != kernel_source_hash(call):
-        return None
-    return k.get("hbm_bytes_per_launch")
+    return rec
 
 
-def roofline_of(call, nbytes, ms, elements=None, workload="dispatch"):
-    """Roofline record of one call: HBM-bound calls against 8 TB/s; the
-    stochastic-rounding pack, bound by its Philox arithmetic, against the
-    multiply issue rate."""
-    if call == "nvfp4_pack_sr" and elements is not None:
-        tmul = elements * PHILOX_MULS_PER_ELEMENT / (ms / 1e3) / 1e12
-        return dict(bound="alu", achieved=round(tmul, 3), peak=round(ALU_PEAK_TMULS, 2), unit="Tmul/s",
-                    frac=round(tmul / ALU_PEAK_TMULS, 4), traffic=traffic_from_profile(call, workload),
-                    kernel=call, kernels=CALL_KERNELS[call], bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
+def entry(cfg, call, nbytes, ms, elements=None):
     gbs = nbytes / (ms / 1e3) / 1e9
-    return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                traffic=traffic_from_profile(call, workload), kernel=call, kernels=CALL_KERNELS[call],
-                bytes_per_launch=nbytes, ms_per_launch=round(ms, 5))
+    e = dict(ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    cnt = counters_of(cfg, call)
+    e["traffic"] = cnt.get("hbm_bytes") if cnt else None
+    if cnt and cnt.get("dram_bytes") is not None:
+        e["dram_bytes"] = cnt["dram_bytes"]
+    if call in VALU_BOUND:
+        valu = cnt.get("valu_insts") if cnt else None
+        e["bound"] = "alu"
+        if valu is not None:
+            gips = valu / (ms / 1e3) / 1e9
+            e.update(valu_insts=valu, valu_per_element=round(valu * 64 / elements, 2), valu_gips=round(gips, 1),
+                     valu_frac=round(gips / VALU_PEAK_GIPS, 4))
+    return e
 
 
-def time_step(step, args):
-    """K graph replays of one captured step (the timed region), then per-call HIP
-    events in eager passes, each pass preceded by a MALL-evicting read (evict_mall)."""
-    import torch
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-    # the timed region: K replays of one captured step (no host work per kernel)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step.run()
-        if hasattr(step, "run_concurrent"):
-            step.run_concurrent()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        if hasattr(step, "run_concurrent"):
-            step.run_concurrent()
-        else:
-            step.run()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
+# ---------------------------------------------------------------------------- CPU baseline
+def _oracle_cfg3(x_bits, topk, E, A, H):
+    """The oracle's path of one sample of config-3 tokens: route plan, pack, direct
+    receive (rowwise + columnwise), unpack of the received rows; returns
+    (seconds, algorithmic bytes)."""
+    from oracle import nvfp4, receive
+    from oracle.routing import route_plan
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # per-call durations: HIP events on the launch stream around every call of
-    # eager steps (each preceded by the read described in evict_mall)
-    n = len(step.names)
-    reps = max(5, min(args.steps, 50))
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-          for _ in range(reps)]
-    for r in range(reps):
-        step.run(ev[r])
-    torch.cuda.synchronize()
-    per_ms = {name: float(np.mean([ev[r][j][0].elapsed_time(ev[r][j][1]) for r in range(reps)]))
-              for j, name in enumerate(step.names)}
-    return ms_step, per_ms
+    plan = route_plan(topk, E, A)
+    packed = nvfp4.pack_rows(x_bits)
+    receive.direct_receive(packed, H, topk, E, A)
+    off, src = plan["offsets"], plan["src_row"]
+    nvfp4.unpack_rows(packed, H, src[: off[-1]][src[: off[-1]] >= 0])
+    dt = time.perf_counter() - t0
+    T, k = topk.shape
+    b = dispatch_bytes(T, H, k, E, src.shape[0], T * k)
+    return dt, sum(b[c] for c in ("route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive",
+                                  "nvfp4_unpack"))
 
 
-def main_config(args, dev):
-    import torch
-    step = ConfigStep(args.workload, dev)
-    ms_step, per_ms = time_step(step, args)
-    total = sum(step.bytes.values())
-    kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=step.bytes[nm],
-                        gbs=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
-                        frac=round(step.bytes[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
-    for nm in step.names:
-        kernels[nm]["traffic"] = traffic_from_profile(nm, args.workload)
-    dom = max(step.names, key=lambda nm: per_ms[nm])
-    out = {"metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
-           "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16->nvfp4/mxfp8", "data": "synthetic",
-           "config": dict(step.desc, bytes_per_step=total),
-           "roofline": roofline_of(dom, step.bytes[dom], per_ms[dom], elements=step.elements,
-                                   workload=args.workload),
-           "kernels": kernels, "cpu_baseline": None}
-    line = json.dumps(out)
-    print(line, flush=True)
-    if args.json_out:
-        with open(args.json_out, "w") as f:
-            f.write(line + "\n")
+def _oracle_worker(args):
+    return _oracle_cfg3(*args)
 
 
-def main_only(args, dev):
-    """Counter-collection aid: run the calls before ONLY once each, launch a
-    marker kernel (a torch random fill, used nowhere else), then run ONLY
-    --steps times; a profile's dispatches after the marker are ONLY's.
-    ONLY = 'copy' runs a 1 GiB device-to-device copy instead (the reference
-    that scales the memory counters)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, n_tok, n_chunk=CPU_CHUNK_TOKENS):
+    """The oracle as it stands on the host, before anything touches the GPU: one
+    process on tokens [0, n_tok) of config 3, then one process per core (at most
+    16, the machine's CPU share), each on its own n_chunk tokens (their own routing)."""
+    import multiprocessing as mp
+    E, A, H = w.num_experts, w.alignment, w.x_bits.shape[1]
+    dt1, b1 = _oracle_cfg3(w.x_bits[:n_tok], w.topk_idx[:n_tok], E, A, H)
+    ncore = max(1, min(len(os.sched_getaffinity(0)), 16, w.x_bits.shape[0] // n_chunk))
+    jobs = [(w.x_bits[i * n_chunk:(i + 1) * n_chunk], w.topk_idx[i * n_chunk:(i + 1) * n_chunk], E, A, H)
+            for i in range(ncore)]
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(ncore) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    dtn = time.perf_counter() - t0
+    bn = sum(r[1] for r in res)
+    return {"value": round(bn / dtn / 1e9, 4), "unit": "GB/s", "cores": ncore, "kind": "oracle",
+            "sample": f"config 3 ({w.name}): route plan, NVFP4 pack, direct receive (rowwise + RHT columnwise), "
+                      f"unpack; {ncore} processes, each on its own {n_chunk} tokens ({ncore * n_chunk} tokens, "
+                      f"{dtn:.1f} s wall incl. process start)",
+            "single_core": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": f"tokens [0, {n_tok}) of config 3, {dt1:.1f} s"},
+            "cpu_model": cpu_model()}
+
+
+# ---------------------------------------------------------------------------- output
+def headline(path3, ms_step, per, steps, warmup, kernels, cpu):
+    calls = path3.step_calls()
+    total = sum(c.bytes for c in calls)
+    dom = max(per, key=lambda nm: per[nm])
+    c = next(c for c in calls if c.name == dom)
+    gbs = c.bytes / (per[dom] / 1e3) / 1e9
+    cnt = counters_of(3, dom)
+    roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                traffic=cnt.get("hbm_bytes") if cnt else None, kernel=dom, kernels=CALLS[dom][1],
+                bytes_per_launch=c.bytes, ms_per_launch=round(per[dom], 5),
+                dominant_by="largest per-launch time in the timed step")
+    if cnt and cnt.get("dram_bytes") is not None:
+        roof["dram_bytes"] = cnt["dram_bytes"]
+    return {
+        "metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->nvfp4", "data": "synthetic",
+        "config": dict(path3.desc, workload=path3.desc["workload"] + ": route plan + NVFP4 pack + D_e + direct "
+                       "receive (rowwise + RHT columnwise) + unpack of the received rows",
+                       bytes_per_step=total, step_calls=[c.name for c in calls],
+                       step_ms={nm: round(v, 5) for nm, v in per.items()}),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+
+
+def config_kernels(n, path, per):
+    out = {}
+    for c in path.calls:
+        if c.name in per and c.name not in out:
+            out[c.name] = entry(n, c.name, c.bytes, per[c.name], c.elements)
+            if not c.in_step:
+                out[c.name]["variant"] = True
+    return dict(workload=path.desc["workload"], calls=out)
+
+
+def main_counters_pass(args, dev):
+    """Counter-collection aid (run under rocprofv3 --pmc): every call of --workload
+    once, then for each call a marker kernel (a torch random fill, used nowhere
+    else) followed by --steps launches of the call, each after the MALL-evicting
+    read (a torch reduction).  A profile's dispatches between two markers that
+    are not the reduction are that call's.  --only copy: a 1 GiB
+    device-to-device copy after one marker instead (the reference that scales
+    the memory counters)."""
     import torch
     marker = torch.empty(64, dtype=torch.float32, device=dev)
     if args.only == "copy":
@@ -581,27 +475,39 @@ def main_only(args, dev):
         for _ in range(args.steps):
             b.copy_(a)
         torch.cuda.synchronize()
+        marker.random_()
+        torch.cuda.synchronize()
         print(json.dumps({"only": "copy", "bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
                           "launches": args.steps}))
         return
-    step = ConfigStep(args.workload, dev) if args.workload != "dispatch" else Step(make_inputs(dev))
-    j = step.names.index(args.only)
-    calls = step.calls()
-    for c in calls[:j]:
-        c()
+    n = int(args.workload[3:])
+    path = Path(n, dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    for c in path.calls:
+        c.fn()
+    segments = []
+    for c in path.calls:
+        torch.cuda.synchronize()
+        marker.random_()
+        torch.cuda.synchronize()
+        reps = args.steps if getattr(c, "record", True) else 1
+        for _ in range(reps):
+            evict_mall(flush)
+            c.fn()
+        segments.append(dict(call=c.name if getattr(c, "record", True) else None, launches=reps, bytes=c.bytes,
+                             elements=c.elements, source_hash=kernel_source_hash(c.name)))
     torch.cuda.synchronize()
     marker.random_()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        calls[j]()
-    torch.cuda.synchronize()
-    if hasattr(step, "bytes"):
-        nbytes = step.bytes[args.only]
-    else:
-        i = step.inp
-        nbytes = algorithmic_bytes(i["T"], i["H"], i["k"], i["E"], step.r_cap, i["R"], i["R"], i["F"])[args.only]
-    print(json.dumps({"only": args.only, "workload": args.workload, "launches": args.steps,
-                      "algorithmic_bytes_per_launch": nbytes}))
+    print(json.dumps({"counters_pass": args.workload, "segments": segments}))
+
+
+def emit(out, args):
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
 
 
 def main():
@@ -610,50 +516,51 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
                                    "(multi-GPU expert-parallel transport is not part of it)"}))
         sys.exit(2)
+    import workloads
+    configs = [int(c) for c in args.configs.split(",") if c]
+    if args.workload:
+        configs = [int(args.workload[3:])]
+    w3 = workloads.config3() if (args.workload is None or args.workload == "cfg3") and not args.counters_pass \
+        else None
+    cpu = None
+    if w3 is not None and not args.no_cpu_baseline and args.workload is None:
+        cpu = cpu_baseline(w3, args.cpu_sample_tokens)           # on the host, before the GPU is touched
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.only is not None:
-        return main_only(args, dev)
-    if args.workload != "dispatch":
-        return main_config(args, dev)
-    inp = make_inputs(dev)
-    step = Step(inp)
-    ms_step, per_ms = time_step(step, args)
-    T, H, k, E, R, F = (inp[s] for s in ("T", "H", "k", "E", "R", "F"))
-    by = algorithmic_bytes(T, H, k, E, step.r_cap, R, R, F)
-    total = sum(by.values())
-    value = total / (ms_step / 1e3) / 1e9
-    kernels = {nm: dict(ms=round(per_ms[nm], 5), bytes=by[nm], gbs=round(by[nm] / (per_ms[nm] / 1e3) / 1e9, 1),
-                        frac=round(by[nm] / (per_ms[nm] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)) for nm in step.names}
-    for nm in step.names:
-        kernels[nm]["traffic"] = traffic_from_profile(nm)
-    # the dominant kernel: the call with the largest share of the step's time
-    dom = max(step.names, key=lambda nm: per_ms[nm])
-    roofline = roofline_of(dom, by[dom], per_ms[dom], elements=T * H)
-    roofline["dominant_by"] = "largest per-call time in the step"
-    out = {
-        "metric": "quantize/pack/receive GB/s (in+out) on 1 MI355X; % of HBM peak",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16->nvfp4/mxfp8", "data": "synthetic",
-        "config": {"workload": "dispatch-4096x4096-e8-top2-zipf1.2 (+ SR combine-bwd grads, grouped dSwiGLU ffn 2048)",
-                   "tokens": T, "hidden": H, "experts": E, "top_k": k, "alignment": inp["A"],
-                   "bytes_per_step": total, "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": roofline,
-        "kernels": kernels,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
-    else:
-        out["cpu_baseline"] = None
-    line = json.dumps(out)
-    print(line, flush=True)
-    if args.json_out:
-        with open(args.json_out, "w") as f:
-            f.write(line + "\n")
+    if args.counters_pass:
+        return main_counters_pass(args, dev)
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: 4x the MALL
+    kernels = {}
+    head = None
+    for n in configs:
+        path = Path(n, dev, w3 if n == 3 else None)
+        per = time_calls(path, args.reps, flush)
+        kernels[f"cfg{n}"] = config_kernels(n, path, per)
+        if n == 3 and args.workload in (None, "cfg3"):
+            ms_step, step_per = time_step(path, args.steps, args.warmup)
+            head = (path, ms_step, step_per)
+        elif args.workload is not None:
+            calls = path.step_calls()
+            ms_step, step_per = time_step(path, args.steps, args.warmup)
+            total = sum(c.bytes for c in calls)
+            emit({"metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+                  "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->nvfp4",
+                  "data": "synthetic", "config": dict(path.desc, bytes_per_step=total),
+                  "step_ms": {nm: round(v, 5) for nm, v in step_per.items()}, "kernels": kernels,
+                  "cpu_baseline": None}, args)
+            return
+        del path
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if head is None:
+        p3 = Path(3, dev, w3)
+        head = (p3,) + time_step(p3, args.steps, args.warmup)
+    path3, ms_step, step_per = head
+    emit(headline(path3, ms_step, step_per, args.steps, args.warmup, kernels, cpu), args)
 
 
 if __name__ == "__main__":

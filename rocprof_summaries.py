@@ -3,15 +3,20 @@
 Run on a machine with an MI355X and rocprofv3, from the repository root; this
 process itself never touches the GPU (every GPU run is a rocprofv3 child).
 
-  python rocprof_summaries.py traffic [--workload dispatch] [--raw DIR]
-      For every call of the step: one FETCH_SIZE run and one WRITE_SIZE run
-      (one counter per run) of `bench.py --only CALL`; the dispatches after
-      bench's marker kernel are CALL's.  A 1 GiB device copy measured the same
-      way gives the scale of each counter (bytes moved / counter KiB).
-      -> profiles/traffic_counters.json (per call: KiB per launch as read,
-      scaled HBM bytes per launch, the hash of the call's kernel sources).
-  python rocprof_summaries.py trace [--workload dispatch] [--raw DIR] [--steps K]
-      Kernel-trace statistics of a bench run -> profiles/kernel_trace_<workload>.md
+  python rocprof_summaries.py counters [--configs 1,2,3,4,5] [--raw DIR]
+      Per configuration, three rocprofv3 --pmc runs of `bench.py --counters-pass
+      --workload cfgN` (every call of the configuration, each K times between
+      marker kernels, each launch after a MALL-evicting read): FETCH_SIZE;
+      WRITE_SIZE; TCC_EA0_RDREQ_DRAM_sum + TCC_EA0_WRREQ_DRAM_sum +
+      SQ_INSTS_VALU.  A 1 GiB device-to-device copy measured the same way gives
+      the bytes per counted unit of each memory counter.
+      -> profiles/counters.json (per call and configuration, per launch: the
+      counters as read, HBM bytes = FETCH and WRITE scaled by the copy, DRAM
+      request bytes scaled the same way, issued VALU instructions, and the hash
+      of the call's kernel sources) and profiles/counters_cfgN.md.
+  python rocprof_summaries.py trace --workload cfgN [--raw DIR] [--steps K]
+      Kernel-trace statistics of `bench.py --workload cfgN`
+      -> profiles/kernel_trace_<workload>.md
 """
 
 import argparse
@@ -27,9 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (imports no GPU state)
 
-WORKLOAD_NAMES = {"dispatch": "dispatch_4096x4096_e8_top2", "cfg1": "roundtrip_256x1024_e4_top1",
-                  "cfg2": "dispatch_4096x4096_e8_top2_cfg", "cfg3": "dsv3_16384x7168_e32_top8",
-                  "cfg4": "combine_bwd_sr_32768x4096_e16_top2", "cfg5": "dswiglu_fc1grad_14841x2x2048_e8"}
+WORKLOAD_NAMES = {"cfg1": "roundtrip_256x1024_e4_top1", "cfg2": "dispatch_4096x4096_e8_top2",
+                  "cfg3": "dsv3_16384x7168_e32_top8", "cfg4": "combine_bwd_sr_32768x4096_e16_top2",
+                  "cfg5": "dswiglu_fc1grad_14841x2x2048_e8"}
+GROUPS = (("FETCH_SIZE",), ("WRITE_SIZE",), ("TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_DRAM_sum", "SQ_INSTS_VALU"))
 
 
 def run(cmd, timeout):
@@ -42,56 +48,103 @@ def run(cmd, timeout):
     return r.stdout
 
 
-def pmc_pass(counter, only, workload, steps, raw):
-    out = os.path.join(raw, f"pmc_{only}_{counter}")
-    cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--",
-           sys.executable, os.path.join(ROOT, "bench.py"), "--only", only, "--workload", workload,
-           "--steps", str(steps)]
-    run(cmd, 240)
+def _is_marker(name):
+    return "distribution" in name or "random" in name.lower()
+
+
+def pmc_run(counters, workload, steps, raw, copy=False):
+    """One rocprofv3 --pmc run of a counters pass; returns (per segment: {counter: value
+    summed over the segment's dispatches and dimensions}, per segment kernel names,
+    the pass's JSON line, the command as shown in the summaries)."""
+    tag = "copy" if copy else workload
+    out = os.path.join(raw, f"pmc_{tag}_{'_'.join(counters)}")
+    bench_args = ["--counters-pass", "--steps", str(steps)] + (["--only", "copy"] if copy else ["--workload", workload])
+    cmd = ["rocprofv3", "--pmc"] + list(counters) + ["--output-format", "csv", "-d", out, "-o", "run", "--",
+                                                      sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
+    text = run(cmd, 600)
+    line = json.loads(next(ln for ln in text.splitlines() if ln.startswith("{\"")))
     rows = list(csv.DictReader(open(os.path.join(out, "run_counter_collection.csv"))))
-    per = {}
-    names = {}
+    disp = {}
     for r in rows:
-        d = int(r["Dispatch_Id"])
-        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])  # summed over the counter's dimensions
-        names[d] = r["Kernel_Name"]
-    marks = [d for d, n in names.items() if "distribution" in n or "random" in n.lower()]
-    if not marks:
-        raise SystemExit(f"marker kernel not found in {out}")
-    after = sorted(d for d in per if d > max(marks))
-    kib = sum(per[d] for d in after) / steps
-    kernels = sorted({names[d].split("(")[0].replace("void ", "") for d in after})
-    shown = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", "OUT", "-o", "run", "--", "python3",
-             "bench.py", "--only", only, "--workload", workload, "--steps", str(steps)]
-    return kib, kernels, " ".join(shown)
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(name=r["Kernel_Name"], ctr={}))
+        d["ctr"][r["Counter_Name"]] = d["ctr"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(disp)
+    marks = [i for i in ids if _is_marker(disp[i]["name"])]
+    segs = []
+    for a, b in zip(marks, marks[1:]):
+        tot, names = {}, set()
+        for i in ids:
+            if a < i < b and "reduce_kernel" not in disp[i]["name"] and "fillBuffer" not in disp[i]["name"]:
+                names.add(disp[i]["name"].split("(")[0].replace("void ", ""))
+                for c, v in disp[i]["ctr"].items():
+                    tot[c] = tot.get(c, 0.0) + v
+        segs.append((tot, sorted(names)))
+    shown = " ".join(["rocprofv3", "--pmc"] + list(counters) + ["--output-format", "csv", "-d", "OUT", "-o", "run",
+                                                              "--", "python3", "bench.py"] + bench_args)
+    return segs, line, shown
 
 
-def traffic(args):
+def counters(args):
     raw = args.raw or tempfile.mkdtemp(prefix="mtb_pmc_")
     steps = 5
-    ref = {}
     cmds = []
-    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-        kib, _, cmd = pmc_pass(ctr, "copy", "dispatch", steps, raw)
-        ref[ctr] = (1 << 30) / (kib * 1024.0)  # bytes moved per counted byte
-        cmds.append(cmd)
-    names = bench.STEP_NAMES if args.workload == "dispatch" else args.calls.split(",")
-    calls = {}
-    for nm in names:
-        f, kernels, c1 = pmc_pass("FETCH_SIZE", nm, args.workload, steps, raw)
-        w, _, c2 = pmc_pass("WRITE_SIZE", nm, args.workload, steps, raw)
-        cmds += [c1, c2]
-        calls[nm] = dict(kernels=kernels, fetch_kib_per_launch=round(f, 1), write_kib_per_launch=round(w, 1),
-                         hbm_bytes_per_launch=int(f * 1024 * ref["FETCH_SIZE"] + w * 1024 * ref["WRITE_SIZE"]),
-                         source_hash=bench.kernel_source_hash(nm))
-    doc = dict(workload=args.workload, date=datetime.date.today().isoformat(),
-               method="FETCH_SIZE and WRITE_SIZE in separate rocprofv3 --pmc runs, KiB summed over each "
-                      "dispatch's dimensions, averaged over the launches after bench's marker; each scaled by "
-                      "bytes/counted-byte of a 1 GiB device-to-device copy",
-               copy_reference=dict(fetch_scale=round(ref["FETCH_SIZE"], 4), write_scale=round(ref["WRITE_SIZE"], 4)),
-               calls=calls, commands=cmds)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    ref = {}
+    for g in GROUPS:
+        segs, line, shown = pmc_run(g, None, steps, raw, copy=True)
+        cmds.append(shown)
+        tot = segs[0][0]
+        for c in g:
+            if c in ("FETCH_SIZE", "TCC_EA0_RDREQ_DRAM_sum"):
+                ref[c] = line["bytes_read"] * steps / (tot[c] * (1024.0 if c == "FETCH_SIZE" else 1.0))
+            elif c in ("WRITE_SIZE", "TCC_EA0_WRREQ_DRAM_sum"):
+                ref[c] = line["bytes_written"] * steps / (tot[c] * (1024.0 if c == "WRITE_SIZE" else 1.0))
+    path = os.path.join(args.out_dir, "counters.json")
+    prev = os.path.join(ROOT, "profiles", "counters.json")
+    doc = json.load(open(path if os.path.exists(path) else prev)) if os.path.exists(path) or os.path.exists(prev) \
+        else {}
+    calls = doc.get("calls", {})
+    for n in [int(c) for c in args.configs.split(",") if c]:
+        wl = f"cfg{n}"
+        per = {}
+        for g in GROUPS:
+            segs, line, shown = pmc_run(g, wl, steps, raw)
+            cmds.append(shown)
+            for (tot, names), seg in zip(segs, line["segments"]):
+                if seg["call"] is None:
+                    continue
+                rec = per.setdefault(seg["call"], dict(kernels=names, launches=seg["launches"],
+                                                       algorithmic_bytes=seg["bytes"], source_hash=seg["source_hash"]))
+                for c in g:
+                    rec[c] = tot.get(c, 0.0) / seg["launches"]
+        lines = [f"# Counters per launch: bench.py --counters-pass --workload {wl}", "",
+                 f"Date {datetime.date.today().isoformat()}.  Each call {steps} times, each launch after a read of a "
+                 "1 GiB buffer that evicts the MALL; values summed over the counter's dimensions and the call's "
+                 "dispatches, divided by the launches.  HBM bytes = FETCH_SIZE KiB x 1024 x "
+                 f"{ref['FETCH_SIZE']:.3f} + WRITE_SIZE KiB x 1024 x {ref['WRITE_SIZE']:.3f} (the bytes a 1 GiB "
+                 "device copy moves per counted byte); DRAM bytes = the TCC_EA0 DRAM read/write requests scaled "
+                 f"by the same copy ({ref['TCC_EA0_RDREQ_DRAM_sum']:.1f} / {ref['TCC_EA0_WRREQ_DRAM_sum']:.1f} "
+                 "bytes per request).  Both count what leaves the L2 for the memory side; MALL hits are not "
+                 "separated by any counter here.", "", "Commands (from the repository root):", "", "```"]
+        lines += [c for c in cmds if wl in c or "copy" in c] + ["```", "",
+                  "| call | kernels | algorithmic MB | HBM MB (fetch+write) | ratio | DRAM MB (rd+wr) | ratio | "
+                  "VALU instr | VALU / element |", "|---|---|---|---|---|---|---|---|---|"]
+        for call, rec in per.items():
+            hbm = rec["FETCH_SIZE"] * 1024 * ref["FETCH_SIZE"] + rec["WRITE_SIZE"] * 1024 * ref["WRITE_SIZE"]
+            dram = (rec["TCC_EA0_RDREQ_DRAM_sum"] * ref["TCC_EA0_RDREQ_DRAM_sum"]
+                    + rec["TCC_EA0_WRREQ_DRAM_sum"] * ref["TCC_EA0_WRREQ_DRAM_sum"])
+            rec.update(hbm_bytes=int(hbm), dram_bytes=int(dram), valu_insts=int(rec["SQ_INSTS_VALU"]))
+            seg = next(s for s in line["segments"] if s["call"] == call)
+            vpe = (f"{rec['valu_insts'] * 64 / seg['elements']:.1f}" if seg.get("elements") else "")
+            lines.append(f"| {call} | {', '.join('`' + k + '`' for k in rec['kernels'])} | "
+                         f"{rec['algorithmic_bytes'] / 1e6:.1f} | {hbm / 1e6:.1f} | {hbm / rec['algorithmic_bytes']:.2f} | "
+                         f"{dram / 1e6:.1f} | {dram / rec['algorithmic_bytes']:.2f} | {rec['valu_insts']:.3g} | {vpe} |")
+            calls[f"{wl}/{call}"] = rec
+        with open(os.path.join(args.out_dir, f"counters_{wl}_{WORKLOAD_NAMES[wl]}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    doc = dict(date=datetime.date.today().isoformat(),
+               method="bench.py --counters-pass under rocprofv3 --pmc, three counter groups per configuration; "
+                      "memory counters scaled by a 1 GiB device-to-device copy",
+               copy_reference={k: round(v, 4) for k, v in ref.items()}, calls=calls)
     with open(path, "w") as fh:
         json.dump(doc, fh, indent=1)
         fh.write("\n")
@@ -101,7 +154,7 @@ def traffic(args):
 def trace(args):
     raw = args.raw or tempfile.mkdtemp(prefix="mtb_trace_")
     out = os.path.join(raw, f"trace_{args.workload}")
-    bench_args = ["--workload", args.workload, "--steps", str(args.steps), "--warmup", "3", "--no-cpu-baseline"]
+    bench_args = ["--workload", args.workload, "--steps", str(args.steps), "--warmup", "5", "--no-cpu-baseline"]
     cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out, "-o", "run", "--",
            sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
     text = run(cmd, 600)
@@ -110,42 +163,40 @@ def trace(args):
     shown = " ".join(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", "OUT", "-o", "run",
                       "--", "python3", "bench.py"] + bench_args)
     md = [f"# Kernel trace: bench.py --workload {args.workload}", "",
-          "Command (from the repository root, via `python rocprof_summaries.py trace --workload "
-          f"{args.workload}`):", "", "```", shown, "```", "",
-          "All dispatches of the run: warm-up, the graph replays of the timed region and the eager per-call "
-          "passes (each pass preceded by a 1 GiB read that evicts the MALL; the reduce_kernel row).", "",
+          f"Date {datetime.date.today().isoformat()}.  Command (from the repository root, via "
+          f"`python rocprof_summaries.py trace --workload {args.workload}`):", "", "```", shown, "```", "",
+          "All dispatches of the run: the per-call passes (each after a 1 GiB read that evicts the MALL: the "
+          "reduce_kernel rows) and the eager steps of the timed region.", "",
           "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].split("(")[0].replace("void ", "")
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    # the eager per-call passes: every dispatch from the first 1 GiB read on runs alone
-    # (one stream, nothing concurrent), so these durations compare with the bench's
-    # per-call figures; the graph replays before them overlap calls on four streams
+    # the timed region: every dispatch after the last marker kernel (bench.time_step launches one
+    # right before its timed steps)
     trace_rows = list(csv.DictReader(open(os.path.join(out, "run_kernel_trace.csv"))))
     trace_rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    dur = [(r["Kernel_Name"].split("(")[0].replace("void ", ""),
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace_rows]
-    first_sweep = next((i for i, (n, us) in enumerate(dur) if "reduce_kernel" in n and us > 50.0), None)
-    if first_sweep is not None:
-        eager = {}
-        for n, us in dur[first_sweep:]:
-            if "reduce_kernel" in n or "fillBuffer" in n:     # the read and its reduction's semaphore clear
-                continue
-            eager.setdefault(n, []).append(us)
-        md += ["", "Eager per-call passes only (each call alone, each pass after the MALL-evicting read; compare with the bench's "
-               "per-call times below):", "", "| kernel | dispatches | avg us | min us |", "|---|---|---|---|"]
-        for n, v in eager.items():
-            md.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
+    last_mark = max(i for i, r in enumerate(trace_rows) if _is_marker(r["Kernel_Name"]))
+    per = {}
+    for r in trace_rows[last_mark + 1:]:
+        nm = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        per.setdefault(nm, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    md += ["", f"Timed region ({args.steps} eager steps; every dispatch after the marker kernel bench.py launches "
+           "right before it):", "", "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for nm, v in per.items():
+        md.append(f"| `{nm}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     if line:
         d = json.loads(line)
-        md += ["", "Bench line of the same profiled run (HIP-event per-call times, MALL flushed):", "",
-               "| call | us | algorithmic MB | GB/s | frac of 8 TB/s |", "|---|---|---|---|---|"]
-        for nm, k in d["kernels"].items():
-            md.append(f"| {nm} | {k['ms'] * 1e3:.1f} | {k['bytes'] / 1e6:.1f} | {k['gbs']} | {k['frac']} |")
-        md += ["", f"Step: {d['ms_per_step'] * 1e3:.1f} us, {d['value']} GB/s (graph replay)."]
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{WORKLOAD_NAMES[args.workload]}.md")
+        md += ["", "Bench line of the same profiled run (HIP events):", "",
+               "| call | us per launch (per-call passes) | algorithmic MB | GB/s | frac of 8 TB/s |",
+               "|---|---|---|---|---|"]
+        for cfg, v in d["kernels"].items():
+            for nm, k in v["calls"].items():
+                md.append(f"| {nm} | {k['ms'] * 1e3:.1f} | {k['bytes'] / 1e6:.1f} | {k['gbs']} | {k['frac']} |")
+        step_ms = d.get("step_ms") or d.get("config", {}).get("step_ms", {})
+        md += ["", f"Step (timed region): {d['ms_per_step'] * 1e3:.1f} us, {d['value']} GB/s; per call (HIP events) "
+               + ", ".join(f"{nm} {v * 1e3:.1f} us" for nm, v in step_ms.items()) + "."]
+    path = os.path.join(args.out_dir, f"kernel_trace_{WORKLOAD_NAMES[args.workload]}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("wrote", path)
@@ -153,16 +204,19 @@ def trace(args):
 
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["traffic", "trace"])
-    p.add_argument("--workload", default="dispatch", choices=list(WORKLOAD_NAMES))
-    p.add_argument("--calls", default="", help="comma-separated calls (non-dispatch workloads)")
+    p.add_argument("what", choices=["counters", "trace"])
+    p.add_argument("--workload", default="cfg3", choices=list(WORKLOAD_NAMES))
+    p.add_argument("--configs", default="1,2,3,4,5")
     p.add_argument("--raw", default=None, help="directory for rocprofv3's raw output (default: a temp dir)")
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"), help="where the summaries go")
     args = p.parse_args()
+    args.out_dir = os.path.abspath(args.out_dir)
+    os.makedirs(args.out_dir, exist_ok=True)
     if args.raw:
         args.raw = os.path.abspath(args.raw)
         os.makedirs(args.raw, exist_ok=True)
-    traffic(args) if args.what == "traffic" else trace(args)
+    counters(args) if args.what == "counters" else trace(args)
 
 
 if __name__ == "__main__":
