@@ -249,34 +249,6 @@ __device__ __forceinline__ void col_encode_sr(const float* y, const ColQuant& q,
   w1 = sr_codes8(u + 8, n0 + 8, klo, khi, q.scale);
 }
 
-// SR: the stream position of the block's row 0 in column c is n_col + c * n_step
-// (the code's index in the columnwise code array plus the counter base).
-template <int SEL, bool SLOW, bool SR>
-__device__ __forceinline__ void column_pair(const uint32_t* cw, const float* cm, const int* ce, int dexp,
-                                            const RcpEntry* tab, uint2* stage_codes, uint32_t* stage_sc, int col0,
-                                            int m, uint64_t n_col, uint64_t n_step, uint32_t klo, uint32_t khi) {
-  float z0[16], z1[16];
-  decode_stage1<SEL, SLOW>(cw, cm, ce, z0, z1);
-  rht16_upper(z0);
-  rht16_upper(z1);
-  const ColQuant q0 = SLOW ? col_block_quant(absmax16(z0), dexp, tab) : col_block_quant_fast(absmax16(z0), dexp, tab);
-  const ColQuant q1 = SLOW ? col_block_quant(absmax16(z1), dexp, tab) : col_block_quant_fast(absmax16(z1), dexp, tab);
-  uint32_t a0, a1, b0, b1;
-  if (!SR) {
-    col_encode(z0, q0, a0, a1);
-    col_encode(z1, q1, b0, b1);
-  } else {
-    const uint64_t n0 = n_col + (uint64_t)(col0 + 2 * SEL) * n_step;
-    col_encode_sr(z0, q0, n0, klo, khi, a0, a1);
-    col_encode_sr(z1, q1, n0 + n_step, klo, khi, b0, b1);
-  }
-  const int c0 = col0 + 2 * SEL, c1 = c0 + 1;
-  stage_codes[stage_at(c0, m)] = make_uint2(a0, a1);
-  stage_codes[stage_at(c1, m)] = make_uint2(b0, b1);
-  stage_sc[stage_at(c0, m)] = q0.sc;
-  stage_sc[stage_at(c1, m)] = q1.sc;
-}
-
 // Where the kernel reads a row's codes, scales and t: the packed rows
 // gathered through src_row (the direct receive), or the grouped rowwise
 // operand itself (GROUPED: grouped row g is its own source).
@@ -287,13 +259,30 @@ struct RowSrc {
   uint32_t cstride, sstride, tstride;  // bytes between consecutive rows
 };
 
-// One workgroup per 256 grouped rows x 128 columns; 1-D grid of
-// row_tiles * col_tiles workgroups.  Workgroup i runs on XCD i % 8, so the
-// logical tile is taken from a contiguous range per XCD, column tile
-// fastest: all column tiles of a row tile run on one XCD at about the same
-// time, and the halves of each 128-byte code line, the scale lines and the
-// token scales they share are fetched into that XCD's L2 once (and partial
-// line writes of the rowwise scales merge there).
+// ------------------------------------------------------------------ one-pass receive, 256 x 256 tiles
+// One workgroup per 256 grouped rows x 256 columns (four waves):
+//   * the rowwise operand: thread t moves 16-byte pieces of rows (t >> 3) +
+//     32 i, so eight threads write one row's 128 code bytes -- whole lines when
+//     H is a multiple of 256, streamed past the caches (nothing in the path
+//     reads them again) -- and row t's scale bytes and token scale;
+//   * the columnwise operand: wave w owns the 16-column groups cg = 4w .. 4w+3
+//     of all sixteen 16-row blocks; lane (m, j) = (lane >> 2, lane & 3)
+//     gathers the 8 code bytes of column group 4w + j of the 16 rows of block
+//     m (16 rows x 32 contiguous bytes per load instruction), decodes them,
+//     runs the RHT and quantizes its 16 columns in registers, and stores each
+//     column's 8 code bytes and scale byte straight to the operand: the sixteen
+//     blocks of a column sit in one wave, so every store instruction writes
+//     four columns' contiguous 128 code bytes.  In the K-blocked layout a
+//     K-block's columnwise output is one contiguous, line-aligned region, and
+//     its code bytes are streamed too.
+// The row copy's loads and the gathers go out together (the same bytes: the L2
+// merges their misses) and the copy is stored before the tile's one barrier,
+// which hands row t's token scale and the tile's 16 scale bytes to the decode
+// through LDS.
+// 1-D grid of row_tiles * col_tiles workgroups.  Workgroup i runs on XCD
+// i % 8, so the logical tile is taken from a contiguous range per XCD, column
+// tile fastest: the column tiles of a row tile run on one XCD at about the
+// same time and share the scale lines and token scales in its L2.
 // KBLOCK: the columnwise operand in K-blocks -- each expert's grouped rows in
 // blocks of 256 (the last one shorter, a multiple of 16), block kb of expert e
 // an [H, len/2] code matrix at byte H*off_e/2 + 128*H*kb (scales [H, len/16]
@@ -302,48 +291,68 @@ struct RowSrc {
 // SR (the compact layout only): stochastic columnwise codes, the code of
 // column h and grouped row g of expert e at stream position counter_base +
 // H*off_e + h*P_e + (g - off_e) -- its index in col_codes, two per byte.
+constexpr int kT2Rows = 256, kT2Cols = 256, kT2Threads = 256;
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+template <int SEL, bool SLOW, bool SR>
+__device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float* cm, const int* ce, int dexp,
+                                                const RcpEntry* tab, uint64_t n0, uint64_t n_step, uint32_t klo,
+                                                uint32_t khi, uint2& c0, uint2& c1, uint32_t& s0, uint32_t& s1) {
+  float z0[16], z1[16];
+  decode_stage1<SEL, SLOW>(cw, cm, ce, z0, z1);
+  rht16_upper(z0);
+  rht16_upper(z1);
+  const ColQuant q0 = SLOW ? col_block_quant(absmax16(z0), dexp, tab) : col_block_quant_fast(absmax16(z0), dexp, tab);
+  const ColQuant q1 = SLOW ? col_block_quant(absmax16(z1), dexp, tab) : col_block_quant_fast(absmax16(z1), dexp, tab);
+  if (!SR) {
+    col_encode(z0, q0, c0.x, c0.y);
+    col_encode(z1, q1, c1.x, c1.y);
+  } else {
+    col_encode_sr(z0, q0, n0, klo, khi, c0.x, c0.y);
+    col_encode_sr(z1, q1, n0 + n_step, klo, khi, c1.x, c1.y);
+  }
+  s0 = q0.sc;
+  s1 = q1.sc;
+}
+
 template <bool GROUPED, bool KBLOCK, bool SR = false>
-__global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
-                                                       const int32_t* __restrict__ offsets, int E,
-                                                       const int32_t* __restrict__ src_row, int r_cap, int n_ct,
-                                                       uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-                                                       float* __restrict__ row_t, uint8_t* __restrict__ col_codes,
-                                                       uint8_t* __restrict__ col_scales,
-                                                       const float* __restrict__ col_scale,
-                                                       const uint64_t* __restrict__ sr_state) {
-  __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block ^ swizzle] 8 code bytes; offsets first
-  __shared__ uint32_t stage_sc[kTileCols * kBlocks];   // [column][block ^ swizzle] scale code
+__global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
+                                                              const int32_t* __restrict__ offsets, int E,
+                                                              const int32_t* __restrict__ src_row, int r_cap, int n_ct,
+                                                              uint8_t* __restrict__ row_codes,
+                                                              uint8_t* __restrict__ row_scales,
+                                                              float* __restrict__ row_t, uint8_t* __restrict__ col_codes,
+                                                              uint8_t* __restrict__ col_scales,
+                                                              const float* __restrict__ col_scale,
+                                                              const uint64_t* __restrict__ sr_state) {
+  __shared__ int s_offs[1025];
+  __shared__ int s_edexp[1024];        // decode exponent of each expert's D_e
   __shared__ RcpEntry s_tab[128];
-  __shared__ int s_src[kTileRows];
-  __shared__ float s_t[kTileRows];
-  __shared__ float s_tq[kTileRows];                    // t * d_i / 4 (i = row mod 16)
-  __shared__ uint32_t s_sw[kTileRows][2];              // the tile's 8 scale bytes of each row
-  __shared__ int s_dexp[kBlocks], s_slow[kBlocks], s_live[kBlocks];
-  __shared__ uint64_t s_cbase[kBlocks], s_sbase[kBlocks];
-  __shared__ uint32_t s_cstr[kBlocks], s_sstr[kBlocks];
-  int* s_offs = reinterpret_cast<int*>(stage_codes);  // offsets[0..E] until the column phase
+  __shared__ float s_t[kT2Rows];
+  __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 scale bytes of each row
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
   const unsigned xq = nb / kXcds, xr = nb % kXcds, x = bx % kXcds;
   const unsigned lt = x * xq + min(x, xr) + bx / kXcds;
   const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
-  const int col0 = ct * kTileCols;
-  const int ncols = min(kTileCols, H - col0);
-  int g_base = rt * kTileRows;  // first grouped row of the tile
-  int kb = 0, tile_rows = kTileRows;
+  const int col0 = ct * kT2Cols;
+  const int ncols = min(kT2Cols, H - col0);  // 64, 128, 192 or 256
+  int g_base = rt * kT2Rows;
+  int kb = 0, tile_rows = kT2Rows;
   if (KBLOCK) {
     // the tile is K-block rt of the concatenated per-expert K-block lists
     __shared__ int s_kbstart[1025];
-    __shared__ int s_wsum[kThreads / 64];
-    for (int i = tid; i <= E; i += kThreads) s_offs[i] = offsets[i];
+    __shared__ int s_wsum[kT2Threads / 64];
+    for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
     __syncthreads();
     int loc[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * tid + i;
       loc[i] = sum;
-      sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kTileRows - 1) / kTileRows : 0;
+      sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kT2Rows - 1) / kT2Rows : 0;
     }
     int incl = sum;
     const int lane = tid & 63;
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
     __syncthreads();
     int wofs = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < kT2Threads / 64; ++w) {
       wofs += w < (tid >> 6) ? s_wsum[w] : 0;
       total += s_wsum[w];
     }
@@ -372,191 +381,232 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_receive(const RowSrc rs, int
       if (s_kbstart[mid] <= rt) lo = mid; else hi = mid - 1;
     }
     kb = rt - s_kbstart[lo];
-    g_base = s_offs[lo] + kb * kTileRows;
-    tile_rows = min(kTileRows, s_offs[lo + 1] - g_base);
+    g_base = s_offs[lo] + kb * kT2Rows;
+    tile_rows = min(kT2Rows, s_offs[lo + 1] - g_base);
   }
 
-  // phase 1: source rows, expert offsets and decode exponents, the reciprocal
-  // table.  The three loads go out together (clamped indices, results
-  // selected afterwards), so the phase waits for one memory round trip.
-  // src_row is -1 for padding and from off_E to r_cap.
-  int* s_edexp = s_offs + 1040;  // decode exponent of each expert (E <= 1024)
-  {
-    const int g = g_base + tid;
-    const int sl = GROUPED ? g : src_row[min(g, r_cap - 1)];
-    const int io = min(tid, E), ie = min(tid, E - 1);
-    const int o = offsets[io];
-    const float cs = col_scale[ie];
-    const int src = g < r_cap ? sl : -1;
-    s_src[tid] = (src >= 0 && src < T) ? src : -1;
-    s_offs[io] = o;  // threads past E rewrite the last entry with its own value
-    s_edexp[ie] = pow2_exponent(cs);
-    for (int i = tid + kThreads; i <= E; i += kThreads) {
-      s_offs[i] = offsets[i];
-      if (i < E) s_edexp[i] = pow2_exponent(col_scale[i]);
-    }
-    for (int i = tid; i < 128; i += kThreads) s_tab[i] = rcp_entry(i);
-  }
-  __syncthreads();
-  const int off_end = min(s_offs[E], r_cap & ~15);  // whole 16-row blocks inside the outputs
-  const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
+  const int lane = tid & 63, w = tid >> 6;
+  const int m = lane >> 2;                    // 16-row block of the column phase
+  const int cg = 4 * w + (lane & 3);          // 16-column group of the column phase
+  const int gb = g_base + 16 * m;
+  const bool col_live = 16 * cg < ncols;
+  const int cgc = col_live ? cg : 0;          // clamped: a dead group re-reads group 0
 
-  // phase 2a: each 16-row block's expert -> its decode exponent and output bases.
-  if (tid < kBlocks) {
-    const int gb = g_base + 16 * tid;
-    int live = gb < tile_end;
-    int e = 0;
-    if (live) {
-      int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
+  // expert offsets, decode exponents and the reciprocal table into LDS
+  for (int i = tid; i <= E; i += kT2Threads) {
+    s_offs[i] = offsets[i];
+    if (i < E) s_edexp[i] = pow2_exponent(col_scale[i]);
+  }
+  if (tid < 128) s_tab[tid] = rcp_entry(tid);
+  const int off_end_g = offsets[E];
+
+  // the loads: the row-copy pieces (16 bytes of rows (tid >> 3) + 32 i), this
+  // thread's row (t and the tile's scale bytes) and its block's 16 code gathers,
+  // all issued before the first wait at clamped indices; the copy's pieces are
+  // the same bytes as the gathers', so the L2 merges their misses
+  const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces per row: 2, 4, 6 or 8
+  int csrc[8];
+  u32x4v cv[8];
+  if (!GROUPED) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gr = g_base + (tid >> 3) + 32 * i;
+      const int sv = src_row[min(gr, r_cap - 1)];
+      csrc[i] = (gr < r_cap && sv >= 0 && sv < T) ? sv : -1;
     }
-    s_live[tid] = live;
-    if (live) {
-      const int off = s_offs[e], len = s_offs[e + 1] - off;
-      s_dexp[tid] = s_edexp[e];
-      if (KBLOCK) {
-        s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * tid;
-        s_cstr[tid] = (uint32_t)(tile_rows >> 1);
-        s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint64_t)H * 16u * (uint32_t)kb + (uint32_t)tid;
-        s_sstr[tid] = (uint32_t)(tile_rows >> 4);
-      } else {
-        s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
-        s_cstr[tid] = (uint32_t)(len >> 1);
-        s_sbase[tid] = (uint64_t)H * (uint32_t)(off >> 4) + (uint32_t)((gb - off) >> 4);
-        s_sstr[tid] = (uint32_t)(len >> 4);
-      }
+    if (T > 0) {
+      const uint8_t* cbase0 = rs.codes + (col0 >> 1) + 16 * (cq < nq ? cq : 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        cv[i] = *reinterpret_cast<const u32x4v*>(cbase0 + (size_t)(uint32_t)max(csrc[i], 0) * rs.cstride);
     }
   }
-
-  // phase 2b (one row per thread: t and the tile's scale words) and phase 2c
-  // (thread (cg, m): the code dwords of columns [8cg, 8cg+8) of the 16 rows
-  // of block m; a wave reads 4 rows x 64 contiguous bytes per instruction).
-  // Every load of both goes out before the first wait, at clamped indices:
-  // rows without a source read row 0 and are zeroed, a 64-column tile reads
-  // its first eight code dwords twice.  Then t and the scale words go to LDS
-  // and to the rowwise operand, and the code dwords, unchanged, to the
-  // rowwise operand.
-  const int cg = tid & 15, m = tid >> 4;
-  const int r0 = 16 * m;
-  const int gb = g_base + r0;
-  const bool live = gb < tile_end && cg * 8 < ncols;
-  uint32_t cw[16];
+  uint2 cw2[16];
   float t = 0.0f;
-  uint32_t sw0 = 0, sw1 = 0;
+  uint4 sw = make_uint4(0, 0, 0, 0);
+  const int g = g_base + tid;
+  int src = -1;
   if (T > 0) {
-    const int src = s_src[tid];
+    int sl[16];
+    if (GROUPED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sl[i] = gb + i < r_cap ? gb + i : -1;
+      src = g < r_cap ? g : -1;
+    } else {
+      if (gb + 16 <= r_cap) {
+        const int4* sp = reinterpret_cast<const int4*>(src_row + gb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int4 v = sp[q];
+          sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = src_row[min(gb + i, r_cap - 1)];
+          sl[i] = gb + i < r_cap ? v : -1;
+        }
+      }
+      const int v = src_row[min(g, r_cap - 1)];
+      src = g < r_cap ? v : -1;
+    }
+    src = (src >= 0 && src < T) ? src : -1;
     const uint32_t srow = (uint32_t)max(src, 0);
     const float tr = *reinterpret_cast<const float*>(rs.t + (size_t)srow * rs.tstride);
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(rs.scales + (size_t)srow * rs.sstride + (col0 >> 4));
-    const uint32_t s0 = sp[0], s1 = sp[ncols > 64 ? 1 : 0];
-    int4 sv[4];
+    const uint8_t* sp = rs.scales + (size_t)srow * rs.sstride + (col0 >> 4);
+    uint4 sv;
+    if (ncols == kT2Cols) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(sp);
+      sv = make_uint4(q[0], q[1], q[2], q[3]);
+    } else {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(sp);
+      const int nw = ncols >> 6;  // 1..3 dwords of scale bytes
+      sv = make_uint4(q[0], nw > 1 ? q[1] : 0u, nw > 2 ? q[2] : 0u, 0u);
+    }
+    const uint8_t* base = rs.codes + (col0 >> 1) + 8 * cgc;
+    uint2 v[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
-    const int* sr = reinterpret_cast<const int*>(sv);
-    const uint8_t* base = rs.codes + (col0 >> 1) + 4 * (cg & ((ncols >> 3) - 1));
-    uint32_t v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(sr[i], 0) * rs.cstride);
+    for (int i = 0; i < 16; ++i) {
+      const int si = (sl[i] >= 0 && sl[i] < T) ? sl[i] : -1;
+      sl[i] = si;
+      v[i] = *reinterpret_cast<const uint2*>(base + (size_t)(uint32_t)max(si, 0) * rs.cstride);
+    }
     if (src >= 0) {
       t = tr;
-      sw0 = s0;
-      sw1 = ncols > 64 ? s1 : 0u;
+      sw = sv;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cw[i] = sr[i] >= 0 ? v[i] : 0u;
+    for (int i = 0; i < 16; ++i) cw2[i] = sl[i] >= 0 ? v[i] : make_uint2(0u, 0u);
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cw[i] = 0u;
+    for (int i = 0; i < 16; ++i) cw2[i] = make_uint2(0u, 0u);
   }
-  {
-    const int g = g_base + tid;
-    s_t[tid] = t;
-    s_tq[tid] = t * rht_in_scale(tid & 15);
-    s_sw[tid][0] = sw0;
-    s_sw[tid][1] = sw1;
-    // a block with a row of t < 2^-88 takes the two-step decode and the
-    // general block quantizer
-    uint64_t bal = __ballot(t < 0x1p-88f && t > 0.0f);
-    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
-    if (!GROUPED && g < tile_end) {
-      uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)g * (H >> 4) + (col0 >> 4));
-      rsc[0] = sw0;
-      if (ncols > 64) rsc[1] = sw1;
+  const int off_end = min(off_end_g, r_cap & ~15);                       // whole 16-row blocks only
+  const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
+  s_t[tid] = t;
+  s_sw[tid] = sw;
+  if (!GROUPED) {
+    // rowwise operand: 16-byte pieces, eight threads per row's 128 code bytes
+    // (whole lines when H is a multiple of 256), streamed past the caches --
+    // nothing in the path reads them again; the row's scale bytes and t
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gr = g_base + (tid >> 3) + 32 * i;
+      if (gr >= tile_end || cq >= nq) continue;
+      const u32x4v xv = (T > 0 && csrc[i] >= 0) ? cv[i] : u32x4v{0u, 0u, 0u, 0u};
+      __builtin_nontemporal_store(
+          xv, reinterpret_cast<u32x4v*>(row_codes + (size_t)(uint32_t)gr * (uint32_t)(H >> 1) + (col0 >> 1) + 16 * cq));
+    }
+    if (g < tile_end) {
+      uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)(uint32_t)g * (uint32_t)(H >> 4) + (col0 >> 4));
+      rsc[0] = sw.x;
+      if (ncols > 64) rsc[1] = sw.y;
+      if (ncols > 128) rsc[2] = sw.z;
+      if (ncols > 192) rsc[3] = sw.w;
       if (ct == 0) row_t[g] = t;
     }
   }
-  if (!GROUPED && live) {
-    uint8_t* rc = row_codes + (size_t)gb * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(rc + (size_t)i * (uint32_t)(H >> 1)) = cw[i];
-  }
   __syncthreads();
+  if (!col_live || gb >= tile_end) return;
 
-  // column phase: decode, 16-point RHT down each column, quantize with D_e.
-  if (live) {
-    float cm[16];
-    const int sh = 8 * ((cg >> 1) & 3);
-    const int dexp = s_dexp[m];
-    uint64_t n_col = 0, n_step = 0;
-    uint32_t klo = 0, khi = 0;
-    if (SR) {
-      const uint64_t seed = sr_state[0];
-      klo = (uint32_t)seed;
-      khi = (uint32_t)(seed >> 32);
-      n_col = sr_state[1] + 2 * (s_cbase[m] + (uint64_t)(uint32_t)col0 * s_cstr[m]);
-      n_step = 2 * (uint64_t)s_cstr[m];
+  // the block's expert, decode exponent and output bases
+  int e = 0;
+  {
+    int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
     }
-    if (s_slow[m] == 0 && dexp >= -95) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
-        cm[i] = s * s_tq[r0 + i];  // exact: s has 4 significant bits, t/4 is a power of two
-      }
-      column_pair<0, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<1, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<2, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<3, false, SR>(cw, cm, nullptr, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-    } else {
-      int ce[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float t = s_t[r0 + i];
-        ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
-        cm[i] = t == 0.0f ? 0.0f : e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * rht_in_scale(i);
-      }
-      column_pair<0, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<1, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<2, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-      column_pair<3, true, SR>(cw, cm, ce, dexp, s_tab, stage_codes, stage_sc, cg * 8, m, n_col, n_step,
-                                   klo, khi);
-    }
+    e = lo;
   }
-  __syncthreads();
-  // transposed copy-out: thread (b, j) writes block b of columns j, j+16, ...;
-  // 16 consecutive threads cover one column's 128 contiguous code bytes.
-  const int b = tid % kBlocks;
-  if (!s_live[b]) return;
-  const uint64_t cbase = s_cbase[b], sbase = s_sbase[b];
-  const uint32_t cstr = s_cstr[b], sstr = s_sstr[b];
+  const int off = s_offs[e], len = s_offs[e + 1] - off;
+  const int dexp = s_edexp[e];
+  uint64_t cbase, sbase;
+  uint32_t cstr, sstr;
+  if (KBLOCK) {
+    cbase = (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * (uint32_t)m;
+    cstr = (uint32_t)(tile_rows >> 1);
+    sbase = (uint64_t)H * (uint32_t)(off >> 4) + (uint64_t)H * 16u * (uint32_t)kb + (uint32_t)m;
+    sstr = (uint32_t)(tile_rows >> 4);
+  } else {
+    cbase = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+    cstr = (uint32_t)(len >> 1);
+    sbase = (uint64_t)H * (uint32_t)(off >> 4) + (uint32_t)((gb - off) >> 4);
+    sstr = (uint32_t)(len >> 4);
+  }
+  uint64_t n_col = 0, n_step = 0;
+  uint32_t klo = 0, khi = 0;
+  if (SR) {
+    const uint64_t seed = sr_state[0];
+    klo = (uint32_t)seed;
+    khi = (uint32_t)(seed >> 32);
+    n_col = sr_state[1] + 2 * cbase;   // the nibble index of (column 0, row gb), plus the counter base
+    n_step = 2 * (uint64_t)cstr;
+  }
+  // decode factors of the 16 rows: c_i = s_i * t_i * d_i / 4 (exact products)
+  const int h0 = col0 + 16 * cg;            // the thread's first column
+  const int sh = 8 * (cg & 3);
+  float cm[16], tv[16];
+  uint32_t sb[16];
+  bool slow = dexp < -95;
+  const uint32_t* swd = reinterpret_cast<const uint32_t*>(s_sw) + 4 * (16 * m) + (cg >> 2);
 #pragma unroll
-  for (int r = 0; r < (kTileCols * kBlocks) / kThreads; ++r) {
-    const int c = r * (kThreads / kBlocks) + tid / kBlocks;
-    if (c >= ncols) break;
-    const uint32_t h = (uint32_t)(col0 + c);
-    *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)h * cstr) = stage_codes[stage_at(c, b)];
-    col_scales[sbase + (uint64_t)h * sstr] = (uint8_t)stage_sc[stage_at(c, b)];
+  for (int i = 0; i < 16; ++i) {
+    tv[i] = s_t[16 * m + i];
+    sb[i] = swd[4 * i] >> sh;
+    slow |= tv[i] < 0x1p-88f && tv[i] > 0.0f;
+  }
+  uint32_t wx[16], wy[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    wx[i] = cw2[i].x;
+    wy[i] = cw2[i].y;
+  }
+  uint8_t* cc = col_codes + cbase;
+  uint8_t* cs = col_scales + sbase;
+  // the K-blocked layout: a K-block's code bytes fill one contiguous region, streamed
+  auto store = [&](int c, uint2 a, uint2 b, uint32_t sa, uint32_t sb2) {
+    const uint32_t h = (uint32_t)(h0 + c);
+    u32x2v* pa = reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr);
+    u32x2v* pb = reinterpret_cast<u32x2v*>(cc + (uint64_t)(h + 1) * cstr);
+    if (KBLOCK) {
+      __builtin_nontemporal_store(u32x2v{a.x, a.y}, pa);
+      __builtin_nontemporal_store(u32x2v{b.x, b.y}, pb);
+    } else {
+      *pa = u32x2v{a.x, a.y};
+      *pb = u32x2v{b.x, b.y};
+    }
+    cs[(uint64_t)h * sstr] = (uint8_t)sa;
+    cs[(uint64_t)(h + 1) * sstr] = (uint8_t)sb2;
+  };
+  if (!slow) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm[i] = e4m3_decode(sb[i]) * (tv[i] * rht_in_scale(i));  // exact
+    static_for<0, 8>([&](auto P) {
+      constexpr int p = P;
+      uint2 a, b;
+      uint32_t sa, sbb;
+      const uint64_t n0 = n_col + (uint64_t)(h0 + 2 * p) * n_step;
+      column_pair_out<p & 3, false, SR>((p < 4) ? wx : wy, cm, nullptr, dexp, s_tab, n0, n_step, klo, khi, a, b,
+                                        sa, sbb);
+      store(2 * p, a, b, sa, sbb);
+    });
+  } else {
+    int ce[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ce[i] = tv[i] > 0.0f ? pow2_exponent(tv[i]) : 0;
+      cm[i] = tv[i] == 0.0f ? 0.0f : e4m3_decode(sb[i]) * rht_in_scale(i);
+    }
+    static_for<0, 8>([&](auto P) {
+      constexpr int p = P;
+      uint2 a, b;
+      uint32_t sa, sbb;
+      const uint64_t n0 = n_col + (uint64_t)(h0 + 2 * p) * n_step;
+      column_pair_out<p & 3, true, SR>((p < 4) ? wx : wy, cm, ce, dexp, s_tab, n0, n_step, klo, khi, a, b, sa,
+                                       sbb);
+      store(2 * p, a, b, sa, sbb);
+    });
   }
 }
 
@@ -893,11 +943,11 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_scaled(const uint8_t* packed, int64_t
   if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale) return EP_ERR_NULL;
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
-  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const int64_t n_rt = (r_cap + kT2Rows - 1) / kT2Rows, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL((k_nvfp4_receive<false, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream, src,
                      (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
                      row_t, col_codes, col_scales, col_scale, nullptr);
   return launch_status();
@@ -914,11 +964,11 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tok
     return EP_ERR_NULL;
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
-  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const int64_t n_rt = (r_cap + kT2Rows - 1) / kT2Rows, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL((k_nvfp4_receive<false, false, true>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false, true>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0,
                      (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, row_t, col_codes, col_scales, col_scale, sr_state);
   return launch_status();
@@ -960,11 +1010,11 @@ MTB_EXPORT int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const u
   hipLaunchKernelGGL(k_expert_scale_grouped, dim3((unsigned)num_experts), dim3(1024), 0, (hipStream_t)stream, row_t,
                      (int)r_cap, offsets, col_scale);
   if (r_cap == 0) return launch_status();
-  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const int64_t n_rt = (r_cap + kT2Rows - 1) / kT2Rows, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const RowSrc src{row_codes, row_scales, reinterpret_cast<const uint8_t*>(row_t), (uint32_t)(H / 2),
                    (uint32_t)(H / 16), 4u};
-  hipLaunchKernelGGL((k_nvfp4_receive<true, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, src,
+  hipLaunchKernelGGL((k_nvfp4_receive<true, false>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream, src,
                      (int)r_cap, H, offsets, (int)num_experts, nullptr, (int)r_cap, (int)n_ct, nullptr, nullptr, nullptr,
                      col_codes, col_scales, col_scale, nullptr);
   return launch_status();
@@ -981,11 +1031,11 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
   // K-blocks over all experts: at most r_cap/256 + E of them
-  const int64_t n_kb = (r_cap + kTileRows - 1) / kTileRows + num_experts, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_kb * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const int64_t n_kb = (r_cap + kT2Rows - 1) / kT2Rows + num_experts, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_kb * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL((k_nvfp4_receive<false, true>), dim3((unsigned)(n_kb * n_ct)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((k_nvfp4_receive<false, true>), dim3((unsigned)(n_kb * n_ct)), dim3(kT2Threads), 0,
                      (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, row_t, col_codes, col_scales, col_scale, nullptr);
   return launch_status();
