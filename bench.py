@@ -5,8 +5,9 @@ Headline step: one pass of the path over the DeepSeek-V3-shaped one-GPU share
 of 32 experts from N(0,1) logits, 16-row aligned slots):
 
   route plan -> NVFP4 pack -> per-expert decode scale D_e -> direct receive
-  (rowwise operand + 16-point-RHT columnwise operand) -> unpack of the
-  received rows to BF16.
+  (rowwise operand + 16-point-RHT columnwise operand, K-blocked: each
+  expert's 256-row K-blocks one contiguous region) -> unpack of the received
+  rows to BF16.
 
 value = algorithmic bytes (distinct inputs read once + outputs, padding rows
 excluded) of the step / step time, in GB/s.  Inputs are resident in HBM
@@ -156,6 +157,7 @@ class Path:
         f32 = dict(dtype=torch.float32, device=dev)
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         self.calls = []
+        self.outputs = {}        # every buffer a call writes (graph-replay test)
         if n == 5:
             T, F, E = w.preact_bits.shape[0], w.dy_bits.shape[1], len(w.counts)
             pre, dy = bf(w.preact_bits), bf(w.dy_bits)
@@ -167,16 +169,18 @@ class Path:
                                  col_codes=torch.empty(2 * F * cap // 2, **u8),
                                  col_scales=torch.empty(2 * F * cap // 16, **u8), col_scale=torch.empty(E, **f32))
             out, out_nodx = mk(True), mk(False)
+            self.outputs.update({f"dsw.{k}": v for k, v in out.items()})
+            self.outputs.update({f"dsw_nodx.{k}": v for k, v in out_nodx.items() if v is not None})
             ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
             sr = torch.tensor([1234, 0], dtype=torch.int64, device=dev)
             self._add("dswiglu_nvfp4_quant", lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws),
-                      dswiglu_bytes(T, F, E))
+                      dswiglu_bytes(T, F, E), elements=T * 2 * F)
             self._add("dswiglu_nvfp4_quant_nodx",
                       lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out_nodx, workspace=ws),
-                      dswiglu_bytes(T, F, E, dx=False), in_step=False)
+                      dswiglu_bytes(T, F, E, dx=False), in_step=False, elements=T * 2 * F)
             self._add("dswiglu_nvfp4_quant_sr",
                       lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws, sr_state=sr),
-                      dswiglu_bytes(T, F, E, sr=True), in_step=False)
+                      dswiglu_bytes(T, F, E, sr=True), in_step=False, elements=T * 2 * F)
             self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)
             return
         T, H = w.x_bits.shape
@@ -193,6 +197,10 @@ class Path:
                     row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
                     col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))
         b = dispatch_bytes(T, H, k, E, r_cap, R)
+        self.outputs.update({f"plan.{nm}": plan[nm] for nm in ("counts", "offsets", "dst_row", "src_row", "d_error")})
+        self.outputs["packed"] = packed
+        self.outputs.update({f"recv.{nm}": v for nm, v in recv.items()})
+        G = int(plan["offsets"][-1].item())     # grouped rows, padding included: the columnwise transform's rows
         self._add("route_plan", lambda: m.ep_route_plan(topk, E, A, d_error=derr, workspace=ws, out=plan),
                   b["route_plan"])
         if n == 4:
@@ -205,14 +213,20 @@ class Path:
             self._add("nvfp4_pack_sr", lambda: m.ep_nvfp4_pack(x, SR_ELEMENT_CARRY, st, out=packed),
                       b["nvfp4_pack_sr"], in_step=False, elements=T * H, record=False)
         else:
-            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(x, out=packed), b["nvfp4_pack"])
+            self._add("nvfp4_pack", lambda: m.ep_nvfp4_pack(x, out=packed), b["nvfp4_pack"], elements=T * H)
         self._add("nvfp4_expert_scale",
                   lambda: m.ep_nvfp4_expert_scale(packed, H, plan, col_scale=recv["col_scale"]), b["nvfp4_expert_scale"])
+        # the step's receive writes the K-blocked columnwise layout (each 256-row
+        # K-block of an expert one contiguous [H, 128 B] region, the tiles a
+        # K-tiled grouped GEMM reads); the compact per-expert layout is a variant
+        self._add("nvfp4_direct_receive_kblock", lambda: m.ep_nvfp4_direct_receive_kblock(packed, H, plan, recv),
+                  b["nvfp4_direct_receive_kblock"], elements=G * H)
         self._add("nvfp4_direct_receive", lambda: m.ep_nvfp4_direct_receive_scaled(packed, H, plan, recv),
-                  b["nvfp4_direct_receive"])
+                  b["nvfp4_direct_receive"], in_step=False, elements=G * H)
         if n == 2:
             mx = torch.empty(T * H + T * H // 32, **u8)
             mx_out = (torch.empty((r_cap, H), **u8), torch.empty((r_cap, H // 32), **u8))
+            self.outputs.update({"mx": mx, "mx_out.data": mx_out[0], "mx_out.scales": mx_out[1]})
             self._add("mxfp8_pack", lambda: m.ep_mxfp8_pack(x, out=mx), b["mxfp8_pack"])
             self._add("mxfp8_receive", lambda: m.ep_mxfp8_direct_receive(
                 mx[: T * H].view(T, H), mx[T * H:].view(T, H // 32), plan, out=mx_out), b["mxfp8_receive"])
@@ -221,15 +235,14 @@ class Path:
             src = plan["src_row"].cpu().numpy()
             src_valid = torch.from_numpy(np.ascontiguousarray(src[: off[-1]][src[: off[-1]] >= 0])).to(dev)
             unpacked = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+            self.outputs["unpacked"] = unpacked
             self._add("nvfp4_unpack", lambda: m.ep_nvfp4_unpack(packed, H, src_row=src_valid, out=unpacked),
-                      b["nvfp4_unpack"])
+                      b["nvfp4_unpack"], elements=R * H)
         if n == 4:
             srr = torch.tensor([1234, 1 << 40], dtype=torch.int64, device=dev)
             self._add("nvfp4_direct_receive_sr", lambda: m.ep_nvfp4_direct_receive_sr(packed, H, plan, recv, srr),
-                      b["nvfp4_direct_receive_sr"], in_step=False)
+                      b["nvfp4_direct_receive_sr"], in_step=False, elements=G * H)
         if n in (2, 3):
-            self._add("nvfp4_direct_receive_kblock", lambda: m.ep_nvfp4_direct_receive_kblock(packed, H, plan, recv),
-                      b["nvfp4_direct_receive_kblock"], in_step=False)
             A32 = max(A, 32)
             plan32 = m.ep_route_plan(topk, E, A32)
             r32 = plan32["r_cap"]
@@ -240,6 +253,8 @@ class Path:
             fused = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
                          row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
                          col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))
+            self.outputs.update({f"mx4.{nm}": v for nm, v in mx4.items()})
+            self.outputs.update({f"fused.{nm}": v for nm, v in fused.items()})
             self._add("nvfp4_pack_scatter", lambda: m.ep_nvfp4_pack_scatter(x, plan, out=fused),
                       b["nvfp4_pack_scatter"], in_step=False)
             self._add("nvfp4_columnwise_grouped", lambda: m.ep_nvfp4_columnwise_grouped(fused, H, plan, out=fused),
@@ -301,9 +316,10 @@ def time_step(path, steps, warmup):
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(steps)]
-    # a marker kernel (a torch random fill, used nowhere else) before the timed
-    # region: in a kernel trace, the dispatches after it are the timed steps'
-    torch.empty(64, dtype=torch.float32, device=calls[0].dev).random_()
+    # marker kernels (a torch random fill, used nowhere else) before and after the
+    # timed region: in a kernel trace, the dispatches between them are the timed steps'
+    marker = torch.empty(64, dtype=torch.float32, device=calls[0].dev)
+    marker.random_()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -313,6 +329,8 @@ def time_step(path, steps, warmup):
             ev[s][j][1].record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    marker.random_()
+    torch.cuda.synchronize()
     per = {}
     for j, c in enumerate(calls):
         per.setdefault(c.name, []).extend(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps))
@@ -343,40 +361,67 @@ def counters_of(cfg, call):
     return rec
 
 
+def kernel_time_of(cfg, call):
+    """The committed kernel-only time of one call at one configuration (the sum of
+    its dispatches' traced durations per launch), or None when the call's kernels
+    changed since the trace was taken."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("calls", {}).get(f"cfg{cfg}/{call}")
+    if rec is None or rec.get("source_hash") != kernel_source_hash(call):
+        return None
+    return rec
+
+
 def entry(cfg, call, nbytes, ms, elements=None):
+    """One call's figures: HIP-event time per launch and the algorithmic rate
+    against the HBM peak; from the committed profiles (while the call's kernels
+    are unchanged): the traced kernel-only time and rate, the HBM and DRAM bytes
+    the counters saw, and the issued VALU instructions against the VALU issue
+    peak at the kernel-only time."""
     gbs = nbytes / (ms / 1e3) / 1e9
     e = dict(ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    kt = kernel_time_of(cfg, call)
+    if kt:
+        kgbs = nbytes / (kt["us_per_launch"] / 1e6) / 1e9
+        e.update(kernel_us=kt["us_per_launch"], kernel_gbs=round(kgbs, 1), kernel_frac=round(kgbs / HBM_PEAK_GBS, 4))
     cnt = counters_of(cfg, call)
     e["traffic"] = cnt.get("hbm_bytes") if cnt else None
     if cnt and cnt.get("dram_bytes") is not None:
         e["dram_bytes"] = cnt["dram_bytes"]
+        e["dram_ratio"] = round(cnt["dram_bytes"] / nbytes, 3)
+    valu = cnt.get("valu_insts") if cnt else None
+    if valu:
+        t = kt["us_per_launch"] / 1e6 if kt else ms / 1e3
+        gips = valu / t / 1e9
+        e.update(valu_insts=valu, valu_gips=round(gips, 1), valu_frac=round(gips / VALU_PEAK_GIPS, 4))
+        if elements:
+            e["valu_per_element"] = round(valu * 64 / elements, 2)
     if call in VALU_BOUND:
-        valu = cnt.get("valu_insts") if cnt else None
         e["bound"] = "alu"
-        if valu is not None:
-            gips = valu / (ms / 1e3) / 1e9
-            e.update(valu_insts=valu, valu_per_element=round(valu * 64 / elements, 2), valu_gips=round(gips, 1),
-                     valu_frac=round(gips / VALU_PEAK_GIPS, 4))
     return e
 
 
 # ---------------------------------------------------------------------------- CPU baseline
 def _oracle_cfg3(x_bits, topk, E, A, H):
     """The oracle's path of one sample of config-3 tokens: route plan, pack, direct
-    receive (rowwise + columnwise), unpack of the received rows; returns
+    receive (rowwise + columnwise, re-laid in K-blocks), unpack of the received
+    rows; returns
     (seconds, algorithmic bytes)."""
     from oracle import nvfp4, receive
     from oracle.routing import route_plan
     t0 = time.perf_counter()
     plan = route_plan(topk, E, A)
     packed = nvfp4.pack_rows(x_bits)
-    receive.direct_receive(packed, H, topk, E, A)
+    r = receive.direct_receive(packed, H, topk, E, A)
+    receive.kblock_layout(r["col_codes"], r["col_scales"], r["offsets"], H)
     off, src = plan["offsets"], plan["src_row"]
     nvfp4.unpack_rows(packed, H, src[: off[-1]][src[: off[-1]] >= 0])
     dt = time.perf_counter() - t0
     T, k = topk.shape
     b = dispatch_bytes(T, H, k, E, src.shape[0], T * k)
-    return dt, sum(b[c] for c in ("route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive",
+    return dt, sum(b[c] for c in ("route_plan", "nvfp4_pack", "nvfp4_expert_scale", "nvfp4_direct_receive_kblock",
                                   "nvfp4_unpack"))
 
 
@@ -432,12 +477,18 @@ def headline(path3, ms_step, per, steps, warmup, kernels, cpu):
                 dominant_by="largest per-launch time in the timed step")
     if cnt and cnt.get("dram_bytes") is not None:
         roof["dram_bytes"] = cnt["dram_bytes"]
+    if cnt and cnt.get("valu_insts"):
+        # the same launch against the VALU issue peak: the receive's decode, 16-point
+        # RHT and quotients are instruction-bound before they are HBM-bound
+        gips = cnt["valu_insts"] / (per[dom] / 1e3) / 1e9
+        roof["valu_issue"] = dict(insts_per_launch=cnt["valu_insts"], achieved=round(gips, 1), peak=VALU_PEAK_GIPS,
+                                  unit="G wave-instructions/s", frac=round(gips / VALU_PEAK_GIPS, 4))
     return {
         "metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16->nvfp4", "data": "synthetic",
         "config": dict(path3.desc, workload=path3.desc["workload"] + ": route plan + NVFP4 pack + D_e + direct "
-                       "receive (rowwise + RHT columnwise) + unpack of the received rows",
+                       "receive (rowwise + RHT columnwise in K-blocks) + unpack of the received rows",
                        bytes_per_step=total, step_calls=[c.name for c in calls],
                        step_ms={nm: round(v, 5) for nm, v in per.items()}),
         "roofline": roof,

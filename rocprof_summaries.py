@@ -14,9 +14,14 @@ process itself never touches the GPU (every GPU run is a rocprofv3 child).
       counters as read, HBM bytes = FETCH and WRITE scaled by the copy, DRAM
       request bytes scaled the same way, issued VALU instructions, and the hash
       of the call's kernel sources) and profiles/counters_cfgN.md.
-  python rocprof_summaries.py trace --workload cfgN [--raw DIR] [--steps K]
-      Kernel-trace statistics of `bench.py --workload cfgN`
-      -> profiles/kernel_trace_<workload>.md
+  python rocprof_summaries.py kernels [--configs 1,2,3,4,5] [--raw DIR]
+      Per configuration, rocprofv3 --kernel-trace of `bench.py --counters-pass
+      --workload cfgN`: each call's kernel-only time per launch (its dispatches'
+      durations summed) -> profiles/kernel_times.json, profiles/kernel_times_cfgN.md.
+  python rocprof_summaries.py trace --workload cfgN|all [--raw DIR] [--steps K]
+      Kernel-trace statistics of `bench.py --workload cfgN` (all: of the default
+      `bench.py`, the command that prints the headline line), with the timed
+      step's dispatches -> profiles/kernel_trace_<workload>.md
 """
 
 import argparse
@@ -52,6 +57,17 @@ def _is_marker(name):
     return "distribution" in name or "random" in name.lower()
 
 
+def _is_evict(name):
+    """The MALL-evicting read before each launch of a counters pass (a torch
+    reduction, and the fill that initialises its one-element result), which
+    belongs to no call: the library itself issues no fills."""
+    return "reduce_kernel" in name or "fillBuffer" in name
+
+
+def kernel_name(name):
+    return name.split("(")[0].replace("void ", "")
+
+
 def pmc_run(counters, workload, steps, raw, copy=False):
     """One rocprofv3 --pmc run of a counters pass; returns (per segment: {counter: value
     summed over the segment's dispatches and dimensions}, per segment kernel names,
@@ -72,13 +88,16 @@ def pmc_run(counters, workload, steps, raw, copy=False):
     marks = [i for i in ids if _is_marker(disp[i]["name"])]
     segs = []
     for a, b in zip(marks, marks[1:]):
-        tot, names = {}, set()
+        tot, names, per_k = {}, set(), {}
         for i in ids:
-            if a < i < b and "reduce_kernel" not in disp[i]["name"] and "fillBuffer" not in disp[i]["name"]:
-                names.add(disp[i]["name"].split("(")[0].replace("void ", ""))
+            if a < i < b and not _is_evict(disp[i]["name"]):
+                nm = kernel_name(disp[i]["name"])
+                names.add(nm)
+                pk = per_k.setdefault(nm, {})
                 for c, v in disp[i]["ctr"].items():
                     tot[c] = tot.get(c, 0.0) + v
-        segs.append((tot, sorted(names)))
+                    pk[c] = pk.get(c, 0.0) + v
+        segs.append((tot, sorted(names), per_k))
     shown = " ".join(["rocprofv3", "--pmc"] + list(counters) + ["--output-format", "csv", "-d", "OUT", "-o", "run",
                                                               "--", "python3", "bench.py"] + bench_args)
     return segs, line, shown
@@ -109,13 +128,18 @@ def counters(args):
         for g in GROUPS:
             segs, line, shown = pmc_run(g, wl, steps, raw)
             cmds.append(shown)
-            for (tot, names), seg in zip(segs, line["segments"]):
+            for (tot, names, per_k), seg in zip(segs, line["segments"]):
                 if seg["call"] is None:
                     continue
                 rec = per.setdefault(seg["call"], dict(kernels=names, launches=seg["launches"],
-                                                       algorithmic_bytes=seg["bytes"], source_hash=seg["source_hash"]))
+                                                       algorithmic_bytes=seg["bytes"], source_hash=seg["source_hash"],
+                                                       per_kernel={}))
                 for c in g:
                     rec[c] = tot.get(c, 0.0) / seg["launches"]
+                for k, kv in per_k.items():
+                    kr = rec["per_kernel"].setdefault(k, {})
+                    for c in g:
+                        kr[c] = kv.get(c, 0.0) / seg["launches"]
         lines = [f"# Counters per launch: bench.py --counters-pass --workload {wl}", "",
                  f"Date {datetime.date.today().isoformat()}.  Each call {steps} times, each launch after a read of a "
                  "1 GiB buffer that evicts the MALL; values summed over the counter's dimensions and the call's "
@@ -138,6 +162,14 @@ def counters(args):
             lines.append(f"| {call} | {', '.join('`' + k + '`' for k in rec['kernels'])} | "
                          f"{rec['algorithmic_bytes'] / 1e6:.1f} | {hbm / 1e6:.1f} | {hbm / rec['algorithmic_bytes']:.2f} | "
                          f"{dram / 1e6:.1f} | {dram / rec['algorithmic_bytes']:.2f} | {rec['valu_insts']:.3g} | {vpe} |")
+            for k, kr in rec["per_kernel"].items():
+                khbm = kr["FETCH_SIZE"] * 1024 * ref["FETCH_SIZE"] + kr["WRITE_SIZE"] * 1024 * ref["WRITE_SIZE"]
+                kdram = (kr["TCC_EA0_RDREQ_DRAM_sum"] * ref["TCC_EA0_RDREQ_DRAM_sum"]
+                         + kr["TCC_EA0_WRREQ_DRAM_sum"] * ref["TCC_EA0_WRREQ_DRAM_sum"])
+                kr.update(hbm_bytes=int(khbm), dram_bytes=int(kdram), valu_insts=int(kr["SQ_INSTS_VALU"]))
+                if len(rec["per_kernel"]) > 1:
+                    lines.append(f"| &nbsp;&nbsp;of which | `{k}` | | {khbm / 1e6:.1f} | | {kdram / 1e6:.1f} | | "
+                                 f"{kr['valu_insts']:.3g} | |")
             calls[f"{wl}/{call}"] = rec
         with open(os.path.join(args.out_dir, f"counters_{wl}_{WORKLOAD_NAMES[wl]}.md"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
@@ -151,10 +183,73 @@ def counters(args):
     print("wrote", path)
 
 
+def kernel_times(args):
+    """Kernel-only times per call: rocprofv3 --kernel-trace of the counters pass
+    (each call K times between marker kernels, each launch after the MALL-evicting
+    read), the call's dispatches between two markers summed per launch."""
+    raw = args.raw or tempfile.mkdtemp(prefix="mtb_ktimes_")
+    steps = 10
+    path = os.path.join(args.out_dir, "kernel_times.json")
+    doc = json.load(open(path)) if os.path.exists(path) else {}
+    calls = doc.get("calls", {})
+    for n in [int(c) for c in args.configs.split(",") if c]:
+        wl = f"cfg{n}"
+        out = os.path.join(raw, f"ktimes_{wl}")
+        bench_args = ["--counters-pass", "--steps", str(steps), "--workload", wl]
+        cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out, "-o", "run", "--",
+               sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
+        text = run(cmd, 600)
+        line = json.loads(next(ln for ln in text.splitlines() if ln.startswith("{\"")))
+        rows = sorted(csv.DictReader(open(os.path.join(out, "run_kernel_trace.csv"))),
+                      key=lambda r: int(r["Start_Timestamp"]))
+        marks = [i for i, r in enumerate(rows) if _is_marker(r["Kernel_Name"])]
+        shown = " ".join(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", "OUT", "-o",
+                          "run", "--", "python3", "bench.py"] + bench_args)
+        md = [f"# Kernel-only time per call: bench.py --counters-pass --workload {wl}", "",
+              f"Date {datetime.date.today().isoformat()}.  Command (from the repository root, via "
+              f"`python rocprof_summaries.py kernels --configs {n}`):", "", "```", shown, "```", "",
+              f"Each call {steps} times, each launch after a read of a 1 GiB buffer that evicts the MALL (the torch "
+              "reduction, not counted); a call's time per launch is the sum of its dispatches' durations "
+              "(start to end of each kernel, as the trace records them) divided by the launches.", "",
+              "| call | kernel | dispatches | avg us | min us | max us | call us per launch | algorithmic MB | "
+              "GB/s | frac of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for (a, b), seg in zip(zip(marks, marks[1:]), line["segments"]):
+            if seg["call"] is None:
+                continue
+            per = {}
+            for r in rows[a + 1:b]:
+                if _is_evict(r["Kernel_Name"]):
+                    continue
+                per.setdefault(kernel_name(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            us = sum(sum(v) for v in per.values()) / seg["launches"]
+            gbs = seg["bytes"] / (us / 1e6) / 1e9
+            calls[f"{wl}/{seg['call']}"] = dict(source_hash=seg["source_hash"], launches=seg["launches"],
+                                               us_per_launch=round(us, 3), algorithmic_bytes=seg["bytes"],
+                                               kernels={k: round(sum(v) / len(v), 3) for k, v in per.items()})
+            first = True
+            for k, v in per.items():
+                md.append(f"| {seg['call'] if first else ''} | `{k}` | {len(v)} | {sum(v) / len(v):.2f} | "
+                          f"{min(v):.2f} | {max(v):.2f} | " + (f"{us:.2f} | {seg['bytes'] / 1e6:.1f} | {gbs:.0f} | "
+                                                               f"{gbs / bench.HBM_PEAK_GBS:.3f} |" if first else "| | | |"))
+                first = False
+        with open(os.path.join(args.out_dir, f"kernel_times_{wl}_{WORKLOAD_NAMES[wl]}.md"), "w") as fh:
+            fh.write("\n".join(md) + "\n")
+    doc = dict(date=datetime.date.today().isoformat(),
+               method="rocprofv3 --kernel-trace of bench.py --counters-pass; per call, the sum of its dispatches' "
+                      "durations per launch", calls=calls)
+    with open(path, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print("wrote", path)
+
+
 def trace(args):
     raw = args.raw or tempfile.mkdtemp(prefix="mtb_trace_")
     out = os.path.join(raw, f"trace_{args.workload}")
-    bench_args = ["--workload", args.workload, "--steps", str(args.steps), "--warmup", "5", "--no-cpu-baseline"]
+    # "all": the bench's default command, exactly as the headline line is produced
+    bench_args = [] if args.workload == "all" else \
+        ["--workload", args.workload, "--steps", str(args.steps), "--warmup", "5", "--no-cpu-baseline"]
     cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out, "-o", "run", "--",
            sys.executable, os.path.join(ROOT, "bench.py")] + bench_args
     text = run(cmd, 600)
@@ -162,7 +257,9 @@ def trace(args):
     rows = list(csv.DictReader(open(os.path.join(out, "run_kernel_stats.csv"))))
     shown = " ".join(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", "OUT", "-o", "run",
                       "--", "python3", "bench.py"] + bench_args)
-    md = [f"# Kernel trace: bench.py --workload {args.workload}", "",
+    title = "bench.py (default: configurations 1-5 per call, the configuration-3 step timed)" \
+        if args.workload == "all" else f"bench.py --workload {args.workload}"
+    md = [f"# Kernel trace: {title}", "",
           f"Date {datetime.date.today().isoformat()}.  Command (from the repository root, via "
           f"`python rocprof_summaries.py trace --workload {args.workload}`):", "", "```", shown, "```", "",
           "All dispatches of the run: the per-call passes (each after a 1 GiB read that evicts the MALL: the "
@@ -172,17 +269,17 @@ def trace(args):
         name = r["Name"].split("(")[0].replace("void ", "")
         md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    # the timed region: every dispatch after the last marker kernel (bench.time_step launches one
-    # right before its timed steps)
+    # the timed region: the dispatches between the two marker kernels bench.time_step
+    # launches right before and right after its timed steps
     trace_rows = list(csv.DictReader(open(os.path.join(out, "run_kernel_trace.csv"))))
     trace_rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    last_mark = max(i for i, r in enumerate(trace_rows) if _is_marker(r["Kernel_Name"]))
+    marks = [i for i, r in enumerate(trace_rows) if _is_marker(r["Kernel_Name"])]
     per = {}
-    for r in trace_rows[last_mark + 1:]:
+    for r in trace_rows[marks[-2] + 1:marks[-1]]:
         nm = r["Kernel_Name"].split("(")[0].replace("void ", "")
         per.setdefault(nm, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    md += ["", f"Timed region ({args.steps} eager steps; every dispatch after the marker kernel bench.py launches "
-           "right before it):", "", "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    md += ["", f"Timed region ({args.steps if args.workload != 'all' else 20} eager steps; the dispatches between "
+           "the marker kernels bench.py launches right before and right after it):", "", "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
     for nm, v in per.items():
         md.append(f"| `{nm}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     if line:
@@ -196,7 +293,8 @@ def trace(args):
         step_ms = d.get("step_ms") or d.get("config", {}).get("step_ms", {})
         md += ["", f"Step (timed region): {d['ms_per_step'] * 1e3:.1f} us, {d['value']} GB/s; per call (HIP events) "
                + ", ".join(f"{nm} {v * 1e3:.1f} us" for nm, v in step_ms.items()) + "."]
-    path = os.path.join(args.out_dir, f"kernel_trace_{WORKLOAD_NAMES[args.workload]}.md")
+    name = "bench_default_" + WORKLOAD_NAMES["cfg3"] if args.workload == "all" else WORKLOAD_NAMES[args.workload]
+    path = os.path.join(args.out_dir, f"kernel_trace_{name}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("wrote", path)
@@ -204,8 +302,8 @@ def trace(args):
 
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["counters", "trace"])
-    p.add_argument("--workload", default="cfg3", choices=list(WORKLOAD_NAMES))
+    p.add_argument("what", choices=["counters", "kernels", "trace"])
+    p.add_argument("--workload", default="cfg3", choices=list(WORKLOAD_NAMES) + ["all"])
     p.add_argument("--configs", default="1,2,3,4,5")
     p.add_argument("--raw", default=None, help="directory for rocprofv3's raw output (default: a temp dir)")
     p.add_argument("--steps", type=int, default=20)
@@ -216,7 +314,7 @@ def main():
     if args.raw:
         args.raw = os.path.abspath(args.raw)
         os.makedirs(args.raw, exist_ok=True)
-    counters(args) if args.what == "counters" else trace(args)
+    {"counters": counters, "kernels": kernel_times, "trace": trace}[args.what](args)
 
 
 if __name__ == "__main__":
