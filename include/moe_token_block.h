@@ -202,7 +202,10 @@ int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, i
  *   scales an [hidden, P_e/16] matrix at byte hidden*off_e/16 of col_scales
  *   (P_e = off_{e+1} - off_e); col_codes/col_scales need hidden*r_cap/2 and
  *   hidden*r_cap/16 bytes.
- *   Requires hidden a positive multiple of 64 and 1 <= num_experts <= 1024. */
+ *   Requires hidden a positive multiple of 64 and 1 <= num_experts <= 1024;
+ *   tokens < 2^24 and tokens * (9*hidden/16+4) < 2^32 (the kernels address
+ *   packed rows with 32-bit offsets; EP_ERR_RANGE otherwise -- this and every
+ *   other receive entry point). */
 int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden,
                                 int64_t num_experts, int64_t r_cap,
                                 const int32_t* offsets, const int32_t* src_row,
@@ -271,8 +274,10 @@ int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tokens, int64_
  * and an [H, len/16] scale matrix at byte H*off_e/16 + 16*H*kb of
  * col_scales.  Same values as ep_nvfp4_direct_receive_scaled's compact
  * layout (the same bytes, re-placed); the rowwise operand is identical.
- * col_scale holds D_e (from ep_nvfp4_expert_scale).  Each 256 x 128 tile's
- * columnwise output is one contiguous 16 KB region. */
+ * col_scale holds D_e (from ep_nvfp4_expert_scale).  A full K-block's
+ * columnwise output for 256 columns is one contiguous 32 KB code region
+ * (128-byte aligned: hidden*off_e/2 is a multiple of 512) and one 4 KB scale
+ * region. */
 int32_t ep_nvfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, int64_t hidden,
                                        int64_t num_experts, int64_t r_cap,
                                        const int32_t* offsets, const int32_t* src_row,

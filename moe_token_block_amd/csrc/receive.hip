@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   __shared__ RcpEntry s_tab[128];
   __shared__ float s_t[kT2Rows];
   __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 scale bytes of each row
+  __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-88
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -411,14 +412,17 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int gr = g_base + (tid >> 3) + 32 * i;
-      const int sv = src_row[min(gr, r_cap - 1)];
+      const int sv = src_row[(uint32_t)min(gr, r_cap - 1)];
       csrc[i] = (gr < r_cap && sv >= 0 && sv < T) ? sv : -1;
     }
     if (T > 0) {
-      const uint8_t* cbase0 = rs.codes + (col0 >> 1) + 16 * (cq < nq ? cq : 0);
+      // a uniform base and 32-bit offsets (T * row bytes < 2^32, T < 2^24: checked
+      // at launch), so each load is one 24-bit multiply-add from its row index
+      const uint8_t* cbase0 = rs.codes + (col0 >> 1);
+      const uint32_t q16 = 16u * (uint32_t)(cq < nq ? cq : 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        cv[i] = *reinterpret_cast<const u32x4v*>(cbase0 + (size_t)(uint32_t)max(csrc[i], 0) * rs.cstride);
+        cv[i] = *reinterpret_cast<const u32x4v*>(cbase0 + (__umul24((uint32_t)max(csrc[i], 0), rs.cstride) + q16));
     }
   }
   uint2 cw2[16];
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       src = g < r_cap ? g : -1;
     } else {
       if (gb + 16 <= r_cap) {
-        const int4* sp = reinterpret_cast<const int4*>(src_row + gb);
+        const int4* sp = reinterpret_cast<const int4*>(src_row + (uint32_t)gb);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int4 v = sp[q];
@@ -443,17 +447,17 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int v = src_row[min(gb + i, r_cap - 1)];
+          const int v = src_row[(uint32_t)min(gb + i, r_cap - 1)];
           sl[i] = gb + i < r_cap ? v : -1;
         }
       }
-      const int v = src_row[min(g, r_cap - 1)];
+      const int v = src_row[(uint32_t)min(g, r_cap - 1)];
       src = g < r_cap ? v : -1;
     }
     src = (src >= 0 && src < T) ? src : -1;
     const uint32_t srow = (uint32_t)max(src, 0);
-    const float tr = *reinterpret_cast<const float*>(rs.t + (size_t)srow * rs.tstride);
-    const uint8_t* sp = rs.scales + (size_t)srow * rs.sstride + (col0 >> 4);
+    const float tr = *reinterpret_cast<const float*>(rs.t + __umul24(srow, rs.tstride));
+    const uint8_t* sp = rs.scales + (col0 >> 4) + __umul24(srow, rs.sstride);
     uint4 sv;
     if (ncols == kT2Cols) {
       const uint32_t* q = reinterpret_cast<const uint32_t*>(sp);
@@ -463,13 +467,14 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       const int nw = ncols >> 6;  // 1..3 dwords of scale bytes
       sv = make_uint4(q[0], nw > 1 ? q[1] : 0u, nw > 2 ? q[2] : 0u, 0u);
     }
-    const uint8_t* base = rs.codes + (col0 >> 1) + 8 * cgc;
+    const uint8_t* base = rs.codes + (col0 >> 1);
+    const uint32_t c8 = 8u * (uint32_t)cgc;
     uint2 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int si = (sl[i] >= 0 && sl[i] < T) ? sl[i] : -1;
       sl[i] = si;
-      v[i] = *reinterpret_cast<const uint2*>(base + (size_t)(uint32_t)max(si, 0) * rs.cstride);
+      v[i] = *reinterpret_cast<const uint2*>(base + (__umul24((uint32_t)max(si, 0), rs.cstride) + c8));
     }
     if (src >= 0) {
       t = tr;
@@ -485,6 +490,11 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
   s_t[tid] = t;
   s_sw[tid] = sw;
+  {
+    // rows tid.. of this wave are blocks 4w .. 4w+3: one ballot gives their flags
+    const uint64_t tiny = __ballot(t < 0x1p-88f && t > 0.0f);
+    if ((tid & 63) < 4) s_tiny[4 * (tid >> 6) + (tid & 3)] = ((tiny >> (16 * (tid & 3))) & 0xFFFFu) != 0;
+  }
   if (!GROUPED) {
     // rowwise operand: 16-byte pieces, eight threads per row's 128 code bytes
     // (whole lines when H is a multiple of 256), streamed past the caches --
@@ -548,13 +558,12 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   const int sh = 8 * (cg & 3);
   float cm[16], tv[16];
   uint32_t sb[16];
-  bool slow = dexp < -95;
+  const bool slow = dexp < -95 || s_tiny[m];
   const uint32_t* swd = reinterpret_cast<const uint32_t*>(s_sw) + 4 * (16 * m) + (cg >> 2);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     tv[i] = s_t[16 * m + i];
     sb[i] = swd[4 * i] >> sh;
-    slow |= tv[i] < 0x1p-88f && tv[i] > 0.0f;
   }
   uint32_t wx[16], wy[16];
 #pragma unroll
@@ -911,11 +920,18 @@ __global__ __launch_bounds__(256) void k_nvfp4_gather(const uint8_t* __restrict_
 
 using namespace mtb;
 
+// The receive kernels address source rows by a 24-bit row index times the row
+// stride within 32 bits: fewer than 2^24 rows of fewer than 2^32 bytes in all.
+static bool rows_addressable(int64_t rows, int64_t row_bytes) {
+  return rows < ((int64_t)1 << 24) && rows * row_bytes < ((int64_t)1 << 32);
+}
+
 static int32_t receive_check(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
                              int64_t r_cap, const int32_t* offsets, const int32_t* src_row) {
   if (tokens < 0 || r_cap < 0 || num_experts < 1 || num_experts > 1024 || hidden <= 0 || hidden % 64 != 0)
     return EP_ERR_SHAPE;
   if (tokens >= INT32_MAX / 4 || r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
+  if (!rows_addressable(tokens, 9 * hidden / 16 + 4)) return EP_ERR_RANGE;
   if (!offsets || !src_row) return EP_ERR_NULL;
   if (tokens > 0 && !packed) return EP_ERR_NULL;
   return EP_OK;
@@ -1003,7 +1019,7 @@ MTB_EXPORT int32_t ep_nvfp4_columnwise_grouped(const uint8_t* row_codes, const u
                                                const int32_t* offsets, uint8_t* col_codes, uint8_t* col_scales,
                                                float* col_scale, void* stream) {
   if (r_cap < 0 || num_experts < 1 || num_experts > 1024 || hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
-  if (r_cap >= INT32_MAX / 4 || hidden > (1 << 20)) return EP_ERR_RANGE;
+  if (r_cap >= INT32_MAX / 4 || hidden > (1 << 20) || !rows_addressable(r_cap, hidden / 2)) return EP_ERR_RANGE;
   if (!offsets || !col_scale) return EP_ERR_NULL;
   if (r_cap > 0 && (!row_codes || !row_scales || !row_t || !col_codes || !col_scales)) return EP_ERR_NULL;
   const int H = (int)hidden;
