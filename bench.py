@@ -441,30 +441,39 @@ def cpu_model():
 
 def cpu_baseline(w, n_tok, n_chunk=CPU_CHUNK_TOKENS):
     """The oracle as it stands on the host, before anything touches the GPU: one
-    process on tokens [0, n_tok) of config 3, then one process per core (at most
-    16, the machine's CPU share), each on its own n_chunk tokens (their own routing)."""
+    single-threaded process on tokens [0, n_tok) of config 3, then one
+    single-threaded process per core (at most 16, the machine's CPU share, whatever
+    the affinity mask shows), each on its own n_chunk tokens (their own routing).
+    The worker processes are spawned with OMP/OpenBLAS/MKL threads set to 1, so
+    each uses exactly one core."""
     import multiprocessing as mp
     E, A, H = w.num_experts, w.alignment, w.x_bits.shape[1]
-    dt1, b1 = _oracle_cfg3(w.x_bits[:n_tok], w.topk_idx[:n_tok], E, A, H)
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[v] = "1"                     # inherited by the spawned workers
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(1) as pool:
+        dt1, b1 = pool.apply(_oracle_worker, ((w.x_bits[:n_tok], w.topk_idx[:n_tok], E, A, H),))
     ncore = max(1, min(len(os.sched_getaffinity(0)), 16, w.x_bits.shape[0] // n_chunk))
     jobs = [(w.x_bits[i * n_chunk:(i + 1) * n_chunk], w.topk_idx[i * n_chunk:(i + 1) * n_chunk], E, A, H)
             for i in range(ncore)]
     t0 = time.perf_counter()
-    with mp.get_context("spawn").Pool(ncore) as pool:
+    with ctx.Pool(ncore) as pool:
         res = pool.map(_oracle_worker, jobs)
     dtn = time.perf_counter() - t0
     bn = sum(r[1] for r in res)
     return {"value": round(bn / dtn / 1e9, 4), "unit": "GB/s", "cores": ncore, "kind": "oracle",
-            "sample": f"config 3 ({w.name}): route plan, NVFP4 pack, direct receive (rowwise + RHT columnwise), "
+            "sample": f"config 3 ({w.name}): route plan, NVFP4 pack, direct receive (rowwise + RHT columnwise, "
+                      f"K-blocked), "
                       f"unpack; {ncore} processes, each on its own {n_chunk} tokens ({ncore * n_chunk} tokens, "
                       f"{dtn:.1f} s wall incl. process start)",
             "single_core": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
-                            "sample": f"tokens [0, {n_tok}) of config 3, {dt1:.1f} s"},
+                            "sample": f"tokens [0, {n_tok}) of config 3, {dt1:.1f} s, one thread"},
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model()}
 
 
 # ---------------------------------------------------------------------------- output
-def headline(path3, ms_step, per, steps, warmup, kernels, cpu):
+def headline(path3, ms_step, per, steps, warmup, kernels, cpu, copy=None):
     calls = path3.step_calls()
     total = sum(c.bytes for c in calls)
     dom = max(per, key=lambda nm: per[nm])
@@ -493,8 +502,33 @@ def headline(path3, ms_step, per, steps, warmup, kernels, cpu):
                        step_ms={nm: round(v, 5) for nm, v in per.items()}),
         "roofline": roof,
         "kernels": kernels,
+        "copy_reference": copy,
         "cpu_baseline": cpu,
     }
+
+
+def copy_reference(dev, reps=10):
+    """A 1 GiB device-to-device copy (torch's copy kernel) timed with HIP events:
+    the rate a plain streaming kernel reaches on this GPU, for context."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    nbytes = 2 * a.numel() * 4
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "kind": "torch device-to-device copy, 1 GiB"}
 
 
 def config_kernels(n, path, per):
@@ -611,7 +645,7 @@ def main():
         p3 = Path(3, dev, w3)
         head = (p3,) + time_step(p3, args.steps, args.warmup)
     path3, ms_step, step_per = head
-    emit(headline(path3, ms_step, step_per, args.steps, args.warmup, kernels, cpu), args)
+    emit(headline(path3, ms_step, step_per, args.steps, args.warmup, kernels, cpu, copy_reference(dev)), args)
 
 
 if __name__ == "__main__":

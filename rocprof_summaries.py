@@ -33,6 +33,8 @@ import subprocess
 import sys
 import tempfile
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (imports no GPU state)
@@ -210,28 +212,36 @@ def kernel_times(args):
               f"`python rocprof_summaries.py kernels --configs {n}`):", "", "```", shown, "```", "",
               f"Each call {steps} times, each launch after a read of a 1 GiB buffer that evicts the MALL (the torch "
               "reduction, not counted); a call's time per launch is the sum of its dispatches' durations "
-              "(start to end of each kernel, as the trace records them) divided by the launches.", "",
-              "| call | kernel | dispatches | avg us | min us | max us | call us per launch | algorithmic MB | "
-              "GB/s | frac of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+              "(start to end of each kernel, as the trace records them) summed per launch; the median launch and "
+              "the interquartile range are reported, and GB/s is the algorithmic bytes over the median.", "",
+              "| call | kernel | dispatches | median us | IQR us | call us per launch: median (IQR) | "
+              "algorithmic MB | GB/s | frac of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
         for (a, b), seg in zip(zip(marks, marks[1:]), line["segments"]):
             if seg["call"] is None:
                 continue
-            per = {}
+            per, launches = {}, []
             for r in rows[a + 1:b]:
                 if _is_evict(r["Kernel_Name"]):
+                    if "reduce_kernel" in r["Kernel_Name"]:
+                        launches.append(0.0)        # each launch follows one evicting read
                     continue
-                per.setdefault(kernel_name(r["Kernel_Name"]), []).append(
-                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-            us = sum(sum(v) for v in per.values()) / seg["launches"]
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                per.setdefault(kernel_name(r["Kernel_Name"]), []).append(d)
+                if launches:
+                    launches[-1] += d
+            lq = np.percentile(launches, [25, 50, 75]) if launches else [0.0, 0.0, 0.0]
+            us = float(lq[1])                       # the median launch
             gbs = seg["bytes"] / (us / 1e6) / 1e9
-            calls[f"{wl}/{seg['call']}"] = dict(source_hash=seg["source_hash"], launches=seg["launches"],
-                                               us_per_launch=round(us, 3), algorithmic_bytes=seg["bytes"],
-                                               kernels={k: round(sum(v) / len(v), 3) for k, v in per.items()})
+            calls[f"{wl}/{seg['call']}"] = dict(source_hash=seg["source_hash"], launches=len(launches),
+                                               us_per_launch=round(us, 3), us_p25=round(float(lq[0]), 3),
+                                               us_p75=round(float(lq[2]), 3), algorithmic_bytes=seg["bytes"],
+                                               kernels={k: round(float(np.median(v)), 3) for k, v in per.items()})
             first = True
             for k, v in per.items():
-                md.append(f"| {seg['call'] if first else ''} | `{k}` | {len(v)} | {sum(v) / len(v):.2f} | "
-                          f"{min(v):.2f} | {max(v):.2f} | " + (f"{us:.2f} | {seg['bytes'] / 1e6:.1f} | {gbs:.0f} | "
-                                                               f"{gbs / bench.HBM_PEAK_GBS:.3f} |" if first else "| | | |"))
+                md.append(f"| {seg['call'] if first else ''} | `{k}` | {len(v)} | {float(np.median(v)):.2f} | "
+                          f"{float(np.percentile(v, 25)):.2f}-{float(np.percentile(v, 75)):.2f} | "
+                          + (f"{us:.2f} ({lq[0]:.2f}-{lq[2]:.2f}) | {seg['bytes'] / 1e6:.1f} | {gbs:.0f} | "
+                             f"{gbs / bench.HBM_PEAK_GBS:.3f} |" if first else "| | | |"))
                 first = False
         with open(os.path.join(args.out_dir, f"kernel_times_{wl}_{WORKLOAD_NAMES[wl]}.md"), "w") as fh:
             fh.write("\n".join(md) + "\n")
