@@ -122,6 +122,16 @@ def dispatch_bytes(T, H, k, E, r_cap, R):
     return b
 
 
+def dswiglu_kernel_bytes(T, F, E, dx=True):
+    """The same bytes split over the call's two main kernels: the epilogue reads
+    preact and dy and writes dX (when materialized) and the per-row maxima; the
+    quantizer reads dX (or preact and dy again) and writes both operands."""
+    ops = 2 * T * (F + 2 * F // 16) + 3 * E * 4
+    epi = T * 2 * F * 2 + T * F * 2 + (T * 2 * F * 2 if dx else 0)
+    quant = (T * 2 * F * 2 if dx else T * 2 * F * 2 + T * F * 2) + ops
+    return {"k_dswiglu_epilogue": epi, "k_fc1_quant": quant}
+
+
 def dswiglu_bytes(T, F, E, dx=True, sr=False):
     """Inputs (preact [T,2F], dy [T,F], counts) read once + outputs (dX if written,
     the per-expert amax and scales, rowwise and columnwise codes and scales)."""
@@ -135,8 +145,9 @@ def dswiglu_bytes(T, F, E, dx=True, sr=False):
 
 # ---------------------------------------------------------------------------- paths
 class Call:
-    def __init__(self, name, fn, nbytes, in_step=True, elements=None):
+    def __init__(self, name, fn, nbytes, in_step=True, elements=None, kernel_bytes=None):
         self.name, self.fn, self.bytes, self.in_step, self.elements = name, fn, nbytes, in_step, elements
+        self.kernel_bytes = kernel_bytes     # {kernel name part: its algorithmic bytes} for multi-kernel calls
 
 
 class Path:
@@ -174,13 +185,15 @@ class Path:
             ws = torch.empty(m.lib().dswiglu_workspace_bytes(T, E), **u8)
             sr = torch.tensor([1234, 0], dtype=torch.int64, device=dev)
             self._add("dswiglu_nvfp4_quant", lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws),
-                      dswiglu_bytes(T, F, E), elements=T * 2 * F)
+                      dswiglu_bytes(T, F, E), elements=T * 2 * F, kernel_bytes=dswiglu_kernel_bytes(T, F, E))
             self._add("dswiglu_nvfp4_quant_nodx",
                       lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out_nodx, workspace=ws),
-                      dswiglu_bytes(T, F, E, dx=False), in_step=False, elements=T * 2 * F)
+                      dswiglu_bytes(T, F, E, dx=False), in_step=False, elements=T * 2 * F,
+                      kernel_bytes=dswiglu_kernel_bytes(T, F, E, dx=False))
             self._add("dswiglu_nvfp4_quant_sr",
                       lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws, sr_state=sr),
-                      dswiglu_bytes(T, F, E, sr=True), in_step=False, elements=T * 2 * F)
+                      dswiglu_bytes(T, F, E, sr=True), in_step=False, elements=T * 2 * F,
+                      kernel_bytes=dswiglu_kernel_bytes(T, F, E))
             self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)
             return
         T, H = w.x_bits.shape
@@ -261,8 +274,8 @@ class Path:
                       b["nvfp4_columnwise_grouped"], in_step=False)
         self.desc = dict(workload=w.name, tokens=T, hidden=H, experts=E, top_k=k, alignment=A)
 
-    def _add(self, name, fn, nbytes, in_step=True, elements=None, record=True):
-        c = Call(name, fn, nbytes, in_step, elements)
+    def _add(self, name, fn, nbytes, in_step=True, elements=None, record=True, kernel_bytes=None):
+        c = Call(name, fn, nbytes, in_step, elements, kernel_bytes)
         c.record = record
         c.dev = self.dev
         self.calls.append(c)
@@ -374,7 +387,7 @@ def kernel_time_of(cfg, call):
     return rec
 
 
-def entry(cfg, call, nbytes, ms, elements=None):
+def entry(cfg, call, nbytes, ms, elements=None, kernel_bytes=None):
     """One call's figures: HIP-event time per launch and the algorithmic rate
     against the HBM peak; from the committed profiles (while the call's kernels
     are unchanged): the traced kernel-only time and rate, the HBM and DRAM bytes
@@ -386,6 +399,14 @@ def entry(cfg, call, nbytes, ms, elements=None):
     if kt:
         kgbs = nbytes / (kt["us_per_launch"] / 1e6) / 1e9
         e.update(kernel_us=kt["us_per_launch"], kernel_gbs=round(kgbs, 1), kernel_frac=round(kgbs / HBM_PEAK_GBS, 4))
+        if kernel_bytes:
+            split = {}
+            for part, kb in kernel_bytes.items():
+                us = sum(v for k, v in kt["kernels"].items() if part in k)
+                if us > 0:
+                    split[part] = dict(us=round(us, 3), bytes=kb,
+                                       frac=round(kb / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4))
+            e["kernel_split"] = split
     cnt = counters_of(cfg, call)
     e["traffic"] = cnt.get("hbm_bytes") if cnt else None
     if cnt and cnt.get("dram_bytes") is not None:
@@ -535,7 +556,7 @@ def config_kernels(n, path, per):
     out = {}
     for c in path.calls:
         if c.name in per and c.name not in out:
-            out[c.name] = entry(n, c.name, c.bytes, per[c.name], c.elements)
+            out[c.name] = entry(n, c.name, c.bytes, per[c.name], c.elements, c.kernel_bytes)
             if not c.in_step:
                 out[c.name]["variant"] = True
     return dict(workload=path.desc["workload"], calls=out)
@@ -580,7 +601,8 @@ def main_counters_pass(args, dev):
             evict_mall(flush)
             c.fn()
         segments.append(dict(call=c.name if getattr(c, "record", True) else None, launches=reps, bytes=c.bytes,
-                             elements=c.elements, source_hash=kernel_source_hash(c.name)))
+                             elements=c.elements, kernel_bytes=c.kernel_bytes,
+                             source_hash=kernel_source_hash(c.name)))
     torch.cuda.synchronize()
     marker.random_()
     torch.cuda.synchronize()

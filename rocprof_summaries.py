@@ -237,12 +237,24 @@ def kernel_times(args):
                                                us_p75=round(float(lq[2]), 3), algorithmic_bytes=seg["bytes"],
                                                kernels={k: round(float(np.median(v)), 3) for k, v in per.items()})
             first = True
+            kb = seg.get("kernel_bytes") or {}
             for k, v in per.items():
+                part = next((p for p in kb if p in k), None)
+                if first:
+                    tail = (f"{us:.2f} ({lq[0]:.2f}-{lq[2]:.2f}) | {seg['bytes'] / 1e6:.1f} | {gbs:.0f} | "
+                            f"{gbs / bench.HBM_PEAK_GBS:.3f} |")
+                elif part is not None:
+                    kg = kb[part] / (float(np.median(v)) / 1e6) / 1e9
+                    tail = f"(this kernel) | {kb[part] / 1e6:.1f} | {kg:.0f} | {kg / bench.HBM_PEAK_GBS:.3f} |"
+                else:
+                    tail = "| | | |"
                 md.append(f"| {seg['call'] if first else ''} | `{k}` | {len(v)} | {float(np.median(v)):.2f} | "
-                          f"{float(np.percentile(v, 25)):.2f}-{float(np.percentile(v, 75)):.2f} | "
-                          + (f"{us:.2f} ({lq[0]:.2f}-{lq[2]:.2f}) | {seg['bytes'] / 1e6:.1f} | {gbs:.0f} | "
-                             f"{gbs / bench.HBM_PEAK_GBS:.3f} |" if first else "| | | |"))
+                          f"{float(np.percentile(v, 25)):.2f}-{float(np.percentile(v, 75)):.2f} | " + tail)
                 first = False
+                if part is not None and k == next(iter(per)):
+                    kg = kb[part] / (float(np.median(v)) / 1e6) / 1e9
+                    md.append(f"| | (`{k}` alone) | | | | (this kernel) | {kb[part] / 1e6:.1f} | {kg:.0f} | "
+                              f"{kg / bench.HBM_PEAK_GBS:.3f} |")
         with open(os.path.join(args.out_dir, f"kernel_times_{wl}_{WORKLOAD_NAMES[wl]}.md"), "w") as fh:
             fh.write("\n".join(md) + "\n")
     doc = dict(date=datetime.date.today().isoformat(),
