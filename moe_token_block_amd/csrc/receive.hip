@@ -294,6 +294,10 @@ struct RowSrc {
 constexpr int kT2Rows = 256, kT2Cols = 256, kT2Threads = 256;
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+// Buffer resources: word 3 of a raw (unstrided, untyped) buffer on gfx9-family
+// parts; a load at an offset beyond the resource's size returns zeros.
+constexpr int kBufDword3 = 0x00020000;
+constexpr uint32_t kNoRow = 0x80000000u;  // beyond every resource (sizes < 2^31)
 
 template <int SEL, bool SLOW, bool SR>
 __device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float* cm, const int* ce, int dexp,
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   __shared__ float s_t[kT2Rows];
   __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 scale bytes of each row
   __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-88
+  __shared__ __align__(16) int s_src[kT2Rows];  // source row of each grouped row (-1: none)
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -393,98 +398,83 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   const bool col_live = 16 * cg < ncols;
   const int cgc = col_live ? cg : 0;          // clamped: a dead group re-reads group 0
 
-  // expert offsets, decode exponents and the reciprocal table into LDS
+  // this thread's own source-row index (issued first), then the expert offsets
+  // (already there in the K-blocked layout), decode exponents and the reciprocal
+  // table into LDS
+  const int g = g_base + tid;
+  int srcv = g;
+  if (!GROUPED) srcv = src_row[(uint32_t)min(g, r_cap - 1)];
   for (int i = tid; i <= E; i += kT2Threads) {
-    s_offs[i] = offsets[i];
+    if (!KBLOCK) s_offs[i] = offsets[i];
     if (i < E) s_edexp[i] = pow2_exponent(col_scale[i]);
   }
   if (tid < 128) s_tab[tid] = rcp_entry(tid);
-  const int off_end_g = offsets[E];
 
-  // the loads: the row-copy pieces (16 bytes of rows (tid >> 3) + 32 i), this
-  // thread's row (t and the tile's scale bytes) and its block's 16 code gathers,
-  // all issued before the first wait at clamped indices; the copy's pieces are
-  // the same bytes as the gathers', so the L2 merges their misses
+  // The loads, in two rounds: each thread's own source-row index (into LDS, so
+  // that the row copy and the column blocks read theirs from there), then every
+  // byte load -- the row-copy pieces (16 bytes of rows (tid >> 3) + 32 i), the
+  // 16 code gathers of its column block, its row's t and the tile's scale bytes.
+  // The byte loads are buffer loads over the source rows: a row that is padding,
+  // an unused slot, past r_cap or out of range gets an offset beyond the
+  // resource, and the hardware's range check returns zeros for it -- no selects,
+  // and no access at all when T = 0.  The copy's pieces are the same bytes as the
+  // gathers', so the L2 merges their misses.
   const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces per row: 2, 4, 6 or 8
-  int csrc[8];
-  u32x4v cv[8];
-  if (!GROUPED) {
+  s_src[tid] = g < r_cap ? srcv : -1;
+  __syncthreads();
+  const int off_end_g = s_offs[E];
+  int rsrc[8], sl[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int gr = g_base + (tid >> 3) + 32 * i;
-      const int sv = src_row[(uint32_t)min(gr, r_cap - 1)];
-      csrc[i] = (gr < r_cap && sv >= 0 && sv < T) ? sv : -1;
-    }
-    if (T > 0) {
-      // a uniform base and 32-bit offsets (T * row bytes < 2^32, T < 2^24: checked
-      // at launch), so each load is one 24-bit multiply-add from its row index
-      const uint8_t* cbase0 = rs.codes + (col0 >> 1);
-      const uint32_t q16 = 16u * (uint32_t)(cq < nq ? cq : 0);
+  for (int i = 0; i < 8; ++i) rsrc[i] = s_src[(tid >> 3) + 32 * i];
+  {
+    const int4* sp = reinterpret_cast<const int4*>(s_src + 16 * m);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        cv[i] = *reinterpret_cast<const u32x4v*>(cbase0 + (__umul24((uint32_t)max(csrc[i], 0), rs.cstride) + q16));
+    for (int q = 0; q < 4; ++q) {
+      const int4 v = sp[q];
+      sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
     }
   }
+  const int src = s_src[tid];
+  // resources of the T source rows (sizes < 2^31: checked at launch)
+  const uint32_t nT = (uint32_t)max(T, 0);
+  const __amdgpu_buffer_rsrc_t r_codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.codes), (short)0, (int)(nT ? (nT - 1) * rs.cstride + (uint32_t)(H >> 1) : 0u), kBufDword3);
+  const __amdgpu_buffer_rsrc_t r_scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.scales), (short)0, (int)(nT ? (nT - 1) * rs.sstride + (uint32_t)(H >> 4) : 0u), kBufDword3);
+  const __amdgpu_buffer_rsrc_t r_t = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.t), (short)0, (int)(nT ? (nT - 1) * rs.tstride + 4u : 0u), kBufDword3);
+  // byte offset of source row s (plus add), or kNoRow
+  auto row_at = [&](int s, uint32_t stride, uint32_t add) -> uint32_t {
+    return (uint32_t)s < nT ? __umul24((uint32_t)s, stride) + add : kNoRow;
+  };
+  u32x4v cv[8];
+  if (!GROUPED) {
+    const uint32_t qa = (uint32_t)(col0 >> 1) + 16u * (uint32_t)(cq < nq ? cq : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = __builtin_amdgcn_raw_buffer_load_b128(r_codes, row_at(rsrc[i], rs.cstride, qa), 0, 0);
+  }
   uint2 cw2[16];
-  float t = 0.0f;
-  uint4 sw = make_uint4(0, 0, 0, 0);
-  const int g = g_base + tid;
-  int src = -1;
-  if (T > 0) {
-    int sl[16];
-    if (GROUPED) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sl[i] = gb + i < r_cap ? gb + i : -1;
-      src = g < r_cap ? g : -1;
-    } else {
-      if (gb + 16 <= r_cap) {
-        const int4* sp = reinterpret_cast<const int4*>(src_row + (uint32_t)gb);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 v = sp[q];
-          sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = src_row[(uint32_t)min(gb + i, r_cap - 1)];
-          sl[i] = gb + i < r_cap ? v : -1;
-        }
-      }
-      const int v = src_row[(uint32_t)min(g, r_cap - 1)];
-      src = g < r_cap ? v : -1;
-    }
-    src = (src >= 0 && src < T) ? src : -1;
-    const uint32_t srow = (uint32_t)max(src, 0);
-    const float tr = *reinterpret_cast<const float*>(rs.t + __umul24(srow, rs.tstride));
-    const uint8_t* sp = rs.scales + (col0 >> 4) + __umul24(srow, rs.sstride);
-    uint4 sv;
-    if (ncols == kT2Cols) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(sp);
-      sv = make_uint4(q[0], q[1], q[2], q[3]);
-    } else {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(sp);
-      const int nw = ncols >> 6;  // 1..3 dwords of scale bytes
-      sv = make_uint4(q[0], nw > 1 ? q[1] : 0u, nw > 2 ? q[2] : 0u, 0u);
-    }
-    const uint8_t* base = rs.codes + (col0 >> 1);
-    const uint32_t c8 = 8u * (uint32_t)cgc;
-    uint2 v[16];
+  {
+    const uint32_t ca = (uint32_t)(col0 >> 1) + 8u * (uint32_t)cgc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int si = (sl[i] >= 0 && sl[i] < T) ? sl[i] : -1;
-      sl[i] = si;
-      v[i] = *reinterpret_cast<const uint2*>(base + (__umul24((uint32_t)max(si, 0), rs.cstride) + c8));
+      const u32x2v w = __builtin_amdgcn_raw_buffer_load_b64(r_codes, row_at(sl[i], rs.cstride, ca), 0, 0);
+      cw2[i] = make_uint2(w.x, w.y);
     }
-    if (src >= 0) {
-      t = tr;
-      sw = sv;
+  }
+  const float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_t, row_at(src, rs.tstride, 0u), 0, 0));
+  uint4 sw;
+  {
+    const uint32_t so = row_at(src, rs.sstride, (uint32_t)(col0 >> 4));
+    if (ncols == kT2Cols) {
+      const u32x4v q = __builtin_amdgcn_raw_buffer_load_b128(r_scales, so, 0, 0);
+      sw = make_uint4(q.x, q.y, q.z, q.w);
+    } else {
+      const int nw = ncols >> 6;  // 1..3 dwords of scale bytes
+      sw = make_uint4(__builtin_amdgcn_raw_buffer_load_b32(r_scales, so, 0, 0),
+                      nw > 1 ? __builtin_amdgcn_raw_buffer_load_b32(r_scales, so + 4u, 0, 0) : 0u,
+                      nw > 2 ? __builtin_amdgcn_raw_buffer_load_b32(r_scales, so + 8u, 0, 0) : 0u, 0u);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cw2[i] = sl[i] >= 0 ? v[i] : make_uint2(0u, 0u);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cw2[i] = make_uint2(0u, 0u);
   }
   const int off_end = min(off_end_g, r_cap & ~15);                       // whole 16-row blocks only
   const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
@@ -503,9 +493,8 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
     for (int i = 0; i < 8; ++i) {
       const int gr = g_base + (tid >> 3) + 32 * i;
       if (gr >= tile_end || cq >= nq) continue;
-      const u32x4v xv = (T > 0 && csrc[i] >= 0) ? cv[i] : u32x4v{0u, 0u, 0u, 0u};
       __builtin_nontemporal_store(
-          xv, reinterpret_cast<u32x4v*>(row_codes + (size_t)(uint32_t)gr * (uint32_t)(H >> 1) + (col0 >> 1) + 16 * cq));
+          cv[i], reinterpret_cast<u32x4v*>(row_codes + (size_t)(uint32_t)gr * (uint32_t)(H >> 1) + (col0 >> 1) + 16 * cq));
     }
     if (g < tile_end) {
       uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)(uint32_t)g * (uint32_t)(H >> 4) + (col0 >> 4));
@@ -920,10 +909,11 @@ __global__ __launch_bounds__(256) void k_nvfp4_gather(const uint8_t* __restrict_
 
 using namespace mtb;
 
-// The receive kernels address source rows by a 24-bit row index times the row
-// stride within 32 bits: fewer than 2^24 rows of fewer than 2^32 bytes in all.
+// The receive kernels address source rows through buffer resources, by a 24-bit
+// row index times the row stride, with 2^31 as the "no row" offset: fewer than
+// 2^24 rows of fewer than 2^31 bytes in all.
 static bool rows_addressable(int64_t rows, int64_t row_bytes) {
-  return rows < ((int64_t)1 << 24) && rows * row_bytes < ((int64_t)1 << 32);
+  return rows < ((int64_t)1 << 24) && rows * row_bytes < ((int64_t)1 << 31);
 }
 
 static int32_t receive_check(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
