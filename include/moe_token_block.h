@@ -203,9 +203,9 @@ int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, i
  *   (P_e = off_{e+1} - off_e); col_codes/col_scales need hidden*r_cap/2 and
  *   hidden*r_cap/16 bytes.
  *   Requires hidden a positive multiple of 64 and 1 <= num_experts <= 1024;
- *   tokens < 2^24 and tokens * (9*hidden/16+4) < 2^32 (the kernels address
- *   packed rows with 32-bit offsets; EP_ERR_RANGE otherwise -- this and every
- *   other receive entry point). */
+ *   tokens < 2^24 and tokens * (9*hidden/16+4) < 2^31 (the kernels address
+ *   packed rows through buffer resources with 31-bit offsets; EP_ERR_RANGE
+ *   otherwise -- this and every other receive entry point). */
 int32_t ep_nvfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t hidden,
                                 int64_t num_experts, int64_t r_cap,
                                 const int32_t* offsets, const int32_t* src_row,

@@ -90,11 +90,11 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, N, P, P, P, P, N, N, N, N) == -1
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 1025, 64, P, P, P, P, P, N, N, N, N) == -2
     assert lib.ep_nvfp4_direct_receive(P, 4, 128, 2, 64, P, P, P, P, P, P, N, P, N) == -1
-    # packed rows are addressed with 32-bit offsets: fewer than 2^24 tokens, under 4 GiB of rows
+    # packed rows are addressed with 31-bit offsets: fewer than 2^24 tokens, under 2 GiB of rows
     assert lib.ep_nvfp4_direct_receive(P, 1 << 24, 64, 2, 64, P, P, P, P, P, P, P, P, N) == -8
-    assert lib.ep_nvfp4_direct_receive_kblock(P, 1064165, 7168, 2, 64, P, P, P, P, P, P, P, P, N) == -8
-    assert lib.ep_nvfp4_direct_receive_scaled(P, 1064164, 7168, 2, 64, N, P, P, P, P, P, P, P, N) == -1
-    assert lib.ep_nvfp4_columnwise_grouped(P, P, P, 7168, 2, 1198373, P, P, P, P, N) == -8
+    assert lib.ep_nvfp4_direct_receive_kblock(P, 532083, 7168, 2, 64, P, P, P, P, P, P, P, P, N) == -8
+    assert lib.ep_nvfp4_direct_receive_scaled(P, 532082, 7168, 2, 64, N, P, P, P, P, P, P, P, N) == -1
+    assert lib.ep_nvfp4_columnwise_grouped(P, P, P, 7168, 2, 599187, P, P, P, P, N) == -8
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 100, P, 2, P, P, P, P, P, P, P, P, P, 16, N) == -2
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 16, 64, P, P, P, P, P, P, N) == -3   # alignment not a multiple of 32
     assert lib.ep_nvfp4_direct_receive_sr(P, 4, 128, 2, 64, P, P, P, P, P, P, P, P, N, N) == -1   # sr_state NULL
