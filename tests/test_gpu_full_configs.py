@@ -171,6 +171,33 @@ def test_config3_dsv3_share(dev):
     gcs = host(got["col_scales"][H * int(off_all[e]) // 16: H * int(off_all[e + 1]) // 16]).reshape(H, p // 16)
     assert_bytes_equal(gcs, cs, f"config3 columnwise scales of expert {e} (whole)")
     assert_bytes_equal(gcc, cc, f"config3 columnwise codes of expert {e} (whole)")
+    # the K-blocked receive (the form bench.py's step runs) at this size: its rowwise
+    # operand and, re-placed block by block, its columnwise operand equal the compact
+    # call's in every byte; expert e's K-blocks equal the oracle's operand re-laid
+    print("config3: K-blocked receive", flush=True)
+    kb = {k: torch.empty_like(v) for k, v in got.items()}
+    kb["col_scale"] = got["col_scale"].clone()
+    mtb.ep_nvfp4_direct_receive_kblock(packed, H, plan, kb)
+    n_off = int(off_all[-1])
+    for key in ("row_codes", "row_scales", "row_t"):
+        assert torch.equal(kb[key][:n_off], got[key][:n_off]), f"config3 K-blocked {key}"
+    kc, ks = host(kb["col_codes"]), host(kb["col_scales"])
+    ccmp, scmp = host(got["col_codes"]), host(got["col_scales"])
+    for ex in range(len(off_all) - 1):
+        o, pe = int(off_all[ex]), int(off_all[ex + 1] - off_all[ex])
+        cm = ccmp[H * o // 2: H * (o + pe) // 2].reshape(H, pe // 2)
+        sm = scmp[H * o // 16: H * (o + pe) // 16].reshape(H, pe // 16)
+        for r0 in range(0, pe, 256):
+            ln = min(256, pe - r0)
+            kcb = kc[H * (o + r0) // 2: H * (o + r0 + ln) // 2].reshape(H, ln // 2)
+            ksb = ks[H * (o + r0) // 16: H * (o + r0 + ln) // 16].reshape(H, ln // 16)
+            assert_bytes_equal(kcb, cm[:, r0 // 2: (r0 + ln) // 2], f"config3 K-block codes e={ex} rows {r0}")
+            assert_bytes_equal(ksb, sm[:, r0 // 16: (r0 + ln) // 16], f"config3 K-block scales e={ex} rows {r0}")
+    wcc, wcs = orecv.kblock_layout(cc.reshape(-1), cs.reshape(-1), np.array([0, p]), H)
+    assert_bytes_equal(kc[H * int(off_all[e]) // 2: H * int(off_all[e + 1]) // 2], wcc,
+                       f"config3 K-blocked codes of expert {e} (whole, oracle)")
+    assert_bytes_equal(ks[H * int(off_all[e]) // 16: H * int(off_all[e + 1]) // 16], wcs,
+                       f"config3 K-blocked scales of expert {e} (whole, oracle)")
     # unpack of the received rows (grouped order) on sampled rows
     off = int(want["offsets"][-1])
     src = want["src_row"][:off]
