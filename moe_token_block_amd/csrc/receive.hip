@@ -272,13 +272,15 @@ struct RowSrc {
 //     runs the RHT and quantizes its 16 columns in registers, and stores each
 //     column's 8 code bytes and scale byte straight to the operand: the sixteen
 //     blocks of a column sit in one wave, so every store instruction writes
-//     four columns' contiguous 128 code bytes.  In the K-blocked layout a
+//     four columns' 128 contiguous code bytes each.  In the K-blocked layout a
 //     K-block's columnwise output is one contiguous, line-aligned region, and
 //     its code bytes are streamed too.
-// The row copy's loads and the gathers go out together (the same bytes: the L2
-// merges their misses) and the copy is stored before the tile's one barrier,
-// which hands row t's token scale and the tile's 16 scale bytes to the decode
-// through LDS.
+// Loads come in two rounds: each thread's source-row index (shared through
+// LDS), then every byte load at once -- the row copy's pieces and the column
+// gathers (the same bytes: the L2 merges their misses), t and the scale bytes
+// -- as range-checked buffer loads that read zeros for rows without a source.
+// The copy is stored before the tile's second barrier, which hands row t's
+// token scale and the tile's 16 scale bytes to the decode through LDS.
 // 1-D grid of row_tiles * col_tiles workgroups.  Workgroup i runs on XCD
 // i % 8, so the logical tile is taken from a contiguous range per XCD, column
 // tile fastest: the column tiles of a row tile run on one XCD at about the
