@@ -351,12 +351,21 @@ def time_step(path, steps, warmup):
 
 
 # ---------------------------------------------------------------------------- counters
+def _code_only(text):
+    """Source text without comments and whitespace (a comment edit changes no kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_hash(call):
-    """Hash of the sources the call's kernels are built from."""
+    """Hash of the code (comments and whitespace dropped) of the sources the
+    call's kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_token_block_amd", "csrc")
     for f in sorted(CALLS[call][0] + _COMMON):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
