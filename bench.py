@@ -525,7 +525,7 @@ def headline(path3, ms_step, per, steps, warmup, kernels, cpu, copy=None):
     return {
         "metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->nvfp4", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": dict(path3.desc, workload=path3.desc["workload"] + ": route plan + NVFP4 pack + D_e + direct "
                        "receive (rowwise + RHT columnwise in K-blocks) + unpack of the received rows",
                        bytes_per_step=total, step_calls=[c.name for c in calls],
@@ -664,7 +664,7 @@ def main():
             total = sum(c.bytes for c in calls)
             emit({"metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
                   "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->nvfp4",
+                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
                   "data": "synthetic", "config": dict(path.desc, bytes_per_step=total),
                   "step_ms": {nm: round(v, 5) for nm, v in step_per.items()}, "kernels": kernels,
                   "cpu_baseline": None}, args)
