@@ -194,6 +194,7 @@ def _check_receive(dev, w, packed_np, got, plan_np, hidden, exact=True):
     dict(seed=5, tokens=7, hidden=64, E=4, k=2, A=16, unused=0.0, empty=[]),
     dict(seed=6, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),   # the maximum expert count
     dict(seed=7, tokens=500, hidden=64, E=300, k=3, A=32, unused=0.1, empty=list(range(0, 300, 3))),
+    dict(seed=8, tokens=300, hidden=448, E=6, k=2, A=16, unused=0.1, empty=[2]),      # a 192-column last tile
 ])
 def test_direct_receive_bit_exact(dev, case):
     w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
@@ -478,6 +479,8 @@ def test_pack_scatter_and_grouped_columnwise(dev, case):
     dict(seed=42, tokens=700, hidden=4096, E=3, k=1, A=16, unused=0.0, empty=[]),    # experts of > 256 rows
     dict(seed=43, tokens=257, hidden=512, E=16, k=8, A=128, unused=0.0, empty=[0, 15]),
     dict(seed=44, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),
+    dict(seed=45, tokens=400, hidden=448, E=6, k=2, A=16, unused=0.1, empty=[2]),     # a 192-column last tile
+    dict(seed=46, tokens=90, hidden=64, E=3, k=2, A=16, unused=0.0, empty=[]),        # one 64-column tile
 ])
 def test_direct_receive_kblock_layout(dev, case):
     """The K-blocked columnwise layout: the oracle's operand re-laid by oracle.kblock_layout,
