@@ -12,6 +12,7 @@ import workloads
 from oracle import formats as F
 from oracle import nvfp4 as onv
 from oracle import mxfp8 as omx
+from oracle import mxfp4 as omx4
 from oracle import receive as orecv
 from oracle import dswiglu as odsw
 from oracle.routing import route_plan as o_route
@@ -138,6 +139,19 @@ def test_config2_nvfp4_and_mxfp8(dev):
     off = int(want["offsets"][-1])
     assert_bytes_equal(host(gd)[:off], ed[:off], "config2 MXFP8 grouped data")
     assert_bytes_equal(host(gs)[:off], es[:off], "config2 MXFP8 grouped scales")
+    # the MXFP4 receive (a 32-row alignment) on the whole tensor
+    print("config2: MXFP4 receive", flush=True)
+    plan32 = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 8, 32)
+    g4 = mtb.ep_mxfp4_direct_receive(packed, 4096, plan32)
+    w4 = omx4.direct_receive(packed_np, 4096, w.topk_idx, 8, 32)
+    off4 = int(w4["offsets"][-1])
+    assert_bytes_equal(host(plan32["offsets"]), w4["offsets"], "config2 MXFP4 plan offsets")
+    for key in ("row_codes", "row_scales"):
+        assert_bytes_equal(host(g4[key])[:off4], w4[key][:off4], f"config2 MXFP4 {key} (whole tensor)")
+    assert_bytes_equal(host(g4["col_codes"])[: 4096 * off4 // 2], w4["col_codes"][: 4096 * off4 // 2],
+                       "config2 MXFP4 columnwise codes (whole tensor)")
+    assert_bytes_equal(host(g4["col_scales"])[: 4096 * off4 // 32], w4["col_scales"][: 4096 * off4 // 32],
+                       "config2 MXFP4 columnwise scales (whole tensor)")
 
 
 def test_config3_dsv3_share(dev):
