@@ -195,6 +195,7 @@ def _check_receive(dev, w, packed_np, got, plan_np, hidden, exact=True):
     dict(seed=6, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),   # the maximum expert count
     dict(seed=7, tokens=500, hidden=64, E=300, k=3, A=32, unused=0.1, empty=list(range(0, 300, 3))),
     dict(seed=8, tokens=300, hidden=448, E=6, k=2, A=16, unused=0.1, empty=[2]),      # a 192-column last tile
+    dict(seed=9, tokens=64, hidden=16384, E=4, k=2, A=16, unused=0.0, empty=[]),      # the widest packed row
 ])
 def test_direct_receive_bit_exact(dev, case):
     w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
@@ -481,6 +482,7 @@ def test_pack_scatter_and_grouped_columnwise(dev, case):
     dict(seed=44, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),
     dict(seed=45, tokens=400, hidden=448, E=6, k=2, A=16, unused=0.1, empty=[2]),     # a 192-column last tile
     dict(seed=46, tokens=90, hidden=64, E=3, k=2, A=16, unused=0.0, empty=[]),        # one 64-column tile
+    dict(seed=47, tokens=64, hidden=16384, E=4, k=2, A=16, unused=0.0, empty=[]),     # the widest packed row
 ])
 def test_direct_receive_kblock_layout(dev, case):
     """The K-blocked columnwise layout: the oracle's operand re-laid by oracle.kblock_layout,
