@@ -1,10 +1,12 @@
-"""A seeded sweep of random small dispatch shapes, every output compared with the
-oracle byte for byte: the pack, the routing plan, the direct receive in both
-columnwise layouts, the unpack of the routed rows and (for 32-row alignments)
-the MXFP4 receive.  The shapes are drawn once from a fixed seed: ragged token
-counts, widths from one to many 256-column tiles with partial last tiles,
-expert counts up to 80 with empty experts, every alignment the plan accepts up
-to 256, and unused (-1) slots."""
+"""Seeded sweeps of random small shapes, every output compared with the oracle
+byte for byte.  Dispatch: the pack, the routing plan, the direct receive in
+both columnwise layouts, the unpack of the routed rows and (for 32-row
+alignments) the MXFP4 receive; dSwiGLU: the epilogue and the FC1-gradient
+operands, with and without a materialized dX.  The shapes are drawn once from
+fixed seeds: ragged token counts, widths from one to many 256-column tiles with
+partial last tiles, expert counts up to 80 with empty experts, every alignment
+the plan accepts up to 256, unused (-1) slots, and grouped row counts that are
+not multiples of 16 with an occasional large expert."""
 
 import numpy as np
 import pytest
@@ -12,6 +14,7 @@ import torch
 
 import moe_token_block_amd as mtb
 import workloads
+from oracle import dswiglu as odsw
 from oracle import mxfp4 as omx4
 from oracle import nvfp4 as onv
 from oracle import receive as orecv
@@ -83,3 +86,49 @@ def test_dispatch_sweep(dev, case):
             assert_bytes_equal(host(g4[key])[:off], w4[key][:off], f"MXFP4 {key}")
         assert_bytes_equal(host(g4["col_codes"])[: n // 2], w4["col_codes"][: n // 2], "MXFP4 columnwise codes")
         assert_bytes_equal(host(g4["col_scales"])[: n // 32], w4["col_scales"][: n // 32], "MXFP4 columnwise scales")
+
+
+def _dswiglu_cases(n=12, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 41))
+        counts = rng.integers(0, 300, size=E)
+        counts[rng.random(E) < 0.2] = 0                       # empty experts
+        if rng.random() < 0.3:
+            counts[int(rng.integers(0, E))] = int(rng.integers(700, 1500))   # one large expert
+        if counts.sum() == 0:
+            counts[0] = 1
+        out.append(dict(seed=2000 + i, counts=[int(c) for c in counts], ffn=64 * int(rng.integers(1, 25))))
+    return out
+
+
+@pytest.mark.parametrize("case", _dswiglu_cases(), ids=lambda c: f"s{c['seed']}-e{len(c['counts'])}-f{c['ffn']}")
+def test_dswiglu_sweep(dev, case):
+    """dSwiGLU + FC1-grad quantization on random grouped shapes: dX within one BF16
+    ulp of float64 and the amax exact (stage 1); the oracle quantizer on the GPU's
+    own dX and amax byte for byte (stage 2); the recompute form (no dX) equal to
+    the materializing call in every operand byte."""
+    counts, ffn = case["counts"], case["ffn"]
+    print(f"dswiglu sweep case seed={case['seed']} E={len(counts)} rows={sum(counts)} ffn={ffn}", flush=True)
+    w = workloads.small_dswiglu(case["seed"], counts, ffn)
+    args = (bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
+    out = mtb.dswiglu_nvfp4_quant(*args)
+    dx = host(out["dx"])
+    want_dx = odsw.dswiglu(w.preact_bits, w.dy_bits)
+    ulp = np.abs(dx.view(np.int16).astype(np.int64) - want_dx.view(np.int16).astype(np.int64))
+    assert ulp.max(initial=0) <= 1, f"dX differs by {ulp.max()} ulp"
+    am = host(out["amax"])
+    assert_bytes_equal(am.view(np.uint32), odsw.expert_amax(dx, w.counts).view(np.uint32), "amax")
+    q = odsw.fc1_grad_quant(dx, w.counts, am)
+    for key in ("row_scale", "col_scale"):
+        assert_bytes_equal(host(out[key]).view(np.uint32), q[key].view(np.uint32), key)
+    assert_bytes_equal(host(out["row_scales"]), q["row_scales"], "rowwise scales")
+    assert_bytes_equal(host(out["row_codes"]), q["row_codes"], "rowwise codes")
+    assert_bytes_equal(host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "columnwise scales")
+    assert_bytes_equal(host(out["col_codes"])[: q["col_codes"].size], q["col_codes"], "columnwise codes")
+    rec = mtb.dswiglu_nvfp4_quant(*args, materialize_dx=False)
+    for key in ("amax", "row_scale", "col_scale", "row_codes", "row_scales"):
+        assert_bytes_equal(host(rec[key]), host(out[key]), f"recompute {key}")
+    assert_bytes_equal(host(rec["col_codes"])[: q["col_codes"].size], q["col_codes"], "recompute columnwise codes")
+    assert_bytes_equal(host(rec["col_scales"])[: q["col_scales"].size], q["col_scales"], "recompute columnwise scales")
