@@ -2,7 +2,8 @@
 byte for byte.  Dispatch: the pack, the routing plan, the direct receive in
 both columnwise layouts, the unpack of the routed rows and (for 32-row
 alignments) the MXFP4 receive; dSwiGLU: the epilogue and the FC1-gradient
-operands, with and without a materialized dX.  The shapes are drawn once from
+operands, with and without a materialized dX; stochastic rounding: the pack in
+each word mapping and rule, and the receive's stochastic columnwise codes.  The shapes are drawn once from
 fixed seeds: ragged token counts, widths from one to many 256-column tiles with
 partial last tiles, expert counts up to 80 with empty experts, every alignment
 the plan accepts up to 256, unused (-1) slots, and grouped row counts that are
@@ -132,3 +133,38 @@ def test_dswiglu_sweep(dev, case):
         assert_bytes_equal(host(rec[key]), host(out[key]), f"recompute {key}")
     assert_bytes_equal(host(rec["col_codes"])[: q["col_codes"].size], q["col_codes"], "recompute columnwise codes")
     assert_bytes_equal(host(rec["col_scales"])[: q["col_scales"].size], q["col_scales"], "recompute columnwise scales")
+
+
+def _sr_cases(n=8, seed=20261204):
+    rng = np.random.default_rng(seed)
+    return [dict(seed=3000 + i, tokens=int(rng.integers(1, 400)), hidden=64 * int(rng.integers(1, 25)),
+                 E=int(rng.integers(2, 33)), k=int(rng.integers(1, 3)), A=int(rng.choice([16, 32, 64, 128])),
+                 mode=int(rng.integers(1, 5)), sr_seed=int(rng.integers(0, 1 << 62)),
+                 base=int(rng.integers(0, 1 << 40))) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _sr_cases(), ids=lambda c: f"s{c['seed']}-t{c['tokens']}-h{c['hidden']}-m{c['mode']}")
+def test_stochastic_sweep(dev, case):
+    """The stochastic-rounding pack in a random word mapping and rule, and the
+    receive's stochastic columnwise codes, on random shapes, seeds and counter bases."""
+    print(f"SR sweep case {case}", flush=True)
+    w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
+                                 alignment=case["A"])
+    h, mode = case["hidden"], case["mode"]
+    st = torch.tensor([case["sr_seed"], case["base"]], dtype=torch.int64, device=dev)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev), round_mode=mode, sr_state=st)
+    want_p = onv.pack_rows(w.x_bits, sr_seed=case["sr_seed"], sr_counter_base=case["base"],
+                           sr_mode="element" if mode in (1, 3) else "stream", sr_rule="carry" if mode >= 3 else "threshold")
+    assert_bytes_equal(host(packed), want_p, f"SR pack mode {mode}")
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
+    ref = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    got = {key: torch.empty_like(v) for key, v in ref.items()}
+    got["col_scale"] = ref["col_scale"].clone()
+    rs = torch.tensor([case["sr_seed"] ^ 0x5A5A, case["base"] + 17], dtype=torch.int64, device=dev)
+    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, rs)
+    want = orecv.direct_receive(want_p, h, w.topk_idx, w.num_experts, w.alignment,
+                                sr=(case["sr_seed"] ^ 0x5A5A, case["base"] + 17))
+    off = int(host(plan["offsets"])[-1])
+    n = h * off
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], want["col_codes"][: n // 2], "SR columnwise codes")
+    assert_bytes_equal(host(got["col_scales"])[: n // 16], want["col_scales"][: n // 16], "SR columnwise scales")
