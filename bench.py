@@ -67,6 +67,7 @@ CALLS = {
     "nvfp4_columnwise_grouped": (("receive.hip",), ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"]),
     "mxfp8_receive": (("unpack.hip",), ["k_mxfp8_receive"]),
     "nvfp4_unpack": (("unpack.hip",), ["k_nvfp4_unpack"]),
+    "nvfp4_unpack_tokens": (("unpack.hip",), ["k_nvfp4_unpack (one row per token, no gather)"]),
     "dswiglu_nvfp4_quant": (("dswiglu.hip",), ["k_dswiglu_epilogue", "k_dswiglu_reduce", "k_fc1_quant"]),
     "dswiglu_nvfp4_quant_nodx": (("dswiglu.hip",), ["k_dswiglu_epilogue (max only)", "k_dswiglu_reduce",
                                                     "k_fc1_quant (recompute)"]),
@@ -119,6 +120,7 @@ def dispatch_bytes(T, H, k, E, r_cap, R):
     b["mxfp8_pack"] = T * H * 2 + T * H + T * (H // 32)
     b["mxfp8_receive"] = T * (H + H // 32) + r_cap * 4 + R * (H + H // 32)
     b["nvfp4_unpack"] = T * rb + R * 4 + R * H * 2
+    b["nvfp4_unpack_tokens"] = T * rb + T * H * 2
     return b
 
 
@@ -251,6 +253,11 @@ class Path:
             self.outputs["unpacked"] = unpacked
             self._add("nvfp4_unpack", lambda: m.ep_nvfp4_unpack(packed, H, src_row=src_valid, out=unpacked),
                       b["nvfp4_unpack"], elements=R * H)
+            # the per-token form (each packed row once, no gather): one row per token
+            unpacked_t = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            self.outputs["unpacked_tokens"] = unpacked_t
+            self._add("nvfp4_unpack_tokens", lambda: m.ep_nvfp4_unpack(packed, H, out=unpacked_t),
+                      b["nvfp4_unpack_tokens"], in_step=False, elements=T * H)
         if n == 4:
             srr = torch.tensor([1234, 1 << 40], dtype=torch.int64, device=dev)
             self._add("nvfp4_direct_receive_sr", lambda: m.ep_nvfp4_direct_receive_sr(packed, H, plan, recv, srr),

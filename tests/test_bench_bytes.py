@@ -31,6 +31,7 @@ def test_dispatch_bytes_per_configuration():
     assert b["nvfp4_direct_receive_kblock"] == b["nvfp4_direct_receive"]   # same bytes, re-placed
     # the unpack of the routed rows: packed rows once in, R rows of BF16 out
     assert b["nvfp4_unpack"] == T * (9 * H // 16 + 4) + T * k * 4 + T * k * H * 2
+    assert _mb(b["nvfp4_unpack_tokens"]) == 301.0   # one row per token
     # config 4: 32768 x 4096, top-2 of 16
     T, H, k, E = 32768, 4096, 2, 16
     b = bench.dispatch_bytes(T, H, k, E, T * k + E * 15, T * k)
