@@ -192,7 +192,9 @@ def kernel_times(args):
     raw = args.raw or tempfile.mkdtemp(prefix="mtb_ktimes_")
     steps = 10
     path = os.path.join(args.out_dir, "kernel_times.json")
-    doc = json.load(open(path)) if os.path.exists(path) else {}
+    prev = os.path.join(ROOT, "profiles", "kernel_times.json")   # the configurations not re-run are kept
+    doc = json.load(open(path if os.path.exists(path) else prev)) if os.path.exists(path) or os.path.exists(prev) \
+        else {}
     calls = doc.get("calls", {})
     for n in [int(c) for c in args.configs.split(",") if c]:
         wl = f"cfg{n}"
