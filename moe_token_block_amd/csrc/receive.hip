@@ -8,23 +8,16 @@
 //
 // Launch 1 (k_expert_scale): D_e = 4 * max t over expert e's rows.  It reads
 // only the 4-byte token scales, not the codes: no amax pass.
-// Launch 2 (k_nvfp4_receive): one workgroup per 256 grouped rows x 128
-// columns, tiles ordered so that one XCD runs all column tiles of a row tile
-// together (shared L2 lines).  Thread (cg, m) owns columns [8cg, 8cg+8) of
-// the tile and the 16-row block m:
-//   * gathers the 16 code dwords of its rows through src_row (a wave reads
-//     4 rows x 64 contiguous bytes per instruction) and stores them unchanged
-//     to the rowwise operand;
-//   * decodes them exactly (E2M1 via the converter, times s*t/4*d_i), fused
-//     with the first butterfly stage, then runs the other three stages down
-//     each of its 8 columns in registers;
-//   * quantizes each 16-value column block with the expert's power-of-two D_e
-//     (reciprocals of the 127 possible block scales from an LDS table) and
-//     stages 8 code bytes + 1 scale per column in LDS;
-// then the workgroup writes the staged transposed tile with stores where 16
-// consecutive threads cover one column's 128 contiguous bytes.
-// Tiles are aligned to 256 global grouped rows; a tile may straddle experts
-// (slots are 16-aligned), so every 16-row block looks up its own expert.
+// Launch 2 (k_nvfp4_receive): one workgroup per 256 grouped rows x 256
+// columns.  The rowwise operand is the gathered rows' bytes, stored unchanged
+// in expert order; the columnwise operand is built per 16 x 16 block in one
+// lane's registers (exact decode fused with the first butterfly stage, the
+// other three stages, quantization against the expert's power-of-two D_e)
+// and stored from there.  The kernel's own comment gives the lane mapping and
+// the two load rounds.  Layouts: compact (each expert's columnwise operand one
+// [H, P_e/2] code matrix) or K-blocked (the same in 256-row K-blocks).
+// The MXFP4 receive (k_mxfp4_receive) works on 256 x 128 tiles and stages its
+// quantized column blocks transposed in LDS before a coalesced copy-out.
 // Without the columnwise operand the receive is a plain row gather
 // (k_nvfp4_gather).
 #include "common.h"
@@ -32,6 +25,7 @@
 
 namespace mtb {
 
+// MXFP4 receive tiles
 constexpr int kTileRows = 256;
 constexpr int kThreads = kTileRows;       // one grouped row per thread in the row rounds
 constexpr int kTileCols = 128;
