@@ -16,8 +16,8 @@
 // and stored from there.  The kernel's own comment gives the lane mapping and
 // the two load rounds.  Layouts: compact (each expert's columnwise operand one
 // [H, P_e/2] code matrix) or K-blocked (the same in 256-row K-blocks).
-// The MXFP4 receive (k_mxfp4_receive) works on 256 x 128 tiles and stages its
-// quantized column blocks transposed in LDS before a coalesced copy-out.
+// The MXFP4 receive (k_mxfp4_receive) has the same tiles and loads and
+// re-quantizes both operands to E2M1 with power-of-two scales per 32.
 // Without the columnwise operand the receive is a plain row gather
 // (k_nvfp4_gather).
 #include "common.h"
@@ -25,11 +25,6 @@
 
 namespace mtb {
 
-// MXFP4 receive tiles
-constexpr int kTileRows = 256;
-constexpr int kThreads = kTileRows;       // one grouped row per thread in the row rounds
-constexpr int kTileCols = 128;
-constexpr int kBlocks = kTileRows / 16;  // 16-row blocks per tile
 constexpr int kXcds = 8;                 // CDNA4: 8 XCDs, workgroups dealt round-robin
 
 __global__ __launch_bounds__(1024) void k_expert_scale(const uint8_t* __restrict__ packed, int T, int H, int row_bytes,
@@ -224,13 +219,6 @@ __device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* c
     }
   }
 }
-
-// LDS staging of the transposed tile: entry (column c, block b) sits at
-// c*16 + (b ^ ((c >> 3) & 15)).  The column phase writes, for a fixed byte
-// pair, 16 lanes with columns 8 apart and one block each -- the XOR spreads
-// them over 16 distinct bank pairs; the copy-out reads all 16 blocks of one
-// column, a permutation inside one 128-byte row.
-__device__ __forceinline__ int stage_at(int c, int b) { return c * kBlocks + (b ^ ((c >> 3) & (kBlocks - 1))); }
 
 // Stochastic variant of col_encode: the same quotients, each code drawn by the
 // carry-form converter with the Philox word of its stream position n0 + i.
@@ -590,7 +578,8 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       ce[i] = tv[i] > 0.0f ? pow2_exponent(tv[i]) : 0;
-      cm[i] = tv[i] == 0.0f ? 0.0f : e4m3_decode(sb[i]) * rht_in_scale(i);
+      // t = 0 (padding): t * d_i / 4, the signed zero the fast path's factor has
+      cm[i] = tv[i] == 0.0f ? tv[i] * rht_in_scale(i) : e4m3_decode(sb[i]) * rht_in_scale(i);
     }
     static_for<0, 8>([&](auto P) {
       constexpr int p = P;
@@ -643,229 +632,229 @@ __device__ __forceinline__ uint32_t mx4_word(const float* v, int e) {
   return fp4_pack2<3>(w, v[6] * k, v[7] * k, sc);
 }
 
-// The value of lane ^ 2 (DPP quad permutation [2, 3, 0, 1]).
-__device__ __forceinline__ float lane_xor2_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+// mx4_word for e >= -126 (the power is a normal float; no prescale).
+__device__ __forceinline__ uint32_t mx4_word_normal(const float* v, int e) {
+  const float sc = pow2f(e);
+  uint32_t w = fp4_pack2<0>(__float_as_uint(v[0]), v[0], v[1], sc);
+  w = fp4_pack2<1>(w, v[2], v[3], sc);
+  w = fp4_pack2<2>(w, v[4], v[5], sc);
+  return fp4_pack2<3>(w, v[6], v[7], sc);
 }
 
-// One workgroup per 256 grouped rows x 128 columns, as the NVFP4 receive.
-// Thread (cg, m) gathers the code dwords of columns [8cg, 8cg+8) of the 16
-// rows of block m.  Rowwise: a 32-column block spans lanes 4j..4j+3 (its max by
-// two lane swaps).  Columnwise: decode + RHT per column pair as the NVFP4
-// receive, a 32-row block spans blocks m and m^1 (lanes 16 apart in one wave).
+// One workgroup per 256 grouped rows x 256 columns, with the NVFP4 receive's
+// tiles, lane mapping and two load rounds (the 16-byte row pieces, the column
+// blocks' 8-byte gathers, t and the scale bytes, as range-checked buffer loads).
+//   * rowwise: thread t re-quantizes the 16-byte pieces it loaded -- piece
+//     t & 7 of rows (t >> 3) + 32 i, i.e. 32 codes, one MXFP4 block -- with
+//     the row's t and two NVFP4 scale bytes from LDS, and stores its 16 code
+//     bytes and scale byte (streamed: whole lines when H is a multiple of 256);
+//   * columnwise: lane (m, j) decodes and transforms its 16 x 16 block as the
+//     NVFP4 receive does; the 32-row block max joins blocks m and m ^ 1
+//     (lanes 4 apart), and each column's 8 code bytes leave from registers --
+//     the sixteen blocks of a column sit in one wave, so a store instruction
+//     writes four columns' 128 contiguous bytes -- and each 32-row block's
+//     scale byte from the even block's lane.
 // Every expert's padded rows are a multiple of 32 (the host checks the
-// alignment), so a 32-row block never straddles two experts.
-__global__ __launch_bounds__(kThreads) void k_mxfp4_receive(const uint8_t* __restrict__ packed, int T, int H,
-                                                       int row_bytes, const int32_t* __restrict__ offsets, int E,
-                                                       const int32_t* __restrict__ src_row, int r_cap, int n_ct,
-                                                       uint8_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-                                                       uint8_t* __restrict__ col_codes,
-                                                       uint8_t* __restrict__ col_scales) {
-  __shared__ uint2 stage_codes[kTileCols * kBlocks];   // [column][block ^ swizzle]; offsets first
-  __shared__ uint8_t stage_sc[kTileCols * (kBlocks / 2)];  // [column][32-row block]
-  __shared__ int s_src[kTileRows];
-  __shared__ float s_t[kTileRows];
-  __shared__ float s_tq[kTileRows];                    // t * d_i / 4 (i = row mod 16)
-  __shared__ uint32_t s_sw[kTileRows][2];              // the tile's 8 NVFP4 scale bytes of each row
-  __shared__ int s_slow[kBlocks], s_live[kBlocks];
-  __shared__ uint64_t s_cbase[kBlocks], s_sbase[kBlocks / 2];
-  __shared__ uint32_t s_cstr[kBlocks], s_sstr[kBlocks / 2];
-  int* s_offs = reinterpret_cast<int*>(stage_codes);  // offsets[0..E] until the column phase
+// alignment), so a 32-row block never straddles two experts; blocks m and
+// m ^ 1 are both live or both dead.
+__global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, int T, int H,
+                                                              const int32_t* __restrict__ offsets, int E,
+                                                              const int32_t* __restrict__ src_row, int r_cap, int n_ct,
+                                                              uint8_t* __restrict__ row_codes,
+                                                              uint8_t* __restrict__ row_scales,
+                                                              uint8_t* __restrict__ col_codes,
+                                                              uint8_t* __restrict__ col_scales) {
+  __shared__ int s_offs[1025];
+  __shared__ float s_t[kT2Rows];
+  __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 NVFP4 scale bytes of each row
+  __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-100
+  __shared__ __align__(16) int s_src[kT2Rows];
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
   const unsigned xq = nb / kXcds, xr = nb % kXcds, x = bx % kXcds;
   const unsigned lt = x * xq + min(x, xr) + bx / kXcds;
   const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
-  const int col0 = ct * kTileCols;
-  const int ncols = min(kTileCols, H - col0);
-  const int g_base = rt * kTileRows;
+  const int col0 = ct * kT2Cols;
+  const int ncols = min(kT2Cols, H - col0);  // 64, 128, 192 or 256
+  const int g_base = rt * kT2Rows;
 
-  {
-    // both loads go out together (clamped indices, results selected afterwards)
-    const int g = g_base + tid;
-    const int sl = src_row[min(g, r_cap - 1)];
-    const int io = min(tid, E);
-    const int o = offsets[io];
-    const int src = g < r_cap ? sl : -1;
-    s_src[tid] = (src >= 0 && src < T) ? src : -1;
-    s_offs[io] = o;  // threads past E rewrite the last entry with its own value
-    for (int i = tid + kThreads; i <= E; i += kThreads) s_offs[i] = offsets[i];
-  }
+  const int lane = tid & 63, w = tid >> 6;
+  const int m = lane >> 2;                    // 16-row block of the column phase
+  const int cg = 4 * w + (lane & 3);          // 16-column group of the column phase
+  const int gb = g_base + 16 * m;
+  const bool col_live = 16 * cg < ncols;
+  const int cgc = col_live ? cg : 0;          // clamped: a dead group re-reads group 0
+
+  const int g = g_base + tid;
+  const int srcv = src_row[(uint32_t)min(g, r_cap - 1)];
+  for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+  const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces (32 columns) per row: 2, 4, 6 or 8
+  s_src[tid] = g < r_cap ? srcv : -1;
   __syncthreads();
-  const int tile_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
-
-  if (tid < kBlocks) {
-    const int gb = g_base + 16 * tid;
-    const int live = gb < tile_end;
-    s_live[tid] = live;
-    if (live) {
-      int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
-      }
-      const int off = s_offs[lo], len = s_offs[lo + 1] - off;
-      s_cbase[tid] = (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
-      s_cstr[tid] = (uint32_t)(len >> 1);
-      if ((tid & 1) == 0) {
-        s_sbase[tid >> 1] = (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
-        s_sstr[tid >> 1] = (uint32_t)(len >> 5);
-      }
+  const int tile_end = min(s_offs[E], r_cap & ~31);  // rows this tile writes: whole 32-row blocks
+  int rsrc[8], sl[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rsrc[i] = s_src[(tid >> 3) + 32 * i];
+  {
+    const int4* sp = reinterpret_cast<const int4*>(s_src + 16 * m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 v = sp[q];
+      sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
     }
   }
-  // One row per thread: t and the tile's scale words; thread (cg, m): the code
-  // dwords of columns [8cg, 8cg+8) of the 16 rows of block m.  Every load goes
-  // out before the first wait, at clamped indices (rows without a source read
-  // row 0, a 64-column tile reads its first eight code dwords twice); the
-  // results are selected afterwards.
-  const int cg = tid & 15, m = tid >> 4;
-  const int r0 = 16 * m;
-  const int gb = g_base + r0;
-  const bool live = gb < tile_end && cg * 8 < ncols;
-  uint32_t cw[16];
-  float t = 0.0f;
-  uint32_t sw0 = 0, sw1 = 0;
-  if (T > 0) {
-    const int src = s_src[tid];
-    const uint8_t* prow = packed + (size_t)(uint32_t)max(src, 0) * (uint32_t)row_bytes;
-    const float tr = *reinterpret_cast<const float*>(prow + (H >> 1) + (H >> 4));
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(prow + (H >> 1) + (col0 >> 4));
-    const uint32_t s0 = sp[0], s1 = sp[ncols > 64 ? 1 : 0];
-    int4 sv[4];
+  const int src = s_src[tid];
+  const uint32_t nT = (uint32_t)max(T, 0);
+  const __amdgpu_buffer_rsrc_t r_codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.codes), (short)0, (int)(nT ? (nT - 1) * rs.cstride + (uint32_t)(H >> 1) : 0u), kBufDword3);
+  const __amdgpu_buffer_rsrc_t r_scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.scales), (short)0, (int)(nT ? (nT - 1) * rs.sstride + (uint32_t)(H >> 4) : 0u), kBufDword3);
+  const __amdgpu_buffer_rsrc_t r_t = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(rs.t), (short)0, (int)(nT ? (nT - 1) * rs.tstride + 4u : 0u), kBufDword3);
+  auto row_at = [&](int s, uint32_t stride, uint32_t add) -> uint32_t {
+    return (uint32_t)s < nT ? __umul24((uint32_t)s, stride) + add : kNoRow;
+  };
+  u32x4v cv[8];
+  {
+    const uint32_t qa = (uint32_t)(col0 >> 1) + 16u * (uint32_t)(cq < nq ? cq : 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sv[q] = *reinterpret_cast<const int4*>(&s_src[r0 + 4 * q]);
-    const int* sr = reinterpret_cast<const int*>(sv);
-    const uint8_t* base = packed + (col0 >> 1) + 4 * (cg & ((ncols >> 3) - 1));
-    uint32_t v[16];
+    for (int i = 0; i < 8; ++i) cv[i] = __builtin_amdgcn_raw_buffer_load_b128(r_codes, row_at(rsrc[i], rs.cstride, qa), 0, 0);
+  }
+  uint32_t wx[16], wy[16];
+  {
+    const uint32_t ca = (uint32_t)(col0 >> 1) + 8u * (uint32_t)cgc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = *reinterpret_cast<const uint32_t*>(base + (size_t)(uint32_t)max(sr[i], 0) * (uint32_t)row_bytes);
-    if (src >= 0) {
-      t = tr;
-      sw0 = s0;
-      sw1 = ncols > 64 ? s1 : 0u;
+    for (int i = 0; i < 16; ++i) {
+      const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r_codes, row_at(sl[i], rs.cstride, ca), 0, 0);
+      wx[i] = v.x;
+      wy[i] = v.y;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cw[i] = (live && sr[i] >= 0) ? v[i] : 0u;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cw[i] = 0u;
+  }
+  const float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_t, row_at(src, rs.tstride, 0u), 0, 0));
+  uint4 sw;
+  {
+    // a 16-byte load past the resource's end reads zeros for the dwords beyond it
+    const u32x4v q = __builtin_amdgcn_raw_buffer_load_b128(r_scales, row_at(src, rs.sstride, (uint32_t)(col0 >> 4)), 0, 0);
+    sw = make_uint4(q.x, q.y, q.z, q.w);
   }
   s_t[tid] = t;
-  s_tq[tid] = t * rht_in_scale(tid & 15);
-  s_sw[tid][0] = sw0;
-  s_sw[tid][1] = sw1;
+  s_sw[tid] = sw;
   {
-    const uint64_t bal = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
-    if ((tid & 15) == 0) s_slow[tid >> 4] = ((bal >> (tid & 48)) & 0xFFFFull) != 0;
+    const uint64_t tiny = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
+    if (lane < 4) s_tiny[4 * w + lane] = ((tiny >> (16 * lane)) & 0xFFFFu) != 0;
   }
   __syncthreads();
 
-  // column phase (every lane takes part: the 32-row max crosses lanes 16 apart)
-  {
-    const int sh = 8 * ((cg >> 1) & 3);
-    const bool slow = s_slow[m] != 0;
-    float cm[16];
+  // rowwise: each of the thread's eight pieces is one 32-column block of a row
+#pragma unroll 1
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const int gr = g_base + r;
+    const float tr = s_t[r];
+    const uint32_t sb2 = reinterpret_cast<const uint16_t*>(&s_sw[r])[cq];  // scale bytes 2cq, 2cq+1
+    const float st0 = e4m3_decode(sb2) * tr, st1 = e4m3_decode(sb2 >> 8) * tr;
+    const uint32_t cw4[4] = {cv[i].x, cv[i].y, cv[i].z, cv[i].w};
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float s = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh);
-      const float t = s_t[r0 + i];
-      // fast: s * t * d_i / 4 (exact: s has 4 significant bits, t/4 is a power
-      // of two); slow (a row with t < 2^-100): s * d_i / 4, t applied per row
-      cm[i] = !slow ? s * s_tq[r0 + i] : (t == 0.0f ? 0.0f : s * rht_in_scale(i));
+    for (int q = 0; q < 4; ++q) {
+      const float st = q < 2 ? st0 : st1;
+      f32x2 u;
+      u = fp4_unpack2<0>(cw4[q], 1.0f); v[8 * q + 0] = u[0] * st; v[8 * q + 1] = u[1] * st;
+      u = fp4_unpack2<1>(cw4[q], 1.0f); v[8 * q + 2] = u[0] * st; v[8 * q + 3] = u[1] * st;
+      u = fp4_unpack2<2>(cw4[q], 1.0f); v[8 * q + 4] = u[0] * st; v[8 * q + 5] = u[1] * st;
+      u = fp4_unpack2<3>(cw4[q], 1.0f); v[8 * q + 6] = u[0] * st; v[8 * q + 7] = u[1] * st;
     }
+    float a = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float z0[16], z1[16];
-      if (!slow) {
-        if (p == 0) decode_stage1<0, false>(cw, cm, nullptr, z0, z1);
-        if (p == 1) decode_stage1<1, false>(cw, cm, nullptr, z0, z1);
-        if (p == 2) decode_stage1<2, false>(cw, cm, nullptr, z0, z1);
-        if (p == 3) decode_stage1<3, false>(cw, cm, nullptr, z0, z1);
-      } else {
-        int ce[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float t = s_t[r0 + i];
-          ce[i] = t > 0.0f ? pow2_exponent(t) : 0;
-        }
-        if (p == 0) decode_stage1<0, true>(cw, cm, ce, z0, z1);
-        if (p == 1) decode_stage1<1, true>(cw, cm, ce, z0, z1);
-        if (p == 2) decode_stage1<2, true>(cw, cm, ce, z0, z1);
-        if (p == 3) decode_stage1<3, true>(cw, cm, ce, z0, z1);
-      }
-      rht16_upper(z0);
-      rht16_upper(z1);
-      float a0 = absmax16(z0), a1 = absmax16(z1);
-      a0 = fmaxf(a0, __shfl_xor(a0, 16, kWave));  // block m ^ 1 of the same columns
-      a1 = fmaxf(a1, __shfl_xor(a1, 16, kWave));
-      const int e0 = mx4_exponent(a0), e1 = mx4_exponent(a1);
-      const int c0 = cg * 8 + 2 * p;
-      if (live) {
-        stage_codes[stage_at(c0, m)] = make_uint2(mx4_word(z0, e0), mx4_word(z0 + 8, e0));
-        stage_codes[stage_at(c0 + 1, m)] = make_uint2(mx4_word(z1, e1), mx4_word(z1 + 8, e1));
-        if ((m & 1) == 0) {
-          stage_sc[c0 * (kBlocks / 2) + (m >> 1)] = (uint8_t)(e0 + 127);
-          stage_sc[(c0 + 1) * (kBlocks / 2) + (m >> 1)] = (uint8_t)(e1 + 127);
-        }
-      }
+    for (int q = 0; q < 32; ++q) a = fmaxf(a, fabsf(v[q]));
+    const int e = mx4_exponent(a);
+    u32x4v out;
+    if (__ballot(e < -126) == 0) {  // every lane's power is a normal float (uniform branch)
+      out = u32x4v{mx4_word_normal(v, e), mx4_word_normal(v + 8, e), mx4_word_normal(v + 16, e),
+                   mx4_word_normal(v + 24, e)};
+    } else {
+      out = u32x4v{mx4_word(v, e), mx4_word(v + 8, e), mx4_word(v + 16, e), mx4_word(v + 24, e)};
     }
+    if (gr >= tile_end || cq >= nq) continue;
+    __builtin_nontemporal_store(
+        out, reinterpret_cast<u32x4v*>(row_codes + (size_t)(uint32_t)gr * (uint32_t)(H >> 1) + (col0 >> 1) + 16 * cq));
+    row_scales[(size_t)(uint32_t)gr * (uint32_t)(H >> 5) + (uint32_t)((col0 >> 5) + cq)] = (uint8_t)(e + 127);
   }
 
-  // rowwise: the decoded values of each row, a 32-column block over lanes 4j..4j+3
+  if (!col_live || gb >= tile_end) return;  // the partner block m ^ 1 returns with it
+  int ex = 0;
   {
-    const int sh = 8 * ((cg >> 1) & 3);
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const float st = e4m3_decode(s_sw[r0 + i][cg >> 3] >> sh) * s_t[r0 + i];
-      float v[8];
-      f32x2 g;
-      g = fp4_unpack2<0>(cw[i], 1.0f); v[0] = g[0] * st; v[1] = g[1] * st;
-      g = fp4_unpack2<1>(cw[i], 1.0f); v[2] = g[0] * st; v[3] = g[1] * st;
-      g = fp4_unpack2<2>(cw[i], 1.0f); v[4] = g[0] * st; v[5] = g[1] * st;
-      g = fp4_unpack2<3>(cw[i], 1.0f); v[6] = g[0] * st; v[7] = g[1] * st;
-      float a = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) a = fmaxf(a, fabsf(v[q]));
-      a = fmaxf(a, __uint_as_float(lane_xor1(__float_as_uint(a))));
-      a = fmaxf(a, lane_xor2_f(a));
-      const int e = mx4_exponent(a);
-      const uint32_t w = mx4_word(v, e);
-      if (live) {
-        const size_t g_row = (size_t)(uint32_t)(gb + i);
-        *reinterpret_cast<uint32_t*>(row_codes + g_row * (uint32_t)(H >> 1) + (col0 >> 1) + 4 * cg) = w;
-        if ((cg & 3) == 0) row_scales[g_row * (uint32_t)(H >> 5) + ((col0 + 8 * cg) >> 5)] = (uint8_t)(e + 127);
-      }
+    int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
     }
+    ex = lo;
   }
-  __syncthreads();
-  // transposed copy-out of the columnwise codes (as the NVFP4 receive), then
-  // the scales: thread (pair, j) writes 32-row block `pair` of columns j, j+32, ...
-  {
-    const int b = tid % kBlocks;
-    if (s_live[b]) {
-      const uint64_t cbase = s_cbase[b];
-      const uint32_t cstr = s_cstr[b];
+  const int off = s_offs[ex], len = s_offs[ex + 1] - off;
+  uint8_t* const cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+  uint8_t* const cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
+  const uint32_t cstr = (uint32_t)(len >> 1), sstr = (uint32_t)(len >> 5);
+  const int h0 = col0 + 16 * cg;
+  const int sh = 8 * (cg & 3);
+  // the decode path is chosen per 32-row block, so that blocks m and m ^ 1 take
+  // the same branch and the lane exchange of their maxima sees both lanes
+  // (the two-step decode is exact for any t)
+  const bool slow = (s_tiny[m] | s_tiny[m ^ 1]) != 0;
+  float tv[16];
+  uint32_t sb[16];
+  const uint32_t* swd = reinterpret_cast<const uint32_t*>(s_sw) + 4 * (16 * m) + (cg >> 2);
 #pragma unroll
-      for (int r = 0; r < (kTileCols * kBlocks) / kThreads; ++r) {
-        const int c = r * (kThreads / kBlocks) + tid / kBlocks;
-        if (c >= ncols) break;
-        *reinterpret_cast<uint2*>(col_codes + cbase + (uint64_t)(uint32_t)(col0 + c) * cstr) =
-            stage_codes[stage_at(c, b)];
-      }
+  for (int i = 0; i < 16; ++i) {
+    tv[i] = s_t[16 * m + i];
+    sb[i] = swd[4 * i] >> sh;
+  }
+  // one column pair: decode + RHT, the 32-row block max with block m ^ 1 (lane
+  // ^ 4), codes and scale bytes
+  auto pair_out = [&](auto P, const float* cm, const int* ce) {
+    constexpr int p = decltype(P)::value;
+    float z0[16], z1[16];
+    if (ce == nullptr) decode_stage1<p & 3, false>((p < 4) ? wx : wy, cm, nullptr, z0, z1);
+    else decode_stage1<p & 3, true>((p < 4) ? wx : wy, cm, ce, z0, z1);
+    rht16_upper(z0);
+    rht16_upper(z1);
+    float a0 = absmax16(z0), a1 = absmax16(z1);
+    a0 = fmaxf(a0, __shfl_xor(a0, 4, kWave));
+    a1 = fmaxf(a1, __shfl_xor(a1, 4, kWave));
+    const int e0 = mx4_exponent(a0), e1 = mx4_exponent(a1);
+    const uint32_t h = (uint32_t)(h0 + 2 * p);
+    u32x2v q0, q1;
+    if (__ballot(min(e0, e1) < -126) == 0) {  // uniform branch, as in the rowwise phase
+      q0 = u32x2v{mx4_word_normal(z0, e0), mx4_word_normal(z0 + 8, e0)};
+      q1 = u32x2v{mx4_word_normal(z1, e1), mx4_word_normal(z1 + 8, e1)};
+    } else {
+      q0 = u32x2v{mx4_word(z0, e0), mx4_word(z0 + 8, e0)};
+      q1 = u32x2v{mx4_word(z1, e1), mx4_word(z1 + 8, e1)};
     }
-    const int pr = tid % (kBlocks / 2);
-    if (s_live[2 * pr]) {
-      const uint64_t sbase = s_sbase[pr];
-      const uint32_t sstr = s_sstr[pr];
+    __builtin_nontemporal_store(q0, reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr));
+    __builtin_nontemporal_store(q1, reinterpret_cast<u32x2v*>(cc + (uint64_t)(h + 1) * cstr));
+    if ((m & 1) == 0) {
+      cs[(uint64_t)h * sstr] = (uint8_t)(e0 + 127);
+      cs[(uint64_t)(h + 1) * sstr] = (uint8_t)(e1 + 127);
+    }
+  };
+  float cm[16];
+  if (!slow) {
+    // s * t * d_i / 4: exact (s has 4 significant bits, t/4 is a power of two)
 #pragma unroll
-      for (int r = 0; r < (kTileCols * (kBlocks / 2)) / kThreads; ++r) {
-        const int c = r * (kThreads / (kBlocks / 2)) + tid / (kBlocks / 2);
-        if (c >= ncols) break;
-        col_scales[sbase + (uint64_t)(uint32_t)(col0 + c) * sstr] = stage_sc[c * (kBlocks / 2) + pr];
-      }
+    for (int i = 0; i < 16; ++i) cm[i] = e4m3_decode(sb[i]) * (tv[i] * rht_in_scale(i));
+    static_for<0, 8>([&](auto P) { pair_out(P, cm, nullptr); });
+  } else {
+    // a row with t < 2^-100: s * d_i / 4, and t applied per row
+    int ce[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ce[i] = tv[i] > 0.0f ? pow2_exponent(tv[i]) : 0;
+      // t = 0 (padding): t * d_i / 4, the signed zero the fast path's factor has
+      cm[i] = tv[i] == 0.0f ? tv[i] * rht_in_scale(i) : e4m3_decode(sb[i]) * rht_in_scale(i);
     }
+    static_for<0, 8>([&](auto P) { pair_out(P, cm, ce); });
   }
 }
 
@@ -1053,11 +1042,13 @@ MTB_EXPORT int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens
   if (!row_codes || !row_scales || !col_codes || !col_scales) return EP_ERR_NULL;
   if (r_cap == 0) return EP_OK;
   const int H = (int)hidden;
-  const int64_t n_rt = (r_cap + kTileRows - 1) / kTileRows, n_ct = (H + kTileCols - 1) / kTileCols;
-  if (n_rt * n_ct * kThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
-  hipLaunchKernelGGL(k_mxfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kThreads), 0, (hipStream_t)stream, packed,
-                     (int)tokens, H, 9 * H / 16 + 4, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
-                     row_codes, row_scales, col_codes, col_scales);
+  const int64_t n_rt = (r_cap + kT2Rows - 1) / kT2Rows, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL(k_mxfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream, src,
+                     (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
+                     col_codes, col_scales);
   return launch_status();
 }
 

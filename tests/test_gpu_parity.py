@@ -520,6 +520,43 @@ def _check_mxfp4(got, want, off, h, exact=True):
                        want["col_scales"][: n // 32], "mxfp4 columnwise", block=32)
 
 
+@pytest.mark.parametrize("h", [256, 512])
+def test_receive_slow_blocks_with_padding(dev, h):
+    """16-row blocks that take the two-step decode (a row with a tiny t) and
+    also hold padding rows, with columns that are zero in every row of the
+    block: the transform of an all-zero column is a pattern of signed zeros set
+    by the sign vector, and its codes carry those signs.  Expert 0 holds one
+    tiny row (zero in its first half) and padding; expert 1 ordinary rows;
+    expert 2 a tiny row among ordinary ones.  The NVFP4 receive in both layouts
+    and the MXFP4 receive, byte for byte."""
+    rng = np.random.default_rng(58 + h)
+    tiny = rng.standard_normal((2, h)) * 1e-30
+    tiny[0, : h // 2] = 0.0
+    x = np.concatenate([tiny[:1], rng.standard_normal((20, h)), tiny[1:], rng.standard_normal((16, h))])
+    topk = np.array([0] + [1] * 20 + [2] * 17, dtype=np.int32)[:, None]
+    bits = _bits(x)
+    print(f"slow blocks with padding h={h}", flush=True)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(bits, dev))
+    packed_np = onv.pack_rows(bits)
+    assert_bytes_equal(host(packed), packed_np, "pack")
+    assert packed_np[0, h // 2 + h // 16:].view(np.float32)[0] < 2.0 ** -100   # the two-step decode's rows
+    plan = mtb.ep_route_plan(torch.from_numpy(topk).to(dev), 3, 32)
+    plan_np = {k: host(v) for k, v in plan.items() if torch.is_tensor(v)}
+    got = mtb.ep_nvfp4_direct_receive(packed, h, plan)
+    w = types.SimpleNamespace(topk_idx=topk, num_experts=3, alignment=32)
+    _check_receive(dev, w, packed_np, got, plan_np, h)
+    kb = {key: torch.empty_like(v) for key, v in got.items()}
+    kb["col_scale"] = got["col_scale"].clone()
+    mtb.ep_nvfp4_direct_receive_kblock(packed, h, plan, kb)
+    want = orecv.direct_receive(packed_np, h, topk, 3, 32)
+    off = plan_np["offsets"].astype(np.int64)
+    n = h * int(off[-1])
+    wc, ws = orecv.kblock_layout(want["col_codes"][: n // 2], want["col_scales"][: n // 16], off, h)
+    assert_bytes_equal(host(kb["col_codes"])[: n // 2], wc, "K-blocked columnwise codes")
+    assert_bytes_equal(host(kb["col_scales"])[: n // 16], ws, "K-blocked columnwise scales")
+    g4 = mtb.ep_mxfp4_direct_receive(packed, h, plan)
+    _check_mxfp4(g4, omx4.direct_receive(packed_np, h, topk, 3, 32), int(off[-1]), h)
+
 @pytest.mark.parametrize("case", [
     dict(seed=51, tokens=150, hidden=256, E=5, k=2, A=32, unused=0.05, empty=[3]),
     dict(seed=52, tokens=600, hidden=192, E=8, k=2, A=128, unused=0.0, empty=[]),     # a 64-column last tile
