@@ -183,21 +183,22 @@ def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None,
     return out
 
 
-def kblock_layout(col_codes, col_scales, offsets, hidden, block_rows=256):
+def kblock_layout(col_codes, col_scales, offsets, hidden, block_rows=256, scale_rows=16):
     """The columnwise operand re-laid in K-blocks (a GEMM-ready variant of R16).
 
     Per expert e (P_e = offsets[e+1] - offsets[e] grouped rows), the grouped
     rows are cut into K-blocks of ``block_rows`` (the last one shorter); block
     kb holds rows [kb*block_rows, kb*block_rows + len) as an [H, len/2] code
     matrix (row h = column h, grouped-row order, low nibble first) at byte
-    H*off_e/2 + H*kb*block_rows/2, and an [H, len/16] scale matrix at byte
-    H*off_e/16 + H*kb*block_rows/16.  The values are those of the compact
-    layout; only their places change.
+    H*off_e/2 + H*kb*block_rows/2, and an [H, len/S] scale matrix at byte
+    H*off_e/S + H*kb*block_rows/S, S = ``scale_rows`` grouped rows per scale
+    (16 for NVFP4, 32 for the MXFP4 receive's R23).  The values are those of
+    the compact layout; only their places change.
     """
     col_codes = np.asarray(col_codes, dtype=np.uint8)
     col_scales = np.asarray(col_scales, dtype=np.uint8)
     off = np.asarray(offsets, dtype=np.int64)
-    h = hidden
+    h, sr = hidden, scale_rows
     out_c = np.zeros_like(col_codes)
     out_s = np.zeros_like(col_scales)
     for e in range(off.shape[0] - 1):
@@ -205,13 +206,13 @@ def kblock_layout(col_codes, col_scales, offsets, hidden, block_rows=256):
         if p == 0:
             continue
         cm = col_codes[h * o // 2 : h * (o + p) // 2].reshape(h, p // 2)
-        sm = col_scales[h * o // 16 : h * (o + p) // 16].reshape(h, p // 16)
+        sm = col_scales[h * o // sr : h * (o + p) // sr].reshape(h, p // sr)
         for r0 in range(0, p, block_rows):
             ln = min(block_rows, p - r0)
             c0 = h * (o + r0) // 2
-            s0 = h * (o + r0) // 16
+            s0 = h * (o + r0) // sr
             out_c[c0 : c0 + h * ln // 2] = cm[:, r0 // 2 : (r0 + ln) // 2].reshape(-1)
-            out_s[s0 : s0 + h * ln // 16] = sm[:, r0 // 16 : (r0 + ln) // 16].reshape(-1)
+            out_s[s0 : s0 + h * ln // sr] = sm[:, r0 // sr : (r0 + ln) // sr].reshape(-1)
     return out_c, out_s
 
 

@@ -217,25 +217,30 @@ def test_fc1_wgrad_error_within_5_percent_of_default():
     assert np.sqrt(errs["default"]) / np.sqrt(ref_norm) < 0.2
 
 
-def test_kblock_layout_is_a_permutation_read_back_by_a_blocked_consumer():
+@pytest.mark.parametrize("scale_rows, sizes", [
+    (16, [272, 0, 256, 16, 528, 32]),     # NVFP4: experts of 256 + 16 rows, exactly 256, 16 and empty
+    (32, [288, 0, 256, 32, 544, 64]),     # MXFP4: one scale per 32 rows
+])
+def test_kblock_layout_is_a_permutation_read_back_by_a_blocked_consumer(scale_rows, sizes):
     """The K-blocked columnwise layout holds the compact operand's bytes: a consumer that
     walks experts, then K-blocks, then columns recovers every (column, grouped row) code
-    and scale of the compact layout -- including experts of 272 rows (blocks 256 + 16),
-    exactly 256, 16 and empty."""
+    and scale of the compact layout -- including a last K-block shorter than 256 rows,
+    an expert of exactly 256 rows, one of a single scale block and an empty one."""
     from oracle.receive import kblock_layout
-    rng = np.random.default_rng(41)
+    rng = np.random.default_rng(41 + scale_rows)
     h = 64
-    sizes = [272, 0, 256, 16, 528, 32]
+    sr = scale_rows
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     n = int(off[-1])
     comp_c = rng.integers(0, 256, h * n // 2, dtype=np.uint8)
-    comp_s = rng.integers(0, 127, h * n // 16, dtype=np.uint8)
-    kc, ks = kblock_layout(comp_c, comp_s, off, h)
+    comp_s = rng.integers(0, 127, h * n // sr, dtype=np.uint8)
+    kc, ks = kblock_layout(comp_c, comp_s, off, h, scale_rows=sr)
     assert sorted(kc.tolist()) == sorted(comp_c.tolist())          # a permutation of the bytes
+    assert sorted(ks.tolist()) == sorted(comp_s.tolist())
     for e, p in enumerate(sizes):
         o = int(off[e])
         cpos = h * o // 2
-        spos = h * o // 16
+        spos = h * o // sr
         for r0 in range(0, p, 256):
             ln = min(256, p - r0)
             for col in range(h):
@@ -244,7 +249,7 @@ def test_kblock_layout_is_a_permutation_read_back_by_a_blocked_consumer():
                     assert kc[cpos] == want, (e, r0, col, j)
                     cpos += 1
             for col in range(h):
-                for b in range(ln // 16):
-                    assert ks[spos] == comp_s[h * o // 16 + col * (p // 16) + r0 // 16 + b]
+                for b in range(ln // sr):
+                    assert ks[spos] == comp_s[h * o // sr + col * (p // sr) + r0 // sr + b]
                     spos += 1
-        assert cpos == h * (o + p) // 2 and spos == h * (o + p) // 16
+        assert cpos == h * (o + p) // 2 and spos == h * (o + p) // sr
