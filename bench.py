@@ -63,6 +63,7 @@ CALLS = {
     "nvfp4_direct_receive_kblock": (("receive.hip",), ["k_nvfp4_receive (K-blocked columnwise layout)"]),
     "nvfp4_direct_receive_sr": (("receive.hip",), ["k_nvfp4_receive (stochastic columnwise codes)"]),
     "mxfp4_receive": (("receive.hip",), ["k_mxfp4_receive"]),
+    "mxfp4_receive_kblock": (("receive.hip",), ["k_mxfp4_receive (K-blocked columnwise layout)"]),
     "nvfp4_pack_scatter": (("pack.hip",), ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"]),
     "nvfp4_columnwise_grouped": (("receive.hip",), ["k_expert_scale_grouped", "k_nvfp4_receive (grouped rows)"]),
     "mxfp8_receive": (("unpack.hip",), ["k_mxfp8_receive"]),
@@ -115,6 +116,7 @@ def dispatch_bytes(T, H, k, E, r_cap, R):
                                  + R * (H // 2 + H // 16 + 4) + R * (H // 2 + H // 16))
     b["nvfp4_direct_receive_kblock"] = b["nvfp4_direct_receive_sr"] = b["nvfp4_direct_receive"]
     b["mxfp4_receive"] = T * rb + r_cap * 4 + (E + 1) * 4 + 2 * R * (H // 2 + H // 32)
+    b["mxfp4_receive_kblock"] = b["mxfp4_receive"]     # the same bytes, placed per K-block
     b["nvfp4_pack_scatter"] = T * H * 2 + T * k * 4 + R * rb
     b["nvfp4_columnwise_grouped"] = R * rb + (E + 1) * 4 + R * (H // 2 + H // 16) + E * 4
     b["mxfp8_pack"] = T * H * 2 + T * H + T * (H // 32)
@@ -270,6 +272,11 @@ class Path:
                        col_codes=torch.empty(r32 * H // 2, **u8), col_scales=torch.empty(r32 * H // 32, **u8))
             self._add("mxfp4_receive", lambda: m.ep_mxfp4_direct_receive(packed, H, plan32, out=mx4),
                       dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive"], in_step=False)
+            mx4k = {nm: torch.empty_like(v) for nm, v in mx4.items()}
+            self.outputs.update({f"mx4k.{nm}": v for nm, v in mx4k.items()})
+            self._add("mxfp4_receive_kblock",
+                      lambda: m.ep_mxfp4_direct_receive(packed, H, plan32, out=mx4k, kblock=True),
+                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive_kblock"], in_step=False)
             fused = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
                          row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
                          col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))

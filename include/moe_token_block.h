@@ -309,6 +309,19 @@ int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens, int64_t h
                                 uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
                                 void* stream);
 
+/* The MXFP4 receive with its columnwise operand in K-blocks, as
+ * ep_nvfp4_direct_receive_kblock lays out NVFP4's: each expert's grouped rows
+ * in blocks of 256 (the last one shorter, a multiple of 32); block kb of
+ * expert e holds an [hidden, len/2] code matrix at byte hidden*off_e/2 +
+ * 128*hidden*kb of col_codes and an [hidden, len/32] scale matrix at byte
+ * hidden*off_e/32 + 8*hidden*kb of col_scales.  The same bytes as
+ * ep_mxfp4_direct_receive's, only placed per K-block; rowwise operand,
+ * arguments, sizes and errors as there. */
+int32_t ep_mxfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, int64_t hidden, int64_t num_experts,
+                                       int64_t alignment, int64_t r_cap, const int32_t* offsets,
+                                       const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                       uint8_t* col_codes, uint8_t* col_scales, void* stream);
+
 /* MXFP8 receive (P2, description and review comments: received data and block
  * scales are returned per expert, grouped, with 128-aligned slots there --
  * here any multiple of 16): grouped row g copies token src_row[g]'s data row

@@ -52,6 +52,7 @@ _SIGS = {
     "ep_mxfp8_direct_receive": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_mxfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_direct_receive_sr": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -386,12 +387,14 @@ def ep_nvfp4_direct_receive_kblock(packed, hidden, plan, out):
     return out
 
 
-def ep_mxfp4_direct_receive(packed, hidden, plan, out=None):
+def ep_mxfp4_direct_receive(packed, hidden, plan, out=None, kblock=False):
     """MXFP4 rowwise and RHT columnwise grouped operands (E2M1 codes, one E8M0 scale
     per 32 elements) from NVFP4 packed rows and a routing plan whose alignment is a
-    multiple of 32."""
+    multiple of 32; ``kblock`` lays the columnwise operand out in 256-row K-blocks
+    (``ep_mxfp4_direct_receive_kblock``)."""
+    name = "ep_mxfp4_direct_receive_kblock" if kblock else "ep_mxfp4_direct_receive"
     dev = _dev(packed)
-    t = _packed(packed, hidden, dev, "ep_mxfp4_direct_receive")
+    t = _packed(packed, hidden, dev, name)
     e, r_cap = _plan(plan, dev)
     if out is None:
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -399,10 +402,10 @@ def ep_mxfp4_direct_receive(packed, hidden, plan, out=None):
                    col_codes=torch.empty(r_cap * hidden // 2, **u8), col_scales=torch.empty(r_cap * hidden // 32, **u8))
     _receive_out(out, r_cap, hidden, e, dev, scale_div=32, col_scale=False)
     with torch.cuda.device(dev):
-        _check(lib().ep_mxfp4_direct_receive(
+        _check(getattr(lib(), name)(
             _ptr(packed), t, hidden, e, plan.get("alignment", 16), r_cap,
             _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
-            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _stream(dev)), "ep_mxfp4_direct_receive")
+            _ptr(out["col_codes"]), _ptr(out["col_scales"]), _stream(dev)), name)
     return out
 
 

@@ -283,6 +283,56 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kBufDword3 = 0x00020000;
 constexpr uint32_t kNoRow = 0x80000000u;  // beyond every resource (sizes < 2^31)
 
+// Tile row rt of the K-blocked layout: K-block rt of the concatenated
+// per-expert K-block lists (each expert's grouped rows in blocks of kT2Rows,
+// the last one shorter).  Gives its expert, K-block index within the expert,
+// first grouped row and row count; false (for the whole workgroup) when rt is
+// beyond the last K-block.  s_offs holds offsets[0..E] (visible to every
+// thread); s_kbstart (E + 1 ints) and s_wsum (one int per wave) are LDS
+// scratch.  Two barriers; E <= 1024 (four experts per thread).
+__device__ __forceinline__ bool kblock_of_tile(int rt, int E, const int* s_offs, int* s_kbstart, int* s_wsum,
+                                               int& expert, int& kb, int& g_base, int& rows) {
+  const int tid = threadIdx.x;
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    loc[i] = sum;
+    sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kT2Rows - 1) / kT2Rows : 0;
+  }
+  int incl = sum;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_wsum[tid >> 6] = incl;
+  __syncthreads();
+  int wofs = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kT2Threads / 64; ++w) {
+    wofs += w < (tid >> 6) ? s_wsum[w] : 0;
+    total += s_wsum[w];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * tid + i < E) s_kbstart[4 * tid + i] = wofs + incl - sum + loc[i];
+  if (tid == 0) s_kbstart[E] = total;
+  __syncthreads();
+  if (rt >= total) return false;  // beyond the last K-block (uniform)
+  int lo = 0, hi = E - 1;         // last expert whose first K-block is <= rt (empty experts share starts)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_kbstart[mid] <= rt) lo = mid; else hi = mid - 1;
+  }
+  expert = lo;
+  kb = rt - s_kbstart[lo];
+  g_base = s_offs[lo] + kb * kT2Rows;
+  rows = min(kT2Rows, s_offs[lo + 1] - g_base);
+  return true;
+}
+
 template <int SEL, bool SLOW, bool SR>
 __device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float* cm, const int* ce, int dexp,
                                                 const RcpEntry* tab, uint64_t n0, uint64_t n_step, uint32_t klo,
@@ -332,47 +382,12 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   int g_base = rt * kT2Rows;
   int kb = 0, tile_rows = kT2Rows;
   if (KBLOCK) {
-    // the tile is K-block rt of the concatenated per-expert K-block lists
     __shared__ int s_kbstart[1025];
     __shared__ int s_wsum[kT2Threads / 64];
     for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
     __syncthreads();
-    int loc[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * tid + i;
-      loc[i] = sum;
-      sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kT2Rows - 1) / kT2Rows : 0;
-    }
-    int incl = sum;
-    const int lane = tid & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int v = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) s_wsum[tid >> 6] = incl;
-    __syncthreads();
-    int wofs = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kT2Threads / 64; ++w) {
-      wofs += w < (tid >> 6) ? s_wsum[w] : 0;
-      total += s_wsum[w];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * tid + i < E) s_kbstart[4 * tid + i] = wofs + incl - sum + loc[i];
-    if (tid == 0) s_kbstart[E] = total;
-    __syncthreads();
-    if (rt >= total) return;  // beyond the last K-block (uniform)
-    int lo = 0, hi = E - 1;   // last expert whose first K-block is <= rt (empty experts share starts)
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_kbstart[mid] <= rt) lo = mid; else hi = mid - 1;
-    }
-    kb = rt - s_kbstart[lo];
-    g_base = s_offs[lo] + kb * kT2Rows;
-    tile_rows = min(kT2Rows, s_offs[lo + 1] - g_base);
+    int ex;
+    if (!kblock_of_tile(rt, E, s_offs, s_kbstart, s_wsum, ex, kb, g_base, tile_rows)) return;
   }
 
   const int lane = tid & 63, w = tid >> 6;
@@ -657,6 +672,11 @@ __device__ __forceinline__ uint32_t mx4_word_normal(const float* v, int e) {
 // Every expert's padded rows are a multiple of 32 (the host checks the
 // alignment), so a 32-row block never straddles two experts; blocks m and
 // m ^ 1 are both live or both dead.
+// KBLOCK: the columnwise operand in 256-row K-blocks, as the NVFP4 receive's
+// (block kb of expert e: an [H, len/2] code matrix at byte H*off_e/2 +
+// 128*H*kb and an [H, len/32] scale matrix at byte H*off_e/32 + 8*H*kb), the
+// tiles following the K-blocks; its code bytes are streamed.
+template <bool KBLOCK>
 __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, int T, int H,
                                                               const int32_t* __restrict__ offsets, int E,
                                                               const int32_t* __restrict__ src_row, int r_cap, int n_ct,
@@ -677,7 +697,14 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   const int rt = (int)(lt / (unsigned)n_ct), ct = (int)(lt % (unsigned)n_ct);
   const int col0 = ct * kT2Cols;
   const int ncols = min(kT2Cols, H - col0);  // 64, 128, 192 or 256
-  const int g_base = rt * kT2Rows;
+  int g_base = rt * kT2Rows, kb = 0, tile_rows = kT2Rows, kex = 0;
+  if (KBLOCK) {
+    __shared__ int s_kbstart[1025];
+    __shared__ int s_wsum[kT2Threads / 64];
+    for (int i = threadIdx.x; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+    __syncthreads();
+    if (!kblock_of_tile(rt, E, s_offs, s_kbstart, s_wsum, kex, kb, g_base, tile_rows)) return;
+  }
 
   const int lane = tid & 63, w = tid >> 6;
   const int m = lane >> 2;                    // 16-row block of the column phase
@@ -688,11 +715,13 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
 
   const int g = g_base + tid;
   const int srcv = src_row[(uint32_t)min(g, r_cap - 1)];
-  for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+  if (!KBLOCK)
+    for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
   const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces (32 columns) per row: 2, 4, 6 or 8
   s_src[tid] = g < r_cap ? srcv : -1;
   __syncthreads();
-  const int tile_end = min(s_offs[E], r_cap & ~31);  // rows this tile writes: whole 32-row blocks
+  const int off_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
+  const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
   int rsrc[8], sl[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) rsrc[i] = s_src[(tid >> 3) + 32 * i];
@@ -783,19 +812,27 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   }
 
   if (!col_live || gb >= tile_end) return;  // the partner block m ^ 1 returns with it
-  int ex = 0;
-  {
+  uint8_t* cc;
+  uint8_t* cs;
+  uint32_t cstr, sstr;
+  if (KBLOCK) {
+    const int off = s_offs[kex];
+    cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * (uint32_t)m;
+    cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint64_t)H * 8u * (uint32_t)kb + (uint32_t)(m >> 1);
+    cstr = (uint32_t)(tile_rows >> 1);
+    sstr = (uint32_t)(tile_rows >> 5);
+  } else {
     int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
     }
-    ex = lo;
+    const int off = s_offs[lo], len = s_offs[lo + 1] - off;
+    cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
+    cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
+    cstr = (uint32_t)(len >> 1);
+    sstr = (uint32_t)(len >> 5);
   }
-  const int off = s_offs[ex], len = s_offs[ex + 1] - off;
-  uint8_t* const cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
-  uint8_t* const cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
-  const uint32_t cstr = (uint32_t)(len >> 1), sstr = (uint32_t)(len >> 5);
   const int h0 = col0 + 16 * cg;
   const int sh = 8 * (cg & 3);
   // the decode path is chosen per 32-row block, so that blocks m and m ^ 1 take
@@ -832,8 +869,15 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
       q0 = u32x2v{mx4_word(z0, e0), mx4_word(z0 + 8, e0)};
       q1 = u32x2v{mx4_word(z1, e1), mx4_word(z1 + 8, e1)};
     }
-    __builtin_nontemporal_store(q0, reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr));
-    __builtin_nontemporal_store(q1, reinterpret_cast<u32x2v*>(cc + (uint64_t)(h + 1) * cstr));
+    u32x2v* const pa = reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr);
+    u32x2v* const pb = reinterpret_cast<u32x2v*>(cc + (uint64_t)(h + 1) * cstr);
+    if (KBLOCK) {  // a K-block's code bytes fill one contiguous region: streamed
+      __builtin_nontemporal_store(q0, pa);
+      __builtin_nontemporal_store(q1, pb);
+    } else {
+      *pa = q0;
+      *pb = q1;
+    }
     if ((m & 1) == 0) {
       cs[(uint64_t)h * sstr] = (uint8_t)(e0 + 127);
       cs[(uint64_t)(h + 1) * sstr] = (uint8_t)(e1 + 127);
@@ -1046,9 +1090,31 @@ MTB_EXPORT int32_t ep_mxfp4_direct_receive(const uint8_t* packed, int64_t tokens
   if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL(k_mxfp4_receive, dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream, src,
+  hipLaunchKernelGGL(k_mxfp4_receive<false>, dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream, src,
                      (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes, row_scales,
                      col_codes, col_scales);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_mxfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                                  int64_t num_experts, int64_t alignment, int64_t r_cap,
+                                                  const int32_t* offsets, const int32_t* src_row, uint8_t* row_codes,
+                                                  uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                                                  void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (alignment < 32 || alignment % 32 != 0) return EP_ERR_ALIGN;
+  if (!row_codes || !row_scales || !col_codes || !col_scales) return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  // K-blocks over all experts: at most r_cap/256 + E of them
+  const int64_t n_kb = (r_cap + kT2Rows - 1) / kT2Rows + num_experts, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_kb * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL(k_mxfp4_receive<true>, dim3((unsigned)(n_kb * n_ct)), dim3(kT2Threads), 0, (hipStream_t)stream,
+                     src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct, row_codes,
+                     row_scales, col_codes, col_scales);
   return launch_status();
 }
 

@@ -29,6 +29,9 @@ def test_dispatch_bytes_per_configuration():
     assert _mb(b["nvfp4_pack"]) == 301.0
     assert _mb(b["nvfp4_direct_receive"]) == 1124.1
     assert b["nvfp4_direct_receive_kblock"] == b["nvfp4_direct_receive"]   # same bytes, re-placed
+    # MXFP4 receive: rows once in + rowwise and columnwise codes (H/2) and scales (H/32) per grouped row
+    assert b["mxfp4_receive"] == T * (9 * H // 16 + 4) + (T * k + E * 15) * 4 + (E + 1) * 4 + 2 * T * k * (H // 2 + H // 32)
+    assert b["mxfp4_receive_kblock"] == b["mxfp4_receive"]
     # the unpack of the routed rows: packed rows once in, R rows of BF16 out
     assert b["nvfp4_unpack"] == T * (9 * H // 16 + 4) + T * k * 4 + T * k * H * 2
     assert _mb(b["nvfp4_unpack_tokens"]) == 301.0   # one row per token

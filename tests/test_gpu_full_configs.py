@@ -152,6 +152,12 @@ def test_config2_nvfp4_and_mxfp8(dev):
                        "config2 MXFP4 columnwise codes (whole tensor)")
     assert_bytes_equal(host(g4["col_scales"])[: 4096 * off4 // 32], w4["col_scales"][: 4096 * off4 // 32],
                        "config2 MXFP4 columnwise scales (whole tensor)")
+    k4 = mtb.ep_mxfp4_direct_receive(packed, 4096, plan32, kblock=True)
+    wc4, ws4 = orecv.kblock_layout(w4["col_codes"][: 4096 * off4 // 2], w4["col_scales"][: 4096 * off4 // 32],
+                                   w4["offsets"].astype(np.int64), 4096, scale_rows=32)
+    assert_bytes_equal(host(k4["row_codes"])[:off4], w4["row_codes"][:off4], "config2 MXFP4 K-blocked row codes")
+    assert_bytes_equal(host(k4["col_codes"])[: 4096 * off4 // 2], wc4, "config2 MXFP4 K-blocked columnwise codes")
+    assert_bytes_equal(host(k4["col_scales"])[: 4096 * off4 // 32], ws4, "config2 MXFP4 K-blocked columnwise scales")
 
 
 def test_config3_dsv3_share(dev):

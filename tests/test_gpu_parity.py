@@ -507,6 +507,19 @@ def test_direct_receive_kblock_layout(dev, case):
         assert_bytes_equal(host(kb[key])[: off[-1]], host(got[key])[: off[-1]], f"K-block receive {key}")
 
 
+def _check_mxfp4_kblock(packed, h, plan, want, off):
+    """The K-blocked MXFP4 receive: the rowwise operand as the compact one's, the
+    columnwise operand the oracle's re-laid by K-blocks of 32-row scale blocks."""
+    got = mtb.ep_mxfp4_direct_receive(packed, h, plan, kblock=True)
+    assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "mxfp4 K-blocked: rowwise codes")
+    assert_bytes_equal(host(got["row_scales"])[:off], want["row_scales"][:off], "mxfp4 K-blocked: rowwise scales")
+    n = h * off
+    offs = host(plan["offsets"]).astype(np.int64)
+    wc, ws = orecv.kblock_layout(want["col_codes"][: n // 2], want["col_scales"][: n // 32], offs, h, scale_rows=32)
+    assert_bytes_equal(host(got["col_codes"])[: n // 2], wc, "mxfp4 K-blocked columnwise codes")
+    assert_bytes_equal(host(got["col_scales"])[: n // 32], ws, "mxfp4 K-blocked columnwise scales")
+
+
 def _check_mxfp4(got, want, off, h, exact=True):
     assert_bytes_equal(host(got["row_codes"])[:off], want["row_codes"][:off], "mxfp4 rowwise codes")
     assert_bytes_equal(host(got["row_scales"])[:off], want["row_scales"][:off], "mxfp4 rowwise scales")
@@ -527,8 +540,8 @@ def test_receive_slow_blocks_with_padding(dev, h):
     block: the transform of an all-zero column is a pattern of signed zeros set
     by the sign vector, and its codes carry those signs.  Expert 0 holds one
     tiny row (zero in its first half) and padding; expert 1 ordinary rows;
-    expert 2 a tiny row among ordinary ones.  The NVFP4 receive in both layouts
-    and the MXFP4 receive, byte for byte."""
+    expert 2 a tiny row among ordinary ones.  The NVFP4 and MXFP4 receives in
+    both layouts, byte for byte."""
     rng = np.random.default_rng(58 + h)
     tiny = rng.standard_normal((2, h)) * 1e-30
     tiny[0, : h // 2] = 0.0
@@ -555,7 +568,9 @@ def test_receive_slow_blocks_with_padding(dev, h):
     assert_bytes_equal(host(kb["col_codes"])[: n // 2], wc, "K-blocked columnwise codes")
     assert_bytes_equal(host(kb["col_scales"])[: n // 16], ws, "K-blocked columnwise scales")
     g4 = mtb.ep_mxfp4_direct_receive(packed, h, plan)
-    _check_mxfp4(g4, omx4.direct_receive(packed_np, h, topk, 3, 32), int(off[-1]), h)
+    w4 = omx4.direct_receive(packed_np, h, topk, 3, 32)
+    _check_mxfp4(g4, w4, int(off[-1]), h)
+    _check_mxfp4_kblock(packed, h, plan, w4, int(off[-1]))
 
 @pytest.mark.parametrize("case", [
     dict(seed=51, tokens=150, hidden=256, E=5, k=2, A=32, unused=0.05, empty=[3]),
@@ -577,6 +592,7 @@ def test_mxfp4_receive_bit_exact(dev, case):
     got = mtb.ep_mxfp4_direct_receive(packed, h, plan)
     want = omx4.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment)
     _check_mxfp4(got, want, int(host(plan["offsets"])[-1]), h)
+    _check_mxfp4_kblock(packed, h, plan, want, int(host(plan["offsets"])[-1]))
 
 
 def test_mxfp4_receive_edge_rows(dev):
@@ -595,6 +611,7 @@ def test_mxfp4_receive_edge_rows(dev):
     got = mtb.ep_mxfp4_direct_receive(packed, h, plan)
     want = omx4.direct_receive(onv.pack_rows(bits), h, topk, 4, 32)
     _check_mxfp4(got, want, int(host(plan["offsets"])[-1]), h)
+    _check_mxfp4_kblock(packed, h, plan, want, int(host(plan["offsets"])[-1]))
 
 
 @pytest.mark.parametrize("case", [

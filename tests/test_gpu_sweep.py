@@ -1,7 +1,7 @@
 """Seeded sweeps of random small shapes, every output compared with the oracle
 byte for byte.  Dispatch: the pack, the routing plan, the direct receive in
 both columnwise layouts, the unpack of the routed rows and (for 32-row
-alignments) the MXFP4 receive; dSwiGLU: the epilogue and the FC1-gradient
+alignments) the MXFP4 receive in both layouts; dSwiGLU: the epilogue and the FC1-gradient
 operands, with and without a materialized dX; stochastic rounding: the pack in
 each word mapping and rule, and the receive's stochastic columnwise codes.  The shapes are drawn once from
 fixed seeds: ragged token counts, widths from one to many 256-column tiles with
@@ -87,6 +87,13 @@ def test_dispatch_sweep(dev, case):
             assert_bytes_equal(host(g4[key])[:off], w4[key][:off], f"MXFP4 {key}")
         assert_bytes_equal(host(g4["col_codes"])[: n // 2], w4["col_codes"][: n // 2], "MXFP4 columnwise codes")
         assert_bytes_equal(host(g4["col_scales"])[: n // 32], w4["col_scales"][: n // 32], "MXFP4 columnwise scales")
+        k4 = mtb.ep_mxfp4_direct_receive(packed, h, plan, kblock=True)
+        for key in ("row_codes", "row_scales"):
+            assert_bytes_equal(host(k4[key])[:off], w4[key][:off], f"MXFP4 K-blocked {key}")
+        wc4, ws4 = orecv.kblock_layout(w4["col_codes"][: n // 2], w4["col_scales"][: n // 32],
+                                       want_plan["offsets"].astype(np.int64), h, scale_rows=32)
+        assert_bytes_equal(host(k4["col_codes"])[: n // 2], wc4, "MXFP4 K-blocked columnwise codes")
+        assert_bytes_equal(host(k4["col_scales"])[: n // 32], ws4, "MXFP4 K-blocked columnwise scales")
 
 
 def _dswiglu_cases(n=12, seed=20261203):
