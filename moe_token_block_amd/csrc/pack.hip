@@ -4,10 +4,12 @@
 // scale per 16 elements and a power-of-two FP32 token scale t.  MXFP8 (P2,
 // description): E4M3 data with one E8M0 scale per 32 elements.
 //
-// Mapping: one wave64 per row; lane l owns 16-element blocks l, l+64, ...,
-// loaded as two 16-byte vectors, so a block's max needs no cross-lane work and
-// one wave-wide reduction gives the row max.  The whole row stays in VGPRs
-// between the max and the encode (hidden <= 16384: at most 16 blocks/lane).
+// Mapping (H < 4096): one wave64 per row; lane l owns 16-element blocks l,
+// l+64, ..., loaded as two 16-byte vectors, so a block's max needs no
+// cross-lane work and one wave-wide reduction gives the row max.  The whole
+// row stays in VGPRs between the max and the encode.  From H = 4096 on, one
+// 256-thread workgroup per row (k_nvfp4_pack_wg: thread j owns blocks j,
+// j + 256, ...; the row max crosses its four waves through LDS).
 #include <algorithm>
 
 #include "common.h"
