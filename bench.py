@@ -270,13 +270,14 @@ class Path:
             r32 = plan32["r_cap"]
             mx4 = dict(row_codes=torch.empty((r32, H // 2), **u8), row_scales=torch.empty((r32, H // 32), **u8),
                        col_codes=torch.empty(r32 * H // 2, **u8), col_scales=torch.empty(r32 * H // 32, **u8))
+            G32 = int(plan32["offsets"][-1].item())   # grouped rows at the 32-row alignment
             self._add("mxfp4_receive", lambda: m.ep_mxfp4_direct_receive(packed, H, plan32, out=mx4),
-                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive"], in_step=False)
+                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive"], in_step=False, elements=G32 * H)
             mx4k = {nm: torch.empty_like(v) for nm, v in mx4.items()}
             self.outputs.update({f"mx4k.{nm}": v for nm, v in mx4k.items()})
             self._add("mxfp4_receive_kblock",
                       lambda: m.ep_mxfp4_direct_receive(packed, H, plan32, out=mx4k, kblock=True),
-                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive_kblock"], in_step=False)
+                      dispatch_bytes(T, H, k, E, r32, R)["mxfp4_receive_kblock"], in_step=False, elements=G32 * H)
             fused = dict(row_codes=torch.empty((r_cap, H // 2), **u8), row_scales=torch.empty((r_cap, H // 16), **u8),
                          row_t=torch.empty(r_cap, **f32), col_codes=torch.empty(r_cap * H // 2, **u8),
                          col_scales=torch.empty(r_cap * H // 16, **u8), col_scale=torch.empty(E, **f32))
@@ -640,6 +641,11 @@ def emit(out, args):
             f.write(line + "\n")
 
 
+def progress(msg):
+    """One line on stderr as each phase of the run ends (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -655,6 +661,7 @@ def main():
     cpu = None
     if w3 is not None and not args.no_cpu_baseline and args.workload is None:
         cpu = cpu_baseline(w3, args.cpu_sample_tokens)           # on the host, before the GPU is touched
+        progress(f"oracle baseline: {cpu['value']} {cpu['unit']}")
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -669,9 +676,11 @@ def main():
         path = Path(n, dev, w3 if n == 3 else None)
         per = time_calls(path, args.reps, flush)
         kernels[f"cfg{n}"] = config_kernels(n, path, per)
+        progress(f"config {n}: {len(per)} calls timed")
         if n == 3 and args.workload in (None, "cfg3"):
             ms_step, step_per = time_step(path, args.steps, args.warmup)
             head = (path, ms_step, step_per)
+            progress(f"step timed: {ms_step * 1e3:.1f} us")
         elif args.workload is not None:
             calls = path.step_calls()
             ms_step, step_per = time_step(path, args.steps, args.warmup)

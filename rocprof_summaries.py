@@ -30,6 +30,7 @@ import datetime
 import json
 import os
 import subprocess
+import time
 import sys
 import tempfile
 
@@ -46,13 +47,28 @@ GROUPS = (("FETCH_SIZE",), ("WRITE_SIZE",), ("TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_
 
 
 def run(cmd, timeout):
+    """Run cmd, echoing its output line by line as it comes (a long profiled run
+    shows its progress), and return that output."""
     print("+", " ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd="/tmp", timeout=timeout, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                       text=True, env=dict(os.environ, TMPDIR="/tmp"))
-    if r.returncode != 0:
-        print(r.stdout[-4000:])
-        raise SystemExit(f"failed ({r.returncode}): {' '.join(cmd)}")
-    return r.stdout
+    t0 = time.monotonic()
+    p = subprocess.Popen(cmd, cwd="/tmp", stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                         env=dict(os.environ, TMPDIR="/tmp"))
+    lines = []
+    try:
+        for line in p.stdout:
+            lines.append(line)
+            print("  " + line.rstrip()[:300], flush=True)
+            if time.monotonic() - t0 > timeout:
+                raise subprocess.TimeoutExpired(cmd, timeout)
+        p.wait(timeout=max(1.0, timeout - (time.monotonic() - t0)))
+    except subprocess.TimeoutExpired:
+        p.kill()
+        p.wait()
+        raise SystemExit(f"timed out after {timeout} s: {' '.join(cmd)}")
+    out = "".join(lines)
+    if p.returncode != 0:
+        raise SystemExit(f"failed ({p.returncode}): {' '.join(cmd)}")
+    return out
 
 
 def _is_marker(name):
