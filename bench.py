@@ -496,15 +496,26 @@ def cpu_baseline(w, n_tok, n_chunk=CPU_CHUNK_TOKENS):
     for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[v] = "1"                     # inherited by the spawned workers
     ctx = mp.get_context("spawn")
-    with ctx.Pool(1) as pool:
+    # pools are closed and joined, not terminated: the workers then exit on
+    # their own, with no signal (a profiler's signal handler in a terminated
+    # worker has held up the parent's join)
+    pool = ctx.Pool(1)
+    try:
         dt1, b1 = pool.apply(_oracle_worker, ((w.x_bits[:n_tok], w.topk_idx[:n_tok], E, A, H),))
+    finally:
+        pool.close()
+        pool.join()
     ncore = max(1, min(len(os.sched_getaffinity(0)), 16, w.x_bits.shape[0] // n_chunk))
     jobs = [(w.x_bits[i * n_chunk:(i + 1) * n_chunk], w.topk_idx[i * n_chunk:(i + 1) * n_chunk], E, A, H)
             for i in range(ncore)]
     t0 = time.perf_counter()
-    with ctx.Pool(ncore) as pool:
+    pool = ctx.Pool(ncore)
+    try:
         res = pool.map(_oracle_worker, jobs)
-    dtn = time.perf_counter() - t0
+        dtn = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
     bn = sum(r[1] for r in res)
     return {"value": round(bn / dtn / 1e9, 4), "unit": "GB/s", "cores": ncore, "kind": "oracle",
             "sample": f"config 3 ({w.name}): route plan, NVFP4 pack, direct receive (rowwise + RHT columnwise, "
