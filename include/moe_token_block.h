@@ -322,6 +322,21 @@ int32_t ep_mxfp4_direct_receive_kblock(const uint8_t* packed, int64_t tokens, in
                                        const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
                                        uint8_t* col_codes, uint8_t* col_scales, void* stream);
 
+/* A consumer of that K-blocked operand, for checking that its bytes are the
+ * operand layout of gfx950's block-scaled matrix instruction
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 with one E8M0 scale per 32 K
+ * values): no page describes it; it is not a GEMM.  For the K-block whose first
+ * grouped row is block_row (off_e + 256*kb) and whose length is len (a
+ * multiple of 32, at most 256), out[i*16 + j] = sum over its rows k of
+ * A[ha+i][k] * A[hb+j][k], A the block's [hidden, len] operand, computed by
+ * that instruction on the stored bytes (each lane reads 16 contiguous code
+ * bytes and one scale byte).  out: 256 FP32, device.  col_codes and
+ * col_scales must hold the block (hidden*(block_row+len)/2 and /32 bytes).
+ * EP_ERR_SHAPE for hidden not a positive multiple of 64, len or block_row off
+ * the 32-row grid, len > 256, or a 16-column range outside [0, hidden). */
+int32_t ep_mxfp4_kblock_tile(const uint8_t* col_codes, const uint8_t* col_scales, int64_t hidden,
+                             int64_t block_row, int64_t len, int64_t ha, int64_t hb, float* out, void* stream);
+
 /* MXFP8 receive (P2, description and review comments: received data and block
  * scales are returned per expert, grouped, with 128-aligned slots there --
  * here any multiple of 16): grouped row g copies token src_row[g]'s data row

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     ep_abi_version, ep_status_string, ep_nvfp4_packed_row_bytes, ep_route_capacity, ep_rht_sign_mask,
     ep_nvfp4_pack, ep_nvfp4_unpack, ep_mxfp8_pack, ep_route_plan, ep_nvfp4_direct_receive,
     ep_mxfp8_direct_receive, ep_nvfp4_expert_scale, ep_nvfp4_direct_receive_scaled, dswiglu_nvfp4_quant,
-    ep_nvfp4_pack_scatter, ep_nvfp4_columnwise_grouped, ep_nvfp4_direct_receive_kblock, ep_mxfp4_direct_receive,
+    ep_nvfp4_pack_scatter, ep_nvfp4_columnwise_grouped, ep_nvfp4_direct_receive_kblock, ep_mxfp4_direct_receive, ep_mxfp4_kblock_tile,
     ep_nvfp4_direct_receive_sr, ep_receive_workspace_bytes, ep_nvfp4_direct_receive_topk,
     dswiglu_nvfp4_quant_noalloc, EP_NOALLOC_SCRATCH_BYTES, EP_ERR_SCRATCH,
     lib, LIB_PATH, EXPORTS,

@@ -53,6 +53,7 @@ _SIGS = {
     "ep_nvfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp4_direct_receive": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_mxfp4_kblock_tile": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "ep_nvfp4_direct_receive_sr": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -406,6 +407,24 @@ def ep_mxfp4_direct_receive(packed, hidden, plan, out=None, kblock=False):
             _ptr(packed), t, hidden, e, plan.get("alignment", 16), r_cap,
             _ptr(plan["offsets"]), _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _stream(dev)), name)
+    return out
+
+
+def ep_mxfp4_kblock_tile(col_codes, col_scales, hidden, block_row, length, ha, hb, out=None):
+    """One 16 x 16 tile, computed by gfx950's block-scaled matrix instruction on the
+    K-blocked MXFP4 operand as stored: out[i, j] = sum_k A[ha+i, k] A[hb+j, k] over the
+    K-block of grouped rows [block_row, block_row + length)."""
+    dev = _dev(col_codes)
+    _need(col_codes, torch.uint8, "col_codes", dev)
+    _need(col_scales, torch.uint8, "col_scales", dev)
+    if col_codes.numel() < hidden * (block_row + length) // 2 or col_scales.numel() < hidden * (block_row + length) // 32:
+        raise ValueError("ep_mxfp4_kblock_tile: the operand buffers do not hold the K-block")
+    if out is None:
+        out = torch.empty((16, 16), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, "out", dev, numel=256)
+    with torch.cuda.device(dev):
+        _check(lib().ep_mxfp4_kblock_tile(_ptr(col_codes), _ptr(col_scales), hidden, block_row, length, ha, hb,
+                                          _ptr(out), _stream(dev)), "ep_mxfp4_kblock_tile")
     return out
 
 

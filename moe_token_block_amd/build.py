@@ -18,7 +18,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_token_block.so")
-SOURCES = ["abi.hip", "pack.hip", "unpack.hip", "route.hip", "receive.hip", "dswiglu.hip"]
+SOURCES = ["abi.hip", "pack.hip", "unpack.hip", "route.hip", "receive.hip", "dswiglu.hip", "consumer.hip"]
 ARCH = "gfx950"
 
 

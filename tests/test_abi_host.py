@@ -103,6 +103,13 @@ def test_argument_validation_before_launch(lib):
     assert lib.ep_mxfp4_direct_receive(P, 4, 100, 2, 32, 64, P, P, P, P, P, P, N) == -2   # hidden not a multiple of 64
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 32, 64, P, P, P, P, N, P, N) == -1   # col_codes NULL
     assert lib.ep_mxfp4_direct_receive(P, 4, 128, 2, 32, 64, N, P, P, P, P, P, N) == -1   # offsets NULL
+    assert lib.ep_mxfp4_direct_receive_kblock(P, 4, 128, 2, 16, 64, P, P, P, P, P, P, N) == -3  # alignment
+    assert lib.ep_mxfp4_direct_receive_kblock(P, 1 << 24, 64, 2, 32, 64, P, P, P, P, P, P, N) == -8
+    assert lib.ep_mxfp4_kblock_tile(P, P, 128, 0, 256, 0, 16, N, N) == -1                     # out NULL
+    assert lib.ep_mxfp4_kblock_tile(P, P, 128, 0, 288, 0, 16, P, N) == -2                     # len > 256
+    assert lib.ep_mxfp4_kblock_tile(P, P, 128, 16, 256, 0, 16, P, N) == -2                    # block_row off the grid
+    assert lib.ep_mxfp4_kblock_tile(P, P, 128, 0, 48, 0, 16, P, N) == -2                      # len off the grid
+    assert lib.ep_mxfp4_kblock_tile(P, P, 128, 0, 256, 120, 0, P, N) == -2                    # columns past hidden
     assert lib.dswiglu_nvfp4_quant(P, P, 10, 128, P, 2, P, P, P, P, P, P, P, P, P, 4, N) == -7
     # the one-call receive checks both halves before its first launch
     R = (P, P, P, P, P, P, P, P, P, P)   # counts .. col_scale

@@ -572,6 +572,49 @@ def test_receive_slow_blocks_with_padding(dev, h):
     _check_mxfp4(g4, w4, int(off[-1]), h)
     _check_mxfp4_kblock(packed, h, plan, w4, int(off[-1]))
 
+def test_mxfp4_kblock_operand_feeds_the_scaled_matrix_instruction(dev):
+    """The K-blocked MXFP4 operand read as stored by gfx950's block-scaled matrix
+    instruction (ep_mxfp4_kblock_tile: each lane 16 contiguous code bytes and one
+    scale byte, no reshuffle) gives the product of the oracle's operand: 16 x 16
+    tiles of A A^T over a full K-block (256 rows: two 128-value K steps) and over
+    a short last block (a K step with K groups past its end), within the worst
+    case of FP32 accumulation.  A tile that read a wrong byte, nibble or scale would be
+    off by far more than that."""
+    h = 512
+    w = workloads.small_dispatch(59, 900, h, 3, 1, alignment=32)
+    packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
+    plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), 3, 32)
+    got = mtb.ep_mxfp4_direct_receive(packed, h, plan, kblock=True)
+    want = omx4.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, 3, 32)
+    off = want["offsets"].astype(np.int64)
+    tried = 0
+    for e in range(3):
+        o, p = int(off[e]), int(off[e + 1] - off[e])
+        if p == 0:
+            continue
+        codes = F.unpack_nibbles(want["col_codes"][h * o // 2 : h * (o + p) // 2].reshape(h, p // 2))
+        vals = omx4.decode(codes, want["col_scales"][h * o // 32 : h * (o + p) // 32].reshape(h, p // 32))
+        for kb in range((p + 255) // 256):
+            r0, ln = 256 * kb, min(256, p - 256 * kb)
+            blk = vals[:, r0 : r0 + ln]
+            for ha, hb in ((0, 16), (128, 496), (240, 240)):
+                print(f"mfma tile expert {e} K-block {kb} (len {ln}) rows {ha}, {hb}", flush=True)
+                tile = host(mtb.ep_mxfp4_kblock_tile(got["col_codes"], got["col_scales"], h, o + r0, ln, ha, hb))
+                ref = blk[ha : ha + 16] @ blk[hb : hb + 16].T
+                bound = np.abs(blk[ha : ha + 16]) @ np.abs(blk[hb : hb + 16]).T
+                # any summation order of 256 exact products in FP32: at most 255 roundings of 2^-24
+                assert np.all(np.abs(tile.astype(np.float64) - ref) <= 2e-5 * bound + 1e-30), (e, kb, ha, hb)
+                assert np.count_nonzero(ref) > 200
+                # the check is sharp: pairing A's K groups with B's from the next group of
+                # the step (a lane mapping off by one group) misses the bound everywhere
+                perm = np.concatenate([np.roll(np.arange(min(128, ln - c)).reshape(-1, 32), 1, axis=0).ravel() + c
+                                       for c in range(0, ln, 128)])
+                off_by = blk[ha : ha + 16] @ blk[hb : hb + 16][:, perm].T
+                if ln > 32:
+                    assert np.mean(np.abs(off_by - ref) > 2e-5 * bound + 1e-30) > 0.9
+                tried += 1
+    assert tried >= 12
+
 @pytest.mark.parametrize("case", [
     dict(seed=51, tokens=150, hidden=256, E=5, k=2, A=32, unused=0.05, empty=[3]),
     dict(seed=52, tokens=600, hidden=192, E=8, k=2, A=128, unused=0.0, empty=[]),     # a 64-column last tile
