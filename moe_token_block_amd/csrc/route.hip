@@ -54,6 +54,8 @@ __global__ __launch_bounds__(256) void k_route_count(const IDX* __restrict__ idx
     for (int e = lane; e < E; e += 64) hist[(int64_t)w * E + e] = cnt[wl][e];
 }
 
+constexpr int kScanBatch = 16;  // histogram loads in flight per thread in the scan
+
 // One workgroup of 1024 threads.  hist [W, E] -> per-wave starting rank
 // (exclusive prefix over waves), counts, padded offsets, -1 padding rows.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist, int W, int E, int A, int r_cap,
@@ -67,8 +69,17 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
   const bool active = g < G;
   const int wpg = (W + G - 1) / G;
   const int w0 = active ? g * wpg : 0, w1 = active ? min(W, w0 + wpg) : 0;
+  // the thread's run of histogram entries, kScanBatch loads in flight at a
+  // time (one dependent round trip per batch, not per entry); the batch stays
+  // in registers for the rank pass below when the run fits in one
   int32_t local = 0;
-  for (int w = w0; w < w1; ++w) local += hist[(int64_t)w * E + e];
+  int32_t keep[kScanBatch];
+  for (int wb = w0; wb < w1; wb += kScanBatch) {
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) keep[u] = wb + u < w1 ? hist[(int64_t)(wb + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) local += keep[u];
+  }
   if (active) part[g * E + e] = local;
   __syncthreads();
   if (tid < E) {
@@ -84,10 +95,25 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
   __syncthreads();
   if (active) {
     int32_t run = part[g * E + e];
-    for (int w = w0; w < w1; ++w) {
-      int32_t c = hist[(int64_t)w * E + e];
-      hist[(int64_t)w * E + e] = run;
-      run += c;
+    if (w1 - w0 <= kScanBatch) {  // the run is still in registers
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        if (w0 + u < w1) {
+          hist[(int64_t)(w0 + u) * E + e] = run;
+          run += keep[u];
+        }
+    } else {
+      for (int wb = w0; wb < w1; wb += kScanBatch) {
+        int32_t c[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) c[u] = wb + u < w1 ? hist[(int64_t)(wb + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+          if (wb + u < w1) {
+            hist[(int64_t)(wb + u) * E + e] = run;
+            run += c[u];
+          }
+      }
     }
   }
   // inclusive scan of the padded sizes over experts (Hillis-Steele in LDS)
