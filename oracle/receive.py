@@ -97,7 +97,7 @@ def quantize_blocks(y, D, mode, words=None):
     return block_codes(y, s_code, D, mode, words), s_code
 
 
-def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None):
+def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None, sr_mode="element"):
     """One expert's columnwise operand from its grouped rows.
 
     values [count, H]: exact values of the expert's rows (float64), in grouped
@@ -106,7 +106,8 @@ def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None):
     other rows (their codes carry the sign bits of the signed-zero results).
     ``sr`` = (seed, n0): stochastic codes (R24); the element of column h and
     grouped row r (0-based in the expert) has stream position n0 + h * P + r,
-    its index in the expert's [H, P] code matrix plus n0.
+    its index in the expert's [H, P] code matrix plus n0; ``sr_mode`` picks
+    the word of a position as the pack does (R8: "element" or "stream").
     Returns (codes uint8 [H, P/2], scale codes uint8 [H, P/16]).
     """
     values = np.asarray(values, dtype=np.float64)
@@ -119,7 +120,7 @@ def columnwise_operand(values, count, D, mode, padded_rows=None, sr=None):
     words = None
     if sr is not None:
         seed, n0 = sr
-        words = sr_word(np.uint64(n0) + np.arange(h * p, dtype=np.uint64).reshape(h, p // 16, 16), seed)
+        words = sr_word(np.uint64(n0) + np.arange(h * p, dtype=np.uint64).reshape(h, p // 16, 16), seed, sr_mode)
     codes, s_code = quantize_blocks(y, D, mode, words)
     return F.pack_nibbles(codes.reshape(h, p)), s_code
 
@@ -131,10 +132,13 @@ def expert_decode_scale(t_rows):
 
 
 # ------------------------------------------------------------------ the direct receive
-def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None, columnwise=True, sr=None):
+def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None, columnwise=True, sr=None,
+                   sr_mode="element"):
     """R12-R16 (and R24 with ``sr`` = (seed, counter_base): stochastic columnwise
     codes, expert e's element (h, r) at stream position counter_base +
-    H * off_e + h * P_e + r -- the code's index in ``col_codes``, two per byte).
+    H * off_e + h * P_e + r -- the code's index in ``col_codes``, two per byte;
+    ``sr_mode`` "element" or "stream" maps a position to its Philox word as R8
+    does for the pack).
     Returns the routing plan plus the grouped operands.
 
     Rowwise (R13): grouped row g with source token s >= 0 holds the sender's
@@ -176,7 +180,7 @@ def direct_receive(packed, hidden, topk_idx, num_experts, alignment, r_cap=None,
             continue
         p = int(off[e + 1] - off[e])                    # P_e: all padded rows of the slot
         cc, cs = columnwise_operand(exact[rows], c, D[e], "pow2", padded_rows=p,
-                                    sr=None if sr is None else (sr[0], sr[1] + h * int(off[e])))
+                                    sr=None if sr is None else (sr[0], sr[1] + h * int(off[e])), sr_mode=sr_mode)
         col_codes[h * off[e] // 2 : h * off[e + 1] // 2] = cc.reshape(-1)
         col_scales[h * off[e] // 16 : h * off[e + 1] // 16] = cs.reshape(-1)
     out.update(col_codes=col_codes, col_scales=col_scales, col_scale=D)

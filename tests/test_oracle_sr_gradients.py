@@ -14,6 +14,7 @@ stream position its index in the operand's code array.
 """
 
 import numpy as np
+import pytest
 
 import workloads
 from oracle import dswiglu as D
@@ -68,7 +69,7 @@ def test_fc1_rowwise_positions_from_midpoint_inputs():
         assert codes[r, c] & 7 == want, (r, c)
 
 
-def _check_columnwise(codes_bytes, scale_bytes, y_blocks, Dv, mode, seed, base, h, p):
+def _check_columnwise(codes_bytes, scale_bytes, y_blocks, Dv, mode, seed, base, h, p, words="element"):
     """Columnwise [h, p] operand of one expert: each code against the carry rule with
     the word at its index in the code bytes (base = the position of byte 0, nibble 0)."""
     codes = F.unpack_nibbles(codes_bytes.reshape(h, p // 2))       # [h, p]
@@ -83,15 +84,19 @@ def _check_columnwise(codes_bytes, scale_bytes, y_blocks, Dv, mode, seed, base, 
             v = np.float32(abs(y) / c) if c > 0 else np.float32(0)
         if s_val[col, r // 16] == 0:
             v = np.float32(0)
-        want = nvfp4.stochastic_e2m1_index_carry(np.float64(v), sr_word(np.uint64(base + j), seed))
+        want = nvfp4.stochastic_e2m1_index_carry(np.float64(v), sr_word(np.uint64(base + j), seed, words))
         assert codes[col, r] & 7 == want, (col, r)
 
 
-def test_receive_columnwise_positions():
+@pytest.mark.parametrize("words, base", [("element", 1 << 33), ("stream", 1 << 33), ("stream", (1 << 33) + 3)])
+def test_receive_columnwise_positions(words, base):
+    """Both word mappings (R8) at the receive's positions (R24); the stream mapping also
+    with a counter base that is not a multiple of 4, so blocks of four words straddle
+    the 16-row blocks."""
     w = workloads.small_dispatch(3, 40, 64, 3, 2, alignment=16, empty=[1])
     packed = nvfp4.pack_rows(w.x_bits)
-    seed, base = 99, 1 << 33
-    out = receive.direct_receive(packed, 64, w.topk_idx, 3, 16, sr=(seed, base))
+    seed = 99
+    out = receive.direct_receive(packed, 64, w.topk_idx, 3, 16, sr=(seed, base), sr_mode=words)
     rne = receive.direct_receive(packed, 64, w.topk_idx, 3, 16)
     assert np.array_equal(out["col_scales"], rne["col_scales"])
     off, src = out["offsets"].astype(np.int64), out["src_row"].astype(np.int64)
@@ -106,7 +111,10 @@ def test_receive_columnwise_positions():
         y = rht.rht16(rows.T.reshape(64, p // 16, 16))
         _check_columnwise(out["col_codes"][64 * off[e] // 2 : 64 * off[e + 1] // 2],
                           out["col_scales"][64 * off[e] // 16 : 64 * off[e + 1] // 16], y, out["col_scale"][e],
-                          "pow2", seed, base + 64 * int(off[e]), 64, p)
+                          "pow2", seed, base + 64 * int(off[e]), 64, p, words)
+    if words == "stream":   # the mappings give different codes: the parameter is not ignored
+        other = receive.direct_receive(packed, 64, w.topk_idx, 3, 16, sr=(seed, base))
+        assert not np.array_equal(out["col_codes"], other["col_codes"])
 
 
 def test_fc1_columnwise_positions_follow_the_rowwise_operand():
