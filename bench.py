@@ -62,6 +62,7 @@ CALLS = {
     "nvfp4_direct_receive": (("receive.hip",), ["k_nvfp4_receive"]),
     "nvfp4_direct_receive_kblock": (("receive.hip",), ["k_nvfp4_receive (K-blocked columnwise layout)"]),
     "nvfp4_direct_receive_sr": (("receive.hip",), ["k_nvfp4_receive (stochastic columnwise codes)"]),
+    "nvfp4_direct_receive_sr_stream": (("receive.hip",), ["k_nvfp4_receive (stochastic codes, stream words)"]),
     "mxfp4_receive": (("receive.hip",), ["k_mxfp4_receive"]),
     "mxfp4_receive_kblock": (("receive.hip",), ["k_mxfp4_receive (K-blocked columnwise layout)"]),
     "nvfp4_pack_scatter": (("pack.hip",), ["k_nvfp4_pack_wg / k_nvfp4_pack (scatter)", "k_zero_padding"]),
@@ -263,6 +264,9 @@ class Path:
         if n == 4:
             srr = torch.tensor([1234, 1 << 40], dtype=torch.int64, device=dev)
             self._add("nvfp4_direct_receive_sr", lambda: m.ep_nvfp4_direct_receive_sr(packed, H, plan, recv, srr),
+                      b["nvfp4_direct_receive_sr"], in_step=False, elements=G * H)
+            self._add("nvfp4_direct_receive_sr_stream",
+                      lambda: m.ep_nvfp4_direct_receive_sr(packed, H, plan, recv, srr, stream_words=True),
                       b["nvfp4_direct_receive_sr"], in_step=False, elements=G * H)
         if n in (2, 3):
             A32 = max(A, 32)

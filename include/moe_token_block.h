@@ -266,6 +266,17 @@ int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tokens, int64_
                                    uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
                                    const uint64_t* sr_state, void* stream);
 
+/* ep_nvfp4_direct_receive_sr with the word-stream mapping of the pack's
+ * EP_ROUND_SR_STREAM modes: the code at stream position n takes word (n & 3)
+ * of Philox4x32-10 block n >> 2 (same key and positions), four words per
+ * block instead of one.  Arguments, layouts and errors as there. */
+int32_t ep_nvfp4_direct_receive_sr_stream(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                          int64_t num_experts, int64_t r_cap,
+                                          const int32_t* offsets, const int32_t* src_row,
+                                          uint8_t* row_codes, uint8_t* row_scales, float* row_t,
+                                          uint8_t* col_codes, uint8_t* col_scales, const float* col_scale,
+                                          const uint64_t* sr_state, void* stream);
+
 /* The direct receive with the columnwise operand in K-blocks, a layout a
  * grouped GEMM can stream (P1, PR description: the receiver builds the expert
  * GEMM's grouped operand): per expert, the grouped rows are cut into blocks

@@ -55,6 +55,7 @@ _SIGS = {
     "ep_mxfp4_direct_receive_kblock": (_I32, [_P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "ep_mxfp4_kblock_tile": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "ep_nvfp4_direct_receive_sr": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_nvfp4_direct_receive_sr_stream": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_pack_scatter": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -507,20 +508,23 @@ def ep_nvfp4_direct_receive_scaled(packed, hidden, plan, out):
     return out
 
 
-def ep_nvfp4_direct_receive_sr(packed, hidden, plan, out, sr_state):
+def ep_nvfp4_direct_receive_sr(packed, hidden, plan, out, sr_state, stream_words=False):
     """The one-pass receive with stochastic columnwise codes; out["col_scale"] must
-    hold D_e (ep_nvfp4_expert_scale); sr_state: device int64 [seed, counter_base]."""
+    hold D_e (ep_nvfp4_expert_scale); sr_state: device int64 [seed, counter_base];
+    ``stream_words`` takes each position's word from the four-word Philox stream
+    (``ep_nvfp4_direct_receive_sr_stream``) instead of a block per position."""
+    name = "ep_nvfp4_direct_receive_sr_stream" if stream_words else "ep_nvfp4_direct_receive_sr"
     dev = _dev(packed)
-    t = _packed(packed, hidden, dev, "ep_nvfp4_direct_receive_sr")
+    t = _packed(packed, hidden, dev, name)
     e, r_cap = _plan(plan, dev)
     _receive_out(out, r_cap, hidden, e, dev)
     _need(sr_state, torch.int64, "sr_state", dev, numel=2)
     with torch.cuda.device(dev):
-        _check(lib().ep_nvfp4_direct_receive_sr(
+        _check(getattr(lib(), name)(
             _ptr(packed), t, hidden, e, r_cap, _ptr(plan["offsets"]),
             _ptr(plan["src_row"]), _ptr(out["row_codes"]), _ptr(out["row_scales"]), _ptr(out["row_t"]),
             _ptr(out["col_codes"]), _ptr(out["col_scales"]), _ptr(out["col_scale"]), _ptr(sr_state), _stream(dev)),
-            "ep_nvfp4_direct_receive_sr")
+            name)
     return out
 
 

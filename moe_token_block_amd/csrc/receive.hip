@@ -222,13 +222,38 @@ __device__ __forceinline__ void decode_stage1(const uint32_t* cw, const float* c
 
 // Stochastic variant of col_encode: the same quotients, each code drawn by the
 // carry-form converter with the Philox word of its stream position n0 + i.
+// STREAM: word n of the stream is word (n & 3) of Philox block n >> 2, so the
+// 16 positions take four blocks (five when n0 is not a multiple of 4; n0 mod
+// 4 is the counter base's for every lane, so the block changes are uniform).
+template <bool STREAM>
 __device__ __forceinline__ void col_encode_sr(const float* y, const ColQuant& q, uint64_t n0, uint32_t klo,
                                               uint32_t khi, uint32_t& w0, uint32_t& w1) {
   float u[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) u[i] = quot_apply(y[i], q.r_hi, q.r_lo);
-  w0 = sr_codes8(u, n0, klo, khi, q.scale);
-  w1 = sr_codes8(u + 8, n0 + 8, klo, khi, q.scale);
+  if (!STREAM) {
+    w0 = sr_codes8(u, n0, klo, khi, q.scale);
+    w1 = sr_codes8(u + 8, n0 + 8, klo, khi, q.scale);
+    return;
+  }
+  uint32_t rnd[16];
+  uint64_t cur = n0 >> 2;
+  U4 blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, klo, khi);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint64_t n = n0 + i;
+    if ((n >> 2) != cur) {
+      cur = n >> 2;
+      blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, klo, khi);
+    }
+    const uint32_t sel = (uint32_t)n & 3u;
+    rnd[i] = sel == 0 ? blk.x : (sel == 1 ? blk.y : (sel == 2 ? blk.z : blk.w));
+  }
+  uint32_t b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = sr_code_lo(u[2 * j], rnd[2 * j], q.scale) | sr_code_hi(u[2 * j + 1], rnd[2 * j + 1], q.scale);
+  w0 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  w1 = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
 }
 
 // Where the kernel reads a row's codes, scales and t: the packed rows
@@ -274,7 +299,9 @@ struct RowSrc {
 // experts), so a tile's columnwise output is one contiguous region.
 // SR (the compact layout only): stochastic columnwise codes, the code of
 // column h and grouped row g of expert e at stream position counter_base +
-// H*off_e + h*P_e + (g - off_e) -- its index in col_codes, two per byte.
+// H*off_e + h*P_e + (g - off_e) -- its index in col_codes, two per byte;
+// SR = 1 takes each position's word from its own Philox block (element
+// mapping), SR = 2 from the word stream (four words per block).
 constexpr int kT2Rows = 256, kT2Cols = 256, kT2Threads = 256;
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -333,7 +360,7 @@ __device__ __forceinline__ bool kblock_of_tile(int rt, int E, const int* s_offs,
   return true;
 }
 
-template <int SEL, bool SLOW, bool SR>
+template <int SEL, bool SLOW, int SR>
 __device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float* cm, const int* ce, int dexp,
                                                 const RcpEntry* tab, uint64_t n0, uint64_t n_step, uint32_t klo,
                                                 uint32_t khi, uint2& c0, uint2& c1, uint32_t& s0, uint32_t& s1) {
@@ -343,18 +370,18 @@ __device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float*
   rht16_upper(z1);
   const ColQuant q0 = SLOW ? col_block_quant(absmax16(z0), dexp, tab) : col_block_quant_fast(absmax16(z0), dexp, tab);
   const ColQuant q1 = SLOW ? col_block_quant(absmax16(z1), dexp, tab) : col_block_quant_fast(absmax16(z1), dexp, tab);
-  if (!SR) {
+  if (SR == 0) {
     col_encode(z0, q0, c0.x, c0.y);
     col_encode(z1, q1, c1.x, c1.y);
   } else {
-    col_encode_sr(z0, q0, n0, klo, khi, c0.x, c0.y);
-    col_encode_sr(z1, q1, n0 + n_step, klo, khi, c1.x, c1.y);
+    col_encode_sr<SR == 2>(z0, q0, n0, klo, khi, c0.x, c0.y);
+    col_encode_sr<SR == 2>(z1, q1, n0 + n_step, klo, khi, c1.x, c1.y);
   }
   s0 = q0.sc;
   s1 = q1.sc;
 }
 
-template <bool GROUPED, bool KBLOCK, bool SR = false>
+template <bool GROUPED, bool KBLOCK, int SR = 0>
 __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, int T, int H,
                                                               const int32_t* __restrict__ offsets, int E,
                                                               const int32_t* __restrict__ src_row, int r_cap, int n_ct,
@@ -1003,7 +1030,28 @@ MTB_EXPORT int32_t ep_nvfp4_direct_receive_sr(const uint8_t* packed, int64_t tok
   if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
   const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
-  hipLaunchKernelGGL((k_nvfp4_receive<false, false, true>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0,
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false, 1>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0,
+                     (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
+                     row_codes, row_scales, row_t, col_codes, col_scales, col_scale, sr_state);
+  return launch_status();
+}
+
+MTB_EXPORT int32_t ep_nvfp4_direct_receive_sr_stream(const uint8_t* packed, int64_t tokens, int64_t hidden,
+                                                     int64_t num_experts, int64_t r_cap, const int32_t* offsets,
+                                                     const int32_t* src_row, uint8_t* row_codes, uint8_t* row_scales,
+                                                     float* row_t, uint8_t* col_codes, uint8_t* col_scales,
+                                                     const float* col_scale, const uint64_t* sr_state, void* stream) {
+  int32_t st = receive_check(packed, tokens, hidden, num_experts, r_cap, offsets, src_row);
+  if (st != EP_OK) return st;
+  if (!row_codes || !row_scales || !row_t || !col_codes || !col_scales || !col_scale || !sr_state)
+    return EP_ERR_NULL;
+  if (r_cap == 0) return EP_OK;
+  const int H = (int)hidden;
+  const int64_t n_rt = (r_cap + kT2Rows - 1) / kT2Rows, n_ct = (H + kT2Cols - 1) / kT2Cols;
+  if (n_rt * n_ct * kT2Threads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
+  const uint32_t rb = (uint32_t)(9 * H / 16 + 4);
+  const RowSrc src{packed, packed + (H >> 1), packed + (H >> 1) + (H >> 4), rb, rb, rb};
+  hipLaunchKernelGGL((k_nvfp4_receive<false, false, 2>), dim3((unsigned)(n_rt * n_ct)), dim3(kT2Threads), 0,
                      (hipStream_t)stream, src, (int)tokens, H, offsets, (int)num_experts, src_row, (int)r_cap, (int)n_ct,
                      row_codes, row_scales, row_t, col_codes, col_scales, col_scale, sr_state);
   return launch_status();

@@ -662,22 +662,25 @@ def test_mxfp4_receive_edge_rows(dev):
     dict(seed=62, tokens=600, hidden=192, E=8, k=2, A=128, unused=0.0, empty=[]),
     dict(seed=63, tokens=1000, hidden=128, E=1024, k=1, A=16, unused=0.0, empty=[]),
 ])
-def test_direct_receive_sr_bit_exact(dev, case):
-    """Stochastic columnwise codes (R24) equal the oracle's byte for byte; the scales
-    and the rowwise operand equal the deterministic receive's."""
+@pytest.mark.parametrize("words", ["element", "stream"])
+def test_direct_receive_sr_bit_exact(dev, case, words):
+    """Stochastic columnwise codes (R24, with either word mapping of R8) equal the
+    oracle's byte for byte; the scales and the rowwise operand equal the deterministic
+    receive's."""
     w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
                                  alignment=case["A"], unused_frac=case["unused"], empty=case["empty"])
     h = case["hidden"]
     seed, base = 1234 + case["seed"], (1 << 33) + 5
-    print(f"receive SR case {case}", flush=True)
+    print(f"receive SR case {case} words={words}", flush=True)
     packed = mtb.ep_nvfp4_pack(bf16_dev(w.x_bits, dev))
     plan = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, w.alignment)
     ref = mtb.ep_nvfp4_direct_receive(packed, h, plan)
     got = {k: torch.empty_like(v) for k, v in ref.items()}
     got["col_scale"] = ref["col_scale"].clone()
     sr = torch.tensor([seed, base], dtype=torch.int64, device=dev)
-    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, sr)
-    want = orecv.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment, sr=(seed, base))
+    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, sr, stream_words=words == "stream")
+    want = orecv.direct_receive(onv.pack_rows(w.x_bits), h, w.topk_idx, w.num_experts, w.alignment, sr=(seed, base),
+                                sr_mode=words)
     off = int(host(plan["offsets"])[-1])
     n = h * off
     assert_bytes_equal(host(got["col_codes"])[: n // 2], want["col_codes"][: n // 2], "SR columnwise codes")

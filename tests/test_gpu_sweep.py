@@ -153,7 +153,8 @@ def _sr_cases(n=8, seed=20261204):
 @pytest.mark.parametrize("case", _sr_cases(), ids=lambda c: f"s{c['seed']}-t{c['tokens']}-h{c['hidden']}-m{c['mode']}")
 def test_stochastic_sweep(dev, case):
     """The stochastic-rounding pack in a random word mapping and rule, and the
-    receive's stochastic columnwise codes, on random shapes, seeds and counter bases."""
+    receive's stochastic columnwise codes (element words in even cases, stream words in
+    odd ones), on random shapes, seeds and counter bases."""
     print(f"SR sweep case {case}", flush=True)
     w = workloads.small_dispatch(case["seed"], case["tokens"], case["hidden"], case["E"], case["k"],
                                  alignment=case["A"])
@@ -168,9 +169,10 @@ def test_stochastic_sweep(dev, case):
     got = {key: torch.empty_like(v) for key, v in ref.items()}
     got["col_scale"] = ref["col_scale"].clone()
     rs = torch.tensor([case["sr_seed"] ^ 0x5A5A, case["base"] + 17], dtype=torch.int64, device=dev)
-    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, rs)
+    words = "stream" if case["seed"] % 2 else "element"   # both word mappings of the receive's codes
+    mtb.ep_nvfp4_direct_receive_sr(packed, h, plan, got, rs, stream_words=words == "stream")
     want = orecv.direct_receive(want_p, h, w.topk_idx, w.num_experts, w.alignment,
-                                sr=(case["sr_seed"] ^ 0x5A5A, case["base"] + 17))
+                                sr=(case["sr_seed"] ^ 0x5A5A, case["base"] + 17), sr_mode=words)
     off = int(host(plan["offsets"])[-1])
     n = h * off
     assert_bytes_equal(host(got["col_codes"])[: n // 2], want["col_codes"][: n // 2], "SR columnwise codes")
