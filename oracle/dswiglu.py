@@ -65,7 +65,7 @@ def expert_amax(dx_bits, counts):
     return out
 
 
-def rowwise_quant(dx_bits, counts, amax, sr=None):
+def rowwise_quant(dx_bits, counts, amax, sr=None, sr_mode="element"):
     """R19: per-expert rowwise NVFP4 operand of the FC1 gradient.
 
     D_row,e = fl32(amax_e / 2688).  Per 16-element block of a row of expert e:
@@ -73,7 +73,8 @@ def rowwise_quant(dx_bits, counts, amax, sr=None):
     v = fl32(|x| / c); index = E2M1 rounding (R2).  D = 0 or s_b = 0 gives
     index 0.  With ``sr`` = (seed, counter_base) the index is the carry-form
     stochastic rounding of v (R24): element (row, col) at stream position
-    counter_base + row * 2F + col, its index in the [T, 2F] code array.
+    counter_base + row * 2F + col, its index in the [T, 2F] code array, its
+    word taken as R8's ``sr_mode`` ("element" or "stream") says.
     Returns (codes uint8 [T, F] packed, scale codes [T, 2F/16], D_row float32 [E]).
     """
     x = F.bf16_to_f32(dx_bits)
@@ -91,14 +92,14 @@ def rowwise_quant(dx_bits, counts, amax, sr=None):
         if sr is not None:
             pos = np.uint64(sr[1]) + (np.arange(r0, r1, dtype=np.uint64)[:, None] * np.uint64(h)
                                       + np.arange(h, dtype=np.uint64)[None, :])
-            words = sr_word(pos.reshape(r1 - r0, h // 16, 16), sr[0])
+            words = sr_word(pos.reshape(r1 - r0, h // 16, 16), sr[0], sr_mode)
         c, s = quantize_blocks(blk, D[e], "fp32", words)
         codes[r0:r1] = c.reshape(r1 - r0, h)
         scales[r0:r1] = s
     return F.pack_nibbles(codes), scales, D
 
 
-def columnwise_quant(dx_bits, counts, amax, exact_amax=False, sr=None):
+def columnwise_quant(dx_bits, counts, amax, exact_amax=False, sr=None, sr_mode="element"):
     """R20 (and R21 with ``exact_amax``): per-expert RHT columnwise operand.
 
     D_col,e = fl32(4 * amax_e / 2688) -- the bound from P4 -- or, for the
@@ -129,18 +130,19 @@ def columnwise_quant(dx_bits, counts, amax, exact_amax=False, sr=None):
         else:
             D[e] = (np.float32(4.0) * np.float32(amax[e])) / np.float32(TOKEN_SCALE_BOUND)
         cc, cs = columnwise_operand(x[off[e] : off[e + 1]], c, D[e], "fp32",
-                                    sr=None if sr is None else (sr[0], sr[1] + h * int(poff[e])))
+                                    sr=None if sr is None else (sr[0], sr[1] + h * int(poff[e])), sr_mode=sr_mode)
         codes[h * poff[e] // 2 : h * poff[e + 1] // 2] = cc.reshape(-1)
         scales[h * poff[e] // 16 : h * poff[e + 1] // 16] = cs.reshape(-1)
     return codes, scales, D
 
 
-def fc1_grad_quant(dx_bits, counts, amax, sr=None):
+def fc1_grad_quant(dx_bits, counts, amax, sr=None, sr_mode="element"):
     """The fused path after the epilogue: rowwise (R19) and columnwise (R20) operands;
     ``sr`` = (seed, counter_base) makes both stochastic (R24), the columnwise
-    operand's positions following the rowwise operand's T * 2F."""
+    operand's positions following the rowwise operand's T * 2F; ``sr_mode`` picks
+    each position's Philox word as R8 does ("element" or "stream")."""
     t, h = np.asarray(dx_bits).shape
-    rc, rs, drow = rowwise_quant(dx_bits, counts, amax, sr)
+    rc, rs, drow = rowwise_quant(dx_bits, counts, amax, sr, sr_mode)
     cc, cs, dcol = columnwise_quant(dx_bits, counts, amax,
-                                    sr=None if sr is None else (sr[0], sr[1] + t * h))
+                                    sr=None if sr is None else (sr[0], sr[1] + t * h), sr_mode=sr_mode)
     return dict(row_codes=rc, row_scales=rs, row_scale=drow, col_codes=cc, col_scales=cs, col_scale=dcol)

@@ -44,7 +44,8 @@ def test_words_at_the_limits_give_floor_and_ceiling():
     assert np.array_equal(down & 7, lo) and np.array_equal(up & 7, hi)
 
 
-def test_fc1_rowwise_positions_from_midpoint_inputs():
+@pytest.mark.parametrize("words, base", [("element", 12345), ("stream", 12345), ("stream", 12346)])
+def test_fc1_rowwise_positions_from_midpoint_inputs(words, base):
     # amax 2688 -> D_row = 1 exactly; each 16-block holds 2688 (s = 448, c = 448) and
     # values 448 * m with m an E2M1 midpoint, so v = m exactly and frac = 1/2
     rng = np.random.default_rng(2)
@@ -53,10 +54,10 @@ def test_fc1_rowwise_positions_from_midpoint_inputs():
     vals[:, ::16] = 2688.0
     bits = F.f32_to_bf16(vals.astype(np.float32))
     counts = np.array([10, 0, 14])
-    seed, base = 77, 12345
+    seed = 77
     amax = D.expert_amax(bits, counts)
     assert np.all(amax[counts > 0] == 2688.0)
-    rc, rs, drow = D.rowwise_quant(bits, counts, amax, sr=(seed, base))
+    rc, rs, drow = D.rowwise_quant(bits, counts, amax, sr=(seed, base), sr_mode=words)
     codes = F.unpack_nibbles(rc)                                     # [t, h]
     lo, hi = _grid_floor_ceil(np.abs(vals) / 448.0)
     for j in range(rc.size * 2):                                     # flat code index = byte * 2 + nibble
@@ -64,7 +65,7 @@ def test_fc1_rowwise_positions_from_midpoint_inputs():
         if c % 16 == 0:
             assert codes[r, c] & 7 == 7
             continue
-        w = int(sr_word(np.uint64(base + j), seed))
+        w = int(sr_word(np.uint64(base + j), seed, words))
         want = hi[r, c] if w >= (1 << 31) else lo[r, c]
         assert codes[r, c] & 7 == want, (r, c)
 
@@ -117,13 +118,14 @@ def test_receive_columnwise_positions(words, base):
         assert not np.array_equal(out["col_codes"], other["col_codes"])
 
 
-def test_fc1_columnwise_positions_follow_the_rowwise_operand():
+@pytest.mark.parametrize("words, base", [("element", 1000), ("stream", 1000), ("stream", 1001)])
+def test_fc1_columnwise_positions_follow_the_rowwise_operand(words, base):
     w = workloads.small_dswiglu(4, [7, 0, 20], 32)
     dx = D.dswiglu(w.preact_bits, w.dy_bits)
     t, h = dx.shape
     amax = D.expert_amax(dx, w.counts)
-    seed, base = 5, 1000
-    q = D.fc1_grad_quant(dx, w.counts, amax, sr=(seed, base))
+    seed = 5
+    q = D.fc1_grad_quant(dx, w.counts, amax, sr=(seed, base), sr_mode=words)
     q_rne = D.fc1_grad_quant(dx, w.counts, amax)
     assert np.array_equal(q["row_scales"], q_rne["row_scales"]) and np.array_equal(q["col_scales"], q_rne["col_scales"])
     x = F.bf16_to_f32(dx).astype(np.float64)
@@ -139,7 +141,7 @@ def test_fc1_columnwise_positions_follow_the_rowwise_operand():
         y = rht.rht16(full.T.reshape(h, p // 16, 16))
         _check_columnwise(q["col_codes"][h * poff[e] // 2 : h * poff[e + 1] // 2],
                           q["col_scales"][h * poff[e] // 16 : h * poff[e + 1] // 16], y, q["col_scale"][e],
-                          "fp32", seed, base + t * h + h * int(poff[e]), h, p)
+                          "fp32", seed, base + t * h + h * int(poff[e]), h, p, words)
 
 
 def test_stochastic_codes_are_unbiased():
