@@ -75,6 +75,8 @@ CALLS = {
                                                     "k_fc1_quant (recompute)"]),
     "dswiglu_nvfp4_quant_sr": (("dswiglu.hip",), ["k_dswiglu_epilogue", "k_dswiglu_reduce",
                                                   "k_fc1_quant (stochastic codes)"]),
+    "dswiglu_nvfp4_quant_sr_stream": (("dswiglu.hip",), ["k_dswiglu_epilogue", "k_dswiglu_reduce",
+                                                         "k_fc1_quant (stochastic codes, stream words)"]),
 }
 VALU_BOUND = ("nvfp4_pack_sr", "nvfp4_pack_sr_stream")
 SR_ELEMENT_CARRY, SR_STREAM_CARRY = 3, 4      # EP_ROUND_SR_ELEMENT_CARRY, EP_ROUND_SR_STREAM_CARRY
@@ -197,6 +199,11 @@ class Path:
                       kernel_bytes=dswiglu_kernel_bytes(T, F, E, dx=False))
             self._add("dswiglu_nvfp4_quant_sr",
                       lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws, sr_state=sr),
+                      dswiglu_bytes(T, F, E, sr=True), in_step=False, elements=T * 2 * F,
+                      kernel_bytes=dswiglu_kernel_bytes(T, F, E))
+            self._add("dswiglu_nvfp4_quant_sr_stream",
+                      lambda: m.dswiglu_nvfp4_quant(pre, dy, counts, out=out, workspace=ws, sr_state=sr,
+                                                    stream_words=True),
                       dswiglu_bytes(T, F, E, sr=True), in_step=False, elements=T * 2 * F,
                       kernel_bytes=dswiglu_kernel_bytes(T, F, E))
             self.desc = dict(workload=w.name, tokens=T, ffn=F, experts=E)

@@ -438,6 +438,18 @@ int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t* dy, int64
                                uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                void* workspace, size_t workspace_bytes, const uint64_t* sr_state, void* stream);
 
+/* dswiglu_nvfp4_quant_sr with the word-stream mapping of the pack's
+ * EP_ROUND_SR_STREAM modes: the code at stream position n takes word (n & 3)
+ * of Philox4x32-10 block n >> 2 (same key and positions).  Arguments, layouts
+ * and errors as there. */
+int32_t dswiglu_nvfp4_quant_sr_stream(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
+                                      const int32_t* counts, int64_t num_experts,
+                                      uint16_t* dx, float* amax,
+                                      uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
+                                      uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
+                                      void* workspace, size_t workspace_bytes, const uint64_t* sr_state,
+                                      void* stream);
+
 /* dswiglu_nvfp4_quant without the workspace argument, for callers that cannot
  * allocate (code under HIP graph capture, serving loops that forbid
  * hipMalloc).  The workspace lives in a static device array of

@@ -60,6 +60,8 @@ _SIGS = {
     "ep_nvfp4_columnwise_grouped": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "dswiglu_nvfp4_quant": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dswiglu_nvfp4_quant_sr": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "dswiglu_nvfp4_quant_sr_stream": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P,
+                                             _P]),
     "dswiglu_nvfp4_quant_noalloc": (_I32, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -599,12 +601,14 @@ def dswiglu_nvfp4_quant_noalloc(preact, dy, counts, out, materialize_dx=True):
     return out
 
 
-def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None):
+def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materialize_dx=True, sr_state=None,
+                        stream_words=False):
     """Grouped dSwiGLU epilogue + FC1-gradient NVFP4 operands; rows expert-major,
     ``counts`` a device int32 [E] tensor.  Returns a dict of output tensors.
     ``materialize_dx=False``: no BF16 dX is written (out["dx"] is None); the
     quantizer recomputes dX from preact and dy.  ``sr_state`` (device int64
-    [seed, counter_base]): stochastic FC1-gradient codes."""
+    [seed, counter_base]): stochastic FC1-gradient codes, each position's Philox
+    word its own block's or, with ``stream_words``, from the four-word stream."""
     dev, t, e, out, args = _dswiglu_args(preact, dy, counts, out, materialize_dx)
     wsb = lib().dswiglu_workspace_bytes(t, e)
     if workspace is None:
@@ -614,7 +618,8 @@ def dswiglu_nvfp4_quant(preact, dy, counts, out=None, workspace=None, materializ
         args = args + (_ptr(workspace), workspace.numel())
         if sr_state is not None:
             _need(sr_state, torch.int64, "sr_state", dev, numel=2)
-            _check(lib().dswiglu_nvfp4_quant_sr(*args, _ptr(sr_state), _stream(dev)), "dswiglu_nvfp4_quant_sr")
+            name = "dswiglu_nvfp4_quant_sr_stream" if stream_words else "dswiglu_nvfp4_quant_sr"
+            _check(getattr(lib(), name)(*args, _ptr(sr_state), _stream(dev)), name)
             return out
         _check(lib().dswiglu_nvfp4_quant(*args, _stream(dev)), "dswiglu_nvfp4_quant")
     return out

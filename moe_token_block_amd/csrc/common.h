@@ -217,6 +217,37 @@ __device__ __forceinline__ uint32_t sr_codes8(const float* u, uint64_t n0, uint3
   return w;
 }
 
+// sr_codes8 with the word-stream mapping: the word of position n is word
+// (n & 3) of Philox block n >> 2, so 8 positions take two blocks (three when
+// n0 is not a multiple of 4; callers' n0 mod 4 is the counter base's in every
+// lane, so the block changes are uniform across the wave).
+__device__ __forceinline__ uint32_t sr_codes8_stream(const float* u, uint64_t n0, uint32_t klo, uint32_t khi,
+                                                     float scale) {
+  uint64_t cur = n0 >> 2;
+  U4 blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, klo, khi);
+  auto word = [&](uint64_t n) -> uint32_t {
+    if ((n >> 2) != cur) {
+      cur = n >> 2;
+      blk = philox4x32_10((uint32_t)cur, (uint32_t)(cur >> 32), 0u, 0u, klo, khi);
+    }
+    const uint32_t sel = (uint32_t)n & 3u;
+    return sel == 0 ? blk.x : (sel == 1 ? blk.y : (sel == 2 ? blk.z : blk.w));
+  };
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // each pair's codes as soon as its two words exist
+    const uint32_t wa = word(n0 + 2 * j), wb = word(n0 + 2 * j + 1);
+    w |= (sr_code_lo(u[2 * j], wa, scale) | sr_code_hi(u[2 * j + 1], wb, scale)) << (8 * j);
+  }
+  return w;
+}
+
+// The stochastic codes of 8 positions with the element (SRM 1) or stream (SRM 2) words.
+template <int SRM>
+__device__ __forceinline__ uint32_t sr_codes8_m(const float* u, uint64_t n0, uint32_t klo, uint32_t khi, float scale) {
+  return SRM == 2 ? sr_codes8_stream(u, n0, klo, khi, scale) : sr_codes8(u, n0, klo, khi, scale);
+}
+
 // ----------------------------------------------------------------- reductions
 // The value of the neighbouring lane (lane ^ 1), by a DPP quad permutation
 // [1, 0, 3, 2] inside the VALU instead of an LDS permute.

@@ -355,7 +355,7 @@ __device__ __forceinline__ int qstage_at(int c, int b) { return c * kQBlocks + (
 // SR: stochastic codes, element (row0 + i, xcol + k) at stream position
 // n0 + i * W + k (n0 = the counter base + row0 * W + xcol: its index in the
 // [T, W] code array).
-template <bool SR = false, bool FAST = false>
+template <int SR = 0, bool FAST = false>
 __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, float Drow, const MantEntry* tab,
                                             uint8_t* cbase, uint32_t coff, uint8_t* sbase, uint32_t soff, uint32_t W,
                                             bool even, uint64_t n0 = 0, uint32_t klo = 0, uint32_t khi = 0) {
@@ -382,7 +382,7 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
         u[2 * k] = quot_apply(bf16lo(wv[k]), gb.r_hi, gb.r_lo);
         u[2 * k + 1] = quot_apply(bf16hi(wv[k]), gb.r_hi, gb.r_lo);
       }
-      w = sr_codes8(u, n0 + (uint64_t)i * W, klo, khi, gb.scale);
+      w = sr_codes8_m<SR>(u, n0 + (uint64_t)i * W, klo, khi, gb.scale);
     }
     *reinterpret_cast<uint32_t*>(cbase + (coff + (uint32_t)i * (W >> 1))) = w;
     if (even) sbase[soff + (uint32_t)i * (W >> 4)] = (uint8_t)sc;
@@ -396,7 +396,7 @@ __device__ __forceinline__ void fc1_rowwise(const uint4 (&v)[16], int nreal, flo
 // SR: stochastic codes, the block's row 0 in the thread's column k at stream
 // position n0 + k * n_step (its index in the columnwise code array plus the
 // counter base).
-template <int P0, int P1, bool SR = false, bool FAST = false, typename ScT>
+template <int P0, int P1, int SR = 0, bool FAST = false, typename ScT>
 __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol, const MantEntry* tab, int cg, int m,
                                                uint2* stage_codes, ScT* stage_sc, uint64_t n0 = 0,
                                                uint64_t n_step = 0, uint32_t klo = 0, uint32_t khi = 0) {
@@ -452,10 +452,10 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
         u1[i] = quot_apply(z1[i], g1.r_hi, g1.r_lo);
       }
       const uint64_t na = n0 + (uint64_t)(2 * p) * n_step, nb = na + n_step;
-      c00 = sr_codes8(u0, na, klo, khi, g0.scale);
-      c01 = sr_codes8(u0 + 8, na + 8, klo, khi, g0.scale);
-      c10 = sr_codes8(u1, nb, klo, khi, g1.scale);
-      c11 = sr_codes8(u1 + 8, nb + 8, klo, khi, g1.scale);
+      c00 = sr_codes8_m<SR>(u0, na, klo, khi, g0.scale);
+      c01 = sr_codes8_m<SR>(u0 + 8, na + 8, klo, khi, g0.scale);
+      c10 = sr_codes8_m<SR>(u1, nb, klo, khi, g1.scale);
+      c11 = sr_codes8_m<SR>(u1 + 8, nb + 8, klo, khi, g1.scale);
     }
     const int c0 = cg * 8 + 2 * p;
     stage_codes[qstage_at(c0, m)] = make_uint2(c00, c01);
@@ -479,9 +479,14 @@ __device__ __forceinline__ void fc1_columnwise(const uint4 (&v)[16], float Dcol,
 // arithmetic (so the values, and the amax already taken from them, agree bit
 // for bit).
 // SR: stochastic codes (rowwise at counter base + row * W + col, columnwise at
-// counter base + T * W + the code's index in the columnwise code array).
-template <bool RECOMPUTE, bool SR = false>
-__global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
+// counter base + T * W + the code's index in the columnwise code array), each
+// position's word its own Philox block's (SR = 1) or from the four-word stream
+// (SR = 2).
+// At most 168 VGPRs (three waves per SIMD): the other forms stay below that,
+// the stream-word form would take 170 and two waves (slower by 20%); capped, it
+// keeps three waves with a few bytes of spill.
+template <bool RECOMPUTE, int SR = 0>
+__global__ __launch_bounds__(kQThreads, 3) void k_fc1_quant(const uint16_t* __restrict__ dx, const uint16_t* __restrict__ preact,
                                                    const uint16_t* __restrict__ dy, int T, int W /* 2F */, int E,
                                                    int n_ct, const int32_t* __restrict__ offs,
                                                    const int32_t* __restrict__ poffs,
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
       // the thread's 8 columns are contiguous in dX (also in the recompute mapping)
       const uint64_t h0 = (uint64_t)qtile_col<RECOMPUTE>(col0, 8 * cg, W);
       const uint64_t n0 = n_base + (uint64_t)(uint32_t)T * (uint32_t)W + 2 * (s_cbase[m] + h0 * s_cstr[m]);
-      fc1_columnwise<0, 4, true>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc, n0,
+      fc1_columnwise<0, 4, SR>(v, s_dcol[m], s_tab[m][1], cg, m, stage_codes, stage_sc, n0,
                                  2 * (uint64_t)s_cstr[m], klo, khi);
     }
   }
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(kQThreads) void k_fc1_quant(const uint16_t* __restr
     const uint32_t rso = rrel * (uint32_t)(W >> 4) + (uint32_t)(xcol >> 4);
     const uint64_t rn0 = n_base + (uint64_t)(uint32_t)s_row0[m] * (uint32_t)W + (uint32_t)xcol;
     if (!SR && s_drow[m] >= 0x1p-85f)
-      fc1_rowwise<false, true>(v, s_nreal[m], s_drow[m], s_tab[m][0], rcb, rco, rsb, rso, (uint32_t)W, (cg & 1) == 0);
+      fc1_rowwise<0, true>(v, s_nreal[m], s_drow[m], s_tab[m][0], rcb, rco, rsb, rso, (uint32_t)W, (cg & 1) == 0);
     else
       fc1_rowwise<SR>(v, s_nreal[m], s_drow[m], s_tab[m][0], rcb, rco, rsb, rso, (uint32_t)W, (cg & 1) == 0, rn0, klo,
                       khi);
@@ -709,7 +714,7 @@ static int32_t dswiglu_quant_impl(const uint16_t* preact, const uint16_t* dy, in
                                        uint8_t* row_codes, uint8_t* row_scales, float* row_scale,
                                        uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                        void* workspace, size_t workspace_bytes,
-                                       const uint64_t* sr_state, void* stream) {
+                                       const uint64_t* sr_state, int sr_words, void* stream) {
   if (tokens < 0 || ffn <= 0 || ffn % 64 != 0 || num_experts < 1 || num_experts > 1024) return EP_ERR_SHAPE;
   if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
@@ -744,18 +749,21 @@ static int32_t dswiglu_quant_impl(const uint16_t* preact, const uint16_t* dy, in
   const int64_t n_rt = (prow_bound + kQTileRows - 1) / kQTileRows, n_ct = (2 * F + kQTileCols - 1) / kQTileCols;
   if (n_rt * n_ct * kQThreads >= ((int64_t)1 << 32)) return EP_ERR_RANGE;  // one 1-D grid
   const dim3 grid((unsigned)(n_rt * n_ct)), block(kQThreads);
-  if (dx && !sr_state)
-    hipLaunchKernelGGL((k_fc1_quant<false, false>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
-                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
-  else if (!sr_state)
-    hipLaunchKernelGGL((k_fc1_quant<true, false>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
-                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
-  else if (dx)
-    hipLaunchKernelGGL((k_fc1_quant<false, true>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
-                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
-  else
-    hipLaunchKernelGGL((k_fc1_quant<true, true>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs,
-                       poffs, row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state);
+#define MTB_FC1(RC, SRM)                                                                                        \
+  hipLaunchKernelGGL((k_fc1_quant<RC, SRM>), grid, block, 0, s, dx, preact, dy, T, 2 * F, E, (int)n_ct, offs, poffs, \
+                     row_scale, col_scale, row_codes, row_scales, col_codes, col_scales, sr_state)
+  const int srm = sr_state ? (sr_words == 2 ? 2 : 1) : 0;
+  if (srm == 0) {
+    if (dx) MTB_FC1(false, 0);
+    else MTB_FC1(true, 0);
+  } else if (srm == 1) {
+    if (dx) MTB_FC1(false, 1);
+    else MTB_FC1(true, 1);
+  } else {
+    if (dx) MTB_FC1(false, 2);
+    else MTB_FC1(true, 2);
+  }
+#undef MTB_FC1
   return launch_status();
 }
 
@@ -765,7 +773,7 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant(const uint16_t* preact, const uint16_t* d
                                        uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
-                            col_codes, col_scales, col_scale, workspace, workspace_bytes, nullptr, stream);
+                            col_codes, col_scales, col_scale, workspace, workspace_bytes, nullptr, 0, stream);
 }
 
 MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t* dy, int64_t tokens, int64_t ffn,
@@ -776,7 +784,18 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr(const uint16_t* preact, const uint16_t
                                           void* stream) {
   if (!sr_state) return EP_ERR_NULL;
   return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
-                            col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, stream);
+                            col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, 1, stream);
+}
+
+MTB_EXPORT int32_t dswiglu_nvfp4_quant_sr_stream(const uint16_t* preact, const uint16_t* dy, int64_t tokens,
+                                                 int64_t ffn, const int32_t* counts, int64_t num_experts, uint16_t* dx,
+                                                 float* amax, uint8_t* row_codes, uint8_t* row_scales,
+                                                 float* row_scale, uint8_t* col_codes, uint8_t* col_scales,
+                                                 float* col_scale, void* workspace, size_t workspace_bytes,
+                                                 const uint64_t* sr_state, void* stream) {
+  if (!sr_state) return EP_ERR_NULL;
+  return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
+                            col_codes, col_scales, col_scale, workspace, workspace_bytes, sr_state, 2, stream);
 }
 
 // ------------------------------------------------------------------ allocation-free variant
@@ -828,5 +847,5 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant_noalloc(const uint16_t* preact, const uin
   const int32_t st = scratch_ptr(&ws);
   if (st != EP_OK) return st;
   return dswiglu_quant_impl(preact, dy, tokens, ffn, counts, num_experts, dx, amax, row_codes, row_scales, row_scale,
-                            col_codes, col_scales, col_scale, ws, kScratchBytes, nullptr, stream);
+                            col_codes, col_scales, col_scale, ws, kScratchBytes, nullptr, 0, stream);
 }

@@ -793,19 +793,22 @@ def test_dswiglu_counts_cut_at_tokens(dev, dev_counts, rows):
                    host(out["col_scales"])[: q["col_scales"].size], q["col_scales"], "cut columnwise")
 
 
+@pytest.mark.parametrize("words", ["element", "stream"])
 @pytest.mark.parametrize("counts,ffn", [([0, 17, 64, 1, 0, 33], 64), ([300, 0, 129], 256), ([40, 24, 19, 8], 128)])
-def test_dswiglu_sr_bit_exact(dev, counts, ffn):
-    """Stochastic FC1-gradient codes (R24) equal the oracle's on the GPU's own dX and
-    amax byte for byte, with and without a materialized dX; scales as the RNE call's."""
+def test_dswiglu_sr_bit_exact(dev, counts, ffn, words):
+    """Stochastic FC1-gradient codes (R24, with either word mapping of R8) equal the
+    oracle's on the GPU's own dX and amax byte for byte, with and without a
+    materialized dX; scales as the RNE call's."""
     w = workloads.small_dswiglu(sum(counts) + 3 * ffn, counts, ffn)
-    print(f"dswiglu SR counts={counts} ffn={ffn}", flush=True)
+    print(f"dswiglu SR counts={counts} ffn={ffn} words={words}", flush=True)
     args = (bf16_dev(w.preact_bits, dev), bf16_dev(w.dy_bits, dev), i32_dev(w.counts, dev))
     seed, base = 777, (1 << 32) + 3
     sr = torch.tensor([seed, base], dtype=torch.int64, device=dev)
-    got = mtb.dswiglu_nvfp4_quant(*args, sr_state=sr)
-    got_nodx = mtb.dswiglu_nvfp4_quant(*args, materialize_dx=False, sr_state=sr)
+    sw = words == "stream"
+    got = mtb.dswiglu_nvfp4_quant(*args, sr_state=sr, stream_words=sw)
+    got_nodx = mtb.dswiglu_nvfp4_quant(*args, materialize_dx=False, sr_state=sr, stream_words=sw)
     ref = mtb.dswiglu_nvfp4_quant(*args)
-    q = odsw.fc1_grad_quant(host(got["dx"]), w.counts, host(got["amax"]), sr=(seed, base))
+    q = odsw.fc1_grad_quant(host(got["dx"]), w.counts, host(got["amax"]), sr=(seed, base), sr_mode=words)
     t = sum(counts)
     n = 2 * ffn * sum((c + 15) // 16 * 16 for c in counts)
     assert_bytes_equal(host(got["row_codes"]), q["row_codes"], "SR rowwise codes")
