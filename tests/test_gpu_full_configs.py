@@ -218,6 +218,27 @@ def test_config3_dsv3_share(dev):
                        f"config3 K-blocked codes of expert {e} (whole, oracle)")
     assert_bytes_equal(ks[H * int(off_all[e]) // 16: H * int(off_all[e + 1]) // 16], wcs,
                        f"config3 K-blocked scales of expert {e} (whole, oracle)")
+    # the MXFP4 receive (32-row alignment) in both layouts at this size: expert e's
+    # rowwise rows and whole columnwise operand against the oracle's for that expert
+    print("config3: MXFP4 receive", flush=True)
+    plan32 = mtb.ep_route_plan(torch.from_numpy(w.topk_idx).to(dev), w.num_experts, 32)
+    off32, src32 = host(plan32["offsets"]).astype(np.int64), host(plan32["src_row"]).astype(np.int64)
+    o32, p32 = int(off32[e]), int(off32[e + 1] - off32[e])
+    assert np.array_equal(src32[o32: o32 + c], erows)       # the same tokens, in the same order
+    vals = onv.decode_exact(ep, H)
+    mc, ms = omx4.columnwise_operand(vals, c, p32)
+    rc4, rs4 = omx4.quantize(vals)
+    mkc, mks = orecv.kblock_layout(mc.reshape(-1), ms.reshape(-1), np.array([0, p32]), H, scale_rows=32)
+    for kblock in (False, True):
+        g4 = mtb.ep_mxfp4_direct_receive(packed, H, plan32, kblock=kblock)
+        tag = "K-blocked" if kblock else "compact"
+        assert_bytes_equal(host(g4["row_codes"][o32: o32 + c]), F.pack_nibbles(rc4), f"config3 MXFP4 {tag} row codes")
+        assert_bytes_equal(host(g4["row_scales"][o32: o32 + c]), rs4, f"config3 MXFP4 {tag} row scales")
+        gc4 = host(g4["col_codes"][H * o32 // 2: H * (o32 + p32) // 2])
+        gs4 = host(g4["col_scales"][H * o32 // 32: H * (o32 + p32) // 32])
+        assert_bytes_equal(gc4, mkc if kblock else mc.reshape(-1), f"config3 MXFP4 {tag} columnwise codes of expert {e}")
+        assert_bytes_equal(gs4, mks if kblock else ms.reshape(-1), f"config3 MXFP4 {tag} columnwise scales of expert {e}")
+        del g4
     # unpack of the received rows (grouped order) on sampled rows
     off = int(want["offsets"][-1])
     src = want["src_row"][:off]
