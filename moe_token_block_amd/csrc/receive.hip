@@ -93,11 +93,11 @@ __global__ __launch_bounds__(1024) void k_expert_scale_grouped(const float* __re
 // (and the NaN code) hold zeros, which quantize every value to a signed zero.
 struct RcpEntry {
   float r_hi, r_lo;
-  int k, pad;
+  int k;
 };
 
 __device__ __forceinline__ RcpEntry rcp_entry(int c) {
-  RcpEntry r{0.0f, 0.0f, 0, 0};
+  RcpEntry r{0.0f, 0.0f, 0};
   float s = e4m3_decode((uint32_t)c);
   if (c != 0 && c < 0x7F) {
     QuotSplit q = quot_split(s);
@@ -391,13 +391,19 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
                                                               uint8_t* __restrict__ col_scales,
                                                               const float* __restrict__ col_scale,
                                                               const uint64_t* __restrict__ sr_state) {
-  __shared__ int s_offs[1025];
-  __shared__ int s_edexp[1024];        // decode exponent of each expert's D_e
+  // The tile's code bytes (256 rows x 128 bytes; row r's 16-byte piece q at
+  // position q ^ ((r >> 4) & 7), so that the column phase's 8-byte reads of
+  // sixteen rows 16 apart fall on different banks).  Until the tile's loads
+  // return, the same bytes hold the expert offsets and the K-block scan.
+  // 40 KB in all, so that four workgroups share a CU's 160 KB.
+  __shared__ __align__(16) uint8_t s_code[kT2Rows * 128];
   __shared__ RcpEntry s_tab[128];
   __shared__ float s_t[kT2Rows];
   __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 scale bytes of each row
   __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-88
   __shared__ __align__(16) int s_src[kT2Rows];  // source row of each grouped row (-1: none)
+  int* const s_offs = reinterpret_cast<int*>(s_code);  // offsets[0..E]
+  int* const s_kbstart = s_offs + 1028;                 // K-block starts (E + 1), then one sum per wave
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -407,59 +413,52 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   const int col0 = ct * kT2Cols;
   const int ncols = min(kT2Cols, H - col0);  // 64, 128, 192 or 256
   int g_base = rt * kT2Rows;
-  int kb = 0, tile_rows = kT2Rows;
-  if (KBLOCK) {
-    __shared__ int s_kbstart[1025];
-    __shared__ int s_wsum[kT2Threads / 64];
-    for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
-    __syncthreads();
-    int ex;
-    if (!kblock_of_tile(rt, E, s_offs, s_kbstart, s_wsum, ex, kb, g_base, tile_rows)) return;
-  }
+  int kb = 0, tile_rows = kT2Rows, e = 0;
+  for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+  __syncthreads();
+  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, s_kbstart, s_kbstart + 1028, e, kb, g_base, tile_rows)) return;
 
   const int lane = tid & 63, w = tid >> 6;
   const int m = lane >> 2;                    // 16-row block of the column phase
   const int cg = 4 * w + (lane & 3);          // 16-column group of the column phase
   const int gb = g_base + 16 * m;
   const bool col_live = 16 * cg < ncols;
-  const int cgc = col_live ? cg : 0;          // clamped: a dead group re-reads group 0
 
-  // this thread's own source-row index (issued first), then the expert offsets
-  // (already there in the K-blocked layout), decode exponents and the reciprocal
-  // table into LDS
+  // this thread's own source-row index (issued first); the column block's
+  // expert (the tile's in the K-blocked layout, else the last expert whose
+  // offset is <= gb: empty experts share offsets), its offset, length and
+  // decode scale; the reciprocal table into LDS.  Every read of s_offs comes
+  // before the barrier that precedes the first write of the tile's code bytes.
   const int g = g_base + tid;
   int srcv = g;
   if (!GROUPED) srcv = src_row[(uint32_t)min(g, r_cap - 1)];
-  for (int i = tid; i <= E; i += kT2Threads) {
-    if (!KBLOCK) s_offs[i] = offsets[i];
-    if (i < E) s_edexp[i] = pow2_exponent(col_scale[i]);
+  if (!KBLOCK) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
   }
+  const float d_e = col_scale[e];
+  const int off = s_offs[e], len = s_offs[e + 1] - off;
+  const int off_end_g = s_offs[E];
   if (tid < 128) s_tab[tid] = rcp_entry(tid);
 
   // The loads, in two rounds: each thread's own source-row index (into LDS, so
-  // that the row copy and the column blocks read theirs from there), then every
-  // byte load -- the row-copy pieces (16 bytes of rows (tid >> 3) + 32 i), the
-  // 16 code gathers of its column block, its row's t and the tile's scale bytes.
-  // The byte loads are buffer loads over the source rows: a row that is padding,
-  // an unused slot, past r_cap or out of range gets an offset beyond the
-  // resource, and the hardware's range check returns zeros for it -- no selects,
-  // and no access at all when T = 0.  The copy's pieces are the same bytes as the
-  // gathers', so the L2 merges their misses.
+  // that the row pieces read theirs from there), then every byte load -- the
+  // row pieces (16 bytes of rows (tid >> 3) + 32 i: the tile's whole 32 KB of
+  // codes, which both the rowwise copy and the columnwise blocks use), its
+  // row's t and the tile's scale bytes.  The byte loads are buffer loads over
+  // the source rows: a row that is padding, an unused slot, past r_cap or out
+  // of range gets an offset beyond the resource, and the hardware's range
+  // check returns zeros for it -- no selects, and no access at all when T = 0.
   const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces per row: 2, 4, 6 or 8
   s_src[tid] = g < r_cap ? srcv : -1;
   __syncthreads();
-  const int off_end_g = s_offs[E];
-  int rsrc[8], sl[16];
+  int rsrc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) rsrc[i] = s_src[(tid >> 3) + 32 * i];
-  {
-    const int4* sp = reinterpret_cast<const int4*>(s_src + 16 * m);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int4 v = sp[q];
-      sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
-    }
-  }
   const int src = s_src[tid];
   // resources of the T source rows (sizes < 2^31: checked at launch)
   const uint32_t nT = (uint32_t)max(T, 0);
@@ -474,19 +473,11 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
     return (uint32_t)s < nT ? __umul24((uint32_t)s, stride) + add : kNoRow;
   };
   u32x4v cv[8];
-  if (!GROUPED) {
+  {
+    // dead pieces of a narrow tile re-read piece 0 (their bytes are never used)
     const uint32_t qa = (uint32_t)(col0 >> 1) + 16u * (uint32_t)(cq < nq ? cq : 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) cv[i] = __builtin_amdgcn_raw_buffer_load_b128(r_codes, row_at(rsrc[i], rs.cstride, qa), 0, 0);
-  }
-  uint2 cw2[16];
-  {
-    const uint32_t ca = (uint32_t)(col0 >> 1) + 8u * (uint32_t)cgc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x2v w = __builtin_amdgcn_raw_buffer_load_b64(r_codes, row_at(sl[i], rs.cstride, ca), 0, 0);
-      cw2[i] = make_uint2(w.x, w.y);
-    }
   }
   const float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_t, row_at(src, rs.tstride, 0u), 0, 0));
   uint4 sw;
@@ -511,10 +502,16 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
     const uint64_t tiny = __ballot(t < 0x1p-88f && t > 0.0f);
     if ((tid & 63) < 4) s_tiny[4 * (tid >> 6) + (tid & 3)] = ((tiny >> (16 * (tid & 3))) & 0xFFFFu) != 0;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    *reinterpret_cast<u32x4v*>(s_code + 128 * r + ((cq ^ ((r >> 4) & 7)) << 4)) = cv[i];
+  }
   if (!GROUPED) {
     // rowwise operand: 16-byte pieces, eight threads per row's 128 code bytes
     // (whole lines when H is a multiple of 256), streamed past the caches --
-    // nothing in the path reads them again; the row's scale bytes and t
+    // nothing in the path reads them again; the row's scale bytes (one 16-byte
+    // piece when H is a multiple of 256) and t
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int gr = g_base + (tid >> 3) + 32 * i;
@@ -524,28 +521,22 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
     }
     if (g < tile_end) {
       uint32_t* rsc = reinterpret_cast<uint32_t*>(row_scales + (size_t)(uint32_t)g * (uint32_t)(H >> 4) + (col0 >> 4));
-      rsc[0] = sw.x;
-      if (ncols > 64) rsc[1] = sw.y;
-      if (ncols > 128) rsc[2] = sw.z;
-      if (ncols > 192) rsc[3] = sw.w;
+      if ((H & 255) == 0) {
+        *reinterpret_cast<uint4*>(rsc) = sw;
+      } else {
+        rsc[0] = sw.x;
+        if (ncols > 64) rsc[1] = sw.y;
+        if (ncols > 128) rsc[2] = sw.z;
+        if (ncols > 192) rsc[3] = sw.w;
+      }
       if (ct == 0) row_t[g] = t;
     }
   }
   __syncthreads();
   if (!col_live || gb >= tile_end) return;
 
-  // the block's expert, decode exponent and output bases
-  int e = 0;
-  {
-    int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-  }
-  const int off = s_offs[e], len = s_offs[e + 1] - off;
-  const int dexp = s_edexp[e];
+  // the block's decode exponent and output bases
+  const int dexp = pow2_exponent(d_e);
   uint64_t cbase, sbase;
   uint32_t cstr, sstr;
   if (KBLOCK) {
@@ -580,11 +571,16 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
     tv[i] = s_t[16 * m + i];
     sb[i] = swd[4 * i] >> sh;
   }
+  // the block's code bytes: 8 bytes (16 columns) of each of its 16 rows
   uint32_t wx[16], wy[16];
+  {
+    const uint8_t* cb = s_code + 128 * (16 * m) + ((((cg >> 1) ^ (m & 7)) << 4) + 8 * (cg & 1));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    wx[i] = cw2[i].x;
-    wy[i] = cw2[i].y;
+    for (int i = 0; i < 16; ++i) {
+      const uint2 v = *reinterpret_cast<const uint2*>(cb + 128 * i);
+      wx[i] = v.x;
+      wy[i] = v.y;
+    }
   }
   uint8_t* cc = col_codes + cbase;
   uint8_t* cs = col_scales + sbase;
