@@ -268,26 +268,31 @@ struct RowSrc {
 
 // ------------------------------------------------------------------ one-pass receive, 256 x 256 tiles
 // One workgroup per 256 grouped rows x 256 columns (four waves):
-//   * the rowwise operand: thread t moves 16-byte pieces of rows (t >> 3) +
-//     32 i, so eight threads write one row's 128 code bytes -- whole lines when
-//     H is a multiple of 256, streamed past the caches (nothing in the path
-//     reads them again) -- and row t's scale bytes and token scale;
+//   * the tile's 32 KB of code bytes: thread t loads 16-byte pieces of rows
+//     (t >> 3) + 32 i (eight threads per row's 128 bytes), keeps them for the
+//     rowwise copy and writes them to LDS for the columnwise blocks;
+//   * the rowwise operand: those pieces stored unchanged -- whole lines when H
+//     is a multiple of 256, streamed past the caches (nothing in the path
+//     reads them again) -- and row t's scale bytes (one 16-byte store) and t;
 //   * the columnwise operand: wave w owns the 16-column groups cg = 4w .. 4w+3
-//     of all sixteen 16-row blocks; lane (m, j) = (lane >> 2, lane & 3)
-//     gathers the 8 code bytes of column group 4w + j of the 16 rows of block
-//     m (16 rows x 32 contiguous bytes per load instruction), decodes them,
-//     runs the RHT and quantizes its 16 columns in registers, and stores each
-//     column's 8 code bytes and scale byte straight to the operand: the sixteen
-//     blocks of a column sit in one wave, so every store instruction writes
-//     four columns' 128 contiguous code bytes each.  In the K-blocked layout a
-//     K-block's columnwise output is one contiguous, line-aligned region, and
-//     its code bytes are streamed too.
+//     of all sixteen 16-row blocks; lane (m, j) = (lane >> 2, lane & 3) reads
+//     the 8 code bytes of column group 4w + j of the 16 rows of block m from
+//     LDS, decodes them, runs the RHT and quantizes its 16 columns in
+//     registers, and stores each column's 8 code bytes and scale byte
+//     straight to the operand: the sixteen blocks of a column sit in one wave,
+//     so every store instruction writes four columns' 128 contiguous code
+//     bytes each.  In the K-blocked layout a K-block's columnwise output is
+//     one contiguous, line-aligned region, and its code bytes are streamed too.
+// Every byte of the tile is fetched once, by a 16-byte load: reading the
+// columnwise blocks' bytes from global memory instead (sixteen 8-byte loads
+// per lane, each instruction touching sixteen rows' lines) costs the memory
+// pipeline about as many cycles as all the rest of the tile's loads together.
 // Loads come in two rounds: each thread's source-row index (shared through
-// LDS), then every byte load at once -- the row copy's pieces and the column
-// gathers (the same bytes: the L2 merges their misses), t and the scale bytes
+// LDS), then every byte load at once -- the row pieces, t and the scale bytes
 // -- as range-checked buffer loads that read zeros for rows without a source.
-// The copy is stored before the tile's second barrier, which hands row t's
-// token scale and the tile's 16 scale bytes to the decode through LDS.
+// The copy is stored before the tile's second barrier, which hands the code
+// bytes, row t's token scale and the tile's 16 scale bytes to the decode
+// through LDS.
 // 1-D grid of row_tiles * col_tiles workgroups.  Workgroup i runs on XCD
 // i % 8, so the logical tile is taken from a contiguous range per XCD, column
 // tile fastest: the column tiles of a row tile run on one XCD at about the
