@@ -712,11 +712,15 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
                                                               uint8_t* __restrict__ row_scales,
                                                               uint8_t* __restrict__ col_codes,
                                                               uint8_t* __restrict__ col_scales) {
-  __shared__ int s_offs[1025];
+  // the tile's code bytes (the NVFP4 receive's swizzled layout), the expert
+  // offsets and the K-block scan until the loads return
+  __shared__ __align__(16) uint8_t s_code[kT2Rows * 128];
   __shared__ float s_t[kT2Rows];
   __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 NVFP4 scale bytes of each row
   __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-100
   __shared__ __align__(16) int s_src[kT2Rows];
+  int* const s_offs = reinterpret_cast<int*>(s_code);
+  int* const s_kbstart = s_offs + 1028;
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -726,41 +730,42 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   const int col0 = ct * kT2Cols;
   const int ncols = min(kT2Cols, H - col0);  // 64, 128, 192 or 256
   int g_base = rt * kT2Rows, kb = 0, tile_rows = kT2Rows, kex = 0;
-  if (KBLOCK) {
-    __shared__ int s_kbstart[1025];
-    __shared__ int s_wsum[kT2Threads / 64];
-    for (int i = threadIdx.x; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
-    __syncthreads();
-    if (!kblock_of_tile(rt, E, s_offs, s_kbstart, s_wsum, kex, kb, g_base, tile_rows)) return;
-  }
+  for (int i = threadIdx.x; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+  __syncthreads();
+  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, s_kbstart, s_kbstart + 1028, kex, kb, g_base, tile_rows)) return;
 
   const int lane = tid & 63, w = tid >> 6;
   const int m = lane >> 2;                    // 16-row block of the column phase
   const int cg = 4 * w + (lane & 3);          // 16-column group of the column phase
   const int gb = g_base + 16 * m;
   const bool col_live = 16 * cg < ncols;
-  const int cgc = col_live ? cg : 0;          // clamped: a dead group re-reads group 0
 
   const int g = g_base + tid;
   const int srcv = src_row[(uint32_t)min(g, r_cap - 1)];
-  if (!KBLOCK)
-    for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
+  // the column block's expert offset and length (the tile's expert in the
+  // K-blocked layout), read before the barrier that precedes the code bytes'
+  // writes into the same LDS
+  int off, len;
+  if (KBLOCK) {
+    off = s_offs[kex];
+    len = s_offs[kex + 1] - off;
+  } else {
+    int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
+    }
+    off = s_offs[lo];
+    len = s_offs[lo + 1] - off;
+  }
+  const int off_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
   const int cq = tid & 7, nq = ncols >> 5;  // 16-byte pieces (32 columns) per row: 2, 4, 6 or 8
   s_src[tid] = g < r_cap ? srcv : -1;
   __syncthreads();
-  const int off_end = min(s_offs[E], r_cap & ~31);  // whole 32-row blocks inside the outputs
   const int tile_end = KBLOCK ? min(g_base + tile_rows, off_end) : off_end;  // rows this tile writes
-  int rsrc[8], sl[16];
+  int rsrc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) rsrc[i] = s_src[(tid >> 3) + 32 * i];
-  {
-    const int4* sp = reinterpret_cast<const int4*>(s_src + 16 * m);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int4 v = sp[q];
-      sl[4 * q] = v.x; sl[4 * q + 1] = v.y; sl[4 * q + 2] = v.z; sl[4 * q + 3] = v.w;
-    }
-  }
   const int src = s_src[tid];
   const uint32_t nT = (uint32_t)max(T, 0);
   const __amdgpu_buffer_rsrc_t r_codes = __builtin_amdgcn_make_buffer_rsrc(
@@ -778,16 +783,6 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) cv[i] = __builtin_amdgcn_raw_buffer_load_b128(r_codes, row_at(rsrc[i], rs.cstride, qa), 0, 0);
   }
-  uint32_t wx[16], wy[16];
-  {
-    const uint32_t ca = (uint32_t)(col0 >> 1) + 8u * (uint32_t)cgc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r_codes, row_at(sl[i], rs.cstride, ca), 0, 0);
-      wx[i] = v.x;
-      wy[i] = v.y;
-    }
-  }
   const float t = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_t, row_at(src, rs.tstride, 0u), 0, 0));
   uint4 sw;
   {
@@ -800,6 +795,11 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   {
     const uint64_t tiny = __ballot(t < 0x1p-100f && t > 0.0f);  // a block with a tiny t: two-step decode
     if (lane < 4) s_tiny[4 * w + lane] = ((tiny >> (16 * lane)) & 0xFFFFu) != 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    *reinterpret_cast<u32x4v*>(s_code + 128 * r + ((cq ^ ((r >> 4) & 7)) << 4)) = cv[i];
   }
   __syncthreads();
 
@@ -844,18 +844,11 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   uint8_t* cs;
   uint32_t cstr, sstr;
   if (KBLOCK) {
-    const int off = s_offs[kex];
     cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint64_t)H * 128u * (uint32_t)kb + 8u * (uint32_t)m;
     cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint64_t)H * 8u * (uint32_t)kb + (uint32_t)(m >> 1);
     cstr = (uint32_t)(tile_rows >> 1);
     sstr = (uint32_t)(tile_rows >> 5);
   } else {
-    int lo = 0, hi = E - 1;  // last expert with offsets[e] <= gb (empty experts share offsets)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_offs[mid] <= gb) lo = mid; else hi = mid - 1;
-    }
-    const int off = s_offs[lo], len = s_offs[lo + 1] - off;
     cc = col_codes + (uint64_t)H * (uint32_t)(off >> 1) + (uint32_t)((gb - off) >> 1);
     cs = col_scales + (uint64_t)H * (uint32_t)(off >> 5) + (uint32_t)((gb - off) >> 5);
     cstr = (uint32_t)(len >> 1);
@@ -874,6 +867,16 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   for (int i = 0; i < 16; ++i) {
     tv[i] = s_t[16 * m + i];
     sb[i] = swd[4 * i] >> sh;
+  }
+  uint32_t wx[16], wy[16];  // 8 code bytes (16 columns) of each of the block's 16 rows
+  {
+    const uint8_t* cb = s_code + 128 * (16 * m) + ((((cg >> 1) ^ (m & 7)) << 4) + 8 * (cg & 1));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint2 v = *reinterpret_cast<const uint2*>(cb + 128 * i);
+      wx[i] = v.x;
+      wy[i] = v.y;
+    }
   }
   // one column pair: decode + RHT, the 32-row block max with block m ^ 1 (lane
   // ^ 4), codes and scale bytes
