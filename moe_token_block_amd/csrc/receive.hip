@@ -590,6 +590,12 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   uint8_t* cc = col_codes + cbase;
   uint8_t* cs = col_scales + sbase;
   // the K-blocked layout: a K-block's code bytes fill one contiguous region, streamed
+  // A whole K-block's scale bytes: column h's sixteen at 16 h, so the wave's 64
+  // columns fill one contiguous KB.  They are transposed through the wave's own
+  // dword of each row of s_sw (wave w reads only dword w, and has read it) and
+  // leave as one 16-byte store per lane instead of sixteen byte stores.
+  const bool stage_sc = KBLOCK && tile_rows == kT2Rows && g_base + kT2Rows <= tile_end;  // uniform
+  uint8_t* const s_scw = reinterpret_cast<uint8_t*>(s_sw) + 4 * w;  // byte b < 4 of row r: s_scw[16 r + b]
   auto store = [&](int c, uint2 a, uint2 b, uint32_t sa, uint32_t sb2) {
     const uint32_t h = (uint32_t)(h0 + c);
     u32x2v* pa = reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr);
@@ -601,8 +607,21 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       *pa = u32x2v{a.x, a.y};
       *pb = u32x2v{b.x, b.y};
     }
-    cs[(uint64_t)h * sstr] = (uint8_t)sa;
-    cs[(uint64_t)(h + 1) * sstr] = (uint8_t)sb2;
+    if (stage_sc) {
+      // the wave's column l = 16 j + c, block m: row 4 l + m / 4, byte m % 4
+      const int l = 16 * (lane & 3) + c;
+      s_scw[16 * (4 * l + (m >> 2)) + (m & 3)] = (uint8_t)sa;
+      s_scw[16 * (4 * (l + 1) + (m >> 2)) + (m & 3)] = (uint8_t)sb2;
+    } else {
+      cs[(uint64_t)h * sstr] = (uint8_t)sa;
+      cs[(uint64_t)(h + 1) * sstr] = (uint8_t)sb2;
+    }
+  };
+  auto store_scales = [&]() {
+    if (!stage_sc) return;
+    const uint32_t* rd = reinterpret_cast<const uint32_t*>(s_scw + 64 * lane);  // rows 4 lane .. 4 lane + 3
+    const uint4 v = make_uint4(rd[0], rd[4], rd[8], rd[12]);
+    *reinterpret_cast<uint4*>(cs - m + 16u * (uint32_t)(col0 + 64 * w + lane)) = v;
   };
   if (!slow) {
 #pragma unroll
@@ -634,6 +653,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       store(2 * p, a, b, sa, sbb);
     });
   }
+  store_scales();
 }
 
 // ------------------------------------------------------------------ MXFP4 receive
