@@ -128,11 +128,11 @@ __device__ __forceinline__ void encode_rne(const uint4& v0, const uint4& v1, con
     u[2 * i] = quot_apply(bf16lo(w[i]), q.r_hi, q.r_lo);
     u[2 * i + 1] = quot_apply(bf16hi(w[i]), q.r_hi, q.r_lo);
   }
-  o0 = fp4_pack2<0>(0u, u[0], u[1], q.scale);
+  o0 = fp4_pack2<0>(__float_as_uint(u[0]), u[0], u[1], q.scale);  // the other bytes: overwritten next
   o0 = fp4_pack2<1>(o0, u[2], u[3], q.scale);
   o0 = fp4_pack2<2>(o0, u[4], u[5], q.scale);
   o0 = fp4_pack2<3>(o0, u[6], u[7], q.scale);
-  o1 = fp4_pack2<0>(0u, u[8], u[9], q.scale);
+  o1 = fp4_pack2<0>(__float_as_uint(u[8]), u[8], u[9], q.scale);
   o1 = fp4_pack2<1>(o1, u[10], u[11], q.scale);
   o1 = fp4_pack2<2>(o1, u[12], u[13], q.scale);
   o1 = fp4_pack2<3>(o1, u[14], u[15], q.scale);
@@ -187,11 +187,11 @@ __device__ __forceinline__ void encode_sr(const uint4& v0, const uint4& v1, cons
     g[2 * i + 1] = sr_round(quot_apply(bf16hi(w[i]), q.r_hi, q.r_lo), q.kexp, rnd[2 * i + 1] >> 8);
   }
   // g holds exact grid values with x's sign: encode with scale 1
-  o0 = fp4_pack2<0>(0u, g[0], g[1], 1.0f);
+  o0 = fp4_pack2<0>(__float_as_uint(g[0]), g[0], g[1], 1.0f);  // the other bytes: overwritten next
   o0 = fp4_pack2<1>(o0, g[2], g[3], 1.0f);
   o0 = fp4_pack2<2>(o0, g[4], g[5], 1.0f);
   o0 = fp4_pack2<3>(o0, g[6], g[7], 1.0f);
-  o1 = fp4_pack2<0>(0u, g[8], g[9], 1.0f);
+  o1 = fp4_pack2<0>(__float_as_uint(g[8]), g[8], g[9], 1.0f);
   o1 = fp4_pack2<1>(o1, g[10], g[11], 1.0f);
   o1 = fp4_pack2<2>(o1, g[12], g[13], 1.0f);
   o1 = fp4_pack2<3>(o1, g[14], g[15], 1.0f);

@@ -123,7 +123,7 @@ __device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp, const 
   float y = __builtin_ldexpf(div6(a), -dexp - (tiny ? 64 : 0));
   ColQuant q;
   q.sc = e4m3_encode(fminf(y, 448.0f));
-  RcpEntry r = tab[q.sc & 0x7F];
+  RcpEntry r = tab[q.sc];  // a value in [0, 448]: code <= 0x7E
   // quotient by s * D = m * 2^K; for K < -104 the quotient is first scaled
   // up by 2^P (exact) so that the power handed to the converter stays normal
   int K = r.k + dexp;
@@ -144,7 +144,7 @@ __device__ __forceinline__ ColQuant col_block_quant_fast(float amax, int dexp, c
   const float y = __builtin_ldexpf(div6(amax), -dexp);
   ColQuant q;
   q.sc = e4m3_encode(fminf(y, 448.0f));
-  const RcpEntry r = tab[q.sc & 0x7F];
+  const RcpEntry r = tab[q.sc];  // a value in [0, 448]: code <= 0x7E
   q.r_hi = r.r_hi;
   q.r_lo = r.r_lo;
   q.scale = q.sc ? pow2f(r.k + dexp) : 1.0f;
@@ -156,11 +156,13 @@ __device__ __forceinline__ void col_encode(const float* y, const ColQuant& q, ui
   float u[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) u[i] = quot_apply(y[i], q.r_hi, q.r_lo);
-  w0 = fp4_pack2<0>(0u, u[0], u[1], q.scale);
+  // (each word's first conversion keeps three bytes of its `old` operand that
+  // the next three overwrite: any register will do)
+  w0 = fp4_pack2<0>(__float_as_uint(u[0]), u[0], u[1], q.scale);
   w0 = fp4_pack2<1>(w0, u[2], u[3], q.scale);
   w0 = fp4_pack2<2>(w0, u[4], u[5], q.scale);
   w0 = fp4_pack2<3>(w0, u[6], u[7], q.scale);
-  w1 = fp4_pack2<0>(0u, u[8], u[9], q.scale);
+  w1 = fp4_pack2<0>(__float_as_uint(u[8]), u[8], u[9], q.scale);
   w1 = fp4_pack2<1>(w1, u[10], u[11], q.scale);
   w1 = fp4_pack2<2>(w1, u[12], u[13], q.scale);
   w1 = fp4_pack2<3>(w1, u[14], u[15], q.scale);
@@ -589,6 +591,13 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   }
   uint8_t* cc = col_codes + cbase;
   uint8_t* cs = col_scales + sbase;
+  uint8_t* kb_codes = col_codes;
+  uint32_t kb_co = 0;
+  if (KBLOCK) {
+    const int off_u = __builtin_amdgcn_readfirstlane(off), kb_u = __builtin_amdgcn_readfirstlane(kb);
+    kb_codes = col_codes + (uint64_t)H * (uint32_t)(off_u >> 1) + (uint64_t)H * 128u * (uint32_t)kb_u;
+    kb_co = 8u * (uint32_t)m + (uint32_t)h0 * cstr;
+  }
   // the K-blocked layout: a K-block's code bytes fill one contiguous region, streamed
   // A whole K-block's scale bytes: column h's sixteen at 16 h, so the wave's 64
   // columns fill one contiguous KB.  They are transposed through the wave's own
@@ -598,8 +607,10 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   uint8_t* const s_scw = reinterpret_cast<uint8_t*>(s_sw) + 4 * w;  // byte b < 4 of row r: s_scw[16 r + b]
   auto store = [&](int c, uint2 a, uint2 b, uint32_t sa, uint32_t sb2) {
     const uint32_t h = (uint32_t)(h0 + c);
-    u32x2v* pa = reinterpret_cast<u32x2v*>(cc + (uint64_t)h * cstr);
-    u32x2v* pb = reinterpret_cast<u32x2v*>(cc + (uint64_t)(h + 1) * cstr);
+    // a K-block's region is H * 128 bytes: 32-bit offsets from its (uniform) base
+    u32x2v* pa = reinterpret_cast<u32x2v*>(KBLOCK ? kb_codes + (kb_co + (uint32_t)c * cstr) : cc + (uint64_t)h * cstr);
+    u32x2v* pb = reinterpret_cast<u32x2v*>(KBLOCK ? kb_codes + (kb_co + (uint32_t)(c + 1) * cstr)
+                                                  : cc + (uint64_t)(h + 1) * cstr);
     if (KBLOCK) {
       __builtin_nontemporal_store(u32x2v{a.x, a.y}, pa);
       __builtin_nontemporal_store(u32x2v{b.x, b.y}, pb);
