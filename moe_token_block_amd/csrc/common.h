@@ -113,11 +113,12 @@ __device__ __forceinline__ float quot_apply(float x, float r_hi, float r_lo) {
 
 // fl32(a / 6) for a >= 0 in float32's normal range: a / 1.5 with the split
 // reciprocal of 1.5 (2/3 = R_HI + R_LO to ~2^-48), then an exact * 0.25.
-__device__ __forceinline__ float div6(float a) {
+__device__ __forceinline__ float div1_5(float a) {
   const float R_HI = 0.666666686534881591796875f;        // RN(2/3)
   const float R_LO = -1.98682149251302083333e-08f;       // RN(2/3 - R_HI)
-  return __builtin_fmaf(a, R_HI, a * R_LO) * 0.25f;
+  return __builtin_fmaf(a, R_HI, a * R_LO);
 }
+__device__ __forceinline__ float div6(float a) { return div1_5(a) * 0.25f; }
 
 // ----------------------------------------------------------------- E2M1
 // Four E2M1 codes of u0..u3 / 2^k packed as the two bytes of a 16-bit result

@@ -89,21 +89,21 @@ __global__ __launch_bounds__(1024) void k_expert_scale_grouped(const float* __re
 }
 
 // Reciprocal split of every E4M3 block-scale code (see quot_split): entry c
-// holds r_hi, r_lo of the significand of s = E4M3(c) and s's exponent; code 0
-// (and the NaN code) hold zeros, which quantize every value to a signed zero.
+// holds r_hi, r_lo of the significand of s = E4M3(c) and 2^k, s's power of
+// two; code 0 (and the NaN code) hold zeros and 2^0, which quantize every
+// value to a signed zero.
 struct RcpEntry {
-  float r_hi, r_lo;
-  int k;
+  float r_hi, r_lo, p2k;
 };
 
 __device__ __forceinline__ RcpEntry rcp_entry(int c) {
-  RcpEntry r{0.0f, 0.0f, 0};
+  RcpEntry r{0.0f, 0.0f, 1.0f};
   float s = e4m3_decode((uint32_t)c);
   if (c != 0 && c < 0x7F) {
     QuotSplit q = quot_split(s);
     r.r_hi = q.r_hi;
     r.r_lo = q.r_lo;
-    r.k = q.k;
+    r.p2k = pow2f(q.k);
   }
   return r;
 }
@@ -126,7 +126,7 @@ __device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp, const 
   RcpEntry r = tab[q.sc];  // a value in [0, 448]: code <= 0x7E
   // quotient by s * D = m * 2^K; for K < -104 the quotient is first scaled
   // up by 2^P (exact) so that the power handed to the converter stays normal
-  int K = r.k + dexp;
+  int K = (int)(__float_as_uint(r.p2k) >> 23) - 127 + dexp;
   int P = max(-104 - K, 0);
   q.r_hi = __builtin_ldexpf(r.r_hi, P);
   q.r_lo = __builtin_ldexpf(r.r_lo, P);
@@ -135,19 +135,24 @@ __device__ __forceinline__ ColQuant col_block_quant(float amax, int dexp, const 
 }
 
 // col_block_quant where the block's rows all have t >= 2^-88 (or t = 0) and
-// D_e >= 2^-95 -- the decode's fast path: a nonzero post-RHT value is then at
-// least 2^-88 * 2^-9 * 2^-1 * 2^-2 = 2^-100 (decoded values are multiples of
-// that, and a rounded sum is far above it), so div6 needs no prescale, and
-// the power s * D_e = m * 2^K has K >= -9 - 95 = -104, so the quotient needs
-// none either.  The same codes as col_block_quant, fewer instructions.
-__device__ __forceinline__ ColQuant col_block_quant_fast(float amax, int dexp, const RcpEntry* tab) {
-  const float y = __builtin_ldexpf(div6(amax), -dexp);
+// 2^-95 <= D_e <= 2^119 -- the decode's fast path: a nonzero post-RHT value is
+// then at least 2^-88 * 2^-9 * 2^-1 * 2^-2 = 2^-100 (decoded values are
+// multiples of that, and a rounded sum is far above it), so div6 needs no
+// prescale, and the power s * D_e = m * 2^K has -104 <= K <= 127, so the
+// quotient needs none either and the converter's power is a normal float.
+// With p2 = 2^(-2 - dexp) and pd = 2^dexp (normal floats in that range),
+// fl32(amax / 1.5) * p2 is fl32(amax / 6) * 2^-dexp (the same exact scalings
+// by powers of two), and the converter's power is 2^k * pd; code 0 keeps any
+// normal power (its quotients are signed zeros).  The same codes as
+// col_block_quant, fewer instructions.
+__device__ __forceinline__ ColQuant col_block_quant_fast(float amax, float p2, float pd, const RcpEntry* tab) {
+  const float y = div1_5(amax) * p2;
   ColQuant q;
   q.sc = e4m3_encode(fminf(y, 448.0f));
   const RcpEntry r = tab[q.sc];  // a value in [0, 448]: code <= 0x7E
   q.r_hi = r.r_hi;
   q.r_lo = r.r_lo;
-  q.scale = q.sc ? pow2f(r.k + dexp) : 1.0f;
+  q.scale = r.p2k * pd;
   return q;
 }
 
@@ -320,63 +325,50 @@ constexpr uint32_t kNoRow = 0x80000000u;  // beyond every resource (sizes < 2^31
 // Tile row rt of the K-blocked layout: K-block rt of the concatenated
 // per-expert K-block lists (each expert's grouped rows in blocks of kT2Rows,
 // the last one shorter).  Gives its expert, K-block index within the expert,
-// first grouped row and row count; false (for the whole workgroup) when rt is
-// beyond the last K-block.  s_offs holds offsets[0..E] (visible to every
-// thread); s_kbstart (E + 1 ints) and s_wsum (one int per wave) are LDS
-// scratch.  Two barriers; E <= 1024 (four experts per thread).
-__device__ __forceinline__ bool kblock_of_tile(int rt, int E, const int* s_offs, int* s_kbstart, int* s_wsum,
-                                               int& expert, int& kb, int& g_base, int& rows) {
-  const int tid = threadIdx.x;
-  int loc[4], sum = 0;
+// first grouped row and row count; false when rt is beyond the last K-block.
+// s_offs holds offsets[0..E] (visible to every thread).  Each wave computes
+// the same answer on its own -- an inclusive scan of the experts' K-block
+// counts, 64 experts at a time, and the first expert whose running count
+// passes rt -- so no barrier and no LDS scratch are needed.
+__device__ __forceinline__ bool kblock_of_tile(int rt, int E, const int* s_offs, int& expert, int& kb, int& g_base,
+                                               int& rows) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;  // K-blocks of the experts of earlier chunks
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    const int e = c0 + lane;
+    const int n = e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kT2Rows - 1) / kT2Rows : 0;
+    int incl = n;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * tid + i;
-    loc[i] = sum;
-    sum += e < E ? (max(s_offs[e + 1] - s_offs[e], 0) + kT2Rows - 1) / kT2Rows : 0;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    const int total = __shfl(incl, 63, kWave);
+    if (rt < before + total) {  // uniform: K-block rt belongs to an expert of this chunk
+      // the first lane whose running count passes rt (empty experts never do)
+      const int l = (int)__builtin_ctzll(__ballot(before + incl > rt));
+      expert = c0 + l;
+      kb = rt - before - __shfl(incl - n, l, kWave);
+      g_base = s_offs[expert] + kb * kT2Rows;
+      rows = min(kT2Rows, s_offs[expert + 1] - g_base);
+      return true;
+    }
+    before += total;
   }
-  int incl = sum;
-  const int lane = tid & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) s_wsum[tid >> 6] = incl;
-  __syncthreads();
-  int wofs = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kT2Threads / 64; ++w) {
-    wofs += w < (tid >> 6) ? s_wsum[w] : 0;
-    total += s_wsum[w];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (4 * tid + i < E) s_kbstart[4 * tid + i] = wofs + incl - sum + loc[i];
-  if (tid == 0) s_kbstart[E] = total;
-  __syncthreads();
-  if (rt >= total) return false;  // beyond the last K-block (uniform)
-  int lo = 0, hi = E - 1;         // last expert whose first K-block is <= rt (empty experts share starts)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_kbstart[mid] <= rt) lo = mid; else hi = mid - 1;
-  }
-  expert = lo;
-  kb = rt - s_kbstart[lo];
-  g_base = s_offs[lo] + kb * kT2Rows;
-  rows = min(kT2Rows, s_offs[lo + 1] - g_base);
-  return true;
+  return false;
 }
 
 template <int SEL, bool SLOW, int SR>
 __device__ __forceinline__ void column_pair_out(const uint32_t* cw, const float* cm, const int* ce, int dexp,
-                                                const RcpEntry* tab, uint64_t n0, uint64_t n_step, uint32_t klo,
-                                                uint32_t khi, uint2& c0, uint2& c1, uint32_t& s0, uint32_t& s1) {
+                                                float p2, float pd, const RcpEntry* tab, uint64_t n0,
+                                                uint64_t n_step, uint32_t klo, uint32_t khi, uint2& c0, uint2& c1,
+                                                uint32_t& s0, uint32_t& s1) {
   float z0[16], z1[16];
   decode_stage1<SEL, SLOW>(cw, cm, ce, z0, z1);
   rht16_upper(z0);
   rht16_upper(z1);
-  const ColQuant q0 = SLOW ? col_block_quant(absmax16(z0), dexp, tab) : col_block_quant_fast(absmax16(z0), dexp, tab);
-  const ColQuant q1 = SLOW ? col_block_quant(absmax16(z1), dexp, tab) : col_block_quant_fast(absmax16(z1), dexp, tab);
+  const ColQuant q0 = SLOW ? col_block_quant(absmax16(z0), dexp, tab) : col_block_quant_fast(absmax16(z0), p2, pd, tab);
+  const ColQuant q1 = SLOW ? col_block_quant(absmax16(z1), dexp, tab) : col_block_quant_fast(absmax16(z1), p2, pd, tab);
   if (SR == 0) {
     col_encode(z0, q0, c0.x, c0.y);
     col_encode(z1, q1, c1.x, c1.y);
@@ -401,7 +393,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   // The tile's code bytes (256 rows x 128 bytes; row r's 16-byte piece q at
   // position q ^ ((r >> 4) & 7), so that the column phase's 8-byte reads of
   // sixteen rows 16 apart fall on different banks).  Until the tile's loads
-  // return, the same bytes hold the expert offsets and the K-block scan.
+  // return, the same bytes hold the expert offsets.
   // 40 KB in all, so that four workgroups share a CU's 160 KB.
   __shared__ __align__(16) uint8_t s_code[kT2Rows * 128];
   __shared__ RcpEntry s_tab[128];
@@ -410,7 +402,6 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-88
   __shared__ __align__(16) int s_src[kT2Rows];  // source row of each grouped row (-1: none)
   int* const s_offs = reinterpret_cast<int*>(s_code);  // offsets[0..E]
-  int* const s_kbstart = s_offs + 1028;                 // K-block starts (E + 1), then one sum per wave
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -423,7 +414,7 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   int kb = 0, tile_rows = kT2Rows, e = 0;
   for (int i = tid; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
   __syncthreads();
-  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, s_kbstart, s_kbstart + 1028, e, kb, g_base, tile_rows)) return;
+  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, e, kb, g_base, tile_rows)) return;
 
   const int lane = tid & 63, w = tid >> 6;
   const int m = lane >> 2;                    // 16-row block of the column phase
@@ -571,7 +562,8 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
   const int sh = 8 * (cg & 3);
   float cm[16], tv[16];
   uint32_t sb[16];
-  const bool slow = dexp < -95 || s_tiny[m];
+  const bool slow = dexp < -95 || dexp > 119 || s_tiny[m];
+  const float p2 = slow ? 1.0f : pow2f(-2 - dexp), pd = slow ? 1.0f : pow2f(dexp);  // the fast quantizer's powers
   const uint32_t* swd = reinterpret_cast<const uint32_t*>(s_sw) + 4 * (16 * m) + (cg >> 2);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -642,8 +634,8 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       uint2 a, b;
       uint32_t sa, sbb;
       const uint64_t n0 = n_col + (uint64_t)(h0 + 2 * p) * n_step;
-      column_pair_out<p & 3, false, SR>((p < 4) ? wx : wy, cm, nullptr, dexp, s_tab, n0, n_step, klo, khi, a, b,
-                                        sa, sbb);
+      column_pair_out<p & 3, false, SR>((p < 4) ? wx : wy, cm, nullptr, dexp, p2, pd, s_tab, n0, n_step, klo, khi,
+                                        a, b, sa, sbb);
       store(2 * p, a, b, sa, sbb);
     });
   } else {
@@ -659,8 +651,8 @@ __global__ __launch_bounds__(kT2Threads) void k_nvfp4_receive(const RowSrc rs, i
       uint2 a, b;
       uint32_t sa, sbb;
       const uint64_t n0 = n_col + (uint64_t)(h0 + 2 * p) * n_step;
-      column_pair_out<p & 3, true, SR>((p < 4) ? wx : wy, cm, ce, dexp, s_tab, n0, n_step, klo, khi, a, b, sa,
-                                       sbb);
+      column_pair_out<p & 3, true, SR>((p < 4) ? wx : wy, cm, ce, dexp, p2, pd, s_tab, n0, n_step, klo, khi, a, b,
+                                       sa, sbb);
       store(2 * p, a, b, sa, sbb);
     });
   }
@@ -743,15 +735,14 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
                                                               uint8_t* __restrict__ row_scales,
                                                               uint8_t* __restrict__ col_codes,
                                                               uint8_t* __restrict__ col_scales) {
-  // the tile's code bytes (the NVFP4 receive's swizzled layout), the expert
-  // offsets and the K-block scan until the loads return
+  // the tile's code bytes (the NVFP4 receive's swizzled layout); the expert
+  // offsets until the loads return
   __shared__ __align__(16) uint8_t s_code[kT2Rows * 128];
   __shared__ float s_t[kT2Rows];
   __shared__ uint4 s_sw[kT2Rows];      // the tile's 16 NVFP4 scale bytes of each row
   __shared__ int s_tiny[kT2Rows / 16];  // a row of the 16-row block has 0 < t < 2^-100
   __shared__ __align__(16) int s_src[kT2Rows];
   int* const s_offs = reinterpret_cast<int*>(s_code);
-  int* const s_kbstart = s_offs + 1028;
 
   const int tid = threadIdx.x;
   const unsigned nb = gridDim.x, bx = blockIdx.x;
@@ -763,7 +754,7 @@ __global__ __launch_bounds__(kT2Threads) void k_mxfp4_receive(const RowSrc rs, i
   int g_base = rt * kT2Rows, kb = 0, tile_rows = kT2Rows, kex = 0;
   for (int i = threadIdx.x; i <= E; i += kT2Threads) s_offs[i] = offsets[i];
   __syncthreads();
-  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, s_kbstart, s_kbstart + 1028, kex, kb, g_base, tile_rows)) return;
+  if (KBLOCK && !kblock_of_tile(rt, E, s_offs, kex, kb, g_base, tile_rows)) return;
 
   const int lane = tid & 63, w = tid >> 6;
   const int m = lane >> 2;                    // 16-row block of the column phase
