@@ -67,7 +67,8 @@ __device__ __forceinline__ int pow2_exponent(float p) {
 // ----------------------------------------------------------------- E4M3
 // E4M3FN code of y in [0, 448] (RNE; the caller guarantees the range).
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
+  // the converter keeps the upper half of its `old` operand: y's own bits, masked off
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, __float_as_int(y), false) & 0xFFu;
 }
 // Value of an E4M3FN code held in the low byte of w.
 __device__ __forceinline__ float e4m3_decode(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, 0); }

@@ -295,6 +295,17 @@ template <bool FAST = false>
 __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, const MantEntry* tab) {
   float s = e4m3_decode(sc);
   GenBlock g;
+  if (FAST) {
+    // branch-free: code 0 reads entry 0 and then zeros its reciprocal, so
+    // every quotient is a signed zero; its power 2^(kD - 1 + kadj) is a
+    // normal float for D >= 2^-85 (any normal power encodes a zero alike)
+    const MantEntry t = tab[(__float_as_uint(s) >> 20) & 7u];
+    const bool z = !(s > 0.0f);  // (D = 0 only gives the code 0)
+    g.r_hi = z ? 0.0f : t.r_hi;
+    g.r_lo = z ? 0.0f : t.r_lo;
+    g.scale = pow2f(__builtin_amdgcn_frexp_expf(s) - 1 + kD + t.kadj);
+    return g;
+  }
   if (!(s > 0.0f)) {  // (D = 0 only gives the code 0)
     g.r_hi = g.r_lo = 0.0f;
     g.scale = 1.0f;
@@ -303,7 +314,7 @@ __device__ __forceinline__ GenBlock gen_block_tab(uint32_t sc, float D, int kD, 
   int ks = __builtin_amdgcn_frexp_expf(s) - 1;
   const MantEntry t = tab[(__float_as_uint(s) >> 20) & 7u];
   int kc = ks + kD + t.kadj;
-  if (!FAST && kc < -104) return gen_block(sc, D);
+  if (kc < -104) return gen_block(sc, D);
   g.r_hi = t.r_hi;
   g.r_lo = t.r_lo;
   g.scale = pow2f(kc);
