@@ -12,7 +12,11 @@ of 32 experts from N(0,1) logits, 16-row aligned slots):
 value = algorithmic bytes (distinct inputs read once + outputs, padding rows
 excluded) of the step / step time, in GB/s.  Inputs are resident in HBM
 before the timed region; the timed region is K eager steps on one stream,
-and HIP events on that stream bracket every call of every timed step.
+and HIP events on that stream bracket every call of every timed step.  It
+follows the configuration's per-call passes at once, and before its W warm-up
+steps untimed steps run for --settle-s seconds (0.1 by default): the GPU's
+clock needs tens of milliseconds of a sustained load to settle, and the
+receive runs up to ~40% slower during that transient (measured).
 
 ``kernels`` lists every call of the path at each of the five configurations
 (their own seeded inputs): its HIP-event time per launch (eager passes, each
@@ -88,6 +92,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--reps", type=int, default=20, help="eager passes per configuration for the per-call times")
+    p.add_argument("--settle-s", type=float, default=STEP_SETTLE_S,
+                   help="untimed steps for this many seconds before the warm-up steps (0: none)")
     p.add_argument("--configs", default="1,2,3,4,5", help="configurations listed under 'kernels'")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=CPU_SAMPLE_TOKENS)
@@ -319,14 +325,35 @@ def evict_mall(buf):
     buf.amax()
 
 
+SETTLE_S = 0.06     # untimed warm-up of each configuration's per-call passes
+STEP_SETTLE_S = 0.1  # untimed steps before the timed region's warm-up steps
+
+
+def settle(calls, flush=None, seconds=SETTLE_S):
+    """Untimed passes of ``calls`` (each after the MALL-evicting read when a flush
+    buffer is given) for at least ``seconds`` of GPU time.  The GPU's clock
+    settles only after tens of milliseconds of a sustained load: measured on
+    config 3, the receive runs at ~400 us per call right after an idle pause or
+    a change of load and ~270-290 us once settled, over 20-40 steps; a timed
+    phase that starts before that would time the transient."""
+    import torch
+    t0 = time.monotonic()
+    while True:
+        if flush is not None:
+            evict_mall(flush)
+        for c in calls:
+            c.fn()
+        torch.cuda.synchronize()
+        if time.monotonic() - t0 >= seconds:
+            return
+
+
 def time_calls(path, reps, flush):
     """Per-call HIP-event times (ms per launch) over ``reps`` eager passes of all
-    the path's calls, each pass after the MALL-evicting read."""
+    the path's calls, each pass after the MALL-evicting read (after ``settle``)."""
     import torch
     calls = path.calls
-    for c in calls:                                   # warm-up pass
-        c.fn()
-    torch.cuda.synchronize()
+    settle(calls, flush)                              # warm-up passes
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(reps)]
     for r in range(reps):
@@ -343,12 +370,16 @@ def time_calls(path, reps, flush):
     return out
 
 
-def time_step(path, steps, warmup):
+def time_step(path, steps, warmup, settle_s=STEP_SETTLE_S):
     """The timed region: ``steps`` eager passes of the step's calls on the current
     stream, HIP events on that stream around every call; returns the wall time
-    per step and each call's mean event time over the timed steps."""
+    per step and each call's mean event time over the timed steps.  Before the
+    ``warmup`` steps, untimed steps run for ``settle_s`` seconds so that the
+    timed steps see the GPU's settled clock (``settle``)."""
     import torch
     calls = path.step_calls()
+    if settle_s > 0:
+        settle(calls, None, settle_s)
     for _ in range(warmup):
         for c in calls:
             c.fn()
@@ -540,7 +571,7 @@ def cpu_baseline(w, n_tok, n_chunk=CPU_CHUNK_TOKENS):
 
 
 # ---------------------------------------------------------------------------- output
-def headline(path3, ms_step, per, steps, warmup, kernels, cpu, copy=None):
+def headline(path3, ms_step, per, steps, warmup, kernels, cpu, copy=None, settle_s=STEP_SETTLE_S):
     calls = path3.step_calls()
     total = sum(c.bytes for c in calls)
     dom = max(per, key=lambda nm: per[nm])
@@ -561,7 +592,8 @@ def headline(path3, ms_step, per, steps, warmup, kernels, cpu, copy=None):
                                   unit="G wave-instructions/s", frac=round(gips / VALU_PEAK_GIPS, 4))
     return {
         "metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "steps": steps, "warmup": warmup, "settle_s": settle_s, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": dict(path3.desc, workload=path3.desc["workload"] + ": route plan + NVFP4 pack + D_e + direct "
                        "receive (rowwise + RHT columnwise in K-blocks) + unpack of the received rows",
@@ -697,18 +729,24 @@ def main():
     for n in configs:
         path = Path(n, dev, w3 if n == 3 else None)
         per = time_calls(path, args.reps, flush)
+        headline_cfg = n == 3 and args.workload in (None, "cfg3")
+        step = None
+        if headline_cfg or args.workload is not None:
+            # the timed step follows the per-call passes at once (the host-side work
+            # of config_kernels comes after it): no idle pause for the clock to drop in
+            step = time_step(path, args.steps, args.warmup, args.settle_s)
         kernels[f"cfg{n}"] = config_kernels(n, path, per)
         progress(f"config {n}: {len(per)} calls timed")
-        if n == 3 and args.workload in (None, "cfg3"):
-            ms_step, step_per = time_step(path, args.steps, args.warmup)
-            head = (path, ms_step, step_per)
-            progress(f"step timed: {ms_step * 1e3:.1f} us")
+        if headline_cfg:
+            head = (path,) + step
+            progress(f"step timed: {step[0] * 1e3:.1f} us")
         elif args.workload is not None:
             calls = path.step_calls()
-            ms_step, step_per = time_step(path, args.steps, args.warmup)
+            ms_step, step_per = step
             total = sum(c.bytes for c in calls)
             emit({"metric": METRIC, "value": round(total / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
-                  "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+                  "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle_s,
+                  "ms_per_step": round(ms_step, 4),
                   "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
                   "data": "synthetic", "config": dict(path.desc, bytes_per_step=total),
                   "step_ms": {nm: round(v, 5) for nm, v in step_per.items()}, "kernels": kernels,
@@ -719,9 +757,10 @@ def main():
         torch.cuda.empty_cache()
     if head is None:
         p3 = Path(3, dev, w3)
-        head = (p3,) + time_step(p3, args.steps, args.warmup)
+        head = (p3,) + time_step(p3, args.steps, args.warmup, args.settle_s)
     path3, ms_step, step_per = head
-    emit(headline(path3, ms_step, step_per, args.steps, args.warmup, kernels, cpu, copy_reference(dev)), args)
+    emit(headline(path3, ms_step, step_per, args.steps, args.warmup, kernels, cpu, copy_reference(dev), args.settle_s),
+         args)
 
 
 if __name__ == "__main__":
