@@ -724,6 +724,12 @@ def main():
     if args.counters_pass:
         return main_counters_pass(args, dev)
     flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: 4x the MALL
+    # torch sets its GPU random generator up on first use (the marker kernel that
+    # time_step launches before its timed steps), and GPU work right after that
+    # runs slower for a while (measured: the first timed step 772 us against 726
+    # us once it had been used): done here, before anything is timed
+    torch.empty(64, dtype=torch.float32, device=dev).random_()
+    torch.cuda.synchronize()
     kernels = {}
     head = None
     for n in configs:
