@@ -92,21 +92,24 @@ int32_t ep_abi_version(void);
 const char* ep_status_string(int32_t status);
 
 /* Bytes of one packed NVFP4 row, 9*hidden/16 + 4; negative (EP_ERR_SHAPE) if
- * hidden is not a positive multiple of 64. */
+ * hidden is not a positive multiple of 64, EP_ERR_RANGE if hidden >= 2^31. */
 int64_t ep_nvfp4_packed_row_bytes(int64_t hidden);
 
 /* Grouped-row capacity the routing plan needs: tokens*top_k +
- * num_experts*(alignment-1); negative status on invalid arguments. */
+ * num_experts*(alignment-1); negative status on invalid arguments
+ * (EP_ERR_RANGE if any argument is >= 2^31). */
 int64_t ep_route_capacity(int64_t tokens, int64_t top_k, int64_t num_experts, int64_t alignment);
 
-/* Workspace bytes ep_route_plan needs for these sizes. */
+/* Workspace bytes ep_route_plan needs for these sizes; 0 if a size is
+ * negative or zero where it must not be, or >= 2^31. */
 size_t ep_route_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_experts);
 
 /* The 16-bit RHT sign mask M: d_i = -1 iff bit i of M is set.  Exported so a
  * caller can apply the same transform to the other wgrad operand. */
 uint32_t ep_rht_sign_mask(void);
 
-/* Workspace bytes dswiglu_nvfp4_quant needs (offsets + one word per token row). */
+/* Workspace bytes dswiglu_nvfp4_quant needs (offsets + one word per token
+ * row); 0 if tokens < 0, num_experts < 1 or either is >= 2^31. */
 size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts);
 
 /* ---------------------------------------------------------------- pack */

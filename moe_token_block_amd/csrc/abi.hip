@@ -22,6 +22,7 @@ MTB_EXPORT const char* ep_status_string(int32_t status) {
 
 MTB_EXPORT int64_t ep_nvfp4_packed_row_bytes(int64_t hidden) {
   if (hidden <= 0 || hidden % 64 != 0) return EP_ERR_SHAPE;
+  if (hidden >= mtb::kSizeLimit) return EP_ERR_RANGE;
   return 9 * hidden / 16 + 4;
 }
 

@@ -54,8 +54,8 @@ MTB_EXPORT int32_t ep_mxfp4_kblock_tile(const uint8_t* col_codes, const uint8_t*
   if (!col_codes || !col_scales || !out) return EP_ERR_NULL;
   if (hidden <= 0 || hidden % 64 != 0 || hidden > (1 << 20)) return EP_ERR_SHAPE;
   if (len <= 0 || len > 256 || len % 32 != 0 || block_row < 0 || block_row % 32 != 0) return EP_ERR_SHAPE;
-  if (ha < 0 || hb < 0 || ha + 16 > hidden || hb + 16 > hidden) return EP_ERR_SHAPE;
-  if ((block_row + len) * hidden / 2 >= ((int64_t)1 << 40)) return EP_ERR_RANGE;
+  if (ha < 0 || hb < 0 || ha > hidden - 16 || hb > hidden - 16) return EP_ERR_SHAPE;
+  if (block_row >= kSizeLimit || (block_row + len) * hidden / 2 >= ((int64_t)1 << 40)) return EP_ERR_RANGE;
   const uint8_t* codes = col_codes + hidden * block_row / 2;
   const uint8_t* scales = col_scales + hidden * block_row / 32;
   hipLaunchKernelGGL(k_mxfp4_kblock_tile, dim3(1), dim3(64), 0, (hipStream_t)stream, codes, scales, (int)len, (int)ha,

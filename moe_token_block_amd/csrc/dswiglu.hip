@@ -716,7 +716,7 @@ using namespace mtb;
 static size_t rowmax_bytes(int64_t tokens) { return (size_t)((tokens + 3) / 4) * 16; }
 
 MTB_EXPORT size_t dswiglu_workspace_bytes(int64_t tokens, int64_t num_experts) {
-  if (num_experts < 1 || tokens < 0) return 0;
+  if (num_experts < 1 || tokens < 0 || tokens >= kSizeLimit || num_experts >= kSizeLimit) return 0;
   return rowmax_bytes(tokens) + (size_t)(2 * (num_experts + 1) * sizeof(int32_t));
 }
 
@@ -727,7 +727,7 @@ static int32_t dswiglu_quant_impl(const uint16_t* preact, const uint16_t* dy, in
                                        void* workspace, size_t workspace_bytes,
                                        const uint64_t* sr_state, int sr_words, void* stream) {
   if (tokens < 0 || ffn <= 0 || ffn % 64 != 0 || num_experts < 1 || num_experts > 1024) return EP_ERR_SHAPE;
-  if (tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
+  if (tokens >= INT32_MAX / 8 || tokens + 16 * num_experts >= INT32_MAX / 8 || ffn > (1 << 20)) return EP_ERR_RANGE;
   if (!counts || !amax || !row_scale || !col_scale) return EP_ERR_NULL;
   if (tokens > 0 && (!preact || !dy || !row_codes || !row_scales || !col_codes || !col_scales)) return EP_ERR_NULL;
   if (!workspace || workspace_bytes < dswiglu_workspace_bytes(tokens, num_experts) || ((uintptr_t)workspace & 15))
@@ -853,7 +853,8 @@ MTB_EXPORT int32_t dswiglu_nvfp4_quant_noalloc(const uint16_t* preact, const uin
                                                uint8_t* col_codes, uint8_t* col_scales, float* col_scale,
                                                void* stream) {
   if (tokens < 0 || num_experts < 1) return EP_ERR_SHAPE;
-  if (dswiglu_workspace_bytes(tokens, num_experts) > kScratchBytes) return EP_ERR_SCRATCH;
+  const size_t need = dswiglu_workspace_bytes(tokens, num_experts);   // 0: sizes past any byte count
+  if (need == 0 || need > kScratchBytes) return EP_ERR_SCRATCH;
   void* ws = nullptr;
   const int32_t st = scratch_ptr(&ws);
   if (st != EP_OK) return st;

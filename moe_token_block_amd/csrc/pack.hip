@@ -606,7 +606,7 @@ MTB_EXPORT int32_t ep_nvfp4_pack_scatter(const uint16_t* x, int64_t tokens, int6
 MTB_EXPORT int32_t ep_mxfp8_pack(const uint16_t* x, int64_t rows, int64_t hidden, uint8_t* data,
                                  uint8_t* scales, void* stream) {
   if (rows < 0 || hidden <= 0 || hidden % 32 != 0) return EP_ERR_SHAPE;
-  if (rows * hidden >= ((int64_t)1 << 40)) return EP_ERR_RANGE;
+  if (rows > (((int64_t)1 << 40) - 1) / hidden) return EP_ERR_RANGE;   // rows * hidden >= 2^40
   if (rows == 0) return EP_OK;
   if (!x || !data || !scales) return EP_ERR_NULL;
   int64_t chunks = rows * hidden / 16;

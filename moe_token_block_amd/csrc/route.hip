@@ -299,13 +299,18 @@ static int64_t route_waves(int64_t tokens, int64_t top_k) { return (tokens * top
 MTB_EXPORT int64_t ep_route_capacity(int64_t tokens, int64_t top_k, int64_t num_experts, int64_t alignment) {
   if (tokens < 0 || top_k < 1 || num_experts < 1) return EP_ERR_SHAPE;
   if (alignment < 16 || alignment % 16 != 0) return EP_ERR_ALIGN;
+  if (tokens >= kSizeLimit || top_k >= kSizeLimit || num_experts >= kSizeLimit || alignment >= kSizeLimit)
+    return EP_ERR_RANGE;
   return tokens * top_k + num_experts * (alignment - 1);
 }
 
 MTB_EXPORT size_t ep_route_workspace_bytes(int64_t tokens, int64_t top_k, int64_t num_experts) {
   if (tokens < 0 || top_k < 1 || num_experts < 1) return 0;
+  if (tokens >= kSizeLimit || top_k >= kSizeLimit || num_experts >= kSizeLimit) return 0;
   int64_t w = route_waves(tokens, top_k);
-  return (size_t)((w > 0 ? w : 1) * num_experts * sizeof(int32_t));
+  int64_t bytes = 0;
+  if (__builtin_mul_overflow((w > 0 ? w : 1) * (int64_t)sizeof(int32_t), num_experts, &bytes)) return 0;
+  return (size_t)bytes;
 }
 
 MTB_EXPORT int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_t tokens, int64_t top_k,
@@ -316,7 +321,9 @@ MTB_EXPORT int32_t ep_route_plan(const void* topk_idx, int32_t idx_dtype, int64_
   if (num_experts > kMaxExperts) return EP_ERR_SHAPE;
   if (alignment < 16 || alignment % 16 != 0) return EP_ERR_ALIGN;
   if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64) return EP_ERR_DTYPE;
-  if (tokens * top_k + num_experts * alignment >= (int64_t)INT32_MAX || r_cap >= (int64_t)INT32_MAX) return EP_ERR_RANGE;
+  if (tokens >= INT32_MAX || top_k >= INT32_MAX || alignment >= INT32_MAX || r_cap >= INT32_MAX ||
+      tokens * top_k + num_experts * alignment >= (int64_t)INT32_MAX)
+    return EP_ERR_RANGE;
   if (r_cap < ep_route_capacity(tokens, top_k, num_experts, alignment)) return EP_ERR_CAPACITY;
   if (!counts || !offsets || !src_row || !d_error || (tokens > 0 && (!topk_idx || !dst_row))) return EP_ERR_NULL;
   if (!workspace || workspace_bytes < ep_route_workspace_bytes(tokens, top_k, num_experts)) return EP_ERR_WORKSPACE;
