@@ -49,7 +49,7 @@ HBM_PEAK_GBS = 8000.0
 # VALU issue: 256 CUs, each issuing one wave64 vector instruction per clock
 # (four 16-lane SIMDs, four clocks per wave64 instruction each), at 2.4 GHz
 VALU_PEAK_GIPS = 256 * 2.4
-CPU_SAMPLE_TOKENS = 4096        # one process: about 10 s of oracle work on the GPU machine host
+CPU_SAMPLE_TOKENS = 4096        # one process: about 10 s of oracle work on one host core
 CPU_CHUNK_TOKENS = 1024         # one process per core: each on its own chunk
 
 # ---------------------------------------------------------------------------- calls
@@ -529,8 +529,8 @@ def cpu_model():
 def cpu_baseline(w, n_tok, n_chunk=CPU_CHUNK_TOKENS):
     """The oracle as it stands on the host, before anything touches the GPU: one
     single-threaded process on tokens [0, n_tok) of config 3, then one
-    single-threaded process per core (at most 16, the machine's CPU share, whatever
-    the affinity mask shows), each on its own n_chunk tokens (their own routing).
+    single-threaded process per core (at most 16, whatever the affinity mask
+    shows), each on its own n_chunk tokens (their own routing).
     The worker processes are spawned with OMP/OpenBLAS/MKL threads set to 1, so
     each uses exactly one core."""
     import multiprocessing as mp
@@ -703,8 +703,8 @@ def progress(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
-                                   "(multi-GPU expert-parallel transport is not part of it)"}))
+        print(json.dumps({"error": "the benchmark measures one GPU only; --gpus must be 1 "
+                                   "(multi-GPU expert-parallel transport is not implemented)"}))
         sys.exit(2)
     import workloads
     configs = [int(c) for c in args.configs.split(",") if c]

@@ -7,7 +7,7 @@ read MXFP4 directly: E2M1 elements with one E8M0 scale (a power of two) per 32
 consecutive elements along K.  This module defines an MXFP4 variant of the same
 receive -- same routing, same decode, same 16-point RHT for the columnwise
 operand -- with only the final quantizer replaced.  Its readings (R22, R23) are
-this build's own; every step is exact except the RHT's float32 sums, which are
+ours, not the pages'; every step is exact except the RHT's float32 sums, which are
 the ones R15 already fixes.
 
 R22 (block quantizer).  For a block of 32 values with a = max |x|:

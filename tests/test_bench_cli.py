@@ -1,5 +1,5 @@
 """bench.py's command line on the host: more than one GPU is refused with a
-message (this build measures one GPU), before any GPU work."""
+message (the benchmark measures one GPU), before any GPU work."""
 import json
 import os
 import subprocess
