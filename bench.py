@@ -104,6 +104,9 @@ def parse():
                    help="profiling aid (with --workload): each call --steps times between marker kernels")
     p.add_argument("--only", default=None, choices=["copy"],
                    help="with --counters-pass: a 1 GiB device copy instead (the counter reference)")
+    p.add_argument("--copy-bytes", type=int, default=1 << 30,
+                   help="with --only copy: bytes per copy (a multiple of 16); below 1 GiB each launch "
+                        "follows the MALL-evicting read, as the calls' launches do")
     return p.parse_args()
 
 
@@ -645,18 +648,25 @@ def main_counters_pass(args, dev):
     once, then for each call a marker kernel (a torch random fill, used nowhere
     else) followed by --steps launches of the call, each after the MALL-evicting
     read (a torch reduction).  A profile's dispatches between two markers that
-    are not the reduction are that call's.  --only copy: a 1 GiB
-    device-to-device copy after one marker instead (the reference that scales
-    the memory counters)."""
+    are not the reduction are that call's.  --only copy: --steps
+    device-to-device copies of --copy-bytes (1 GiB: the reference that scales
+    the memory counters; smaller: the kernel-only time a plain copy of a call's
+    size takes, each launch after the MALL-evicting read) after one marker
+    instead."""
     import torch
     marker = torch.empty(64, dtype=torch.float32, device=dev)
     if args.only == "copy":
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        if args.copy_bytes <= 0 or args.copy_bytes % 16 != 0 or args.copy_bytes > (1 << 30):
+            raise SystemExit("--copy-bytes must be a positive multiple of 16, at most 1 GiB")
+        a = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         b = torch.empty_like(a)
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev) if args.copy_bytes < (1 << 30) else None
         torch.cuda.synchronize()
         marker.random_()
         torch.cuda.synchronize()
         for _ in range(args.steps):
+            if flush is not None:
+                evict_mall(flush)
             b.copy_(a)
         torch.cuda.synchronize()
         marker.random_()
